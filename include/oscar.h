@@ -1,0 +1,283 @@
+/*
+ * oscar.h — C ABI of liboscar: the online hot path of OSCAR (Offline Spectral
+ * Covariance-Aware Rotation for 2-bit KV cache quantization) on AMD Instinct
+ * MI355X (gfx950).
+ *
+ * Sources cited in this header (the method is described in prose only):
+ *   [TS]  "Technical Summary: OSCAR - Offline Spectral Covariance-Aware Rotation
+ *         for 2-bit KV Cache Quantization" (gist.science), sections 2.1, 2.2.A
+ *         (Offline Calibration Phase), 2.2.B (Online Serving Phase), 4.
+ *   [AB]  the arXiv abstract of "OSCAR: Offline Spectral Covariance-Aware
+ *         Rotation for 2-bit KV Cache Quantization" (mlsanity.com paper page,
+ *         section "Abstract (arXiv)").
+ * Where the sources are silent, the reading taken is stated next to the
+ * definition ("Reading:").
+ *
+ * Conventions used everywhere below
+ *   d          head dimension, 64 or 128.
+ *   H_kv, H_q  key/value heads and query heads; G = H_q / H_kv, 1 <= G <= 16.
+ *              Query head i reads KV head floor(i / G).
+ *   page       16 consecutive token positions [16p, 16p + 16) of one sequence.
+ *   group      32 consecutive rotated channels [32g, 32g + 32); n_g = d / 32.
+ *   rows       vectors are row vectors; a rotation acts as y = x . R, with R
+ *              stored row-major as R[k][c] (k = input channel, c = output).
+ *   bf16, f16  IEEE-754 binary16 ("f16") and bfloat16 ("bf16") bit patterns,
+ *              little-endian, stored as uint16.
+ *
+ * Ownership and execution
+ *   The caller owns every buffer.  The library never allocates device memory,
+ *   never synchronises a stream and keeps no state apart from a thread-local
+ *   error string.  Device calls are asynchronous on the given stream
+ *   (hipStream_t passed as void*; NULL = the null stream).  No call throws.
+ *
+ * Errors
+ *   Every call validates its host-visible arguments (pointers, geometry,
+ *   sizes) before launching anything; on a violation it launches nothing and
+ *   returns OSCAR_ERR_INVALID_ARG, OSCAR_ERR_UNSUPPORTED or
+ *   OSCAR_ERR_WORKSPACE.  A failed launch returns OSCAR_ERR_HIP.  Device-side
+ *   contents (page ids inside block tables, sequence lengths, row positions)
+ *   are preconditions stated per call; they are not checked.
+ *   oscar_last_error() returns a readable detail for the last non-OK status of
+ *   the calling thread.
+ */
+#ifndef OSCAR_H_
+#define OSCAR_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  OSCAR_OK = 0,
+  OSCAR_ERR_INVALID_ARG = 1, /* null pointer, negative size, inconsistent shape   */
+  OSCAR_ERR_UNSUPPORTED = 2, /* geometry outside d in {64,128}, G in [1,16], ...  */
+  OSCAR_ERR_NUMERIC = 3,     /* non-finite input or eigensolver non-convergence   */
+  OSCAR_ERR_WORKSPACE = 4,   /* workspace pointer null or smaller than required   */
+  OSCAR_ERR_HIP = 5          /* a HIP runtime call or kernel launch failed        */
+} oscar_status;
+
+#define OSCAR_PAGE_TOKENS 16
+#define OSCAR_GROUP_CHANNELS 32
+#define OSCAR_VERSION 1
+
+/* Name of a status code ("OSCAR_OK", ...). Never NULL. */
+const char* oscar_status_string(oscar_status s);
+/* Detail for the calling thread's last non-OK status; "" if none. */
+const char* oscar_last_error(void);
+/* OSCAR_VERSION of the built library. */
+int32_t oscar_version(void);
+
+/* ------------------------------------------------------------------------ *
+ * Offline calibration (host, synchronous, float64 arithmetic inside).
+ *
+ * Computes, per KV head h with query group Q(h) = {hG, ..., hG + G - 1}
+ * ([TS] 2.1 and 2.2.A steps 1-4; [AB]):
+ *   C_Q(h) = 1/(N G) sum_{i in Q(h)} Q_i^T Q_i              (query-aware key
+ *            target; Q_i is the [N, d] matrix of query head i's rows)
+ *   C_S(h) = 1/(N G) sum_{i in Q(h)} O_i^T O_i,  O_i = S_i V_h (score-aware value
+ *            target V^T S^T S V / N; S_i is the attention-score matrix)
+ *   U = eigenvectors of C, ordered by descending eigenvalue
+ *   R = U . H . P_br  with H = H_d / sqrt(d) (Sylvester Hadamard, H_1 = [1],
+ *            H_2n = [[H_n, H_n], [H_n, -H_n]]) and P_br[r][c] = 1 iff r is the
+ *            log2(d)-bit reversal of c (an involution).
+ *   R_K uses U_Q (of C_Q), R_V uses U_S (of C_S).
+ *   tau_K (tau_V) = the clip_quantile quantile of |K_h . R_K(h)| (|V_h . R_V(h)|)
+ *            pooled over all N rows, all KV heads and all d channels ([TS] 2.2.A
+ *            step 4: one threshold per layer).
+ * Readings:
+ *   - S_i = row-softmax(Q_i K_h^T / sqrt(d) + causal mask), i.e. calibration
+ *     row r attends to rows 0..r.  If o_calib is given it is used as O_i
+ *     directly (a model run can capture S V itself).
+ *   - Eigenvector sign: each column of U is negated if needed so that its
+ *     entry of largest magnitude is positive (lowest index on ties).
+ *   - Quantile: the M values |y| sorted ascending a[0..M-1]; rr = q (M - 1);
+ *     tau = a[floor(rr)] + (rr - floor(rr)) (a[floor(rr)+1] - a[floor(rr)]).
+ * Eigen-decomposition is a cyclic Jacobi iteration in float64 that stops
+ * when every off-diagonal entry is below 1e-15 * ||C||_F, after at most
+ * max_sweeps sweeps (0 selects 64); not reaching that returns
+ * OSCAR_ERR_NUMERIC.
+ * n_threads: host worker threads for the calibration attention (0 = all).
+ * Inputs (host, row-major float32): q_calib [n_rows][H_kv*G][d],
+ * k_calib and v_calib [n_rows][H_kv][d], o_calib NULL or [n_rows][H_kv*G][d].
+ * Outputs (host, float64): r_k, r_v [H_kv][d][d]; *tau_k, *tau_v;
+ * eig_k, eig_v NULL or [H_kv][d] (descending).
+ * Errors: INVALID_ARG for null required pointers, n_rows < 2, H_kv < 1 or
+ * clip_quantile outside (0, 1]; UNSUPPORTED for d not in {64, 128} or G
+ * outside [1, 16]; NUMERIC for a non-finite input value or non-convergence.
+ * ------------------------------------------------------------------------ */
+oscar_status oscar_build_rotation(int32_t d, int32_t n_kv_heads, int32_t group_q,
+                                  int64_t n_rows, const float* q_calib,
+                                  const float* k_calib, const float* v_calib,
+                                  const float* o_calib, double clip_quantile,
+                                  int32_t max_sweeps, int32_t n_threads,
+                                  double* r_k, double* r_v, double* tau_k,
+                                  double* tau_v, double* eig_k, double* eig_v);
+
+/* ------------------------------------------------------------------------ *
+ * Paged cache geometry ([TS] 2.2.B: sink and recent tokens in BF16, the
+ * middle history in INT2 after rotation and clipping, paged and compatible
+ * with prefix caching; [AB]: paged KV-cache serving).
+ *
+ * Regions of a sequence of length L (L counts the token being decoded):
+ *   sink   = [0, min(S, L))
+ *   recent = [max(S, L - W), L)
+ *   middle = [S, L - W) when L - W > S, else empty
+ * with S = n_sink and W = n_recent.  Sink and recent tokens live raw
+ * (unrotated) in BF16 pages; middle tokens live rotated, clipped and
+ * quantized in INT2 pages.
+ *
+ * Block tables bt_q and bt_h are int32 [B][max_pages] (row stride
+ * max_pages).  Entry [b][p] names the physical INT2 (resp. BF16) page that
+ * holds logical page p = floor(t / 16) of sequence b.  bt_q[b][p] is read
+ * only when page p holds a middle token, bt_h[b][p] only when it holds a sink
+ * or recent token; other entries may hold any value (e.g. -1).  Several
+ * sequences may name the same physical page (a shared prefix); pages are
+ * only read by the decode call.
+ *
+ * INT2 page.  A physical INT2 page holds all H_kv heads; head h of page P
+ * starts at byte (P * H_kv + h) * B_q, B_q = 12 d  (1536 B at d = 128, 768 B
+ * at d = 64).  Inside it, six areas follow each other:
+ *   KC  K codes    4d bytes = (16 d / 64) uint32 words
+ *   VC  V codes    4d bytes
+ *   KS  K scales   f16 [16 slots][n_g]
+ *   KZ  K zeros    f16 [16 slots][n_g]
+ *   VS  V scales   f16 [4][n_g][4]   index (q n_g + g) 4 + r, slot = 4q + r
+ *   VZ  V zeros    f16 [4][n_g][4]   same index
+ * A code is a 2-bit unsigned integer c in {0,1,2,3} at bit positions
+ * [b, b+1] of a little-endian uint32 word.  With n_w = d / 64:
+ *   KC: the code of slot m, channel c lives in word (quad * 16 + m) * n_w + w,
+ *       where g = c / 32, hb = (c / 16) % 2, quad = (c / 4) % 4, r = c % 4,
+ *       w = g / 2, and bit b = 16 (r % 2) + 8 (g % 2) + 4 hb + 2 (r / 2).
+ *   VC: the code of slot t = 4q + r (q, r in 0..3), channel c lives in word
+ *       (q * 16 + c16) * n_w + w, where c16 = c % 16, blk = c / 16,
+ *       w = blk / 4, bb = blk % 4, and bit b = 16 (r % 2) + 8 (r / 2) + 2 bb.
+ * Slots of a page that hold no middle token are never read.
+ * The decoded (dequantized) value of a code is c * s + z, with s, z the f16
+ * scale and zero of that slot's channel group.
+ *
+ * BF16 page.  Head h of physical BF16 page P starts at element
+ * (P * H_kv + h) * 32 d of a bf16 array and holds
+ *   K  [16 slots][d]    (token-major)
+ *   V  [d][16 slots]    (channel-major)
+ * ------------------------------------------------------------------------ */
+size_t oscar_int2_page_bytes(int32_t d, int32_t n_kv_heads); /* per physical page */
+size_t oscar_bf16_page_bytes(int32_t d, int32_t n_kv_heads); /* per physical page */
+
+typedef struct {
+  int32_t d;            /* 64 or 128                                          */
+  int32_t n_kv_heads;   /* H_kv >= 1                                          */
+  int32_t n_sink;       /* S >= 0                                             */
+  int32_t n_recent;     /* W >= 0                                             */
+  void* int2_pool;      /* device, n_int2_pages * oscar_int2_page_bytes bytes */
+  int64_t n_int2_pages;
+  void* bf16_pool;      /* device, n_bf16_pages * oscar_bf16_page_bytes bytes */
+  int64_t n_bf16_pages;
+} oscar_cache;
+
+/* ------------------------------------------------------------------------ *
+ * Quantize-append ([TS] 2.2.B: the middle history is stored in INT2 after the
+ * fixed rotation and clipping; 2.2.A step 4 for the clip).
+ * For every row j < n_rows, every KV head h, and X in {K, V}:
+ *   y = x_j,h . R_X(h)                       (R_K or R_V, float32 [H_kv][d][d])
+ *   y = min(max(y, -tau_X), tau_X)
+ *   per group g: mn = min, mx = max of its 32 values;
+ *       s = f16_rne((mx - mn) / 3), z = f16_rne(mn)
+ *   code = clamp(rne((y - z) / s), 0, 3); code = 0 where s == 0
+ * and the codes, s and z are written to slot row_pos[j] % 16 of INT2 page
+ * bt_q[row_seq[j]][row_pos[j] / 16] in the layout above.  Other slots of the
+ * page are left unchanged.
+ * Readings: asymmetric INT2 with z = group minimum and s = range / 3, groups
+ * of 32 consecutive rotated channels per token, codes taken against the
+ * stored f16 s and z, round-half-to-even, symmetric clip.
+ * k_new, v_new: device bf16 [n_rows][H_kv][d].  row_seq, row_pos: device
+ * int32 [n_rows].  bt_q: device int32 [B][max_pages].  r_k, r_v: device
+ * float32 [H_kv][d][d].
+ * Preconditions (device contents): 0 <= row_pos[j] < 16 max_pages, the named
+ * page is valid and not shared with another sequence, and no two rows name
+ * the same (sequence, position).
+ * Arithmetic: y is accumulated in float32 from an exact three-way bfloat16
+ * split of R, so a code can differ from exact arithmetic only when
+ * (y - z) / s lies within about 1e-6 of a rounding boundary.
+ * n_rows == 0 returns OSCAR_OK and launches nothing.
+ * ------------------------------------------------------------------------ */
+oscar_status oscar_quantize_append(const oscar_cache* cache, const void* k_new,
+                                   const void* v_new, int64_t n_rows,
+                                   const int32_t* row_seq, const int32_t* row_pos,
+                                   const int32_t* bt_q, int32_t max_pages,
+                                   const float* r_k, const float* r_v,
+                                   float tau_k, float tau_v, void* stream);
+
+/* Raw BF16 rows into BF16 pages (the sink and recent store of [TS] 2.2.B):
+ * row j, head h goes to slot row_pos[j] % 16 of BF16 page
+ * bt_h[row_seq[j]][row_pos[j] / 16], K token-major and V channel-major.
+ * Same argument conventions and preconditions as oscar_quantize_append. */
+oscar_status oscar_write_bf16(const oscar_cache* cache, const void* k_new,
+                              const void* v_new, int64_t n_rows,
+                              const int32_t* row_seq, const int32_t* row_pos,
+                              const int32_t* bt_h, int32_t max_pages, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Paged decode attention over the mixed cache ([TS] 2.2.B "kernel
+ * integration": unpacking, dequantization, inverse rotation and attention for
+ * the INT2 history in one fused kernel, paged and prefix-cache compatible;
+ * [AB]).  For sequence b, query head i, h = floor(i / G), scale sm_scale:
+ *   logit_j = sm_scale * q_i . k_j                  j in sink or recent (raw)
+ *   logit_j = sm_scale * (q_i . R_K(h)) . kh_j      j in middle, kh_j the
+ *                                                   decoded rotated key
+ *   p = softmax(logit) over j in [0, L_b)
+ *   out_i = sum_{raw j} p_j v_j + (sum_{middle j} p_j vh_j) . R_V(h)^T
+ * Because R is orthogonal this is attention over the decoded cache mapped
+ * back to the original basis (the "inverse rotation").  Output is bf16.
+ * The kernel splits each (sequence, KV head) into chunks of split_pages pages
+ * and merges the chunk results with a log-sum-exp reduction in the same
+ * launch.
+ * q: device bf16 [B][H_q][d].  seq_lens: device int32 [B].  bt_q, bt_h:
+ * device int32 [B][max_pages].  r_k, r_v: device float32 [H_kv][d][d].
+ * max_seq_len: host-known upper bound of seq_lens, <= 16 max_pages (sizes the
+ * grid).  split_pages: pages per chunk, a multiple of 8 in [8, 4096], or 0
+ * for automatic.  workspace: device memory of at least
+ * oscar_decode_workspace_bytes(...) bytes, prepared once with
+ * oscar_decode_workspace_init; every completed call leaves it prepared.
+ * out: device bf16 [B][H_q][d].
+ * Preconditions (device contents): 0 <= seq_lens[b] <= max_seq_len, valid
+ * page ids wherever they are read.  A sequence with seq_lens[b] == 0 gets a
+ * zero output.  Two calls sharing one workspace must not overlap in time.
+ * Arithmetic: the rotated query is rounded to f16 once; probabilities enter
+ * the value products as f16; accumulation is float32.
+ * batch == 0 returns OSCAR_OK and launches nothing.
+ * ------------------------------------------------------------------------ */
+oscar_status oscar_decode_workspace_bytes(int32_t batch, int32_t n_kv_heads,
+                                          int32_t n_q_heads, int32_t d,
+                                          int32_t max_seq_len, int32_t split_pages,
+                                          size_t* bytes);
+oscar_status oscar_decode_workspace_init(void* workspace, size_t workspace_bytes,
+                                         void* stream);
+oscar_status oscar_paged_decode_attn(const oscar_cache* cache, const void* q,
+                                     int32_t batch, int32_t n_q_heads,
+                                     const int32_t* seq_lens, int32_t max_seq_len,
+                                     const int32_t* bt_q, const int32_t* bt_h,
+                                     int32_t max_pages, const float* r_k,
+                                     const float* r_v, float sm_scale,
+                                     int32_t split_pages, void* workspace,
+                                     size_t workspace_bytes, void* out, void* stream);
+
+/* The same decode with every token in BF16 pages (bt_h for all positions,
+ * no rotation): the uncompressed baseline the INT2 cache is compared with
+ * ([TS] 4 and [AB] compare OSCAR's decode against BF16).  Same arguments and
+ * workspace rules minus the INT2 table and rotations; the cache's n_sink and
+ * n_recent are ignored. */
+oscar_status oscar_paged_decode_attn_bf16(const oscar_cache* cache, const void* q,
+                                          int32_t batch, int32_t n_q_heads,
+                                          const int32_t* seq_lens, int32_t max_seq_len,
+                                          const int32_t* bt_h, int32_t max_pages,
+                                          float sm_scale, int32_t split_pages,
+                                          void* workspace, size_t workspace_bytes,
+                                          void* out, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* OSCAR_H_ */

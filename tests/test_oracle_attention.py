@@ -1,0 +1,171 @@
+"""Pins of oracle.attention: exactness of the rotated route (R orthogonal),
+library attention, special cases, the split/merge formula, and a brute-force
+8-token run of the whole pipeline ([TS] 2.2.B; [AB])."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention as att
+from oracle import cache as oc
+from oracle import layout, quant, rotation
+from int2_rotated_kv_oscar_amd import synth
+
+
+def _orth(rng, d):
+    q, r = np.linalg.qr(rng.standard_normal((d, d)))
+    return q * np.sign(np.diag(r))
+
+
+def test_softmax_attention_matches_torch_sdpa():
+    # O12: the textbook definition equals torch's SDPA (float64, CPU)
+    rng = np.random.default_rng(0)
+    q = rng.standard_normal((4, 64)); k = rng.standard_normal((37, 64)); v = rng.standard_normal((37, 64))
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.tensor(q)[None, None], torch.tensor(k)[None, None], torch.tensor(v)[None, None]).numpy()[0, 0]
+    np.testing.assert_allclose(att.softmax_attention(q, k, v, 1 / 8.0), ref, rtol=1e-12, atol=1e-13)
+
+
+@pytest.mark.parametrize("chunks", [1, 2, 7, 64])
+def test_rotated_route_without_quantization_is_exact(chunks):
+    # O11 + O14: with exact (unquantized) rotated rows, the rotated-space route
+    # (q R_K logits, two value sums, LSE merge, R_V^T after the merge) equals
+    # plain attention for any chunking.
+    rng = np.random.default_rng(chunks)
+    d, L, G = 64, 300, 4
+    rk, rv = _orth(rng, d), _orth(rng, d)
+    q = rng.standard_normal((G, d)); k = rng.standard_normal((L, d)) * 3; v = rng.standard_normal((L, d))
+    raw = np.zeros(L, bool); raw[:4] = True; raw[-20:] = True
+    plain = att.softmax_attention(q, k, v, 1 / np.sqrt(d))
+    bounds = np.linspace(0, L, chunks + 1).astype(int)
+    states = []
+    for a, b in zip(bounds[:-1], bounds[1:]):
+        sel = np.zeros(L, bool); sel[a:b] = True
+        states.append(att.partial_state(q, q @ rk, k[sel & raw], v[sel & raw], k[sel & ~raw] @ rk,
+                                        v[sel & ~raw] @ rv, 1 / np.sqrt(d)))
+    np.testing.assert_allclose(att.merge_states(states, rv), plain, rtol=1e-10, atol=1e-12)
+
+
+def test_identity_rotation_is_plain_attention():
+    rng = np.random.default_rng(1)
+    d = 64
+    q = rng.standard_normal((2, d)); k = rng.standard_normal((40, d)); v = rng.standard_normal((40, d))
+    st = att.partial_state(q, q, k[:10], v[:10], k[10:], v[10:], 0.125)
+    np.testing.assert_allclose(att.merge_states([st], np.eye(d)), att.softmax_attention(q, k, v, 0.125), rtol=1e-12)
+
+
+def test_special_cases_single_token_and_equal_logits():
+    # O14: L = 1 gives out = v; q = 0 gives the mean of the (decoded) values.
+    w = synth.Workload("t", 9, 1, 4, 1, 64, 4, 32, 64, ("fixed", 1, 1))
+    rng = np.random.default_rng(2)
+    rk, rv = _orth(rng, 64)[None], _orth(rng, 64)[None]
+    inp = synth.decode_inputs(w, seq_lens=np.array([1]))
+    int2, bf, _, _ = oc.build_from_inputs(inp, rk, rv, 100.0, 100.0)
+    q = synth.bf16_bits_to_f32(inp.q).astype(np.float64)
+    out = att.decode_attention(q, int2, bf, inp.seq_lens, inp.bt_q, inp.bt_h, rk, rv, 4, 32)
+    v0 = layout.bf16_to_f64(inp.v_rows[0, 0])
+    np.testing.assert_allclose(out[0], np.tile(v0, (4, 1)), rtol=0, atol=0)
+    # equal logits
+    w2 = synth.WORKLOADS["tiny"]
+    inp2 = synth.decode_inputs(w2, seq_lens=np.array([100]))
+    int2, bf, res, (ms, mp, mr) = oc.build_from_inputs(inp2, rk, rv, 100.0, 100.0)
+    qz = np.zeros((1, 4, 64))
+    out = att.decode_attention(qz, int2, bf, inp2.seq_lens, inp2.bt_q, inp2.bt_h, rk, rv, 4, 32)
+    raw_idx = np.r_[0:4, 68:100]
+    vals = [layout.bf16_to_f64(inp2.v_rows[inp2.row_of[0][raw_idx], 0])]
+    vals.append(quant.dequantize(res.v[0].codes, res.v[0].s16, res.v[0].z16) @ rv[0].T)
+    np.testing.assert_allclose(out[0, 0], np.concatenate(vals).mean(axis=0), rtol=1e-12, atol=1e-12)
+
+
+def test_short_sequence_is_plain_bf16_attention():
+    # O12: L <= S + W has no middle: the decode is plain attention over bf16 rows
+    w = synth.WORKLOADS["tiny"]
+    inp = synth.decode_inputs(w, seq_lens=np.array([30]))
+    rng = np.random.default_rng(3)
+    rk, rv = _orth(rng, 64)[None], _orth(rng, 64)[None]
+    int2, bf, _, _ = oc.build_from_inputs(inp, rk, rv, 5.0, 5.0)
+    q = synth.bf16_bits_to_f32(inp.q).astype(np.float64)
+    out = att.decode_attention(q, int2, bf, inp.seq_lens, inp.bt_q, inp.bt_h, rk, rv, 4, 32)
+    k = layout.bf16_to_f64(inp.k_rows[inp.row_of[0], 0]); v = layout.bf16_to_f64(inp.v_rows[inp.row_of[0], 0])
+    np.testing.assert_allclose(out[0], att.softmax_attention(q[0], k, v, 0.125), rtol=1e-12, atol=1e-13)
+
+
+def test_direct_and_rotated_routes_agree_on_tiny_workload():
+    w = synth.WORKLOADS["tiny"]
+    cal = synth.calibration_set(w, n_rows=512)
+    rt = rotation.build_rotation(cal.q, cal.k, cal.v, w.group_q)
+    rk = rt["r_k"].astype(np.float32).astype(np.float64)
+    rv = rt["r_v"].astype(np.float32).astype(np.float64)
+    inp = synth.decode_inputs(w)
+    int2, bf, _, _ = oc.build_from_inputs(inp, rk, rv, np.float32(rt["tau_k"]), np.float32(rt["tau_v"]))
+    q = synth.bf16_bits_to_f32(inp.q).astype(np.float64)
+    a = att.decode_attention(q, int2, bf, inp.seq_lens, inp.bt_q, inp.bt_h, rk, rv, w.n_sink, w.n_recent)
+    for ct in (None, 16, 112):
+        b = att.decode_attention_rotated(q, int2, bf, inp.seq_lens, inp.bt_q, inp.bt_h, rk, rv, w.n_sink,
+                                         w.n_recent, chunk_tokens=ct)
+        np.testing.assert_allclose(b, a, rtol=1e-10, atol=1e-12)
+    assert np.isfinite(a).all()
+
+
+def _nearest_code(y, s, z):
+    best, bc = None, 0
+    for c in range(4):
+        e = abs(y - (z + c * s))
+        if best is None or e < best or (e == best and c % 2 == 0):
+            best, bc = e, c
+    return bc
+
+
+def test_brute_force_eight_tokens():
+    # O13: 1 sequence, 1 KV head, G = 4, d = 64, L = 8, S = 2, W = 2 (middle =
+    # tokens 2..5).  Scalar loops for rotation, clip, group statistics, nearest
+    # level, logits, exp/sum and the output rotation, against the oracle.
+    d, G, L, S, W = 64, 4, 8, 2, 2
+    w = synth.Workload("bf8", 8, 1, G, 1, d, S, W, 64, ("fixed", L, L))
+    inp = synth.decode_inputs(w)
+    rng = np.random.default_rng(8)
+    rk = _orth(rng, d).astype(np.float32).astype(np.float64)
+    rv = _orth(rng, d).astype(np.float32).astype(np.float64)
+    tau_k, tau_v = 2.5, 1.75
+    int2, bf, _, _ = oc.build_from_inputs(inp, rk[None], rv[None], tau_k, tau_v)
+    q = synth.bf16_bits_to_f32(inp.q).astype(np.float64)[0]
+    K = layout.bf16_to_f64(inp.k_rows[inp.row_of[0], 0])
+    V = layout.bf16_to_f64(inp.v_rows[inp.row_of[0], 0])
+
+    def encode_decode(x, R, tau):
+        y = [min(max(sum(x[k] * R[k, c] for k in range(d)), -tau), tau) for c in range(d)]
+        out = [0.0] * d
+        for g in range(d // 32):
+            grp = y[32 * g:32 * g + 32]
+            s16 = float(np.float16((max(grp) - min(grp)) / 3))
+            z16 = float(np.float16(min(grp)))
+            for j, yy in enumerate(grp):
+                c = _nearest_code(yy, s16, z16) if s16 != 0 else 0
+                out[32 * g + j] = c * s16 + z16
+        return out
+
+    logits, vals_raw, vals_rot = [], [], []
+    qt = [sum(q[i, k] * rk[k, c] for k in range(d)) for i in range(G) for c in range(d)]
+    qt = np.array(qt).reshape(G, d)
+    for t in range(L):
+        if S <= t < L - W:
+            kh = encode_decode(K[t], rk, tau_k)
+            vh = encode_decode(V[t], rv, tau_v)
+            logits.append([sum(qt[i, c] * kh[c] for c in range(d)) / np.sqrt(d) for i in range(G)])
+            vals_rot.append((t, vh))
+        else:
+            logits.append([sum(q[i, c] * K[t, c] for c in range(d)) / np.sqrt(d) for i in range(G)])
+            vals_raw.append((t, list(V[t])))
+    expect = np.zeros((G, d))
+    for i in range(G):
+        mx = max(l[i] for l in logits)
+        e = [np.exp(l[i] - mx) for l in logits]
+        tot = sum(e)
+        acc_raw = [sum(e[t] * v[c] for t, v in vals_raw) for c in range(d)]
+        acc_rot = [sum(e[t] * v[c] for t, v in vals_rot) for c in range(d)]
+        for c in range(d):
+            expect[i, c] = (acc_raw[c] + sum(acc_rot[k] * rv[c, k] for k in range(d))) / tot
+    out = att.decode_attention(q[None], int2, bf, inp.seq_lens, inp.bt_q, inp.bt_h, rk[None], rv[None], S, W)
+    np.testing.assert_allclose(out[0], expect, rtol=1e-12, atol=1e-12)
+    out2 = att.decode_attention_rotated(q[None], int2, bf, inp.seq_lens, inp.bt_q, inp.bt_h, rk[None], rv[None], S, W,
+                                        chunk_tokens=3)
+    np.testing.assert_allclose(out2[0], expect, rtol=1e-12, atol=1e-12)
