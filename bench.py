@@ -1,0 +1,272 @@
+"""Benchmark of the OSCAR INT2 decode hot path on one MI355X.
+
+One step = quantize-append of the token leaving each sequence's BF16 recent
+window (its INT2 slot re-written) + fused paged INT2 decode attention of one
+query per sequence, over a cache filled once by the same kernels.  The timed
+steps rotate over enough copies of the cache (pools, tables, rotations,
+queries) that the 256 MB Infinity Cache cannot serve them, as consecutive
+layers of a model would.
+
+Prints ONE JSON line (rank 0):
+  value        KV-tokens/s  (sum of context lengths / step time, all KV heads)
+  roofline     decode kernel: algorithmic bytes / its average launch time
+               (HIP events around each launch on the launch stream) vs 8 TB/s
+  cpu_baseline the float64 NumPy oracle decoding the same cache on host cores
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "INT2 paged decode-attn KV-tokens/s + achieved HBM GB/s (% of peak), Qwen3-8B layer"
+
+
+def algorithmic_bytes(inp, w) -> dict:
+    """Unique bytes the decode must move: INT2 middle tokens at 96 B (d=128)
+    per KV head (2 x d/4 B codes + 2 x 2 (d/32) f16 scale/zero x 2 B), BF16
+    sink/recent tokens at 4 d B per KV head, R_K and R_V (f32), q and out
+    (bf16) and the block-table entries read."""
+    from int2_rotated_kv_oscar_amd import synth
+    d, hkv = w.d, w.n_kv_heads
+    per_mid = 2 * (d // 4) + 2 * 2 * (d // 32) * 2
+    mid = raw = pages = 0
+    seen_mid = set()
+    for b, L in enumerate(inp.seq_lens):
+        sink, m, rec = synth.regions(int(L), w.n_sink, w.n_recent)
+        # shared-prefix middle tokens are stored once
+        lo = m[0] if (b == 0 or not w.shared_prefix) else max(m[0], w.shared_prefix)
+        mid += max(0, m[1] - lo)
+        raw += (sink[1] - sink[0]) + (rec[1] - rec[0]) if (b == 0 or not w.shared_prefix) else (rec[1] - rec[0])
+        pages += (int(L) + 15) // 16
+    B = len(inp.seq_lens)
+    parts = {
+        "int2": mid * per_mid * hkv,
+        "bf16": raw * 4 * d * hkv,
+        "rotations": 2 * d * d * 4 * hkv,
+        "q_out": 2 * B * w.n_q_heads * d * 2,
+        "tables": pages * 4,
+    }
+    parts["total"] = sum(parts.values())
+    return parts
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="qwen3-8b-b1-32k")
+    ap.add_argument("--split-pages", type=int, default=0)
+    ap.add_argument("--copies", type=int, default=0, help="cache copies rotated over (0: >= 1 GiB total)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-bf16-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the decode path shards by KV head "
+              f"with no exchange; see DESIGN.md)", file=sys.stderr)
+        return 2
+
+    import torch
+    from int2_rotated_kv_oscar_amd import lib, synth
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    lib.load()
+    dev = "cuda:0"
+    w = synth.WORKLOADS[args.workload]
+    t0 = time.time()
+    inp = synth.decode_inputs(w)
+    log(f"inputs {time.time() - t0:.1f}s  B={len(inp.seq_lens)} max_len={inp.max_seq_len}")
+    t0 = time.time()
+    cal = synth.calibration_set(w)
+    rt = lib.build_rotation(cal.q, cal.k, cal.v, w.group_q)
+    log(f"calibration (oscar_build_rotation, {w.calib_rows} rows) {time.time() - t0:.1f}s")
+    r_k = torch.from_numpy(rt["r_k"].astype(np.float32)).to(dev)
+    r_v = torch.from_numpy(rt["r_v"].astype(np.float32)).to(dev)
+    tau_k, tau_v = float(np.float32(rt["tau_k"])), float(np.float32(rt["tau_v"]))
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    nbq = lib.int2_page_bytes(w.d, w.n_kv_heads)
+    nbh = lib.bf16_page_bytes(w.d, w.n_kv_heads)
+    int2 = torch.zeros(inp.n_int2_pages * nbq, dtype=torch.uint8, device=dev)
+    bf16 = torch.zeros(inp.n_bf16_pages * nbh // 2, dtype=torch.int16, device=dev)
+    cache = lib.make_cache(w.d, w.n_kv_heads, w.n_sink, w.n_recent, int2, bf16)
+    bt_q, bt_h = i32(inp.bt_q), i32(inp.bt_h)
+    ms, mp, mr = synth.middle_rows(inp)
+    lib.quantize_append(cache, bf(inp.k_rows[mr]), bf(inp.v_rows[mr]), i32(ms), i32(mp), bt_q, r_k, r_v, tau_k, tau_v)
+    hs, hp, hr = synth.bf16_rows(inp)
+    lib.write_bf16(cache, bf(inp.k_rows[hr]), bf(inp.v_rows[hr]), i32(hs), i32(hp), bt_h)
+    torch.cuda.synchronize()
+
+    # per step: the row leaving the recent window of every sequence
+    ap_seq, ap_pos, ap_row = [], [], []
+    for b, L in enumerate(inp.seq_lens):
+        t = int(L) - w.n_recent - 1
+        if t >= w.n_sink:
+            ap_seq.append(b); ap_pos.append(t); ap_row.append(inp.row_of[b][t])
+    a_seq, a_pos = i32(ap_seq), i32(ap_pos)
+    a_k, a_v = bf(inp.k_rows[np.array(ap_row)]), bf(inp.v_rows[np.array(ap_row)])
+
+    nbytes = algorithmic_bytes(inp, w)
+    footprint = int2.numel() + bf16.numel() * 2 + r_k.numel() * 8
+    copies = args.copies or max(1, int(np.ceil((1 << 30) / footprint)))
+    pools = [(int2, bf16, r_k, r_v)]
+    for _ in range(copies - 1):
+        pools.append((int2.clone(), bf16.clone(), r_k.clone(), r_v.clone()))
+    caches = [lib.make_cache(w.d, w.n_kv_heads, w.n_sink, w.n_recent, p[0], p[1]) for p in pools]
+    q = bf(inp.q)
+    qs = [q] + [q.clone() for _ in range(copies - 1)]
+    seq_lens = i32(inp.seq_lens)
+    B = len(inp.seq_lens)
+    ws_bytes = lib.decode_workspace_bytes(B, w.n_kv_heads, w.n_q_heads, w.d, inp.max_seq_len, args.split_pages)
+    ws = torch.empty((ws_bytes + 3) // 4, dtype=torch.int32, device=dev)
+    lib.decode_workspace_init(ws)
+    out = torch.empty(B, w.n_q_heads, w.d, dtype=torch.bfloat16, device=dev)
+    log(f"cache footprint {footprint / 1e6:.1f} MB x {copies} copies; workspace {ws_bytes / 1e6:.2f} MB")
+
+    def step(i, ev=None):
+        c = caches[i % copies]
+        pk, _, prk, prv = pools[i % copies]
+        lib.quantize_append(c, a_k, a_v, a_seq, a_pos, bt_q, prk, prv, tau_k, tau_v)
+        if ev is not None:
+            ev[0].record()
+        lib.paged_decode_attn(c, qs[i % copies], seq_lens, inp.max_seq_len, bt_q, bt_h, prk, prv, out, ws,
+                              split_pages=args.split_pages)
+        if ev is not None:
+            ev[1].record()
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for i in range(K):
+        step(i, evs[i])
+    t_end.record()
+    torch.cuda.synchronize()
+    ms_step = t_start.elapsed_time(t_end) / K
+    dec_ms = [a.elapsed_time(b) for a, b in evs]
+    dec_avg = float(np.mean(dec_ms))
+    tokens = int(inp.seq_lens.sum())
+    value = tokens / (ms_step * 1e-3)
+    achieved = nbytes["total"] / (dec_avg * 1e-3) / 1e9
+    log(f"step {ms_step * 1e3:.1f} us, decode kernel avg {dec_avg * 1e3:.1f} us (median {np.median(dec_ms) * 1e3:.1f}),"
+        f" {achieved:.0f} GB/s, bytes {nbytes}")
+
+    result = {
+        "metric": METRIC, "value": round(value, 1), "unit": "KV-tokens/s", "n_gpus": 1, "steps": K,
+        "warmup": args.warmup, "ms_per_step": round(ms_step, 5), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "int2 codes x f16 MFMA, f32 accumulate", "data": "synthetic",
+        "config": {"workload": w.name, "batch": B, "context": inp.max_seq_len, "q_heads": w.n_q_heads,
+                   "kv_heads": w.n_kv_heads, "head_dim": w.d, "page_tokens": 16, "sink": w.n_sink,
+                   "recent": w.n_recent, "split_pages": args.split_pages or "auto", "cache_copies": copies},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "decode_kernel<128,false>", "algorithmic_bytes_per_launch": nbytes["total"],
+                     "avg_launch_us": round(dec_avg * 1e3, 2)},
+    }
+
+    if not args.no_bf16_baseline:
+        # the same decode over an all-BF16 cache (every token in BF16 pages)
+        wb = synth.Workload(**{**w.__dict__, "n_sink": 1 << 30, "n_recent": 0})
+        inb = synth.DecodeInputs(wb, inp.seq_lens, inp.k_rows, inp.v_rows, inp.row_of, inp.q,
+                                 inp.bt_q, *_all_bf16_tables(inp))
+        bt_hb = i32(inb.bt_h)
+        hb_pool = torch.zeros(inb.n_bf16_pages * nbh // 2, dtype=torch.int16, device=dev)
+        cb = lib.make_cache(w.d, w.n_kv_heads, 0, 0, None, hb_pool)
+        hs2, hp2, hr2 = synth.bf16_rows(inb)
+        lib.write_bf16(cb, bf(inp.k_rows[hr2]), bf(inp.v_rows[hr2]), i32(hs2), i32(hp2), bt_hb)
+        ncopy = max(1, int(np.ceil((1 << 30) / (hb_pool.numel() * 2))))
+        hpools = [hb_pool] + [hb_pool.clone() for _ in range(ncopy - 1)]
+        hcaches = [lib.make_cache(w.d, w.n_kv_heads, 0, 0, None, p) for p in hpools]
+        for i in range(args.warmup):
+            lib.paged_decode_attn_bf16(hcaches[i % ncopy], q, seq_lens, inp.max_seq_len, bt_hb, out, ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(K):
+            lib.paged_decode_attn_bf16(hcaches[i % ncopy], q, seq_lens, inp.max_seq_len, bt_hb, out, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        bms = e0.elapsed_time(e1) / K
+        bbytes = tokens * 4 * w.d * w.n_kv_heads + 2 * B * w.n_q_heads * w.d * 2
+        result["bf16_baseline"] = {"kernel": "decode_kernel<128,true>", "us_per_call": round(bms * 1e3, 2),
+                                   "KV_tokens_per_s": round(tokens / (bms * 1e-3), 1),
+                                   "achieved_GBps": round(bbytes / (bms * 1e-3) / 1e9, 1),
+                                   "int2_decode_speedup": round(bms / dec_avg, 3)}
+        log(f"bf16 baseline {bms * 1e3:.1f} us/call")
+        del hpools, hcaches
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = _cpu_baseline(inp, w, cache, int2, bf16, rt, tokens, log)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def _all_bf16_tables(inp):
+    B, mp = inp.bt_h.shape
+    bt = np.full((B, mp), -1, np.int32)
+    n = 0
+    for b, L in enumerate(inp.seq_lens):
+        k = (int(L) + 15) // 16
+        bt[b, :k] = np.arange(n, n + k)
+        n += k
+    return bt, inp.n_int2_pages, max(n, 1), mp
+
+
+def _cpu_baseline(inp, w, cache, int2, bf16, rt, tokens, log) -> dict:
+    """The oracle (float64 NumPy) decoding the same cache, on the host cores."""
+    import torch
+    from oracle import attention as oatt
+    from oracle import layout as olayout
+    from int2_rotated_kv_oscar_amd import synth
+    cores = len(os.sched_getaffinity(0))
+    pool_q = olayout.Int2Pool(inp.n_int2_pages, w.n_kv_heads, w.d, int2.cpu().numpy())
+    pool_h = olayout.Bf16Pool(inp.n_bf16_pages, w.n_kv_heads, w.d, bf16.cpu().numpy().view(np.uint16))
+    q = synth.bf16_bits_to_f32(inp.q).astype(np.float64)
+    rk = rt["r_k"].astype(np.float32).astype(np.float64)
+    rv = rt["r_v"].astype(np.float32).astype(np.float64)
+    # bounded sample: as many KV heads of the full-length batch as fit ~10 s
+    heads = []
+    t0 = time.time()
+    for h in range(w.n_kv_heads):
+        one_q = olayout.Int2Pool(inp.n_int2_pages, 1, w.d, pool_q.data[:, h:h + 1])
+        one_h = olayout.Bf16Pool(inp.n_bf16_pages, 1, w.d, pool_h.data[:, h:h + 1])
+        G = w.group_q
+        oatt.decode_attention(q[:, h * G:(h + 1) * G], one_q, one_h, inp.seq_lens, inp.bt_q, inp.bt_h,
+                              rk[h:h + 1], rv[h:h + 1], w.n_sink, w.n_recent)
+        heads.append(h)
+        if time.time() - t0 > 10.0:
+            break
+    dt = time.time() - t0
+    per_layer = dt * w.n_kv_heads / len(heads)
+    log(f"cpu oracle: {len(heads)} KV heads in {dt:.1f}s on {cores} cores")
+    return {"value": round(tokens / per_layer, 1), "unit": "KV-tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"oracle float64 decode of {len(heads)}/{w.n_kv_heads} KV heads of the same cache "
+                      f"({tokens} tokens), time scaled to all heads; numpy BLAS threads = {cores}"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

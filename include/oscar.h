@@ -96,7 +96,7 @@ int32_t oscar_version(void);
  *   - Quantile: the M values |y| sorted ascending a[0..M-1]; rr = q (M - 1);
  *     tau = a[floor(rr)] + (rr - floor(rr)) (a[floor(rr)+1] - a[floor(rr)]).
  * Eigen-decomposition is a cyclic Jacobi iteration in float64 that stops
- * when every off-diagonal entry is below 1e-15 * ||C||_F, after at most
+ * when every off-diagonal entry is at most 1e-14 * ||C||_F, after at most
  * max_sweeps sweeps (0 selects 64); not reaching that returns
  * OSCAR_ERR_NUMERIC.
  * n_threads: host worker threads for the calibration attention (0 = all).

@@ -1,0 +1,274 @@
+// liboscar C ABI: argument validation, workspace planning and launches.  The
+// semantics of every entry point are specified in include/oscar.h.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+
+#include "common.h"
+#include "kernels.h"
+
+namespace oscar {
+
+static thread_local char g_err[512] = "";
+
+void set_error(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_err, sizeof(g_err), fmt, ap);
+  va_end(ap);
+}
+void clear_error() { g_err[0] = '\0'; }
+
+}  // namespace oscar
+
+using oscar::fail;
+
+namespace {
+
+bool supported_d(int32_t d) { return d == 64 || d == 128; }
+
+oscar_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return OSCAR_OK;
+  oscar::set_error("OSCAR_ERR_HIP: %s: %s", what, hipGetErrorString(e));
+  return OSCAR_ERR_HIP;
+}
+
+oscar_status check_cache(const oscar_cache* c, bool need_int2, bool need_bf16) {
+  if (!c) return fail(OSCAR_ERR_INVALID_ARG, "cache is NULL");
+  if (!supported_d(c->d)) return fail(OSCAR_ERR_UNSUPPORTED, "cache d must be 64 or 128");
+  if (c->n_kv_heads < 1) return fail(OSCAR_ERR_INVALID_ARG, "cache n_kv_heads < 1");
+  if (c->n_sink < 0 || c->n_recent < 0) return fail(OSCAR_ERR_INVALID_ARG, "negative n_sink or n_recent");
+  if (need_int2 && (!c->int2_pool || c->n_int2_pages < 1)) return fail(OSCAR_ERR_INVALID_ARG, "INT2 pool missing");
+  if (need_bf16 && (!c->bf16_pool || c->n_bf16_pages < 1)) return fail(OSCAR_ERR_INVALID_ARG, "BF16 pool missing");
+  return OSCAR_OK;
+}
+
+// Chunk planning shared by the workspace query and the decode calls.
+struct DecodePlan {
+  int split_pages;
+  int n_chunks;     // grid x: chunks per (sequence, KV head)
+  int rec_floats;
+  size_t counter_bytes;
+  size_t bytes;
+};
+
+constexpr int kRawChunkPages = 16;  // pages per BF16 chunk (matches the decode kernel)
+
+int device_cu_count() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (!cached[dev]) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Pages per INT2 chunk: enough workgroups to fill the compute units in whole
+// rounds (one 8-wave workgroup per CU at a time), at most ~128 pages of work
+// per workgroup and round, and at most decode_max_splits() / 2 chunks.
+int auto_split_pages(int batch, int n_kv, int max_pages) {
+  const long long cus = device_cu_count();
+  const long long pages = (long long)batch * n_kv * std::max(1, max_pages);
+  const long long raw_wgs = 2LL * batch * n_kv;
+  const long long rounds = std::max(1LL, (pages + cus * 128 - 1) / (cus * 128));
+  const long long wgs = std::max(cus / 2, rounds * cus - raw_wgs);
+  long long sp = (pages + wgs - 1) / wgs;
+  const int cap = oscar_launch::decode_max_splits() / 2;
+  sp = std::max<long long>(sp, (max_pages + cap - 1) / cap);
+  sp = (sp + 7) / 8 * 8;
+  return int(std::min<long long>(4096, std::max<long long>(16, sp)));
+}
+
+// exact == false: a bound valid for every n_sink / n_recent (workspace query)
+oscar_status plan_decode(int32_t batch, int32_t n_kv, int32_t n_q, int32_t d, int32_t max_seq_len,
+                         int32_t split_pages, bool exact, bool all_raw, int32_t S, int32_t W, DecodePlan* plan) {
+  if (batch < 0 || max_seq_len < 0) return fail(OSCAR_ERR_INVALID_ARG, "negative batch or max_seq_len");
+  if (!supported_d(d)) return fail(OSCAR_ERR_UNSUPPORTED, "d must be 64 or 128");
+  if (n_kv < 1 || n_q < 1 || n_q % n_kv) return fail(OSCAR_ERR_INVALID_ARG, "n_q_heads must be a positive multiple of n_kv_heads");
+  const int G = n_q / n_kv;
+  if (G > 16) return fail(OSCAR_ERR_UNSUPPORTED, "query group size above 16");
+  if (split_pages != 0 && (split_pages < 8 || split_pages > 4096 || split_pages % 8))
+    return fail(OSCAR_ERR_INVALID_ARG, "split_pages must be 0 or a multiple of 8 in [8, 4096]");
+  const int max_pages = (max_seq_len + 15) / 16;
+  plan->split_pages = split_pages ? split_pages : auto_split_pages(batch, n_kv, max_pages);
+  const int n_int2 = (max_pages + plan->split_pages - 1) / plan->split_pages;
+  if (exact) {
+    plan->n_chunks = oscar_launch::decode_chunks_max(all_raw, max_seq_len, S, W, plan->split_pages);
+    if (plan->n_chunks > oscar_launch::decode_max_splits())
+      return fail(OSCAR_ERR_UNSUPPORTED, "more than 256 chunks per sequence; use a larger split_pages");
+  } else {
+    plan->n_chunks = std::max(1, n_int2 + (max_pages + kRawChunkPages - 1) / kRawChunkPages + 1);
+  }
+  plan->rec_floats = (2 * G + G * d + 1 + 3) / 4 * 4;
+  plan->counter_bytes = (size_t(batch) * n_kv * 4 + 255) / 256 * 256;
+  plan->bytes = plan->counter_bytes + size_t(batch) * n_kv * plan->n_chunks * plan->rec_floats * 4;
+  return OSCAR_OK;
+}
+
+__global__ void fill_zero_kernel(uint32_t* p, size_t n_words) {
+  for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n_words; i += size_t(gridDim.x) * blockDim.x)
+    p[i] = 0u;
+}
+
+// BF16 rows into BF16 pages: K token-major [16][d], V channel-major [d][16].
+__global__ void write_bf16_kernel(const uint16_t* __restrict__ k_new, const uint16_t* __restrict__ v_new,
+                                  const int32_t* __restrict__ row_seq, const int32_t* __restrict__ row_pos,
+                                  const int32_t* __restrict__ bt_h, int32_t max_pages, uint16_t* __restrict__ pool,
+                                  int32_t n_kv, int32_t d) {
+  const int64_t row = blockIdx.x;
+  const int h = blockIdx.y;
+  const int c = threadIdx.x;
+  const int32_t pos = row_pos[row];
+  const int64_t page = bt_h[int64_t(row_seq[row]) * max_pages + (pos >> 4)];
+  const int slot = pos & 15;
+  uint16_t* base = pool + (page * n_kv + h) * int64_t(32) * d;
+  const int64_t src = (row * n_kv + h) * d + c;
+  base[slot * d + c] = k_new[src];
+  base[16 * d + c * 16 + slot] = v_new[src];
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* oscar_status_string(oscar_status s) {
+  switch (s) {
+    case OSCAR_OK: return "OSCAR_OK";
+    case OSCAR_ERR_INVALID_ARG: return "OSCAR_ERR_INVALID_ARG";
+    case OSCAR_ERR_UNSUPPORTED: return "OSCAR_ERR_UNSUPPORTED";
+    case OSCAR_ERR_NUMERIC: return "OSCAR_ERR_NUMERIC";
+    case OSCAR_ERR_WORKSPACE: return "OSCAR_ERR_WORKSPACE";
+    case OSCAR_ERR_HIP: return "OSCAR_ERR_HIP";
+  }
+  return "OSCAR_ERR_UNKNOWN";
+}
+
+const char* oscar_last_error(void) { return oscar::g_err; }
+
+int32_t oscar_version(void) { return OSCAR_VERSION; }
+
+size_t oscar_int2_page_bytes(int32_t d, int32_t n_kv_heads) {
+  if (!supported_d(d) || n_kv_heads < 1) return 0;
+  return size_t(12) * d * n_kv_heads;
+}
+
+size_t oscar_bf16_page_bytes(int32_t d, int32_t n_kv_heads) {
+  if (!supported_d(d) || n_kv_heads < 1) return 0;
+  return size_t(64) * d * n_kv_heads;
+}
+
+oscar_status oscar_quantize_append(const oscar_cache* cache, const void* k_new, const void* v_new, int64_t n_rows,
+                                   const int32_t* row_seq, const int32_t* row_pos, const int32_t* bt_q,
+                                   int32_t max_pages, const float* r_k, const float* r_v, float tau_k, float tau_v,
+                                   void* stream) {
+  oscar::clear_error();
+  if (oscar_status s = check_cache(cache, true, false)) return s;
+  if (n_rows < 0) return fail(OSCAR_ERR_INVALID_ARG, "n_rows < 0");
+  if (n_rows == 0) return OSCAR_OK;
+  if (!k_new || !v_new || !row_seq || !row_pos || !bt_q || !r_k || !r_v)
+    return fail(OSCAR_ERR_INVALID_ARG, "null device pointer");
+  if (max_pages < 1) return fail(OSCAR_ERR_INVALID_ARG, "max_pages < 1");
+  if (!(tau_k > 0.f) || !(tau_v > 0.f) || !std::isfinite(tau_k) || !std::isfinite(tau_v))
+    return fail(OSCAR_ERR_INVALID_ARG, "clip thresholds must be finite and positive");
+  if ((n_rows + 15) / 16 > int64_t(0x7FFFFFFF)) return fail(OSCAR_ERR_UNSUPPORTED, "n_rows too large");
+  return hip_status(oscar_launch::quantize_append(cache->d, cache->n_kv_heads, cache->int2_pool, k_new, v_new, n_rows,
+                                                  row_seq, row_pos, bt_q, max_pages, r_k, r_v, tau_k, tau_v,
+                                                  static_cast<hipStream_t>(stream)),
+                    "quantize_append launch");
+}
+
+oscar_status oscar_write_bf16(const oscar_cache* cache, const void* k_new, const void* v_new, int64_t n_rows,
+                              const int32_t* row_seq, const int32_t* row_pos, const int32_t* bt_h, int32_t max_pages,
+                              void* stream) {
+  oscar::clear_error();
+  if (oscar_status s = check_cache(cache, false, true)) return s;
+  if (n_rows < 0) return fail(OSCAR_ERR_INVALID_ARG, "n_rows < 0");
+  if (n_rows == 0) return OSCAR_OK;
+  if (!k_new || !v_new || !row_seq || !row_pos || !bt_h) return fail(OSCAR_ERR_INVALID_ARG, "null device pointer");
+  if (max_pages < 1) return fail(OSCAR_ERR_INVALID_ARG, "max_pages < 1");
+  if (n_rows > int64_t(0x7FFFFFFF)) return fail(OSCAR_ERR_UNSUPPORTED, "n_rows too large");
+  hipLaunchKernelGGL(write_bf16_kernel, dim3(unsigned(n_rows), unsigned(cache->n_kv_heads)), dim3(cache->d), 0,
+                     static_cast<hipStream_t>(stream), static_cast<const uint16_t*>(k_new),
+                     static_cast<const uint16_t*>(v_new), row_seq, row_pos, bt_h, max_pages,
+                     static_cast<uint16_t*>(cache->bf16_pool), cache->n_kv_heads, cache->d);
+  return hip_status(hipGetLastError(), "write_bf16 launch");
+}
+
+oscar_status oscar_decode_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads, int32_t d,
+                                          int32_t max_seq_len, int32_t split_pages, size_t* bytes) {
+  oscar::clear_error();
+  if (!bytes) return fail(OSCAR_ERR_INVALID_ARG, "bytes is NULL");
+  DecodePlan plan;
+  if (oscar_status s = plan_decode(batch, n_kv_heads, n_q_heads, d, max_seq_len, split_pages, false, false, 0, 0, &plan))
+    return s;
+  *bytes = plan.bytes;
+  return OSCAR_OK;
+}
+
+oscar_status oscar_decode_workspace_init(void* workspace, size_t workspace_bytes, void* stream) {
+  oscar::clear_error();
+  if (!workspace) return fail(OSCAR_ERR_WORKSPACE, "workspace is NULL");
+  if (workspace_bytes % 4) return fail(OSCAR_ERR_INVALID_ARG, "workspace_bytes not a multiple of 4");
+  if (workspace_bytes == 0) return OSCAR_OK;
+  const size_t words = workspace_bytes / 4;
+  const unsigned blocks = unsigned(std::min<size_t>(4096, (words + 255) / 256));
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
+                     static_cast<uint32_t*>(workspace), words);
+  return hip_status(hipGetLastError(), "workspace init launch");
+}
+
+static oscar_status decode_common(bool all_raw, const oscar_cache* cache, const void* q, int32_t batch,
+                                  int32_t n_q_heads, const int32_t* seq_lens, int32_t max_seq_len,
+                                  const int32_t* bt_q, const int32_t* bt_h, int32_t max_pages, const float* r_k,
+                                  const float* r_v, float sm_scale, int32_t split_pages, void* workspace,
+                                  size_t workspace_bytes, void* out, void* stream) {
+  oscar::clear_error();
+  if (oscar_status s = check_cache(cache, !all_raw, true)) return s;
+  DecodePlan plan;
+  if (oscar_status s = plan_decode(batch, cache->n_kv_heads, n_q_heads, cache->d, max_seq_len, split_pages, true,
+                                   all_raw, cache->n_sink, cache->n_recent, &plan))
+    return s;
+  if (batch == 0) return OSCAR_OK;
+  if (!q || !seq_lens || !bt_h || !out || (!all_raw && (!bt_q || !r_k || !r_v)))
+    return fail(OSCAR_ERR_INVALID_ARG, "null device pointer");
+  if (max_pages < 1 || int64_t(max_seq_len) > int64_t(max_pages) * 16)
+    return fail(OSCAR_ERR_INVALID_ARG, "max_seq_len exceeds 16 * max_pages");
+  if (!(std::isfinite(sm_scale) && sm_scale > 0.f)) return fail(OSCAR_ERR_INVALID_ARG, "sm_scale must be finite and positive");
+  if (!workspace) return fail(OSCAR_ERR_WORKSPACE, "workspace is NULL");
+  if (workspace_bytes < plan.bytes) return fail(OSCAR_ERR_WORKSPACE, "workspace smaller than oscar_decode_workspace_bytes");
+  if (batch > 65535) return fail(OSCAR_ERR_UNSUPPORTED, "batch above 65535");
+  const int G = n_q_heads / cache->n_kv_heads;
+  int32_t* counters = static_cast<int32_t*>(workspace);
+  float* partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.counter_bytes);
+  return hip_status(
+      oscar_launch::paged_decode(cache->d, all_raw, cache->int2_pool, cache->bf16_pool, cache->n_kv_heads, G,
+                                 cache->n_sink, cache->n_recent, n_q_heads, q, batch, seq_lens, all_raw ? bt_h : bt_q,
+                                 bt_h, max_pages, r_k, r_v, sm_scale, plan.split_pages, plan.n_chunks, partials,
+                                 counters, plan.rec_floats, out, static_cast<hipStream_t>(stream)),
+      "decode launch");
+}
+
+oscar_status oscar_paged_decode_attn(const oscar_cache* cache, const void* q, int32_t batch, int32_t n_q_heads,
+                                     const int32_t* seq_lens, int32_t max_seq_len, const int32_t* bt_q,
+                                     const int32_t* bt_h, int32_t max_pages, const float* r_k, const float* r_v,
+                                     float sm_scale, int32_t split_pages, void* workspace, size_t workspace_bytes,
+                                     void* out, void* stream) {
+  return decode_common(false, cache, q, batch, n_q_heads, seq_lens, max_seq_len, bt_q, bt_h, max_pages, r_k, r_v,
+                       sm_scale, split_pages, workspace, workspace_bytes, out, stream);
+}
+
+oscar_status oscar_paged_decode_attn_bf16(const oscar_cache* cache, const void* q, int32_t batch, int32_t n_q_heads,
+                                          const int32_t* seq_lens, int32_t max_seq_len, const int32_t* bt_h,
+                                          int32_t max_pages, float sm_scale, int32_t split_pages, void* workspace,
+                                          size_t workspace_bytes, void* out, void* stream) {
+  return decode_common(true, cache, q, batch, n_q_heads, seq_lens, max_seq_len, nullptr, bt_h, max_pages, nullptr,
+                       nullptr, sm_scale, split_pages, workspace, workspace_bytes, out, stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,725 @@
+// Kernel B — fused paged decode attention over the mixed cache ([TS] 2.2.B
+// "kernel integration": unpacking, dequantization, inverse rotation and
+// attention for the INT2 history in one kernel, paged and prefix-cache
+// compatible; [AB]).  Also the all-BF16 baseline the INT2 cache is compared
+// with ([TS] 4).
+//
+// Work split.  Grid (chunk, KV head, sequence).  The pages of a sequence are
+// cut into chunks of one kind: INT2 chunks (split_pages pages of the middle
+// history) and BF16 chunks (the sink and recent pages).  A workgroup of 8
+// waves takes one chunk of one (sequence, KV head); each wave takes page
+// pairs.  The G query heads of the group are the 16 columns of every MFMA
+// tile.  INT2 page pairs stream through registers with whole-wave coalesced
+// loads four pairs ahead of the compute, and are re-read per lane from a
+// private LDS slot in the layout the MFMA operands need.
+//
+// INT2 tokens are never dequantized.  A 2-bit code c masked in place inside a
+// 16-bit half is the f16 subnormal c * 4^p * 2^-24 (p = its 2-bit position),
+// exact, and the MFMA multiplies it exactly.  The group affine map is
+// factored out of the dot products:
+//   q~ . (c s + z) = s (q~ . c) + z sum(q~)                          (keys)
+//   sum_t p_t (c_t s_t + z_t) = sum_t (p_t s_t) c_t + sum_t p_t z_t   (values)
+// so scales multiply either the 16x16 logit tile or the f16 probabilities,
+// and the zero terms are one extra small MFMA each.  The position factors
+// 4^p are folded into the query (keys) or applied once at the end (values).
+// Logits are kept in log2 units (q~ pre-scaled by sm_scale * log2 e).
+//
+// Each chunk's result (max, sum, value sum in the rotated or the raw basis)
+// goes to the workspace with device-coherent stores; the last workgroup of a
+// (sequence, KV head) merges them by log-sum-exp and applies the output
+// rotation R_V^T on the MFMA.
+#include <algorithm>
+
+#include "device_utils.h"
+#include "layout.h"
+#include "kernels.h"
+
+using namespace oscar_dev;
+
+namespace {
+
+struct DecParams {
+  const uint8_t* int2_pool;
+  const uint16_t* bf16_pool;
+  int32_t n_kv, G, S, W, Hq;
+  const uint16_t* q;
+  const int32_t* seq_lens;
+  const int32_t* bt_q;
+  const int32_t* bt_h;
+  int32_t max_pages;
+  const float* r_k;
+  const float* r_v;
+  float sm_scale;
+  int32_t split_pages;
+  float* partials;
+  int32_t* counters;
+  int32_t rec_floats;
+  int32_t n_chunks_max;
+  uint16_t* out;
+};
+
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRawChunk = 16;     // pages per BF16 chunk of the mixed cache
+constexpr int kMaxChunks = 256;   // chunks per (sequence, KV head)
+constexpr int kMergeBatch = 32;   // chunk records loaded per merge round
+static_assert(kMergeBatch * 16 == kThreads, "one thread stages one (record, query row) of a merge batch");
+constexpr float kTwo24 = 16777216.0f;
+constexpr float kNegInf = -__builtin_inff();
+
+__device__ __forceinline__ bool overlaps(int a0, int a1, int b0, int b1) { return max(a0, b0) < min(a1, b1); }
+
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v) {
+  return pack_f16x2(bf16_to_f32(v & 0xFFFFu), bf16_to_f32(v >> 16));
+}
+
+// device-coherent (write-through / L2-bypassing) 32-bit accesses for the
+// chunk records exchanged between workgroups on different XCDs
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Keep-mask of an f16/bf16 pair for tokens (t, t+1): stale bytes in slots
+// outside the region must not reach the value sums (0 * NaN is NaN).
+__device__ __forceinline__ uint32_t pair_keep(bool k0, bool k1) {
+  return (k0 ? 0x0000FFFFu : 0u) | (k1 ? 0xFFFF0000u : 0u);
+}
+
+// Chunk plan of one sequence: BF16 page ranges A and B (sink, recent; one
+// range when they meet), the INT2 page range, and their chunk counts.
+struct SeqPlan {
+  int L, n_pages, s1, m0, m1, r0;
+  int ra0, ra1, rb0, rb1, q0, q1;
+  int n_ra, n_rb, n_q, n_chunks, raw_chunk;
+};
+
+template <bool ALL_RAW>
+__device__ __forceinline__ SeqPlan make_plan(const DecParams& p, int L) {
+  SeqPlan sp;
+  sp.L = L;
+  sp.n_pages = (L + 15) >> 4;
+  sp.s1 = ALL_RAW ? L : min(p.S, L);
+  sp.m0 = p.S;
+  sp.m1 = ALL_RAW ? 0 : L - p.W;
+  sp.r0 = ALL_RAW ? L : max(p.S, L - p.W);
+  if (ALL_RAW) {
+    sp.ra0 = 0; sp.ra1 = sp.n_pages; sp.rb0 = sp.rb1 = 0; sp.q0 = sp.q1 = 0;
+    sp.raw_chunk = p.split_pages;
+  } else {
+    const int hs1 = (sp.s1 + 15) >> 4;                       // pages holding sink tokens
+    const int hr0 = sp.r0 < L ? (sp.r0 >> 4) : sp.n_pages;   // first page holding a recent token
+    if (hs1 >= hr0) {
+      sp.ra0 = 0; sp.ra1 = sp.n_pages; sp.rb0 = sp.rb1 = 0;
+    } else {
+      sp.ra0 = 0; sp.ra1 = hs1; sp.rb0 = hr0; sp.rb1 = sp.n_pages;
+    }
+    if (sp.m1 > sp.m0) { sp.q0 = sp.m0 >> 4; sp.q1 = (sp.m1 + 15) >> 4; }
+    else { sp.q0 = sp.q1 = 0; }
+    sp.raw_chunk = kRawChunk;
+  }
+  sp.n_ra = (sp.ra1 - sp.ra0 + sp.raw_chunk - 1) / sp.raw_chunk;
+  sp.n_rb = (sp.rb1 - sp.rb0 + sp.raw_chunk - 1) / sp.raw_chunk;
+  sp.n_q = (sp.q1 - sp.q0 + p.split_pages - 1) / p.split_pages;
+  sp.n_chunks = sp.n_ra + sp.n_rb + sp.n_q;
+  return sp;
+}
+
+// Operands one lane needs from one INT2 page-head image (global or LDS).
+template <int D>
+struct PageOps {
+  static constexpr int NG = D / 32, NW = D / 64;
+  uint32_t kc[NW];      // KC words: token l16, K-slots of this quad
+  uint32_t ks[2 * NG];  // K scales of tokens 4quad..4quad+3, all groups ([slot][g] f16)
+  uint32_t kz[2];       // K zeros of token l16 (quads 0, 1 only)
+  uint32_t vc[NW];      // VC words: channel l16 of each block, tokens of this quad
+  uint32_t vs[2 * NG];  // V scales [quad][g][4 tokens]
+  uint32_t vz[2];       // V zeros of group l16, tokens 4quad..4quad+3 (l16 < NG only)
+
+  __device__ __forceinline__ void read(const uint8_t* base, int l16, int quad) {
+    using GG = Geo<D>;
+    const uint32_t* kcp = reinterpret_cast<const uint32_t*>(base + GG::KC) + (quad * 16 + l16) * NW;
+    const uint32_t* vcp = reinterpret_cast<const uint32_t*>(base + GG::VC) + (quad * 16 + l16) * NW;
+    const uint32_t* ksp = reinterpret_cast<const uint32_t*>(base + GG::KS) + quad * 2 * NG;
+    const uint32_t* vsp = reinterpret_cast<const uint32_t*>(base + GG::VS) + quad * 2 * NG;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) { kc[i] = kcp[i]; vc[i] = vcp[i]; }
+#pragma unroll
+    for (int i = 0; i < 2 * NG; ++i) { ks[i] = ksp[i]; vs[i] = vsp[i]; }
+    kz[0] = kz[1] = vz[0] = vz[1] = 0;
+    if (quad < 2) {
+      const uint32_t* kzp = reinterpret_cast<const uint32_t*>(base + GG::KZ) + l16 * (NG / 2);
+      kz[0] = kzp[0];
+      if (NG == 4) kz[1] = kzp[1];
+    }
+    if (l16 < NG) {
+      const uint32_t* vzp = reinterpret_cast<const uint32_t*>(base + GG::VZ) + (quad * NG + l16) * 2;
+      vz[0] = vzp[0];
+      vz[1] = vzp[1];
+    }
+  }
+};
+
+// A page pair in flight: whole-wave coalesced loads of two page-head images
+// (lane l holds bytes [16l, 16l+16) and, for d = 128, [1024 + 8l, 1024 + 8l + 8)).
+template <int D>
+struct PairStage {
+  static constexpr int HB = Geo<D>::HEAD_BYTES;  // 1536 or 768
+  u32x4 a[2];
+  u32x2 b[2];
+  __device__ __forceinline__ void load(const uint8_t* pa, const uint8_t* pb, int lane) {
+    const uint8_t* src[2] = {pa, pb};
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (HB == 1536) {
+        a[j] = *reinterpret_cast<const u32x4*>(src[j] + 16 * lane);
+        b[j] = *reinterpret_cast<const u32x2*>(src[j] + 1024 + 8 * lane);
+      } else {  // 768 B: 48 lanes x 16 B
+        a[j] = lane < 48 ? *reinterpret_cast<const u32x4*>(src[j] + 16 * lane) : u32x4{0, 0, 0, 0};
+      }
+    }
+  }
+  __device__ __forceinline__ void store(uint8_t* slot, int lane) const {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (HB == 1536) {
+        *reinterpret_cast<u32x4*>(slot + j * HB + 16 * lane) = a[j];
+        *reinterpret_cast<u32x2*>(slot + j * HB + 1024 + 8 * lane) = b[j];
+      } else if (lane < 48) {
+        *reinterpret_cast<u32x4*>(slot + j * HB + 16 * lane) = a[j];
+      }
+    }
+  }
+};
+
+template <int D, bool ALL_RAW>
+__global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
+  using GG = Geo<D>;
+  constexpr int NG = GG::NG, NCB = GG::NCB, NKB = GG::NKB, HB = GG::HEAD_BYTES;
+  extern __shared__ __attribute__((aligned(16))) float smem[];
+  const int G = p.G;
+  // LDS: q-hat B operands [NG][64][4] u32 | zero-term operand [64][4] u32 |
+  // misc 512 floats | page slots [8 waves][2][2 pages][HB] | results/merge
+  uint32_t* s_qhat = reinterpret_cast<uint32_t*>(smem);
+  uint32_t* s_qz = s_qhat + NG * 256;
+  float* s_misc = reinterpret_cast<float*>(s_qz + 256);
+  float* s_m = s_misc;             // [8][16] per-wave max
+  float* s_l = s_misc + 128;       // [8][16] per-wave sum
+  int* s_flag = reinterpret_cast<int*>(s_misc + 256);  // [16]
+  uint8_t* s_slots = reinterpret_cast<uint8_t*>(s_misc + 512);
+  float* s_res = reinterpret_cast<float*>(s_slots + (ALL_RAW ? 0 : kWaves * 2 * 2 * HB));
+  // s_res: per-wave results [8][G][D]; in the last workgroup: merged [G][D] rot
+  // and [G][D] raw
+
+  const int x = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, quad = lane >> 4;
+  const int L = p.seq_lens[b];
+  const int hq0 = h * G;
+  if (L <= 0) {
+    if (x == 0)
+      for (int e = tid; e < G * D; e += kThreads) p.out[(size_t(b) * p.Hq + hq0) * D + e] = 0;
+    return;
+  }
+  const SeqPlan sp = make_plan<ALL_RAW>(p, L);
+  if (x >= sp.n_chunks) return;
+  const float qscale = p.sm_scale * kLog2e;
+  const uint16_t* qb = p.q + (size_t(b) * p.Hq + hq0) * D;
+  const int32_t* btq = p.bt_q + size_t(b) * p.max_pages;
+  const int32_t* bth = p.bt_h + size_t(b) * p.max_pages;
+  const bool is_raw = x < sp.n_ra + sp.n_rb;
+  int c0, c1;
+  if (x < sp.n_ra) { c0 = sp.ra0 + x * sp.raw_chunk; c1 = min(sp.ra1, c0 + sp.raw_chunk); }
+  else if (is_raw) { c0 = sp.rb0 + (x - sp.n_ra) * sp.raw_chunk; c1 = min(sp.rb1, c0 + sp.raw_chunk); }
+  else { c0 = sp.q0 + (x - sp.n_ra - sp.n_rb) * p.split_pages; c1 = min(sp.q1, c0 + p.split_pages); }
+  const int n_pairs = (c1 - c0 + 1) >> 1;
+  const int m0 = sp.m0, m1 = sp.m1, s1 = sp.s1, r0 = sp.r0;
+
+  float m_run = kNegInf, l_part = 0.f;
+  f32x4 acc[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc_z = {0.f, 0.f, 0.f, 0.f};
+
+  // online-softmax step shared by both chunk kinds: logits lg (log2 units,
+  // -inf = masked) -> probabilities pv, accumulators rescaled as needed
+  auto softmax_step = [&](float (&lg)[2][4], float (&pv)[2][4]) {
+    float mx = fmaxf(fmaxf(fmaxf(lg[0][0], lg[0][1]), fmaxf(lg[0][2], lg[0][3])),
+                     fmaxf(fmaxf(lg[1][0], lg[1][1]), fmaxf(lg[1][2], lg[1][3])));
+    mx = wave_max16(mx);
+    const float m_new = fmaxf(m_run, mx);
+    if (__any(m_new > m_run)) {
+      const float f = (m_run == kNegInf) ? 0.f : exp2f(m_run - m_new);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) acc[cb] *= f;
+      acc_z *= f;
+      l_part *= f;
+      m_run = m_new;
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pv[j][r] = (lg[j][r] == kNegInf) ? 0.f : exp2f(lg[j][r] - m_run);
+        l_part += pv[j][r];
+      }
+  };
+
+  if (is_raw) {
+    // ---------------- BF16 chunk: raw q . k, raw-basis value sums ----------------
+    u32x4 bqr[NKB];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      bqr[kb] = u32x4{0, 0, 0, 0};
+      if (l16 < G) bqr[kb] = *reinterpret_cast<const u32x4*>(qb + size_t(l16) * D + 32 * kb + 8 * quad);
+    }
+    for (int pr = wave; pr < n_pairs; pr += kWaves) {
+      const int pg0 = c0 + 2 * pr;
+      float lg[2][4];
+      uint32_t vraw[2][NCB][2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int pg = pg0 + j;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lg[j][r] = kNegInf;
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) vraw[j][cb][0] = vraw[j][cb][1] = 0;
+        if (pg >= c1) continue;
+        const uint16_t* hbase = p.bf16_pool + (size_t(bth[pg]) * p.n_kv + h) * GG::BF16_HEAD_ELEMS;
+        f32x4 d = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb)
+          d = mfma_bf16(*reinterpret_cast<const u32x4*>(hbase + l16 * D + 32 * kb + 8 * quad), bqr[kb], d);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {  // V^T rows: channel 16cb + l16, tokens 4quad .. 4quad+3
+          const u32x2 v = *reinterpret_cast<const u32x2*>(hbase + 16 * D + (16 * cb + l16) * 16 + 4 * quad);
+          vraw[j][cb][0] = v[0];
+          vraw[j][cb][1] = v[1];
+        }
+        bool keep[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * pg + 4 * quad + r;
+          keep[r] = t < s1 || (t >= r0 && t < L);
+          if (keep[r]) lg[j][r] = d[r] * qscale;
+        }
+        const uint32_t k01 = pair_keep(keep[0], keep[1]), k23 = pair_keep(keep[2], keep[3]);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) { vraw[j][cb][0] &= k01; vraw[j][cb][1] &= k23; }
+      }
+      float pv[2][4];
+      softmax_step(lg, pv);
+      if (ALL_RAW) {
+        // baseline: bf16 probabilities against bf16 values
+        const u32x4 bpr = {pack2(bf16_rne(pv[0][0]), bf16_rne(pv[0][1])), pack2(bf16_rne(pv[0][2]), bf16_rne(pv[0][3])),
+                           pack2(bf16_rne(pv[1][0]), bf16_rne(pv[1][1])), pack2(bf16_rne(pv[1][2]), bf16_rne(pv[1][3]))};
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb)
+          acc[cb] = mfma_bf16(u32x4{vraw[0][cb][0], vraw[0][cb][1], vraw[1][cb][0], vraw[1][cb][1]}, bpr, acc[cb]);
+      } else {
+        // sink/recent tokens of the mixed cache: f16 probabilities and values
+        const u32x4 bpr = {pack_f16x2(pv[0][0], pv[0][1]), pack_f16x2(pv[0][2], pv[0][3]),
+                           pack_f16x2(pv[1][0], pv[1][1]), pack_f16x2(pv[1][2], pv[1][3])};
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const u32x4 a = {bf16x2_to_f16x2(vraw[0][cb][0]), bf16x2_to_f16x2(vraw[0][cb][1]),
+                           bf16x2_to_f16x2(vraw[1][cb][0]), bf16x2_to_f16x2(vraw[1][cb][1])};
+          acc[cb] = mfma_f16(a, bpr, acc[cb]);
+        }
+      }
+    }
+  } else if (!ALL_RAW) {
+    // ---------------- INT2 chunk ----------------
+    const int n_mine = n_pairs > wave ? (n_pairs - wave + kWaves - 1) / kWaves : 0;
+    auto pair_pages = [&](int k, const uint8_t*& pa, const uint8_t*& pb) {
+      const int pg = c0 + 2 * (wave + kWaves * k);
+      pa = p.int2_pool + (size_t(btq[pg]) * p.n_kv + h) * HB;
+      pb = pg + 1 < c1 ? p.int2_pool + (size_t(btq[pg + 1]) * p.n_kv + h) * HB : pa;
+    };
+    // query-rotation operands are requested first, then the first four page
+    // pairs; the rotation runs while the pages are in flight.  Wave w rotates
+    // the 16-channel block cb = w (group w/2, half w%2) with a bf16 hi/lo
+    // split of R_K (16 significant bits; q~ is rounded to f16 afterwards).
+    const float* rk = p.r_k + size_t(h) * D * D;
+    const bool rot_wave = wave < NCB;
+    float rvals[NKB][8];
+    u32x4 bqv[NKB];
+    if (rot_wave) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rvals[kb][i] = rk[size_t(32 * kb + 8 * quad + i) * D + 16 * wave + l16];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        bqv[kb] = u32x4{0, 0, 0, 0};
+        if (l16 < G) bqv[kb] = *reinterpret_cast<const u32x4*>(qb + size_t(l16) * D + 32 * kb + 8 * quad);
+      }
+    }
+    constexpr int kDepth = 4;  // page pairs in flight per wave
+    PairStage<D> st[kDepth];
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) {
+      if (u < n_mine) {
+        const uint8_t *pa, *pb;
+        pair_pages(u, pa, pb);
+        st[u].load(pa, pb, lane);
+      }
+    }
+    float* s_qsp = s_misc + 272;  // [NCB][16] per-block query sums
+    if (rot_wave) {
+      const int g = wave >> 1, hb = wave & 1;
+      f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        uint32_t ph[4], pl[4];
+#pragma unroll
+        for (int i = 0; i < 8; i += 2) {
+          uint32_t h0, l0, h1, l1;
+          split2(rvals[kb][i], h0, l0);
+          split2(rvals[kb][i + 1], h1, l1);
+          ph[i / 2] = pack2(h0, h1); pl[i / 2] = pack2(l0, l1);
+        }
+        a4 = mfma_bf16(u32x4{pl[0], pl[1], pl[2], pl[3]}, bqv[kb], a4);
+        a4 = mfma_bf16(u32x4{ph[0], ph[1], ph[2], ph[3]}, bqv[kb], a4);
+      }
+      // a4[r] = q~[n = l16][c = 32g + 16hb + 4quad + r]; K-slot (e = 2hb + r/2, half r%2)
+      const float v0 = a4[0] * qscale, v1 = a4[1] * qscale, v2 = a4[2] * qscale, v3 = a4[3] * qscale;
+      const float f0 = hb ? 1.f / 16.f : 1.f, f1 = hb ? 1.f / 64.f : 1.f / 4.f;
+      s_qhat[(g * 64 + lane) * 4 + 2 * hb] = pack_f16x2(v0 * f0, v1 * f0);
+      s_qhat[(g * 64 + lane) * 4 + 2 * hb + 1] = pack_f16x2(v2 * f1, v3 * f1);
+      const float qs = wave_sum16((v0 + v1) + (v2 + v3));
+      if (quad == 0) s_qsp[wave * 16 + l16] = qs;
+    }
+    __syncthreads();
+    u32x4 bq[NG];
+#pragma unroll
+    for (int g = 0; g < NG; ++g) bq[g] = *reinterpret_cast<const u32x4*>(s_qhat + (g * 64 + lane) * 4);
+    // zero-term B operand: K-slots of quad 0 carry the per-group query sums
+    // (f16 hi), quad 1 their f16 remainders, the rest zero
+    u32x4 bz = {0, 0, 0, 0};
+    if (quad < 2) {
+      uint32_t hv[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const float qsum = s_qsp[(2 * g) * 16 + l16] + s_qsp[(2 * g + 1) * 16 + l16];
+        const uint32_t hi = f16_bits(qsum);
+        hv[g] = quad == 0 ? hi : f16_bits(qsum - f16_to_f32(hi));
+      }
+      bz = u32x4{pack2(hv[0], hv[1]), pack2(hv[2], hv[3]), pack2(hv[4], hv[5]), pack2(hv[6], hv[7])};
+    }
+    uint8_t* myslots = s_slots + wave * 2 * 2 * HB;
+    // one page pair: logits, softmax, value sums
+    auto do_pair = [&](int k, const uint8_t* slot) {
+      const int pg0 = c0 + 2 * (wave + kWaves * k);
+      float lg[2][4];
+      PageOps<D> P[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int pg = pg0 + j;
+        P[j].read(slot + j * HB, l16, quad);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) lg[j][r] = kNegInf;
+        if (pg >= c1 || 16 * pg < m0 || 16 * pg + 16 > m1) {
+          // boundary (or absent) page: clear scale/zero of slots outside the middle
+          bool keep[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = 16 * pg + 4 * quad + r;
+            keep[r] = pg < c1 && t >= m0 && t < m1;
+          }
+          const uint32_t k01 = pair_keep(keep[0], keep[1]), k23 = pair_keep(keep[2], keep[3]);
+#pragma unroll
+          for (int g = 0; g < NG; ++g) { P[j].vs[2 * g] &= k01; P[j].vs[2 * g + 1] &= k23; }
+          P[j].vz[0] &= k01;
+          P[j].vz[1] &= k23;
+        }
+        if (pg >= c1) continue;
+        const f32x4 dz = mfma_f16(u32x4{P[j].kz[0], P[j].kz[1], 0u, 0u}, bz, f32x4{0.f, 0.f, 0.f, 0.f});
+        float lk[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          const uint32_t src = (g & 1) ? shr8_halves(P[j].kc[g >> 1]) : P[j].kc[g >> 1];
+          const u32x4 a = {src & 0x00030003u, src & 0x000C000Cu, src & 0x00300030u, src & 0x00C000C0u};
+          const f32x4 dg = mfma_f16(a, bq[g], f32x4{0.f, 0.f, 0.f, 0.f});
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int idx = r * NG + g;  // scale of token 4quad + r, group g
+            lk[r] = fmaf(dg[r], f16_to_f32(P[j].ks[idx >> 1] >> (16 * (idx & 1))), lk[r]);
+          }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = 16 * pg + 4 * quad + r;
+          if (t >= m0 && t < m1) lg[j][r] = fmaf(lk[r], kTwo24, dz[r]);
+        }
+      }
+      float pv[2][4];
+      softmax_step(lg, pv);
+      // K-slot e = 2 page + token pair, half = token parity
+      const uint32_t bp[4] = {pack_f16x2(pv[0][0], pv[0][1]), pack_f16x2(pv[0][2], pv[0][3]),
+                              pack_f16x2(pv[1][0], pv[1][1]), pack_f16x2(pv[1][2], pv[1][3])};
+      acc_z = mfma_f16(u32x4{P[0].vz[0], P[0].vz[1], P[1].vz[0], P[1].vz[1]}, u32x4{bp[0], bp[1], bp[2], bp[3]}, acc_z);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        const u32x4 bs = {hmul2(bp[0], P[0].vs[2 * g]), hmul2(bp[1], P[0].vs[2 * g + 1]),
+                          hmul2(bp[2], P[1].vs[2 * g]), hmul2(bp[3], P[1].vs[2 * g + 1])};
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          const int cb = 2 * g + hb, w = cb >> 2, bb = cb & 3;
+          const uint32_t m = 0x00030003u << (2 * bb);
+          const u32x4 a = {P[0].vc[w] & m, shr8_halves(P[0].vc[w]) & m, P[1].vc[w] & m, shr8_halves(P[1].vc[w]) & m};
+          acc[cb] = mfma_f16(a, bs, acc[cb]);
+        }
+      }
+    };
+
+    // kDepth register stages and two LDS slots per wave: pair k is computed
+    // from LDS while pairs k+1 .. k+kDepth are in flight
+    for (int k = 0; k < n_mine; k += kDepth) {
+#pragma unroll
+      for (int u = 0; u < kDepth; ++u) {
+        const int kk = k + u;
+        if (kk < n_mine) {
+          uint8_t* slot = myslots + (u & 1) * 2 * HB;
+          st[u].store(slot, lane);
+          if (kk + kDepth < n_mine) {
+            const uint8_t *pa, *pb;
+            pair_pages(kk + kDepth, pa, pb);
+            st[u].load(pa, pb, lane);
+          }
+          do_pair(kk, slot);
+        }
+      }
+    }
+  }
+
+  // ---- per-wave results -> LDS, merged over the 8 waves ----
+  const float l_w = wave_sum16(l_part);
+  float zg[NG];
+#pragma unroll
+  for (int g = 0; g < NG; ++g) zg[g] = __shfl(acc_z[g], l16, 64);  // Z[g][n] lives in lane (n, quad 0)
+  if (quad == 0) {
+    s_m[wave * 16 + l16] = m_run;
+    s_l[wave * 16 + l16] = l_w;
+  }
+  __syncthreads();
+  float M = kNegInf;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w * 16 + l16]);
+  const float sc = (m_run == kNegInf) ? 0.f : exp2f(m_run - M);
+  if (l16 < G) {
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      f32x4 v;
+      if (is_raw) {
+        v = acc[cb] * sc;
+      } else {
+        const float fpos = kTwo24 / float(1 << (2 * (cb & 3)));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = sc * (acc[cb][r] * fpos + zg[cb >> 1]);
+      }
+      *reinterpret_cast<f32x4*>(s_res + (wave * G + l16) * D + 16 * cb + 4 * quad) = v;
+    }
+  }
+  __syncthreads();
+
+  // ---- workgroup record [m G][l G][acc G D][basis flag] -> workspace ----
+  float* rec = p.partials + ((size_t(b) * p.n_kv + h) * p.n_chunks_max + x) * size_t(p.rec_floats);
+  if (tid < G) {
+    float mm = kNegInf;
+    for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, s_m[w * 16 + tid]);
+    float ll = 0.f;
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = s_m[w * 16 + tid];
+      if (mw != kNegInf) ll += exp2f(mw - mm) * s_l[w * 16 + tid];
+    }
+    st_dev(rec + tid, mm);
+    st_dev(rec + G + tid, ll);
+  }
+  if (tid == 0) st_dev(rec + 2 * G + G * D, is_raw ? 1.f : 0.f);
+  for (int e = tid; e < G * D; e += kThreads) {
+    float s = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) s += s_res[w * G * D + e];
+    st_dev(rec + 2 * G + e, s);
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // records acknowledged before the arrival is counted
+  __syncthreads();
+  if (tid == 0) {
+    const int old = __hip_atomic_fetch_add(p.counters + b * p.n_kv + h, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    s_flag[8] = (old == sp.n_chunks - 1) ? 1 : 0;
+  }
+  __syncthreads();
+  if (!s_flag[8]) return;
+
+  // ---- last workgroup: log-sum-exp merge of the chunk records ----
+  const int n_s = sp.n_chunks;
+  const float* rv = p.r_v + size_t(h) * D * D;
+  const int cbm = wave;  // output block of this wave (NCB <= 8)
+  f32x4 rva[NKB][2];
+  if (!ALL_RAW && cbm < NCB) {  // issued first; latency overlaps the merge
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const float* src = rv + size_t(16 * cbm + l16) * D + 32 * kb + 8 * quad;
+      rva[kb][0] = *reinterpret_cast<const f32x4*>(src);
+      rva[kb][1] = *reinterpret_cast<const f32x4*>(src + 4);
+    }
+  }
+  const float* recs = p.partials + (size_t(b) * p.n_kv + h) * p.n_chunks_max * size_t(p.rec_floats);
+  float* m_rot = s_res;
+  float* m_raw = s_res + G * D;
+  float* s_cm = s_res + 2 * G * D;        // [kMaxChunks][16] chunk maxima
+  float* s_cl = s_cm + kMaxChunks * 16;   // [kMaxChunks][16] chunk sums
+  float* s_cf = s_cl + kMaxChunks * 16;   // [kMaxChunks] basis flags
+  constexpr int EPT = (16 * 128 + kThreads - 1) / kThreads;  // output elements per thread (G*D <= 2048)
+  float Mx[EPT], Lx[EPT], sr[EPT], su[EPT];
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) { Mx[j] = kNegInf; Lx[j] = sr[j] = su[j] = 0.f; }
+  for (int s0 = 0; s0 < n_s; s0 += kMergeBatch) {
+    const int s1b = min(n_s, s0 + kMergeBatch);
+    // chunk maxima/sums/flags and this thread's value sums of the batch are
+    // requested together: one memory round trip per batch
+    const int ms_s = s0 + (tid >> 4), ms_n = tid & 15;  // record and query row this thread stages
+    const bool ms_on = ms_s < s1b && ms_n < G;
+    float cm = 0.f, cl = 0.f, cf = 0.f;
+    if (ms_on) {
+      cm = ld_dev(recs + size_t(ms_s) * p.rec_floats + ms_n);
+      cl = ld_dev(recs + size_t(ms_s) * p.rec_floats + G + ms_n);
+      cf = ld_dev(recs + size_t(ms_s) * p.rec_floats + 2 * G + G * D);
+    }
+    float vv[EPT][kMergeBatch];
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const int e = tid + j * kThreads;
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k)
+        vv[j][k] = (e < G * D && s0 + k < s1b) ? ld_dev(recs + size_t(s0 + k) * p.rec_floats + 2 * G + e) : 0.f;
+    }
+    if (ms_on) {
+      s_cm[ms_s * 16 + ms_n] = cm;
+      s_cl[ms_s * 16 + ms_n] = cl;
+      if (ms_n == 0) s_cf[ms_s] = cf;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < EPT; ++j) {
+      const int e = tid + j * kThreads;
+      if (e >= G * D) continue;
+      const int n = e / D;
+      float bm = kNegInf;
+      for (int s = s0; s < s1b; ++s) bm = fmaxf(bm, s_cm[s * 16 + n]);
+      const float nm = fmaxf(Mx[j], bm);
+      if (nm == kNegInf) continue;
+      const float f = (Mx[j] == kNegInf) ? 0.f : exp2f(Mx[j] - nm);
+      Lx[j] *= f; sr[j] *= f; su[j] *= f;
+      Mx[j] = nm;
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) {
+        const int s = s0 + k;
+        if (s < s1b) {
+          const float ms = s_cm[s * 16 + n];
+          if (ms != kNegInf) {
+            const float wgt = exp2f(ms - nm);
+            Lx[j] = fmaf(wgt, s_cl[s * 16 + n], Lx[j]);
+            if (s_cf[s] != 0.f) su[j] = fmaf(wgt, vv[j][k], su[j]); else sr[j] = fmaf(wgt, vv[j][k], sr[j]);
+          }
+        }
+      }
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int j = 0; j < EPT; ++j) {
+    const int e = tid + j * kThreads;
+    if (e < G * D) {
+      const float inv = 1.f / Lx[j];
+      m_rot[e] = sr[j] * inv;
+      m_raw[e] = su[j] * inv;
+    }
+  }
+  __syncthreads();
+  // out^T[c][n] = raw[n][c] + sum_k R_V[c][k] rot[n][k]   (bf16 hi/lo splits, 3 MFMAs)
+  if (cbm < NCB) {
+    f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+    if (!ALL_RAW) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        uint32_t ah[4], al[4], bh[4], bl[4];
+        const float* rot_row = m_rot + l16 * D + 32 * kb + 8 * quad;
+#pragma unroll
+        for (int k = 0; k < 8; k += 2) {
+          uint32_t h0, l0, h1, l1;
+          split2(rva[kb][k / 4][k % 4], h0, l0);
+          split2(rva[kb][(k + 1) / 4][(k + 1) % 4], h1, l1);
+          ah[k / 2] = pack2(h0, h1); al[k / 2] = pack2(l0, l1);
+          const float x0 = l16 < G ? rot_row[k] : 0.f, x1 = l16 < G ? rot_row[k + 1] : 0.f;
+          split2(x0, h0, l0);
+          split2(x1, h1, l1);
+          bh[k / 2] = pack2(h0, h1); bl[k / 2] = pack2(l0, l1);
+        }
+        const u32x4 AH{ah[0], ah[1], ah[2], ah[3]}, AL{al[0], al[1], al[2], al[3]};
+        const u32x4 BH{bh[0], bh[1], bh[2], bh[3]}, BL{bl[0], bl[1], bl[2], bl[3]};
+        a4 = mfma_bf16(AL, BH, a4);
+        a4 = mfma_bf16(AH, BL, a4);
+        a4 = mfma_bf16(AH, BH, a4);
+      }
+    }
+    if (l16 < G) {
+      uint16_t* o = p.out + (size_t(b) * p.Hq + hq0 + l16) * D + 16 * cbm + 4 * quad;
+      const float* rw = m_raw + l16 * D + 16 * cbm + 4 * quad;
+      u32x2 ov;
+      ov[0] = pack2(bf16_rne(a4[0] + rw[0]), bf16_rne(a4[1] + rw[1]));
+      ov[1] = pack2(bf16_rne(a4[2] + rw[2]), bf16_rne(a4[3] + rw[3]));
+      *reinterpret_cast<u32x2*>(o) = ov;
+    }
+  }
+  if (tid == 0) __hip_atomic_store(p.counters + b * p.n_kv + h, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace
+
+namespace oscar_launch {
+
+int decode_max_splits() { return kMaxChunks; }
+
+// chunks per (sequence, KV head) that a length <= max_seq_len can need
+int decode_chunks_max(bool all_raw, int max_seq_len, int S, int W, int split_pages) {
+  const int max_pages = (max_seq_len + 15) / 16;
+  if (all_raw) return std::max(1, (max_pages + split_pages - 1) / split_pages);
+  const int sink_pages = std::min(max_pages, (S + 15) / 16);
+  const int rec_pages = std::min(max_pages, (W + 15) / 16 + 1);
+  const int raw = std::max((sink_pages + kRawChunk - 1) / kRawChunk + (rec_pages + kRawChunk - 1) / kRawChunk,
+                           (std::min(max_pages, sink_pages + rec_pages) + kRawChunk - 1) / kRawChunk);
+  return std::max(1, raw + (max_pages + split_pages - 1) / split_pages);
+}
+
+size_t decode_lds_bytes(int d, int G, bool all_raw) {
+  const int ng = d / 32;
+  const size_t slots = all_raw ? 0 : size_t(kWaves) * 2 * 2 * 12 * d;
+  size_t res = size_t(kWaves) * G * d;                                             // per-wave results
+  res = std::max(res, size_t(2) * G * d + size_t(kMaxChunks) * 33);                 // merge
+  return (size_t(ng) * 256 + 256 + 512) * 4 + slots + res * 4;
+}
+
+hipError_t paged_decode(int d, bool all_raw, const void* int2_pool, const void* bf16_pool, int n_kv, int G, int S,
+                        int W, int Hq, const void* q, int batch, const int32_t* seq_lens, const int32_t* bt_q,
+                        const int32_t* bt_h, int max_pages, const float* r_k, const float* r_v, float sm_scale,
+                        int split_pages, int n_chunks_max, float* partials, int32_t* counters, int rec_floats,
+                        void* out, hipStream_t stream) {
+  DecParams p{static_cast<const uint8_t*>(int2_pool), static_cast<const uint16_t*>(bf16_pool), n_kv, G, S, W, Hq,
+              static_cast<const uint16_t*>(q), seq_lens, bt_q, bt_h, max_pages, r_k, r_v, sm_scale, split_pages,
+              partials, counters, rec_floats, n_chunks_max, static_cast<uint16_t*>(out)};
+  const dim3 grid(static_cast<unsigned>(n_chunks_max), static_cast<unsigned>(n_kv), static_cast<unsigned>(batch));
+  const size_t lds = decode_lds_bytes(d, G, all_raw);
+  if (d == 128) {
+    if (all_raw) hipLaunchKernelGGL((decode_kernel<128, true>), grid, dim3(kThreads), lds, stream, p);
+    else hipLaunchKernelGGL((decode_kernel<128, false>), grid, dim3(kThreads), lds, stream, p);
+  } else {
+    if (all_raw) hipLaunchKernelGGL((decode_kernel<64, true>), grid, dim3(kThreads), lds, stream, p);
+    else hipLaunchKernelGGL((decode_kernel<64, false>), grid, dim3(kThreads), lds, stream, p);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace oscar_launch

@@ -1,0 +1,94 @@
+// Device helpers for gfx950 (CDNA4) kernels: MFMA operand types, exact
+// bfloat16 three-way splits, f16/bf16 conversions, wave64 shuffles.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace oscar_dev {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// D = A(16x32) B(32x16) + C.  Lane l holds A[l%16][8(l/16) .. +7],
+// B[8(l/16) .. +7][l%16]; D[4(l/16) + r][l%16] in element r.
+__device__ __forceinline__ f32x4 mfma_f16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+}
+__device__ __forceinline__ f32x4 mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// float32 -> bfloat16 bits, round half to even (finite inputs).
+__device__ __forceinline__ uint32_t bf16_rne(float x) {
+  uint32_t u = __float_as_uint(x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// x = hi + mid + lo exactly (each a bfloat16): a float32 significand has 24
+// bits, each part carries 8.
+struct Split3 {
+  uint32_t hi, mid, lo;
+};
+__device__ __forceinline__ Split3 split3(float x) {
+  Split3 s;
+  s.hi = bf16_rne(x);
+  const float r1 = x - bf16_to_f32(s.hi);
+  s.mid = bf16_rne(r1);
+  const float r2 = r1 - bf16_to_f32(s.mid);
+  s.lo = bf16_rne(r2);
+  return s;
+}
+// x = hi + lo to 16 significant bits.
+__device__ __forceinline__ void split2(float x, uint32_t& hi, uint32_t& lo) {
+  hi = bf16_rne(x);
+  lo = bf16_rne(x - bf16_to_f32(hi));
+}
+
+__device__ __forceinline__ uint32_t pack2(uint32_t lo16, uint32_t hi16) { return (lo16 & 0xFFFFu) | (hi16 << 16); }
+
+__device__ __forceinline__ uint32_t f16_bits(float x) {
+  _Float16 h = (_Float16)x;
+  return __builtin_bit_cast(unsigned short, h);
+}
+__device__ __forceinline__ float f16_to_f32(uint32_t b) {
+  return (float)__builtin_bit_cast(_Float16, (unsigned short)(b & 0xFFFFu));
+}
+// two floats -> packed f16x2 (round to nearest even)
+__device__ __forceinline__ uint32_t pack_f16x2(float a, float b) { return pack2(f16_bits(a), f16_bits(b)); }
+
+// packed f16x2 multiply
+__device__ __forceinline__ uint32_t hmul2(uint32_t a, uint32_t b) {
+  f16x2 x = __builtin_bit_cast(f16x2, a) * __builtin_bit_cast(f16x2, b);
+  return __builtin_bit_cast(uint32_t, x);
+}
+
+// each 16-bit half shifted right by 8
+__device__ __forceinline__ uint32_t shr8_halves(uint32_t x) {
+  u16x2 v = __builtin_bit_cast(u16x2, x);
+  v = v >> (unsigned short)8;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
+__device__ __forceinline__ float wave_max16(float v) {  // over lanes with equal l%16
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+__device__ __forceinline__ float wave_sum16(float v) {
+  v += __shfl_xor(v, 16, 64);
+  return v + __shfl_xor(v, 32, 64);
+}
+
+}  // namespace oscar_dev

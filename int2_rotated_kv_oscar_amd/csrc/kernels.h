@@ -1,0 +1,25 @@
+// Launch functions of the liboscar kernels (internal; called by abi.hip after
+// argument validation).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace oscar_launch {
+
+hipError_t quantize_append(int d, int n_kv, void* pool, const void* k_new, const void* v_new, int64_t n_rows,
+                           const int32_t* row_seq, const int32_t* row_pos, const int32_t* bt_q,
+                           int32_t max_pages, const float* r_k, const float* r_v, float tau_k, float tau_v,
+                           hipStream_t stream);
+
+size_t decode_lds_bytes(int d, int G, bool all_raw);
+int decode_max_splits();
+int decode_chunks_max(bool all_raw, int max_seq_len, int S, int W, int split_pages);
+
+hipError_t paged_decode(int d, bool all_raw, const void* int2_pool, const void* bf16_pool, int n_kv, int G, int S,
+                        int W, int Hq, const void* q, int batch, const int32_t* seq_lens, const int32_t* bt_q,
+                        const int32_t* bt_h, int max_pages, const float* r_k, const float* r_v, float sm_scale,
+                        int split_pages, int n_chunks_max, float* partials, int32_t* counters, int rec_floats,
+                        void* out, hipStream_t stream);
+
+}  // namespace oscar_launch

@@ -1,0 +1,86 @@
+"""The C-ABI library (CPU side): it loads, exports every symbol the header
+declares, and rejects bad host-visible arguments before touching a GPU."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from int2_rotated_kv_oscar_amd import lib
+
+HDR = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "oscar.h")
+
+
+def _declared():
+    txt = open(HDR).read()
+    return sorted(set(re.findall(r"\b(oscar_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert set(names) == set(lib.EXPORTS)
+    L = lib.load()
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings_and_geometry():
+    L = lib.load()
+    assert L.oscar_status_string(0) == b"OSCAR_OK"
+    assert L.oscar_status_string(4) == b"OSCAR_ERR_WORKSPACE"
+    assert lib.version() == 1
+    assert lib.int2_page_bytes(128, 8) == 8 * 1536 and lib.int2_page_bytes(64, 1) == 768
+    assert lib.bf16_page_bytes(128, 8) == 8 * 16 * 128 * 2 * 2
+    assert lib.int2_page_bytes(96, 1) == 0
+
+
+def test_workspace_planning():
+    # bound valid for any sink/recent sizes: INT2 chunks + BF16 chunks of 16 pages + 1
+    b = lib.decode_workspace_bytes(1, 8, 32, 128, 32768, 64)
+    rec = (2 * 4 + 4 * 128 + 1 + 3) // 4 * 4
+    assert b == 256 + 8 * (2048 // 64 + 2048 // 16 + 1) * rec * 4
+    assert lib.decode_workspace_bytes(0, 8, 32, 128, 0) == 0
+    for bad, status in (((1, 8, 30, 128, 100, 0), 1), ((1, 1, 17, 128, 100, 0), 2), ((1, 1, 4, 96, 100, 0), 2),
+                        ((1, 1, 4, 128, 100, 12), 1), ((-1, 1, 4, 128, 100, 0), 1)):
+        with pytest.raises(lib.OscarError) as e:
+            lib.decode_workspace_bytes(*bad)
+        assert e.value.status == status
+
+
+def test_device_calls_validate_before_launch():
+    L = lib.load()
+    c = lib.OscarCache()
+    c.d, c.n_kv_heads = 96, 1
+    assert L.oscar_quantize_append(ctypes.byref(c), None, None, 1, None, None, None, 1, None, None, 1.0, 1.0, None) == 2
+    c.d = 128
+    assert L.oscar_quantize_append(ctypes.byref(c), None, None, 1, None, None, None, 1, None, None, 1.0, 1.0, None) == 1
+    assert L.oscar_quantize_append(None, None, None, 1, None, None, None, 1, None, None, 1.0, 1.0, None) == 1
+    assert b"cache is NULL" in L.oscar_last_error()
+    c.int2_pool, c.n_int2_pages = 16, 1   # never dereferenced: validation fails first
+    assert L.oscar_quantize_append(ctypes.byref(c), None, None, 0, None, None, None, 1, None, None, 1.0, 1.0, None) == 0
+    assert L.oscar_quantize_append(ctypes.byref(c), None, None, -1, None, None, None, 1, None, None, 1.0, 1.0, None) == 1
+    c.bf16_pool, c.n_bf16_pages = 16, 1
+    # batch 0 is a no-op; a missing workspace is reported before any launch
+    assert L.oscar_paged_decode_attn(ctypes.byref(c), None, 0, 4, None, 0, None, None, 1, None, None, 0.1, 0,
+                                     None, 0, None, None) == 0
+    assert L.oscar_paged_decode_attn(ctypes.byref(c), 16, 1, 4, 16, 32, 16, 16, 2, 16, 16, 0.1, 0,
+                                     None, 0, 16, None) == 4
+    assert L.oscar_paged_decode_attn(ctypes.byref(c), 16, 1, 4, 16, 33, 16, 16, 2, 16, 16, 0.1, 0,
+                                     16, 1 << 20, 16, None) == 1   # max_seq_len > 16 * max_pages
+    assert L.oscar_decode_workspace_init(None, 64, None) == 4
+
+
+def test_build_rotation_validation():
+    q = np.zeros((4, 2, 64), np.float32); k = np.zeros((4, 1, 64), np.float32)
+    with pytest.raises(lib.OscarError) as e:
+        lib.build_rotation(q, k, k, 2, clip_quantile=1.5)
+    assert e.value.status == 1
+    bad = k.copy(); bad[0, 0, 0] = np.nan
+    with pytest.raises(lib.OscarError) as e:
+        lib.build_rotation(q, bad, k, 2)
+    assert e.value.status == 3
+    with pytest.raises(lib.OscarError) as e:
+        lib.build_rotation(np.zeros((4, 1, 96), np.float32), np.zeros((4, 1, 96), np.float32),
+                           np.zeros((4, 1, 96), np.float32), 1)
+    assert e.value.status == 2

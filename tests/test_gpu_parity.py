@@ -1,0 +1,251 @@
+"""GPU parity of the C ABI (HIP kernels on gfx950) against the CPU oracle.
+
+Quantize-append: codes bit-exact except within 1e-5 of a rounding boundary
+(<= 0.01 % of codes), f16 scale/zero bit-equal except within 1e-6 (relative)
+of an f16 rounding midpoint.  Decode: rel-L2 <= 5e-3 and max-abs <= 2e-2
+against the oracle's float64 output on the same pages.
+"""
+import numpy as np
+import pytest
+import torch
+
+from int2_rotated_kv_oscar_amd import lib, synth
+from oracle import cache as ocache
+from oracle import layout as olayout
+
+import gpu_helpers as gh
+
+pytestmark = pytest.mark.gpu
+
+
+def _tiny(**kw):
+    w = synth.WORKLOADS["tiny"]
+    return synth.Workload(**{**w.__dict__, **kw}) if kw else w
+
+
+@pytest.fixture(scope="module")
+def tiny_rot():
+    return gh.oracle_rotation(_tiny())
+
+
+def _page_slot(inp, rows):
+    ms, mp, _ = rows
+    return inp.bt_q[ms, mp // 16].astype(np.int64), (mp % 16).astype(np.int64)
+
+
+def test_library_loaded_from_tree():
+    import os
+    assert os.path.dirname(lib.LIB_PATH).endswith("int2_rotated_kv_oscar_amd")
+    lib.load()
+    maps = open("/proc/self/maps").read()
+    assert lib.LIB_PATH in maps
+
+
+def test_quantize_append_tiny(tiny_rot):
+    w = _tiny()
+    inp = synth.decode_inputs(w)
+    gc = gh.alloc_cache(inp, tiny_rot)
+    rows = synth.middle_rows(inp)
+    print(f"[quantize_append tiny] rows={len(rows[0])}", flush=True)
+    gh.gpu_fill(inp, tiny_rot, gc, rows)
+    torch.cuda.synchronize()
+    _, _, res, _ = gh.oracle_pools(inp, tiny_rot)
+    page, slot = _page_slot(inp, rows)
+    rep = gh.compare_appended(gc.int2.cpu().numpy(), w, inp.n_int2_pages, res, page, slot)
+    print(rep)
+    gh.assert_codes_ok(rep, "tiny")
+
+
+@pytest.mark.parametrize("d,hkv,n_seq,chunk", [(128, 2, 3, 48), (64, 3, 2, 8200)])
+def test_quantize_append_page_aligned_prefill(d, hkv, n_seq, chunk):
+    # whole pages back to back (the direct-store path), shuffled page ids,
+    # a ragged last page, and (d=64) enough rows for the multi-tile waves
+    w = synth.Workload("prefill-test", 5, n_seq, 4 * hkv, hkv, d, 4, 128, 64, ("fixed", chunk, chunk), k_noise="t3")
+    k, v, row_seq, row_pos = synth.prefill_rows(w, n_seq, chunk)
+    pages_per = (chunk + 15) // 16
+    perm = synth.rng_for(99, 7).permutation(n_seq * pages_per).astype(np.int32)
+    bt_q = perm.reshape(n_seq, pages_per)
+    cal = synth.calibration_set(w, n_rows=256)
+    from oracle import rotation as orot
+    rt = orot.build_rotation(cal.q, cal.k, cal.v, w.group_q)
+    rot = gh.Rotation(rt["r_k"].astype(np.float32).astype(np.float64), rt["r_v"].astype(np.float32).astype(np.float64),
+                      float(np.float32(rt["tau_k"])), float(np.float32(rt["tau_v"])))
+    int2 = torch.zeros(n_seq * pages_per * lib.int2_page_bytes(d, hkv), dtype=torch.uint8, device=gh.DEV)
+    cache = lib.make_cache(d, hkv, 4, 128, int2, None)
+    print(f"[prefill d={d} rows={len(row_seq)}]", flush=True)
+    lib.quantize_append(cache, gh.bits_to_dev_bf16(k), gh.bits_to_dev_bf16(v), gh.i32(row_seq), gh.i32(row_pos),
+                        gh.i32(bt_q), torch.from_numpy(rot.r_k.astype(np.float32)).to(gh.DEV),
+                        torch.from_numpy(rot.r_v.astype(np.float32)).to(gh.DEV), rot.tau_k, rot.tau_v)
+    torch.cuda.synchronize()
+    pool = olayout.Int2Pool(n_seq * pages_per, hkv, d)
+    res = ocache.quantize_append(pool, k, v, row_seq, row_pos, bt_q, rot.r_k, rot.r_v, rot.tau_k, rot.tau_v,
+                                 olayout.bf16_to_f64)
+    page = bt_q[row_seq, row_pos // 16].astype(np.int64)
+    rep = gh.compare_appended(int2.cpu().numpy(), w, n_seq * pages_per, res, page, (row_pos % 16).astype(np.int64))
+    print(rep)
+    gh.assert_codes_ok(rep, "prefill")
+
+
+def test_quantize_append_scattered_single_rows(tiny_rot):
+    # rows in random order: neighbouring slots of one page written by
+    # different waves at once (the partial-word path)
+    w = _tiny()
+    inp = synth.decode_inputs(w)
+    ms, mp, mr = synth.middle_rows(inp)
+    perm = np.random.default_rng(5).permutation(len(ms))
+    rows = (ms[perm], mp[perm], mr[perm])
+    gc = gh.alloc_cache(inp, tiny_rot)
+    gc.int2.random_(0, 256)  # stale bytes in the pool must be replaced, not OR-ed
+    gh.gpu_fill(inp, tiny_rot, gc, rows)
+    torch.cuda.synchronize()
+    _, _, res, _ = gh.oracle_pools(inp, tiny_rot)
+    # oracle record is in middle_rows order; compare in that order
+    page = inp.bt_q[ms, mp // 16].astype(np.int64)
+    rep = gh.compare_appended(gc.int2.cpu().numpy(), w, inp.n_int2_pages, res, page, (mp % 16).astype(np.int64))
+    gh.assert_codes_ok(rep, "scattered")
+
+
+def test_decode_on_oracle_pages_tiny(tiny_rot):
+    w = _tiny()
+    inp = synth.decode_inputs(w)
+    int2, bf, _, _ = gh.oracle_pools(inp, tiny_rot)
+    gc = gh.alloc_cache(inp, tiny_rot, int2.data, bf.data)
+    ref = gh.oracle_decode(inp, tiny_rot, int2, bf)
+    for sp in (0, 8, 16):
+        print(f"[decode tiny oracle pages] split_pages={sp}", flush=True)
+        got = gh.gpu_decode(inp, gc, split_pages=sp)
+        print(sp, gh.attention_errors(got, ref))
+        gh.assert_attention_close(got, ref, f"split {sp}")
+
+
+def test_end_to_end_tiny(tiny_rot):
+    w = _tiny()
+    inp = synth.decode_inputs(w)
+    gc = gh.alloc_cache(inp, tiny_rot)
+    gh.gpu_fill(inp, tiny_rot, gc)
+    got = gh.gpu_decode(inp, gc)
+    int2, bf, _, _ = gh.oracle_pools(inp, tiny_rot)
+    ref = gh.oracle_decode(inp, tiny_rot, int2, bf)
+    print(gh.attention_errors(got, ref))
+    gh.assert_attention_close(got, ref, "end-to-end tiny")
+
+
+@pytest.mark.parametrize("lens", [[1], [2], [17], [36], [37], [100], [512, 1, 300, 0, 37, 129]])
+def test_decode_lengths_and_ragged_batch(tiny_rot, lens):
+    w = _tiny(batch=len(lens))
+    inp = synth.decode_inputs(w, seq_lens=np.array(lens))
+    gc = gh.alloc_cache(inp, tiny_rot)
+    gh.gpu_fill(inp, tiny_rot, gc)
+    print(f"[decode lens={lens}]", flush=True)
+    got = gh.gpu_decode(inp, gc)
+    int2, bf, _, _ = gh.oracle_pools(inp, tiny_rot)
+    ref = gh.oracle_decode(inp, tiny_rot, int2, bf)
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.all(got[b] == 0)
+        else:
+            gh.assert_attention_close(got[b], ref[b], f"len {L}")
+
+
+@pytest.mark.parametrize("hq,hkv,d,q_scale", [(4, 4, 64, 1.0), (16, 1, 128, 1.0), (12, 1, 128, 8.0),
+                                              (8, 2, 128, 8.0), (3, 1, 64, 1.0)])
+def test_decode_group_shapes(hq, hkv, d, q_scale):
+    w = synth.Workload("shape", 6, 2, hq, hkv, d, 4, 32, 512, ("fixed", 700, 700), q_scale=q_scale)
+    rot = gh.oracle_rotation(w, n_rows=512, q_scale=q_scale)
+    inp = synth.decode_inputs(w, seq_lens=np.array([700, 333]), q_scale=q_scale)
+    gc = gh.alloc_cache(inp, rot)
+    gh.gpu_fill(inp, rot, gc)
+    print(f"[decode shape hq={hq} hkv={hkv} d={d}]", flush=True)
+    got = gh.gpu_decode(inp, gc, split_pages=8)
+    int2, bf, res, rows = gh.oracle_pools(inp, rot)
+    page, slot = _page_slot(inp, rows)
+    gh.assert_codes_ok(gh.compare_appended(gc.int2.cpu().numpy(), w, inp.n_int2_pages, res, page, slot))
+    ref = gh.oracle_decode(inp, rot, int2, bf)
+    print(gh.attention_errors(got, ref))
+    gh.assert_attention_close(got, ref, "shape")
+
+
+def test_invariances_tables_splits_determinism(tiny_rot):
+    w = _tiny(batch=2)
+    lens = np.array([512, 400])
+    a = synth.decode_inputs(w, seq_lens=lens, shuffle=True)
+    b = synth.decode_inputs(w, seq_lens=lens, shuffle=False)
+    ga = gh.alloc_cache(a, tiny_rot); gh.gpu_fill(a, tiny_rot, ga)
+    gb = gh.alloc_cache(b, tiny_rot); gh.gpu_fill(b, tiny_rot, gb)
+    oa = gh.gpu_decode(a, ga, split_pages=8)
+    ob = gh.gpu_decode(b, gb, split_pages=8)
+    assert np.array_equal(oa, ob), "shuffled and identity block tables differ"
+    assert np.array_equal(oa, gh.gpu_decode(a, ga, split_pages=8)), "not deterministic"
+    o64 = gh.gpu_decode(a, ga, split_pages=64)
+    # outputs are bf16: different chunkings may round to neighbouring values;
+    # both must meet the oracle bound and stay close to each other
+    rel, mx = gh.attention_errors(o64, oa)
+    assert rel <= 2e-3 and mx <= 1e-2, (rel, mx)
+    int2, bf, _, _ = gh.oracle_pools(a, tiny_rot)
+    ref = gh.oracle_decode(a, tiny_rot, int2, bf)
+    gh.assert_attention_close(o64, ref, "64-page chunks")
+    gh.assert_attention_close(oa, ref, "8-page chunks")
+
+
+def test_shared_prefix_pages_alias(tiny_rot):
+    # three sequences name the same physical pages for their first 64 tokens;
+    # the output equals a run where each sequence owns a copy of them
+    w = _tiny(batch=3, shared_prefix=64)
+    lens = np.array([300, 512, 222])
+    inp = synth.decode_inputs(w, seq_lens=lens)
+    gc = gh.alloc_cache(inp, tiny_rot)
+    gh.gpu_fill(inp, tiny_rot, gc)
+    got = gh.gpu_decode(inp, gc)
+    int2, bf, _, _ = gh.oracle_pools(inp, tiny_rot)
+    ref = gh.oracle_decode(inp, tiny_rot, int2, bf)
+    gh.assert_attention_close(got, ref, "shared prefix")
+    # copies: each sequence alone with private pages gives bit-identical rows
+    for b in range(3):
+        wb = _tiny(batch=1, shared_prefix=0)
+        single = synth.DecodeInputs(wb, lens[b:b + 1], inp.k_rows, inp.v_rows, [inp.row_of[b]], inp.q[b:b + 1],
+                                    *_private_tables(inp, b))
+        gs = gh.alloc_cache(single, tiny_rot)
+        gh.gpu_fill(single, tiny_rot, gs)
+        assert np.array_equal(gh.gpu_decode(single, gs), got[b:b + 1]), f"sequence {b}"
+
+
+def _private_tables(inp, b):
+    L = int(inp.seq_lens[b])
+    n = (L + 15) // 16
+    bt_q = np.where(inp.bt_q[b:b + 1, :n] >= 0, np.arange(n, dtype=np.int32)[None], -1).astype(np.int32)
+    bt_h = np.where(inp.bt_h[b:b + 1, :n] >= 0, np.arange(n, dtype=np.int32)[None], -1).astype(np.int32)
+    return bt_q, bt_h, n, n, n
+
+
+def test_bf16_baseline_matches_plain_attention(tiny_rot):
+    from oracle import attention as oatt
+    w = _tiny(batch=2, n_sink=100000, n_recent=0)   # every token in BF16 pages
+    lens = np.array([512, 77])
+    inp = synth.decode_inputs(w, seq_lens=lens)
+    gc = gh.alloc_cache(inp, tiny_rot)
+    gh.gpu_fill(inp, tiny_rot, gc)
+    got = gh.gpu_decode(inp, gc, all_raw=True)
+    q = synth.bf16_bits_to_f32(inp.q).astype(np.float64)
+    for b, L in enumerate(lens):
+        k = olayout.bf16_to_f64(inp.k_rows[inp.row_of[b], 0]); v = olayout.bf16_to_f64(inp.v_rows[inp.row_of[b], 0])
+        ref = oatt.softmax_attention(q[b], k, v, 1 / 8.0)
+        gh.assert_attention_close(got[b], ref, "bf16 baseline")
+
+
+def test_abi_rejects_bad_arguments_on_device():
+    w = _tiny()
+    with pytest.raises(lib.OscarError) as e:
+        lib.decode_workspace_bytes(1, 1, 4, 96, 512)
+    assert e.value.status == 2
+    with pytest.raises(lib.OscarError) as e:
+        lib.decode_workspace_bytes(1, 2, 3, 128, 512)
+    assert e.value.status == 1
+    ws = torch.zeros(4, dtype=torch.int32, device=gh.DEV)
+    inp = synth.decode_inputs(w)
+    rot = gh.Rotation(np.eye(64)[None], np.eye(64)[None], 1.0, 1.0)
+    gc = gh.alloc_cache(inp, rot)
+    q = gh.bits_to_dev_bf16(inp.q)
+    out = torch.zeros(1, 4, 64, dtype=torch.bfloat16, device=gh.DEV)
+    with pytest.raises(lib.OscarError) as e:
+        lib.paged_decode_attn(gc.cache, q, gh.i32(inp.seq_lens), 512, gc.bt_q, gc.bt_h, gc.r_k, gc.r_v, out, ws)
+    assert e.value.status == 4

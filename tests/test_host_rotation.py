@@ -1,0 +1,53 @@
+"""oscar_build_rotation (host C++, float64) against the oracle and the
+invariants of the method ([TS] 2.1, 2.2.A)."""
+import numpy as np
+import pytest
+
+from int2_rotated_kv_oscar_amd import lib, synth
+from oracle import rotation as orot
+
+
+@pytest.mark.parametrize("name,n_rows", [("tiny", 2048), ("qwen3-8b-b1-32k", 384)])
+def test_matches_oracle(name, n_rows):
+    w = synth.WORKLOADS[name]
+    cal = synth.calibration_set(w, n_rows=n_rows)
+    got = lib.build_rotation(cal.q, cal.k, cal.v, w.group_q)
+    ref = orot.build_rotation(cal.q, cal.k, cal.v, w.group_q)
+    d = w.d
+    for key in ("eig_k", "eig_v"):
+        np.testing.assert_allclose(got[key], ref[key], rtol=0, atol=1e-10 * np.abs(ref[key]).max())
+    for h in range(w.n_kv_heads):
+        for rk, c, lam in ((got["r_k"][h], ref["c_q"][h], ref["eig_k"][h]), (got["r_v"][h], ref["c_s"][h], ref["eig_v"][h])):
+            assert np.abs(rk.T @ rk - np.eye(d)).max() <= 1e-10                         # O1
+            np.testing.assert_allclose(np.diag(rk.T @ c @ rk), np.trace(c) / d, rtol=1e-9)  # O6
+        # columns of R agree wherever the eigenvalue gap is wide (signs are canonical)
+        for key, ek in (("r_k", ref["eig_k"][h]), ("r_v", ref["eig_v"][h])):
+            gap = np.minimum(np.r_[np.inf, -np.diff(ek)], np.r_[-np.diff(ek), np.inf]) / ek[0]
+            u_got = got[key][h] @ orot.bitrev_perm(d) @ (orot.hadamard(d) / np.sqrt(d)).T
+            u_ref = ref[key][h] @ orot.bitrev_perm(d) @ (orot.hadamard(d) / np.sqrt(d)).T
+            wide = gap > 1e-3
+            assert np.abs(u_got[:, wide] - u_ref[:, wide]).max() <= 1e-8
+    # tau depends on R, which is unique only up to rotations inside
+    # near-degenerate eigenspaces, so it agrees to the eigensolver's accuracy
+    assert got["tau_k"] == pytest.approx(ref["tau_k"], rel=1e-9)
+    assert got["tau_v"] == pytest.approx(ref["tau_v"], rel=1e-9)
+
+
+def test_supplied_attention_output_and_threads():
+    w = synth.WORKLOADS["tiny"]
+    cal = synth.calibration_set(w, n_rows=300)
+    o = np.random.default_rng(1).standard_normal(cal.q.shape).astype(np.float32)
+    got = lib.build_rotation(cal.q, cal.k, cal.v, w.group_q, o_calib=o, n_threads=3)
+    ref = orot.build_rotation(cal.q, cal.k, cal.v, w.group_q, oc=o)
+    np.testing.assert_allclose(got["eig_v"], ref["eig_v"], rtol=0, atol=1e-10 * ref["eig_v"].max())
+    one = lib.build_rotation(cal.q, cal.k, cal.v, w.group_q, n_threads=1)
+    many = lib.build_rotation(cal.q, cal.k, cal.v, w.group_q, n_threads=8)
+    assert np.array_equal(one["r_k"], many["r_k"]) and np.array_equal(one["r_v"], many["r_v"])
+
+
+def test_jacobi_non_convergence_is_reported():
+    w = synth.WORKLOADS["tiny"]
+    cal = synth.calibration_set(w, n_rows=64)
+    with pytest.raises(lib.OscarError) as e:
+        lib.build_rotation(cal.q, cal.k, cal.v, w.group_q, max_sweeps=1)
+    assert e.value.status == 3
