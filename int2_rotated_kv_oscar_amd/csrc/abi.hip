@@ -105,7 +105,7 @@ oscar_status plan_decode(int32_t batch, int32_t n_kv, int32_t n_q, int32_t d, in
   } else {
     plan->n_chunks = std::max(1, n_int2 + (max_pages + kRawChunkPages - 1) / kRawChunkPages + 1);
   }
-  plan->rec_floats = (2 * G + G * d + 1 + 3) / 4 * 4;
+  plan->rec_floats = (2 * G + G * d + 1 + 3) / 4 * 4;  // [max G][sum G][value sums G d][basis flag]
   plan->counter_bytes = (size_t(batch) * n_kv * 4 + 255) / 256 * 256;
   plan->bytes = plan->counter_bytes + size_t(batch) * n_kv * plan->n_chunks * plan->rec_floats * 4;
   return OSCAR_OK;

@@ -29,6 +29,7 @@
 // (sequence, KV head) merges them by log-sum-exp and applies the output
 // rotation R_V^T on the MFMA.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_utils.h"
 #include "layout.h"
@@ -63,8 +64,9 @@ constexpr int kThreads = 64 * kWaves;
 constexpr int kRawChunk = 16;     // pages per BF16 chunk of the mixed cache
 constexpr int kMaxChunks = 256;   // chunks per (sequence, KV head)
 constexpr int kMergeBatch = 32;   // chunk records loaded per merge round
-static_assert(kMergeBatch * 16 == kThreads, "one thread stages one (record, query row) of a merge batch");
+static_assert(kMaxChunks * 16 % kThreads == 0, "merge: (record, query row) slots split evenly over threads");
 constexpr float kTwo24 = 16777216.0f;
+constexpr float kSlack = 4.0f;    // log2 units
 constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ bool overlaps(int a0, int a1, int b0, int b1) { return max(a0, b0) < min(a1, b1); }
@@ -214,7 +216,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   // and [G][D] raw
 
   const int x = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, l16 = lane & 15, quad = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, quad = lane >> 4;
+  // wave index in a scalar register: page-table lookups become scalar loads,
+  // which the vector-memory counter does not wait on
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int L = p.seq_lens[b];
   const int hq0 = h * G;
   if (L <= 0) {
@@ -225,6 +230,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   const SeqPlan sp = make_plan<ALL_RAW>(p, L);
   if (x >= sp.n_chunks) return;
   const float qscale = p.sm_scale * kLog2e;
+  const int qrow = min(l16, G - 1);  // MFMA columns n >= G repeat a real head; their results are dropped
   const uint16_t* qb = p.q + (size_t(b) * p.Hq + hq0) * D;
   const int32_t* btq = p.bt_q + size_t(b) * p.max_pages;
   const int32_t* bth = p.bt_h + size_t(b) * p.max_pages;
@@ -248,8 +254,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     float mx = fmaxf(fmaxf(fmaxf(lg[0][0], lg[0][1]), fmaxf(lg[0][2], lg[0][3])),
                      fmaxf(fmaxf(lg[1][0], lg[1][1]), fmaxf(lg[1][2], lg[1][3])));
     mx = wave_max16(mx);
+    // lazy rescaling: the reference max moves only when a logit exceeds it
+    // by more than kSlack (probabilities stay <= 2^kSlack, safe in f16)
     const float m_new = fmaxf(m_run, mx);
-    if (__any(m_new > m_run)) {
+    if (__any(mx > m_run + kSlack)) {
       const float f = (m_run == kNegInf) ? 0.f : exp2f(m_run - m_new);
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) acc[cb] *= f;
@@ -257,11 +265,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
       l_part *= f;
       m_run = m_new;
     }
+    // every page pair holds at least one unmasked token, so m_run is finite
+    // here unless the logits themselves are not; masked logits (-inf) give 0
+    const float m_use = (m_run == kNegInf) ? 0.f : m_run;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        pv[j][r] = (lg[j][r] == kNegInf) ? 0.f : exp2f(lg[j][r] - m_run);
+        pv[j][r] = __builtin_amdgcn_exp2f(lg[j][r] - m_use);
         l_part += pv[j][r];
       }
   };
@@ -270,10 +281,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     // ---------------- BF16 chunk: raw q . k, raw-basis value sums ----------------
     u32x4 bqr[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      bqr[kb] = u32x4{0, 0, 0, 0};
-      if (l16 < G) bqr[kb] = *reinterpret_cast<const u32x4*>(qb + size_t(l16) * D + 32 * kb + 8 * quad);
-    }
+    for (int kb = 0; kb < NKB; ++kb) bqr[kb] = *reinterpret_cast<const u32x4*>(qb + size_t(qrow) * D + 32 * kb + 8 * quad);
     for (int pr = wave; pr < n_pairs; pr += kWaves) {
       const int pg0 = c0 + 2 * pr;
       float lg[2][4];
@@ -332,8 +340,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   } else if (!ALL_RAW) {
     // ---------------- INT2 chunk ----------------
     const int n_mine = n_pairs > wave ? (n_pairs - wave + kWaves - 1) / kWaves : 0;
+    // pair k of this wave (k = -1: the chunk's first pair, always present)
     auto pair_pages = [&](int k, const uint8_t*& pa, const uint8_t*& pb) {
-      const int pg = c0 + 2 * (wave + kWaves * k);
+      const int pg = k < 0 ? c0 : c0 + 2 * (wave + kWaves * k);
       pa = p.int2_pool + (size_t(btq[pg]) * p.n_kv + h) * HB;
       pb = pg + 1 < c1 ? p.int2_pool + (size_t(btq[pg + 1]) * p.n_kv + h) * HB : pa;
     };
@@ -351,20 +360,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) rvals[kb][i] = rk[size_t(32 * kb + 8 * quad + i) * D + 16 * wave + l16];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        bqv[kb] = u32x4{0, 0, 0, 0};
-        if (l16 < G) bqv[kb] = *reinterpret_cast<const u32x4*>(qb + size_t(l16) * D + 32 * kb + 8 * quad);
-      }
+      for (int kb = 0; kb < NKB; ++kb) bqv[kb] = *reinterpret_cast<const u32x4*>(qb + size_t(qrow) * D + 32 * kb + 8 * quad);
     }
+    // Page loads are issued unconditionally (a wave short of pairs reloads a
+    // valid pair) so that every wait for a stage counts exactly the loads
+    // issued after it instead of draining all of them.
     constexpr int kDepth = 4;  // page pairs in flight per wave
     PairStage<D> st[kDepth];
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) {
-      if (u < n_mine) {
-        const uint8_t *pa, *pb;
-        pair_pages(u, pa, pb);
-        st[u].load(pa, pb, lane);
-      }
+      const uint8_t *pa, *pb;
+      pair_pages(min(u, n_mine - 1), pa, pb);
+      st[u].load(pa, pb, lane);
     }
     float* s_qsp = s_misc + 272;  // [NCB][16] per-block query sums
     if (rot_wave) {
@@ -391,7 +398,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
       const float qs = wave_sum16((v0 + v1) + (v2 + v3));
       if (quad == 0) s_qsp[wave * 16 + l16] = qs;
     }
-    __syncthreads();
+    lds_barrier();
     u32x4 bq[NG];
 #pragma unroll
     for (int g = 0; g < NG; ++g) bq[g] = *reinterpret_cast<const u32x4*>(s_qhat + (g * 64 + lane) * 4);
@@ -410,7 +417,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     }
     uint8_t* myslots = s_slots + wave * 2 * 2 * HB;
     // one page pair: logits, softmax, value sums
-    auto do_pair = [&](int k, const uint8_t* slot) {
+    // INTERIOR: both pages present and wholly inside the middle region (no
+    // per-token masking); the general form handles the chunk edges
+    auto do_pair = [&](int k, const uint8_t* slot, auto interior_tag) {
+      constexpr bool INTERIOR = decltype(interior_tag)::value;
       const int pg0 = c0 + 2 * (wave + kWaves * k);
       float lg[2][4];
       PageOps<D> P[2];
@@ -420,7 +430,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
         P[j].read(slot + j * HB, l16, quad);
 #pragma unroll
         for (int r = 0; r < 4; ++r) lg[j][r] = kNegInf;
-        if (pg >= c1 || 16 * pg < m0 || 16 * pg + 16 > m1) {
+        if (!INTERIOR && (pg >= c1 || 16 * pg < m0 || 16 * pg + 16 > m1)) {
           // boundary (or absent) page: clear scale/zero of slots outside the middle
           bool keep[4];
 #pragma unroll
@@ -434,7 +444,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
           P[j].vz[0] &= k01;
           P[j].vz[1] &= k23;
         }
-        if (pg >= c1) continue;
+        if (!INTERIOR && pg >= c1) continue;
         const f32x4 dz = mfma_f16(u32x4{P[j].kz[0], P[j].kz[1], 0u, 0u}, bz, f32x4{0.f, 0.f, 0.f, 0.f});
         float lk[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -451,7 +461,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * pg + 4 * quad + r;
-          if (t >= m0 && t < m1) lg[j][r] = fmaf(lk[r], kTwo24, dz[r]);
+          if (INTERIOR || (t >= m0 && t < m1)) lg[j][r] = fmaf(lk[r], kTwo24, dz[r]);
         }
       }
       float pv[2][4];
@@ -476,19 +486,21 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
 
     // kDepth register stages and two LDS slots per wave: pair k is computed
     // from LDS while pairs k+1 .. k+kDepth are in flight
+    // (stage stores and loads run unconditionally, past the last pair too, so
+    // the compiler's load counting stays exact; only the compute is skipped)
     for (int k = 0; k < n_mine; k += kDepth) {
 #pragma unroll
       for (int u = 0; u < kDepth; ++u) {
         const int kk = k + u;
+        uint8_t* slot = myslots + (u & 1) * 2 * HB;
+        st[u].store(slot, lane);
+        const uint8_t *pa, *pb;
+        pair_pages(min(kk + kDepth, n_mine - 1), pa, pb);  // tail: harmless reload
+        st[u].load(pa, pb, lane);
         if (kk < n_mine) {
-          uint8_t* slot = myslots + (u & 1) * 2 * HB;
-          st[u].store(slot, lane);
-          if (kk + kDepth < n_mine) {
-            const uint8_t *pa, *pb;
-            pair_pages(kk + kDepth, pa, pb);
-            st[u].load(pa, pb, lane);
-          }
-          do_pair(kk, slot);
+          const int pg0 = c0 + 2 * (wave + kWaves * kk);
+          if (pg0 + 2 <= c1 && 16 * pg0 >= m0 && 16 * pg0 + 32 <= m1) do_pair(kk, slot, std::true_type{});
+          else do_pair(kk, slot, std::false_type{});
         }
       }
     }
@@ -503,7 +515,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     s_m[wave * 16 + l16] = m_run;
     s_l[wave * 16 + l16] = l_w;
   }
-  __syncthreads();
+  lds_barrier();
   float M = kNegInf;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w * 16 + l16]);
@@ -522,9 +534,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
       *reinterpret_cast<f32x4*>(s_res + (wave * G + l16) * D + 16 * cb + 4 * quad) = v;
     }
   }
-  __syncthreads();
+  lds_barrier();
 
-  // ---- workgroup record [m G][l G][acc G D][basis flag] -> workspace ----
+  // ---- workgroup record [m G][l G][value sums G D][basis flag] -> workspace ----
   float* rec = p.partials + ((size_t(b) * p.n_kv + h) * p.n_chunks_max + x) * size_t(p.rec_floats);
   if (tid < G) {
     float mm = kNegInf;
@@ -539,10 +551,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   }
   if (tid == 0) st_dev(rec + 2 * G + G * D, is_raw ? 1.f : 0.f);
   for (int e = tid; e < G * D; e += kThreads) {
-    float s = 0.f;
+    float a = 0.f;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) s += s_res[w * G * D + e];
-    st_dev(rec + 2 * G + e, s);
+    for (int w = 0; w < kWaves; ++w) a += s_res[w * G * D + e];
+    st_dev(rec + 2 * G + e, a);
   }
   __builtin_amdgcn_s_waitcnt(0);  // records acknowledged before the arrival is counted
   __syncthreads();
@@ -554,108 +566,108 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   if (!s_flag[8]) return;
 
   // ---- last workgroup: log-sum-exp merge of the chunk records ----
+  // The weights w_s[n] = 2^(m_s[n] - M[n]) come first, from every record's
+  // max and sum, so the value sums are added without rescaling:
+  //   out = (R_V^T-rotated sum_s w_s v_s over INT2 chunks + sum_s w_s v_s over
+  //          BF16 chunks) / sum_s w_s l_s
+  // Loads of maxima, sums, flags, the first values and R_V go out together.
   const int n_s = sp.n_chunks;
+  const float* recs = p.partials + (size_t(b) * p.n_kv + h) * p.n_chunks_max * size_t(p.rec_floats);
+  float* s_wr = s_res;                       // [kMaxChunks][16] weights of INT2 records
+  float* s_wu = s_wr + kMaxChunks * 16;      // [kMaxChunks][16] weights of BF16 records
+  float* s_red = s_wu + kMaxChunks * 16;     // [2][8 waves][16] partial max / sum
+  float* m_rot = s_red + 2 * kWaves * 16;    // [G][D] merged, rotated basis
+  float* m_raw = m_rot + G * D;              // [G][D] merged, model basis
+  constexpr int kPass = kMaxChunks * 16 / kThreads;  // (record, row) slots per thread
+  const int ms_n = tid & 15;
   const float* rv = p.r_v + size_t(h) * D * D;
-  const int cbm = wave;  // output block of this wave (NCB <= 8)
   f32x4 rva[NKB][2];
-  if (!ALL_RAW && cbm < NCB) {  // issued first; latency overlaps the merge
+  if (!ALL_RAW && wave < NCB) {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const float* src = rv + size_t(16 * cbm + l16) * D + 32 * kb + 8 * quad;
+      const float* src = rv + size_t(16 * wave + l16) * D + 32 * kb + 8 * quad;
       rva[kb][0] = *reinterpret_cast<const f32x4*>(src);
       rva[kb][1] = *reinterpret_cast<const f32x4*>(src + 4);
     }
   }
-  const float* recs = p.partials + (size_t(b) * p.n_kv + h) * p.n_chunks_max * size_t(p.rec_floats);
-  float* m_rot = s_res;
-  float* m_raw = s_res + G * D;
-  float* s_cm = s_res + 2 * G * D;        // [kMaxChunks][16] chunk maxima
-  float* s_cl = s_cm + kMaxChunks * 16;   // [kMaxChunks][16] chunk sums
-  float* s_cf = s_cl + kMaxChunks * 16;   // [kMaxChunks] basis flags
-  constexpr int EPT = (16 * 128 + kThreads - 1) / kThreads;  // output elements per thread (G*D <= 2048)
-  float Mx[EPT], Lx[EPT], sr[EPT], su[EPT];
+  float cm[kPass], cl[kPass], cf[kPass];
 #pragma unroll
-  for (int j = 0; j < EPT; ++j) { Mx[j] = kNegInf; Lx[j] = sr[j] = su[j] = 0.f; }
-  for (int s0 = 0; s0 < n_s; s0 += kMergeBatch) {
-    const int s1b = min(n_s, s0 + kMergeBatch);
-    // chunk maxima/sums/flags and this thread's value sums of the batch are
-    // requested together: one memory round trip per batch
-    const int ms_s = s0 + (tid >> 4), ms_n = tid & 15;  // record and query row this thread stages
-    const bool ms_on = ms_s < s1b && ms_n < G;
-    float cm = 0.f, cl = 0.f, cf = 0.f;
-    if (ms_on) {
-      cm = ld_dev(recs + size_t(ms_s) * p.rec_floats + ms_n);
-      cl = ld_dev(recs + size_t(ms_s) * p.rec_floats + G + ms_n);
-      cf = ld_dev(recs + size_t(ms_s) * p.rec_floats + 2 * G + G * D);
-    }
-    float vv[EPT][kMergeBatch];
+  for (int i = 0; i < kPass; ++i) {  // clamped addresses: every load is in bounds and unconditional
+    const int s = min((tid >> 4) + i * (kThreads / 16), n_s - 1), n = min(ms_n, G - 1);
+    cm[i] = ld_dev(recs + size_t(s) * p.rec_floats + n);
+    cl[i] = ld_dev(recs + size_t(s) * p.rec_floats + G + n);
+    cf[i] = ld_dev(recs + size_t(s) * p.rec_floats + 2 * G + G * D);
+  }
+  float vv[kMergeBatch];
+  auto load_batch = [&](int e0, int s0) {
+    const size_t e = size_t(2 * G + min(e0 + tid, G * D - 1));
 #pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-      const int e = tid + j * kThreads;
+    for (int k = 0; k < kMergeBatch; ++k) vv[k] = ld_dev(recs + size_t(min(s0 + k, n_s - 1)) * p.rec_floats + e);
+  };
+  load_batch(0, 0);
+  float mx = kNegInf;
 #pragma unroll
-      for (int k = 0; k < kMergeBatch; ++k)
-        vv[j][k] = (e < G * D && s0 + k < s1b) ? ld_dev(recs + size_t(s0 + k) * p.rec_floats + 2 * G + e) : 0.f;
-    }
-    if (ms_on) {
-      s_cm[ms_s * 16 + ms_n] = cm;
-      s_cl[ms_s * 16 + ms_n] = cl;
-      if (ms_n == 0) s_cf[ms_s] = cf;
-    }
-    __syncthreads();
+  for (int i = 0; i < kPass; ++i) {
+    const int s = (tid >> 4) + i * (kThreads / 16);
+    if (s < n_s && ms_n < G) mx = fmaxf(mx, cm[i]);
+  }
+  mx = wave_max16(mx);
+  if (quad == 0) s_red[wave * 16 + ms_n] = mx;
+  lds_barrier();
+  float Mn = kNegInf;
 #pragma unroll
-    for (int j = 0; j < EPT; ++j) {
-      const int e = tid + j * kThreads;
-      if (e >= G * D) continue;
-      const int n = e / D;
-      float bm = kNegInf;
-      for (int s = s0; s < s1b; ++s) bm = fmaxf(bm, s_cm[s * 16 + n]);
-      const float nm = fmaxf(Mx[j], bm);
-      if (nm == kNegInf) continue;
-      const float f = (Mx[j] == kNegInf) ? 0.f : exp2f(Mx[j] - nm);
-      Lx[j] *= f; sr[j] *= f; su[j] *= f;
-      Mx[j] = nm;
+  for (int w = 0; w < kWaves; ++w) Mn = fmaxf(Mn, s_red[w * 16 + ms_n]);
+  float lsum = 0.f;
+#pragma unroll
+  for (int i = 0; i < kPass; ++i) {
+    const int s = (tid >> 4) + i * (kThreads / 16);
+    const bool ok = s < n_s && ms_n < G && cm[i] != kNegInf;
+    const float wgt = ok ? exp2f(cm[i] - Mn) : 0.f;
+    lsum = fmaf(wgt, cl[i], lsum);
+    s_wr[s * 16 + ms_n] = cf[i] != 0.f ? 0.f : wgt;  // every slot written: zero past n_s
+    s_wu[s * 16 + ms_n] = cf[i] != 0.f ? wgt : 0.f;
+  }
+  lsum = wave_sum16(lsum);
+  if (quad == 0) s_red[128 + wave * 16 + ms_n] = lsum;
+  lds_barrier();
+  for (int e0 = 0; e0 < G * D; e0 += kThreads) {
+    const int e = e0 + tid;
+    const int n = min(e / D, 15);
+    float orot = 0.f, oraw = 0.f;
+    for (int s0 = 0; s0 < n_s; s0 += kMergeBatch) {
+      if (e0 > 0 || s0 > 0) load_batch(e0, s0);
 #pragma unroll
       for (int k = 0; k < kMergeBatch; ++k) {
-        const int s = s0 + k;
-        if (s < s1b) {
-          const float ms = s_cm[s * 16 + n];
-          if (ms != kNegInf) {
-            const float wgt = exp2f(ms - nm);
-            Lx[j] = fmaf(wgt, s_cl[s * 16 + n], Lx[j]);
-            if (s_cf[s] != 0.f) su[j] = fmaf(wgt, vv[j][k], su[j]); else sr[j] = fmaf(wgt, vv[j][k], sr[j]);
-          }
-        }
+        orot = fmaf(s_wr[(s0 + k) * 16 + n], vv[k], orot);
+        oraw = fmaf(s_wu[(s0 + k) * 16 + n], vv[k], oraw);
       }
     }
-    __syncthreads();
-  }
-#pragma unroll
-  for (int j = 0; j < EPT; ++j) {
-    const int e = tid + j * kThreads;
     if (e < G * D) {
-      const float inv = 1.f / Lx[j];
-      m_rot[e] = sr[j] * inv;
-      m_raw[e] = su[j] * inv;
+      float Ln = 0.f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) Ln += s_red[128 + w * 16 + n];
+      const float inv = 1.f / Ln;
+      m_rot[e] = orot * inv;
+      m_raw[e] = oraw * inv;
     }
   }
-  __syncthreads();
+  lds_barrier();
   // out^T[c][n] = raw[n][c] + sum_k R_V[c][k] rot[n][k]   (bf16 hi/lo splits, 3 MFMAs)
-  if (cbm < NCB) {
+  if (wave < NCB) {
     f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
     if (!ALL_RAW) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         uint32_t ah[4], al[4], bh[4], bl[4];
-        const float* rot_row = m_rot + l16 * D + 32 * kb + 8 * quad;
+        const float* rot_row = m_rot + qrow * D + 32 * kb + 8 * quad;
 #pragma unroll
         for (int k = 0; k < 8; k += 2) {
           uint32_t h0, l0, h1, l1;
           split2(rva[kb][k / 4][k % 4], h0, l0);
           split2(rva[kb][(k + 1) / 4][(k + 1) % 4], h1, l1);
           ah[k / 2] = pack2(h0, h1); al[k / 2] = pack2(l0, l1);
-          const float x0 = l16 < G ? rot_row[k] : 0.f, x1 = l16 < G ? rot_row[k + 1] : 0.f;
-          split2(x0, h0, l0);
-          split2(x1, h1, l1);
+          split2(rot_row[k], h0, l0);
+          split2(rot_row[k + 1], h1, l1);
           bh[k / 2] = pack2(h0, h1); bl[k / 2] = pack2(l0, l1);
         }
         const u32x4 AH{ah[0], ah[1], ah[2], ah[3]}, AL{al[0], al[1], al[2], al[3]};
@@ -666,8 +678,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
       }
     }
     if (l16 < G) {
-      uint16_t* o = p.out + (size_t(b) * p.Hq + hq0 + l16) * D + 16 * cbm + 4 * quad;
-      const float* rw = m_raw + l16 * D + 16 * cbm + 4 * quad;
+      uint16_t* o = p.out + (size_t(b) * p.Hq + hq0 + l16) * D + 16 * wave + 4 * quad;
+      const float* rw = m_raw + l16 * D + 16 * wave + 4 * quad;
       u32x2 ov;
       ov[0] = pack2(bf16_rne(a4[0] + rw[0]), bf16_rne(a4[1] + rw[1]));
       ov[1] = pack2(bf16_rne(a4[2] + rw[2]), bf16_rne(a4[3] + rw[3]));
@@ -697,8 +709,8 @@ int decode_chunks_max(bool all_raw, int max_seq_len, int S, int W, int split_pag
 size_t decode_lds_bytes(int d, int G, bool all_raw) {
   const int ng = d / 32;
   const size_t slots = all_raw ? 0 : size_t(kWaves) * 2 * 2 * 12 * d;
-  size_t res = size_t(kWaves) * G * d;                                             // per-wave results
-  res = std::max(res, size_t(2) * G * d + size_t(kMaxChunks) * 33);                 // merge
+  size_t res = size_t(kWaves) * G * d;                              // per-wave results
+  res = std::max(res, size_t(kMaxChunks) * 32 + 2 * kWaves * 16 + size_t(2) * G * d);  // merge
   return (size_t(ng) * 256 + 256 + 512) * 4 + slots + res * 4;
 }
 
