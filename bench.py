@@ -59,6 +59,29 @@ def algorithmic_bytes(inp, w) -> dict:
     return parts
 
 
+def measured_traffic(workload: str):
+    """HBM bytes per decode launch from the committed rocprofv3 counter summary
+    for this workload (FETCH_SIZE / WRITE_SIZE scaled by a plain-copy
+    calibration), or None when there is none or the decode sources changed
+    since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"decode_kernel_{workload}_hbm_counters.txt")
+    if not os.path.exists(path):
+        return None
+    h = hashlib.sha256()
+    for f in ["decode.hip", "device_utils.h", "layout.h"]:
+        with open(os.path.join(ROOT, "int2_rotated_kv_oscar_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    digest, traffic = None, None
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("decode sources sha256[:16] = "):
+                digest = line.split("=")[1].strip()
+            if line.startswith("traffic_bytes = "):
+                traffic = int(line.split("=")[1].strip())
+    return traffic if digest == h.hexdigest()[:16] else None
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -69,6 +92,8 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=0, help="cache copies rotated over (0: >= 1 GiB total)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run 5 plain device copies of MIB MiB (calibrates HBM byte counters), then exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the decode path shards by KV head "
@@ -84,8 +109,17 @@ def main() -> int:
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         return 1
-    lib.load()
     dev = "cuda:0"
+    if args.copy_probe:
+        n = args.copy_probe << 20
+        src = torch.ones(n, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copy probe: 5 copies of {n} B")
+        return 0
+    lib.load()
     w = synth.WORKLOADS[args.workload]
     t0 = time.time()
     inp = synth.decode_inputs(w)
@@ -183,7 +217,7 @@ def main() -> int:
                    "kv_heads": w.n_kv_heads, "head_dim": w.d, "page_tokens": 16, "sink": w.n_sink,
                    "recent": w.n_recent, "split_pages": args.split_pages or "auto", "cache_copies": copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(w.name),
                      "kernel": "decode_kernel<128,false>", "algorithmic_bytes_per_launch": nbytes["total"],
                      "avg_launch_us": round(dec_avg * 1e3, 2)},
     }
