@@ -179,7 +179,7 @@ oscar_status oscar_quantize_append(const oscar_cache* cache, const void* k_new, 
   if ((n_rows + 15) / 16 > int64_t(0x7FFFFFFF)) return fail(OSCAR_ERR_UNSUPPORTED, "n_rows too large");
   return hip_status(oscar_launch::quantize_append(cache->d, cache->n_kv_heads, cache->int2_pool, k_new, v_new, n_rows,
                                                   row_seq, row_pos, bt_q, max_pages, r_k, r_v, tau_k, tau_v,
-                                                  static_cast<hipStream_t>(stream)),
+                                                  device_cu_count(), static_cast<hipStream_t>(stream)),
                     "quantize_append launch");
 }
 

@@ -90,13 +90,37 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// Cross-row exchange without LDS: v_permlane16_swap / v_permlane32_swap on two
+// copies of v leave, in every lane, the values of rows (r, r^1) or (r, r^2) of
+// 16 lanes as the pair (first, second) in the same order for both rows, so a
+// commutative reduction of the pair is identical in both partner lanes.
+__device__ __forceinline__ void pair16(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
+__device__ __forceinline__ void pair32(float v, float& a, float& b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  a = __uint_as_float(r[0]);
+  b = __uint_as_float(r[1]);
+}
 __device__ __forceinline__ float wave_max16(float v) {  // over lanes with equal l%16
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  return fmaxf(v, __shfl_xor(v, 32, 64));
+  float a, b;
+  pair16(v, a, b);
+  pair32(fmaxf(a, b), a, b);
+  return fmaxf(a, b);
+}
+__device__ __forceinline__ float wave_min16(float v) {
+  float a, b;
+  pair16(v, a, b);
+  pair32(fminf(a, b), a, b);
+  return fminf(a, b);
 }
 __device__ __forceinline__ float wave_sum16(float v) {
-  v += __shfl_xor(v, 16, 64);
-  return v + __shfl_xor(v, 32, 64);
+  float a, b;
+  pair16(v, a, b);
+  pair32(a + b, a, b);
+  return a + b;
 }
 
 }  // namespace oscar_dev

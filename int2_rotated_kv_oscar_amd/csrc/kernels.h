@@ -10,7 +10,7 @@ namespace oscar_launch {
 hipError_t quantize_append(int d, int n_kv, void* pool, const void* k_new, const void* v_new, int64_t n_rows,
                            const int32_t* row_seq, const int32_t* row_pos, const int32_t* bt_q,
                            int32_t max_pages, const float* r_k, const float* r_v, float tau_k, float tau_v,
-                           hipStream_t stream);
+                           int n_cus, hipStream_t stream);
 
 size_t decode_lds_bytes(int d, int G, bool all_raw);
 int decode_max_splits();

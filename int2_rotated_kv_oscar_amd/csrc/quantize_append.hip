@@ -4,15 +4,19 @@
 // stored in INT2 after the fixed OSCAR rotation and clipping; [TS] 2.2.A
 // step 4 for the per-layer clip).
 //
-// One workgroup handles T tiles of 16 rows for one (KV head, tensor), one
-// wave per 32-channel group (so group statistics stay inside a wave).  The
+// A workgroup takes one (KV head, tensor) and loops over tiles of 16 rows,
+// one wave per 32-channel group (so group statistics stay inside a wave).  The
 // rotation y = x . R is a dense 16 x d x d product per tile and runs on the
 // 16x16x32 bf16 MFMA: x is exact in bf16, R (float32) is split exactly into
-// three bf16 parts, so y is float32-accurate.  K tiles use the transposed
+// three bf16 parts, so y is float32-accurate.  Tiles use the transposed
 // product y^T = R^T x^T, whose output lane layout (one row per lane, 4
-// consecutive channels per 16-channel block) is exactly the KC word layout;
-// V tiles use y = x R, whose layout (4 rows per lane, one channel per block)
-// is exactly the VC word layout.  Group statistics are cross-lane min/max.
+// consecutive channels per 16-channel block) keeps a 32-channel group inside
+// one wave over its 4 lane quads: group min/max take two cross-lane steps.
+// Codes are OR-combined into the page's word layout in LDS; a tile that is
+// one whole page is written with plain coalesced stores, scattered rows with
+// per-field atomic updates.
+#include <algorithm>
+
 #include "device_utils.h"
 #include "layout.h"
 #include "kernels.h"
@@ -36,241 +40,257 @@ struct QAParams {
   int32_t n_kv;
 };
 
-template <int D>
-__device__ __forceinline__ uint8_t* head_base(const QAParams& p, int64_t row, int h, int& slot) {
-  const int32_t s = p.row_seq[row], pos = p.row_pos[row];
-  slot = pos & 15;
-  const int64_t page = p.bt_q[int64_t(s) * p.max_pages + (pos >> 4)];
-  return p.pool + (page * p.n_kv + h) * int64_t(Geo<D>::HEAD_BYTES);
-}
-
-// Group statistics -> f16 scale/zero (RNE) and a code generator.
+// Group statistics -> f16 scale/zero (RNE) and a code generator.  s is
+// (max - min) / 3 taken as a product with fp32(1/3) and the reciprocal of the
+// stored f16 scale is the hardware approximation: both stay far inside the
+// agreement windows (1e-6 of the group range for s, 1e-5 of a step for codes).
 struct GroupQ {
   float zf, inv;
-  bool zero_scale;
   uint32_t s16, z16;
   __device__ __forceinline__ void make(float mn, float mx) {
-    const float s = (mx - mn) / 3.0f;
-    s16 = f16_bits(s);
+    s16 = f16_bits((mx - mn) * (1.0f / 3.0f));
     z16 = f16_bits(mn);
     const float sf = f16_to_f32(s16);
     zf = f16_to_f32(z16);
-    zero_scale = (sf == 0.0f);
-    inv = zero_scale ? 0.0f : 1.0f / sf;
+    inv = sf == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(sf);  // s16 = 0: every code is 0
   }
   __device__ __forceinline__ uint32_t code(float y) const {
-    if (zero_scale) return 0u;
     const float t = __builtin_rintf((y - zf) * inv);
-    return uint32_t(fminf(fmaxf(t, 0.0f), 3.0f));
+    return uint32_t(__builtin_amdgcn_fmed3f(t, 0.0f, 3.0f));
   }
 };
 
-template <int D, int T, int TENSOR>
-__device__ void qa_body(const QAParams& p, int h, int64_t tile0) {
+// Per-tile row metadata: lane l16 describes row tile*16 + l16 (all quads hold
+// the same), page -1 for rows past n_rows.
+struct TileMeta {
+  int32_t page, slot;
+  bool valid;    // the row exists (page is meaningful only then)
+  bool aligned;  // 16 consecutive positions of one sequence starting on a page boundary
+};
+
+template <int D, int TENSOR>
+__device__ void qa_tiles(const QAParams& p, int h) {
   using GG = Geo<D>;
   constexpr int NG = GG::NG, NKB = GG::NKB, NW = GG::NW;
-  // one wave per channel group; code words are OR-combined in LDS
-  __shared__ uint32_t s_words[T][64][NW];
-  const int tid = threadIdx.x, g = tid >> 6, lane = tid & 63, l16 = lane & 15, quad = lane >> 4;
+  constexpr int kDepth = 8;              // tiles in flight per workgroup
+  constexpr int kRowBytes = 2 * D + 16;  // padded LDS row of the x tile (conflict-free operand reads)
+  // x tiles (double-buffered), code words of a tile (one slot per lane,
+  // OR-combined by the NG waves) and its f16 scales/zeros in page-area order
+  __shared__ __attribute__((aligned(16))) uint8_t s_x[2][16 * kRowBytes];
+  __shared__ uint32_t s_words[2][64][NW];
+  __shared__ uint32_t s_sz[2][16 * NG];  // [scale area | zero area] as u32 pairs of f16
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, quad = lane >> 4;
+  const int g = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint16_t* X = TENSOR ? p.v_new : p.k_new;
   const float* R = (TENSOR ? p.r_v : p.r_k) + size_t(h) * D * D;
   const float tau = TENSOR ? p.tau_v : p.tau_k;
+  const int64_t n_tiles = (p.n_rows + 15) / 16;
+  const int64_t n_mine = (n_tiles - blockIdx.x + gridDim.x - 1) / gridDim.x;  // >= 1 by the grid size
 
-  for (int i = tid; i < T * 64 * NW; i += 64 * NG) (&s_words[0][0][0])[i] = 0u;
+  for (int i = tid; i < 2 * 64 * NW; i += 64 * NG) (&s_words[0][0][0])[i] = 0u;
 
-  // R operand values of this group, all issued at once: lane (c16 = l16, quad)
-  // holds R[32kb + 8quad + i][16cb + l16] for cb = 2g + hb
-  float rv[2][NKB][8];
+  // R operands of this group, split once into exact bf16 hi/mid/lo: lane
+  // (c16 = l16, quad) holds R[32kb + 8quad + i][16cb + l16], cb = 2g + hb
+  u32x4 rop[2][NKB][3];
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) rv[hb][kb][i] = R[size_t(32 * kb + 8 * quad + i) * D + 16 * (2 * g + hb) + l16];
-
-  // x operands: lane (row l16, quad) holds channels 32kb + 8quad .. +7 of its row;
-  // the same registers serve as the B operand (K) and the A operand (V).
-  u32x4 xop[T][NKB];
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
-    const int64_t row = (tile0 + t) * 16 + l16;
-#pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      if (row < p.n_rows)
-        xop[t][kb] = *reinterpret_cast<const u32x4*>(X + (row * p.n_kv + h) * D + 32 * kb + 8 * quad);
-      else
-        xop[t][kb] = u32x4{0, 0, 0, 0};
-    }
-  }
-
-  // Row metadata.  K: the lane's row is l16.  V: the lane's rows are 4quad + r.
-  uint8_t* kbase[T];
-  int kslot[T];
-  uint8_t* vbase[T][4];
-  int vslot[T][4];
-  bool aligned[T];
+      float rv[8];
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-    if (TENSOR == 0) {
-      const int64_t row = (tile0 + t) * 16 + l16;
-      kslot[t] = 0;
-      kbase[t] = row < p.n_rows ? head_base<D>(p, row, h, kslot[t]) : nullptr;
-    } else {
-      const int64_t row0 = (tile0 + t) * 16;
-      bool ok = true;
-      if (lane < 16) {
-        const int64_t row = row0 + lane;
-        ok = row < p.n_rows && p.row_seq[row] == p.row_seq[row0] && p.row_pos[row] == p.row_pos[row0] + lane &&
-             (p.row_pos[row0] & 15) == 0;
-      }
-      aligned[t] = __ballot(ok) == ~0ull;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int64_t row = row0 + 4 * quad + r;
-        vslot[t][r] = 0;
-        vbase[t][r] = row < p.n_rows ? head_base<D>(p, row, h, vslot[t][r]) : nullptr;
-      }
-    }
-  }
-
-  f32x4 acc[T][2];
-#pragma unroll
-  for (int t = 0; t < T; ++t) acc[t][0] = acc[t][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) {
-#pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
+      for (int i = 0; i < 8; ++i) rv[i] = R[size_t(32 * kb + 8 * quad + i) * D + 16 * (2 * g + hb) + l16];
       uint32_t ph[4], pm[4], pl[4];
 #pragma unroll
       for (int i = 0; i < 8; i += 2) {
-        const Split3 a = split3(rv[hb][kb][i]);
-        const Split3 b = split3(rv[hb][kb][i + 1]);
-        ph[i / 2] = pack2(a.hi, b.hi);
-        pm[i / 2] = pack2(a.mid, b.mid);
-        pl[i / 2] = pack2(a.lo, b.lo);
+        const Split3 a = split3(rv[i]), c = split3(rv[i + 1]);
+        ph[i / 2] = pack2(a.hi, c.hi);
+        pm[i / 2] = pack2(a.mid, c.mid);
+        pl[i / 2] = pack2(a.lo, c.lo);
       }
-      const u32x4 rh{ph[0], ph[1], ph[2], ph[3]}, rm{pm[0], pm[1], pm[2], pm[3]}, rl{pl[0], pl[1], pl[2], pl[3]};
+      rop[hb][kb][0] = u32x4{ph[0], ph[1], ph[2], ph[3]};
+      rop[hb][kb][1] = u32x4{pm[0], pm[1], pm[2], pm[3]};
+      rop[hb][kb][2] = u32x4{pl[0], pl[1], pl[2], pl[3]};
+    }
+
+  // The i-th tile of this workgroup (clamped: past the end repeats the last).
+  auto tile_of = [&](int64_t i) { return int64_t(blockIdx.x) + min(i, n_mine - 1) * int64_t(gridDim.x); };
+  // Ring of tiles in flight: wave g holds rows 4g .. 4g+3 of a tile (16 B per
+  // lane), every lane the position of row l16.  Rows past n_rows re-read the
+  // last row; their results are never stored.
+  constexpr int kQuarterRows = 16 / NG;        // rows of a tile per wave
+  constexpr int kChunks = 2 * D / 16;          // 16-byte chunks per row
+  static_assert(kQuarterRows * kChunks == 64, "one 16-byte chunk per lane");
+  u32x4 xr[kDepth];
+  int32_t sr[kDepth], pr[kDepth];
+  auto issue = [&](int u, int64_t i) {
+    const int64_t t = tile_of(i);
+    const int64_t xrow = min(t * 16 + kQuarterRows * g + lane / kChunks, p.n_rows - 1);
+    xr[u] = *reinterpret_cast<const u32x4*>(X + (xrow * p.n_kv + h) * D + 8 * (lane % kChunks));
+    const int64_t row = min(t * 16 + l16, p.n_rows - 1);
+    sr[u] = p.row_seq[row];
+    pr[u] = p.row_pos[row];
+  };
 #pragma unroll
-      for (int t = 0; t < T; ++t) {
-        if (TENSOR == 0) {
-          acc[t][hb] = mfma_bf16(rl, xop[t][kb], acc[t][hb]);
-          acc[t][hb] = mfma_bf16(rm, xop[t][kb], acc[t][hb]);
-          acc[t][hb] = mfma_bf16(rh, xop[t][kb], acc[t][hb]);
-        } else {
-          acc[t][hb] = mfma_bf16(xop[t][kb], rl, acc[t][hb]);
-          acc[t][hb] = mfma_bf16(xop[t][kb], rm, acc[t][hb]);
-          acc[t][hb] = mfma_bf16(xop[t][kb], rh, acc[t][hb]);
+  for (int u = 0; u < kDepth; ++u) issue(u, u);
+
+  // stores of a finished tile: wave 0 the codes (then clears its word buffer),
+  // wave 1 the scale/zero areas of an aligned tile
+  auto store_tile = [&](const TileMeta& mc, int buf) {
+    if (g == 0) {
+      if (TENSOR == 0) {
+        if (mc.valid) {  // K code words hold a single token: plain stores
+          uint8_t* base = p.pool + (int64_t(mc.page) * p.n_kv + h) * int64_t(GG::HEAD_BYTES);
+          uint32_t* kc = reinterpret_cast<uint32_t*>(base + GG::KC) + (quad * 16 + mc.slot) * NW;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) kc[w] = s_words[buf][lane][w];
+        }
+      } else if (mc.aligned) {
+        // 16 rows = slots 0..15 of one page: the words are the page's VC words
+        const int page0 = __shfl(mc.page, 0, 64);
+        uint8_t* base = p.pool + (int64_t(page0) * p.n_kv + h) * int64_t(GG::HEAD_BYTES);
+        uint32_t* vc = reinterpret_cast<uint32_t*>(base + GG::VC) + lane * NW;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) vc[w] = s_words[buf][lane][w];
+      } else {
+        // rows of different pages/slots: replace this row's 2-bit fields with
+        // an atomic xor (other rows may update other fields of the same word)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int vpage = __shfl(mc.valid ? mc.page : -1, 4 * quad + r, 64), vslot = __shfl(mc.slot, 4 * quad + r, 64);
+          if (vpage < 0) continue;
+          uint8_t* base = p.pool + (int64_t(vpage) * p.n_kv + h) * int64_t(GG::HEAD_BYTES);
+          const int sh = 16 * (vslot & 1) + 8 * ((vslot >> 1) & 1);
+          uint32_t* vc = reinterpret_cast<uint32_t*>(base + GG::VC) + ((vslot >> 2) * 16 + l16) * NW;
+#pragma unroll
+          for (int w = 0; w < NW; ++w) {
+            const uint32_t bits = ((s_words[buf][lane][w] >> (16 * (r & 1) + 8 * (r >> 1))) & 0xFFu) << sh;
+            const uint32_t mask = 0xFFu << sh;
+            const uint32_t old = __hip_atomic_load(vc + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            const uint32_t delta = (old & mask) ^ bits;
+            if (delta) atomicXor(vc + w, delta);
+          }
         }
       }
-    }
-  }
-  __syncthreads();  // s_words zeroed
-
-  // ---- epilogue for group g ----
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
+      for (int w = 0; w < NW; ++w) s_words[buf][lane][w] = 0u;
+    } else if (g == 1 && mc.aligned) {
+      // scale and zero areas of the page are contiguous: 2 x 32 NG bytes
+      const int page0 = __shfl(mc.page, 0, 64);
+      uint8_t* base = p.pool + (int64_t(page0) * p.n_kv + h) * int64_t(GG::HEAD_BYTES);
+      uint32_t* dst = reinterpret_cast<uint32_t*>(base + (TENSOR == 0 ? GG::KS : GG::VS));
+      for (int i = lane; i < 16 * NG; i += 64) dst[i] = s_sz[buf][i];
+    }
+  };
+
+  // Three-stage software pipeline over tiles: at step i the MFMAs of tile i run
+  // while the epilogue of tile i-1 (codes, scales into LDS) executes, and the
+  // words of tile i-2 are stored.  One barrier per step.
+  auto epilogue = [&](const f32x4 (&acc)[2], const TileMeta& mc, int buf) {
+    // ---- epilogue for group g: y[hb][r] = row m = l16, channel 32g + 16hb + 4quad + r ----
     float y[2][4];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) y[hb][r] = fminf(fmaxf(acc[t][hb][r], -tau), tau);
+      for (int r = 0; r < 4; ++r) y[hb][r] = __builtin_amdgcn_fmed3f(acc[hb][r], -tau, tau);
+    float mn = fminf(fminf(fminf(y[0][0], y[0][1]), fminf(y[0][2], y[0][3])),
+                     fminf(fminf(y[1][0], y[1][1]), fminf(y[1][2], y[1][3])));
+    float mx = fmaxf(fmaxf(fmaxf(y[0][0], y[0][1]), fmaxf(y[0][2], y[0][3])),
+                     fmaxf(fmaxf(y[1][0], y[1][1]), fmaxf(y[1][2], y[1][3])));
+    GroupQ q; q.make(wave_min16(mn), wave_max16(mx));
+    uint16_t* sz16 = reinterpret_cast<uint16_t*>(s_sz[buf]);
+    const int m = l16;
     if (TENSOR == 0) {
-      // y[hb][r] = row l16, channel 32g + 16hb + 4quad + r; the group spans the 4 quads
-      float mn = y[0][0], mx = y[0][0];
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) { mn = fminf(mn, y[hb][r]); mx = fmaxf(mx, y[hb][r]); }
-      mn = fminf(mn, __shfl_xor(mn, 16, 64)); mn = fminf(mn, __shfl_xor(mn, 32, 64));
-      mx = fmaxf(mx, __shfl_xor(mx, 16, 64)); mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      GroupQ q; q.make(mn, mx);
+      // KC word (quad*16 + m)*NW + g/2 belongs to this lane
       uint32_t bits = 0;
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
         for (int r = 0; r < 4; ++r) bits |= q.code(y[hb][r]) << (16 * (r & 1) + 8 * (g & 1) + 4 * hb + 2 * (r >> 1));
-      atomicOr(&s_words[t][lane][g / 2], bits);
-      if (quad == 0 && kbase[t]) {
-        reinterpret_cast<uint16_t*>(kbase[t] + GG::KS)[kslot[t] * NG + g] = uint16_t(q.s16);
-        reinterpret_cast<uint16_t*>(kbase[t] + GG::KZ)[kslot[t] * NG + g] = uint16_t(q.z16);
-      }
+      atomicOr(&s_words[buf][lane][g / 2], bits);
     } else {
-      // y[hb][r] = row 4quad + r, channel 32g + 16hb + l16; the group spans the 16 lanes
-      uint32_t bits = 0;  // 8 bits per row r: code of block bb at 2bb
+      // VC word ((m/4)*16 + c16)*NW + w, c16 = 4quad + r, w = g/2; tile row m
+      // at bit 16(m%2) + 8((m/2)%2), block bb = (2g + hb)%4 at 2bb
+      const int sh = 16 * (m & 1) + 8 * ((m >> 1) & 1);
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        float mn = fminf(y[0][r], y[1][r]), mx = fmaxf(y[0][r], y[1][r]);
-#pragma unroll
-        for (int m = 1; m < 16; m <<= 1) {
-          mn = fminf(mn, __shfl_xor(mn, m, 64));
-          mx = fmaxf(mx, __shfl_xor(mx, m, 64));
-        }
-        GroupQ q; q.make(mn, mx);
-#pragma unroll
-        for (int hb = 0; hb < 2; ++hb) bits |= q.code(y[hb][r]) << (8 * r + 2 * (2 * (g & 1) + hb));
-        if (l16 == 0 && vbase[t][r]) {
-          const int s = vslot[t][r];
-          const int idx = ((s >> 2) * NG + g) * 4 + (s & 3);
-          reinterpret_cast<uint16_t*>(vbase[t][r] + GG::VS)[idx] = uint16_t(q.s16);
-          reinterpret_cast<uint16_t*>(vbase[t][r] + GG::VZ)[idx] = uint16_t(q.z16);
-        }
+        const uint32_t bits = (q.code(y[0][r]) << (sh + 2 * ((2 * g) & 3))) |
+                              (q.code(y[1][r]) << (sh + 2 * ((2 * g + 1) & 3)));
+        atomicOr(&s_words[buf][(m >> 2) * 16 + 4 * quad + r][g / 2], bits);
       }
-      atomicOr(&s_words[t][lane][g / 2], bits);
     }
-  }
-  __syncthreads();
-  if (g != 0) return;
+    if (quad == 0) {
+      const int ia = TENSOR == 0 ? m * NG + g : ((m >> 2) * NG + g) * 4 + (m & 3);  // aligned: slot = m
+      if (mc.aligned) {
+        sz16[ia] = uint16_t(q.s16);
+        sz16[16 * NG + ia] = uint16_t(q.z16);
+      } else if (mc.valid) {
+        uint8_t* base = p.pool + (int64_t(mc.page) * p.n_kv + h) * int64_t(GG::HEAD_BYTES);
+        const int s = mc.slot;
+        const int iu = TENSOR == 0 ? s * NG + g : ((s >> 2) * NG + g) * 4 + (s & 3);
+        reinterpret_cast<uint16_t*>(base + (TENSOR == 0 ? GG::KS : GG::VS))[iu] = uint16_t(q.s16);
+        reinterpret_cast<uint16_t*>(base + (TENSOR == 0 ? GG::KZ : GG::VZ))[iu] = uint16_t(q.z16);
+      }
+    }
+  };
 
-  // ---- code stores (wave 0) ----
+  TileMeta m1 = {0, 0, false, false}, m2 = m1;
+  f32x4 accp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  __syncthreads();  // s_words zeroed
+  for (int64_t i0 = 0; i0 < n_mine + 2; i0 += kDepth) {
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-    if (TENSOR == 0) {
-      if (kbase[t]) {
-        uint32_t* kc = reinterpret_cast<uint32_t*>(kbase[t] + GG::KC) + (quad * 16 + kslot[t]) * NW;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) kc[w] = s_words[t][lane][w];
+    for (int u = 0; u < kDepth; ++u) {
+      const int64_t i = i0 + u;
+      const int buf = int(i & 1);
+      // tile i: x quarter -> LDS, positions -> page, slot, alignment
+      *reinterpret_cast<u32x4*>(&s_x[buf][(kQuarterRows * g + lane / kChunks) * kRowBytes + 16 * (lane % kChunks)]) = xr[u];
+      TileMeta mc;
+      {
+        const int64_t t = tile_of(i);
+        const int32_t seq = sr[u], pos = pr[u];
+        const bool valid = i < n_mine && t * 16 + l16 < p.n_rows;
+        mc.page = p.bt_q[int64_t(seq) * p.max_pages + (pos >> 4)];  // seq/pos of a real row
+        mc.valid = valid;
+        mc.slot = pos & 15;
+        const int32_t seq0 = __shfl(seq, 0, 64), pos0 = __shfl(pos, 0, 64);
+        const bool ok = valid && seq == seq0 && pos == pos0 + l16 && (pos0 & 15) == 0;
+        mc.aligned = (__ballot(ok) & 0xFFFFull) == 0xFFFFull;
       }
-    } else if (aligned[t]) {
-      // 16 rows = slots 0..15 of one page: the lane owns whole VC words
-      uint32_t* vc = reinterpret_cast<uint32_t*>(vbase[t][0] + GG::VC) + (quad * 16 + l16) * NW;
+      // refill the ring slot kDepth tiles ahead (clamped: always issued)
+      issue(u, i + kDepth);
+      lds_barrier();
+      // tile i-2: its LDS words are complete (buffer i&1)
+      if (i >= 2 && i - 2 < n_mine) store_tile(m2, buf);
+      f32x4 accn[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+      if (i < n_mine) {
+        u32x4 xc[NKB];
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const uint32_t b = s_words[t][lane][w];
-        uint32_t out = 0;
+        for (int kb = 0; kb < NKB; ++kb)
+          xc[kb] = *reinterpret_cast<const u32x4*>(&s_x[buf][l16 * kRowBytes + 64 * kb + 16 * quad]);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) out |= ((b >> (8 * r)) & 0xFFu) << (16 * (r & 1) + 8 * (r >> 1));
-        vc[w] = out;
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+            for (int j = 2; j >= 0; --j)  // lo, mid, hi: small terms first
+              accn[hb] = mfma_bf16(rop[hb][kb][j], xc[kb], accn[hb]);
       }
-    } else {
-      // rows of different pages/slots: replace this row's 2-bit fields with
-      // an atomic xor (other rows may update other fields of the same word)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (!vbase[t][r]) continue;
-        const int s = vslot[t][r];
-        const int sh = 16 * (s & 1) + 8 * ((s >> 1) & 1);
-        uint32_t* vc = reinterpret_cast<uint32_t*>(vbase[t][r] + GG::VC) + ((s >> 2) * 16 + l16) * NW;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) {
-          const uint32_t bits = ((s_words[t][lane][w] >> (8 * r)) & 0xFFu) << sh;
-          const uint32_t mask = 0xFFu << sh;
-          const uint32_t old = __hip_atomic_load(vc + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          const uint32_t delta = (old & mask) ^ bits;
-          if (delta) atomicXor(vc + w, delta);
-        }
-      }
+      // tile i-1: codes and scales into LDS buffer (i-1)&1
+      if (i >= 1 && i - 1 < n_mine) epilogue(accp, m1, buf ^ 1);
+      accp[0] = accn[0];
+      accp[1] = accn[1];
+      m2 = m1;
+      m1 = mc;
     }
   }
 }
 
-template <int D, int T>
+template <int D>
 __global__ __launch_bounds__(64 * (D / 32)) void quantize_append_kernel(QAParams p) {
   const int h = blockIdx.y;
-  const int64_t tile0 = int64_t(blockIdx.x) * T;
   if (blockIdx.z == 0)
-    qa_body<D, T, 0>(p, h, tile0);
+    qa_tiles<D, 0>(p, h);
   else
-    qa_body<D, T, 1>(p, h, tile0);
+    qa_tiles<D, 1>(p, h);
 }
 
 }  // namespace
@@ -280,20 +300,16 @@ namespace oscar_launch {
 hipError_t quantize_append(int d, int n_kv, void* pool, const void* k_new, const void* v_new, int64_t n_rows,
                            const int32_t* row_seq, const int32_t* row_pos, const int32_t* bt_q,
                            int32_t max_pages, const float* r_k, const float* r_v, float tau_k, float tau_v,
-                           hipStream_t stream) {
+                           int n_cus, hipStream_t stream) {
   QAParams p{static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), n_rows, row_seq, row_pos,
              bt_q, max_pages, r_k, r_v, tau_k, tau_v, static_cast<uint8_t*>(pool), n_kv};
+  // workgroups loop over tiles of 16 rows (the split rotation stays in
+  // registers); about two workgroups per CU over all (head, tensor) pairs
   const int64_t tiles = (n_rows + 15) / 16;
-  const bool big = tiles >= 4 * 256;
-  const int T = big ? 4 : 1;
-  const dim3 grid(static_cast<unsigned>((tiles + T - 1) / T), static_cast<unsigned>(n_kv), 2u);
-  if (d == 128) {
-    if (big) hipLaunchKernelGGL((quantize_append_kernel<128, 4>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((quantize_append_kernel<128, 1>), grid, dim3(256), 0, stream, p);
-  } else {
-    if (big) hipLaunchKernelGGL((quantize_append_kernel<64, 4>), grid, dim3(128), 0, stream, p);
-    else hipLaunchKernelGGL((quantize_append_kernel<64, 1>), grid, dim3(128), 0, stream, p);
-  }
+  const int64_t per_pair = std::max<int64_t>(1, (2 * int64_t(n_cus) + 2 * n_kv - 1) / (2 * n_kv));
+  const dim3 grid(static_cast<unsigned>(std::min(tiles, per_pair)), static_cast<unsigned>(n_kv), 2u);
+  if (d == 128) hipLaunchKernelGGL((quantize_append_kernel<128>), grid, dim3(256), 0, stream, p);
+  else hipLaunchKernelGGL((quantize_append_kernel<64>), grid, dim3(128), 0, stream, p);
   return hipGetLastError();
 }
 

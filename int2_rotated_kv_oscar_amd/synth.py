@@ -20,7 +20,7 @@ from __future__ import annotations
 
 import dataclasses
 import math
-from typing import List, Optional, Tuple
+from typing import List, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -223,24 +223,41 @@ def _page_flags(L: int, S: int, W: int) -> Tuple[np.ndarray, np.ndarray]:
     return overlaps(mid), overlaps(sink) | overlaps(rec)
 
 
+def _history_rng(cfg_id: int, part: int) -> np.random.Generator:
+    """K/V history stream (role 4): part 0 the shared prefix, part b + 1 the
+    own rows of sequence b, so any subset of sequences can be drawn alone."""
+    return np.random.Generator(np.random.PCG64(np.random.SeedSequence([ROOT_SEED, cfg_id, 4, part])))
+
+
 def decode_inputs(w: Workload, seq_lens: Optional[np.ndarray] = None, q_scale: Optional[float] = None,
-                  shuffle: bool = True, spare_pages: int = 0) -> DecodeInputs:
-    """Raw K/V history, block tables and one decode query per sequence."""
+                  shuffle: bool = True, spare_pages: int = 0,
+                  draw_seqs: Optional[Sequence[int]] = None) -> DecodeInputs:
+    """Raw K/V history, block tables and one decode query per sequence.
+
+    ``draw_seqs`` limits the drawn history to those sequences (and the shared
+    prefix); the own rows of the other sequences are left zero.  Drawn values
+    do not depend on the subset."""
     lens = context_lengths(w) if seq_lens is None else np.asarray(seq_lens, dtype=np.int32)
     B = len(lens)
     S, W = w.n_sink, w.n_recent
     pre = w.shared_prefix
     if pre:
         assert pre % PAGE == 0 and all(L >= pre + W + PAGE for L in lens)
-    rng = rng_for(w.cfg_id, 4)
     n_rows = pre + int(sum(int(L) - pre for L in lens))
-    k_rows, v_rows = kv_rows(rng, n_rows, w)
+    k_rows = np.zeros((n_rows, w.n_kv_heads, w.d), np.uint16)
+    v_rows = np.zeros((n_rows, w.n_kv_heads, w.d), np.uint16)
+    if pre:
+        k_rows[:pre], v_rows[:pre] = kv_rows(_history_rng(w.cfg_id, 0), pre, w)
+    drawn = set(range(B)) if draw_seqs is None else {int(b) for b in draw_seqs}
     row_of = []
     nxt = pre
-    for L in lens:
-        own = np.arange(nxt, nxt + int(L) - pre, dtype=np.int64)
+    for b, L in enumerate(lens):
+        n_own = int(L) - pre
+        own = np.arange(nxt, nxt + n_own, dtype=np.int64)
         row_of.append(np.concatenate([np.arange(pre, dtype=np.int64), own]))
-        nxt += int(L) - pre
+        if b in drawn and n_own > 0:
+            k_rows[nxt:nxt + n_own], v_rows[nxt:nxt + n_own] = kv_rows(_history_rng(w.cfg_id, b + 1), n_own, w)
+        nxt += n_own
     max_pages = max(1, (int(lens.max()) + PAGE - 1) // PAGE) if B else 1
     pre_pages = pre // PAGE
     # logical -> "virtual" page ids (shared prefix pages once), then a seeded

@@ -1,0 +1,119 @@
+"""GPU parity at the workloads' full sizes, checked on sampled outputs.
+
+Every workload is run at its real shape (sequence count, context lengths,
+head counts, shuffled and aliased block tables), in the launch configuration
+the benchmark uses (automatic split).  The cache is written by the library's
+own kernels; the oracle then
+
+* re-quantizes a random sample of the appended rows (codes bit-exact up to the
+  rounding-boundary exemption, f16 scale/zero up to the midpoint exemption),
+* decodes sampled sequences from the very pages the GPU wrote (rel-L2 <= 5e-3,
+  max-abs <= 2e-2 against its float64 output).
+
+For the batched workloads only the sampled sequences' histories are drawn;
+the others keep all-zero rows (their outputs are computed but not checked).
+"""
+import numpy as np
+import pytest
+import torch
+
+from int2_rotated_kv_oscar_amd import synth
+from oracle import cache as ocache
+from oracle import layout as olayout
+
+import gpu_helpers as gh
+
+pytestmark = pytest.mark.gpu
+
+CALIB_ROWS = 1024  # the rotation is an input of both sides; its calibration size does not matter here
+
+
+def _run(name, sample_seqs, n_code_rows=2048, seed=0):
+    w = synth.WORKLOADS[name]
+    lens = synth.context_lengths(w)
+    if sample_seqs == "all":
+        sample_seqs = list(range(len(lens)))
+    print(f"[fullsize {name}] B={len(lens)} max_len={int(lens.max())} sampled={sample_seqs}", flush=True)
+    inp = synth.decode_inputs(w, draw_seqs=sample_seqs)
+    rot = gh.oracle_rotation(w, n_rows=CALIB_ROWS)
+    gc = gh.alloc_cache(inp, rot)
+    rows = synth.middle_rows(inp)
+    print(f"[fullsize {name}] quantize_append rows={len(rows[0])}", flush=True)
+    gh.gpu_fill(inp, rot, gc, rows)
+    torch.cuda.synchronize()
+
+    # codes and scales of sampled appended rows (from the sampled sequences)
+    ms, mp, mr = rows
+    mine = np.nonzero(np.isin(ms, sample_seqs))[0]
+    rng = np.random.default_rng(seed)
+    sel = np.sort(rng.choice(mine, size=min(n_code_rows, len(mine)), replace=False))
+    k, v = inp.k_rows[mr[sel]], inp.v_rows[mr[sel]]
+    scratch = olayout.Int2Pool(inp.n_int2_pages, w.n_kv_heads, w.d)
+    res = ocache.quantize_append(scratch, k, v, ms[sel], mp[sel], inp.bt_q, rot.r_k, rot.r_v, rot.tau_k, rot.tau_v,
+                                 olayout.bf16_to_f64)
+    int2_bytes = gc.int2.cpu().numpy()
+    page = inp.bt_q[ms[sel], mp[sel] // 16].astype(np.int64)
+    rep = gh.compare_appended(int2_bytes, w, inp.n_int2_pages, res, page, (mp[sel] % 16).astype(np.int64))
+    print(rep, flush=True)
+    gh.assert_codes_ok(rep, name)
+
+    # decode (all sequences on the GPU), checked on the sampled ones
+    print(f"[fullsize {name}] decode", flush=True)
+    got = gh.gpu_decode(inp, gc, split_pages=0)
+    assert np.isfinite(got).all()
+    int2 = olayout.Int2Pool(inp.n_int2_pages, w.n_kv_heads, w.d, int2_bytes)
+    bf = olayout.Bf16Pool(inp.n_bf16_pages, w.n_kv_heads, w.d, gc.bf16.cpu().numpy().view(np.uint16))
+    from oracle import attention as oatt
+    sb = np.asarray(sample_seqs)
+    q = synth.bf16_bits_to_f32(inp.q[sb]).astype(np.float64)
+    ref = oatt.decode_attention(q, int2, bf, inp.seq_lens[sb], inp.bt_q[sb], inp.bt_h[sb], rot.r_k, rot.r_v,
+                                w.n_sink, w.n_recent)
+    err = gh.attention_errors(got[sb], ref)
+    print(f"[fullsize {name}] decode errors {err}", flush=True)
+    gh.assert_attention_close(got[sb], ref, name)
+
+
+def test_qwen3_8b_b1_32k_bench_config():
+    _run("qwen3-8b-b1-32k", "all")
+
+
+def test_qwen3_8b_b28_ragged_shared_prefix():
+    _run("qwen3-8b-b28-ragged", [0, 13, 27])
+
+
+def test_qwen3_32b_b1_128k():
+    _run("qwen3-32b-b1-128k", "all", n_code_rows=1024)
+
+
+def test_qwen3_32b_b4_128k():
+    _run("qwen3-32b-b4-128k", [2], n_code_rows=1024)
+
+
+def test_gqa96_b64_ragged():
+    _run("gqa96-b64-ragged", [5, 40])
+
+
+def test_prefill_8x8192_rows_per_sequence():
+    # the large-GQA layer's prefill: 8 sequences x 8192 rows, page-aligned chunks
+    w = synth.WORKLOADS["gqa96-b64-ragged"]
+    n_seq, chunk = 8, 8192
+    print(f"[fullsize prefill] {n_seq} x {chunk} rows", flush=True)
+    k, v, row_seq, row_pos = synth.prefill_rows(w, n_seq, chunk)
+    pages_per = (chunk + 15) // 16
+    bt_q = synth.rng_for(w.cfg_id, 7).permutation(n_seq * pages_per).astype(np.int32).reshape(n_seq, pages_per)
+    rot = gh.oracle_rotation(w, n_rows=CALIB_ROWS)
+    from int2_rotated_kv_oscar_amd import lib
+    int2 = torch.zeros(n_seq * pages_per * lib.int2_page_bytes(w.d, w.n_kv_heads), dtype=torch.uint8, device=gh.DEV)
+    cache = lib.make_cache(w.d, w.n_kv_heads, w.n_sink, w.n_recent, int2, None)
+    lib.quantize_append(cache, gh.bits_to_dev_bf16(k), gh.bits_to_dev_bf16(v), gh.i32(row_seq), gh.i32(row_pos),
+                        gh.i32(bt_q), torch.from_numpy(rot.r_k.astype(np.float32)).to(gh.DEV),
+                        torch.from_numpy(rot.r_v.astype(np.float32)).to(gh.DEV), rot.tau_k, rot.tau_v)
+    torch.cuda.synchronize()
+    sel = np.sort(np.random.default_rng(1).choice(len(row_seq), size=4096, replace=False))
+    scratch = olayout.Int2Pool(n_seq * pages_per, w.n_kv_heads, w.d)
+    res = ocache.quantize_append(scratch, k[sel], v[sel], row_seq[sel], row_pos[sel], bt_q, rot.r_k, rot.r_v,
+                                 rot.tau_k, rot.tau_v, olayout.bf16_to_f64)
+    page = bt_q[row_seq[sel], row_pos[sel] // 16].astype(np.int64)
+    rep = gh.compare_appended(int2.cpu().numpy(), w, n_seq * pages_per, res, page, (row_pos[sel] % 16).astype(np.int64))
+    print(rep, flush=True)
+    gh.assert_codes_ok(rep, "prefill 8x8192")
