@@ -72,13 +72,17 @@ int device_cu_count() {
 // Pages per INT2 chunk: enough workgroups to fill the compute units in whole
 // rounds (one 8-wave workgroup per CU at a time), at most ~128 pages of work
 // per workgroup and round, and at most decode_max_splits() / 2 chunks.
+// Automatic chunk size.  Few (sequence, KV head) units (under a quarter of the
+// CUs): one round of chunks, leaving a CU for each unit's two BF16 chunks.
+// Otherwise about eight chunks per CU for the longest possible lengths, which
+// keeps the largest chunk well below the per-CU share of a ragged batch (whose
+// real lengths only the device knows).
 int auto_split_pages(int batch, int n_kv, int max_pages) {
   const long long cus = device_cu_count();
-  const long long pages = (long long)batch * n_kv * std::max(1, max_pages);
-  const long long raw_wgs = 2LL * batch * n_kv;
-  const long long rounds = std::max(1LL, (pages + cus * 128 - 1) / (cus * 128));
-  const long long wgs = std::max(cus / 2, rounds * cus - raw_wgs);
-  long long sp = (pages + wgs - 1) / wgs;
+  const long long units = (long long)batch * n_kv;
+  const long long pages = units * std::max(1, max_pages);
+  const long long chunks = 4 * units < cus ? std::max(1LL, cus - 2 * units) : 8 * cus;
+  long long sp = (pages + chunks - 1) / chunks;
   const int cap = oscar_launch::decode_max_splits() / 2;
   sp = std::max<long long>(sp, (max_pages + cap - 1) / cap);
   sp = (sp + 7) / 8 * 8;

@@ -271,10 +271,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pv[j][r] = __builtin_amdgcn_exp2f(lg[j][r] - m_use);
-        l_part += pv[j][r];
-      }
+      for (int r = 0; r < 4; ++r) pv[j][r] = __builtin_amdgcn_exp2f(lg[j][r] - m_use);
   };
 
   if (is_raw) {
@@ -318,6 +315,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
       }
       float pv[2][4];
       softmax_step(lg, pv);
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) l_part += pv[j][r];
       if (ALL_RAW) {
         // baseline: bf16 probabilities against bf16 values
         const u32x4 bpr = {pack2(bf16_rne(pv[0][0]), bf16_rne(pv[0][1])), pack2(bf16_rne(pv[0][2]), bf16_rne(pv[0][3])),
@@ -340,11 +341,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   } else if (!ALL_RAW) {
     // ---------------- INT2 chunk ----------------
     const int n_mine = n_pairs > wave ? (n_pairs - wave + kWaves - 1) / kWaves : 0;
-    // pair k of this wave (k = -1: the chunk's first pair, always present)
+    // Page ids of this wave's pairs, 32 pairs per register block: lane L holds
+    // page 2(wave + 8k) + L%2 of pair k = 32 blk + L/2, clamped into the chunk
+    // (a pair's missing second page repeats the last one).  Reading them with
+    // readlane keeps memory waits out of the prefetch issue.
+    auto load_tab = [&](int blk) {
+      const int k = 32 * blk + (lane >> 1);
+      return btq[min(c0 + 2 * (wave + kWaves * k) + (lane & 1), c1 - 1)];
+    };
+    int tab = load_tab(0), tab_nx = load_tab(1), tab_blk = 0;
     auto pair_pages = [&](int k, const uint8_t*& pa, const uint8_t*& pb) {
-      const int pg = k < 0 ? c0 : c0 + 2 * (wave + kWaves * k);
-      pa = p.int2_pool + (size_t(btq[pg]) * p.n_kv + h) * HB;
-      pb = pg + 1 < c1 ? p.int2_pool + (size_t(btq[pg + 1]) * p.n_kv + h) * HB : pa;
+      const int i = 2 * (max(k, 0) & 31);
+      pa = p.int2_pool + (size_t(__builtin_amdgcn_readlane(tab, i)) * p.n_kv + h) * HB;
+      pb = p.int2_pool + (size_t(__builtin_amdgcn_readlane(tab, i + 1)) * p.n_kv + h) * HB;
     };
     // query-rotation operands are requested first, then the first four page
     // pairs; the rotation runs while the pages are in flight.  Wave w rotates
@@ -416,6 +425,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
       bz = u32x4{pack2(hv[0], hv[1]), pack2(hv[2], hv[3]), pack2(hv[4], hv[5]), pack2(hv[6], hv[7])};
     }
     uint8_t* myslots = s_slots + wave * 2 * 2 * HB;
+    const uint32_t ones = l16 == NG ? 0x3C003C00u : 0u;  // f16 1.0 pairs in A row NG
     // one page pair: logits, softmax, value sums
     // INTERIOR: both pages present and wholly inside the middle region (no
     // per-token masking); the general form handles the chunk edges
@@ -467,9 +477,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
       float pv[2][4];
       softmax_step(lg, pv);
       // K-slot e = 2 page + token pair, half = token parity
-      const uint32_t bp[4] = {pack_f16x2(pv[0][0], pv[0][1]), pack_f16x2(pv[0][2], pv[0][3]),
-                              pack_f16x2(pv[1][0], pv[1][1]), pack_f16x2(pv[1][2], pv[1][3])};
-      acc_z = mfma_f16(u32x4{P[0].vz[0], P[0].vz[1], P[1].vz[0], P[1].vz[1]}, u32x4{bp[0], bp[1], bp[2], bp[3]}, acc_z);
+      const uint32_t bp[4] = {pack_f16x2_rtz(pv[0][0], pv[0][1]), pack_f16x2_rtz(pv[0][2], pv[0][3]),
+                              pack_f16x2_rtz(pv[1][0], pv[1][1]), pack_f16x2_rtz(pv[1][2], pv[1][3])};
+      // zero terms (rows g < NG) and the softmax denominator (row NG: ones),
+      // both from the same f16 probabilities the value sums use
+      acc_z = mfma_f16(u32x4{P[0].vz[0] | ones, P[0].vz[1] | ones, P[1].vz[0] | ones, P[1].vz[1] | ones},
+                       u32x4{bp[0], bp[1], bp[2], bp[3]}, acc_z);
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         const u32x4 bs = {hmul2(bp[0], P[0].vs[2 * g]), hmul2(bp[1], P[0].vs[2 * g + 1]),
@@ -488,7 +501,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     // from LDS while pairs k+1 .. k+kDepth are in flight
     // (stage stores and loads run unconditionally, past the last pair too, so
     // the compiler's load counting stays exact; only the compute is skipped)
+    static_assert(32 % kDepth == 0, "a group of prefetch targets stays in one page-id block");
     for (int k = 0; k < n_mine; k += kDepth) {
+      // page-id block of this group's prefetch targets (advances one block at a time)
+      const int jb = min(k + kDepth, n_mine - 1) >> 5;
+      if (jb != tab_blk) { tab = tab_nx; tab_blk = jb; }
+      tab_nx = load_tab(tab_blk + 1);
 #pragma unroll
       for (int u = 0; u < kDepth; ++u) {
         const int kk = k + u;
@@ -507,7 +525,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   }
 
   // ---- per-wave results -> LDS, merged over the 8 waves ----
-  const float l_w = wave_sum16(l_part);
+  // row NG of the zero-term tile (lane (n, NG/4), element NG%4) holds an INT2
+  // chunk's denominator; BF16 chunks summed theirs per lane
+  const float l_w = is_raw ? wave_sum16(l_part) : __shfl(acc_z[NG & 3], l16 + 16 * (NG >> 2), 64);
   float zg[NG];
 #pragma unroll
   for (int g = 0; g < NG; ++g) zg[g] = __shfl(acc_z[g], l16, 64);  // Z[g][n] lives in lane (n, quad 0)

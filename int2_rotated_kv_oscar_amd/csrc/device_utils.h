@@ -69,6 +69,10 @@ __device__ __forceinline__ float f16_to_f32(uint32_t b) {
 __device__ __forceinline__ uint32_t pack_f16x2(float a, float b) { return pack2(f16_bits(a), f16_bits(b)); }
 
 // packed f16x2 multiply
+// Two floats -> packed f16 pair, rounded toward zero (one instruction).
+__device__ __forceinline__ uint32_t pack_f16x2_rtz(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(a, b));
+}
 __device__ __forceinline__ uint32_t hmul2(uint32_t a, uint32_t b) {
   f16x2 x = __builtin_bit_cast(f16x2, a) * __builtin_bit_cast(f16x2, b);
   return __builtin_bit_cast(uint32_t, x);
