@@ -72,13 +72,15 @@ template <int D, int TENSOR>
 __device__ void qa_tiles(const QAParams& p, int h) {
   using GG = Geo<D>;
   constexpr int NG = GG::NG, NKB = GG::NKB, NW = GG::NW;
-  constexpr int kDepth = 8;              // tiles in flight per workgroup
+  constexpr int kDepth = 4;              // tiles in flight per workgroup
+  constexpr float kRScale = 256.0f;
   constexpr int kRowBytes = 2 * D + 16;  // padded LDS row of the x tile (conflict-free operand reads)
   // x tiles (double-buffered), code words of a tile (one slot per lane,
   // OR-combined by the NG waves) and its f16 scales/zeros in page-area order
   __shared__ __attribute__((aligned(16))) uint8_t s_x[2][16 * kRowBytes];
   __shared__ uint32_t s_words[2][64][NW];
   __shared__ uint32_t s_sz[2][16 * NG];  // [scale area | zero area] as u32 pairs of f16
+  __shared__ int32_t s_rexp[2][16];       // per-row power-of-two prescale of the x tile
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, quad = lane >> 4;
   const int g = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint16_t* X = TENSOR ? p.v_new : p.k_new;
@@ -89,27 +91,26 @@ __device__ void qa_tiles(const QAParams& p, int h) {
 
   for (int i = tid; i < 2 * 64 * NW; i += 64 * NG) (&s_words[0][0][0])[i] = 0u;
 
-  // R operands of this group, split once into exact bf16 hi/mid/lo: lane
-  // (c16 = l16, quad) holds R[32kb + 8quad + i][16cb + l16], cb = 2g + hb
-  u32x4 rop[2][NKB][3];
+  // R operands of this group, split once: 256 R (a power of two keeps the
+  // low parts out of the f16 subnormal range) as f16 hi + lo, 22 significant
+  // bits; lane (c16 = l16, quad) holds R[32kb + 8quad + i][16cb + l16], cb = 2g + hb
+  u32x4 rop[2][NKB][2];
 #pragma unroll
   for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
       float rv[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) rv[i] = R[size_t(32 * kb + 8 * quad + i) * D + 16 * (2 * g + hb) + l16];
-      uint32_t ph[4], pm[4], pl[4];
+      for (int i = 0; i < 8; ++i) rv[i] = kRScale * R[size_t(32 * kb + 8 * quad + i) * D + 16 * (2 * g + hb) + l16];
+      uint32_t ph[4], pl[4];
 #pragma unroll
       for (int i = 0; i < 8; i += 2) {
-        const Split3 a = split3(rv[i]), c = split3(rv[i + 1]);
-        ph[i / 2] = pack2(a.hi, c.hi);
-        pm[i / 2] = pack2(a.mid, c.mid);
-        pl[i / 2] = pack2(a.lo, c.lo);
+        const uint32_t h0 = f16_bits(rv[i]), h1 = f16_bits(rv[i + 1]);
+        ph[i / 2] = pack2(h0, h1);
+        pl[i / 2] = pack2(f16_bits(rv[i] - f16_to_f32(h0)), f16_bits(rv[i + 1] - f16_to_f32(h1)));
       }
       rop[hb][kb][0] = u32x4{ph[0], ph[1], ph[2], ph[3]};
-      rop[hb][kb][1] = u32x4{pm[0], pm[1], pm[2], pm[3]};
-      rop[hb][kb][2] = u32x4{pl[0], pl[1], pl[2], pl[3]};
+      rop[hb][kb][1] = u32x4{pl[0], pl[1], pl[2], pl[3]};
     }
 
   // The i-th tile of this workgroup (clamped: past the end repeats the last).
@@ -185,18 +186,24 @@ __device__ void qa_tiles(const QAParams& p, int h) {
   // Three-stage software pipeline over tiles: at step i the MFMAs of tile i run
   // while the epilogue of tile i-1 (codes, scales into LDS) executes, and the
   // words of tile i-2 are stored.  One barrier per step.
-  auto epilogue = [&](const f32x4 (&acc)[2], const TileMeta& mc, int buf) {
-    // ---- epilogue for group g: y[hb][r] = row m = l16, channel 32g + 16hb + 4quad + r ----
+  auto epilogue = [&](const f32x4 (&acc)[2], const TileMeta& mc, int rexp, int buf) {
+    // ---- epilogue for group g: acc[hb][r] = y / F for row m = l16, channel
+    // 32g + 16hb + 4quad + r, F = 2^(e - 8) (R scale and row prescale); the
+    // clip, the codes and the statistics run on acc with F folded into them ----
+    const float F = __builtin_ldexpf(1.0f, rexp - 8), iF = __builtin_ldexpf(1.0f, 8 - rexp);
+    const float tc = tau * iF;
     float y[2][4];
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) y[hb][r] = __builtin_amdgcn_fmed3f(acc[hb][r], -tau, tau);
+      for (int r = 0; r < 4; ++r) y[hb][r] = __builtin_amdgcn_fmed3f(acc[hb][r], -tc, tc);
     float mn = fminf(fminf(fminf(y[0][0], y[0][1]), fminf(y[0][2], y[0][3])),
                      fminf(fminf(y[1][0], y[1][1]), fminf(y[1][2], y[1][3])));
     float mx = fmaxf(fmaxf(fmaxf(y[0][0], y[0][1]), fmaxf(y[0][2], y[0][3])),
                      fmaxf(fmaxf(y[1][0], y[1][1]), fmaxf(y[1][2], y[1][3])));
-    GroupQ q; q.make(wave_min16(mn), wave_max16(mx));
+    GroupQ q; q.make(wave_min16(mn) * F, wave_max16(mx) * F);
+    q.zf *= iF;   // codes from acc directly: (y - z) / s = (acc - z/F) / (s/F)
+    q.inv *= F;
     uint16_t* sz16 = reinterpret_cast<uint16_t*>(s_sz[buf]);
     const int m = l16;
     if (TENSOR == 0) {
@@ -210,13 +217,20 @@ __device__ void qa_tiles(const QAParams& p, int h) {
     } else {
       // VC word ((m/4)*16 + c16)*NW + w, c16 = 4quad + r, w = g/2; tile row m
       // at bit 16(m%2) + 8((m/2)%2), block bb = (2g + hb)%4 at 2bb
+      // the four rows m = 4j..4j+3 (consecutive lanes) share these words: their
+      // fields are OR-combined across the lane quartet first, then lane m
+      // writes word r = m%4, one writer per word and wave
       const int sh = 16 * (m & 1) + 8 * ((m >> 1) & 1);
+      uint32_t mine = 0;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const uint32_t bits = (q.code(y[0][r]) << (sh + 2 * ((2 * g) & 3))) |
-                              (q.code(y[1][r]) << (sh + 2 * ((2 * g + 1) & 3)));
-        atomicOr(&s_words[buf][(m >> 2) * 16 + 4 * quad + r][g / 2], bits);
+        uint32_t bits = (q.code(y[0][r]) << (sh + 2 * ((2 * g) & 3))) |
+                        (q.code(y[1][r]) << (sh + 2 * ((2 * g + 1) & 3)));
+        bits |= uint32_t(__builtin_amdgcn_mov_dpp(int(bits), 0xB1, 0xF, 0xF, false));  // lanes ^1
+        bits |= uint32_t(__builtin_amdgcn_mov_dpp(int(bits), 0x4E, 0xF, 0xF, false));  // lanes ^2
+        if ((m & 3) == r) mine = bits;
       }
+      atomicOr(&s_words[buf][(m >> 2) * 16 + 4 * quad + (m & 3)][g / 2], mine);
     }
     if (quad == 0) {
       const int ia = TENSOR == 0 ? m * NG + g : ((m >> 2) * NG + g) * 4 + (m & 3);  // aligned: slot = m
@@ -233,7 +247,38 @@ __device__ void qa_tiles(const QAParams& p, int h) {
     }
   };
 
+  // bf16 -> f16 is exact for |x| < 2^15 (down to 2^-17; smaller values round
+  // at 2^-25).  A row holding a larger value is scaled by a power of two
+  // 2^-e (e recorded per row and undone in the epilogue) before conversion.
+  auto stage_x = [&](const u32x4& v, int buf) {
+    const int row = kQuarterRows * g + lane / kChunks;
+    bool big = false;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      big |= ((v[i] & 0x7F80u) >= (142u << 7)) | (((v[i] >> 16) & 0x7F80u) >= (142u << 7));
+    u32x4 o;
+    int e = 0;
+    if (__builtin_expect(__any(big), 0)) {
+      // exponent of the row's largest value, over the row's kChunks lanes
+      int ex = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ex = max(ex, int(max(v[i] & 0x7F80u, (v[i] >> 16) & 0x7F80u) >> 7));
+#pragma unroll
+      for (int msk = 1; msk < kChunks; msk <<= 1) ex = max(ex, __shfl_xor(ex, msk, 64));
+      e = max(0, ex - 141);
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        o[i] = pack_f16x2_rtz(__builtin_ldexpf(bf16_to_f32(v[i] & 0xFFFFu), -e), __builtin_ldexpf(bf16_to_f32(v[i] >> 16), -e));
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] = pack_f16x2_rtz(bf16_to_f32(v[i] & 0xFFFFu), bf16_to_f32(v[i] >> 16));
+    }
+    *reinterpret_cast<u32x4*>(&s_x[buf][row * kRowBytes + 16 * (lane % kChunks)]) = o;
+    if (lane % kChunks == 0) s_rexp[buf][row] = e;
+  };
+
   TileMeta m1 = {0, 0, false, false}, m2 = m1;
+  int rep = 0;  // row prescale of the tile whose epilogue runs next
   f32x4 accp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   __syncthreads();  // s_words zeroed
   for (int64_t i0 = 0; i0 < n_mine + 2; i0 += kDepth) {
@@ -241,8 +286,8 @@ __device__ void qa_tiles(const QAParams& p, int h) {
     for (int u = 0; u < kDepth; ++u) {
       const int64_t i = i0 + u;
       const int buf = int(i & 1);
-      // tile i: x quarter -> LDS, positions -> page, slot, alignment
-      *reinterpret_cast<u32x4*>(&s_x[buf][(kQuarterRows * g + lane / kChunks) * kRowBytes + 16 * (lane % kChunks)]) = xr[u];
+      // tile i: x quarter -> f16 in LDS, positions -> page, slot, alignment
+      stage_x(xr[u], buf);
       TileMeta mc;
       {
         const int64_t t = tile_of(i);
@@ -271,13 +316,15 @@ __device__ void qa_tiles(const QAParams& p, int h) {
 #pragma unroll
           for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-            for (int j = 2; j >= 0; --j)  // lo, mid, hi: small terms first
-              accn[hb] = mfma_bf16(rop[hb][kb][j], xc[kb], accn[hb]);
+            for (int j = 1; j >= 0; --j)  // lo, then hi
+              accn[hb] = mfma_f16(rop[hb][kb][j], xc[kb], accn[hb]);
       }
+      const int ren = s_rexp[buf][l16];  // read now: the buffer is rewritten two steps on
       // tile i-1: codes and scales into LDS buffer (i-1)&1
-      if (i >= 1 && i - 1 < n_mine) epilogue(accp, m1, buf ^ 1);
+      if (i >= 1 && i - 1 < n_mine) epilogue(accp, m1, rep, buf ^ 1);
       accp[0] = accn[0];
       accp[1] = accn[1];
+      rep = ren;
       m2 = m1;
       m1 = mc;
     }
@@ -304,9 +351,9 @@ hipError_t quantize_append(int d, int n_kv, void* pool, const void* k_new, const
   QAParams p{static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), n_rows, row_seq, row_pos,
              bt_q, max_pages, r_k, r_v, tau_k, tau_v, static_cast<uint8_t*>(pool), n_kv};
   // workgroups loop over tiles of 16 rows (the split rotation stays in
-  // registers); about two workgroups per CU over all (head, tensor) pairs
+  // registers); about three workgroups per CU over all (head, tensor) pairs
   const int64_t tiles = (n_rows + 15) / 16;
-  const int64_t per_pair = std::max<int64_t>(1, (2 * int64_t(n_cus) + 2 * n_kv - 1) / (2 * n_kv));
+  const int64_t per_pair = std::max<int64_t>(1, (3 * int64_t(n_cus) + 2 * n_kv - 1) / (2 * n_kv));
   const dim3 grid(static_cast<unsigned>(std::min(tiles, per_pair)), static_cast<unsigned>(n_kv), 2u);
   if (d == 128) hipLaunchKernelGGL((quantize_append_kernel<128>), grid, dim3(256), 0, stream, p);
   else hipLaunchKernelGGL((quantize_append_kernel<64>), grid, dim3(128), 0, stream, p);
