@@ -251,10 +251,11 @@ static oscar_status decode_common(bool all_raw, const oscar_cache* cache, const 
   int32_t* counters = static_cast<int32_t*>(workspace);
   float* partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.counter_bytes);
   return hip_status(
-      oscar_launch::paged_decode(cache->d, all_raw, cache->int2_pool, cache->bf16_pool, cache->n_kv_heads, G,
+      oscar_launch::paged_decode(cache->d, all_raw, cache->int2_pool, cache->n_int2_pages, cache->bf16_pool, cache->n_kv_heads, G,
                                  cache->n_sink, cache->n_recent, n_q_heads, q, batch, seq_lens, all_raw ? bt_h : bt_q,
                                  bt_h, max_pages, r_k, r_v, sm_scale, plan.split_pages, plan.n_chunks, partials,
-                                 counters, plan.rec_floats, out, static_cast<hipStream_t>(stream)),
+                                 counters, plan.rec_floats, out,
+                                 4LL * batch * cache->n_kv_heads < device_cu_count(), static_cast<hipStream_t>(stream)),
       "decode launch");
 }
 

@@ -41,6 +41,7 @@ namespace {
 
 struct DecParams {
   const uint8_t* int2_pool;
+  int32_t n_int2_pages;
   const uint16_t* bf16_pool;
   int32_t n_kv, G, S, W, Hq;
   const uint16_t* q;
@@ -57,6 +58,7 @@ struct DecParams {
   int32_t rec_floats;
   int32_t n_chunks_max;
   uint16_t* out;
+  int32_t speculate;  // issue the INT2-chunk requests before reading the sequence length
 };
 
 constexpr int kWaves = 8;
@@ -220,8 +222,65 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   // wave index in a scalar register: page-table lookups become scalar loads,
   // which the vector-memory counter does not wait on
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int L = p.seq_lens[b];
   const int hq0 = h * G;
+  const int qrow = min(l16, G - 1);  // MFMA columns n >= G repeat a real head; their results are dropped
+  const uint16_t* qb = p.q + (size_t(b) * p.Hq + hq0) * D;
+  const int32_t* btq = p.bt_q + size_t(b) * p.max_pages;
+  const int32_t* bth = p.bt_h + size_t(b) * p.max_pages;
+
+  // ---- requests issued before the sequence length is known, for this
+  // workgroup as INT2 chunk x (INT2 chunks come first; chunk x starts at page
+  // S/16 + x*split_pages whatever the length): the query-rotation operands, the
+  // query, this wave's page ids and its first kDepth page pairs.  Entries past
+  // the sequence may be anything: table reads stay inside the row and page ids
+  // are clamped into the pool; such pages are never used unmasked. ----
+  constexpr int kDepth = 4;  // page pairs in flight per wave
+  const bool rot_wave = wave < NCB;
+  float rvals[NKB][8];
+  u32x4 bqv[NKB];
+  int sc0 = (p.S >> 4) + x * p.split_pages;  // INT2 chunk x's first page (re-set for late requests)
+  // Page ids of this wave's pairs, 32 pairs per register block: lane L holds
+  // page sc0 + 2(wave + 8k) + L%2 of pair k = 32 blk + L/2.  Reading them with
+  // readlane keeps memory waits out of the prefetch issue.
+  auto load_tab = [&](int blk) {
+    const int k = 32 * blk + (lane >> 1);
+    const int v = btq[min(sc0 + 2 * (wave + kWaves * k) + (lane & 1), p.max_pages - 1)];
+    return min(max(v, 0), p.n_int2_pages - 1);
+  };
+  int tab = 0, tab_nx = 0, tab_blk = 0;
+  auto pair_pages = [&](int k, const uint8_t*& pa, const uint8_t*& pb) {
+    const int i = 2 * (max(k, 0) & 31);
+    pa = p.int2_pool + (size_t(__builtin_amdgcn_readlane(tab, i)) * p.n_kv + h) * HB;
+    pb = p.int2_pool + (size_t(__builtin_amdgcn_readlane(tab, i + 1)) * p.n_kv + h) * HB;
+  };
+  PairStage<D> st[kDepth];
+  auto int2_requests = [&]() {
+    tab = load_tab(0);
+    tab_nx = load_tab(1);
+    if (rot_wave) {
+      const float* rk = p.r_k + size_t(h) * D * D;
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rvals[kb][i] = rk[size_t(32 * kb + 8 * quad + i) * D + 16 * wave + l16];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) bqv[kb] = *reinterpret_cast<const u32x4*>(qb + size_t(qrow) * D + 32 * kb + 8 * quad);
+    }
+    // page loads are issued unconditionally (a wave short of pairs loads
+    // unused pages) so that every wait for a stage counts exactly the loads
+    // issued after it instead of draining all of them
+#pragma unroll
+    for (int u = 0; u < kDepth; ++u) {
+      const uint8_t *pa, *pb;
+      pair_pages(u, pa, pb);
+      st[u].load(pa, pb, lane);
+    }
+  };
+  // speculation pays where latency dominates (few units of work); in large
+  // batches most workgroups past a short sequence's last chunk would only add traffic
+  if (!ALL_RAW && p.speculate) int2_requests();
+
+  const int L = p.seq_lens[b];
   if (L <= 0) {
     if (x == 0)
       for (int e = tid; e < G * D; e += kThreads) p.out[(size_t(b) * p.Hq + hq0) * D + e] = 0;
@@ -230,15 +289,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   const SeqPlan sp = make_plan<ALL_RAW>(p, L);
   if (x >= sp.n_chunks) return;
   const float qscale = p.sm_scale * kLog2e;
-  const int qrow = min(l16, G - 1);  // MFMA columns n >= G repeat a real head; their results are dropped
-  const uint16_t* qb = p.q + (size_t(b) * p.Hq + hq0) * D;
-  const int32_t* btq = p.bt_q + size_t(b) * p.max_pages;
-  const int32_t* bth = p.bt_h + size_t(b) * p.max_pages;
-  const bool is_raw = x < sp.n_ra + sp.n_rb;
+  // chunk order: with the early requests, INT2 chunks first (chunk x's pages
+  // do not depend on the length), then BF16 chunks of range A and of range B;
+  // without them, the BF16 chunks first
+  const int xi = p.speculate ? x : x - sp.n_ra - sp.n_rb;   // INT2 chunk index
+  const int xr = p.speculate ? x - sp.n_q : x;              // BF16 chunk index
+  const bool is_raw = xi < 0 || xi >= sp.n_q;
+  if (!ALL_RAW && !p.speculate && !is_raw) {
+    sc0 = sp.q0 + xi * p.split_pages;
+    int2_requests();
+  }
   int c0, c1;
-  if (x < sp.n_ra) { c0 = sp.ra0 + x * sp.raw_chunk; c1 = min(sp.ra1, c0 + sp.raw_chunk); }
-  else if (is_raw) { c0 = sp.rb0 + (x - sp.n_ra) * sp.raw_chunk; c1 = min(sp.rb1, c0 + sp.raw_chunk); }
-  else { c0 = sp.q0 + (x - sp.n_ra - sp.n_rb) * p.split_pages; c1 = min(sp.q1, c0 + p.split_pages); }
+  if (!is_raw) { c0 = sp.q0 + xi * p.split_pages; c1 = min(sp.q1, c0 + p.split_pages); }
+  else if (xr < sp.n_ra) { c0 = sp.ra0 + xr * sp.raw_chunk; c1 = min(sp.ra1, c0 + sp.raw_chunk); }
+  else { c0 = sp.rb0 + (xr - sp.n_ra) * sp.raw_chunk; c1 = min(sp.rb1, c0 + sp.raw_chunk); }
   const int n_pairs = (c1 - c0 + 1) >> 1;
   const int m0 = sp.m0, m1 = sp.m1, s1 = sp.s1, r0 = sp.r0;
 
@@ -341,47 +405,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   } else if (!ALL_RAW) {
     // ---------------- INT2 chunk ----------------
     const int n_mine = n_pairs > wave ? (n_pairs - wave + kWaves - 1) / kWaves : 0;
-    // Page ids of this wave's pairs, 32 pairs per register block: lane L holds
-    // page 2(wave + 8k) + L%2 of pair k = 32 blk + L/2, clamped into the chunk
-    // (a pair's missing second page repeats the last one).  Reading them with
-    // readlane keeps memory waits out of the prefetch issue.
-    auto load_tab = [&](int blk) {
-      const int k = 32 * blk + (lane >> 1);
-      return btq[min(c0 + 2 * (wave + kWaves * k) + (lane & 1), c1 - 1)];
-    };
-    int tab = load_tab(0), tab_nx = load_tab(1), tab_blk = 0;
-    auto pair_pages = [&](int k, const uint8_t*& pa, const uint8_t*& pb) {
-      const int i = 2 * (max(k, 0) & 31);
-      pa = p.int2_pool + (size_t(__builtin_amdgcn_readlane(tab, i)) * p.n_kv + h) * HB;
-      pb = p.int2_pool + (size_t(__builtin_amdgcn_readlane(tab, i + 1)) * p.n_kv + h) * HB;
-    };
-    // query-rotation operands are requested first, then the first four page
-    // pairs; the rotation runs while the pages are in flight.  Wave w rotates
-    // the 16-channel block cb = w (group w/2, half w%2) with a bf16 hi/lo
-    // split of R_K (16 significant bits; q~ is rounded to f16 afterwards).
-    const float* rk = p.r_k + size_t(h) * D * D;
-    const bool rot_wave = wave < NCB;
-    float rvals[NKB][8];
-    u32x4 bqv[NKB];
-    if (rot_wave) {
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) rvals[kb][i] = rk[size_t(32 * kb + 8 * quad + i) * D + 16 * wave + l16];
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) bqv[kb] = *reinterpret_cast<const u32x4*>(qb + size_t(qrow) * D + 32 * kb + 8 * quad);
-    }
-    // Page loads are issued unconditionally (a wave short of pairs reloads a
-    // valid pair) so that every wait for a stage counts exactly the loads
-    // issued after it instead of draining all of them.
-    constexpr int kDepth = 4;  // page pairs in flight per wave
-    PairStage<D> st[kDepth];
-#pragma unroll
-    for (int u = 0; u < kDepth; ++u) {
-      const uint8_t *pa, *pb;
-      pair_pages(min(u, n_mine - 1), pa, pb);
-      st[u].load(pa, pb, lane);
-    }
+    // the rotation of the query runs while the first page pairs are in flight:
+    // wave w rotates the 16-channel block cb = w (group w/2, half w%2) with a
+    // bf16 hi/lo split of R_K (16 significant bits; q~ is rounded to f16 afterwards)
     float* s_qsp = s_misc + 272;  // [NCB][16] per-block query sums
     if (rot_wave) {
       const int g = wave >> 1, hb = wave & 1;
@@ -590,7 +616,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   // max and sum, so the value sums are added without rescaling:
   //   out = (R_V^T-rotated sum_s w_s v_s over INT2 chunks + sum_s w_s v_s over
   //          BF16 chunks) / sum_s w_s l_s
-  // Loads of maxima, sums, flags, the first values and R_V go out together.
+  // Loads of maxima, sums, flags and the first values go out together, then R_V.
   const int n_s = sp.n_chunks;
   const float* recs = p.partials + (size_t(b) * p.n_kv + h) * p.n_chunks_max * size_t(p.rec_floats);
   float* s_wr = s_res;                       // [kMaxChunks][16] weights of INT2 records
@@ -600,16 +626,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   float* m_raw = m_rot + G * D;              // [G][D] merged, model basis
   constexpr int kPass = kMaxChunks * 16 / kThreads;  // (record, row) slots per thread
   const int ms_n = tid & 15;
-  const float* rv = p.r_v + size_t(h) * D * D;
-  f32x4 rva[NKB][2];
-  if (!ALL_RAW && wave < NCB) {
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const float* src = rv + size_t(16 * wave + l16) * D + 32 * kb + 8 * quad;
-      rva[kb][0] = *reinterpret_cast<const f32x4*>(src);
-      rva[kb][1] = *reinterpret_cast<const f32x4*>(src + 4);
-    }
-  }
   float cm[kPass], cl[kPass], cf[kPass];
 #pragma unroll
   for (int i = 0; i < kPass; ++i) {  // clamped addresses: every load is in bounds and unconditional
@@ -625,6 +641,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     for (int k = 0; k < kMergeBatch; ++k) vv[k] = ld_dev(recs + size_t(min(s0 + k, n_s - 1)) * p.rec_floats + e);
   };
   load_batch(0, 0);
+  // R_V rows of output block cb = wave, requested after the records (the
+  // weights wait only for the records; R_V is needed last)
+  const float* rv = p.r_v + size_t(h) * D * D;
+  f32x4 rva[NKB][2];
+  if (!ALL_RAW && wave < NCB) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const float* src = rv + size_t(16 * wave + l16) * D + 32 * kb + 8 * quad;
+      rva[kb][0] = *reinterpret_cast<const f32x4*>(src);
+      rva[kb][1] = *reinterpret_cast<const f32x4*>(src + 4);
+    }
+  }
   float mx = kNegInf;
 #pragma unroll
   for (int i = 0; i < kPass; ++i) {
@@ -734,14 +762,14 @@ size_t decode_lds_bytes(int d, int G, bool all_raw) {
   return (size_t(ng) * 256 + 256 + 512) * 4 + slots + res * 4;
 }
 
-hipError_t paged_decode(int d, bool all_raw, const void* int2_pool, const void* bf16_pool, int n_kv, int G, int S,
+hipError_t paged_decode(int d, bool all_raw, const void* int2_pool, int n_int2_pages, const void* bf16_pool, int n_kv, int G, int S,
                         int W, int Hq, const void* q, int batch, const int32_t* seq_lens, const int32_t* bt_q,
                         const int32_t* bt_h, int max_pages, const float* r_k, const float* r_v, float sm_scale,
                         int split_pages, int n_chunks_max, float* partials, int32_t* counters, int rec_floats,
-                        void* out, hipStream_t stream) {
-  DecParams p{static_cast<const uint8_t*>(int2_pool), static_cast<const uint16_t*>(bf16_pool), n_kv, G, S, W, Hq,
+                        void* out, bool speculate, hipStream_t stream) {
+  DecParams p{static_cast<const uint8_t*>(int2_pool), std::max(1, n_int2_pages), static_cast<const uint16_t*>(bf16_pool), n_kv, G, S, W, Hq,
               static_cast<const uint16_t*>(q), seq_lens, bt_q, bt_h, max_pages, r_k, r_v, sm_scale, split_pages,
-              partials, counters, rec_floats, n_chunks_max, static_cast<uint16_t*>(out)};
+              partials, counters, rec_floats, n_chunks_max, static_cast<uint16_t*>(out), speculate ? 1 : 0};
   const dim3 grid(static_cast<unsigned>(n_chunks_max), static_cast<unsigned>(n_kv), static_cast<unsigned>(batch));
   const size_t lds = decode_lds_bytes(d, G, all_raw);
   if (d == 128) {

@@ -16,10 +16,10 @@ size_t decode_lds_bytes(int d, int G, bool all_raw);
 int decode_max_splits();
 int decode_chunks_max(bool all_raw, int max_seq_len, int S, int W, int split_pages);
 
-hipError_t paged_decode(int d, bool all_raw, const void* int2_pool, const void* bf16_pool, int n_kv, int G, int S,
+hipError_t paged_decode(int d, bool all_raw, const void* int2_pool, int n_int2_pages, const void* bf16_pool, int n_kv, int G, int S,
                         int W, int Hq, const void* q, int batch, const int32_t* seq_lens, const int32_t* bt_q,
                         const int32_t* bt_h, int max_pages, const float* r_k, const float* r_v, float sm_scale,
                         int split_pages, int n_chunks_max, float* partials, int32_t* counters, int rec_floats,
-                        void* out, hipStream_t stream);
+                        void* out, bool speculate, hipStream_t stream);
 
 }  // namespace oscar_launch

@@ -86,6 +86,35 @@ def test_quantize_append_page_aligned_prefill(d, hkv, n_seq, chunk):
     gh.assert_codes_ok(rep, "prefill")
 
 
+def test_quantize_append_large_inputs(tiny_rot):
+    # rows holding values of magnitude 2^15 and above take the kernel's
+    # per-row power-of-two prescale (f16 staging); rows beside them do not
+    w = _tiny()
+    inp = synth.decode_inputs(w)
+    ms, mp, mr = synth.middle_rows(inp)
+    k = inp.k_rows[mr].copy()
+    v = inp.v_rows[mr].copy()
+    big = np.array([40000.0, -1.0e6, 3.0e5, 65504.0])
+    rng = np.random.default_rng(11)
+    rows = rng.choice(len(ms), size=24, replace=False)
+    for j, r in enumerate(rows):
+        c = rng.integers(0, w.d, size=2)
+        k[r, 0, c] = synth.to_bf16_bits(np.full(2, big[j % 4]))
+        v[r, 0, c[::-1]] = synth.to_bf16_bits(np.full(2, -big[(j + 1) % 4]))
+    gc = gh.alloc_cache(inp, tiny_rot)
+    print("[quantize_append large inputs]", flush=True)
+    lib.quantize_append(gc.cache, gh.bits_to_dev_bf16(k), gh.bits_to_dev_bf16(v), gh.i32(ms), gh.i32(mp), gc.bt_q,
+                        gc.r_k, gc.r_v, tiny_rot.tau_k, tiny_rot.tau_v)
+    torch.cuda.synchronize()
+    pool = olayout.Int2Pool(inp.n_int2_pages, w.n_kv_heads, w.d)
+    res = ocache.quantize_append(pool, k, v, ms, mp, inp.bt_q, tiny_rot.r_k, tiny_rot.r_v, tiny_rot.tau_k,
+                                 tiny_rot.tau_v, olayout.bf16_to_f64)
+    page, slot = _page_slot(inp, (ms, mp, mr))
+    rep = gh.compare_appended(gc.int2.cpu().numpy(), w, inp.n_int2_pages, res, page, slot)
+    print(rep)
+    gh.assert_codes_ok(rep, "large inputs")
+
+
 def test_quantize_append_scattered_single_rows(tiny_rot):
     # rows in random order: neighbouring slots of one page written by
     # different waves at once (the partial-word path)
