@@ -91,6 +91,27 @@ __device__ void qa_tiles(const QAParams& p, int h) {
 
   for (int i = tid; i < 2 * 64 * NW; i += 64 * NG) (&s_words[0][0][0])[i] = 0u;
 
+  // The i-th tile of this workgroup (clamped: past the end repeats the last).
+  auto tile_of = [&](int64_t i) { return int64_t(blockIdx.x) + min(i, n_mine - 1) * int64_t(gridDim.x); };
+  // Ring of tiles in flight: wave g holds rows 4g .. 4g+3 of a tile (16 B per
+  // lane), every lane the position of row l16.  Rows past n_rows re-read the
+  // last row; their results are never stored.
+  constexpr int kQuarterRows = 16 / NG;        // rows of a tile per wave
+  constexpr int kChunks = 2 * D / 16;          // 16-byte chunks per row
+  static_assert(kQuarterRows * kChunks == 64, "one 16-byte chunk per lane");
+  u32x4 xr[kDepth];
+  int32_t sr[kDepth], pr[kDepth];
+  auto issue = [&](int u, int64_t i) {
+    const int64_t t = tile_of(i);
+    const int64_t xrow = min(t * 16 + kQuarterRows * g + lane / kChunks, p.n_rows - 1);
+    xr[u] = *reinterpret_cast<const u32x4*>(X + (xrow * p.n_kv + h) * D + 8 * (lane % kChunks));
+    const int64_t row = min(t * 16 + l16, p.n_rows - 1);
+    sr[u] = p.row_seq[row];
+    pr[u] = p.row_pos[row];
+  };
+#pragma unroll
+  for (int u = 0; u < kDepth; ++u) issue(u, u);  // requested before R: the latencies overlap
+
   // R operands of this group, split once: 256 R (a power of two keeps the
   // low parts out of the f16 subnormal range) as f16 hi + lo, 22 significant
   // bits; lane (c16 = l16, quad) holds R[32kb + 8quad + i][16cb + l16], cb = 2g + hb
@@ -113,26 +134,6 @@ __device__ void qa_tiles(const QAParams& p, int h) {
       rop[hb][kb][1] = u32x4{pl[0], pl[1], pl[2], pl[3]};
     }
 
-  // The i-th tile of this workgroup (clamped: past the end repeats the last).
-  auto tile_of = [&](int64_t i) { return int64_t(blockIdx.x) + min(i, n_mine - 1) * int64_t(gridDim.x); };
-  // Ring of tiles in flight: wave g holds rows 4g .. 4g+3 of a tile (16 B per
-  // lane), every lane the position of row l16.  Rows past n_rows re-read the
-  // last row; their results are never stored.
-  constexpr int kQuarterRows = 16 / NG;        // rows of a tile per wave
-  constexpr int kChunks = 2 * D / 16;          // 16-byte chunks per row
-  static_assert(kQuarterRows * kChunks == 64, "one 16-byte chunk per lane");
-  u32x4 xr[kDepth];
-  int32_t sr[kDepth], pr[kDepth];
-  auto issue = [&](int u, int64_t i) {
-    const int64_t t = tile_of(i);
-    const int64_t xrow = min(t * 16 + kQuarterRows * g + lane / kChunks, p.n_rows - 1);
-    xr[u] = *reinterpret_cast<const u32x4*>(X + (xrow * p.n_kv + h) * D + 8 * (lane % kChunks));
-    const int64_t row = min(t * 16 + l16, p.n_rows - 1);
-    sr[u] = p.row_seq[row];
-    pr[u] = p.row_pos[row];
-  };
-#pragma unroll
-  for (int u = 0; u < kDepth; ++u) issue(u, u);
 
   // stores of a finished tile: wave 0 the codes (then clears its word buffer),
   // wave 1 the scale/zero areas of an aligned tile
