@@ -142,22 +142,30 @@ struct PageOps {
   uint32_t vs[2 * NG];  // V scales [quad][g][4 tokens]
   uint32_t vz[2];       // V zeros of group l16, tokens 4quad..4quad+3 (l16 < NG only)
 
-  __device__ __forceinline__ void read(const uint8_t* base, int l16, int quad) {
+  __device__ __forceinline__ void read_k(const uint8_t* base, int l16, int quad) {
     using GG = Geo<D>;
     const uint32_t* kcp = reinterpret_cast<const uint32_t*>(base + GG::KC) + (quad * 16 + l16) * NW;
-    const uint32_t* vcp = reinterpret_cast<const uint32_t*>(base + GG::VC) + (quad * 16 + l16) * NW;
     const uint32_t* ksp = reinterpret_cast<const uint32_t*>(base + GG::KS) + quad * 2 * NG;
-    const uint32_t* vsp = reinterpret_cast<const uint32_t*>(base + GG::VS) + quad * 2 * NG;
 #pragma unroll
-    for (int i = 0; i < NW; ++i) { kc[i] = kcp[i]; vc[i] = vcp[i]; }
+    for (int i = 0; i < NW; ++i) kc[i] = kcp[i];
 #pragma unroll
-    for (int i = 0; i < 2 * NG; ++i) { ks[i] = ksp[i]; vs[i] = vsp[i]; }
-    kz[0] = kz[1] = vz[0] = vz[1] = 0;
+    for (int i = 0; i < 2 * NG; ++i) ks[i] = ksp[i];
+    kz[0] = kz[1] = 0;
     if (quad < 2) {
       const uint32_t* kzp = reinterpret_cast<const uint32_t*>(base + GG::KZ) + l16 * (NG / 2);
       kz[0] = kzp[0];
       if (NG == 4) kz[1] = kzp[1];
     }
+  }
+  __device__ __forceinline__ void read_v(const uint8_t* base, int l16, int quad) {
+    using GG = Geo<D>;
+    const uint32_t* vcp = reinterpret_cast<const uint32_t*>(base + GG::VC) + (quad * 16 + l16) * NW;
+    const uint32_t* vsp = reinterpret_cast<const uint32_t*>(base + GG::VS) + quad * 2 * NG;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) vc[i] = vcp[i];
+#pragma unroll
+    for (int i = 0; i < 2 * NG; ++i) vs[i] = vsp[i];
+    vz[0] = vz[1] = 0;
     if (l16 < NG) {
       const uint32_t* vzp = reinterpret_cast<const uint32_t*>(base + GG::VZ) + (quad * NG + l16) * 2;
       vz[0] = vzp[0];
@@ -314,9 +322,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
 
   // online-softmax step shared by both chunk kinds: logits lg (log2 units,
   // -inf = masked) -> probabilities pv, accumulators rescaled as needed
-  auto softmax_step = [&](float (&lg)[2][4], float (&pv)[2][4]) {
-    float mx = fmaxf(fmaxf(fmaxf(lg[0][0], lg[0][1]), fmaxf(lg[0][2], lg[0][3])),
-                     fmaxf(fmaxf(lg[1][0], lg[1][1]), fmaxf(lg[1][2], lg[1][3])));
+  auto softmax_step = [&](auto& lg, auto& pv) {
+    constexpr int NP = sizeof(lg) / sizeof(lg[0]);  // pages of logits
+    float mx = kNegInf;
+#pragma unroll
+    for (int j = 0; j < NP; ++j)
+      mx = fmaxf(mx, fmaxf(fmaxf(lg[j][0], lg[j][1]), fmaxf(lg[j][2], lg[j][3])));
     mx = wave_max16(mx);
     // lazy rescaling: the reference max moves only when a logit exceeds it
     // by more than kSlack (probabilities stay <= 2^kSlack, safe in f16)
@@ -333,7 +344,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     // here unless the logits themselves are not; masked logits (-inf) give 0
     const float m_use = (m_run == kNegInf) ? 0.f : m_run;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < NP; ++j)
 #pragma unroll
       for (int r = 0; r < 4; ++r) pv[j][r] = __builtin_amdgcn_exp2f(lg[j][r] - m_use);
   };
@@ -453,98 +464,119 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     uint8_t* myslots = s_slots + wave * 2 * 2 * HB;
     const uint32_t ones = l16 == NG ? 0x3C003C00u : 0u;  // f16 1.0 pairs in A row NG
     // one page pair: logits, softmax, value sums
-    // INTERIOR: both pages present and wholly inside the middle region (no
-    // per-token masking); the general form handles the chunk edges
-    auto do_pair = [&](int k, const uint8_t* slot, auto interior_tag) {
+    // Two page pairs per step (pair k from slot A, pair k+1 from slot B): K
+    // operands and logits of the four pages, one softmax step over their 64
+    // tokens, then V operands and value sums pair by pair.  INTERIOR: all four
+    // pages present and wholly inside the middle region (no per-token masking).
+    auto page_of = [&](int k, int j) { return c0 + 2 * (wave + kWaves * k) + j; };
+    auto page_live = [&](int pg) { return pg < c1; };
+    auto do_two = [&](int k, const uint8_t* sa, const uint8_t* sb, bool has_b, auto interior_tag) {
       constexpr bool INTERIOR = decltype(interior_tag)::value;
-      const int pg0 = c0 + 2 * (wave + kWaves * k);
-      float lg[2][4];
-      PageOps<D> P[2];
+      float lg[4][4];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int pg = pg0 + j;
-        P[j].read(slot + j * HB, l16, quad);
+      for (int jj = 0; jj < 4; ++jj) {
+        const int pg = page_of(k + (jj >> 1), jj & 1);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) lg[j][r] = kNegInf;
-        if (!INTERIOR && (pg >= c1 || 16 * pg < m0 || 16 * pg + 16 > m1)) {
-          // boundary (or absent) page: clear scale/zero of slots outside the middle
-          bool keep[4];
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = 16 * pg + 4 * quad + r;
-            keep[r] = pg < c1 && t >= m0 && t < m1;
-          }
-          const uint32_t k01 = pair_keep(keep[0], keep[1]), k23 = pair_keep(keep[2], keep[3]);
-#pragma unroll
-          for (int g = 0; g < NG; ++g) { P[j].vs[2 * g] &= k01; P[j].vs[2 * g + 1] &= k23; }
-          P[j].vz[0] &= k01;
-          P[j].vz[1] &= k23;
-        }
-        if (!INTERIOR && pg >= c1) continue;
-        const f32x4 dz = mfma_f16(u32x4{P[j].kz[0], P[j].kz[1], 0u, 0u}, bz, f32x4{0.f, 0.f, 0.f, 0.f});
+        for (int r = 0; r < 4; ++r) lg[jj][r] = kNegInf;
+        if (jj >= 2 && !has_b) continue;
+        if (!INTERIOR && !page_live(pg)) continue;
+        PageOps<D> P;
+        P.read_k((jj < 2 ? sa : sb) + (jj & 1) * HB, l16, quad);
+        const f32x4 dz = mfma_f16(u32x4{P.kz[0], P.kz[1], 0u, 0u}, bz, f32x4{0.f, 0.f, 0.f, 0.f});
         float lk[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
-          const uint32_t src = (g & 1) ? shr8_halves(P[j].kc[g >> 1]) : P[j].kc[g >> 1];
+          const uint32_t src = (g & 1) ? shr8_halves(P.kc[g >> 1]) : P.kc[g >> 1];
           const u32x4 a = {src & 0x00030003u, src & 0x000C000Cu, src & 0x00300030u, src & 0x00C000C0u};
           const f32x4 dg = mfma_f16(a, bq[g], f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int idx = r * NG + g;  // scale of token 4quad + r, group g
-            lk[r] = fmaf(dg[r], f16_to_f32(P[j].ks[idx >> 1] >> (16 * (idx & 1))), lk[r]);
+            lk[r] = fmaf(dg[r], f16_to_f32(P.ks[idx >> 1] >> (16 * (idx & 1))), lk[r]);
           }
         }
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * pg + 4 * quad + r;
-          if (INTERIOR || (t >= m0 && t < m1)) lg[j][r] = fmaf(lk[r], kTwo24, dz[r]);
+          if (INTERIOR || (t >= m0 && t < m1)) lg[jj][r] = fmaf(lk[r], kTwo24, dz[r]);
         }
       }
-      float pv[2][4];
+      float pv[4][4];
       softmax_step(lg, pv);
-      // K-slot e = 2 page + token pair, half = token parity
-      const uint32_t bp[4] = {pack_f16x2_rtz(pv[0][0], pv[0][1]), pack_f16x2_rtz(pv[0][2], pv[0][3]),
-                              pack_f16x2_rtz(pv[1][0], pv[1][1]), pack_f16x2_rtz(pv[1][2], pv[1][3])};
-      // zero terms (rows g < NG) and the softmax denominator (row NG: ones),
-      // both from the same f16 probabilities the value sums use
-      acc_z = mfma_f16(u32x4{P[0].vz[0] | ones, P[0].vz[1] | ones, P[1].vz[0] | ones, P[1].vz[1] | ones},
-                       u32x4{bp[0], bp[1], bp[2], bp[3]}, acc_z);
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-        const u32x4 bs = {hmul2(bp[0], P[0].vs[2 * g]), hmul2(bp[1], P[0].vs[2 * g + 1]),
-                          hmul2(bp[2], P[1].vs[2 * g]), hmul2(bp[3], P[1].vs[2 * g + 1])};
+      for (int pr = 0; pr < 2; ++pr) {
+        if (pr == 1 && !has_b) break;
+        const uint8_t* slot = pr ? sb : sa;
+        PageOps<D> P[2];
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
-          const int cb = 2 * g + hb, w = cb >> 2, bb = cb & 3;
-          const uint32_t m = 0x00030003u << (2 * bb);
-          const u32x4 a = {P[0].vc[w] & m, shr8_halves(P[0].vc[w]) & m, P[1].vc[w] & m, shr8_halves(P[1].vc[w]) & m};
-          acc[cb] = mfma_f16(a, bs, acc[cb]);
+        for (int j = 0; j < 2; ++j) {
+          P[j].read_v(slot + j * HB, l16, quad);
+          const int pg = page_of(k + pr, j);
+          if (!INTERIOR && (!page_live(pg) || 16 * pg < m0 || 16 * pg + 16 > m1)) {
+            // boundary (or absent) page: clear scale/zero of slots outside the middle
+            bool keep[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int t = 16 * pg + 4 * quad + r;
+              keep[r] = page_live(pg) && t >= m0 && t < m1;
+            }
+            const uint32_t k01 = pair_keep(keep[0], keep[1]), k23 = pair_keep(keep[2], keep[3]);
+#pragma unroll
+            for (int g = 0; g < NG; ++g) { P[j].vs[2 * g] &= k01; P[j].vs[2 * g + 1] &= k23; }
+            P[j].vz[0] &= k01;
+            P[j].vz[1] &= k23;
+          }
+        }
+        // K-slot e = 2 page + token pair, half = token parity
+        const uint32_t bp[4] = {pack_f16x2_rtz(pv[2 * pr][0], pv[2 * pr][1]), pack_f16x2_rtz(pv[2 * pr][2], pv[2 * pr][3]),
+                                pack_f16x2_rtz(pv[2 * pr + 1][0], pv[2 * pr + 1][1]),
+                                pack_f16x2_rtz(pv[2 * pr + 1][2], pv[2 * pr + 1][3])};
+        // zero terms (rows g < NG) and the softmax denominator (row NG: ones),
+        // both from the same f16 probabilities the value sums use
+        acc_z = mfma_f16(u32x4{P[0].vz[0] | ones, P[0].vz[1] | ones, P[1].vz[0] | ones, P[1].vz[1] | ones},
+                         u32x4{bp[0], bp[1], bp[2], bp[3]}, acc_z);
+#pragma unroll
+        for (int g = 0; g < NG; ++g) {
+          const u32x4 bs = {hmul2(bp[0], P[0].vs[2 * g]), hmul2(bp[1], P[0].vs[2 * g + 1]),
+                            hmul2(bp[2], P[1].vs[2 * g]), hmul2(bp[3], P[1].vs[2 * g + 1])};
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            const int cb = 2 * g + hb, w = cb >> 2, bb = cb & 3;
+            const uint32_t m = 0x00030003u << (2 * bb);
+            const u32x4 a = {P[0].vc[w] & m, shr8_halves(P[0].vc[w]) & m, P[1].vc[w] & m, shr8_halves(P[1].vc[w]) & m};
+            acc[cb] = mfma_f16(a, bs, acc[cb]);
+          }
         }
       }
     };
 
-    // kDepth register stages and two LDS slots per wave: pair k is computed
-    // from LDS while pairs k+1 .. k+kDepth are in flight
+    // kDepth register stages and two LDS slots per wave: pairs k, k+1 are
+    // computed from the two slots while pairs k+2 .. k+kDepth+1 are in flight
     // (stage stores and loads run unconditionally, past the last pair too, so
     // the compiler's load counting stays exact; only the compute is skipped)
-    static_assert(32 % kDepth == 0, "a group of prefetch targets stays in one page-id block");
+    static_assert(32 % kDepth == 0 && kDepth % 2 == 0, "page-id blocks and pair steps");
     for (int k = 0; k < n_mine; k += kDepth) {
       // page-id block of this group's prefetch targets (advances one block at a time)
       const int jb = min(k + kDepth, n_mine - 1) >> 5;
       if (jb != tab_blk) { tab = tab_nx; tab_blk = jb; }
       tab_nx = load_tab(tab_blk + 1);
 #pragma unroll
-      for (int u = 0; u < kDepth; ++u) {
+      for (int u = 0; u < kDepth; u += 2) {
         const int kk = k + u;
-        uint8_t* slot = myslots + (u & 1) * 2 * HB;
-        st[u].store(slot, lane);
-        const uint8_t *pa, *pb;
-        pair_pages(min(kk + kDepth, n_mine - 1), pa, pb);  // tail: harmless reload
-        st[u].load(pa, pb, lane);
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+          st[u + v].store(myslots + v * 2 * HB, lane);
+          const uint8_t *pa, *pb;
+          pair_pages(min(kk + v + kDepth, n_mine - 1), pa, pb);  // tail: harmless reload
+          st[u + v].load(pa, pb, lane);
+        }
         if (kk < n_mine) {
-          const int pg0 = c0 + 2 * (wave + kWaves * kk);
-          if (pg0 + 2 <= c1 && 16 * pg0 >= m0 && 16 * pg0 + 32 <= m1) do_pair(kk, slot, std::true_type{});
-          else do_pair(kk, slot, std::false_type{});
+          const bool has_b = kk + 1 < n_mine;
+          const int pg0 = page_of(kk, 0), pg3 = page_of(kk + 1, 1);
+          const bool interior = has_b && pg3 + 1 <= c1 && 16 * pg0 >= m0 && 16 * pg3 + 16 <= m1 &&
+                                page_of(kk, 1) + 1 <= c1 && 16 * page_of(kk + 1, 0) >= m0;
+          if (interior) do_two(kk, myslots, myslots + 2 * HB, true, std::true_type{});
+          else do_two(kk, myslots, myslots + 2 * HB, has_b, std::false_type{});
         }
       }
     }
