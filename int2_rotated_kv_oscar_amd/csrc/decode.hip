@@ -658,13 +658,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   float* m_raw = m_rot + G * D;              // [G][D] merged, model basis
   constexpr int kPass = kMaxChunks * 16 / kThreads;  // (record, row) slots per thread
   const int ms_n = tid & 15;
+  const int n_pass = (n_s * 16 + kThreads - 1) / kThreads;  // passes holding real records
   float cm[kPass], cl[kPass], cf[kPass];
 #pragma unroll
-  for (int i = 0; i < kPass; ++i) {  // clamped addresses: every load is in bounds and unconditional
-    const int s = min((tid >> 4) + i * (kThreads / 16), n_s - 1), n = min(ms_n, G - 1);
-    cm[i] = ld_dev(recs + size_t(s) * p.rec_floats + n);
-    cl[i] = ld_dev(recs + size_t(s) * p.rec_floats + G + n);
-    cf[i] = ld_dev(recs + size_t(s) * p.rec_floats + 2 * G + G * D);
+  for (int i = 0; i < kPass; ++i) {  // clamped addresses: every load is in bounds
+    cm[i] = kNegInf;
+    cl[i] = cf[i] = 0.f;
+    if (i < n_pass) {
+      const int s = min((tid >> 4) + i * (kThreads / 16), n_s - 1), n = min(ms_n, G - 1);
+      cm[i] = ld_dev(recs + size_t(s) * p.rec_floats + n);
+      cl[i] = ld_dev(recs + size_t(s) * p.rec_floats + G + n);
+      cf[i] = ld_dev(recs + size_t(s) * p.rec_floats + 2 * G + G * D);
+    }
   }
   float vv[kMergeBatch];
   auto load_batch = [&](int e0, int s0) {
