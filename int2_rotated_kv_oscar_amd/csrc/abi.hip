@@ -46,16 +46,17 @@ oscar_status check_cache(const oscar_cache* c, bool need_int2, bool need_bf16) {
   return OSCAR_OK;
 }
 
-// Chunk planning shared by the workspace query and the decode calls.
+// Decode work planning shared by the workspace query and the decode calls.
 struct DecodePlan {
-  int split_pages;
-  int n_chunks;     // grid x: chunks per (sequence, KV head)
+  bool per_unit;    // per-unit items, or balanced slices over all units
+  int unit_items;   // per-unit items: workgroups per (sequence, KV head)
+  int fixed_ppw;    // per-unit items: pages per item; slices: pages per slice (0: spread evenly)
+  int n_wg;         // workgroups in the grid
+  int cap;          // record slots per (sequence, KV head)
   int rec_floats;
   size_t counter_bytes;
   size_t bytes;
 };
-
-constexpr int kRawChunkPages = 16;  // pages per BF16 chunk (matches the decode kernel)
 
 int device_cu_count() {
   static int cached[64] = {0};
@@ -69,49 +70,60 @@ int device_cu_count() {
   return cached[dev];
 }
 
-// Pages per INT2 chunk: enough workgroups to fill the compute units in whole
-// rounds (one 8-wave workgroup per CU at a time), at most ~128 pages of work
-// per workgroup and round, and at most decode_max_splits() / 2 chunks.
-// Automatic chunk size.  Few (sequence, KV head) units (under a quarter of the
-// CUs): one round of chunks, leaving a CU for each unit's two BF16 chunks.
-// Otherwise about eight chunks per CU for the longest possible lengths, which
-// keeps the largest chunk well below the per-CU share of a ragged batch (whose
-// real lengths only the device knows).
-int auto_split_pages(int batch, int n_kv, int max_pages) {
-  const long long cus = device_cu_count();
-  const long long units = (long long)batch * n_kv;
-  const long long pages = units * std::max(1, max_pages);
-  const long long chunks = 4 * units < cus ? std::max(1LL, cus - 2 * units) : 8 * cus;
-  long long sp = (pages + chunks - 1) / chunks;
-  const int cap = oscar_launch::decode_max_splits() / 2;
-  sp = std::max<long long>(sp, (max_pages + cap - 1) / cap);
-  sp = (sp + 7) / 8 * 8;
-  return int(std::min<long long>(4096, std::max<long long>(16, sp)));
-}
-
-// exact == false: a bound valid for every n_sink / n_recent (workspace query)
+// The grid (one 8-wave workgroup fits a CU).
+// * split_pages > 0: per-unit items of split_pages pages each.
+// * Automatic, few units (at most a quarter of the CUs): per-unit items sized
+//   so that one round fills the CUs: one BF16 item per unit and the INT2
+//   pages of all units spread over the remaining CUs (for the longest
+//   possible lengths).  One segment per workgroup keeps the latency chain
+//   short.
+// * Automatic, many units: one workgroup per CU, each taking an even share
+//   of all units' pages (balanced slices), whatever the device-side lengths;
+//   about three record slots per workgroup a unit could span, at least 8 (the
+//   kernel widens the slices where a unit would need more).
+// A sequence covers at most n_pages + 2 pages of work (the pages at the two
+// ends of the INT2 range also hold BF16 tokens).
 oscar_status plan_decode(int32_t batch, int32_t n_kv, int32_t n_q, int32_t d, int32_t max_seq_len,
-                         int32_t split_pages, bool exact, bool all_raw, int32_t S, int32_t W, DecodePlan* plan) {
+                         int32_t split_pages, bool all_raw, DecodePlan* plan) {
   if (batch < 0 || max_seq_len < 0) return fail(OSCAR_ERR_INVALID_ARG, "negative batch or max_seq_len");
   if (!supported_d(d)) return fail(OSCAR_ERR_UNSUPPORTED, "d must be 64 or 128");
   if (n_kv < 1 || n_q < 1 || n_q % n_kv) return fail(OSCAR_ERR_INVALID_ARG, "n_q_heads must be a positive multiple of n_kv_heads");
   const int G = n_q / n_kv;
   if (G > 16) return fail(OSCAR_ERR_UNSUPPORTED, "query group size above 16");
-  if (split_pages != 0 && (split_pages < 8 || split_pages > 4096 || split_pages % 8))
-    return fail(OSCAR_ERR_INVALID_ARG, "split_pages must be 0 or a multiple of 8 in [8, 4096]");
-  const int max_pages = (max_seq_len + 15) / 16;
-  plan->split_pages = split_pages ? split_pages : auto_split_pages(batch, n_kv, max_pages);
-  const int n_int2 = (max_pages + plan->split_pages - 1) / plan->split_pages;
-  if (exact) {
-    plan->n_chunks = oscar_launch::decode_chunks_max(all_raw, max_seq_len, S, W, plan->split_pages);
-    if (plan->n_chunks > oscar_launch::decode_max_splits())
-      return fail(OSCAR_ERR_UNSUPPORTED, "more than 256 chunks per sequence; use a larger split_pages");
+  if (split_pages != 0 && (split_pages < 8 || split_pages > 1 << 20 || split_pages % 8))
+    return fail(OSCAR_ERR_INVALID_ARG, "split_pages must be 0 or a multiple of 8 in [8, 2^20]");
+  const long long units = (long long)batch * n_kv;
+  const long long max_pages = (max_seq_len + 15LL) / 16;
+  const long long max_cost = max_pages + 2;
+  if (units * max_cost >= (1LL << 31)) return fail(OSCAR_ERR_UNSUPPORTED, "2^31 or more pages of work in one call; split the batch");
+  const int max_rec = oscar_launch::decode_max_records();
+  const long long cus = device_cu_count();
+  plan->per_unit = split_pages != 0 || 4 * units <= cus;
+  if (plan->per_unit) {
+    long long split = split_pages;
+    if (!split) {
+      const long long items = std::max(1LL, all_raw ? cus : cus - units);
+      split = std::max<long long>(oscar_launch::decode_min_slice(), (units * max_pages + items - 1) / items);
+      split = std::max(split, (max_pages + max_rec - 2) / (max_rec - 1));
+      split += split & 1;
+    }
+    const long long n_items = 1 + (max_pages + split - 1) / split;
+    if (n_items > max_rec) return fail(OSCAR_ERR_UNSUPPORTED, "more than 256 chunks per (sequence, KV head); use a larger split_pages");
+    if (units * n_items > (1LL << 31) - 1) return fail(OSCAR_ERR_UNSUPPORTED, "grid too large; use a larger split_pages");
+    plan->fixed_ppw = int(split);
+    plan->unit_items = int(n_items);
+    plan->cap = int(n_items);
+    plan->n_wg = int(std::max(1LL, units * n_items));
   } else {
-    plan->n_chunks = std::max(1, n_int2 + (max_pages + kRawChunkPages - 1) / kRawChunkPages + 1);
+    plan->fixed_ppw = 0;
+    plan->unit_items = 0;
+    plan->n_wg = int(cus);
+    const long long per = (3 * cus + units - 1) / units + 3;
+    plan->cap = int(std::min<long long>(max_rec, std::max(8LL, per)));
   }
   plan->rec_floats = (2 * G + G * d + 1 + 3) / 4 * 4;  // [max G][sum G][value sums G d][basis flag]
-  plan->counter_bytes = (size_t(batch) * n_kv * 4 + 255) / 256 * 256;
-  plan->bytes = plan->counter_bytes + size_t(batch) * n_kv * plan->n_chunks * plan->rec_floats * 4;
+  plan->counter_bytes = (size_t(units) * 4 + 255) / 256 * 256;
+  plan->bytes = plan->counter_bytes + size_t(units) * plan->cap * plan->rec_floats * 4;
   return OSCAR_OK;
 }
 
@@ -208,10 +220,12 @@ oscar_status oscar_decode_workspace_bytes(int32_t batch, int32_t n_kv_heads, int
                                           int32_t max_seq_len, int32_t split_pages, size_t* bytes) {
   oscar::clear_error();
   if (!bytes) return fail(OSCAR_ERR_INVALID_ARG, "bytes is NULL");
-  DecodePlan plan;
-  if (oscar_status s = plan_decode(batch, n_kv_heads, n_q_heads, d, max_seq_len, split_pages, false, false, 0, 0, &plan))
+  DecodePlan plan, plan_raw;  // valid for the mixed cache and the all-BF16 decode
+  if (oscar_status s = plan_decode(batch, n_kv_heads, n_q_heads, d, max_seq_len, split_pages, false, &plan))
     return s;
-  *bytes = plan.bytes;
+  if (oscar_status s = plan_decode(batch, n_kv_heads, n_q_heads, d, max_seq_len, split_pages, true, &plan_raw))
+    return s;
+  *bytes = std::max(plan.bytes, plan_raw.bytes);
   return OSCAR_OK;
 }
 
@@ -235,8 +249,7 @@ static oscar_status decode_common(bool all_raw, const oscar_cache* cache, const 
   oscar::clear_error();
   if (oscar_status s = check_cache(cache, !all_raw, true)) return s;
   DecodePlan plan;
-  if (oscar_status s = plan_decode(batch, cache->n_kv_heads, n_q_heads, cache->d, max_seq_len, split_pages, true,
-                                   all_raw, cache->n_sink, cache->n_recent, &plan))
+  if (oscar_status s = plan_decode(batch, cache->n_kv_heads, n_q_heads, cache->d, max_seq_len, split_pages, all_raw, &plan))
     return s;
   if (batch == 0) return OSCAR_OK;
   if (!q || !seq_lens || !bt_h || !out || (!all_raw && (!bt_q || !r_k || !r_v)))
@@ -253,8 +266,8 @@ static oscar_status decode_common(bool all_raw, const oscar_cache* cache, const 
   return hip_status(
       oscar_launch::paged_decode(cache->d, all_raw, cache->int2_pool, cache->n_int2_pages, cache->bf16_pool, cache->n_kv_heads, G,
                                  cache->n_sink, cache->n_recent, n_q_heads, q, batch, seq_lens, all_raw ? bt_h : bt_q,
-                                 bt_h, max_pages, r_k, r_v, sm_scale, plan.split_pages, plan.n_chunks, partials,
-                                 counters, plan.rec_floats, out,
+                                 bt_h, max_pages, r_k, r_v, sm_scale, plan.per_unit, plan.unit_items, plan.fixed_ppw,
+                                 plan.n_wg, plan.cap, max_seq_len, partials, counters, plan.rec_floats, out,
                                  4LL * batch * cache->n_kv_heads < device_cu_count(), static_cast<hipStream_t>(stream)),
       "decode launch");
 }

@@ -52,19 +52,23 @@ struct DecParams {
   const float* r_k;
   const float* r_v;
   float sm_scale;
-  int32_t split_pages;
+  int32_t fixed_ppw;  // per-unit items: pages per item; balanced slices: pages per slice (0: spread evenly)
   float* partials;
   int32_t* counters;
   int32_t rec_floats;
-  int32_t n_chunks_max;
+  int32_t cap;        // record slots per (sequence, KV head)
   uint16_t* out;
-  int32_t speculate;  // issue the INT2-chunk requests before reading the sequence length
+  int32_t speculate;  // issue the first INT2 requests before reading the sequence lengths
+  int32_t max_seq_len;
+  int32_t batch;
+  int32_t per_unit;    // per-unit items (1) or balanced slices (0)
+  int32_t unit_items;  // per-unit items: workgroups per (sequence, KV head)
 };
 
 constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRawChunk = 16;     // pages per BF16 chunk of the mixed cache
-constexpr int kMaxChunks = 256;   // chunks per (sequence, KV head)
+constexpr int kMaxChunks = 256;   // records (segments) per (sequence, KV head)
+constexpr int kMinSlice = 16;     // pages per workgroup slice at least (a page pair per wave)
 constexpr int kMergeBatch = 32;   // chunk records loaded per merge round
 static_assert(kMaxChunks * 16 % kThreads == 0, "merge: (record, query row) slots split evenly over threads");
 constexpr float kTwo24 = 16777216.0f;
@@ -92,12 +96,13 @@ __device__ __forceinline__ uint32_t pair_keep(bool k0, bool k1) {
   return (k0 ? 0x0000FFFFu : 0u) | (k1 ? 0xFFFF0000u : 0u);
 }
 
-// Chunk plan of one sequence: BF16 page ranges A and B (sink, recent; one
-// range when they meet), the INT2 page range, and their chunk counts.
+// Page plan of one sequence: BF16 page ranges A and B (sink, recent; one
+// range when they meet) and the INT2 page range.  Its work, in pages, is the
+// BF16 pages (A then B) followed by the INT2 pages.
 struct SeqPlan {
   int L, n_pages, s1, m0, m1, r0;
   int ra0, ra1, rb0, rb1, q0, q1;
-  int n_ra, n_rb, n_q, n_chunks, raw_chunk;
+  int n_raw, cost;  // BF16 pages; BF16 + INT2 pages
 };
 
 template <bool ALL_RAW>
@@ -111,7 +116,6 @@ __device__ __forceinline__ SeqPlan make_plan(const DecParams& p, int L) {
   sp.r0 = ALL_RAW ? L : max(p.S, L - p.W);
   if (ALL_RAW) {
     sp.ra0 = 0; sp.ra1 = sp.n_pages; sp.rb0 = sp.rb1 = 0; sp.q0 = sp.q1 = 0;
-    sp.raw_chunk = p.split_pages;
   } else {
     const int hs1 = (sp.s1 + 15) >> 4;                       // pages holding sink tokens
     const int hr0 = sp.r0 < L ? (sp.r0 >> 4) : sp.n_pages;   // first page holding a recent token
@@ -122,13 +126,21 @@ __device__ __forceinline__ SeqPlan make_plan(const DecParams& p, int L) {
     }
     if (sp.m1 > sp.m0) { sp.q0 = sp.m0 >> 4; sp.q1 = (sp.m1 + 15) >> 4; }
     else { sp.q0 = sp.q1 = 0; }
-    sp.raw_chunk = kRawChunk;
   }
-  sp.n_ra = (sp.ra1 - sp.ra0 + sp.raw_chunk - 1) / sp.raw_chunk;
-  sp.n_rb = (sp.rb1 - sp.rb0 + sp.raw_chunk - 1) / sp.raw_chunk;
-  sp.n_q = (sp.q1 - sp.q0 + p.split_pages - 1) / p.split_pages;
-  sp.n_chunks = sp.n_ra + sp.n_rb + sp.n_q;
+  sp.n_raw = (sp.ra1 - sp.ra0) + (sp.rb1 - sp.rb0);
+  sp.cost = sp.n_raw + (sp.q1 - sp.q0);
   return sp;
+}
+
+// Pages per workgroup slice: the total spread evenly over the grid, but
+// large enough that no unit is cut into more than cap - 3 slices (its
+// records then fit in cap slots) and that every wave gets a page pair.
+// Positions stay below 2^31 (the host bounds the work of one call).
+__device__ __forceinline__ int slice_pages(const DecParams& p, int total, int max_cost) {
+  if (p.fixed_ppw) return p.fixed_ppw;
+  const int even = int((static_cast<long long>(total) + gridDim.x - 1) / gridDim.x);
+  const int fit = (max_cost + p.cap - 4) / (p.cap - 3);
+  return max(max(even, fit), kMinSlice);
 }
 
 // Operands one lane needs from one INT2 page-head image (global or LDS).
@@ -225,28 +237,36 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   // s_res: per-wave results [8][G][D]; in the last workgroup: merged [G][D] rot
   // and [G][D] raw
 
-  const int x = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, quad = lane >> 4;
   // wave index in a scalar register: page-table lookups become scalar loads,
   // which the vector-memory counter does not wait on
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int hq0 = h * G;
+  const int wg = blockIdx.x;
   const int qrow = min(l16, G - 1);  // MFMA columns n >= G repeat a real head; their results are dropped
-  const uint16_t* qb = p.q + (size_t(b) * p.Hq + hq0) * D;
-  const int32_t* btq = p.bt_q + size_t(b) * p.max_pages;
-  const int32_t* bth = p.bt_h + size_t(b) * p.max_pages;
+  const float qscale = p.sm_scale * kLog2e;
 
-  // ---- requests issued before the sequence length is known, for this
-  // workgroup as INT2 chunk x (INT2 chunks come first; chunk x starts at page
-  // S/16 + x*split_pages whatever the length): the query-rotation operands, the
-  // query, this wave's page ids and its first kDepth page pairs.  Entries past
-  // the sequence may be anything: table reads stay inside the row and page ids
-  // are clamped into the pool; such pages are never used unmasked. ----
+  // the (sequence, KV head) unit of the current segment
+  int b = 0, h = 0;
+  const uint16_t* qb = p.q;
+  const int32_t* btq = p.bt_q;
+  const int32_t* bth = p.bt_h;
+  auto set_unit = [&](int bb, int hh) {
+    b = bb;
+    h = hh;
+    qb = p.q + (size_t(b) * p.Hq + h * G) * D;
+    btq = p.bt_q + size_t(b) * p.max_pages;
+    bth = p.bt_h + size_t(b) * p.max_pages;
+  };
+
+  // ---- requests of an INT2 segment starting at page sc0: the query-rotation
+  // operands, the query, this wave's page ids and its first kDepth page pairs.
+  // Entries past the segment may be anything: table reads stay inside the row
+  // and page ids are clamped into the pool; such pages are never used unmasked. ----
   constexpr int kDepth = 4;  // page pairs in flight per wave
   const bool rot_wave = wave < NCB;
   float rvals[NKB][8];
   u32x4 bqv[NKB];
-  int sc0 = (p.S >> 4) + x * p.split_pages;  // INT2 chunk x's first page (re-set for late requests)
+  int sc0 = 0;  // first page of the segment the requests are for
   // Page ids of this wave's pairs, 32 pairs per register block: lane L holds
   // page sc0 + 2(wave + 8k) + L%2 of pair k = 32 blk + L/2.  Reading them with
   // readlane keeps memory waits out of the prefetch issue.
@@ -263,14 +283,15 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   };
   PairStage<D> st[kDepth];
   auto int2_requests = [&]() {
+    tab_blk = 0;
     tab = load_tab(0);
     tab_nx = load_tab(1);
-    if (rot_wave) {
+    {  // every wave loads (waves past NCB repeat a block) so that no path leaves them unset
       const float* rk = p.r_k + size_t(h) * D * D;
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) rvals[kb][i] = rk[size_t(32 * kb + 8 * quad + i) * D + 16 * wave + l16];
+        for (int i = 0; i < 8; ++i) rvals[kb][i] = rk[size_t(32 * kb + 8 * quad + i) * D + 16 * (wave & (NCB - 1)) + l16];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) bqv[kb] = *reinterpret_cast<const u32x4*>(qb + size_t(qrow) * D + 32 * kb + 8 * quad);
     }
@@ -284,33 +305,36 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
       st[u].load(pa, pb, lane);
     }
   };
-  // speculation pays where latency dominates (few units of work); in large
-  // batches most workgroups past a short sequence's last chunk would only add traffic
-  if (!ALL_RAW && p.speculate) int2_requests();
 
-  const int L = p.seq_lens[b];
-  if (L <= 0) {
-    if (x == 0)
-      for (int e = tid; e < G * D; e += kThreads) p.out[(size_t(b) * p.Hq + hq0) * D + e] = 0;
-    return;
-  }
-  const SeqPlan sp = make_plan<ALL_RAW>(p, L);
-  if (x >= sp.n_chunks) return;
-  const float qscale = p.sm_scale * kLog2e;
-  // chunk order: with the early requests, INT2 chunks first (chunk x's pages
-  // do not depend on the length), then BF16 chunks of range A and of range B;
-  // without them, the BF16 chunks first
-  const int xi = p.speculate ? x : x - sp.n_ra - sp.n_rb;   // INT2 chunk index
-  const int xr = p.speculate ? x - sp.n_q : x;              // BF16 chunk index
-  const bool is_raw = xi < 0 || xi >= sp.n_q;
-  if (!ALL_RAW && !p.speculate && !is_raw) {
-    sc0 = sp.q0 + xi * p.split_pages;
+  // ---- work layout ----
+  const int units = p.batch * p.n_kv;
+  bool spec_issued = false;  // INT2 requests issued before the lengths were known
+  int spec_b = 0, spec_h = 0;
+  auto speculate_at = [&](int bb, int hh, int page) {
+    set_unit(bb, hh);
+    sc0 = page;
     int2_requests();
-  }
-  int c0, c1;
-  if (!is_raw) { c0 = sp.q0 + xi * p.split_pages; c1 = min(sp.q1, c0 + p.split_pages); }
-  else if (xr < sp.n_ra) { c0 = sp.ra0 + xr * sp.raw_chunk; c1 = min(sp.ra1, c0 + sp.raw_chunk); }
-  else { c0 = sp.rb0 + (xr - sp.n_ra) * sp.raw_chunk; c1 = min(sp.rb1, c0 + sp.raw_chunk); }
+    spec_issued = true;
+    spec_b = bb;
+    spec_h = hh;
+  };
+  SeqPlan sp;
+  // ---------------- one segment of unit (b, h) ----------------
+  // INT2 (!is_raw): pages [c0, c1).  BF16: positions [c0, c1) in the list of
+  // the sequence's BF16 pages (range A, then range B).  The segment leaves
+  // record kseg of the unit's nseg.  The first segment of a workgroup is a
+  // separate instance: only it can use the early requests, so no request
+  // registers stay live from one segment to the next.
+  auto segment = [&](auto first_tag, const bool is_raw, const int c0, const int c1, const int nseg,
+                     const int kseg) __attribute__((always_inline)) {
+  constexpr bool FIRST = decltype(first_tag)::value;
+  // lane indices re-derived per segment through an opaque copy: addresses
+  // built from them are then computed where they are used instead of being
+  // hoisted out of the segment loop and kept live through the page loop
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
+  const int lane = tid & 63, l16 = lane & 15, quad = lane >> 4;
+  const int qrow = min(l16, G - 1);
   const int n_pairs = (c1 - c0 + 1) >> 1;
   const int m0 = sp.m0, m1 = sp.m1, s1 = sp.s1, r0 = sp.r0;
 
@@ -354,18 +378,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     u32x4 bqr[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) bqr[kb] = *reinterpret_cast<const u32x4*>(qb + size_t(qrow) * D + 32 * kb + 8 * quad);
+    const int n_a = sp.ra1 - sp.ra0;
     for (int pr = wave; pr < n_pairs; pr += kWaves) {
-      const int pg0 = c0 + 2 * pr;
       float lg[2][4];
       uint32_t vraw[2][NCB][2];
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const int pg = pg0 + j;
+        const int vi = c0 + 2 * pr + j;
+        const int pg = vi < n_a ? sp.ra0 + vi : sp.rb0 + (vi - n_a);
 #pragma unroll
         for (int r = 0; r < 4; ++r) lg[j][r] = kNegInf;
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) vraw[j][cb][0] = vraw[j][cb][1] = 0;
-        if (pg >= c1) continue;
+        if (vi >= c1) continue;
         const uint16_t* hbase = p.bf16_pool + (size_t(bth[pg]) * p.n_kv + h) * GG::BF16_HEAD_ELEMS;
         f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -381,7 +406,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = 16 * pg + 4 * quad + r;
-          keep[r] = t < s1 || (t >= r0 && t < L);
+          keep[r] = t < s1 || (t >= r0 && t < sp.L);
           if (keep[r]) lg[j][r] = d[r] * qscale;
         }
         const uint32_t k01 = pair_keep(keep[0], keep[1]), k23 = pair_keep(keep[2], keep[3]);
@@ -414,7 +439,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
       }
     }
   } else if (!ALL_RAW) {
-    // ---------------- INT2 chunk ----------------
+    // ---------------- INT2 segment ----------------
+    if (!(FIRST && spec_issued && spec_b == b && spec_h == h && sc0 == c0)) {
+      sc0 = c0;
+      int2_requests();
+    }
     const int n_mine = n_pairs > wave ? (n_pairs - wave + kWaves - 1) / kWaves : 0;
     // the rotation of the query runs while the first page pairs are in flight:
     // wave w rotates the 16-channel block cb = w (group w/2, half w%2) with a
@@ -615,7 +644,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   lds_barrier();
 
   // ---- workgroup record [m G][l G][value sums G D][basis flag] -> workspace ----
-  float* rec = p.partials + ((size_t(b) * p.n_kv + h) * p.n_chunks_max + x) * size_t(p.rec_floats);
+  float* rec = p.partials + ((size_t(b) * p.n_kv + h) * p.cap + kseg) * size_t(p.rec_floats);
   if (tid < G) {
     float mm = kNegInf;
     for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, s_m[w * 16 + tid]);
@@ -638,10 +667,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   __syncthreads();
   if (tid == 0) {
     const int old = __hip_atomic_fetch_add(p.counters + b * p.n_kv + h, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_flag[8] = (old == sp.n_chunks - 1) ? 1 : 0;
+    s_flag[8] = (old == nseg - 1) ? 1 : 0;
   }
   __syncthreads();
-  if (!s_flag[8]) return;
+  if (s_flag[8]) {
 
   // ---- last workgroup: log-sum-exp merge of the chunk records ----
   // The weights w_s[n] = 2^(m_s[n] - M[n]) come first, from every record's
@@ -649,8 +678,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   //   out = (R_V^T-rotated sum_s w_s v_s over INT2 chunks + sum_s w_s v_s over
   //          BF16 chunks) / sum_s w_s l_s
   // Loads of maxima, sums, flags and the first values go out together, then R_V.
-  const int n_s = sp.n_chunks;
-  const float* recs = p.partials + (size_t(b) * p.n_kv + h) * p.n_chunks_max * size_t(p.rec_floats);
+  const int n_s = nseg;
+  const float* recs = p.partials + (size_t(b) * p.n_kv + h) * p.cap * size_t(p.rec_floats);
   float* s_wr = s_res;                       // [kMaxChunks][16] weights of INT2 records
   float* s_wu = s_wr + kMaxChunks * 16;      // [kMaxChunks][16] weights of BF16 records
   float* s_red = s_wu + kMaxChunks * 16;     // [2][8 waves][16] partial max / sum
@@ -763,7 +792,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
       }
     }
     if (l16 < G) {
-      uint16_t* o = p.out + (size_t(b) * p.Hq + hq0 + l16) * D + 16 * wave + 4 * quad;
+      uint16_t* o = p.out + (size_t(b) * p.Hq + h * G + l16) * D + 16 * wave + 4 * quad;
       const float* rw = m_raw + l16 * D + 16 * wave + 4 * quad;
       u32x2 ov;
       ov[0] = pack2(bf16_rne(a4[0] + rw[0]), bf16_rne(a4[1] + rw[1]));
@@ -772,24 +801,175 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     }
   }
   if (tid == 0) __hip_atomic_store(p.counters + b * p.n_kv + h, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }  // merge
+  };
+
+  if (p.per_unit) {
+    // Per-unit items (few units): workgroup wg is item x of unit u.  Item 0
+    // takes the unit's BF16 pages, item x >= 1 INT2 pages
+    // [q0 + (x-1) split, q0 + x split) (for the all-BF16 cache: item x takes
+    // BF16 positions [x split, (x+1) split)).  INT2 items do not depend on the
+    // length, so their requests go out before it is read.
+    const int per = p.unit_items, split = p.fixed_ppw;
+    const int u = wg / per, x = wg - u * per;
+    set_unit(u / p.n_kv, u - (u / p.n_kv) * p.n_kv);
+    if (!ALL_RAW && p.speculate && x >= 1) speculate_at(b, h, (p.S >> 4) + (x - 1) * split);
+    const int L = p.seq_lens[b];
+    if (L <= 0) {
+      if (x == 0 && h == 0)
+        for (int e = tid; e < p.Hq * D; e += kThreads) p.out[size_t(b) * p.Hq * D + e] = 0;
+      return;
+    }
+    sp = make_plan<ALL_RAW>(p, L);
+    if (ALL_RAW) {
+      const int nseg = (sp.n_raw + split - 1) / split;
+      if (x >= nseg) return;
+      segment(std::true_type{}, true, x * split, min(sp.n_raw, (x + 1) * split), nseg, x);
+      return;
+    }
+    const int has_raw = sp.n_raw > 0 ? 1 : 0, nq = (sp.q1 - sp.q0 + split - 1) / split;
+    if (x == 0 ? !has_raw : x - 1 >= nq) return;
+    const int q0 = sp.q0 + (x - 1) * split;
+    segment(std::true_type{}, x == 0, x == 0 ? 0 : q0, x == 0 ? sp.n_raw : min(sp.q1, q0 + split), has_raw + nq,
+            x == 0 ? 0 : has_raw + x - 1);
+    return;
+  }
+
+  // Balanced slices (many units): the units, sequence-major, put their pages
+  // (BF16 sink and recent pages, then INT2 pages) in one row; workgroup wg
+  // takes the slice [wg ppw, wg ppw + ppw) of it.  A segment is the part of a
+  // slice inside one unit and one page kind; each leaves one record, and the
+  // unit's last segment to finish merges its records.
+  // Early requests: assume every length is max_seq_len and issue the first
+  // segment's INT2 requests before the lengths arrive.
+  if (!ALL_RAW && p.speculate) {
+    const SeqPlan sp0 = make_plan<false>(p, p.max_seq_len);
+    const int c = sp0.cost;
+    const int total0 = units * c;
+    const long long lo0 = (long long)wg * slice_pages(p, total0, c);
+    if (c > 0 && lo0 < total0) {
+      const int u = int(lo0) / c, off = int(lo0) - u * c;
+      if (off >= sp0.n_raw) speculate_at(u / p.n_kv, u % p.n_kv, sp0.q0 + off - sp0.n_raw);
+    }
+  }
+
+  // page counts of the sequences: thread t sums a block of them; a block
+  // scan gives each block's first position
+  int* s_scan = reinterpret_cast<int*>(s_res);  // [8] wave totals, [8] owner's first position
+  int* s_scani = reinterpret_cast<int*>(s_scan + 16);       // [8] wave max cost, [8] all-full flags, [16] owner
+  const int seq_blk = (p.batch + kThreads - 1) / kThreads;
+  int v = 0;
+  int cmax = 0;
+  bool full = true;
+  {
+    const int b0 = tid * seq_blk, b1 = min(p.batch, b0 + seq_blk);
+    for (int bb = b0; bb < b1; ++bb) {
+      const int L = p.seq_lens[bb];
+      const int c = make_plan<ALL_RAW>(p, max(L, 0)).cost;
+      v += p.n_kv * c;
+      cmax = max(cmax, c);
+      full = full && L == p.max_seq_len;
+      if (L <= 0 && wg == 0) {  // no tokens: zero output
+        u32x4* o = reinterpret_cast<u32x4*>(p.out + size_t(bb) * p.Hq * D);
+        for (int e = 0; e < p.Hq * D / 8; ++e) o[e] = u32x4{0, 0, 0, 0};
+      }
+    }
+  }
+  int inc = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int t = __shfl_up(inc, o, 64);
+    if (lane >= o) inc += t;
+  }
+  int wmax = cmax;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) wmax = max(wmax, __shfl_xor(wmax, o, 64));
+  const bool wfull = __all(full);
+  if (lane == 63) s_scan[wave] = inc;
+  if (lane == 0) {
+    s_scani[wave] = wmax;
+    s_scani[8 + wave] = wfull ? 1 : 0;
+  }
+  lds_barrier();
+  int total = 0, woff = 0;
+  int max_cost = 0, n_full = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) {
+    const int t = s_scan[w];
+    woff += w < wave ? t : 0;
+    total += t;
+    max_cost = max(max_cost, s_scani[w]);
+    n_full += s_scani[8 + w];
+  }
+  // workgroup-uniform values read from LDS: scalar registers from here on
+  total = __builtin_amdgcn_readfirstlane(total);
+  max_cost = __builtin_amdgcn_readfirstlane(max_cost);
+  const bool all_full = __builtin_amdgcn_readfirstlane(n_full) == kWaves;
+  const int ppw = slice_pages(p, total, max_cost);
+  if ((long long)wg * ppw >= total) return;
+  const int lo = wg * ppw;
+  const int hi = int(min((long long)total, (long long)lo + ppw));
+  const int excl = woff + inc - v;  // first position of this thread's sequences
+  if (v > 0 && excl <= lo && lo < excl + v) {
+    s_scan[8] = excl;
+    s_scani[16] = tid;
+  }
+  lds_barrier();
+  // walk the owner's block to the unit holding position lo
+  int Cu = __builtin_amdgcn_readfirstlane(s_scan[8]);
+  {
+    int bb = __builtin_amdgcn_readfirstlane(s_scani[16]) * seq_blk;
+    sp = make_plan<ALL_RAW>(p, max(p.seq_lens[bb], 0));
+    while (Cu + p.n_kv * sp.cost <= lo) {
+      Cu += p.n_kv * sp.cost;
+      ++bb;
+      sp = make_plan<ALL_RAW>(p, max(p.seq_lens[bb], 0));
+    }
+    const int hh = int((lo - Cu) / sp.cost);
+    Cu += hh * sp.cost;
+    set_unit(bb, hh);
+  }
+
+  int pos = lo;
+  auto run = [&](auto first_tag) __attribute__((always_inline)) {
+    const int raw_end = Cu + sp.n_raw, u_end = Cu + sp.cost;
+    const bool is_raw = pos < raw_end;
+    const int seg_end = min(hi, is_raw ? raw_end : u_end);
+    const int n_raw_seg = sp.n_raw > 0 ? (raw_end - 1) / ppw - Cu / ppw + 1 : 0;
+    const int nseg = n_raw_seg + (sp.cost > sp.n_raw ? (u_end - 1) / ppw - raw_end / ppw + 1 : 0);
+    const int kseg = is_raw ? wg - Cu / ppw : n_raw_seg + wg - raw_end / ppw;
+    segment(first_tag, is_raw, is_raw ? pos - Cu : sp.q0 + (pos - raw_end),
+            is_raw ? seg_end - Cu : sp.q0 + (seg_end - raw_end), nseg, kseg);
+    pos = seg_end;
+    if (pos >= hi) return false;
+    if (pos >= u_end) {  // next unit with pages
+      Cu = u_end;
+      if (h + 1 < p.n_kv) {
+        set_unit(b, h + 1);
+      } else {
+        int bb = b;
+        do {
+          ++bb;
+          sp = make_plan<ALL_RAW>(p, max(p.seq_lens[bb], 0));
+        } while (sp.cost == 0);
+        set_unit(bb, 0);
+      }
+    }
+    lds_barrier();  // LDS of this segment's merge is rewritten by the next segment
+    return true;
+  };
+  if (run(std::true_type{}))
+    while (run(std::false_type{})) {
+    }
 }
 
 }  // namespace
 
 namespace oscar_launch {
 
-int decode_max_splits() { return kMaxChunks; }
+int decode_max_records() { return kMaxChunks; }
 
-// chunks per (sequence, KV head) that a length <= max_seq_len can need
-int decode_chunks_max(bool all_raw, int max_seq_len, int S, int W, int split_pages) {
-  const int max_pages = (max_seq_len + 15) / 16;
-  if (all_raw) return std::max(1, (max_pages + split_pages - 1) / split_pages);
-  const int sink_pages = std::min(max_pages, (S + 15) / 16);
-  const int rec_pages = std::min(max_pages, (W + 15) / 16 + 1);
-  const int raw = std::max((sink_pages + kRawChunk - 1) / kRawChunk + (rec_pages + kRawChunk - 1) / kRawChunk,
-                           (std::min(max_pages, sink_pages + rec_pages) + kRawChunk - 1) / kRawChunk);
-  return std::max(1, raw + (max_pages + split_pages - 1) / split_pages);
-}
+int decode_min_slice() { return kMinSlice; }
 
 size_t decode_lds_bytes(int d, int G, bool all_raw) {
   const int ng = d / 32;
@@ -802,12 +982,14 @@ size_t decode_lds_bytes(int d, int G, bool all_raw) {
 hipError_t paged_decode(int d, bool all_raw, const void* int2_pool, int n_int2_pages, const void* bf16_pool, int n_kv, int G, int S,
                         int W, int Hq, const void* q, int batch, const int32_t* seq_lens, const int32_t* bt_q,
                         const int32_t* bt_h, int max_pages, const float* r_k, const float* r_v, float sm_scale,
-                        int split_pages, int n_chunks_max, float* partials, int32_t* counters, int rec_floats,
-                        void* out, bool speculate, hipStream_t stream) {
+                        bool per_unit, int unit_items, int fixed_ppw, int n_wg, int cap, int max_seq_len,
+                        float* partials, int32_t* counters, int rec_floats, void* out, bool speculate,
+                        hipStream_t stream) {
   DecParams p{static_cast<const uint8_t*>(int2_pool), std::max(1, n_int2_pages), static_cast<const uint16_t*>(bf16_pool), n_kv, G, S, W, Hq,
-              static_cast<const uint16_t*>(q), seq_lens, bt_q, bt_h, max_pages, r_k, r_v, sm_scale, split_pages,
-              partials, counters, rec_floats, n_chunks_max, static_cast<uint16_t*>(out), speculate ? 1 : 0};
-  const dim3 grid(static_cast<unsigned>(n_chunks_max), static_cast<unsigned>(n_kv), static_cast<unsigned>(batch));
+              static_cast<const uint16_t*>(q), seq_lens, bt_q, bt_h, max_pages, r_k, r_v, sm_scale, fixed_ppw,
+              partials, counters, rec_floats, cap, static_cast<uint16_t*>(out), speculate ? 1 : 0, max_seq_len, batch,
+              per_unit ? 1 : 0, unit_items};
+  const dim3 grid(static_cast<unsigned>(n_wg));
   const size_t lds = decode_lds_bytes(d, G, all_raw);
   if (d == 128) {
     if (all_raw) hipLaunchKernelGGL((decode_kernel<128, true>), grid, dim3(kThreads), lds, stream, p);

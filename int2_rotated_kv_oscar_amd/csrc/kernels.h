@@ -13,13 +13,14 @@ hipError_t quantize_append(int d, int n_kv, void* pool, const void* k_new, const
                            int n_cus, hipStream_t stream);
 
 size_t decode_lds_bytes(int d, int G, bool all_raw);
-int decode_max_splits();
-int decode_chunks_max(bool all_raw, int max_seq_len, int S, int W, int split_pages);
+int decode_max_records();  // record slots per (sequence, KV head) the merge can hold
+int decode_min_slice();    // pages per workgroup slice at least
 
 hipError_t paged_decode(int d, bool all_raw, const void* int2_pool, int n_int2_pages, const void* bf16_pool, int n_kv, int G, int S,
                         int W, int Hq, const void* q, int batch, const int32_t* seq_lens, const int32_t* bt_q,
                         const int32_t* bt_h, int max_pages, const float* r_k, const float* r_v, float sm_scale,
-                        int split_pages, int n_chunks_max, float* partials, int32_t* counters, int rec_floats,
-                        void* out, bool speculate, hipStream_t stream);
+                        bool per_unit, int unit_items, int fixed_ppw, int n_wg, int cap, int max_seq_len,
+                        float* partials, int32_t* counters, int rec_floats, void* out, bool speculate,
+                        hipStream_t stream);
 
 }  // namespace oscar_launch

@@ -36,13 +36,16 @@ def test_status_strings_and_geometry():
 
 
 def test_workspace_planning():
-    # bound valid for any sink/recent sizes: INT2 chunks + BF16 chunks of 16 pages + 1
+    # split_pages = 64: per (sequence, KV head) one BF16 item and ceil(2048 / 64)
+    # INT2 items of 64 pages, one record each
     b = lib.decode_workspace_bytes(1, 8, 32, 128, 32768, 64)
     rec = (2 * 4 + 4 * 128 + 1 + 3) // 4 * 4
-    assert b == 256 + 8 * (2048 // 64 + 2048 // 16 + 1) * rec * 4
+    assert b == 256 + 8 * (1 + 2048 // 64) * rec * 4
     assert lib.decode_workspace_bytes(0, 8, 32, 128, 0) == 0
     for bad, status in (((1, 8, 30, 128, 100, 0), 1), ((1, 1, 17, 128, 100, 0), 2), ((1, 1, 4, 96, 100, 0), 2),
-                        ((1, 1, 4, 128, 100, 12), 1), ((-1, 1, 4, 128, 100, 0), 1)):
+                        ((1, 1, 4, 128, 100, 12), 1), ((-1, 1, 4, 128, 100, 0), 1),
+                        ((1, 1, 4, 128, 32768, 8), 2),  # 2048 pages in 8-page items: more than 256 records
+                        ((16, 1, 4, 128, 2 ** 31 - 1, 0), 2)):  # 2^31 pages of work or more in one call
         with pytest.raises(lib.OscarError) as e:
             lib.decode_workspace_bytes(*bad)
         assert e.value.status == status

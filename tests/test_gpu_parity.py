@@ -218,7 +218,9 @@ def test_invariances_tables_splits_determinism(tiny_rot):
 
 def test_shared_prefix_pages_alias(tiny_rot):
     # three sequences name the same physical pages for their first 64 tokens;
-    # the output equals a run where each sequence owns a copy of them
+    # the output equals a run of the same batch where each sequence owns a
+    # copy of them (same lengths, so the same work split: bit-identical); each
+    # sequence decoded alone (another work split) meets the oracle bar too
     w = _tiny(batch=3, shared_prefix=64)
     lens = np.array([300, 512, 222])
     inp = synth.decode_inputs(w, seq_lens=lens)
@@ -228,22 +230,33 @@ def test_shared_prefix_pages_alias(tiny_rot):
     int2, bf, _, _ = gh.oracle_pools(inp, tiny_rot)
     ref = gh.oracle_decode(inp, tiny_rot, int2, bf)
     gh.assert_attention_close(got, ref, "shared prefix")
-    # copies: each sequence alone with private pages gives bit-identical rows
+    wp = _tiny(batch=3, shared_prefix=0)
+    private = synth.DecodeInputs(wp, lens, inp.k_rows, inp.v_rows, inp.row_of, inp.q,
+                                 *_private_tables(inp, range(3)))
+    gp = gh.alloc_cache(private, tiny_rot)
+    gh.gpu_fill(private, tiny_rot, gp)
+    assert np.array_equal(gh.gpu_decode(private, gp), got), "aliased and private prefix pages differ"
     for b in range(3):
         wb = _tiny(batch=1, shared_prefix=0)
         single = synth.DecodeInputs(wb, lens[b:b + 1], inp.k_rows, inp.v_rows, [inp.row_of[b]], inp.q[b:b + 1],
-                                    *_private_tables(inp, b))
+                                    *_private_tables(inp, [b]))
         gs = gh.alloc_cache(single, tiny_rot)
         gh.gpu_fill(single, tiny_rot, gs)
-        assert np.array_equal(gh.gpu_decode(single, gs), got[b:b + 1]), f"sequence {b}"
+        gh.assert_attention_close(gh.gpu_decode(single, gs), ref[b:b + 1], f"sequence {b} alone")
 
 
-def _private_tables(inp, b):
-    L = int(inp.seq_lens[b])
-    n = (L + 15) // 16
-    bt_q = np.where(inp.bt_q[b:b + 1, :n] >= 0, np.arange(n, dtype=np.int32)[None], -1).astype(np.int32)
-    bt_h = np.where(inp.bt_h[b:b + 1, :n] >= 0, np.arange(n, dtype=np.int32)[None], -1).astype(np.int32)
-    return bt_q, bt_h, n, n, n
+def _private_tables(inp, seqs):
+    # identity-style tables: sequence i of seqs owns pages [i n, i n + n)
+    seqs = list(seqs)
+    n = int(max((int(inp.seq_lens[b]) + 15) // 16 for b in seqs))
+    bt_q = np.full((len(seqs), n), -1, np.int32)
+    bt_h = np.full((len(seqs), n), -1, np.int32)
+    for i, b in enumerate(seqs):
+        m = (int(inp.seq_lens[b]) + 15) // 16
+        own = i * n + np.arange(m, dtype=np.int32)
+        bt_q[i, :m] = np.where(inp.bt_q[b, :m] >= 0, own, -1)
+        bt_h[i, :m] = np.where(inp.bt_h[b, :m] >= 0, own, -1)
+    return bt_q, bt_h, len(seqs) * n, len(seqs) * n, n
 
 
 def test_bf16_baseline_matches_plain_attention(tiny_rot):
