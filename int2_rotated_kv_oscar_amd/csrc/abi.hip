@@ -82,7 +82,8 @@ int device_cu_count() {
 //   about three record slots per workgroup a unit could span, at least 8 (the
 //   kernel widens the slices where a unit would need more).
 // A sequence covers at most n_pages + 2 pages of work (the pages at the two
-// ends of the INT2 range also hold BF16 tokens).
+// ends of the INT2 range also hold BF16 tokens), plus the per-range overhead
+// positions of balanced slices.
 oscar_status plan_decode(int32_t batch, int32_t n_kv, int32_t n_q, int32_t d, int32_t max_seq_len,
                          int32_t split_pages, bool all_raw, DecodePlan* plan) {
   if (batch < 0 || max_seq_len < 0) return fail(OSCAR_ERR_INVALID_ARG, "negative batch or max_seq_len");
@@ -94,7 +95,7 @@ oscar_status plan_decode(int32_t batch, int32_t n_kv, int32_t n_q, int32_t d, in
     return fail(OSCAR_ERR_INVALID_ARG, "split_pages must be 0 or a multiple of 8 in [8, 2^20]");
   const long long units = (long long)batch * n_kv;
   const long long max_pages = (max_seq_len + 15LL) / 16;
-  const long long max_cost = max_pages + 2;
+  const long long max_cost = max_pages + 2 + 2LL * oscar_launch::decode_seg_pages();
   if (units * max_cost >= (1LL << 31)) return fail(OSCAR_ERR_UNSUPPORTED, "2^31 or more pages of work in one call; split the batch");
   const int max_rec = oscar_launch::decode_max_records();
   const long long cus = device_cu_count();

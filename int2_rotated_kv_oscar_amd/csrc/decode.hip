@@ -69,6 +69,11 @@ constexpr int kWaves = 8;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMaxChunks = 256;   // records (segments) per (sequence, KV head)
 constexpr int kMinSlice = 16;     // pages per workgroup slice at least (a page pair per wave)
+// Balanced slices count each nonempty page range (a unit's BF16 pages, its
+// INT2 pages) as this many extra pages: the fixed cost of a segment
+// (requests, query rotation, record, arrival), about what a CU streams of
+// INT2 pages in that time.  Slices crossing many short units get fewer pages.
+constexpr int kSegPages = 96;
 constexpr int kMergeBatch = 32;   // chunk records loaded per merge round
 static_assert(kMaxChunks * 16 % kThreads == 0, "merge: (record, query row) slots split evenly over threads");
 constexpr float kTwo24 = 16777216.0f;
@@ -102,7 +107,7 @@ __device__ __forceinline__ uint32_t pair_keep(bool k0, bool k1) {
 struct SeqPlan {
   int L, n_pages, s1, m0, m1, r0;
   int ra0, ra1, rb0, rb1, q0, q1;
-  int n_raw, cost;  // BF16 pages; BF16 + INT2 pages
+  int n_raw, real, cost;  // BF16 pages; BF16 + INT2 pages; with the per-range overhead
 };
 
 template <bool ALL_RAW>
@@ -128,7 +133,8 @@ __device__ __forceinline__ SeqPlan make_plan(const DecParams& p, int L) {
     else { sp.q0 = sp.q1 = 0; }
   }
   sp.n_raw = (sp.ra1 - sp.ra0) + (sp.rb1 - sp.rb0);
-  sp.cost = sp.n_raw + (sp.q1 - sp.q0);
+  sp.real = sp.n_raw + (sp.q1 - sp.q0);
+  sp.cost = sp.real + kSegPages * ((sp.n_raw > 0 ? 1 : 0) + (sp.q1 > sp.q0 ? 1 : 0));
   return sp;
 }
 
@@ -835,32 +841,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     return;
   }
 
-  // Balanced slices (many units): the units, sequence-major, put their pages
-  // (BF16 sink and recent pages, then INT2 pages) in one row; workgroup wg
-  // takes the slice [wg ppw, wg ppw + ppw) of it.  A segment is the part of a
-  // slice inside one unit and one page kind; each leaves one record, and the
-  // unit's last segment to finish merges its records.
-  // Early requests: assume every length is max_seq_len and issue the first
-  // segment's INT2 requests before the lengths arrive.
-  if (!ALL_RAW && p.speculate) {
-    const SeqPlan sp0 = make_plan<false>(p, p.max_seq_len);
-    const int c = sp0.cost;
-    const int total0 = units * c;
-    const long long lo0 = (long long)wg * slice_pages(p, total0, c);
-    if (c > 0 && lo0 < total0) {
-      const int u = int(lo0) / c, off = int(lo0) - u * c;
-      if (off >= sp0.n_raw) speculate_at(u / p.n_kv, u % p.n_kv, sp0.q0 + off - sp0.n_raw);
-    }
-  }
-
-  // page counts of the sequences: thread t sums a block of them; a block
-  // scan gives each block's first position
+  // Balanced slices (many units): the units, sequence-major, put their work
+  // (BF16 sink and recent pages, INT2 pages, then kSegPages positions per
+  // nonempty range that hold no pages) in one row; workgroup wg takes the
+  // slice [wg ppw, wg ppw + ppw) of it.  A segment is the part of a slice
+  // inside one unit and one page kind; each leaves one record, and the unit's
+  // last segment to finish merges its records.
+  // Work of the sequences: thread t sums a block of them; a block scan gives
+  // each block's first position.
   int* s_scan = reinterpret_cast<int*>(s_res);  // [8] wave totals, [8] owner's first position
-  int* s_scani = reinterpret_cast<int*>(s_scan + 16);       // [8] wave max cost, [8] all-full flags, [16] owner
+  int* s_scani = s_scan + 16;                   // [8] wave max cost, [8] owner
   const int seq_blk = (p.batch + kThreads - 1) / kThreads;
-  int v = 0;
-  int cmax = 0;
-  bool full = true;
+  int v = 0, cmax = 0;
   {
     const int b0 = tid * seq_blk, b1 = min(p.batch, b0 + seq_blk);
     for (int bb = b0; bb < b1; ++bb) {
@@ -868,7 +860,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
       const int c = make_plan<ALL_RAW>(p, max(L, 0)).cost;
       v += p.n_kv * c;
       cmax = max(cmax, c);
-      full = full && L == p.max_seq_len;
       if (L <= 0 && wg == 0) {  // no tokens: zero output
         u32x4* o = reinterpret_cast<u32x4*>(p.out + size_t(bb) * p.Hq * D);
         for (int e = 0; e < p.Hq * D / 8; ++e) o[e] = u32x4{0, 0, 0, 0};
@@ -884,27 +875,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   int wmax = cmax;
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) wmax = max(wmax, __shfl_xor(wmax, o, 64));
-  const bool wfull = __all(full);
   if (lane == 63) s_scan[wave] = inc;
-  if (lane == 0) {
-    s_scani[wave] = wmax;
-    s_scani[8 + wave] = wfull ? 1 : 0;
-  }
+  if (lane == 0) s_scani[wave] = wmax;
   lds_barrier();
-  int total = 0, woff = 0;
-  int max_cost = 0, n_full = 0;
+  int total = 0, woff = 0, max_cost = 0;
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) {
     const int t = s_scan[w];
     woff += w < wave ? t : 0;
     total += t;
     max_cost = max(max_cost, s_scani[w]);
-    n_full += s_scani[8 + w];
   }
   // workgroup-uniform values read from LDS: scalar registers from here on
   total = __builtin_amdgcn_readfirstlane(total);
   max_cost = __builtin_amdgcn_readfirstlane(max_cost);
-  const bool all_full = __builtin_amdgcn_readfirstlane(n_full) == kWaves;
   const int ppw = slice_pages(p, total, max_cost);
   if ((long long)wg * ppw >= total) return;
   const int lo = wg * ppw;
@@ -912,38 +896,31 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   const int excl = woff + inc - v;  // first position of this thread's sequences
   if (v > 0 && excl <= lo && lo < excl + v) {
     s_scan[8] = excl;
-    s_scani[16] = tid;
+    s_scani[8] = tid;
   }
   lds_barrier();
   // walk the owner's block to the unit holding position lo
   int Cu = __builtin_amdgcn_readfirstlane(s_scan[8]);
   {
-    int bb = __builtin_amdgcn_readfirstlane(s_scani[16]) * seq_blk;
+    int bb = __builtin_amdgcn_readfirstlane(s_scani[8]) * seq_blk;
     sp = make_plan<ALL_RAW>(p, max(p.seq_lens[bb], 0));
     while (Cu + p.n_kv * sp.cost <= lo) {
       Cu += p.n_kv * sp.cost;
       ++bb;
       sp = make_plan<ALL_RAW>(p, max(p.seq_lens[bb], 0));
     }
-    const int hh = int((lo - Cu) / sp.cost);
+    const int hh = (lo - Cu) / sp.cost;
     Cu += hh * sp.cost;
     set_unit(bb, hh);
   }
-
   int pos = lo;
-  auto run = [&](auto first_tag) __attribute__((always_inline)) {
-    const int raw_end = Cu + sp.n_raw, u_end = Cu + sp.cost;
-    const bool is_raw = pos < raw_end;
-    const int seg_end = min(hi, is_raw ? raw_end : u_end);
-    const int n_raw_seg = sp.n_raw > 0 ? (raw_end - 1) / ppw - Cu / ppw + 1 : 0;
-    const int nseg = n_raw_seg + (sp.cost > sp.n_raw ? (u_end - 1) / ppw - raw_end / ppw + 1 : 0);
-    const int kseg = is_raw ? wg - Cu / ppw : n_raw_seg + wg - raw_end / ppw;
-    segment(first_tag, is_raw, is_raw ? pos - Cu : sp.q0 + (pos - raw_end),
-            is_raw ? seg_end - Cu : sp.q0 + (seg_end - raw_end), nseg, kseg);
-    pos = seg_end;
-    if (pos >= hi) return false;
-    if (pos >= u_end) {  // next unit with pages
-      Cu = u_end;
+  // move pos onto pages of this or a later unit; false if none before hi
+  auto settle = [&]() -> bool {
+    for (;;) {
+      if (pos < Cu + sp.real) return pos < hi;
+      const int nxt = Cu + sp.cost;
+      if (nxt >= hi) return false;
+      pos = Cu = nxt;
       if (h + 1 < p.n_kv) {
         set_unit(b, h + 1);
       } else {
@@ -955,6 +932,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
         set_unit(bb, 0);
       }
     }
+  };
+  if (!settle()) return;
+  auto run = [&](auto first_tag) __attribute__((always_inline)) {
+    const int raw_end = Cu + sp.n_raw, real_end = Cu + sp.real;
+    const bool is_raw = pos < raw_end;
+    const int seg_end = min(hi, is_raw ? raw_end : real_end);
+    const int n_raw_seg = sp.n_raw > 0 ? (raw_end - 1) / ppw - Cu / ppw + 1 : 0;
+    const int nseg = n_raw_seg + (sp.real > sp.n_raw ? (real_end - 1) / ppw - raw_end / ppw + 1 : 0);
+    const int kseg = is_raw ? wg - Cu / ppw : n_raw_seg + wg - raw_end / ppw;
+    segment(first_tag, is_raw, is_raw ? pos - Cu : sp.q0 + (pos - raw_end),
+            is_raw ? seg_end - Cu : sp.q0 + (seg_end - raw_end), nseg, kseg);
+    pos = seg_end;
+    if (!settle()) return false;
     lds_barrier();  // LDS of this segment's merge is rewritten by the next segment
     return true;
   };
@@ -970,6 +960,8 @@ namespace oscar_launch {
 int decode_max_records() { return kMaxChunks; }
 
 int decode_min_slice() { return kMinSlice; }
+
+int decode_seg_pages() { return kSegPages; }
 
 size_t decode_lds_bytes(int d, int G, bool all_raw) {
   const int ng = d / 32;

@@ -15,6 +15,7 @@ hipError_t quantize_append(int d, int n_kv, void* pool, const void* k_new, const
 size_t decode_lds_bytes(int d, int G, bool all_raw);
 int decode_max_records();  // record slots per (sequence, KV head) the merge can hold
 int decode_min_slice();    // pages per workgroup slice at least
+int decode_seg_pages();    // extra positions per nonempty page range in balanced slices
 
 hipError_t paged_decode(int d, bool all_raw, const void* int2_pool, int n_int2_pages, const void* bf16_pool, int n_kv, int G, int S,
                         int W, int Hq, const void* q, int batch, const int32_t* seq_lens, const int32_t* bt_q,
