@@ -231,14 +231,17 @@ oscar_status oscar_write_bf16(const oscar_cache* cache, const void* k_new,
  *   out_i = sum_{raw j} p_j v_j + (sum_{middle j} p_j vh_j) . R_V(h)^T
  * Because R is orthogonal this is attention over the decoded cache mapped
  * back to the original basis (the "inverse rotation").  Output is bf16.
- * The kernel splits each (sequence, KV head) into chunks of split_pages pages
- * and merges the chunk results with a log-sum-exp reduction in the same
+ * The kernel splits the pages of each (sequence, KV head) over workgroups
+ * and merges the partial results with a log-sum-exp reduction in the same
  * launch.
  * q: device bf16 [B][H_q][d].  seq_lens: device int32 [B].  bt_q, bt_h:
  * device int32 [B][max_pages].  r_k, r_v: device float32 [H_kv][d][d].
  * max_seq_len: host-known upper bound of seq_lens, <= 16 max_pages (sizes the
- * grid).  split_pages: pages per chunk, a multiple of 8 in [8, 4096], or 0
- * for automatic.  workspace: device memory of at least
+ * grid).  split_pages: pages per workgroup item of one (sequence, KV head),
+ * a multiple of 8 in [8, 2^20] with at most 255 INT2 items per sequence, or 0
+ * for automatic (per-(sequence, KV head) items sized to the device's compute
+ * units for small batches, equal page slices over the whole batch for large
+ * ones).  workspace: device memory of at least
  * oscar_decode_workspace_bytes(...) bytes, prepared once with
  * oscar_decode_workspace_init; every completed call leaves it prepared.
  * out: device bf16 [B][H_q][d].
