@@ -192,37 +192,27 @@ struct PageOps {
   }
 };
 
-// A page pair in flight: whole-wave coalesced loads of two page-head images
-// (lane l holds bytes [16l, 16l+16) and, for d = 128, [1024 + 8l, 1024 + 8l + 8)).
+// A page pair goes from HBM straight into an LDS ring slot of its wave with
+// global_load_lds_dwordx4: LOADS whole-wave loads of 1024 B, lane l of load i
+// carrying pair bytes [1024 i + 16 l, +16) (page A, then page B; for d = 64
+// the last 512 B of the slot are padding, filled from page B's last bytes).
+// No registers hold pages in flight.
 template <int D>
-struct PairStage {
+struct PairDma {
   static constexpr int HB = Geo<D>::HEAD_BYTES;  // 1536 or 768
-  u32x4 a[2];
-  u32x2 b[2];
-  __device__ __forceinline__ void load(const uint8_t* pa, const uint8_t* pb, int lane) {
-    const uint8_t* src[2] = {pa, pb};
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (HB == 1536) {
-        a[j] = *reinterpret_cast<const u32x4*>(src[j] + 16 * lane);
-        b[j] = *reinterpret_cast<const u32x2*>(src[j] + 1024 + 8 * lane);
-      } else {  // 768 B: 48 lanes x 16 B
-        a[j] = lane < 48 ? *reinterpret_cast<const u32x4*>(src[j] + 16 * lane) : u32x4{0, 0, 0, 0};
-      }
-    }
-  }
-  __device__ __forceinline__ void store(uint8_t* slot, int lane) const {
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (HB == 1536) {
-        *reinterpret_cast<u32x4*>(slot + j * HB + 16 * lane) = a[j];
-        *reinterpret_cast<u32x2*>(slot + j * HB + 1024 + 8 * lane) = b[j];
-      } else if (lane < 48) {
-        *reinterpret_cast<u32x4*>(slot + j * HB + 16 * lane) = a[j];
-      }
-    }
-  }
+  static constexpr int LOADS = (2 * HB + 1023) / 1024;
+  static constexpr int SLOT = LOADS * 1024;
 };
+constexpr int kRing = 6;  // pair slots per wave: the two steps being computed and two pairs in flight
+
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding), and no memory
+// access moved across it: LDS written by the ring loads is read after it.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
 
 template <int D, bool ALL_RAW>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
@@ -231,15 +221,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   const int G = p.G;
   // LDS: q-hat B operands [NG][64][4] u32 | zero-term operand [64][4] u32 |
-  // misc 512 floats | page slots [8 waves][2][2 pages][HB] | results/merge
+  // misc 512 floats | page rings [8 waves][kRing][SLOT], which the per-wave
+  // results and the merge reuse once the page loop is over
   uint32_t* s_qhat = reinterpret_cast<uint32_t*>(smem);
   uint32_t* s_qz = s_qhat + NG * 256;
   float* s_misc = reinterpret_cast<float*>(s_qz + 256);
   float* s_m = s_misc;             // [8][16] per-wave max
   float* s_l = s_misc + 128;       // [8][16] per-wave sum
   int* s_flag = reinterpret_cast<int*>(s_misc + 256);  // [16]
-  uint8_t* s_slots = reinterpret_cast<uint8_t*>(s_misc + 512);
-  float* s_res = reinterpret_cast<float*>(s_slots + (ALL_RAW ? 0 : kWaves * 2 * 2 * HB));
+  uint32_t* s_tabs = reinterpret_cast<uint32_t*>(s_misc + 512);  // [8 waves][2][64] page-id blocks
+  uint8_t* s_slots = reinterpret_cast<uint8_t*>(s_tabs + kWaves * 2 * 64);
+  float* s_res = reinterpret_cast<float*>(s_slots);
   // s_res: per-wave results [8][G][D]; in the last workgroup: merged [G][D] rot
   // and [G][D] raw
 
@@ -265,33 +257,55 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   };
 
   // ---- requests of an INT2 segment starting at page sc0: the query-rotation
-  // operands, the query, this wave's page ids and its first kDepth page pairs.
-  // Entries past the segment may be anything: table reads stay inside the row
-  // and page ids are clamped into the pool; such pages are never used unmasked. ----
-  constexpr int kDepth = 4;  // page pairs in flight per wave
+  // operands, the query, this wave's page ids and its first kDepth page pairs
+  // (into ring slots 0..kDepth-1).  Entries past the segment may be anything:
+  // table reads stay inside the row and page ids are clamped into the pool;
+  // such pages are never used unmasked. ----
+  using PD = PairDma<D>;
+  constexpr int kDepth = 4;  // page pairs requested ahead of the step being computed
+  static_assert(kRing == kDepth + 2, "ring: two pairs computed, kDepth in flight");
+  uint8_t* const ring = s_slots + wave * kRing * PD::SLOT;
   const bool rot_wave = wave < NCB;
   float rvals[NKB][8];
   u32x4 bqv[NKB];
   int sc0 = 0;  // first page of the segment the requests are for
   // Page ids of this wave's pairs, 32 pairs per register block: lane L holds
   // page sc0 + 2(wave + 8k) + L%2 of pair k = 32 blk + L/2.  Reading them with
-  // readlane keeps memory waits out of the prefetch issue.
-  auto load_tab = [&](int blk) {
+  // readlane keeps memory waits out of the prefetch issue.  Block 0 is a
+  // plain load; later blocks come through the wave's LDS table area (block
+  // blk in area blk % 2), requested a whole block of pairs before they are
+  // read: page loads that land in LDS are invisible to the compiler's wait
+  // counting, so a plain load consumed mid-loop would drain them all.
+  uint32_t* const my_tabs = s_tabs + wave * 2 * 64;
+  auto tab_entry = [&](int blk) {
     const int k = 32 * blk + (lane >> 1);
-    const int v = btq[min(sc0 + 2 * (wave + kWaves * k) + (lane & 1), p.max_pages - 1)];
-    return min(max(v, 0), p.n_int2_pages - 1);
+    return btq + min(sc0 + 2 * (wave + kWaves * k) + (lane & 1), p.max_pages - 1);
   };
-  int tab = 0, tab_nx = 0, tab_blk = 0;
+  auto clamp_page = [&](int v) { return min(max(v, 0), p.n_int2_pages - 1); };
+  auto tab_dma = [&](int blk) {
+    __builtin_amdgcn_global_load_lds(tab_entry(blk), my_tabs + 64 * (blk & 1), 4, 0, 0);
+  };
+  int tab = 0, tab_blk = 0;
   auto pair_pages = [&](int k, const uint8_t*& pa, const uint8_t*& pb) {
     const int i = 2 * (max(k, 0) & 31);
     pa = p.int2_pool + (size_t(__builtin_amdgcn_readlane(tab, i)) * p.n_kv + h) * HB;
     pb = p.int2_pool + (size_t(__builtin_amdgcn_readlane(tab, i + 1)) * p.n_kv + h) * HB;
   };
-  PairStage<D> st[kDepth];
+  // pair j (clamped to this wave's pairs) -> ring slot dst
+  auto pair_dma = [&](int j, uint8_t* dst) {
+    const uint8_t *pa, *pb;
+    pair_pages(j, pa, pb);
+#pragma unroll
+    for (int i = 0; i < PD::LOADS; ++i) {
+      const int o = 1024 * i + 16 * lane;
+      const uint8_t* src = o < HB ? pa + o : pb + min(o - HB, HB - 16);
+      __builtin_amdgcn_global_load_lds(src, dst + 1024 * i, 16, 0, 0);
+    }
+  };
   auto int2_requests = [&]() {
     tab_blk = 0;
-    tab = load_tab(0);
-    tab_nx = load_tab(1);
+    tab = clamp_page(*tab_entry(0));
+    tab_dma(1);
     {  // every wave loads (waves past NCB repeat a block) so that no path leaves them unset
       const float* rk = p.r_k + size_t(h) * D * D;
 #pragma unroll
@@ -302,14 +316,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
       for (int kb = 0; kb < NKB; ++kb) bqv[kb] = *reinterpret_cast<const u32x4*>(qb + size_t(qrow) * D + 32 * kb + 8 * quad);
     }
     // page loads are issued unconditionally (a wave short of pairs loads
-    // unused pages) so that every wait for a stage counts exactly the loads
-    // issued after it instead of draining all of them
+    // unused pages) so that every wait counts exactly the loads issued after
+    // the pair it waits for
 #pragma unroll
-    for (int u = 0; u < kDepth; ++u) {
-      const uint8_t *pa, *pb;
-      pair_pages(u, pa, pb);
-      st[u].load(pa, pb, lane);
-    }
+    for (int u = 0; u < kDepth; ++u) pair_dma(u, ring + u * PD::SLOT);
   };
 
   // ---- work layout ----
@@ -496,7 +506,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
       }
       bz = u32x4{pack2(hv[0], hv[1]), pack2(hv[2], hv[3]), pack2(hv[4], hv[5]), pack2(hv[6], hv[7])};
     }
-    uint8_t* myslots = s_slots + wave * 2 * 2 * HB;
     const uint32_t ones = l16 == NG ? 0x3C003C00u : 0u;  // f16 1.0 pairs in A row NG
     // one page pair: logits, softmax, value sums
     // Two page pairs per step (pair k from slot A, pair k+1 from slot B): K
@@ -585,36 +594,52 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
       }
     };
 
-    // kDepth register stages and two LDS slots per wave: pairs k, k+1 are
-    // computed from the two slots while pairs k+2 .. k+kDepth+1 are in flight
-    // (stage stores and loads run unconditionally, past the last pair too, so
-    // the compiler's load counting stays exact; only the compute is skipped)
-    static_assert(32 % kDepth == 0 && kDepth % 2 == 0, "page-id blocks and pair steps");
+    // Ring of kRing pair slots per wave, pair j in slot j % kRing.  Four pairs
+    // per iteration, two steps of two: before each step the next two pairs
+    // are requested (into the slots the previous step read) and the step's
+    // own pairs are waited for.  The loads after a step's pairs are the
+    // 4 pairs requested since, hence vmcnt(4 LOADS).
+    // Loads run unconditionally, past the last pair too (clamped), so that
+    // the count holds; only the compute is skipped.
+    // (A page-id block request between them only makes the wait stronger.)
+    static_assert(32 % kDepth == 0 && kDepth == 4, "page-id blocks and pair steps");
+    constexpr int kAfter = 4 * PD::LOADS;
     for (int k = 0; k < n_mine; k += kDepth) {
-      // page-id block of this group's prefetch targets (advances one block at a time)
+      // page-id block of this group's prefetch targets (advances one block at
+      // a time; its LDS copy was requested a whole block of pairs ago)
       const int jb = min(k + kDepth, n_mine - 1) >> 5;
-      if (jb != tab_blk) { tab = tab_nx; tab_blk = jb; }
-      tab_nx = load_tab(tab_blk + 1);
-#pragma unroll
-      for (int u = 0; u < kDepth; u += 2) {
-        const int kk = k + u;
-#pragma unroll
-        for (int v = 0; v < 2; ++v) {
-          st[u + v].store(myslots + v * 2 * HB, lane);
-          const uint8_t *pa, *pb;
-          pair_pages(min(kk + v + kDepth, n_mine - 1), pa, pb);  // tail: harmless reload
-          st[u + v].load(pa, pb, lane);
-        }
+      if (jb != tab_blk) {
+        tab = clamp_page(int(my_tabs[64 * (jb & 1) + lane]));
+        tab_blk = jb;
+        tab_dma(jb + 1);
+      }
+      const int s0 = k % kRing;
+      auto slot = [&](int i) {
+        const int t = s0 + i;
+        return ring + (t >= kRing ? t - kRing : t) * PD::SLOT;
+      };
+      auto step = [&](int kk) {
         if (kk < n_mine) {
           const bool has_b = kk + 1 < n_mine;
           const int pg0 = page_of(kk, 0), pg3 = page_of(kk + 1, 1);
           const bool interior = has_b && pg3 + 1 <= c1 && 16 * pg0 >= m0 && 16 * pg3 + 16 <= m1 &&
                                 page_of(kk, 1) + 1 <= c1 && 16 * page_of(kk + 1, 0) >= m0;
-          if (interior) do_two(kk, myslots, myslots + 2 * HB, true, std::true_type{});
-          else do_two(kk, myslots, myslots + 2 * HB, has_b, std::false_type{});
+          uint8_t* sa = slot(kk - k);
+          uint8_t* sb = slot(kk - k + 1);
+          if (interior) do_two(kk, sa, sb, true, std::true_type{});
+          else do_two(kk, sa, sb, has_b, std::false_type{});
         }
-      }
+      };
+      pair_dma(min(k + 4, n_mine - 1), slot(4));
+      pair_dma(min(k + 5, n_mine - 1), slot(5));
+      wait_vm<kAfter>();
+      step(k);
+      pair_dma(min(k + 6, n_mine - 1), slot(6));
+      pair_dma(min(k + 7, n_mine - 1), slot(7));
+      wait_vm<kAfter>();
+      step(k + 2);
     }
+    wait_vm<0>();  // no ring load lands after the results reuse the ring
   }
 
   // ---- per-wave results -> LDS, merged over the 8 waves ----
@@ -819,8 +844,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     const int per = p.unit_items, split = p.fixed_ppw;
     const int u = wg / per, x = wg - u * per;
     set_unit(u / p.n_kv, u - (u / p.n_kv) * p.n_kv);
-    if (!ALL_RAW && p.speculate && x >= 1) speculate_at(b, h, (p.S >> 4) + (x - 1) * split);
+    // the length is requested first: waiting for it then leaves the early
+    // page requests in flight
     const int L = p.seq_lens[b];
+    if (!ALL_RAW && p.speculate && x >= 1) speculate_at(b, h, (p.S >> 4) + (x - 1) * split);
     if (L <= 0) {
       if (x == 0 && h == 0)
         for (int e = tid; e < p.Hq * D; e += kThreads) p.out[size_t(b) * p.Hq * D + e] = 0;
@@ -965,10 +992,11 @@ int decode_seg_pages() { return kSegPages; }
 
 size_t decode_lds_bytes(int d, int G, bool all_raw) {
   const int ng = d / 32;
-  const size_t slots = all_raw ? 0 : size_t(kWaves) * 2 * 2 * 12 * d;
+  const size_t slot = d == 128 ? PairDma<128>::SLOT : PairDma<64>::SLOT;
+  const size_t rings = all_raw ? 0 : size_t(kWaves) * kRing * slot;
   size_t res = size_t(kWaves) * G * d;                              // per-wave results
   res = std::max(res, size_t(kMaxChunks) * 32 + 2 * kWaves * 16 + size_t(2) * G * d);  // merge
-  return (size_t(ng) * 256 + 256 + 512) * 4 + slots + res * 4;
+  return (size_t(ng) * 256 + 256 + 512 + kWaves * 2 * 64) * 4 + std::max(rings, res * 4);
 }
 
 hipError_t paged_decode(int d, bool all_raw, const void* int2_pool, int n_int2_pages, const void* bf16_pool, int n_kv, int G, int S,
