@@ -315,6 +315,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) bqv[kb] = *reinterpret_cast<const u32x4*>(qb + size_t(qrow) * D + 32 * kb + 8 * quad);
     }
+    // The rotation operands are waited for here, before the page requests:
+    // the compiler does not count loads that land in LDS, so a wait for them
+    // placed after the page requests would drain those too, and the rotation
+    // would no longer overlap the page latency.
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      asm volatile("" ::"v"(bqv[kb]));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(rvals[kb][i]));
+    }
     // page loads are issued unconditionally (a wave short of pairs loads
     // unused pages) so that every wait counts exactly the loads issued after
     // the pair it waits for
