@@ -224,7 +224,7 @@ def main() -> int:
                    "recent": w.n_recent, "split_pages": args.split_pages or "auto", "cache_copies": copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(w.name),
-                     "kernel": "decode_kernel<128,false>", "algorithmic_bytes_per_launch": nbytes["total"],
+                     "kernel": "decode_kernel<128,false,false>", "algorithmic_bytes_per_launch": nbytes["total"],
                      "avg_launch_us": round(dec_avg * 1e3, 2)},
     }
 
@@ -252,7 +252,7 @@ def main() -> int:
         torch.cuda.synchronize()
         bms = e0.elapsed_time(e1) / K
         bbytes = tokens * 4 * w.d * w.n_kv_heads + 2 * B * w.n_q_heads * w.d * 2
-        result["bf16_baseline"] = {"kernel": "decode_kernel<128,true>", "us_per_call": round(bms * 1e3, 2),
+        result["bf16_baseline"] = {"kernel": "decode_kernel<128,true,false>", "us_per_call": round(bms * 1e3, 2),
                                    "KV_tokens_per_s": round(tokens / (bms * 1e-3), 1),
                                    "achieved_GBps": round(bbytes / (bms * 1e-3) / 1e9, 1),
                                    "int2_decode_speedup": round(bms / dec_avg, 3)}

@@ -214,7 +214,10 @@ __device__ __forceinline__ void wait_vm() {
   asm volatile("" ::: "memory");
 }
 
-template <int D, bool ALL_RAW>
+// SLICES: balanced slices over all units (several segments per workgroup),
+// else per-unit items (one segment per workgroup, early requests).  Separate
+// kernels keep each one's code to a single instance of the segment.
+template <int D, bool ALL_RAW, bool SLICES>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   using GG = Geo<D>;
   constexpr int NG = GG::NG, NCB = GG::NCB, NKB = GG::NKB, HB = GG::HEAD_BYTES;
@@ -845,7 +848,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   }  // merge
   };
 
-  if (p.per_unit) {
+  if constexpr (!SLICES) {
     // Per-unit items (few units): workgroup wg is item x of unit u.  Item 0
     // takes the unit's BF16 pages, item x >= 1 INT2 pages
     // [q0 + (x-1) split, q0 + x split) (for the all-BF16 cache: item x takes
@@ -875,9 +878,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     const int q0 = sp.q0 + (x - 1) * split;
     segment(std::true_type{}, x == 0, x == 0 ? 0 : q0, x == 0 ? sp.n_raw : min(sp.q1, q0 + split), has_raw + nq,
             x == 0 ? 0 : has_raw + x - 1);
-    return;
-  }
-
+  } else {
   // Balanced slices (many units): the units, sequence-major, put their work
   // (BF16 sink and recent pages, INT2 pages, then kSegPages positions per
   // nonempty range that hold no pages) in one row; workgroup wg takes the
@@ -985,9 +986,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     lds_barrier();  // LDS of this segment's merge is rewritten by the next segment
     return true;
   };
-  if (run(std::true_type{}))
-    while (run(std::false_type{})) {
-    }
+  while (run(std::false_type{})) {
+  }
+  }  // balanced slices
 }
 
 }  // namespace
@@ -1021,13 +1022,19 @@ hipError_t paged_decode(int d, bool all_raw, const void* int2_pool, int n_int2_p
               per_unit ? 1 : 0, unit_items};
   const dim3 grid(static_cast<unsigned>(n_wg));
   const size_t lds = decode_lds_bytes(d, G, all_raw);
+#define OSCAR_DECODE_LAUNCH(DD, RAW)                                                                     \
+  do {                                                                                                  \
+    if (per_unit) hipLaunchKernelGGL((decode_kernel<DD, RAW, false>), grid, dim3(kThreads), lds, stream, p); \
+    else hipLaunchKernelGGL((decode_kernel<DD, RAW, true>), grid, dim3(kThreads), lds, stream, p);           \
+  } while (0)
   if (d == 128) {
-    if (all_raw) hipLaunchKernelGGL((decode_kernel<128, true>), grid, dim3(kThreads), lds, stream, p);
-    else hipLaunchKernelGGL((decode_kernel<128, false>), grid, dim3(kThreads), lds, stream, p);
+    if (all_raw) OSCAR_DECODE_LAUNCH(128, true);
+    else OSCAR_DECODE_LAUNCH(128, false);
   } else {
-    if (all_raw) hipLaunchKernelGGL((decode_kernel<64, true>), grid, dim3(kThreads), lds, stream, p);
-    else hipLaunchKernelGGL((decode_kernel<64, false>), grid, dim3(kThreads), lds, stream, p);
+    if (all_raw) OSCAR_DECODE_LAUNCH(64, true);
+    else OSCAR_DECODE_LAUNCH(64, false);
   }
+#undef OSCAR_DECODE_LAUNCH
   return hipGetLastError();
 }
 
