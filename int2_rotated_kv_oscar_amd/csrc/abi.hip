@@ -106,7 +106,7 @@ oscar_status plan_decode(int32_t batch, int32_t n_kv, int32_t n_q, int32_t d, in
       const long long items = std::max(1LL, all_raw ? cus : cus - units);
       split = std::max<long long>(oscar_launch::decode_min_slice(), (units * max_pages + items - 1) / items);
       split = std::max(split, (max_pages + max_rec - 2) / (max_rec - 1));
-      split += split & 1;
+      split = (split + 7) / 8 * 8;  // measured: fewer, slightly larger items beat an uneven last pair round
     }
     const long long n_items = 1 + (max_pages + split - 1) / split;
     if (n_items > max_rec) return fail(OSCAR_ERR_UNSUPPORTED, "more than 256 chunks per (sequence, KV head); use a larger split_pages");

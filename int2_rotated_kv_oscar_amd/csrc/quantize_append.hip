@@ -68,7 +68,8 @@ struct TileMeta {
   bool aligned;  // 16 consecutive positions of one sequence starting on a page boundary
 };
 
-template <int D, int TENSOR>
+// ONE: every workgroup has exactly one tile (a decode step's appends)
+template <int D, int TENSOR, bool ONE>
 __device__ void qa_tiles(const QAParams& p, int h) {
   using GG = Geo<D>;
   constexpr int NG = GG::NG, NKB = GG::NKB, NW = GG::NW;
@@ -110,7 +111,7 @@ __device__ void qa_tiles(const QAParams& p, int h) {
     pr[u] = p.row_pos[row];
   };
 #pragma unroll
-  for (int u = 0; u < kDepth; ++u) issue(u, u);  // requested before R: the latencies overlap
+  for (int u = 0; u < (ONE ? 1 : kDepth); ++u) issue(u, u);  // requested before R: the latencies overlap
 
   // R operands of this group, split once: 256 R (a power of two keeps the
   // low parts out of the f16 subnormal range) as f16 hi + lo, 22 significant
@@ -282,6 +283,38 @@ __device__ void qa_tiles(const QAParams& p, int h) {
   int rep = 0;  // row prescale of the tile whose epilogue runs next
   f32x4 accp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
   __syncthreads();  // s_words zeroed
+  if constexpr (ONE) {
+    // one tile for this workgroup: the same steps without the pipeline, two
+    // barriers instead of three rounds
+    stage_x(xr[0], 0);
+    TileMeta mc;
+    {
+      const int64_t t = tile_of(0);
+      const int32_t seq = sr[0], pos = pr[0];
+      mc.page = p.bt_q[int64_t(seq) * p.max_pages + (pos >> 4)];
+      mc.valid = t * 16 + l16 < p.n_rows;
+      mc.slot = pos & 15;
+      const int32_t seq0 = __shfl(seq, 0, 64), pos0 = __shfl(pos, 0, 64);
+      const bool ok = mc.valid && seq == seq0 && pos == pos0 + l16 && (pos0 & 15) == 0;
+      mc.aligned = (__ballot(ok) & 0xFFFFull) == 0xFFFFull;
+    }
+    lds_barrier();
+    f32x4 acc1[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    {
+      u32x4 xc[NKB];
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) xc[kb] = *reinterpret_cast<const u32x4*>(&s_x[0][l16 * kRowBytes + 64 * kb + 16 * quad]);
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int j = 1; j >= 0; --j) acc1[hb] = mfma_f16(rop[hb][kb][j], xc[kb], acc1[hb]);
+    }
+    epilogue(acc1, mc, s_rexp[0][l16], 0);
+    lds_barrier();
+    store_tile(mc, 0);
+  } else {
   for (int64_t i0 = 0; i0 < n_mine + 2; i0 += kDepth) {
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) {
@@ -330,15 +363,16 @@ __device__ void qa_tiles(const QAParams& p, int h) {
       m1 = mc;
     }
   }
+  }  // pipelined tiles
 }
 
-template <int D>
+template <int D, bool ONE>
 __global__ __launch_bounds__(64 * (D / 32)) void quantize_append_kernel(QAParams p) {
   const int h = blockIdx.y;
   if (blockIdx.z == 0)
-    qa_tiles<D, 0>(p, h);
+    qa_tiles<D, 0, ONE>(p, h);
   else
-    qa_tiles<D, 1>(p, h);
+    qa_tiles<D, 1, ONE>(p, h);
 }
 
 }  // namespace
@@ -356,8 +390,15 @@ hipError_t quantize_append(int d, int n_kv, void* pool, const void* k_new, const
   const int64_t tiles = (n_rows + 15) / 16;
   const int64_t per_pair = std::max<int64_t>(1, (3 * int64_t(n_cus) + 2 * n_kv - 1) / (2 * n_kv));
   const dim3 grid(static_cast<unsigned>(std::min(tiles, per_pair)), static_cast<unsigned>(n_kv), 2u);
-  if (d == 128) hipLaunchKernelGGL((quantize_append_kernel<128>), grid, dim3(256), 0, stream, p);
-  else hipLaunchKernelGGL((quantize_append_kernel<64>), grid, dim3(128), 0, stream, p);
+  // one tile per workgroup (few rows, as in a decode step): the unpipelined variant
+  const bool one = tiles <= per_pair;
+  if (d == 128) {
+    if (one) hipLaunchKernelGGL((quantize_append_kernel<128, true>), grid, dim3(256), 0, stream, p);
+    else hipLaunchKernelGGL((quantize_append_kernel<128, false>), grid, dim3(256), 0, stream, p);
+  } else {
+    if (one) hipLaunchKernelGGL((quantize_append_kernel<64, true>), grid, dim3(128), 0, stream, p);
+    else hipLaunchKernelGGL((quantize_append_kernel<64, false>), grid, dim3(128), 0, stream, p);
+  }
   return hipGetLastError();
 }
 
