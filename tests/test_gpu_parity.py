@@ -274,6 +274,57 @@ def test_bf16_baseline_matches_plain_attention(tiny_rot):
         gh.assert_attention_close(got[b], ref, "bf16 baseline")
 
 
+def test_decode_balanced_slices_many_units(tiny_rot):
+    # more (sequence, KV head) units than a quarter of the CUs: the kernel
+    # that spreads all units' pages over one workgroup per CU, so workgroups
+    # cross unit and page-kind boundaries (several segments each) and skip
+    # the overhead positions; ragged lengths including empty and one-page
+    # sequences, every sequence checked.  The cache is the one the GPU wrote
+    # (its codes checked against the oracle's, whose f16 ties at a rounding
+    # midpoint may legitimately round the other way and move that group's
+    # codes), and the oracle decodes those very pages.
+    from oracle import attention as oatt
+    lens = np.random.default_rng(11).integers(1, 700, size=80)
+    lens[[3, 40]] = 0
+    lens[[5, 6, 7]] = [1, 16, 37]
+    w = _tiny(batch=len(lens))
+    inp = synth.decode_inputs(w, seq_lens=lens)
+    gc = gh.alloc_cache(inp, tiny_rot)
+    gh.gpu_fill(inp, tiny_rot, gc)
+    print(f"[decode balanced slices] B={len(lens)}", flush=True)
+    got = gh.gpu_decode(inp, gc)
+    _, _, res, rows = gh.oracle_pools(inp, tiny_rot)
+    page, slot = _page_slot(inp, rows)
+    int2_bytes = gc.int2.cpu().numpy()
+    gh.assert_codes_ok(gh.compare_appended(int2_bytes, w, inp.n_int2_pages, res, page, slot), "balanced slices fill")
+    int2 = olayout.Int2Pool(inp.n_int2_pages, w.n_kv_heads, w.d, int2_bytes)
+    bf = olayout.Bf16Pool(inp.n_bf16_pages, w.n_kv_heads, w.d, gc.bf16.cpu().numpy().view(np.uint16))
+    q = synth.bf16_bits_to_f32(inp.q).astype(np.float64)
+    ref = oatt.decode_attention(q, int2, bf, inp.seq_lens, inp.bt_q, inp.bt_h, tiny_rot.r_k, tiny_rot.r_v,
+                                w.n_sink, w.n_recent)
+    for b, L in enumerate(lens):
+        if L == 0:
+            assert np.all(got[b] == 0)
+        else:
+            gh.assert_attention_close(got[b], ref[b], f"seq {b} len {L}")
+
+
+def test_bf16_baseline_balanced_slices(tiny_rot):
+    from oracle import attention as oatt
+    lens = np.random.default_rng(12).integers(1, 600, size=72)
+    w = _tiny(batch=len(lens), n_sink=100000, n_recent=0)   # every token in BF16 pages
+    inp = synth.decode_inputs(w, seq_lens=lens)
+    gc = gh.alloc_cache(inp, tiny_rot)
+    gh.gpu_fill(inp, tiny_rot, gc)
+    print(f"[bf16 baseline balanced slices] B={len(lens)}", flush=True)
+    got = gh.gpu_decode(inp, gc, all_raw=True)
+    q = synth.bf16_bits_to_f32(inp.q).astype(np.float64)
+    for b, L in enumerate(lens):
+        k = olayout.bf16_to_f64(inp.k_rows[inp.row_of[b], 0]); v = olayout.bf16_to_f64(inp.v_rows[inp.row_of[b], 0])
+        ref = oatt.softmax_attention(q[b], k, v, 1 / 8.0)
+        gh.assert_attention_close(got[b], ref, f"bf16 baseline seq {b}")
+
+
 def test_abi_rejects_bad_arguments_on_device():
     w = _tiny()
     with pytest.raises(lib.OscarError) as e:
