@@ -13,6 +13,11 @@ Prints ONE JSON line (rank 0):
                (HIP events on the launch stream around K decode launches back
                to back over the same cache copies, a second pass) vs 8 TB/s
   cpu_baseline the float64 NumPy oracle decoding the same cache on host cores
+
+--append-prefill measures quantize-append alone on the large-GQA layer's
+prefill (8 sequences x 8192 rows, 96 q / 8 KV heads, d = 128) and prints the
+same kind of line for it (rows/s, roofline of the quantize-append kernel, the
+oracle quantizing a sample of the rows).
 """
 from __future__ import annotations
 
@@ -60,23 +65,27 @@ def algorithmic_bytes(inp, w) -> dict:
     return parts
 
 
-def measured_traffic(workload: str):
-    """HBM bytes per decode launch from the committed rocprofv3 counter summary
-    for this workload (FETCH_SIZE / WRITE_SIZE scaled by a plain-copy
-    calibration), or None when there is none or the decode sources changed
+DECODE_SOURCES = ["decode.hip", "device_utils.h", "layout.h"]
+APPEND_SOURCES = ["quantize_append.hip", "device_utils.h", "layout.h"]
+
+
+def measured_traffic(workload: str, kernel: str = "decode_kernel", sources=DECODE_SOURCES):
+    """HBM bytes per launch of ``kernel`` from the committed rocprofv3 counter
+    summary for this workload (FETCH_SIZE / WRITE_SIZE scaled by a plain-copy
+    calibration), or None when there is none or the kernel's sources changed
     since the counters were taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", f"decode_kernel_{workload}_hbm_counters.txt")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_hbm_counters.txt")
     if not os.path.exists(path):
         return None
     h = hashlib.sha256()
-    for f in ["decode.hip", "device_utils.h", "layout.h"]:
+    for f in sources:
         with open(os.path.join(ROOT, "int2_rotated_kv_oscar_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     digest, traffic = None, None
     with open(path) as fh:
         for line in fh:
-            if line.startswith("decode sources sha256[:16] = "):
+            if line.startswith("sources sha256[:16] = ") or line.startswith("decode sources sha256[:16] = "):
                 digest = line.split("=")[1].strip()
             if line.startswith("traffic_bytes = "):
                 traffic = int(line.split("=")[1].strip())
@@ -95,6 +104,8 @@ def main() -> int:
     ap.add_argument("--no-bf16-baseline", action="store_true")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (calibrates HBM byte counters), then exit")
+    ap.add_argument("--append-prefill", action="store_true",
+                    help="measure quantize-append alone on the large-GQA layer's prefill (8 sequences x 8192 rows)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the decode path shards by KV head "
@@ -121,6 +132,8 @@ def main() -> int:
         log(f"copy probe: 5 copies of {n} B")
         return 0
     lib.load()
+    if args.append_prefill:
+        return run_append_prefill(args, log)
     w = synth.WORKLOADS[args.workload]
     t0 = time.time()
     inp = synth.decode_inputs(w)
@@ -263,6 +276,124 @@ def main() -> int:
         result["cpu_baseline"] = _cpu_baseline(inp, w, cache, int2, bf16, rt, tokens, log)
     print(json.dumps(result), flush=True)
     return 0
+
+
+PREFILL_METRIC = "INT2 quantize-append rows/s + achieved HBM GB/s (% of peak), 96q/8kv layer prefill"
+
+
+def append_bytes(n_rows: int, n_kv: int, d: int, n_pages: int) -> int:
+    """Unique bytes one quantize-append launch must move: per row, KV head and
+    tensor the bf16 row in (2d B), its codes (d/4 B) and f16 scale/zero
+    (2 x 2 (d/32) B) out; R_K and R_V (f32); row_seq/row_pos; one table entry
+    per page written."""
+    per = 2 * d + d // 4 + 4 * (d // 32)
+    return n_rows * n_kv * 2 * per + 2 * n_kv * d * d * 4 + n_rows * 8 + n_pages * 4
+
+
+def run_append_prefill(args, log) -> int:
+    """Kernel A alone on the large-GQA layer's prefill: 8 sequences append an
+    8192-token chunk each (page-aligned, shuffled pages), 8 KV heads, d = 128.
+    The timed launches rotate over input/pool copies totalling >= 1 GiB."""
+    import torch
+    from int2_rotated_kv_oscar_amd import lib, synth
+    dev = "cuda:0"
+    w = synth.WORKLOADS["gqa96-b64-ragged"]
+    n_seq, chunk = 8, 8192
+    t0 = time.time()
+    k, v, row_seq, row_pos = synth.prefill_rows(w, n_seq, chunk)
+    pages_per = (chunk + 15) // 16
+    bt = synth.rng_for(w.cfg_id, 7).permutation(n_seq * pages_per).astype(np.int32).reshape(n_seq, pages_per)
+    # the rotation is an input of the kernel; 1024 calibration rows per KV
+    # head keep the host calibration short (its size does not change the work)
+    cal = synth.calibration_set(w, n_rows=1024)
+    rt = lib.build_rotation(cal.q, cal.k, cal.v, w.group_q)
+    log(f"prefill rows {k.shape} + calibration {time.time() - t0:.1f}s")
+    tau_k, tau_v = float(np.float32(rt["tau_k"])), float(np.float32(rt["tau_v"]))
+    n_rows = len(row_seq)
+    n_pages = n_seq * pages_per
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    nbq = lib.int2_page_bytes(w.d, w.n_kv_heads)
+    per_copy = 2 * k.nbytes + n_pages * nbq
+    copies = args.copies or max(1, int(np.ceil((1 << 30) / per_copy)))
+    sets = []
+    base = (bf(k), bf(v), i32(row_seq), i32(row_pos), i32(bt),
+            torch.from_numpy(rt["r_k"].astype(np.float32)).to(dev),
+            torch.from_numpy(rt["r_v"].astype(np.float32)).to(dev))
+    for c in range(copies):
+        t = base if c == 0 else tuple(x.clone() for x in base)
+        pool = torch.zeros(n_pages * nbq, dtype=torch.uint8, device=dev)
+        sets.append((lib.make_cache(w.d, w.n_kv_heads, w.n_sink, w.n_recent, pool, None), t))
+    log(f"{n_rows} rows x {w.n_kv_heads} KV heads; {per_copy / 1e6:.1f} MB x {copies} copies")
+
+    def launch(i):
+        c, (kk, vv, rs, rp, bb, rk, rv) = sets[i % copies]
+        lib.quantize_append(c, kk, vv, rs, rp, bb, rk, rv, tau_k, tau_v)
+
+    for i in range(args.warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    # HIP events on the stream the binding launches on (torch's current one)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(K):
+        launch(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    nbytes = append_bytes(n_rows, w.n_kv_heads, w.d, n_pages)
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    flops = 2 * n_rows * w.n_kv_heads * 2 * w.d * w.d  # the rotation y = x R, K and V
+    log(f"quantize_append {ms * 1e3:.1f} us, {achieved:.0f} GB/s, {flops / (ms * 1e-3) / 1e12:.1f} TFLOP/s (x2 split)")
+    result = {
+        "metric": PREFILL_METRIC, "value": round(n_rows / (ms * 1e-3), 1), "unit": "rows/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 in, f16 hi/lo MFMA, f32 accumulate, int2 out",
+        "data": "synthetic",
+        "config": {"workload": "gqa96-prefill-8x8192", "sequences": n_seq, "rows_per_sequence": chunk,
+                   "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads, "head_dim": w.d, "page_tokens": 16,
+                   "copies": copies},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic("gqa96-prefill-8x8192", "quantize_append_kernel", APPEND_SOURCES),
+                     "kernel": "quantize_append_kernel<128,false>", "algorithmic_bytes_per_launch": nbytes,
+                     "avg_launch_us": round(ms * 1e3, 2),
+                     "mfma_tflops_algorithmic": round(flops / (ms * 1e-3) / 1e12, 2)},
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = _cpu_append_baseline(k, v, row_seq, row_pos, bt, rt, w, n_rows, log)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def _cpu_append_baseline(k, v, row_seq, row_pos, bt, rt, w, n_rows, log) -> dict:
+    """The oracle (float64 NumPy) quantizing a bounded sample of the same rows."""
+    from oracle import cache as ocache
+    from oracle import layout as olayout
+    cores = len(os.sched_getaffinity(0))
+    rk = rt["r_k"].astype(np.float32).astype(np.float64)
+    rv = rt["r_v"].astype(np.float32).astype(np.float64)
+    n_pages = bt.size
+    done, dt, n = 0, 0.0, 256
+    while dt < 10.0 and done < n_rows:
+        sel = slice(done, min(n_rows, done + n))
+        pool = olayout.Int2Pool(n_pages, w.n_kv_heads, w.d)
+        t0 = time.time()
+        ocache.quantize_append(pool, k[sel], v[sel], row_seq[sel], row_pos[sel], bt, rk, rv,
+                               float(np.float32(rt["tau_k"])), float(np.float32(rt["tau_v"])), olayout.bf16_to_f64)
+        dt += time.time() - t0
+        done = sel.stop
+        n *= 2
+    log(f"cpu oracle: {done} rows in {dt:.1f}s on {cores} cores")
+    return {"value": round(done / dt, 1), "unit": "rows/s", "cores": cores, "kind": "oracle",
+            "sample": f"oracle float64 quantize-append of the first {done} of the {n_rows} rows "
+                      f"(all {w.n_kv_heads} KV heads, K and V); numpy BLAS threads = {cores}"}
 
 
 def _all_bf16_tables(inp):
