@@ -205,14 +205,6 @@ struct PairDma {
 };
 constexpr int kRing = 6;  // pair slots per wave: the two steps being computed and two pairs in flight
 
-// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding), and no memory
-// access moved across it: LDS written by the ring loads is read after it.
-template <int N>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-  asm volatile("" ::: "memory");
-}
 
 // SLICES: balanced slices over all units (several segments per workgroup),
 // else per-unit items (one segment per workgroup, early requests).  Separate

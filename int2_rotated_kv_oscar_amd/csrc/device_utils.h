@@ -94,6 +94,27 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// s_waitcnt vmcnt(N), other counters untouched (gfx9 encoding), and no memory
+// access moved across it: LDS written by global_load_lds (whose completion the
+// compiler does not track) is read after it.
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+  asm volatile("" ::: "memory");
+}
+
+// Workgroup barrier after this wave's own LDS reads and writes completed
+// (lgkmcnt(0)), with global_load_lds requests still in flight: a release
+// fence on LDS would also wait for those (vmcnt(0)).  LDS written by such
+// requests is covered by wait_vm, not by this barrier.
+__device__ __forceinline__ void lds_barrier_keep_dma() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt 63, expcnt 7: not waited for
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // Cross-row exchange without LDS: v_permlane16_swap / v_permlane32_swap on two
 // copies of v leave, in every lane, the values of rows (r, r^1) or (r, r^2) of
 // 16 lanes as the pair (first, second) in the same order for both rows, so a

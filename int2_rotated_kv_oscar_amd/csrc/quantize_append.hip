@@ -7,12 +7,13 @@
 // A workgroup takes one (KV head, tensor) and loops over tiles of 16 rows,
 // one wave per 32-channel group (so group statistics stay inside a wave).  The
 // rotation y = x . R is a dense 16 x d x d product per tile and runs on the
-// 16x16x32 bf16 MFMA: x is exact in bf16, R (float32) is split exactly into
-// three bf16 parts, so y is float32-accurate.  Tiles use the transposed
-// product y^T = R^T x^T, whose output lane layout (one row per lane, 4
-// consecutive channels per 16-channel block) keeps a 32-channel group inside
-// one wave over its 4 lane quads: group min/max take two cross-lane steps.
-// Codes are OR-combined into the page's word layout in LDS; a tile that is
+// 16x16x32 f16 MFMA: x is converted exactly from bf16 to f16, 256 R (float32)
+// is split into f16 hi + lo parts (22 significant bits), so y is accurate to
+// about 2^-22 relative.  Tiles use the transposed product y^T = R^T x^T,
+// whose output lane layout (one row per lane, 4 consecutive channels per
+// 16-channel block) keeps a 32-channel group inside one wave over its 4 lane
+// quads: group min/max take three lane swaps.  Each wave's code bits go to
+// LDS and are OR-combined into the page's words when stored; a tile that is
 // one whole page is written with plain coalesced stores, scattered rows with
 // per-field atomic updates.
 #include <algorithm>
@@ -40,48 +41,78 @@ struct QAParams {
   int32_t n_kv;
 };
 
-// Group statistics -> f16 scale/zero (RNE) and a code generator.  s is
-// (max - min) / 3 taken as a product with fp32(1/3) and the reciprocal of the
-// stored f16 scale is the hardware approximation: both stay far inside the
-// agreement windows (1e-6 of the group range for s, 1e-5 of a step for codes).
-struct GroupQ {
-  float zf, inv;
-  uint32_t s16, z16;
-  __device__ __forceinline__ void make(float mn, float mx) {
-    s16 = f16_bits((mx - mn) * (1.0f / 3.0f));
-    z16 = f16_bits(mn);
-    const float sf = f16_to_f32(s16);
-    zf = f16_to_f32(z16);
-    inv = sf == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(sf);  // s16 = 0: every code is 0
-  }
-  __device__ __forceinline__ uint32_t code(float y) const {
-    const float t = __builtin_rintf((y - zf) * inv);
-    return uint32_t(__builtin_amdgcn_fmed3f(t, 0.0f, 3.0f));
-  }
-};
-
 // Per-tile row metadata: lane l16 describes row tile*16 + l16 (all quads hold
-// the same), page -1 for rows past n_rows.
+// the same).
 struct TileMeta {
   int32_t page, slot;
   bool valid;    // the row exists (page is meaningful only then)
   bool aligned;  // 16 consecutive positions of one sequence starting on a page boundary
 };
 
+// Codes through the float adder: fma(v - z, 1/s, 1.5 * 2^23) rounds the
+// scaled value to the nearest integer (ties to even) in the low mantissa bits,
+// so the clamp to [0, 3] is an integer med3 on the bit pattern (monotone for
+// every finite value, negative ones included) and the packing adds the pattern
+// shifted into place; the shifted copies of the constant part are removed by
+// starting each word from minus their sum (all modulo 2^32).
+constexpr float kMagic = 12582912.0f;
+constexpr uint32_t kMagicBits = 0x4B400000u;
+__device__ __forceinline__ uint32_t code_bits(float v, float z, float inv) {
+  const int b = __float_as_int(__builtin_fmaf(v - z, inv, kMagic));
+  return uint32_t(min(max(b, int(kMagicBits)), int(kMagicBits + 3u)));
+}
+
+// Reduction over the four lanes l16 + 16q of a row: the minimum of mn and the
+// maximum of mx, both computed in every lane with three lane swaps (the lower
+// half of the wave carries the minima, the upper half the negated maxima).
+__device__ __forceinline__ void row_min_max(float& mn, float& mx) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(mn), __float_as_uint(-mx), false, false);
+  const float c = fminf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(c), __float_as_uint(c), false, false);
+  const float e = fminf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+  auto f = __builtin_amdgcn_permlane32_swap(__float_as_uint(e), __float_as_uint(e), false, false);
+  mn = __uint_as_float(f[0]);
+  mx = -__uint_as_float(f[1]);
+}
+
+// LDS of a workgroup (shared by the K and V instances of the tile loop).
+template <int D, bool ONE>
+struct QAShared {
+  static constexpr int NG = D / 32;
+  // tiles in flight per workgroup: x and page ids of kX tiles, positions of kS
+  static constexpr int kX = ONE ? 1 : 4, kS = ONE ? 1 : 8;
+  static constexpr int kRowBytes = 2 * D + 16;  // padded LDS row of the x tile (conflict-free operand reads)
+  // Rings filled by global_load_lds (no registers hold requests in flight):
+  // wave g's quarter of the raw bf16 x tile (rows 4g .. 4g+3 for d = 128,
+  // 1 KB), its copy of the tile's row_seq (lanes 0-15) and row_pos (lanes
+  // 16-31) and of the rows' page ids (lanes 0-15).  Each wave reads only what
+  // it requested itself.
+  __attribute__((aligned(16))) uint8_t raw[kX][NG][1024];
+  int32_t sp[kS][NG][64];
+  int32_t pg[kX][NG][64];
+  // x tiles in f16, each wave's code bits of a tile (by word lane) and its
+  // f16 scales/zeros in page-area order; double-buffered
+  __attribute__((aligned(16))) uint8_t x[2][16 * kRowBytes];
+  uint32_t part[2][NG][64];
+  uint32_t sz[2][16 * NG];  // [scale area | zero area] as u32 pairs of f16
+  int32_t rexp[2][16];      // per-row power-of-two prescale of the x tile
+};
+
 // ONE: every workgroup has exactly one tile (a decode step's appends)
 template <int D, int TENSOR, bool ONE>
-__device__ void qa_tiles(const QAParams& p, int h) {
+__device__ void qa_tiles(const QAParams& p, int h, QAShared<D, ONE>& sh) {
   using GG = Geo<D>;
   constexpr int NG = GG::NG, NKB = GG::NKB, NW = GG::NW;
-  constexpr int kDepth = 4;              // tiles in flight per workgroup
+  constexpr int kX = QAShared<D, ONE>::kX, kS = QAShared<D, ONE>::kS;
+  constexpr int kRowBytes = QAShared<D, ONE>::kRowBytes;
   constexpr float kRScale = 256.0f;
-  constexpr int kRowBytes = 2 * D + 16;  // padded LDS row of the x tile (conflict-free operand reads)
-  // x tiles (double-buffered), code words of a tile (one slot per lane,
-  // OR-combined by the NG waves) and its f16 scales/zeros in page-area order
-  __shared__ __attribute__((aligned(16))) uint8_t s_x[2][16 * kRowBytes];
-  __shared__ uint32_t s_words[2][64][NW];
-  __shared__ uint32_t s_sz[2][16 * NG];  // [scale area | zero area] as u32 pairs of f16
-  __shared__ int32_t s_rexp[2][16];       // per-row power-of-two prescale of the x tile
+  auto& s_raw = sh.raw;
+  auto& s_sp = sh.sp;
+  auto& s_pg = sh.pg;
+  auto& s_x = sh.x;
+  auto& s_part = sh.part;
+  auto& s_sz = sh.sz;
+  auto& s_rexp = sh.rexp;
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, quad = lane >> 4;
   const int g = __builtin_amdgcn_readfirstlane(tid >> 6);
   const uint16_t* X = TENSOR ? p.v_new : p.k_new;
@@ -90,28 +121,43 @@ __device__ void qa_tiles(const QAParams& p, int h) {
   const int64_t n_tiles = (p.n_rows + 15) / 16;
   const int64_t n_mine = (n_tiles - blockIdx.x + gridDim.x - 1) / gridDim.x;  // >= 1 by the grid size
 
-  for (int i = tid; i < 2 * 64 * NW; i += 64 * NG) (&s_words[0][0][0])[i] = 0u;
-
   // The i-th tile of this workgroup (clamped: past the end repeats the last).
-  auto tile_of = [&](int64_t i) { return int64_t(blockIdx.x) + min(i, n_mine - 1) * int64_t(gridDim.x); };
-  // Ring of tiles in flight: wave g holds rows 4g .. 4g+3 of a tile (16 B per
-  // lane), every lane the position of row l16.  Rows past n_rows re-read the
-  // last row; their results are never stored.
+  auto tile_of = [&](int64_t i) { return int64_t(blockIdx.x) + (i < n_mine ? i : n_mine - 1) * int64_t(gridDim.x); };
+  // rows of tile t (1 .. 16)
+  auto rows_of = [&](int64_t t) { const int64_t rem = p.n_rows - t * 16; return rem < 16 ? int(rem) : 16; };
+  // Requests of the ring: lane l of wave g loads 16 B of row 4g + l/16 (for
+  // d = 128) of the tile; rows past n_rows re-read the last row, tiles past
+  // the workgroup's last re-read that tile (their results are never stored).
   constexpr int kQuarterRows = 16 / NG;        // rows of a tile per wave
   constexpr int kChunks = 2 * D / 16;          // 16-byte chunks per row
   static_assert(kQuarterRows * kChunks == 64, "one 16-byte chunk per lane");
-  u32x4 xr[kDepth];
-  int32_t sr[kDepth], pr[kDepth];
-  auto issue = [&](int u, int64_t i) {
+  const int xrow = kQuarterRows * g + lane / kChunks;
+  const uint32_t xcol = 8u * uint32_t(lane % kChunks);
+  const uint32_t row_elems = uint32_t(p.n_kv) * D;
+  auto issue_x = [&](int64_t i) {  // x quarter of tile i
     const int64_t t = tile_of(i);
-    const int64_t xrow = min(t * 16 + kQuarterRows * g + lane / kChunks, p.n_rows - 1);
-    xr[u] = *reinterpret_cast<const u32x4*>(X + (xrow * p.n_kv + h) * D + 8 * (lane % kChunks));
-    const int64_t row = min(t * 16 + l16, p.n_rows - 1);
-    sr[u] = p.row_seq[row];
-    pr[u] = p.row_pos[row];
+    const uint16_t* xb = X + (t * 16 * p.n_kv + h) * D;
+    __builtin_amdgcn_global_load_lds(xb + (uint32_t(min(xrow, rows_of(t) - 1)) * row_elems + xcol),
+                                     &s_raw[i % kX][g][0], 16, 0, 0);
   };
+  auto issue_sp = [&](int64_t i) {  // positions of tile i
+    const int64_t t = tile_of(i);
+    const int32_t* sp = ((lane & 16) ? p.row_pos : p.row_seq) + t * 16;
+    __builtin_amdgcn_global_load_lds(sp + min(lane & 15, rows_of(t) - 1), &s_sp[i % kS][g][0], 4, 0, 0);
+  };
+  auto issue_pages = [&](int64_t i) {  // page ids of tile i's rows (its positions have landed)
+    const int32_t seq = s_sp[i % kS][g][l16], pos = s_sp[i % kS][g][16 + l16];
+    __builtin_amdgcn_global_load_lds(p.bt_q + (int64_t(seq) * p.max_pages + (pos >> 4)), &s_pg[i % kX][g][0], 4, 0, 0);
+  };
+  // positions first: the page ids need them
 #pragma unroll
-  for (int u = 0; u < (ONE ? 1 : kDepth); ++u) issue(u, u);  // requested before R: the latencies overlap
+  for (int u = 0; u < kS; ++u) issue_sp(u);
+  wait_vm<0>();
+#pragma unroll
+  for (int u = 0; u < kX; ++u) {
+    issue_pages(u);
+    issue_x(u);
+  }
 
   // R operands of this group, split once: 256 R (a power of two keeps the
   // low parts out of the f16 subnormal range) as f16 hi + lo, 22 significant
@@ -135,63 +181,94 @@ __device__ void qa_tiles(const QAParams& p, int h) {
       rop[hb][kb][1] = u32x4{pl[0], pl[1], pl[2], pl[3]};
     }
 
+  // Where this lane's code bits go.  K: word (quad*16 + m)*NW + g/2 of row
+  // m = l16 is lane `lane`'s, its fields at 16(r%2) + 8(g%2) + 4hb + 2(r/2).
+  // V: after combining the four rows of a word across the lane quartet, lane
+  // m writes word ((m/4)*16 + 4quad + m%4)*NW + g/2, its fields at
+  // sh + 2((2g + hb)%4) with sh = 16(m%2) + 8((m/2)%2).
+  const int pidx = TENSOR == 0 ? lane : ((l16 >> 2) * 16 + 4 * quad + (l16 & 3));
+  const uint32_t vsh = 16u * (l16 & 1) + 8u * ((l16 >> 1) & 1);
+  const uint32_t vsh0 = vsh + 2u * ((2 * g) & 3), vsh1 = vsh + 2u * ((2 * g + 1) & 3);
+  uint32_t word0;  // minus the sum of the shifted constant parts of one word's fields
+  if (TENSOR == 0) {
+    uint32_t c = 0;
+#pragma unroll
+    for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) c += kMagicBits << (16 * (r & 1) + 8 * (g & 1) + 4 * hb + 2 * (r >> 1));
+    word0 = 0u - c;
+  } else {
+    word0 = 0u - ((kMagicBits << vsh0) + (kMagicBits << vsh1));
+  }
 
-  // stores of a finished tile: wave 0 the codes (then clears its word buffer),
-  // wave 1 the scale/zero areas of an aligned tile
+  // stores of a finished tile: wave 0 the codes, wave 1 the scales/zeros
   auto store_tile = [&](const TileMeta& mc, int buf) {
-    if (g == 0) {
-      if (TENSOR == 0) {
-        if (mc.valid) {  // K code words hold a single token: plain stores
-          uint8_t* base = p.pool + (int64_t(mc.page) * p.n_kv + h) * int64_t(GG::HEAD_BYTES);
-          uint32_t* kc = reinterpret_cast<uint32_t*>(base + GG::KC) + (quad * 16 + mc.slot) * NW;
-#pragma unroll
-          for (int w = 0; w < NW; ++w) kc[w] = s_words[buf][lane][w];
-        }
-      } else if (mc.aligned) {
-        // 16 rows = slots 0..15 of one page: the words are the page's VC words
-        const int page0 = __shfl(mc.page, 0, 64);
+    if (g > 1) return;
+    if (g == 1) {
+      if (mc.aligned) {
+        // scale and zero areas of the page are contiguous: 2 x 32 NG bytes
+        const int page0 = __builtin_amdgcn_readfirstlane(mc.page);
         uint8_t* base = p.pool + (int64_t(page0) * p.n_kv + h) * int64_t(GG::HEAD_BYTES);
-        uint32_t* vc = reinterpret_cast<uint32_t*>(base + GG::VC) + lane * NW;
-#pragma unroll
-        for (int w = 0; w < NW; ++w) vc[w] = s_words[buf][lane][w];
+        uint32_t* dst = reinterpret_cast<uint32_t*>(base + (TENSOR == 0 ? GG::KS : GG::VS));
+        if (lane < 16 * NG) dst[lane] = s_sz[buf][lane];
       } else {
-        // rows of different pages/slots: replace this row's 2-bit fields with
-        // an atomic xor (other rows may update other fields of the same word)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int vpage = __shfl(mc.valid ? mc.page : -1, 4 * quad + r, 64), vslot = __shfl(mc.slot, 4 * quad + r, 64);
-          if (vpage < 0) continue;
-          uint8_t* base = p.pool + (int64_t(vpage) * p.n_kv + h) * int64_t(GG::HEAD_BYTES);
-          const int sh = 16 * (vslot & 1) + 8 * ((vslot >> 1) & 1);
-          uint32_t* vc = reinterpret_cast<uint32_t*>(base + GG::VC) + ((vslot >> 2) * 16 + l16) * NW;
-#pragma unroll
-          for (int w = 0; w < NW; ++w) {
-            const uint32_t bits = ((s_words[buf][lane][w] >> (16 * (r & 1) + 8 * (r >> 1))) & 0xFFu) << sh;
-            const uint32_t mask = 0xFFu << sh;
-            const uint32_t old = __hip_atomic_load(vc + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            const uint32_t delta = (old & mask) ^ bits;
-            if (delta) atomicXor(vc + w, delta);
-          }
+        // lane j: row m = j / NG, group gg = j % NG, to that row's page and slot
+        const int m = min(lane / NG, 15), gg = lane % NG;
+        const int page = __shfl(mc.page, m, 64), slot = __shfl(mc.slot, m, 64);
+        const bool valid = __shfl(int(mc.valid), m, 64) != 0;
+        if (lane < 16 * NG && valid) {
+          const uint16_t* sz16 = reinterpret_cast<const uint16_t*>(s_sz[buf]);
+          const int ia = TENSOR == 0 ? m * NG + gg : ((m >> 2) * NG + gg) * 4 + (m & 3);
+          const int iu = TENSOR == 0 ? slot * NG + gg : ((slot >> 2) * NG + gg) * 4 + (slot & 3);
+          uint8_t* base = p.pool + (int64_t(page) * p.n_kv + h) * int64_t(GG::HEAD_BYTES);
+          reinterpret_cast<uint16_t*>(base + (TENSOR == 0 ? GG::KS : GG::VS))[iu] = sz16[ia];
+          reinterpret_cast<uint16_t*>(base + (TENSOR == 0 ? GG::KZ : GG::VZ))[iu] = sz16[16 * NG + ia];
         }
       }
+      return;
+    }
+    uint32_t wd[NW];
 #pragma unroll
-      for (int w = 0; w < NW; ++w) s_words[buf][lane][w] = 0u;
-    } else if (g == 1 && mc.aligned) {
-      // scale and zero areas of the page are contiguous: 2 x 32 NG bytes
-      const int page0 = __shfl(mc.page, 0, 64);
+    for (int w = 0; w < NW; ++w) wd[w] = s_part[buf][2 * w][lane] | s_part[buf][2 * w + 1][lane];
+    if (mc.aligned) {
+      // 16 rows = slots 0..15 of one page: the words are the page's code words
+      const int page0 = __builtin_amdgcn_readfirstlane(mc.page);
       uint8_t* base = p.pool + (int64_t(page0) * p.n_kv + h) * int64_t(GG::HEAD_BYTES);
-      uint32_t* dst = reinterpret_cast<uint32_t*>(base + (TENSOR == 0 ? GG::KS : GG::VS));
-      for (int i = lane; i < 16 * NG; i += 64) dst[i] = s_sz[buf][i];
+      uint32_t* dst = reinterpret_cast<uint32_t*>(base + (TENSOR == 0 ? GG::KC : GG::VC)) + lane * NW;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) dst[w] = wd[w];
+    } else if (TENSOR == 0) {
+      if (mc.valid) {  // K code words hold a single token: plain stores
+        uint8_t* base = p.pool + (int64_t(mc.page) * p.n_kv + h) * int64_t(GG::HEAD_BYTES);
+        uint32_t* kc = reinterpret_cast<uint32_t*>(base + GG::KC) + (quad * 16 + mc.slot) * NW;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) kc[w] = wd[w];
+      }
+    } else {
+      // rows of different pages/slots: replace this row's 2-bit fields with
+      // an atomic and (clear) and an atomic or (set); other rows may update
+      // other fields of the same word meanwhile
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int vpage = __shfl(mc.valid ? mc.page : -1, 4 * quad + r, 64), vslot = __shfl(mc.slot, 4 * quad + r, 64);
+        if (vpage < 0) continue;
+        uint8_t* base = p.pool + (int64_t(vpage) * p.n_kv + h) * int64_t(GG::HEAD_BYTES);
+        const int sh = 16 * (vslot & 1) + 8 * ((vslot >> 1) & 1);
+        uint32_t* vc = reinterpret_cast<uint32_t*>(base + GG::VC) + ((vslot >> 2) * 16 + l16) * NW;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) {
+          const uint32_t bits = ((wd[w] >> (16 * (r & 1) + 8 * (r >> 1))) & 0xFFu) << sh;
+          atomicAnd(vc + w, ~(0xFFu << sh));
+          atomicOr(vc + w, bits);
+        }
+      }
     }
   };
 
-  // Three-stage software pipeline over tiles: at step i the MFMAs of tile i run
-  // while the epilogue of tile i-1 (codes, scales into LDS) executes, and the
-  // words of tile i-2 are stored.  One barrier per step.
-  auto epilogue = [&](const f32x4 (&acc)[2], const TileMeta& mc, int rexp, int buf) {
-    // ---- epilogue for group g: acc[hb][r] = y / F for row m = l16, channel
+  auto epilogue = [&](const f32x4 (&acc)[2], int rexp, int buf) {
+    // ---- group g of row m = l16: acc[hb][r] = y / F for channel
     // 32g + 16hb + 4quad + r, F = 2^(e - 8) (R scale and row prescale); the
-    // clip, the codes and the statistics run on acc with F folded into them ----
+    // clip, the statistics and the codes run on acc with F folded in ----
     const float F = __builtin_ldexpf(1.0f, rexp - 8), iF = __builtin_ldexpf(1.0f, 8 - rexp);
     const float tc = tau * iF;
     float y[2][4];
@@ -199,53 +276,48 @@ __device__ void qa_tiles(const QAParams& p, int h) {
     for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
       for (int r = 0; r < 4; ++r) y[hb][r] = __builtin_amdgcn_fmed3f(acc[hb][r], -tc, tc);
-    float mn = fminf(fminf(fminf(y[0][0], y[0][1]), fminf(y[0][2], y[0][3])),
-                     fminf(fminf(y[1][0], y[1][1]), fminf(y[1][2], y[1][3])));
-    float mx = fmaxf(fmaxf(fmaxf(y[0][0], y[0][1]), fmaxf(y[0][2], y[0][3])),
-                     fmaxf(fmaxf(y[1][0], y[1][1]), fmaxf(y[1][2], y[1][3])));
-    GroupQ q; q.make(wave_min16(mn) * F, wave_max16(mx) * F);
-    q.zf *= iF;   // codes from acc directly: (y - z) / s = (acc - z/F) / (s/F)
-    q.inv *= F;
-    uint16_t* sz16 = reinterpret_cast<uint16_t*>(s_sz[buf]);
+    float mn = fminf(fminf(fminf(y[0][0], y[0][1]), y[0][2]), fminf(fminf(y[0][3], y[1][0]), y[1][1]));
+    mn = fminf(mn, fminf(y[1][2], y[1][3]));
+    float mx = fmaxf(fmaxf(fmaxf(y[0][0], y[0][1]), y[0][2]), fmaxf(fmaxf(y[0][3], y[1][0]), y[1][1]));
+    mx = fmaxf(mx, fmaxf(y[1][2], y[1][3]));
+    row_min_max(mn, mx);
+    // s = (max - min) / 3 and z = min in true units (F is a power of two:
+    // the scalings are exact), rounded to f16; codes against the f16 values
+    const uint32_t s16 = f16_bits((mx - mn) * (F * (1.0f / 3.0f)));
+    const uint32_t z16 = f16_bits(mn * F);
+    const float sf = f16_to_f32(s16);
+    const float inv = sf == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(sf);  // s16 = 0: every code is 0
+    const float zr = f16_to_f32(z16) * iF;  // (y - z) / s = (acc - z/F) / (s/F)
+    const float invr = inv * F;
     const int m = l16;
+    uint32_t bits;
     if (TENSOR == 0) {
-      // KC word (quad*16 + m)*NW + g/2 belongs to this lane
-      uint32_t bits = 0;
+      bits = word0;
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) bits |= q.code(y[hb][r]) << (16 * (r & 1) + 8 * (g & 1) + 4 * hb + 2 * (r >> 1));
-      atomicOr(&s_words[buf][lane][g / 2], bits);
+        for (int r = 0; r < 4; ++r)
+          bits += code_bits(y[hb][r], zr, invr) << (16 * (r & 1) + 8 * (g & 1) + 4 * hb + 2 * (r >> 1));
     } else {
-      // VC word ((m/4)*16 + c16)*NW + w, c16 = 4quad + r, w = g/2; tile row m
-      // at bit 16(m%2) + 8((m/2)%2), block bb = (2g + hb)%4 at 2bb
-      // the four rows m = 4j..4j+3 (consecutive lanes) share these words: their
-      // fields are OR-combined across the lane quartet first, then lane m
-      // writes word r = m%4, one writer per word and wave
-      const int sh = 16 * (m & 1) + 8 * ((m >> 1) & 1);
-      uint32_t mine = 0;
+      // the four rows m = 4j..4j+3 (consecutive lanes) share these words:
+      // their fields are OR-combined across the lane quartet, then lane m
+      // keeps word r = m%4, one writer per word and wave
+      bits = 0;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        uint32_t bits = (q.code(y[0][r]) << (sh + 2 * ((2 * g) & 3))) |
-                        (q.code(y[1][r]) << (sh + 2 * ((2 * g + 1) & 3)));
-        bits |= uint32_t(__builtin_amdgcn_mov_dpp(int(bits), 0xB1, 0xF, 0xF, false));  // lanes ^1
-        bits |= uint32_t(__builtin_amdgcn_mov_dpp(int(bits), 0x4E, 0xF, 0xF, false));  // lanes ^2
-        if ((m & 3) == r) mine = bits;
+        uint32_t wr = (code_bits(y[0][r], zr, invr) << vsh0) + word0;
+        wr += code_bits(y[1][r], zr, invr) << vsh1;
+        wr |= uint32_t(__builtin_amdgcn_mov_dpp(int(wr), 0xB1, 0xF, 0xF, false));  // lanes ^1
+        wr |= uint32_t(__builtin_amdgcn_mov_dpp(int(wr), 0x4E, 0xF, 0xF, false));  // lanes ^2
+        bits = (m & 3) == r ? wr : bits;
       }
-      atomicOr(&s_words[buf][(m >> 2) * 16 + 4 * quad + (m & 3)][g / 2], mine);
     }
-    if (quad == 0) {
-      const int ia = TENSOR == 0 ? m * NG + g : ((m >> 2) * NG + g) * 4 + (m & 3);  // aligned: slot = m
-      if (mc.aligned) {
-        sz16[ia] = uint16_t(q.s16);
-        sz16[16 * NG + ia] = uint16_t(q.z16);
-      } else if (mc.valid) {
-        uint8_t* base = p.pool + (int64_t(mc.page) * p.n_kv + h) * int64_t(GG::HEAD_BYTES);
-        const int s = mc.slot;
-        const int iu = TENSOR == 0 ? s * NG + g : ((s >> 2) * NG + g) * 4 + (s & 3);
-        reinterpret_cast<uint16_t*>(base + (TENSOR == 0 ? GG::KS : GG::VS))[iu] = uint16_t(q.s16);
-        reinterpret_cast<uint16_t*>(base + (TENSOR == 0 ? GG::KZ : GG::VZ))[iu] = uint16_t(q.z16);
-      }
+    s_part[buf][g][pidx] = bits;
+    if (quad == 0) {  // in the page-area order of an aligned tile (slot = m)
+      const int ia = TENSOR == 0 ? m * NG + g : ((m >> 2) * NG + g) * 4 + (m & 3);
+      uint16_t* sz16 = reinterpret_cast<uint16_t*>(s_sz[buf]);
+      sz16[ia] = uint16_t(s16);
+      sz16[16 * NG + ia] = uint16_t(z16);
     }
   };
 
@@ -254,17 +326,18 @@ __device__ void qa_tiles(const QAParams& p, int h) {
   // 2^-e (e recorded per row and undone in the epilogue) before conversion.
   auto stage_x = [&](const u32x4& v, int buf) {
     const int row = kQuarterRows * g + lane / kChunks;
-    bool big = false;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      big |= ((v[i] & 0x7F80u) >= (142u << 7)) | (((v[i] >> 16) & 0x7F80u) >= (142u << 7));
+    // largest bf16 magnitude of each half over the lane's 8 values
+    typedef unsigned short us2 __attribute__((ext_vector_type(2)));
+    us2 mm = __builtin_elementwise_max(
+        __builtin_elementwise_max(__builtin_bit_cast(us2, v[0] & 0x7FFF7FFFu), __builtin_bit_cast(us2, v[1] & 0x7FFF7FFFu)),
+        __builtin_elementwise_max(__builtin_bit_cast(us2, v[2] & 0x7FFF7FFFu), __builtin_bit_cast(us2, v[3] & 0x7FFF7FFFu)));
+    const uint32_t mb = __builtin_bit_cast(uint32_t, mm);
+    const bool big = (mb & 0xFFFFu) >= (142u << 7) || mb >= ((142u << 7) << 16);
     u32x4 o;
     int e = 0;
     if (__builtin_expect(__any(big), 0)) {
       // exponent of the row's largest value, over the row's kChunks lanes
-      int ex = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ex = max(ex, int(max(v[i] & 0x7F80u, (v[i] >> 16) & 0x7F80u) >> 7));
+      int ex = int(max(mb & 0x7F80u, (mb >> 16) & 0x7F80u) >> 7);
 #pragma unroll
       for (int msk = 1; msk < kChunks; msk <<= 1) ex = max(ex, __shfl_xor(ex, msk, 64));
       e = max(0, ex - 141);
@@ -279,100 +352,71 @@ __device__ void qa_tiles(const QAParams& p, int h) {
     if (lane % kChunks == 0) s_rexp[buf][row] = e;
   };
 
-  TileMeta m1 = {0, 0, false, false}, m2 = m1;
-  int rep = 0;  // row prescale of the tile whose epilogue runs next
-  f32x4 accp[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-  __syncthreads();  // s_words zeroed
-  if constexpr (ONE) {
-    // one tile for this workgroup: the same steps without the pipeline, two
-    // barriers instead of three rounds
-    stage_x(xr[0], 0);
+  // tile i's rows: page, slot, alignment (a uniform decision)
+  auto meta = [&](int64_t i) {
     TileMeta mc;
-    {
-      const int64_t t = tile_of(0);
-      const int32_t seq = sr[0], pos = pr[0];
-      mc.page = p.bt_q[int64_t(seq) * p.max_pages + (pos >> 4)];
-      mc.valid = t * 16 + l16 < p.n_rows;
-      mc.slot = pos & 15;
-      const int32_t seq0 = __shfl(seq, 0, 64), pos0 = __shfl(pos, 0, 64);
-      const bool ok = mc.valid && seq == seq0 && pos == pos0 + l16 && (pos0 & 15) == 0;
-      mc.aligned = (__ballot(ok) & 0xFFFFull) == 0xFFFFull;
+    const int rl = rows_of(tile_of(i));
+    const int32_t seq = s_sp[i % kS][g][l16], pos = s_sp[i % kS][g][16 + l16];
+    mc.valid = l16 < rl;
+    mc.page = s_pg[i % kX][g][l16];
+    mc.slot = pos & 15;
+    const int32_t seq0 = __builtin_amdgcn_readfirstlane(seq), pos0 = __builtin_amdgcn_readfirstlane(pos);
+    const bool ok = seq == seq0 && pos == pos0 + l16;
+    mc.aligned = rl == 16 && (pos0 & 15) == 0 && (__ballot(ok) & 0xFFFFull) == 0xFFFFull;
+    return mc;
+  };
+
+  wait_vm<0>();  // the first tiles' requests (R's plain loads drained them already)
+
+  // One barrier per tile: step i stages tile i, stores tile i-1 (its words
+  // completed before the barrier), then runs tile i's MFMAs and epilogue.
+  // After its stores every step issues the same three requests: positions of
+  // tile i+8, x and page ids of tile i+4 (from positions that landed four
+  // steps before).  A step waits for the requests of four steps before (at
+  // most nine requests younger), never for stores of the last three steps.
+  // Steps past the last tile re-request the clamped last tile and only store.
+  TileMeta mprev = {0, 0, false, false};
+  for (int64_t i = 0; i < n_mine + 1; ++i) {
+    const int buf = int(i & 1);
+    if (!ONE) wait_vm<9>();
+    stage_x(*reinterpret_cast<const u32x4*>(&s_raw[i % kX][g][16 * lane]), buf);
+    const TileMeta mc = meta(i);
+    lds_barrier_keep_dma();
+    if (i >= 1) store_tile(mprev, buf ^ 1);
+    if (!ONE) {
+      asm volatile("" ::: "memory");  // this step's ring reads are done before the refills are requested
+      issue_sp(i + kS);
+      issue_x(i + kX);
+      issue_pages(i + kX);
     }
-    lds_barrier();
-    f32x4 acc1[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-    {
+    if (i < n_mine) {
+      f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
       u32x4 xc[NKB];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) xc[kb] = *reinterpret_cast<const u32x4*>(&s_x[0][l16 * kRowBytes + 64 * kb + 16 * quad]);
+      for (int kb = 0; kb < NKB; ++kb)
+        xc[kb] = *reinterpret_cast<const u32x4*>(&s_x[buf][l16 * kRowBytes + 64 * kb + 16 * quad]);
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
         for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
-          for (int j = 1; j >= 0; --j) acc1[hb] = mfma_f16(rop[hb][kb][j], xc[kb], acc1[hb]);
+          for (int j = 1; j >= 0; --j)  // lo, then hi
+            acc[hb] = mfma_f16(rop[hb][kb][j], xc[kb], acc[hb]);
+      epilogue(acc, s_rexp[buf][l16], buf);
     }
-    epilogue(acc1, mc, s_rexp[0][l16], 0);
-    lds_barrier();
-    store_tile(mc, 0);
-  } else {
-  for (int64_t i0 = 0; i0 < n_mine + 2; i0 += kDepth) {
-#pragma unroll
-    for (int u = 0; u < kDepth; ++u) {
-      const int64_t i = i0 + u;
-      const int buf = int(i & 1);
-      // tile i: x quarter -> f16 in LDS, positions -> page, slot, alignment
-      stage_x(xr[u], buf);
-      TileMeta mc;
-      {
-        const int64_t t = tile_of(i);
-        const int32_t seq = sr[u], pos = pr[u];
-        const bool valid = i < n_mine && t * 16 + l16 < p.n_rows;
-        mc.page = p.bt_q[int64_t(seq) * p.max_pages + (pos >> 4)];  // seq/pos of a real row
-        mc.valid = valid;
-        mc.slot = pos & 15;
-        const int32_t seq0 = __shfl(seq, 0, 64), pos0 = __shfl(pos, 0, 64);
-        const bool ok = valid && seq == seq0 && pos == pos0 + l16 && (pos0 & 15) == 0;
-        mc.aligned = (__ballot(ok) & 0xFFFFull) == 0xFFFFull;
-      }
-      // refill the ring slot kDepth tiles ahead (clamped: always issued)
-      issue(u, i + kDepth);
-      lds_barrier();
-      // tile i-2: its LDS words are complete (buffer i&1)
-      if (i >= 2 && i - 2 < n_mine) store_tile(m2, buf);
-      f32x4 accn[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-      if (i < n_mine) {
-        u32x4 xc[NKB];
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-          xc[kb] = *reinterpret_cast<const u32x4*>(&s_x[buf][l16 * kRowBytes + 64 * kb + 16 * quad]);
-#pragma unroll
-        for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-          for (int hb = 0; hb < 2; ++hb)
-#pragma unroll
-            for (int j = 1; j >= 0; --j)  // lo, then hi
-              accn[hb] = mfma_f16(rop[hb][kb][j], xc[kb], accn[hb]);
-      }
-      const int ren = s_rexp[buf][l16];  // read now: the buffer is rewritten two steps on
-      // tile i-1: codes and scales into LDS buffer (i-1)&1
-      if (i >= 1 && i - 1 < n_mine) epilogue(accp, m1, rep, buf ^ 1);
-      accp[0] = accn[0];
-      accp[1] = accn[1];
-      rep = ren;
-      m2 = m1;
-      m1 = mc;
-    }
+    mprev = mc;
   }
-  }  // pipelined tiles
+  wait_vm<0>();  // no ring request lands after the workgroup ends
 }
 
 template <int D, bool ONE>
 __global__ __launch_bounds__(64 * (D / 32)) void quantize_append_kernel(QAParams p) {
+  __shared__ QAShared<D, ONE> sh;
   const int h = blockIdx.y;
   if (blockIdx.z == 0)
-    qa_tiles<D, 0, ONE>(p, h);
+    qa_tiles<D, 0, ONE>(p, h, sh);
   else
-    qa_tiles<D, 1, ONE>(p, h);
+    qa_tiles<D, 1, ONE>(p, h, sh);
 }
 
 }  // namespace
