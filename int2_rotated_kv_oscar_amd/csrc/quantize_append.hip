@@ -410,7 +410,7 @@ __device__ void qa_tiles(const QAParams& p, int h, QAShared<D, ONE>& sh) {
 }
 
 template <int D, bool ONE>
-__global__ __launch_bounds__(64 * (D / 32)) void quantize_append_kernel(QAParams p) {
+__global__ __launch_bounds__(64 * (D / 32), 4) void quantize_append_kernel(QAParams p) {
   __shared__ QAShared<D, ONE> sh;
   const int h = blockIdx.y;
   if (blockIdx.z == 0)
@@ -432,7 +432,7 @@ hipError_t quantize_append(int d, int n_kv, void* pool, const void* k_new, const
   // workgroups loop over tiles of 16 rows (the split rotation stays in
   // registers); about three workgroups per CU over all (head, tensor) pairs
   const int64_t tiles = (n_rows + 15) / 16;
-  const int64_t per_pair = std::max<int64_t>(1, (3 * int64_t(n_cus) + 2 * n_kv - 1) / (2 * n_kv));
+  const int64_t per_pair = std::max<int64_t>(1, (4 * int64_t(n_cus) + 2 * n_kv - 1) / (2 * n_kv));
   const dim3 grid(static_cast<unsigned>(std::min(tiles, per_pair)), static_cast<unsigned>(n_kv), 2u);
   // one tile per workgroup (few rows, as in a decode step): the unpipelined variant
   const bool one = tiles <= per_pair;
