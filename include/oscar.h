@@ -198,9 +198,12 @@ typedef struct {
  * Preconditions (device contents): 0 <= row_pos[j] < 16 max_pages, the named
  * page is valid and not shared with another sequence, and no two rows name
  * the same (sequence, position).
- * Arithmetic: y is accumulated in float32 from an exact three-way bfloat16
- * split of R, so a code can differ from exact arithmetic only when
- * (y - z) / s lies within about 1e-6 of a rounding boundary.
+ * Arithmetic: y is accumulated in float32, from float32 products for up to
+ * 64 rows per call and, for more rows, on the matrix cores from an f16
+ * hi + lo split of 256 R (22 significant bits) and an exact f16 copy of x,
+ * so a code can differ from exact arithmetic only when (y - z) / s lies
+ * within about 1e-5 of a rounding boundary.  Up to 64 rows, values of
+ * magnitude beyond 2^120 may overflow the float32 products.
  * n_rows == 0 returns OSCAR_OK and launches nothing.
  * ------------------------------------------------------------------------ */
 oscar_status oscar_quantize_append(const oscar_cache* cache, const void* k_new,

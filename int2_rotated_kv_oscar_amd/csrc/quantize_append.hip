@@ -419,6 +419,140 @@ __global__ __launch_bounds__(64 * (D / 32), 4) void quantize_append_kernel(QAPar
     qa_tiles<D, 1, ONE>(p, h, sh);
 }
 
+// ---------------------------------------------------------------------------
+// Few rows (a decode step's appends): the rotation is a handful of d x d
+// vector-matrix products, too small for the tile pipeline above, whose time
+// goes to fetching and splitting all of R per workgroup.  Here a workgroup
+// takes one (KV head, tensor), one pair of channel groups (64 rotated
+// channels, a slice of R of d x 64 float32) and up to kRowsPerWg rows, and
+// computes y in plain float32 fused multiply-adds.  A group pair owns whole
+// code words of a K row and whole code bytes of a V row in the page layout,
+// so every field is written with a plain store: no atomics, whatever other
+// rows share the words.
+constexpr int kRowsPerWg = 8;
+constexpr int kRowThreads = 256;
+constexpr int64_t kFewRows = 64;  // row counts up to this take the few-row kernel
+
+template <int D>
+__global__ __launch_bounds__(kRowThreads) void quantize_rows_kernel(QAParams p) {
+  using GG = Geo<D>;
+  constexpr int NG = GG::NG, NW = GG::NW;
+  constexpr int KS_PER = D / 16;  // reduction length of one k-slice (16 slices)
+  const int tid = threadIdx.x;
+  const int h = blockIdx.y;
+  const int tensor = blockIdx.z & 1, pair = blockIdx.z >> 1;
+  const uint16_t* X = tensor ? p.v_new : p.k_new;
+  const float* R = (tensor ? p.r_v : p.r_k) + size_t(h) * D * D;
+  const float tau = tensor ? p.tau_v : p.tau_k;
+  const int64_t row0 = int64_t(blockIdx.x) * kRowsPerWg;
+  const int nr = int(min<int64_t>(kRowsPerWg, p.n_rows - row0));  // >= 1 by the grid size
+
+  __shared__ float s_part[kRowsPerWg][16][64];  // [row][k-slice][channel of the pair]
+  __shared__ uint16_t s_x[kRowsPerWg][D];
+  __shared__ uint8_t s_code[kRowsPerWg][64];
+  __shared__ int32_t s_page[kRowsPerWg], s_slot[kRowsPerWg];
+
+  // row metadata first (the page ids need a second round trip)
+  if (tid < nr) {
+    const int32_t seq = p.row_seq[row0 + tid], pos = p.row_pos[row0 + tid];
+    s_page[tid] = p.bt_q[int64_t(seq) * p.max_pages + (pos >> 4)];
+    s_slot[tid] = pos & 15;
+  }
+  // the chunk's x rows to LDS (rows past the chunk re-read its last row;
+  // their results are never stored)
+  constexpr int kXPer = kRowsPerWg * D / kRowThreads;
+#pragma unroll
+  for (int i = 0; i < kXPer; ++i) {
+    const int e = tid * kXPer + i, r = e / D, c = e % D;
+    s_x[r][c] = X[((row0 + min(r, nr - 1)) * p.n_kv + h) * D + c];
+  }
+  // products: thread (k-slice ks, channel quad c4) over the rows
+  const int c4 = tid & 15, ks = tid >> 4;
+  f32x4 rr[KS_PER];
+#pragma unroll
+  for (int j = 0; j < KS_PER; ++j)
+    rr[j] = *reinterpret_cast<const f32x4*>(R + size_t(ks * KS_PER + j) * D + 64 * pair + 4 * c4);
+  __syncthreads();
+#pragma unroll
+  for (int r = 0; r < kRowsPerWg; ++r) {
+    f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KS_PER; ++j) {
+      const float x = bf16_to_f32(s_x[r][ks * KS_PER + j]);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) a[c] = __builtin_fmaf(x, rr[j][c], a[c]);
+    }
+    *reinterpret_cast<f32x4*>(&s_part[r][ks][4 * c4]) = a;
+  }
+  __syncthreads();
+
+  // statistics and codes: thread (row rw, channel cc) holds channel cc of the
+  // pair's first group and channel cc of its second, a row's 32 lanes being
+  // one half of a wave
+  const int rw = tid >> 5, cc = tid & 31;
+  float y[2] = {0.f, 0.f};
+#pragma unroll
+  for (int gp = 0; gp < 2; ++gp) {
+#pragma unroll
+    for (int k = 0; k < 16; ++k) y[gp] += s_part[rw][k][32 * gp + cc];
+    y[gp] = __builtin_amdgcn_fmed3f(y[gp], -tau, tau);
+  }
+#pragma unroll
+  for (int gp = 0; gp < 2; ++gp) {
+    float mn = y[gp], mx = y[gp];
+#pragma unroll
+    for (int m = 1; m < 32; m <<= 1) {
+      mn = fminf(mn, __shfl_xor(mn, m, 64));
+      mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+    }
+    const uint32_t s16 = f16_bits((mx - mn) / 3.0f);
+    const uint32_t z16 = f16_bits(mn);
+    const float sf = f16_to_f32(s16), zf = f16_to_f32(z16);
+    int code = 0;
+    if (sf != 0.0f) code = min(max(int(__builtin_rintf((y[gp] - zf) / sf)), 0), 3);
+    s_code[rw][32 * gp + cc] = uint8_t(code);
+    if (cc == 0 && rw < nr) {
+      const int g = 2 * pair + gp, slot = s_slot[rw];
+      uint8_t* base = p.pool + (int64_t(s_page[rw]) * p.n_kv + h) * int64_t(GG::HEAD_BYTES);
+      const int iu = tensor == 0 ? slot * NG + g : ((slot >> 2) * NG + g) * 4 + (slot & 3);
+      reinterpret_cast<uint16_t*>(base + (tensor == 0 ? GG::KS : GG::VS))[iu] = uint16_t(s16);
+      reinterpret_cast<uint16_t*>(base + (tensor == 0 ? GG::KZ : GG::VZ))[iu] = uint16_t(z16);
+    }
+  }
+  __syncthreads();
+
+  // code fields of the page layout.  K, row slot m: word (quad 16 + m) NW + pair
+  // holds channel 32 gp + 16 hb + 4 quad + r of the pair at bit
+  // 16 (r % 2) + 8 gp + 4 hb + 2 (r / 2).  V, row slot t = 4q + r: the byte
+  // 2 (r % 2) + r / 2 of word (q 16 + c16) NW + pair holds channel 16 bb + c16
+  // of the pair at bit 2 bb.
+  if (tensor == 0) {
+    if (tid < 4 * nr) {
+      const int row = tid >> 2, quad = tid & 3, slot = s_slot[row];
+      uint32_t w = 0;
+#pragma unroll
+      for (int gp = 0; gp < 2; ++gp)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            w |= uint32_t(s_code[row][32 * gp + 16 * hb + 4 * quad + r]) << (16 * (r & 1) + 8 * gp + 4 * hb + 2 * (r >> 1));
+      uint8_t* base = p.pool + (int64_t(s_page[row]) * p.n_kv + h) * int64_t(GG::HEAD_BYTES);
+      reinterpret_cast<uint32_t*>(base + GG::KC)[(quad * 16 + slot) * NW + pair] = w;
+    }
+  } else {
+    if (tid < 16 * nr) {
+      const int row = tid >> 4, c16 = tid & 15, slot = s_slot[row];
+      const int q = slot >> 2, r = slot & 3;
+      uint32_t bits = 0;
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) bits |= uint32_t(s_code[row][16 * bb + c16]) << (2 * bb);
+      uint8_t* base = p.pool + (int64_t(s_page[row]) * p.n_kv + h) * int64_t(GG::HEAD_BYTES);
+      base[GG::VC + ((q * 16 + c16) * NW + pair) * 4 + 2 * (r & 1) + (r >> 1)] = uint8_t(bits);
+    }
+  }
+}
+
 }  // namespace
 
 namespace oscar_launch {
@@ -431,6 +565,14 @@ hipError_t quantize_append(int d, int n_kv, void* pool, const void* k_new, const
              bt_q, max_pages, r_k, r_v, tau_k, tau_v, static_cast<uint8_t*>(pool), n_kv};
   // workgroups loop over tiles of 16 rows (the split rotation stays in
   // registers); about three workgroups per CU over all (head, tensor) pairs
+  if (n_rows <= kFewRows) {
+    // few rows: plain float32 products, a slice of R per workgroup
+    const dim3 grid(static_cast<unsigned>((n_rows + kRowsPerWg - 1) / kRowsPerWg), static_cast<unsigned>(n_kv),
+                    static_cast<unsigned>(d / 32));  // (tensor, group pair)
+    if (d == 128) hipLaunchKernelGGL((quantize_rows_kernel<128>), grid, dim3(kRowThreads), 0, stream, p);
+    else hipLaunchKernelGGL((quantize_rows_kernel<64>), grid, dim3(kRowThreads), 0, stream, p);
+    return hipGetLastError();
+  }
   const int64_t tiles = (n_rows + 15) / 16;
   const int64_t per_pair = std::max<int64_t>(1, (4 * int64_t(n_cus) + 2 * n_kv - 1) / (2 * n_kv));
   const dim3 grid(static_cast<unsigned>(std::min(tiles, per_pair)), static_cast<unsigned>(n_kv), 2u);

@@ -134,6 +134,54 @@ def test_quantize_append_scattered_single_rows(tiny_rot):
     gh.assert_codes_ok(rep, "scattered")
 
 
+@pytest.mark.parametrize("d,hkv,n_rows", [(64, 1, 1), (64, 3, 7), (128, 8, 28), (128, 2, 64), (128, 2, 65)])
+def test_quantize_append_few_rows(d, hkv, n_rows):
+    # a decode step's appends: a few rows in random order at scattered slots
+    # of pages holding stale bytes (up to 64 rows take the few-row kernel,
+    # 65 the matrix-core one); every other byte of the pool stays as it was
+    n_seq, chunk = 4, 64
+    w = synth.Workload("few-rows", 5, n_seq, 4 * hkv, hkv, d, 4, 128, 64, ("fixed", chunk, chunk), k_noise="t3")
+    k, v, row_seq, row_pos = synth.prefill_rows(w, n_seq, chunk)
+    rng = np.random.default_rng(1000 + n_rows)
+    sel = rng.choice(len(row_seq), size=n_rows, replace=False)
+    k, v, row_seq, row_pos = k[sel], v[sel], row_seq[sel], row_pos[sel]
+    pages_per = chunk // 16
+    n_pages = n_seq * pages_per
+    bt_q = synth.rng_for(98, 7).permutation(n_pages).astype(np.int32).reshape(n_seq, pages_per)
+    cal = synth.calibration_set(w, n_rows=256)
+    from oracle import rotation as orot
+    rt = orot.build_rotation(cal.q, cal.k, cal.v, w.group_q)
+    rot = gh.Rotation(rt["r_k"].astype(np.float32).astype(np.float64), rt["r_v"].astype(np.float32).astype(np.float64),
+                      float(np.float32(rt["tau_k"])), float(np.float32(rt["tau_v"])))
+    stale = rng.integers(0, 256, size=n_pages * lib.int2_page_bytes(d, hkv), dtype=np.uint8)
+    int2 = torch.from_numpy(stale.copy()).to(gh.DEV)
+    cache = lib.make_cache(d, hkv, 4, 128, int2, None)
+    print(f"[few rows d={d} hkv={hkv} rows={n_rows}]", flush=True)
+    lib.quantize_append(cache, gh.bits_to_dev_bf16(k), gh.bits_to_dev_bf16(v), gh.i32(row_seq), gh.i32(row_pos),
+                        gh.i32(bt_q), torch.from_numpy(rot.r_k.astype(np.float32)).to(gh.DEV),
+                        torch.from_numpy(rot.r_v.astype(np.float32)).to(gh.DEV), rot.tau_k, rot.tau_v)
+    torch.cuda.synchronize()
+    got = int2.cpu().numpy()
+    pool = olayout.Int2Pool(n_pages, hkv, d, stale.copy())
+    res = ocache.quantize_append(pool, k, v, row_seq, row_pos, bt_q, rot.r_k, rot.r_v, rot.tau_k, rot.tau_v,
+                                 olayout.bf16_to_f64)
+    page = bt_q[row_seq, row_pos // 16].astype(np.int64)
+    slot = (row_pos % 16).astype(np.int64)
+    rep = gh.compare_appended(got, w, n_pages, res, page, slot)
+    print(rep)
+    gh.assert_codes_ok(rep, "few rows")
+    # with the appended rows' fields cleared in both, the pools are identical
+    cleared = []
+    for data in (got.copy(), pool.data.copy()):
+        pc = olayout.Int2Pool(n_pages, hkv, d, data)
+        zc = np.zeros((n_rows, d), np.uint8)
+        zs = np.zeros((n_rows, d // 32), np.float16)
+        for h in range(hkv):
+            pc.write(page, slot, h, zc, zc, zs, zs, zs, zs)
+        cleared.append(pc.data)
+    assert np.array_equal(cleared[0], cleared[1]), "bytes outside the appended rows changed"
+
+
 def test_decode_on_oracle_pages_tiny(tiny_rot):
     w = _tiny()
     inp = synth.decode_inputs(w)
