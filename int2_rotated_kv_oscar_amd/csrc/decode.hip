@@ -175,14 +175,16 @@ struct PageOps {
       if (NG == 4) kz[1] = kzp[1];
     }
   }
-  __device__ __forceinline__ void read_v(const uint8_t* base, int l16, int quad) {
+  // GROUPED: only the V scales of group gsel (in vs[0], vs[1])
+  template <bool GROUPED = false>
+  __device__ __forceinline__ void read_v(const uint8_t* base, int l16, int quad, int gsel = 0) {
     using GG = Geo<D>;
     const uint32_t* vcp = reinterpret_cast<const uint32_t*>(base + GG::VC) + (quad * 16 + l16) * NW;
-    const uint32_t* vsp = reinterpret_cast<const uint32_t*>(base + GG::VS) + quad * 2 * NG;
+    const uint32_t* vsp = reinterpret_cast<const uint32_t*>(base + GG::VS) + quad * 2 * NG + (GROUPED ? 2 * gsel : 0);
 #pragma unroll
     for (int i = 0; i < NW; ++i) vc[i] = vcp[i];
 #pragma unroll
-    for (int i = 0; i < 2 * NG; ++i) vs[i] = vsp[i];
+    for (int i = 0; i < (GROUPED ? 2 : 2 * NG); ++i) vs[i] = vsp[i];
     vz[0] = vz[1] = 0;
     if (l16 < NG) {
       const uint32_t* vzp = reinterpret_cast<const uint32_t*>(base + GG::VZ) + (quad * NG + l16) * 2;
@@ -209,7 +211,11 @@ constexpr int kRing = 6;  // pair slots per wave: the two steps being computed a
 // SLICES: balanced slices over all units (several segments per workgroup),
 // else per-unit items (one segment per workgroup, early requests).  Separate
 // kernels keep each one's code to a single instance of the segment.
-template <int D, bool ALL_RAW, bool SLICES>
+// GC (grouped columns, G <= 4): MFMA column n carries query n/4, and in the
+// value products it also stands for channel group n%4, so that one B operand
+// (probability times that group's V scale) serves every channel block;
+// otherwise column n carries query n and each group has its own B operand.
+template <int D, bool ALL_RAW, bool SLICES, bool GC>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   using GG = Geo<D>;
   constexpr int NG = GG::NG, NCB = GG::NCB, NKB = GG::NKB, HB = GG::HEAD_BYTES;
@@ -235,7 +241,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   // which the vector-memory counter does not wait on
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wg = blockIdx.x;
-  const int qrow = min(l16, G - 1);  // MFMA columns n >= G repeat a real head; their results are dropped
+  const int qrow = min(l16, G - 1);  // per-query rows of the merge
+  // query of MFMA column l16 (columns past the group repeat a real head;
+  // their results are dropped)
+  const int qcol = GC ? min(l16 >> 2, G - 1) : min(l16, G - 1);
   const float qscale = p.sm_scale * kLog2e;
 
   // the (sequence, KV head) unit of the current segment
@@ -308,7 +317,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) rvals[kb][i] = rk[size_t(32 * kb + 8 * quad + i) * D + 16 * (wave & (NCB - 1)) + l16];
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) bqv[kb] = *reinterpret_cast<const u32x4*>(qb + size_t(qrow) * D + 32 * kb + 8 * quad);
+      for (int kb = 0; kb < NKB; ++kb) bqv[kb] = *reinterpret_cast<const u32x4*>(qb + size_t(qcol) * D + 32 * kb + 8 * quad);
     }
     // The rotation operands are waited for here, before the page requests:
     // the compiler does not count loads that land in LDS, so a wait for them
@@ -355,7 +364,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   const int lane = tid & 63, l16 = lane & 15, quad = lane >> 4;
-  const int qrow = min(l16, G - 1);
+  const int qcol = GC ? min(l16 >> 2, G - 1) : min(l16, G - 1);
   const int n_pairs = (c1 - c0 + 1) >> 1;
   const int m0 = sp.m0, m1 = sp.m1, s1 = sp.s1, r0 = sp.r0;
 
@@ -394,11 +403,43 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
       for (int r = 0; r < 4; ++r) pv[j][r] = __builtin_amdgcn_exp2f(lg[j][r] - m_use);
   };
 
+  // INT2 steps: the logits arrive already offset by -m_off (m_off = m_run,
+  // or 0 before the first step), folded into the zero-term MFMA's
+  // accumulator, so the exponent needs no subtraction unless the reference
+  // max moves
+  auto softmax_step_off = [&](auto& lg, auto& pv, float m_off) {
+    constexpr int NP = sizeof(lg) / sizeof(lg[0]);
+    float mx = kNegInf;
+#pragma unroll
+    for (int j = 0; j < NP; ++j)
+      mx = fmaxf(mx, fmaxf(fmaxf(lg[j][0], lg[j][1]), fmaxf(lg[j][2], lg[j][3])));
+    mx = wave_max16(mx);
+    if (__any(mx > kSlack || m_run == kNegInf)) {
+      const float m_new = fmaxf(m_run, mx + m_off);
+      const float f = (m_run == kNegInf) ? 0.f : exp2f(m_run - m_new);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) acc[cb] *= f;
+      acc_z *= f;
+      l_part *= f;
+      m_run = m_new;
+      const float dl = (m_new == kNegInf) ? 0.f : m_new - m_off;
+#pragma unroll
+      for (int j = 0; j < NP; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pv[j][r] = __builtin_amdgcn_exp2f(lg[j][r] - dl);
+    } else {
+#pragma unroll
+      for (int j = 0; j < NP; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) pv[j][r] = __builtin_amdgcn_exp2f(lg[j][r]);
+    }
+  };
+
   if (is_raw) {
     // ---------------- BF16 chunk: raw q . k, raw-basis value sums ----------------
     u32x4 bqr[NKB];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) bqr[kb] = *reinterpret_cast<const u32x4*>(qb + size_t(qrow) * D + 32 * kb + 8 * quad);
+    for (int kb = 0; kb < NKB; ++kb) bqr[kb] = *reinterpret_cast<const u32x4*>(qb + size_t(qcol) * D + 32 * kb + 8 * quad);
     const int n_a = sp.ra1 - sp.ra0;
     for (int pr = wave; pr < n_pairs; pr += kWaves) {
       float lg[2][4];
@@ -512,6 +553,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
       bz = u32x4{pack2(hv[0], hv[1]), pack2(hv[2], hv[3]), pack2(hv[4], hv[5]), pack2(hv[6], hv[7])};
     }
     const uint32_t ones = l16 == NG ? 0x3C003C00u : 0u;  // f16 1.0 pairs in A row NG
+    constexpr int NGV = GC ? 1 : NG;                       // V-scale B operands per pair
+    const int gsel = min(l16 & 3, NG - 1);                 // GC: the group of column l16
     // one page pair: logits, softmax, value sums
     // Two page pairs per step (pair k from slot A, pair k+1 from slot B): K
     // operands and logits of the four pages, one softmax step over their 64
@@ -521,6 +564,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     auto page_live = [&](int pg) { return pg < c1; };
     auto do_two = [&](int k, const uint8_t* sa, const uint8_t* sb, bool has_b, auto interior_tag) {
       constexpr bool INTERIOR = decltype(interior_tag)::value;
+      const float m_off = (m_run == kNegInf) ? 0.f : m_run;
+      const f32x4 zinit = {-m_off, -m_off, -m_off, -m_off};
       float lg[4][4];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
@@ -531,7 +576,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
         if (!INTERIOR && !page_live(pg)) continue;
         PageOps<D> P;
         P.read_k((jj < 2 ? sa : sb) + (jj & 1) * HB, l16, quad);
-        const f32x4 dz = mfma_f16(u32x4{P.kz[0], P.kz[1], 0u, 0u}, bz, f32x4{0.f, 0.f, 0.f, 0.f});
+        const f32x4 dz = mfma_f16(u32x4{P.kz[0], P.kz[1], 0u, 0u}, bz, zinit);
         float lk[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int g = 0; g < NG; ++g) {
@@ -551,7 +596,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
         }
       }
       float pv[4][4];
-      softmax_step(lg, pv);
+      softmax_step_off(lg, pv, m_off);
 #pragma unroll
       for (int pr = 0; pr < 2; ++pr) {
         if (pr == 1 && !has_b) break;
@@ -559,7 +604,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
         PageOps<D> P[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          P[j].read_v(slot + j * HB, l16, quad);
+          P[j].template read_v<GC>(slot + j * HB, l16, quad, gsel);
           const int pg = page_of(k + pr, j);
           if (!INTERIOR && (!page_live(pg) || 16 * pg < m0 || 16 * pg + 16 > m1)) {
             // boundary (or absent) page: clear scale/zero of slots outside the middle
@@ -571,7 +616,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
             }
             const uint32_t k01 = pair_keep(keep[0], keep[1]), k23 = pair_keep(keep[2], keep[3]);
 #pragma unroll
-            for (int g = 0; g < NG; ++g) { P[j].vs[2 * g] &= k01; P[j].vs[2 * g + 1] &= k23; }
+            for (int g = 0; g < NGV; ++g) { P[j].vs[2 * g] &= k01; P[j].vs[2 * g + 1] &= k23; }
             P[j].vz[0] &= k01;
             P[j].vz[1] &= k23;
           }
@@ -584,17 +629,19 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
         // both from the same f16 probabilities the value sums use
         acc_z = mfma_f16(u32x4{P[0].vz[0] | ones, P[0].vz[1] | ones, P[1].vz[0] | ones, P[1].vz[1] | ones},
                          u32x4{bp[0], bp[1], bp[2], bp[3]}, acc_z);
+        // B operands: probabilities times V scales, one per group (GC: the
+        // column's own group, one operand for every block)
+        u32x4 bs[NGV];
 #pragma unroll
-        for (int g = 0; g < NG; ++g) {
-          const u32x4 bs = {hmul2(bp[0], P[0].vs[2 * g]), hmul2(bp[1], P[0].vs[2 * g + 1]),
-                            hmul2(bp[2], P[1].vs[2 * g]), hmul2(bp[3], P[1].vs[2 * g + 1])};
+        for (int g = 0; g < NGV; ++g)
+          bs[g] = u32x4{hmul2(bp[0], P[0].vs[2 * g]), hmul2(bp[1], P[0].vs[2 * g + 1]),
+                        hmul2(bp[2], P[1].vs[2 * g]), hmul2(bp[3], P[1].vs[2 * g + 1])};
 #pragma unroll
-          for (int hb = 0; hb < 2; ++hb) {
-            const int cb = 2 * g + hb, w = cb >> 2, bb = cb & 3;
-            const uint32_t m = 0x00030003u << (2 * bb);
-            const u32x4 a = {P[0].vc[w] & m, shr8_halves(P[0].vc[w]) & m, P[1].vc[w] & m, shr8_halves(P[1].vc[w]) & m};
-            acc[cb] = mfma_f16(a, bs, acc[cb]);
-          }
+        for (int cb = 0; cb < NCB; ++cb) {
+          const int w = cb >> 2, bb = cb & 3;
+          const uint32_t m = 0x00030003u << (2 * bb);
+          const u32x4 a = {P[0].vc[w] & m, shr8_halves(P[0].vc[w]) & m, P[1].vc[w] & m, shr8_halves(P[1].vc[w]) & m};
+          acc[cb] = mfma_f16(a, bs[GC ? 0 : cb >> 1], acc[cb]);
         }
       }
     };
@@ -663,9 +710,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w * 16 + l16]);
   const float sc = (m_run == kNegInf) ? 0.f : exp2f(m_run - M);
-  if (l16 < G) {
+  {
+    // the column holding query qi's value sums of block cb (GC: column
+    // 4 qi + group of cb for INT2 chunks, 4 qi for BF16 chunks)
+    const int qi = GC ? (l16 >> 2) : l16;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
+      const bool mine = qi < G && (!GC || (l16 & 3) == (is_raw ? 0 : (cb >> 1)));
+      if (!mine) continue;
       f32x4 v;
       if (is_raw) {
         v = acc[cb] * sc;
@@ -674,7 +726,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) v[r] = sc * (acc[cb][r] * fpos + zg[cb >> 1]);
       }
-      *reinterpret_cast<f32x4*>(s_res + (wave * G + l16) * D + 16 * cb + 4 * quad) = v;
+      *reinterpret_cast<f32x4*>(s_res + (wave * G + qi) * D + 16 * cb + 4 * quad) = v;
     }
   }
   lds_barrier();
@@ -682,12 +734,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   // ---- workgroup record [m G][l G][value sums G D][basis flag] -> workspace ----
   float* rec = p.partials + ((size_t(b) * p.n_kv + h) * p.cap + kseg) * size_t(p.rec_floats);
   if (tid < G) {
+    const int cq = GC ? 4 * tid : tid;  // a column of query tid
     float mm = kNegInf;
-    for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, s_m[w * 16 + tid]);
+    for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, s_m[w * 16 + cq]);
     float ll = 0.f;
     for (int w = 0; w < kWaves; ++w) {
-      const float mw = s_m[w * 16 + tid];
-      if (mw != kNegInf) ll += exp2f(mw - mm) * s_l[w * 16 + tid];
+      const float mw = s_m[w * 16 + cq];
+      if (mw != kNegInf) ll += exp2f(mw - mm) * s_l[w * 16 + cq];
     }
     st_dev(rec + tid, mm);
     st_dev(rec + G + tid, ll);
@@ -1014,17 +1067,21 @@ hipError_t paged_decode(int d, bool all_raw, const void* int2_pool, int n_int2_p
               per_unit ? 1 : 0, unit_items};
   const dim3 grid(static_cast<unsigned>(n_wg));
   const size_t lds = decode_lds_bytes(d, G, all_raw);
-#define OSCAR_DECODE_LAUNCH(DD, RAW)                                                                     \
-  do {                                                                                                  \
-    if (per_unit) hipLaunchKernelGGL((decode_kernel<DD, RAW, false>), grid, dim3(kThreads), lds, stream, p); \
-    else hipLaunchKernelGGL((decode_kernel<DD, RAW, true>), grid, dim3(kThreads), lds, stream, p);           \
+  // grouped columns when the query group fits four columns per query
+  const bool gc = !all_raw && G <= 4;
+#define OSCAR_DECODE_LAUNCH(DD, RAW, GCOL)                                                                     \
+  do {                                                                                                        \
+    if (per_unit) hipLaunchKernelGGL((decode_kernel<DD, RAW, false, GCOL>), grid, dim3(kThreads), lds, stream, p); \
+    else hipLaunchKernelGGL((decode_kernel<DD, RAW, true, GCOL>), grid, dim3(kThreads), lds, stream, p);           \
   } while (0)
   if (d == 128) {
-    if (all_raw) OSCAR_DECODE_LAUNCH(128, true);
-    else OSCAR_DECODE_LAUNCH(128, false);
+    if (all_raw) OSCAR_DECODE_LAUNCH(128, true, false);
+    else if (gc) OSCAR_DECODE_LAUNCH(128, false, true);
+    else OSCAR_DECODE_LAUNCH(128, false, false);
   } else {
-    if (all_raw) OSCAR_DECODE_LAUNCH(64, true);
-    else OSCAR_DECODE_LAUNCH(64, false);
+    if (all_raw) OSCAR_DECODE_LAUNCH(64, true, false);
+    else if (gc) OSCAR_DECODE_LAUNCH(64, false, true);
+    else OSCAR_DECODE_LAUNCH(64, false, false);
   }
 #undef OSCAR_DECODE_LAUNCH
   return hipGetLastError();
