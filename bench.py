@@ -65,6 +65,19 @@ def algorithmic_bytes(inp, w) -> dict:
     return parts
 
 
+def decode_kernel_name(w, split_pages: int, all_raw: bool) -> str:
+    """The decode kernel instance the library launches for this workload
+    (template arguments: head dim, all-BF16 cache, balanced slices, grouped
+    columns), by the library's rule: per-unit items when split_pages is given
+    or the (sequence, KV head) units are at most a quarter of the CUs."""
+    import torch
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    slices = not (split_pages != 0 or 4 * w.batch * w.n_kv_heads <= cus)
+    gc = (not all_raw) and w.n_q_heads // w.n_kv_heads <= 4
+    b = lambda x: "true" if x else "false"  # noqa: E731
+    return f"decode_kernel<{w.d},{b(all_raw)},{b(slices)},{b(gc)}>"
+
+
 DECODE_SOURCES = ["decode.hip", "device_utils.h", "layout.h"]
 APPEND_SOURCES = ["quantize_append.hip", "device_utils.h", "layout.h"]
 
@@ -237,7 +250,7 @@ def main() -> int:
                    "recent": w.n_recent, "split_pages": args.split_pages or "auto", "cache_copies": copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(w.name),
-                     "kernel": "decode_kernel<128,false,false>", "algorithmic_bytes_per_launch": nbytes["total"],
+                     "kernel": decode_kernel_name(w, args.split_pages, False), "algorithmic_bytes_per_launch": nbytes["total"],
                      "avg_launch_us": round(dec_avg * 1e3, 2)},
     }
 
@@ -265,7 +278,7 @@ def main() -> int:
         torch.cuda.synchronize()
         bms = e0.elapsed_time(e1) / K
         bbytes = tokens * 4 * w.d * w.n_kv_heads + 2 * B * w.n_q_heads * w.d * 2
-        result["bf16_baseline"] = {"kernel": "decode_kernel<128,true,false>", "us_per_call": round(bms * 1e3, 2),
+        result["bf16_baseline"] = {"kernel": decode_kernel_name(w, args.split_pages, True), "us_per_call": round(bms * 1e3, 2),
                                    "KV_tokens_per_s": round(tokens / (bms * 1e-3), 1),
                                    "achieved_GBps": round(bbytes / (bms * 1e-3) / 1e9, 1),
                                    "int2_decode_speedup": round(bms / dec_avg, 3)}
