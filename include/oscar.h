@@ -117,6 +117,34 @@ oscar_status oscar_build_rotation(int32_t d, int32_t n_kv_heads, int32_t group_q
                                   double* tau_v, double* eig_k, double* eig_v);
 
 /* ------------------------------------------------------------------------ *
+ * Comparison rotations through the same cache path ([TS] 1: Hadamard
+ * transforms are the data-oblivious rotations OSCAR improves on; [TS] 4,
+ * "Accuracy Preservation": naive INT2 and Hadamard-only are the baselines).
+ *   OSCAR_ROTATION_HADAMARD: R_K = R_V = H . P_br for every KV head, the
+ *       fixed factor of the composite rotation above (U = I);
+ *   OSCAR_ROTATION_IDENTITY: R_K = R_V = I (no rotation).
+ * tau_K, tau_V: the clip_quantile quantiles of |K_h . R| and |V_h . R| as in
+ * oscar_build_rotation.  The results feed oscar_quantize_append and
+ * oscar_paged_decode_attn unchanged.
+ * Inputs (host, row-major float32): k_calib, v_calib [n_rows][H_kv][d].
+ * Outputs (host, float64): r_k, r_v [H_kv][d][d]; *tau_k, *tau_v.
+ * n_threads: host worker threads (0 = all).
+ * Errors: INVALID_ARG for an unknown variant, null pointers, n_rows < 2,
+ * H_kv < 1 or clip_quantile outside (0, 1]; UNSUPPORTED for d not in
+ * {64, 128}; NUMERIC for a non-finite input value.
+ * ------------------------------------------------------------------------ */
+typedef enum {
+  OSCAR_ROTATION_HADAMARD = 1,
+  OSCAR_ROTATION_IDENTITY = 2
+} oscar_rotation_variant;
+
+oscar_status oscar_build_fixed_rotation(int32_t variant, int32_t d, int32_t n_kv_heads,
+                                        int64_t n_rows, const float* k_calib,
+                                        const float* v_calib, double clip_quantile,
+                                        int32_t n_threads, double* r_k, double* r_v,
+                                        double* tau_k, double* tau_v);
+
+/* ------------------------------------------------------------------------ *
  * Paged cache geometry ([TS] 2.2.B: sink and recent tokens in BF16, the
  * middle history in INT2 after rotation and clipping, paged and compatible
  * with prefix caching; [AB]: paged KV-cache serving).

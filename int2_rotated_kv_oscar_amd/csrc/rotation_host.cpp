@@ -205,6 +205,33 @@ double linear_quantile(std::vector<double>& a, double qq) {
   return alo + (rr - double(lo)) * (ahi - alo);
 }
 
+// Per-layer clip thresholds ([TS] 2.2.A step 4): the quantile of |x R|
+// pooled over rows, heads and channels, for K (which 0) and V (which 1).
+void clip_thresholds(int d, int n_kv_heads, size_t N, const std::vector<double>& k, const std::vector<double>& v,
+                     const double* r_k, const double* r_v, double clip_quantile, int n_threads, double* tau_k,
+                     double* tau_v) {
+  for (int which = 0; which < 2; ++which) {
+    const std::vector<double>& x = which ? v : k;
+    const double* r = which ? r_v : r_k;
+    std::vector<double> y(N * n_kv_heads * d);
+    run_parallel(n_threads, n_kv_heads, [&](int h, int) {
+      const double* rh = r + size_t(h) * d * d;
+      for (size_t n = 0; n < N; ++n) {
+        const double* xr = &x[(n * n_kv_heads + h) * d];
+        double* out = &y[(size_t(h) * N + n) * d];
+        for (int c = 0; c < d; ++c) out[c] = 0.0;
+        for (int kk = 0; kk < d; ++kk) {
+          const double xv = xr[kk];
+          const double* rrow = rh + size_t(kk) * d;
+          for (int c = 0; c < d; ++c) out[c] += xv * rrow[c];
+        }
+        for (int c = 0; c < d; ++c) out[c] = std::fabs(out[c]);
+      }
+    });
+    (which ? *tau_v : *tau_k) = linear_quantile(y, clip_quantile);
+  }
+}
+
 }  // namespace
 
 extern "C" oscar_status oscar_build_rotation(int32_t d, int32_t n_kv_heads, int32_t group_q,
@@ -286,26 +313,42 @@ extern "C" oscar_status oscar_build_rotation(int32_t d, int32_t n_kv_heads, int3
   for (int h = 0; h < n_kv_heads; ++h)
     if (!ok[h]) return fail(OSCAR_ERR_NUMERIC, "Jacobi eigensolver did not converge");
 
-  // Per-layer clip thresholds: quantile of |x R| pooled over rows, heads, channels.
-  for (int which = 0; which < 2; ++which) {
-    const std::vector<double>& x = which ? v : k;
-    const double* r = which ? r_v : r_k;
-    std::vector<double> y(N * n_kv_heads * d);
-    run_parallel(n_threads, n_kv_heads, [&](int h, int) {
-      const double* rh = r + size_t(h) * d * d;
-      for (size_t n = 0; n < N; ++n) {
-        const double* xr = &x[(n * n_kv_heads + h) * d];
-        double* out = &y[(size_t(h) * N + n) * d];
-        for (int c = 0; c < d; ++c) out[c] = 0.0;
-        for (int kk = 0; kk < d; ++kk) {
-          const double xv = xr[kk];
-          const double* rrow = rh + size_t(kk) * d;
-          for (int c = 0; c < d; ++c) out[c] += xv * rrow[c];
-        }
-        for (int c = 0; c < d; ++c) out[c] = std::fabs(out[c]);
-      }
-    });
-    (which ? *tau_v : *tau_k) = linear_quantile(y, clip_quantile);
+  clip_thresholds(d, n_kv_heads, N, k, v, r_k, r_v, clip_quantile, n_threads, tau_k, tau_v);
+  return OSCAR_OK;
+}
+
+extern "C" oscar_status oscar_build_fixed_rotation(int32_t variant, int32_t d, int32_t n_kv_heads, int64_t n_rows,
+                                                   const float* k_calib, const float* v_calib,
+                                                   double clip_quantile, int32_t n_threads, double* r_k,
+                                                   double* r_v, double* tau_k, double* tau_v) {
+  using oscar::fail;
+  oscar::clear_error();
+  if (!k_calib || !v_calib || !r_k || !r_v || !tau_k || !tau_v)
+    return fail(OSCAR_ERR_INVALID_ARG, "null required pointer");
+  if (variant != OSCAR_ROTATION_HADAMARD && variant != OSCAR_ROTATION_IDENTITY)
+    return fail(OSCAR_ERR_INVALID_ARG, "unknown rotation variant");
+  if (n_rows < 2 || n_kv_heads < 1) return fail(OSCAR_ERR_INVALID_ARG, "n_rows < 2 or n_kv_heads < 1");
+  if (!(clip_quantile > 0.0 && clip_quantile <= 1.0))
+    return fail(OSCAR_ERR_INVALID_ARG, "clip_quantile outside (0, 1]");
+  if (d != 64 && d != 128) return fail(OSCAR_ERR_UNSUPPORTED, "d must be 64 or 128");
+  if (n_threads <= 0) n_threads = int(std::max(1u, std::thread::hardware_concurrency()));
+  const size_t N = size_t(n_rows);
+  const size_t nkv = N * n_kv_heads * d;
+  for (size_t i = 0; i < nkv; ++i)
+    if (!std::isfinite(k_calib[i]) || !std::isfinite(v_calib[i]))
+      return fail(OSCAR_ERR_NUMERIC, "non-finite calibration value");
+  // Hadamard-only: the fixed factor H . P_br of the composite rotation (U = I);
+  // identity: no rotation
+  std::vector<double> eye(size_t(d) * d, 0.0);
+  for (int i = 0; i < d; ++i) eye[size_t(i) * d + i] = 1.0;
+  std::vector<double> r(size_t(d) * d);
+  if (variant == OSCAR_ROTATION_HADAMARD) compose_rotation(d, eye, r.data());
+  else r = eye;
+  for (int h = 0; h < n_kv_heads; ++h) {
+    std::memcpy(r_k + size_t(h) * d * d, r.data(), sizeof(double) * d * d);
+    std::memcpy(r_v + size_t(h) * d * d, r.data(), sizeof(double) * d * d);
   }
+  std::vector<double> k(k_calib, k_calib + nkv), v(v_calib, v_calib + nkv);
+  clip_thresholds(d, n_kv_heads, N, k, v, r_k, r_v, clip_quantile, n_threads, tau_k, tau_v);
   return OSCAR_OK;
 }

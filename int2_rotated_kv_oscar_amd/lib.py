@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "OSCAR_OK", 1: "OSCAR_ERR_INVALID_ARG", 2: "OSCAR_ERR_UNSUPPO
 # Every symbol include/oscar.h declares.
 EXPORTS = [
     "oscar_status_string", "oscar_last_error", "oscar_version", "oscar_build_rotation",
-    "oscar_int2_page_bytes", "oscar_bf16_page_bytes", "oscar_quantize_append", "oscar_write_bf16",
+    "oscar_build_fixed_rotation", "oscar_int2_page_bytes", "oscar_bf16_page_bytes", "oscar_quantize_append", "oscar_write_bf16",
     "oscar_decode_workspace_bytes", "oscar_decode_workspace_init", "oscar_paged_decode_attn",
     "oscar_paged_decode_attn_bf16",
 ]
@@ -67,6 +67,7 @@ def load(path: str = LIB_PATH):
         "oscar_version": (_I32, []),
         "oscar_build_rotation": (_STATUS, [_I32, _I32, _I32, _I64, _P, _P, _P, _P, _F64, _I32, _I32,
                                            _P, _P, _P, _P, _P, _P]),
+        "oscar_build_fixed_rotation": (_STATUS, [_I32, _I32, _I32, _I64, _P, _P, _F64, _I32, _P, _P, _P, _P]),
         "oscar_int2_page_bytes": (_SZ, [_I32, _I32]),
         "oscar_bf16_page_bytes": (_SZ, [_I32, _I32]),
         "oscar_quantize_append": (_STATUS, [ctypes.POINTER(OscarCache), _P, _P, _I64, _P, _P, _P, _I32, _P, _P,
@@ -125,6 +126,22 @@ def build_rotation(q_calib, k_calib, v_calib, group_q: int, clip_quantile: float
                                        max_sweeps, n_threads, ptr(rk), ptr(rv), ctypes.byref(tk),
                                        ctypes.byref(tv), ptr(ek), ptr(ev)))
     return dict(r_k=rk, r_v=rv, tau_k=tk.value, tau_v=tv.value, eig_k=ek, eig_v=ev)
+
+
+ROTATION_HADAMARD = 1
+ROTATION_IDENTITY = 2
+
+
+def build_fixed_rotation(variant: int, k_calib, v_calib, clip_quantile: float = 0.999, n_threads: int = 0) -> dict:
+    """Comparison rotations (oscar_build_fixed_rotation).  Arrays are [N, H_kv, d]."""
+    k = _host_f32(k_calib); v = _host_f32(v_calib)
+    n, hkv, d = k.shape
+    rk = np.zeros((hkv, d, d)); rv = np.zeros((hkv, d, d))
+    tk = ctypes.c_double(); tv = ctypes.c_double()
+    ptr = lambda a: a.ctypes.data_as(_P)  # noqa: E731
+    _check(load().oscar_build_fixed_rotation(int(variant), d, hkv, n, ptr(k), ptr(v), clip_quantile, n_threads,
+                                             ptr(rk), ptr(rv), ctypes.byref(tk), ctypes.byref(tv)))
+    return dict(r_k=rk, r_v=rv, tau_k=tk.value, tau_v=tv.value)
 
 
 # ---------------------------------------------------------- device calls ---

@@ -146,3 +146,27 @@ def build_rotation(qc: np.ndarray, kc: np.ndarray, vc: np.ndarray, group_q: int,
     return dict(r_k=rk, r_v=rv, eig_k=ek, eig_v=ev, c_q=cq, c_s=cs,
                 tau_k=clip_threshold(kc, rk, clip_quantile),
                 tau_v=clip_threshold(vc, rv, clip_quantile))
+
+
+HADAMARD_ONLY = 1
+IDENTITY = 2
+
+
+def fixed_rotation(variant: int, kc: np.ndarray, vc: np.ndarray, clip_quantile: float = 0.999) -> dict:
+    """The pages' comparison rotations ([TS] 1: Hadamard transforms, the
+    data-oblivious rotations; [TS] 4 "Accuracy Preservation": naive INT2 and
+    Hadamard-only baselines), for every KV head and both K and V:
+    Hadamard-only R = (H_d / sqrt(d)) . P_br, the composite rotation with the
+    eigenbasis left out; naive R = I.  Clip thresholds as in step 4.
+    """
+    kc, vc = (np.asarray(a, dtype=np.float64) for a in (kc, vc))
+    hkv, d = kc.shape[1], kc.shape[2]
+    if variant == HADAMARD_ONLY:
+        r = (hadamard(d) / np.sqrt(d)) @ bitrev_perm(d)
+    elif variant == IDENTITY:
+        r = np.eye(d)
+    else:
+        raise ValueError(f"unknown rotation variant {variant}")
+    rr = np.broadcast_to(r, (hkv, d, d)).copy()
+    return dict(r_k=rr, r_v=rr.copy(), tau_k=clip_threshold(kc, rr, clip_quantile),
+                tau_v=clip_threshold(vc, rr, clip_quantile))

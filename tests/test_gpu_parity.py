@@ -242,6 +242,30 @@ def test_decode_group_shapes(hq, hkv, d, q_scale):
     gh.assert_attention_close(got, ref, "shape")
 
 
+@pytest.mark.parametrize("variant", [lib.ROTATION_HADAMARD, lib.ROTATION_IDENTITY])
+@pytest.mark.parametrize("hq,hkv,d", [(4, 1, 64), (8, 2, 128)])
+def test_comparison_rotations_end_to_end(variant, hq, hkv, d):
+    # the pages' baselines (Hadamard-only, naive INT2) through the same
+    # kernels: rotation from the host library (equal to the oracle's, pinned
+    # on the CPU), cache written and decoded on the GPU, against the oracle
+    w = synth.Workload("ablation", 6, 2, hq, hkv, d, 4, 32, 512, ("fixed", 600, 600))
+    cal = synth.calibration_set(w, n_rows=512)
+    rt = lib.build_fixed_rotation(variant, cal.k, cal.v)
+    f = lambda a: np.asarray(a, np.float32).astype(np.float64)  # noqa: E731
+    rot = gh.Rotation(f(rt["r_k"]), f(rt["r_v"]), float(np.float32(rt["tau_k"])), float(np.float32(rt["tau_v"])))
+    inp = synth.decode_inputs(w, seq_lens=np.array([600, 291]))
+    gc = gh.alloc_cache(inp, rot)
+    gh.gpu_fill(inp, rot, gc)
+    print(f"[comparison rotation {variant} hq={hq} hkv={hkv} d={d}]", flush=True)
+    got = gh.gpu_decode(inp, gc)
+    int2, bf, res, rows = gh.oracle_pools(inp, rot)
+    page, slot = _page_slot(inp, rows)
+    gh.assert_codes_ok(gh.compare_appended(gc.int2.cpu().numpy(), w, inp.n_int2_pages, res, page, slot))
+    ref = gh.oracle_decode(inp, rot, int2, bf)
+    print(gh.attention_errors(got, ref))
+    gh.assert_attention_close(got, ref, "comparison rotation")
+
+
 def test_invariances_tables_splits_determinism(tiny_rot):
     w = _tiny(batch=2)
     lens = np.array([512, 400])

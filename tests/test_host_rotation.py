@@ -51,3 +51,29 @@ def test_jacobi_non_convergence_is_reported():
     with pytest.raises(lib.OscarError) as e:
         lib.build_rotation(cal.q, cal.k, cal.v, w.group_q, max_sweeps=1)
     assert e.value.status == 3
+
+
+@pytest.mark.parametrize("variant", [lib.ROTATION_HADAMARD, lib.ROTATION_IDENTITY])
+def test_fixed_rotation_matches_oracle(variant):
+    w = synth.WORKLOADS["qwen3-8b-b1-32k"]
+    cal = synth.calibration_set(w, n_rows=256)
+    got = lib.build_fixed_rotation(variant, cal.k, cal.v, n_threads=3)
+    ref = orot.fixed_rotation(variant, cal.k, cal.v)
+    assert np.array_equal(got["r_k"], ref["r_k"]) and np.array_equal(got["r_v"], ref["r_v"])
+    assert got["tau_k"] == pytest.approx(ref["tau_k"], rel=1e-13)
+    assert got["tau_v"] == pytest.approx(ref["tau_v"], rel=1e-13)
+
+
+def test_fixed_rotation_validation():
+    k = np.zeros((4, 1, 64), np.float32)
+    with pytest.raises(lib.OscarError) as e:
+        lib.build_fixed_rotation(5, k, k)
+    assert e.value.status == 1
+    with pytest.raises(lib.OscarError) as e:
+        lib.build_fixed_rotation(lib.ROTATION_IDENTITY, np.zeros((4, 1, 96), np.float32),
+                                 np.zeros((4, 1, 96), np.float32))
+    assert e.value.status == 2
+    bad = k.copy(); bad[1, 0, 3] = np.inf
+    with pytest.raises(lib.OscarError) as e:
+        lib.build_fixed_rotation(lib.ROTATION_HADAMARD, bad, k)
+    assert e.value.status == 3

@@ -194,3 +194,40 @@ def test_clip_threshold_pools_heads_and_channels():
     lo = int(rr)
     expect = pooled[lo] + (rr - lo) * (pooled[lo + 1] - pooled[lo])
     assert rot.clip_threshold(x, r, 0.9) == pytest.approx(expect, rel=1e-12)
+
+
+def test_fixed_rotation_hadamard_only_pins():
+    # [TS] 1 / 4: the Hadamard-only baseline is the composite rotation without
+    # the eigenbasis.  d = 4 from the textbook H_4 with the columns taken in
+    # 2-bit reversed order (0, 2, 1, 3), halved.
+    h4 = np.array(_golden_rows("hadamard_bitrev.txt", "H4"), dtype=np.float64)
+    kc = np.random.default_rng(3).standard_normal((9, 2, 4))
+    r = rot.fixed_rotation(rot.HADAMARD_ONLY, kc, kc)
+    assert np.array_equal(r["r_k"][0], h4[:, [0, 2, 1, 3]] / 2.0)
+    assert np.array_equal(r["r_k"][1], r["r_k"][0]) and np.array_equal(r["r_v"], r["r_k"])
+    for d in (64, 128):
+        x = np.zeros((d, 1, d))
+        a = 3.0
+        for j in range(d):
+            x[j, 0, j] = a  # one spike per row: the rotation spreads it evenly
+        r = rot.fixed_rotation(rot.HADAMARD_ONLY, x, x)
+        rk = r["r_k"][0]
+        assert np.array_equal(np.abs(rk), np.full((d, d), 1.0 / np.sqrt(d)))
+        assert np.abs(rk.T @ rk - np.eye(d)).max() <= 1e-14
+        np.testing.assert_allclose(r["tau_k"], a / np.sqrt(d), rtol=1e-14)
+
+
+def test_fixed_rotation_identity_pins():
+    # naive INT2: no rotation; tau is the plain order statistic of |x|
+    rng = np.random.default_rng(4)
+    kc = rng.standard_normal((50, 3, 64))
+    vc = rng.standard_normal((50, 3, 64)) * 2.0
+    r = rot.fixed_rotation(rot.IDENTITY, kc, vc, clip_quantile=0.9)
+    assert np.array_equal(r["r_k"], np.broadcast_to(np.eye(64), (3, 64, 64)))
+    for key, x in (("tau_k", kc), ("tau_v", vc)):
+        a = sorted(abs(float(t)) for t in x.ravel())
+        rr = 0.9 * (len(a) - 1)
+        lo = int(rr)
+        assert r[key] == pytest.approx(a[lo] + (rr - lo) * (a[lo + 1] - a[lo]), rel=1e-15)
+    with pytest.raises(ValueError):
+        rot.fixed_rotation(7, kc, vc)
