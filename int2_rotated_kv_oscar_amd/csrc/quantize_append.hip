@@ -49,16 +49,24 @@ struct TileMeta {
   bool aligned;  // 16 consecutive positions of one sequence starting on a page boundary
 };
 
-// Codes through the float adder: fma(v - z, 1/s, 1.5 * 2^23) rounds the
-// scaled value to the nearest integer (ties to even) in the low mantissa bits,
-// so the clamp to [0, 3] is an integer med3 on the bit pattern (monotone for
-// every finite value, negative ones included) and the packing adds the pattern
-// shifted into place; the shifted copies of the constant part are removed by
-// starting each word from minus their sum (all modulo 2^32).
+// Codes through the float adder: t + 1.5 * 2^23 rounds t = (v - z) / s to
+// the nearest integer (ties to even) in the low mantissa bits, so the clamp
+// to [0, 3] is an integer med3 on the bit pattern (monotone for every finite
+// value, negative ones included) and the packing adds the pattern shifted into
+// place; the shifted copies of the constant part are removed by starting each
+// word from minus their sum (all modulo 2^32).  The quotient is t0 = (v - z)
+// inv refined once with its exact residual, t = t0 + (v - z - t0 s) inv,
+// which is the exact quotient whenever that is a representable number: an
+// exact midpoint k + 1/2 (frequent when the rotated values are themselves
+// coarse, as without rotation) then rounds to even instead of to the side
+// the reciprocal's error happens to fall on.  s = 0 gives inv = 0 and code 0.
 constexpr float kMagic = 12582912.0f;
 constexpr uint32_t kMagicBits = 0x4B400000u;
-__device__ __forceinline__ uint32_t code_bits(float v, float z, float inv) {
-  const int b = __float_as_int(__builtin_fmaf(v - z, inv, kMagic));
+__device__ __forceinline__ uint32_t code_bits(float v, float z, float inv, float s) {
+  const float d = v - z;
+  const float t0 = d * inv;
+  const float t = __builtin_fmaf(__builtin_fmaf(-t0, s, d), inv, t0);
+  const int b = __float_as_int(t + kMagic);
   return uint32_t(min(max(b, int(kMagicBits)), int(kMagicBits + 3u)));
 }
 
@@ -288,7 +296,7 @@ __device__ void qa_tiles(const QAParams& p, int h, QAShared<D, ONE>& sh) {
     const float sf = f16_to_f32(s16);
     const float inv = sf == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(sf);  // s16 = 0: every code is 0
     const float zr = f16_to_f32(z16) * iF;  // (y - z) / s = (acc - z/F) / (s/F)
-    const float invr = inv * F;
+    const float invr = inv * F, sr = sf * iF;
     const int m = l16;
     uint32_t bits;
     if (TENSOR == 0) {
@@ -297,7 +305,7 @@ __device__ void qa_tiles(const QAParams& p, int h, QAShared<D, ONE>& sh) {
       for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
         for (int r = 0; r < 4; ++r)
-          bits += code_bits(y[hb][r], zr, invr) << (16 * (r & 1) + 8 * (g & 1) + 4 * hb + 2 * (r >> 1));
+          bits += code_bits(y[hb][r], zr, invr, sr) << (16 * (r & 1) + 8 * (g & 1) + 4 * hb + 2 * (r >> 1));
     } else {
       // the four rows m = 4j..4j+3 (consecutive lanes) share these words:
       // their fields are OR-combined across the lane quartet, then lane m
@@ -305,8 +313,8 @@ __device__ void qa_tiles(const QAParams& p, int h, QAShared<D, ONE>& sh) {
       bits = 0;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        uint32_t wr = (code_bits(y[0][r], zr, invr) << vsh0) + word0;
-        wr += code_bits(y[1][r], zr, invr) << vsh1;
+        uint32_t wr = (code_bits(y[0][r], zr, invr, sr) << vsh0) + word0;
+        wr += code_bits(y[1][r], zr, invr, sr) << vsh1;
         wr |= uint32_t(__builtin_amdgcn_mov_dpp(int(wr), 0xB1, 0xF, 0xF, false));  // lanes ^1
         wr |= uint32_t(__builtin_amdgcn_mov_dpp(int(wr), 0x4E, 0xF, 0xF, false));  // lanes ^2
         bits = (m & 3) == r ? wr : bits;
