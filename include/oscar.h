@@ -250,6 +250,36 @@ oscar_status oscar_write_bf16(const oscar_cache* cache, const void* k_new,
                               const int32_t* row_seq, const int32_t* row_pos,
                               const int32_t* bt_h, int32_t max_pages, void* stream);
 
+/* One decode step's cache update in one launch ([TS] 2.2.B "Mixed-Precision
+ * Layout": sink and recent tokens stay in BF16, the middle history is INT2
+ * after the fixed rotation and clip).  For every sequence b < batch with
+ * L = seq_lens[b] >= 1 (the length the step decodes, its new token at
+ * position L - 1 included), with S = n_sink and W = n_recent of the cache:
+ *   - the new token (row b of k_new, v_new) is written to slot (L - 1) % 16 of
+ *     BF16 page bt_h[b][(L - 1) / 16] when it is a sink or recent token
+ *     (W >= 1, or L - 1 < S);
+ *   - the token entering the middle history, t = L - 1 - W (t = L - 1 when
+ *     W = 0), if t >= S, is quantized exactly as oscar_quantize_append does
+ *     into slot t % 16 of INT2 page bt_q[b][t / 16]; with W >= 1 its raw row
+ *     is read from its BF16 slot (bt_h[b][t / 16], t % 16), where the
+ *     previous steps left it.
+ * Sequences with L <= 0 are skipped.  Nothing else is written.
+ * k_new, v_new: device bf16 [batch][H_kv][d].  seq_lens: device int32 [batch].
+ * bt_q, bt_h: device int32 [B][max_pages] with B >= batch.  r_k, r_v: device
+ * float32 [H_kv][d][d].
+ * Preconditions (device contents): the named pages are valid and not shared
+ * with another sequence; the BF16 slot of token t still holds its row and is
+ * not the BF16 slot the new token goes to.
+ * Arithmetic: as oscar_quantize_append for up to 64 rows (float32 products).
+ * Errors: as oscar_quantize_append; both pools of the cache are required.
+ * batch == 0 returns OSCAR_OK and launches nothing. */
+oscar_status oscar_decode_step_update(const oscar_cache* cache, const void* k_new,
+                                      const void* v_new, int32_t batch,
+                                      const int32_t* seq_lens, const int32_t* bt_q,
+                                      const int32_t* bt_h, int32_t max_pages,
+                                      const float* r_k, const float* r_v,
+                                      float tau_k, float tau_v, void* stream);
+
 /* ------------------------------------------------------------------------ *
  * Paged decode attention over the mixed cache ([TS] 2.2.B "kernel
  * integration": unpacking, dequantization, inverse rotation and attention for

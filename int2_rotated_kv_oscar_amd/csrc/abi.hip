@@ -217,6 +217,26 @@ oscar_status oscar_write_bf16(const oscar_cache* cache, const void* k_new, const
   return hip_status(hipGetLastError(), "write_bf16 launch");
 }
 
+oscar_status oscar_decode_step_update(const oscar_cache* cache, const void* k_new, const void* v_new, int32_t batch,
+                                     const int32_t* seq_lens, const int32_t* bt_q, const int32_t* bt_h,
+                                     int32_t max_pages, const float* r_k, const float* r_v, float tau_k, float tau_v,
+                                     void* stream) {
+  oscar::clear_error();
+  if (oscar_status s = check_cache(cache, true, true)) return s;
+  if (batch < 0) return fail(OSCAR_ERR_INVALID_ARG, "batch < 0");
+  if (batch == 0) return OSCAR_OK;
+  if (!k_new || !v_new || !seq_lens || !bt_q || !bt_h || !r_k || !r_v)
+    return fail(OSCAR_ERR_INVALID_ARG, "null device pointer");
+  if (max_pages < 1) return fail(OSCAR_ERR_INVALID_ARG, "max_pages < 1");
+  if (!(tau_k > 0.f) || !(tau_v > 0.f) || !std::isfinite(tau_k) || !std::isfinite(tau_v))
+    return fail(OSCAR_ERR_INVALID_ARG, "clip thresholds must be finite and positive");
+  return hip_status(oscar_launch::decode_step_update(cache->d, cache->n_kv_heads, cache->n_sink, cache->n_recent,
+                                                     cache->int2_pool, cache->bf16_pool, k_new, v_new, batch,
+                                                     seq_lens, bt_q, bt_h, max_pages, r_k, r_v, tau_k, tau_v,
+                                                     static_cast<hipStream_t>(stream)),
+                    "decode_step_update launch");
+}
+
 oscar_status oscar_decode_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads, int32_t d,
                                           int32_t max_seq_len, int32_t split_pages, size_t* bytes) {
   oscar::clear_error();

@@ -12,6 +12,13 @@ hipError_t quantize_append(int d, int n_kv, void* pool, const void* k_new, const
                            int32_t max_pages, const float* r_k, const float* r_v, float tau_k, float tau_v,
                            int n_cus, hipStream_t stream);
 
+// one decode step's cache update: new tokens to BF16 slots, the token
+// leaving each recent window to INT2
+hipError_t decode_step_update(int d, int n_kv, int n_sink, int n_recent, void* int2_pool, void* bf16_pool,
+                              const void* k_new, const void* v_new, int batch, const int32_t* seq_lens,
+                              const int32_t* bt_q, const int32_t* bt_h, int32_t max_pages, const float* r_k,
+                              const float* r_v, float tau_k, float tau_v, hipStream_t stream);
+
 size_t decode_lds_bytes(int d, int G, bool all_raw);
 int decode_max_records();  // record slots per (sequence, KV head) the merge can hold
 int decode_min_slice();    // pages per workgroup slice at least

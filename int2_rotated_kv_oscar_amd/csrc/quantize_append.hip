@@ -39,6 +39,11 @@ struct QAParams {
   float tau_k, tau_v;
   uint8_t* pool;
   int32_t n_kv;
+  // decode-step update only: lengths, BF16 tables and pool, regions
+  const int32_t* seq_lens;
+  const int32_t* bt_h;
+  uint16_t* bf16_pool;
+  int32_t n_sink, n_recent;
 };
 
 // Per-tile row metadata: lane l16 describes row tile*16 + l16 (all quads hold
@@ -437,11 +442,18 @@ __global__ __launch_bounds__(64 * (D / 32), 4) void quantize_append_kernel(QAPar
 // code words of a K row and whole code bytes of a V row in the page layout,
 // so every field is written with a plain store: no atomics, whatever other
 // rows share the words.
+//
+// STEP (a decode step's cache update, one row per sequence): for sequence b
+// of length L (the new token at position L - 1 included) the row entering the
+// middle history is the token L - 1 - W leaving the recent window, read from
+// its BF16 slot (with W = 0, the new token itself, from k_new/v_new), if it
+// lies at or past the sink; and the new token is written to its BF16 slot
+// when it is a sink or recent token.
 constexpr int kRowsPerWg = 8;
 constexpr int kRowThreads = 256;
 constexpr int64_t kFewRows = 64;  // row counts up to this take the few-row kernel
 
-template <int D>
+template <int D, bool STEP>
 __global__ __launch_bounds__(kRowThreads) void quantize_rows_kernel(QAParams p) {
   using GG = Geo<D>;
   constexpr int NG = GG::NG, NW = GG::NW;
@@ -458,21 +470,50 @@ __global__ __launch_bounds__(kRowThreads) void quantize_rows_kernel(QAParams p) 
   __shared__ float s_part[kRowsPerWg][16][64];  // [row][k-slice][channel of the pair]
   __shared__ uint16_t s_x[kRowsPerWg][D];
   __shared__ uint8_t s_code[kRowsPerWg][64];
-  __shared__ int32_t s_page[kRowsPerWg], s_slot[kRowsPerWg];
+  __shared__ int32_t s_page[kRowsPerWg], s_slot[kRowsPerWg];  // INT2 destination (-1: none)
+  __shared__ int32_t s_src[kRowsPerWg];                        // STEP: BF16 page of the row (-1: k_new/v_new)
+  __shared__ int32_t s_new[kRowsPerWg], s_newslot[kRowsPerWg];  // STEP: BF16 slot of the new token (-1: none)
 
   // row metadata first (the page ids need a second round trip)
   if (tid < nr) {
-    const int32_t seq = p.row_seq[row0 + tid], pos = p.row_pos[row0 + tid];
-    s_page[tid] = p.bt_q[int64_t(seq) * p.max_pages + (pos >> 4)];
-    s_slot[tid] = pos & 15;
+    if (!STEP) {
+      const int32_t seq = p.row_seq[row0 + tid], pos = p.row_pos[row0 + tid];
+      s_page[tid] = p.bt_q[int64_t(seq) * p.max_pages + (pos >> 4)];
+      s_slot[tid] = pos & 15;
+    } else {
+      const int64_t b = row0 + tid;
+      const int32_t L = p.seq_lens[b];
+      int32_t t = -1, src = -1, nw = -1;
+      if (L >= 1) {
+        if (p.n_recent >= 1 || L - 1 < p.n_sink) nw = p.bt_h[b * p.max_pages + ((L - 1) >> 4)];
+        t = p.n_recent >= 1 ? L - 1 - p.n_recent : L - 1;
+        if (t < p.n_sink) t = -1;
+        else if (p.n_recent >= 1) src = p.bt_h[b * p.max_pages + (t >> 4)];
+      }
+      s_page[tid] = t >= 0 ? p.bt_q[b * p.max_pages + (t >> 4)] : -1;
+      s_slot[tid] = t & 15;
+      s_src[tid] = src;
+      s_new[tid] = nw;
+      s_newslot[tid] = (L - 1) & 15;
+    }
   }
+  if (STEP) __syncthreads();
   // the chunk's x rows to LDS (rows past the chunk re-read its last row;
   // their results are never stored)
   constexpr int kXPer = kRowsPerWg * D / kRowThreads;
 #pragma unroll
   for (int i = 0; i < kXPer; ++i) {
-    const int e = tid * kXPer + i, r = e / D, c = e % D;
-    s_x[r][c] = X[((row0 + min(r, nr - 1)) * p.n_kv + h) * D + c];
+    const int e = tid * kXPer + i, r = e / D, c = e % D, rr = min(r, nr - 1);
+    uint16_t val = 0;
+    if (!STEP) {
+      val = X[((row0 + rr) * p.n_kv + h) * D + c];
+    } else if (s_src[rr] >= 0) {  // K token-major, V channel-major in the BF16 page
+      const uint16_t* hp = p.bf16_pool + (int64_t(s_src[rr]) * p.n_kv + h) * GG::BF16_HEAD_ELEMS;
+      val = tensor == 0 ? hp[s_slot[rr] * D + c] : hp[16 * D + c * 16 + s_slot[rr]];
+    } else if (s_page[rr] >= 0) {
+      val = X[((row0 + rr) * p.n_kv + h) * D + c];
+    }
+    s_x[r][c] = val;
   }
   // products: thread (k-slice ks, channel quad c4) over the rows
   const int c4 = tid & 15, ks = tid >> 4;
@@ -519,7 +560,7 @@ __global__ __launch_bounds__(kRowThreads) void quantize_rows_kernel(QAParams p) 
     int code = 0;
     if (sf != 0.0f) code = min(max(int(__builtin_rintf((y[gp] - zf) / sf)), 0), 3);
     s_code[rw][32 * gp + cc] = uint8_t(code);
-    if (cc == 0 && rw < nr) {
+    if (cc == 0 && rw < nr && s_page[rw] >= 0) {
       const int g = 2 * pair + gp, slot = s_slot[rw];
       uint8_t* base = p.pool + (int64_t(s_page[rw]) * p.n_kv + h) * int64_t(GG::HEAD_BYTES);
       const int iu = tensor == 0 ? slot * NG + g : ((slot >> 2) * NG + g) * 4 + (slot & 3);
@@ -535,7 +576,7 @@ __global__ __launch_bounds__(kRowThreads) void quantize_rows_kernel(QAParams p) 
   // 2 (r % 2) + r / 2 of word (q 16 + c16) NW + pair holds channel 16 bb + c16
   // of the pair at bit 2 bb.
   if (tensor == 0) {
-    if (tid < 4 * nr) {
+    if (tid < 4 * nr && s_page[tid >> 2] >= 0) {
       const int row = tid >> 2, quad = tid & 3, slot = s_slot[row];
       uint32_t w = 0;
 #pragma unroll
@@ -549,7 +590,7 @@ __global__ __launch_bounds__(kRowThreads) void quantize_rows_kernel(QAParams p) 
       reinterpret_cast<uint32_t*>(base + GG::KC)[(quad * 16 + slot) * NW + pair] = w;
     }
   } else {
-    if (tid < 16 * nr) {
+    if (tid < 16 * nr && s_page[tid >> 4] >= 0) {
       const int row = tid >> 4, c16 = tid & 15, slot = s_slot[row];
       const int q = slot >> 2, r = slot & 3;
       uint32_t bits = 0;
@@ -557,6 +598,19 @@ __global__ __launch_bounds__(kRowThreads) void quantize_rows_kernel(QAParams p) 
       for (int bb = 0; bb < 4; ++bb) bits |= uint32_t(s_code[row][16 * bb + c16]) << (2 * bb);
       uint8_t* base = p.pool + (int64_t(s_page[row]) * p.n_kv + h) * int64_t(GG::HEAD_BYTES);
       base[GG::VC + ((q * 16 + c16) * NW + pair) * 4 + 2 * (r & 1) + (r >> 1)] = uint8_t(bits);
+    }
+  }
+  if (STEP && pair == 0) {
+    // the new tokens to their BF16 slots (the first group pair's workgroups)
+    const int rw2 = tid >> 5;
+    if (rw2 < nr && s_new[rw2] >= 0) {
+      uint16_t* hp = p.bf16_pool + (int64_t(s_new[rw2]) * p.n_kv + h) * GG::BF16_HEAD_ELEMS;
+      const uint16_t* xr = X + ((row0 + rw2) * p.n_kv + h) * D;
+      const int slot = s_newslot[rw2];
+      for (int c = tid & 31; c < D; c += 32) {
+        if (tensor == 0) hp[slot * D + c] = xr[c];
+        else hp[16 * D + c * 16 + slot] = xr[c];
+      }
     }
   }
 }
@@ -577,8 +631,8 @@ hipError_t quantize_append(int d, int n_kv, void* pool, const void* k_new, const
     // few rows: plain float32 products, a slice of R per workgroup
     const dim3 grid(static_cast<unsigned>((n_rows + kRowsPerWg - 1) / kRowsPerWg), static_cast<unsigned>(n_kv),
                     static_cast<unsigned>(d / 32));  // (tensor, group pair)
-    if (d == 128) hipLaunchKernelGGL((quantize_rows_kernel<128>), grid, dim3(kRowThreads), 0, stream, p);
-    else hipLaunchKernelGGL((quantize_rows_kernel<64>), grid, dim3(kRowThreads), 0, stream, p);
+    if (d == 128) hipLaunchKernelGGL((quantize_rows_kernel<128, false>), grid, dim3(kRowThreads), 0, stream, p);
+    else hipLaunchKernelGGL((quantize_rows_kernel<64, false>), grid, dim3(kRowThreads), 0, stream, p);
     return hipGetLastError();
   }
   const int64_t tiles = (n_rows + 15) / 16;
@@ -593,6 +647,20 @@ hipError_t quantize_append(int d, int n_kv, void* pool, const void* k_new, const
     if (one) hipLaunchKernelGGL((quantize_append_kernel<64, true>), grid, dim3(128), 0, stream, p);
     else hipLaunchKernelGGL((quantize_append_kernel<64, false>), grid, dim3(128), 0, stream, p);
   }
+  return hipGetLastError();
+}
+
+hipError_t decode_step_update(int d, int n_kv, int n_sink, int n_recent, void* int2_pool, void* bf16_pool,
+                              const void* k_new, const void* v_new, int batch, const int32_t* seq_lens,
+                              const int32_t* bt_q, const int32_t* bt_h, int32_t max_pages, const float* r_k,
+                              const float* r_v, float tau_k, float tau_v, hipStream_t stream) {
+  QAParams p{static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), batch, nullptr, nullptr,
+             bt_q, max_pages, r_k, r_v, tau_k, tau_v, static_cast<uint8_t*>(int2_pool), n_kv,
+             seq_lens, bt_h, static_cast<uint16_t*>(bf16_pool), n_sink, n_recent};
+  const dim3 grid(static_cast<unsigned>((batch + kRowsPerWg - 1) / kRowsPerWg), static_cast<unsigned>(n_kv),
+                  static_cast<unsigned>(d / 32));
+  if (d == 128) hipLaunchKernelGGL((quantize_rows_kernel<128, true>), grid, dim3(kRowThreads), 0, stream, p);
+  else hipLaunchKernelGGL((quantize_rows_kernel<64, true>), grid, dim3(kRowThreads), 0, stream, p);
   return hipGetLastError();
 }
 

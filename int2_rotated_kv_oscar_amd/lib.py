@@ -24,8 +24,8 @@ STATUS_NAMES = {0: "OSCAR_OK", 1: "OSCAR_ERR_INVALID_ARG", 2: "OSCAR_ERR_UNSUPPO
 # Every symbol include/oscar.h declares.
 EXPORTS = [
     "oscar_status_string", "oscar_last_error", "oscar_version", "oscar_build_rotation",
-    "oscar_build_fixed_rotation", "oscar_int2_page_bytes", "oscar_bf16_page_bytes", "oscar_quantize_append", "oscar_write_bf16",
-    "oscar_decode_workspace_bytes", "oscar_decode_workspace_init", "oscar_paged_decode_attn",
+    "oscar_build_fixed_rotation", "oscar_int2_page_bytes", "oscar_bf16_page_bytes", "oscar_quantize_append",
+    "oscar_write_bf16", "oscar_decode_step_update", "oscar_decode_workspace_bytes", "oscar_decode_workspace_init", "oscar_paged_decode_attn",
     "oscar_paged_decode_attn_bf16",
 ]
 
@@ -73,6 +73,8 @@ def load(path: str = LIB_PATH):
         "oscar_quantize_append": (_STATUS, [ctypes.POINTER(OscarCache), _P, _P, _I64, _P, _P, _P, _I32, _P, _P,
                                             _F32, _F32, _P]),
         "oscar_write_bf16": (_STATUS, [ctypes.POINTER(OscarCache), _P, _P, _I64, _P, _P, _P, _I32, _P]),
+        "oscar_decode_step_update": (_STATUS, [ctypes.POINTER(OscarCache), _P, _P, _I32, _P, _P, _P, _I32, _P, _P,
+                                               _F32, _F32, _P]),
         "oscar_decode_workspace_bytes": (_STATUS, [_I32, _I32, _I32, _I32, _I32, _I32, ctypes.POINTER(_SZ)]),
         "oscar_decode_workspace_init": (_STATUS, [_P, _SZ, _P]),
         "oscar_paged_decode_attn": (_STATUS, [ctypes.POINTER(OscarCache), _P, _I32, _I32, _P, _I32, _P, _P, _I32,
@@ -188,6 +190,15 @@ def write_bf16(cache: OscarCache, k_new, v_new, row_seq, row_pos, bt_h, stream=N
     n = k_new.shape[0]
     _check(load().oscar_write_bf16(ctypes.byref(cache), _dptr(k_new), _dptr(v_new), n, _dptr(row_seq),
                                    _dptr(row_pos), _dptr(bt_h), bt_h.shape[1], _stream(stream)))
+
+
+def decode_step_update(cache: OscarCache, k_new, v_new, seq_lens, bt_q, bt_h, r_k, r_v, tau_k: float, tau_v: float,
+                       stream=None):
+    """k_new/v_new bf16 [B, H_kv, d] (the new tokens); seq_lens int32 [B] (lengths with them)."""
+    b = k_new.shape[0]
+    _check(load().oscar_decode_step_update(ctypes.byref(cache), _dptr(k_new), _dptr(v_new), b, _dptr(seq_lens),
+                                           _dptr(bt_q), _dptr(bt_h), bt_q.shape[1], _dptr(r_k), _dptr(r_v),
+                                           float(tau_k), float(tau_v), _stream(stream)))
 
 
 def decode_workspace_bytes(batch: int, n_kv_heads: int, n_q_heads: int, d: int, max_seq_len: int,

@@ -59,3 +59,43 @@ def build_from_inputs(inp, r_k, r_v, tau_k: float, tau_v: float):
     hs, hp, hr = synth.bf16_rows(inp)
     write_bf16(bf, inp.k_rows[hr], inp.v_rows[hr], hs, hp, inp.bt_h)
     return int2, bf, res, (ms, mp, mr)
+
+
+def decode_step_update(int2: Int2Pool, bf: Bf16Pool, k_new: np.ndarray, v_new: np.ndarray, seq_lens, bt_q, bt_h,
+                       n_sink: int, n_recent: int, r_k, r_v, tau_k: float, tau_v: float, bf16_to_f64):
+    """One decode step's cache writes under the mixed-precision layout
+    ([TS] 2.2.B: sink and recent tokens in BF16, the middle history in INT2).
+
+    For sequence b of length L (its new token at L - 1 included): the new
+    token goes to its BF16 slot if it is a sink or recent token; the token
+    that enters the middle history at this length (L - 1 - W, the one leaving
+    the recent window; L - 1 itself when W = 0) is quantized into its INT2
+    slot, its raw row taken from its BF16 slot (W >= 1) or from the new row.
+    Returns (AppendResult of the quantized rows, their (seq, pos) arrays).
+    """
+    rows_k, rows_v, seqs, poss = [], [], [], []
+    new_seq, new_pos = [], []
+    bt_q = np.asarray(bt_q); bt_h = np.asarray(bt_h)
+    for b, L in enumerate(np.asarray(seq_lens, np.int64)):
+        if L < 1:
+            continue
+        p = int(L) - 1
+        t = p - n_recent if n_recent >= 1 else p
+        if t >= n_sink:
+            if n_recent >= 1:
+                pg, sl = bt_h[b, t // PAGE], t % PAGE
+                kv = [bf.read(np.array([pg]), np.array([sl]), h) for h in range(bf.hkv)]
+                rows_k.append(np.stack([x[0][0] for x in kv]))
+                rows_v.append(np.stack([x[1][0] for x in kv]))
+            else:
+                rows_k.append(k_new[b]); rows_v.append(v_new[b])
+            seqs.append(b); poss.append(t)
+        if n_recent >= 1 or p < n_sink:
+            new_seq.append(b); new_pos.append(p)
+    res = None
+    if seqs:
+        res = quantize_append(int2, np.stack(rows_k), np.stack(rows_v), seqs, poss, bt_q, r_k, r_v, tau_k, tau_v,
+                              bf16_to_f64)
+    if new_seq:
+        write_bf16(bf, k_new[new_seq], v_new[new_seq], new_seq, new_pos, bt_h)
+    return res, (np.array(seqs, np.int64), np.array(poss, np.int64))

@@ -71,6 +71,18 @@ def test_device_calls_validate_before_launch():
                                      None, 0, 16, None) == 4
     assert L.oscar_paged_decode_attn(ctypes.byref(c), 16, 1, 4, 16, 33, 16, 16, 2, 16, 16, 0.1, 0,
                                      16, 1 << 20, 16, None) == 1   # max_seq_len > 16 * max_pages
+    # decode-step update: both pools required, batch 0 a no-op, then pointers and clips
+    c2 = lib.OscarCache()
+    c2.d, c2.n_kv_heads, c2.n_recent = 128, 1, 4
+    c2.int2_pool, c2.n_int2_pages = 16, 1
+    assert L.oscar_decode_step_update(ctypes.byref(c2), 16, 16, 1, 16, 16, 16, 1, 16, 16, 1.0, 1.0, None) == 1
+    assert b"BF16 pool missing" in L.oscar_last_error()
+    c2.bf16_pool, c2.n_bf16_pages = 16, 1
+    assert L.oscar_decode_step_update(ctypes.byref(c2), None, None, 0, None, None, None, 1, None, None, 1.0, 1.0,
+                                      None) == 0
+    assert L.oscar_decode_step_update(ctypes.byref(c2), 16, 16, -1, 16, 16, 16, 1, 16, 16, 1.0, 1.0, None) == 1
+    assert L.oscar_decode_step_update(ctypes.byref(c2), 16, 16, 1, 16, None, 16, 1, 16, 16, 1.0, 1.0, None) == 1
+    assert L.oscar_decode_step_update(ctypes.byref(c2), 16, 16, 1, 16, 16, 16, 1, 16, 16, 0.0, 1.0, None) == 1
     assert L.oscar_decode_workspace_init(None, 64, None) == 4
 
 

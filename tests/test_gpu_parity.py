@@ -182,6 +182,65 @@ def test_quantize_append_few_rows(d, hkv, n_rows):
     assert np.array_equal(cleared[0], cleared[1]), "bytes outside the appended rows changed"
 
 
+@pytest.mark.parametrize("d,hkv,S,W", [(64, 1, 4, 32), (128, 2, 4, 128), (64, 2, 4, 0), (128, 1, 0, 16)])
+def test_decode_step_update(d, hkv, S, W):
+    # one decode step's cache update (new tokens to BF16, the tokens leaving
+    # the recent windows to INT2, read from their BF16 slots) against the
+    # oracle's, over lengths around the region edges, on stale pools
+    lens = np.array([0, 1, 3, 4, 5, S + W, S + W + 1, S + W + 2, 77, 160, 161, 300, 47, 250, 299], np.int32)
+    B, maxl = len(lens), int(lens.max())
+    mp = (maxl + 15) // 16
+    w = synth.Workload("step", 6, B, 4 * hkv, hkv, d, S, W, 64, ("fixed", maxl, maxl))
+    k, v, _, _ = synth.prefill_rows(w, B, maxl)   # row b * maxl + position
+    rng = np.random.default_rng(77 + d + W)
+    bt_q = rng.permutation(B * mp).astype(np.int32).reshape(B, mp)
+    bt_h = rng.permutation(B * mp).astype(np.int32).reshape(B, mp)
+    cal = synth.calibration_set(w, n_rows=256)
+    from oracle import rotation as orot
+    rt = orot.build_rotation(cal.q, cal.k, cal.v, w.group_q)
+    f = lambda a: np.asarray(a, np.float32).astype(np.float64)  # noqa: E731
+    rot = gh.Rotation(f(rt["r_k"]), f(rt["r_v"]), float(np.float32(rt["tau_k"])), float(np.float32(rt["tau_v"])))
+    # state the previous steps left: every earlier token's raw row in its BF16 slot
+    int2_0 = rng.integers(0, 256, size=B * mp * lib.int2_page_bytes(d, hkv), dtype=np.uint8)
+    bf_0 = olayout.Bf16Pool(B * mp, hkv, d, rng.integers(0, 65536, size=(B * mp, hkv, 32 * d), dtype=np.uint16))
+    seq = np.repeat(np.arange(B), np.maximum(lens - 1, 0))
+    pos = np.concatenate([np.arange(max(L - 1, 0)) for L in lens]).astype(np.int64)
+    ocache.write_bf16(bf_0, k[seq * maxl + pos], v[seq * maxl + pos], seq, pos, bt_h)
+    newrow = np.arange(B) * maxl + np.maximum(lens - 1, 0)
+    k_new, v_new = k[newrow], v[newrow]
+    # GPU
+    int2 = torch.from_numpy(int2_0.copy()).to(gh.DEV)
+    bf16 = torch.from_numpy(bf_0.data.copy().reshape(-1).view(np.int16)).to(gh.DEV)
+    cache = lib.make_cache(d, hkv, S, W, int2, bf16)
+    print(f"[step update d={d} hkv={hkv} S={S} W={W}]", flush=True)
+    lib.decode_step_update(cache, gh.bits_to_dev_bf16(k_new), gh.bits_to_dev_bf16(v_new), gh.i32(lens), gh.i32(bt_q),
+                           gh.i32(bt_h), torch.from_numpy(rot.r_k.astype(np.float32)).to(gh.DEV),
+                           torch.from_numpy(rot.r_v.astype(np.float32)).to(gh.DEV), rot.tau_k, rot.tau_v)
+    torch.cuda.synchronize()
+    got_q = int2.cpu().numpy()
+    got_h = bf16.cpu().numpy().view(np.uint16).reshape(B * mp, hkv, 32 * d)
+    # oracle
+    i2 = olayout.Int2Pool(B * mp, hkv, d, int2_0.copy())
+    bf = olayout.Bf16Pool(B * mp, hkv, d, bf_0.data.copy())
+    res, (sq, ps) = ocache.decode_step_update(i2, bf, k_new, v_new, lens, bt_q, bt_h, S, W, rot.r_k, rot.r_v,
+                                              rot.tau_k, rot.tau_v, olayout.bf16_to_f64)
+    assert np.array_equal(got_h, bf.data), "BF16 pool differs"
+    page, slot = bt_q[sq, ps // 16].astype(np.int64), (ps % 16).astype(np.int64)
+    assert len(sq) >= 7
+    rep = gh.compare_appended(got_q, w, B * mp, res, page, slot)
+    print(rep)
+    gh.assert_codes_ok(rep, "step update")
+    cleared = []
+    for data in (got_q.copy(), i2.data.copy()):
+        pc = olayout.Int2Pool(B * mp, hkv, d, data)
+        zc = np.zeros((len(sq), d), np.uint8)
+        zs = np.zeros((len(sq), d // 32), np.float16)
+        for h in range(hkv):
+            pc.write(page, slot, h, zc, zc, zs, zs, zs, zs)
+        cleared.append(pc.data)
+    assert np.array_equal(cleared[0], cleared[1]), "INT2 bytes outside the quantized rows changed"
+
+
 def test_decode_on_oracle_pages_tiny(tiny_rot):
     w = _tiny()
     inp = synth.decode_inputs(w)

@@ -169,3 +169,36 @@ def test_brute_force_eight_tokens():
     out2 = att.decode_attention_rotated(q[None], int2, bf, inp.seq_lens, inp.bt_q, inp.bt_h, rk[None], rv[None], S, W,
                                         chunk_tokens=3)
     np.testing.assert_allclose(out2[0], expect, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("S,W", [(4, 32), (4, 0), (0, 16)])
+def test_step_updates_rebuild_the_batch_fill(S, W):
+    # a sequence grown one decode step at a time (new token to BF16, the token
+    # leaving the recent window to INT2) ends with the same sink/recent BF16
+    # slots and the same INT2 middle slots as filling the cache at once from
+    # the raw rows by region ([TS] 2.2.B mixed-precision layout)
+    from oracle import cache as oc
+    from oracle import layout as ol
+    d, hkv, L = 64, 1, 90
+    rng = np.random.default_rng(21)
+    k = synth.to_bf16_bits(rng.standard_normal((L, hkv, d)))
+    v = synth.to_bf16_bits(rng.standard_normal((L, hkv, d)))
+    r = np.linalg.qr(rng.standard_normal((d, d)))[0][None]
+    pages = (L + 15) // 16
+    bt = rng.permutation(pages).reshape(1, pages)
+    i2, bf = ol.Int2Pool(pages, hkv, d), ol.Bf16Pool(pages, hkv, d)
+    for n in range(1, L + 1):
+        oc.decode_step_update(i2, bf, k[n - 1:n], v[n - 1:n], [n], bt, bt, S, W, r, r, 2.5, 2.5, ol.bf16_to_f64)
+    i2f, bff = ol.Int2Pool(pages, hkv, d), ol.Bf16Pool(pages, hkv, d)
+    mid = np.arange(S, L - W)
+    oc.quantize_append(i2f, k[mid], v[mid], np.zeros_like(mid), mid, bt, r, r, 2.5, 2.5, ol.bf16_to_f64)
+    raw = np.r_[np.arange(min(S, L)), np.arange(max(S, L - W), L)]
+    oc.write_bf16(bff, k[raw], v[raw], np.zeros_like(raw), raw, bt)
+    page_q, slot_q = bt[0, mid // 16], mid % 16
+    a, b = i2.read(page_q, slot_q, 0), i2f.read(page_q, slot_q, 0)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+    page_h, slot_h = bt[0, raw // 16], raw % 16
+    for x, y in zip(bf.read(page_h, slot_h, 0), bff.read(page_h, slot_h, 0)):
+        assert np.array_equal(x, y)
+    assert len(mid) == L - W - S and len(raw) == S + W
