@@ -168,13 +168,30 @@ def main() -> int:
     nbq = lib.int2_page_bytes(w.d, w.n_kv_heads)
     nbh = lib.bf16_page_bytes(w.d, w.n_kv_heads)
     int2 = torch.zeros(inp.n_int2_pages * nbq, dtype=torch.uint8, device=dev)
-    bf16 = torch.zeros(inp.n_bf16_pages * nbh // 2, dtype=torch.int16, device=dev)
+    B0 = len(inp.seq_lens)
+    # one spare BF16 page per sequence: the serving step reads the token that
+    # leaves the recent window from its BF16 slot, whose page the current
+    # window may no longer hold
+    bf16 = torch.zeros((inp.n_bf16_pages + B0) * nbh // 2, dtype=torch.int16, device=dev)
     cache = lib.make_cache(w.d, w.n_kv_heads, w.n_sink, w.n_recent, int2, bf16)
-    bt_q, bt_h = i32(inp.bt_q), i32(inp.bt_h)
+    bt_h_np = inp.bt_h.copy()
+    lv_seq, lv_pos, lv_row = [], [], []
+    for b, L in enumerate(inp.seq_lens):
+        t = int(L) - 1 - w.n_recent
+        if w.n_recent >= 1 and t >= w.n_sink:
+            if bt_h_np[b, t // 16] < 0:
+                bt_h_np[b, t // 16] = inp.n_bf16_pages + b
+            lv_seq.append(b); lv_pos.append(t); lv_row.append(inp.row_of[b][t])
+    bt_q, bt_h = i32(inp.bt_q), i32(bt_h_np)
     ms, mp, mr = synth.middle_rows(inp)
     lib.quantize_append(cache, bf(inp.k_rows[mr]), bf(inp.v_rows[mr]), i32(ms), i32(mp), bt_q, r_k, r_v, tau_k, tau_v)
     hs, hp, hr = synth.bf16_rows(inp)
     lib.write_bf16(cache, bf(inp.k_rows[hr]), bf(inp.v_rows[hr]), i32(hs), i32(hp), bt_h)
+    if lv_seq:  # the leaving tokens' rows, where the previous steps left them
+        lib.write_bf16(cache, bf(inp.k_rows[np.array(lv_row)]), bf(inp.v_rows[np.array(lv_row)]), i32(lv_seq),
+                       i32(lv_pos), bt_h)
+    new_rows = np.array([inp.row_of[b][max(int(L) - 1, 0)] for b, L in enumerate(inp.seq_lens)])
+    n_k, n_v = bf(inp.k_rows[new_rows]), bf(inp.v_rows[new_rows])
     torch.cuda.synchronize()
 
     # per step: the row leaving the recent window of every sequence
@@ -253,6 +270,39 @@ def main() -> int:
                      "kernel": decode_kernel_name(w, args.split_pages, False), "algorithmic_bytes_per_launch": nbytes["total"],
                      "avg_launch_us": round(dec_avg * 1e3, 2)},
     }
+
+    # serving step: one launch of the decode-step cache update (the new token
+    # to its BF16 slot, the token leaving the recent window quantized into
+    # INT2 from its BF16 slot) + the decode
+    def serve(i):
+        c = caches[i % copies]
+        _, _, prk, prv = pools[i % copies]
+        lib.decode_step_update(c, n_k, n_v, seq_lens, bt_q, bt_h, prk, prv, tau_k, tau_v)
+        lib.paged_decode_attn(c, qs[i % copies], seq_lens, inp.max_seq_len, bt_q, bt_h, prk, prv, out, ws,
+                              split_pages=args.split_pages)
+
+    for i in range(args.warmup):
+        serve(i)
+    torch.cuda.synchronize()
+    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s0.record()
+    for i in range(K):
+        serve(i)
+    s1.record()
+    torch.cuda.synchronize()
+    serve_ms = s0.elapsed_time(s1) / K
+    s0.record()
+    for i in range(K):
+        lib.decode_step_update(caches[i % copies], n_k, n_v, seq_lens, bt_q, bt_h, pools[i % copies][2],
+                               pools[i % copies][3], tau_k, tau_v)
+    s1.record()
+    torch.cuda.synchronize()
+    upd_ms = s0.elapsed_time(s1) / K
+    result["serving_step"] = {"kernels": [f"quantize_rows_kernel<{w.d},true>", decode_kernel_name(w, args.split_pages, False)],
+                              "us_per_step": round(serve_ms * 1e3, 2),
+                              "KV_tokens_per_s": round(tokens / (serve_ms * 1e-3), 1),
+                              "update_us_per_call": round(upd_ms * 1e3, 2)}
+    log(f"serving step (update + decode) {serve_ms * 1e3:.1f} us, update alone {upd_ms * 1e3:.1f} us")
 
     if not args.no_bf16_baseline:
         # the same decode over an all-BF16 cache (every token in BF16 pages)
@@ -425,10 +475,11 @@ def _cpu_baseline(inp, w, cache, int2, bf16, rt, tokens, log) -> dict:
     import torch
     from oracle import attention as oatt
     from oracle import layout as olayout
-    from int2_rotated_kv_oscar_amd import synth
+    from int2_rotated_kv_oscar_amd import lib, synth
     cores = len(os.sched_getaffinity(0))
     pool_q = olayout.Int2Pool(inp.n_int2_pages, w.n_kv_heads, w.d, int2.cpu().numpy())
-    pool_h = olayout.Bf16Pool(inp.n_bf16_pages, w.n_kv_heads, w.d, bf16.cpu().numpy().view(np.uint16))
+    pool_h = olayout.Bf16Pool(bf16.numel() * 2 // lib.bf16_page_bytes(w.d, w.n_kv_heads), w.n_kv_heads, w.d,
+                              bf16.cpu().numpy().view(np.uint16))
     q = synth.bf16_bits_to_f32(inp.q).astype(np.float64)
     rk = rt["r_k"].astype(np.float32).astype(np.float64)
     rv = rt["r_v"].astype(np.float32).astype(np.float64)
@@ -437,7 +488,7 @@ def _cpu_baseline(inp, w, cache, int2, bf16, rt, tokens, log) -> dict:
     t0 = time.time()
     for h in range(w.n_kv_heads):
         one_q = olayout.Int2Pool(inp.n_int2_pages, 1, w.d, pool_q.data[:, h:h + 1])
-        one_h = olayout.Bf16Pool(inp.n_bf16_pages, 1, w.d, pool_h.data[:, h:h + 1])
+        one_h = olayout.Bf16Pool(pool_h.n_pages, 1, w.d, pool_h.data[:, h:h + 1])
         G = w.group_q
         oatt.decode_attention(q[:, h * G:(h + 1) * G], one_q, one_h, inp.seq_lens, inp.bt_q, inp.bt_h,
                               rk[h:h + 1], rv[h:h + 1], w.n_sink, w.n_recent)
