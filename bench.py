@@ -119,6 +119,8 @@ def main() -> int:
                     help="only run 5 plain device copies of MIB MiB (calibrates HBM byte counters), then exit")
     ap.add_argument("--append-prefill", action="store_true",
                     help="measure quantize-append alone on the large-GQA layer's prefill (8 sequences x 8192 rows)")
+    ap.add_argument("--calib-gram", action="store_true",
+                    help="measure the GPU calibration target (Q^T Q per KV head) on the Qwen3-8B calibration rows")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the decode path shards by KV head "
@@ -147,6 +149,8 @@ def main() -> int:
     lib.load()
     if args.append_prefill:
         return run_append_prefill(args, log)
+    if args.calib_gram:
+        return run_calib_gram(args, log)
     w = synth.WORKLOADS[args.workload]
     t0 = time.time()
     inp = synth.decode_inputs(w)
@@ -431,6 +435,72 @@ def run_append_prefill(args, log) -> int:
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = _cpu_append_baseline(k, v, row_seq, row_pos, bt, rt, w, n_rows, log)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+GRAM_METRIC = "calibration Gram pooled rows/s + achieved HBM GB/s (% of peak), Qwen3-8B calibration"
+
+
+def run_calib_gram(args, log) -> int:
+    """oscar_calib_gram on the Qwen3-8B calibration set (8192 rows x 32 query
+    heads, d = 128, pooled over 8 KV groups of 4): bytes = the bf16 rows read
+    + the float64 targets written; inputs rotate over copies totalling >= 1 GiB."""
+    import torch
+    from int2_rotated_kv_oscar_amd import lib, synth
+    dev = "cuda:0"
+    w = synth.WORKLOADS["qwen3-8b-b1-32k"]
+    cal = synth.calibration_set(w)
+    q_bits = synth.to_bf16_bits(cal.q)
+    n, hx, d = q_bits.shape
+    x0 = torch.from_numpy(np.ascontiguousarray(q_bits).view(np.int16)).to(dev).view(torch.bfloat16)
+    copies = args.copies or max(1, int(np.ceil((1 << 30) / q_bits.nbytes)))
+    xs = [x0] + [x0.clone() for _ in range(copies - 1)]
+    outs = [torch.empty((w.n_kv_heads, d, d), dtype=torch.float64, device=dev) for _ in range(copies)]
+    for i in range(args.warmup):
+        lib.calib_gram(xs[i % copies], w.n_kv_heads, outs[i % copies])
+    torch.cuda.synchronize()
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(K):
+        lib.calib_gram(xs[i % copies], w.n_kv_heads, outs[i % copies])
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / K
+    nbytes = q_bits.nbytes + w.n_kv_heads * d * d * 8
+    flops = 2 * n * hx * d * d
+    achieved = nbytes / (ms * 1e-3) / 1e9
+    log(f"calib_gram {ms * 1e3:.1f} us, {achieved:.0f} GB/s, {flops / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
+    result = {
+        "metric": GRAM_METRIC, "value": round(n * hx / (ms * 1e-3), 1), "unit": "pooled rows/s", "n_gpus": 1,
+        "steps": K, "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16 in, bf16 MFMA, f32 blocks, f64 sums", "data": "synthetic",
+        "config": {"workload": "qwen3-8b-calibration", "rows": n, "q_heads": hx, "kv_heads": w.n_kv_heads,
+                   "head_dim": d, "copies": copies},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "calib_gram_kernel<128>", "algorithmic_bytes_per_launch": nbytes,
+                     "avg_launch_us": round(ms * 1e3, 2),
+                     "mfma_tflops_algorithmic": round(flops / (ms * 1e-3) / 1e12, 2)},
+    }
+    if not args.no_cpu_baseline:
+        from oracle import rotation as orot
+        cores = len(os.sched_getaffinity(0))
+        q64 = cal.q.astype(np.float64)
+        t0 = time.time()
+        heads = 0
+        for h in range(w.n_kv_heads):  # the oracle's Q target, head by head, for about 10 s at most
+            orot.calibration_targets(q64[:, 4 * h:4 * h + 4], cal.k[:, h:h + 1].astype(np.float64),
+                                     cal.v[:, h:h + 1].astype(np.float64), 4, oc=q64[:, 4 * h:4 * h + 4])
+            heads += 1
+            if time.time() - t0 > 10.0:
+                break
+        dt = (time.time() - t0) / 2  # each call forms the Q and the O target
+        result["cpu_baseline"] = {"value": round(n * 4 * heads / dt, 1), "unit": "pooled rows/s", "cores": cores,
+                                  "kind": "oracle",
+                                  "sample": f"oracle float64 targets of {heads}/{w.n_kv_heads} KV heads "
+                                            f"(numpy BLAS threads = {cores})"}
     print(json.dumps(result), flush=True)
     return 0
 

@@ -117,6 +117,38 @@ oscar_status oscar_build_rotation(int32_t d, int32_t n_kv_heads, int32_t group_q
                                   double* tau_v, double* eig_k, double* eig_v);
 
 /* ------------------------------------------------------------------------ *
+ * Calibration targets on the GPU ([TS] 2.1 and 2.2.A step 1: the key target
+ * is the query second moment Q^T Q / N and the value target V^T S^T S V / N =
+ * O^T O / N with O = S V, each pooled over the query heads of a KV group).
+ * For x the Q rows (or the O rows) of a calibration forward pass:
+ *   out[h] = (1 / (N G)) sum_{n < N} sum_{i = hG}^{hG+G-1} x[n][i]^T x[n][i]
+ * with G = n_x_heads / n_kv_heads (x[n][i] a row vector, so out[h] is d x d).
+ * The Gram products run on the bf16 matrix cores (exact products, float32
+ * sums over blocks of 256 pooled rows, float64 sums of the blocks by atomic
+ * adds, so the last bits may differ from run to run).
+ * x: device bf16 [n_rows][n_x_heads][d], 16-byte aligned.  out: device
+ * float64 [n_kv_heads][d][d], overwritten (zeroed by the call first).
+ * Errors: INVALID_ARG for null pointers, n_rows < 1, n_kv_heads < 1,
+ * n_x_heads not a positive multiple of n_kv_heads or x not 16-byte aligned;
+ * UNSUPPORTED for d not in {64, 128} or more than 2^39 pooled rows. */
+oscar_status oscar_calib_gram(const void* x, int64_t n_rows, int32_t n_x_heads,
+                              int32_t n_kv_heads, int32_t d, double* out, void* stream);
+
+/* oscar_build_rotation's steps 2-4 from given targets (host, float64
+ * [n_kv_heads][d][d], e.g. copied back from oscar_calib_gram): each target is
+ * symmetrised ((C + C^T) / 2), decomposed and composed exactly as there; the
+ * clip thresholds come from k_calib, v_calib (host float32
+ * [n_rows][n_kv_heads][d]).  Outputs and errors as oscar_build_rotation
+ * (NUMERIC also for a non-finite target entry). */
+oscar_status oscar_build_rotation_from_targets(int32_t d, int32_t n_kv_heads,
+                                               const double* c_q, const double* c_s,
+                                               int64_t n_rows, const float* k_calib,
+                                               const float* v_calib, double clip_quantile,
+                                               int32_t max_sweeps, int32_t n_threads,
+                                               double* r_k, double* r_v, double* tau_k,
+                                               double* tau_v, double* eig_k, double* eig_v);
+
+/* ------------------------------------------------------------------------ *
  * Comparison rotations through the same cache path ([TS] 1: Hadamard
  * transforms are the data-oblivious rotations OSCAR improves on; [TS] 4,
  * "Accuracy Preservation": naive INT2 and Hadamard-only are the baselines).

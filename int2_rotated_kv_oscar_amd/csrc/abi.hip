@@ -237,6 +237,20 @@ oscar_status oscar_decode_step_update(const oscar_cache* cache, const void* k_ne
                     "decode_step_update launch");
 }
 
+oscar_status oscar_calib_gram(const void* x, int64_t n_rows, int32_t n_x_heads, int32_t n_kv_heads, int32_t d,
+                              double* out, void* stream) {
+  oscar::clear_error();
+  if (!x || !out) return fail(OSCAR_ERR_INVALID_ARG, "null device pointer");
+  if (!supported_d(d)) return fail(OSCAR_ERR_UNSUPPORTED, "d must be 64 or 128");
+  if (n_rows < 1 || n_kv_heads < 1) return fail(OSCAR_ERR_INVALID_ARG, "n_rows < 1 or n_kv_heads < 1");
+  if (n_x_heads < n_kv_heads || n_x_heads % n_kv_heads) return fail(OSCAR_ERR_INVALID_ARG, "n_x_heads not a multiple of n_kv_heads");
+  if (reinterpret_cast<uintptr_t>(x) % 16) return fail(OSCAR_ERR_INVALID_ARG, "x not 16-byte aligned");
+  const int64_t pooled = n_rows * (n_x_heads / n_kv_heads);
+  if (pooled / 256 >= int64_t(0x7FFFFFFF) || n_rows > (int64_t(1) << 40)) return fail(OSCAR_ERR_UNSUPPORTED, "too many rows");
+  return hip_status(oscar_launch::calib_gram(d, x, n_rows, n_x_heads, n_kv_heads, out, static_cast<hipStream_t>(stream)),
+                    "calib_gram launch");
+}
+
 oscar_status oscar_decode_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads, int32_t d,
                                           int32_t max_seq_len, int32_t split_pages, size_t* bytes) {
   oscar::clear_error();

@@ -19,6 +19,10 @@ hipError_t decode_step_update(int d, int n_kv, int n_sink, int n_recent, void* i
                               const int32_t* bt_q, const int32_t* bt_h, int32_t max_pages, const float* r_k,
                               const float* r_v, float tau_k, float tau_v, hipStream_t stream);
 
+// calibration second moments C(h) = (1 / (N G)) sum x^T x over the G heads of
+// each KV group (float64 out, zeroed first)
+hipError_t calib_gram(int d, const void* x, int64_t n_rows, int n_x_heads, int n_kv, void* out, hipStream_t stream);
+
 size_t decode_lds_bytes(int d, int G, bool all_raw);
 int decode_max_records();  // record slots per (sequence, KV head) the merge can hold
 int decode_min_slice();    // pages per workgroup slice at least

@@ -205,6 +205,17 @@ double linear_quantile(std::vector<double>& a, double qq) {
   return alo + (rr - double(lo)) * (ahi - alo);
 }
 
+// [TS] 2.2.A steps 2-3 for one target: eigenbasis (descending, canonical
+// signs) and R = U . H . P_br; false if the eigensolver did not converge.
+bool rotation_from_target(int d, std::vector<double>& c, int max_sweeps, double* r, double* eig, int h) {
+  std::vector<double> w, u;
+  const bool ok = jacobi_eigen(c, d, max_sweeps, w, u);
+  sort_and_sign(d, w, u);
+  compose_rotation(d, u, r);
+  if (eig) std::memcpy(eig + size_t(h) * d, w.data(), sizeof(double) * d);
+  return ok;
+}
+
 // Per-layer clip thresholds ([TS] 2.2.A step 4): the quantile of |x R|
 // pooled over rows, heads and channels, for K (which 0) and V (which 1).
 void clip_thresholds(int d, int n_kv_heads, size_t N, const std::vector<double>& k, const std::vector<double>& v,
@@ -303,12 +314,8 @@ extern "C" oscar_status oscar_build_rotation(int32_t d, int32_t n_kv_heads, int3
       }
     const double norm = 1.0 / (double(N) * group_q);
     for (double& x : c) x *= norm;
-    std::vector<double> w, u;
-    if (!jacobi_eigen(c, d, max_sweeps, w, u)) ok[h] = 0;
-    sort_and_sign(d, w, u);
-    compose_rotation(d, u, (value ? r_v : r_k) + size_t(h) * d * d);
-    double* e = value ? eig_v : eig_k;
-    if (e) std::memcpy(e + size_t(h) * d, w.data(), sizeof(double) * d);
+    if (!rotation_from_target(d, c, max_sweeps, (value ? r_v : r_k) + size_t(h) * d * d,
+                              value ? eig_v : eig_k, h)) ok[h] = 0;
   });
   for (int h = 0; h < n_kv_heads; ++h)
     if (!ok[h]) return fail(OSCAR_ERR_NUMERIC, "Jacobi eigensolver did not converge");
@@ -348,6 +355,49 @@ extern "C" oscar_status oscar_build_fixed_rotation(int32_t variant, int32_t d, i
     std::memcpy(r_k + size_t(h) * d * d, r.data(), sizeof(double) * d * d);
     std::memcpy(r_v + size_t(h) * d * d, r.data(), sizeof(double) * d * d);
   }
+  std::vector<double> k(k_calib, k_calib + nkv), v(v_calib, v_calib + nkv);
+  clip_thresholds(d, n_kv_heads, N, k, v, r_k, r_v, clip_quantile, n_threads, tau_k, tau_v);
+  return OSCAR_OK;
+}
+
+extern "C" oscar_status oscar_build_rotation_from_targets(int32_t d, int32_t n_kv_heads, const double* c_q,
+                                                          const double* c_s, int64_t n_rows, const float* k_calib,
+                                                          const float* v_calib, double clip_quantile,
+                                                          int32_t max_sweeps, int32_t n_threads, double* r_k,
+                                                          double* r_v, double* tau_k, double* tau_v, double* eig_k,
+                                                          double* eig_v) {
+  using oscar::fail;
+  oscar::clear_error();
+  if (!c_q || !c_s || !k_calib || !v_calib || !r_k || !r_v || !tau_k || !tau_v)
+    return fail(OSCAR_ERR_INVALID_ARG, "null required pointer");
+  if (n_rows < 2 || n_kv_heads < 1) return fail(OSCAR_ERR_INVALID_ARG, "n_rows < 2 or n_kv_heads < 1");
+  if (!(clip_quantile > 0.0 && clip_quantile <= 1.0))
+    return fail(OSCAR_ERR_INVALID_ARG, "clip_quantile outside (0, 1]");
+  if (d != 64 && d != 128) return fail(OSCAR_ERR_UNSUPPORTED, "d must be 64 or 128");
+  if (max_sweeps < 0) return fail(OSCAR_ERR_INVALID_ARG, "max_sweeps < 0");
+  if (max_sweeps == 0) max_sweeps = 64;
+  if (n_threads <= 0) n_threads = int(std::max(1u, std::thread::hardware_concurrency()));
+  const size_t N = size_t(n_rows), nkv = N * n_kv_heads * d, nc = size_t(n_kv_heads) * d * d;
+  for (size_t i = 0; i < nc; ++i)
+    if (!std::isfinite(c_q[i]) || !std::isfinite(c_s[i])) return fail(OSCAR_ERR_NUMERIC, "non-finite target value");
+  for (size_t i = 0; i < nkv; ++i)
+    if (!std::isfinite(k_calib[i]) || !std::isfinite(v_calib[i]))
+      return fail(OSCAR_ERR_NUMERIC, "non-finite calibration value");
+  std::vector<int> ok(n_kv_heads, 1);
+  run_parallel(n_threads, 2 * n_kv_heads, [&](int t, int) {
+    const int h = t / 2;
+    const bool value = t % 2;
+    const double* src = (value ? c_s : c_q) + size_t(h) * d * d;
+    // symmetric part (targets accumulated on the GPU may differ from
+    // symmetry by rounding)
+    std::vector<double> c(size_t(d) * d);
+    for (int a = 0; a < d; ++a)
+      for (int b = 0; b < d; ++b) c[size_t(a) * d + b] = 0.5 * (src[size_t(a) * d + b] + src[size_t(b) * d + a]);
+    if (!rotation_from_target(d, c, max_sweeps, (value ? r_v : r_k) + size_t(h) * d * d, value ? eig_v : eig_k, h))
+      ok[h] = 0;
+  });
+  for (int h = 0; h < n_kv_heads; ++h)
+    if (!ok[h]) return fail(OSCAR_ERR_NUMERIC, "Jacobi eigensolver did not converge");
   std::vector<double> k(k_calib, k_calib + nkv), v(v_calib, v_calib + nkv);
   clip_thresholds(d, n_kv_heads, N, k, v, r_k, r_v, clip_quantile, n_threads, tau_k, tau_v);
   return OSCAR_OK;

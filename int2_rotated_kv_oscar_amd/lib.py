@@ -25,7 +25,8 @@ STATUS_NAMES = {0: "OSCAR_OK", 1: "OSCAR_ERR_INVALID_ARG", 2: "OSCAR_ERR_UNSUPPO
 EXPORTS = [
     "oscar_status_string", "oscar_last_error", "oscar_version", "oscar_build_rotation",
     "oscar_build_fixed_rotation", "oscar_int2_page_bytes", "oscar_bf16_page_bytes", "oscar_quantize_append",
-    "oscar_write_bf16", "oscar_decode_step_update", "oscar_decode_workspace_bytes", "oscar_decode_workspace_init", "oscar_paged_decode_attn",
+    "oscar_write_bf16", "oscar_decode_step_update", "oscar_decode_workspace_bytes", "oscar_calib_gram",
+    "oscar_build_rotation_from_targets", "oscar_decode_workspace_init", "oscar_paged_decode_attn",
     "oscar_paged_decode_attn_bf16",
 ]
 
@@ -68,6 +69,9 @@ def load(path: str = LIB_PATH):
         "oscar_build_rotation": (_STATUS, [_I32, _I32, _I32, _I64, _P, _P, _P, _P, _F64, _I32, _I32,
                                            _P, _P, _P, _P, _P, _P]),
         "oscar_build_fixed_rotation": (_STATUS, [_I32, _I32, _I32, _I64, _P, _P, _F64, _I32, _P, _P, _P, _P]),
+        "oscar_calib_gram": (_STATUS, [_P, _I64, _I32, _I32, _I32, _P, _P]),
+        "oscar_build_rotation_from_targets": (_STATUS, [_I32, _I32, _P, _P, _I64, _P, _P, _F64, _I32, _I32,
+                                                        _P, _P, _P, _P, _P, _P]),
         "oscar_int2_page_bytes": (_SZ, [_I32, _I32]),
         "oscar_bf16_page_bytes": (_SZ, [_I32, _I32]),
         "oscar_quantize_append": (_STATUS, [ctypes.POINTER(OscarCache), _P, _P, _I64, _P, _P, _P, _I32, _P, _P,
@@ -127,6 +131,23 @@ def build_rotation(q_calib, k_calib, v_calib, group_q: int, clip_quantile: float
     _check(load().oscar_build_rotation(d, hkv, group_q, n, ptr(q), ptr(k), ptr(v), ptr(o), clip_quantile,
                                        max_sweeps, n_threads, ptr(rk), ptr(rv), ctypes.byref(tk),
                                        ctypes.byref(tv), ptr(ek), ptr(ev)))
+    return dict(r_k=rk, r_v=rv, tau_k=tk.value, tau_v=tv.value, eig_k=ek, eig_v=ev)
+
+
+def build_rotation_from_targets(c_q, c_s, k_calib, v_calib, clip_quantile: float = 0.999, max_sweeps: int = 0,
+                                n_threads: int = 0) -> dict:
+    """Steps 2-4 of the calibration from given targets (oscar_build_rotation_from_targets).
+    c_q, c_s float64 [H_kv, d, d]; k_calib, v_calib [N, H_kv, d]."""
+    cq = np.ascontiguousarray(c_q, dtype=np.float64); cs = np.ascontiguousarray(c_s, dtype=np.float64)
+    k = _host_f32(k_calib); v = _host_f32(v_calib)
+    n, hkv, d = k.shape
+    rk = np.zeros((hkv, d, d)); rv = np.zeros((hkv, d, d))
+    ek = np.zeros((hkv, d)); ev = np.zeros((hkv, d))
+    tk = ctypes.c_double(); tv = ctypes.c_double()
+    ptr = lambda a: a.ctypes.data_as(_P)  # noqa: E731
+    _check(load().oscar_build_rotation_from_targets(d, hkv, ptr(cq), ptr(cs), n, ptr(k), ptr(v), clip_quantile,
+                                                    max_sweeps, n_threads, ptr(rk), ptr(rv), ctypes.byref(tk),
+                                                    ctypes.byref(tv), ptr(ek), ptr(ev)))
     return dict(r_k=rk, r_v=rv, tau_k=tk.value, tau_v=tv.value, eig_k=ek, eig_v=ev)
 
 
@@ -199,6 +220,16 @@ def decode_step_update(cache: OscarCache, k_new, v_new, seq_lens, bt_q, bt_h, r_
     _check(load().oscar_decode_step_update(ctypes.byref(cache), _dptr(k_new), _dptr(v_new), b, _dptr(seq_lens),
                                            _dptr(bt_q), _dptr(bt_h), bt_q.shape[1], _dptr(r_k), _dptr(r_v),
                                            float(tau_k), float(tau_v), _stream(stream)))
+
+
+def calib_gram(x, n_kv_heads: int, out=None, stream=None):
+    """x device bf16 [N, H_x, d] -> device float64 [H_kv, d, d] (oscar_calib_gram)."""
+    import torch
+    n, hx, d = x.shape
+    if out is None:
+        out = torch.empty((n_kv_heads, d, d), dtype=torch.float64, device=x.device)
+    _check(load().oscar_calib_gram(_dptr(x), n, hx, n_kv_heads, d, _dptr(out), _stream(stream)))
+    return out
 
 
 def decode_workspace_bytes(batch: int, n_kv_heads: int, n_q_heads: int, d: int, max_seq_len: int,

@@ -83,6 +83,13 @@ def test_device_calls_validate_before_launch():
     assert L.oscar_decode_step_update(ctypes.byref(c2), 16, 16, -1, 16, 16, 16, 1, 16, 16, 1.0, 1.0, None) == 1
     assert L.oscar_decode_step_update(ctypes.byref(c2), 16, 16, 1, 16, None, 16, 1, 16, 16, 1.0, 1.0, None) == 1
     assert L.oscar_decode_step_update(ctypes.byref(c2), 16, 16, 1, 16, 16, 16, 1, 16, 16, 0.0, 1.0, None) == 1
+    # calibration Gram: validated before any launch
+    assert L.oscar_calib_gram(None, 8, 4, 1, 128, 16, None) == 1
+    assert L.oscar_calib_gram(16, 8, 4, 1, 96, 16, None) == 2
+    assert L.oscar_calib_gram(16, 8, 6, 4, 128, 16, None) == 1     # 6 heads over 4 KV heads
+    assert L.oscar_calib_gram(24, 8, 4, 1, 128, 16, None) == 1     # not 16-byte aligned
+    assert b"aligned" in L.oscar_last_error()
+    assert L.oscar_calib_gram(16, 0, 4, 1, 128, 16, None) == 1
     assert L.oscar_decode_workspace_init(None, 64, None) == 4
 
 

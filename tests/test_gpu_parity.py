@@ -12,6 +12,7 @@ import torch
 from int2_rotated_kv_oscar_amd import lib, synth
 from oracle import cache as ocache
 from oracle import layout as olayout
+from oracle import rotation as orot
 
 import gpu_helpers as gh
 
@@ -239,6 +240,37 @@ def test_decode_step_update(d, hkv, S, W):
             pc.write(page, slot, h, zc, zc, zs, zs, zs, zs)
         cleared.append(pc.data)
     assert np.array_equal(cleared[0], cleared[1]), "INT2 bytes outside the quantized rows changed"
+
+
+@pytest.mark.parametrize("d,hq,hkv,n", [(128, 32, 8, 1000), (64, 4, 1, 2048), (128, 12, 1, 77)])
+def test_calib_gram_matches_oracle_targets(d, hq, hkv, n):
+    # GPU calibration targets (Q^T Q and O^T O over N G pooled rows) against
+    # the oracle's on the same bf16 rows, within the float32 accumulation bound
+    # of 256-row blocks (|err| <= 256 2^-24 sum|x_a||x_b| / (N G)); then the
+    # rotation built from them, whose eigenvalues move by at most ||dC|| (Weyl)
+    w = synth.Workload("calib", 6, 1, hq, hkv, d, 4, 32, n, ("fixed", 64, 64))
+    cal = synth.calibration_set(w, n_rows=n)
+    o = synth.bf16_bits_to_f32(synth.to_bf16_bits(np.random.default_rng(n).standard_normal(cal.q.shape) * 0.7))
+    G = hq // hkv
+    cq, cs = orot.calibration_targets(cal.q.astype(np.float64), cal.k.astype(np.float64), cal.v.astype(np.float64), G,
+                                      oc=o.astype(np.float64))
+    print(f"[calib gram d={d} hq={hq} hkv={hkv} n={n}]", flush=True)
+    gq = lib.calib_gram(gh.bits_to_dev_bf16(synth.to_bf16_bits(cal.q)), hkv)
+    go = lib.calib_gram(gh.bits_to_dev_bf16(synth.to_bf16_bits(o)), hkv)
+    torch.cuda.synchronize()
+    gq, go = gq.cpu().numpy(), go.cpu().numpy()
+    for got, ref, x in ((gq, cq, cal.q), (go, cs, o)):
+        ax = np.abs(x.astype(np.float64))
+        for h in range(hkv):
+            xa = ax[:, h * G:(h + 1) * G, :].reshape(-1, d)
+            bound = 2.0 ** -16 * (xa.T @ xa) / xa.shape[0] + 1e-300
+            err = np.abs(got[h] - ref[h])
+            assert (err <= bound).all(), f"max err/bound {(err / bound).max():.3g}"
+    rg = lib.build_rotation_from_targets(gq, go, cal.k, cal.v)
+    ro = lib.build_rotation_from_targets(cq, cs, cal.k, cal.v)
+    for key, dc in (("eig_k", gq - cq), ("eig_v", go - cs)):
+        for h in range(hkv):
+            assert np.abs(rg[key][h] - ro[key][h]).max() <= np.linalg.norm(dc[h]) + 1e-12
 
 
 def test_decode_on_oracle_pages_tiny(tiny_rot):

@@ -77,3 +77,30 @@ def test_fixed_rotation_validation():
     with pytest.raises(lib.OscarError) as e:
         lib.build_fixed_rotation(lib.ROTATION_HADAMARD, bad, k)
     assert e.value.status == 3
+
+
+def test_rotation_from_targets_matches_build_rotation():
+    # steps 2-4 from the oracle's targets reproduce the full host calibration
+    w = synth.WORKLOADS["tiny"]
+    cal = synth.calibration_set(w, n_rows=600)
+    o = np.random.default_rng(2).standard_normal(cal.q.shape).astype(np.float32)
+    full = lib.build_rotation(cal.q, cal.k, cal.v, w.group_q, o_calib=o)
+    cq, cs = orot.calibration_targets(np.asarray(cal.q, np.float32).astype(np.float64),
+                                      np.asarray(cal.k, np.float32).astype(np.float64),
+                                      np.asarray(cal.v, np.float32).astype(np.float64), w.group_q,
+                                      oc=o.astype(np.float64))
+    got = lib.build_rotation_from_targets(cq, cs, cal.k, cal.v, n_threads=2)
+    for key in ("eig_k", "eig_v"):
+        np.testing.assert_allclose(got[key], full[key], rtol=0, atol=1e-10 * np.abs(full[key]).max())
+    for key in ("r_k", "r_v"):
+        assert np.abs(got[key] - full[key]).max() <= 1e-6
+    assert got["tau_k"] == pytest.approx(full["tau_k"], rel=1e-9)
+    assert got["tau_v"] == pytest.approx(full["tau_v"], rel=1e-9)
+    # the symmetric part is what counts
+    skew = np.random.default_rng(3).standard_normal(cq.shape) * 1e-3
+    got2 = lib.build_rotation_from_targets(cq + skew - skew.transpose(0, 2, 1), cs, cal.k, cal.v)
+    np.testing.assert_allclose(got2["eig_k"], got["eig_k"], rtol=0, atol=1e-10 * np.abs(got["eig_k"]).max())
+    bad = cq.copy(); bad[0, 1, 2] = np.nan
+    with pytest.raises(lib.OscarError) as e:
+        lib.build_rotation_from_targets(bad, cs, cal.k, cal.v)
+    assert e.value.status == 3
