@@ -57,6 +57,28 @@ def _run(name, sample_seqs, n_code_rows=2048, seed=0):
     print(rep, flush=True)
     gh.assert_codes_ok(rep, name)
 
+    # the bench step's append: every sequence's row leaving the recent window,
+    # appended again (the few-row kernel for these counts), checked on the
+    # sampled sequences
+    lv = [(b, int(L) - 1 - w.n_recent) for b, L in enumerate(lens) if int(L) - 1 - w.n_recent >= w.n_sink]
+    if lv:
+        ls = np.array([b for b, _ in lv]); lp = np.array([t for _, t in lv])
+        lr = np.array([inp.row_of[b][t] for b, t in lv])
+        print(f"[fullsize {name}] leaving-row append rows={len(lv)}", flush=True)
+        from int2_rotated_kv_oscar_amd import lib
+        lib.quantize_append(gc.cache, gh.bits_to_dev_bf16(inp.k_rows[lr]), gh.bits_to_dev_bf16(inp.v_rows[lr]),
+                            gh.i32(ls), gh.i32(lp), gc.bt_q, gc.r_k, gc.r_v, rot.tau_k, rot.tau_v)
+        torch.cuda.synchronize()
+        chk = np.nonzero(np.isin(ls, sample_seqs))[0]
+        res2 = ocache.quantize_append(olayout.Int2Pool(inp.n_int2_pages, w.n_kv_heads, w.d), inp.k_rows[lr[chk]],
+                                      inp.v_rows[lr[chk]], ls[chk], lp[chk], inp.bt_q, rot.r_k, rot.r_v, rot.tau_k,
+                                      rot.tau_v, olayout.bf16_to_f64)
+        int2_bytes = gc.int2.cpu().numpy()
+        rep2 = gh.compare_appended(int2_bytes, w, inp.n_int2_pages, res2, inp.bt_q[ls[chk], lp[chk] // 16].astype(np.int64),
+                                   (lp[chk] % 16).astype(np.int64))
+        print(rep2, flush=True)
+        gh.assert_codes_ok(rep2, name + " leaving rows")
+
     # decode (all sequences on the GPU), checked on the sampled ones
     print(f"[fullsize {name}] decode", flush=True)
     got = gh.gpu_decode(inp, gc, split_pages=0)
