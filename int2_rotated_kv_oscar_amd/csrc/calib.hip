@@ -20,7 +20,7 @@ using namespace oscar_dev;
 
 namespace {
 
-constexpr int kGramRows = 2048;  // pooled rows per workgroup
+constexpr int kGramRows = 1024;  // pooled rows per workgroup
 constexpr int kGramBlock = 256;  // rows per float32 block (then added into float64 registers)
 constexpr int kGramStage = 128;  // rows staged in LDS per barrier pair
 constexpr int kGramThreads = 512;
@@ -34,21 +34,26 @@ struct GramParams {
   double scale;        // 1 / (N G)
 };
 
-// Workgroup (chunk of 2048 pooled rows r = n G + j, KV head h).  Wave w owns
+// Workgroup (chunk of 1024 pooled rows r = n G + j, KV head h).  Wave w owns
 // the output rows 16 w .. 16 w + 15 (D = 128: all eight waves; D = 64: waves
-// 0-3) against every column block.  Rows are staged transposed in LDS
-// (channel-major, 128 rows + 8 padding per channel), so both MFMA operands
-// are 16-byte reads: A[i][k] = x[row k][16 ti + i], B[k][j] = x[row k][16 tj + j].
+// 0-3) against every column block.  Rows are loaded coalesced (16 lanes per
+// 256-byte row) and staged transposed in LDS (channel-major), so both MFMA
+// operands are 16-byte reads: A[i][k] = x[row k][16 ti + i], B[k][j] =
+// x[row k][16 tj + j].  Row r of channel ch sits at position r ^ swz(ch),
+// swz(ch) = 8 ((ch ^ (ch >> 3)) mod 16): a bijection over the 16 channels one
+// write instruction touches (8 c + e, c = 0..15) and over the 16 one operand
+// read touches (16 t + i, i = 0..15), so the 2-byte writes and the 16-byte
+// reads fall in distinct banks, and every aligned 8-row group stays contiguous.
 // Each block of 256 rows is summed in float32 (exact products) and then
 // added into float64 registers; the workgroup's float64 partial, scaled by
 // 1 / (N G), goes to the result with float64 atomic adds.
 template <int D>
 __global__ __launch_bounds__(kGramThreads) void calib_gram_kernel(GramParams p) {
   constexpr int NB = D / 16;             // channel blocks
-  constexpr int kPad = kGramStage + 8;   // LDS row of one channel (bf16)
-  __shared__ __attribute__((aligned(16))) uint16_t s_xt[D][kPad];
+  __shared__ __attribute__((aligned(16))) uint16_t s_xt[D][kGramStage];
+  auto swz = [](int ch) { return 8 * ((ch ^ (ch >> 3)) & 15); };
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, quad = lane >> 4;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: tile choices are scalar branches
   const int h = blockIdx.y;
   const int64_t pooled = p.n_rows * p.group;
   const int64_t r0 = int64_t(blockIdx.x) * kGramRows;
@@ -59,24 +64,35 @@ __global__ __launch_bounds__(kGramThreads) void calib_gram_kernel(GramParams p) 
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc64[j][r] = 0.0;
   f32x4 acc[NB];
-  // staging: lane l of wave w loads the 16-byte channel chunks w + 8 c of
-  // rows l and l + 64 of the stage, so that a wave's transposed 2-byte LDS
-  // writes cover 64 consecutive rows of one channel (no bank conflicts)
-  constexpr int kCsel = D / 64;              // chunks per lane and row: 2 (D = 128) or 1 (D = 64)
-  constexpr int kLoads = 2 * kCsel;          // rows l, l + 64
+  // staging: load i of lane l in wave w is the 16-byte channel chunk l % NC of
+  // stage row 16 w + (64 / NC) i + l / NC (NC = D / 8 chunks per row)
+  constexpr int NC = D / 8;
+  constexpr int kLoads = kGramStage * NC / kGramThreads;  // 4 (D = 128) or 2 (D = 64)
   static_assert(kGramStage == 128 && kGramBlock % (2 * kGramStage) == 0 && kGramThreads == 512, "staging map");
+  auto srow = [&](int i) { return 16 * wave + (64 / NC) * i + lane / NC; };
+  const int c8 = 8 * (lane % NC);
   // the rows of stage `st` (kGramStage rows from r0 + st kGramStage) into v;
-  // rows past the end read as zeros
+  // rows past the end read as zeros.  Pooled row r = n G + j sits at element
+  // (n H_x + h G + j) D: one scalar division per stage gives the stage's
+  // first (n, j), and a lane's offset t = j0 + row (< 128 + 16) splits as
+  // t = q G + j with q = floor((t + 1/2) / G) from a float reciprocal (exact:
+  // (t + 1/2) / G is at least 1/32 away from an integer for G <= 16)
+  const float inv_g = 1.0f / float(p.group);
+  const uint16_t* xh = p.x + int64_t(h) * p.group * D;
   auto load_stage = [&](u32x4 (&v)[kLoads], int st) {
+    const int64_t rb = r0 + int64_t(st) * kGramStage;
+    const int64_t nb = rb / p.group;
+    const int j0 = int(rb - nb * p.group);
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int rr = lane + 64 * (i / kCsel), c8 = 8 * (wave + 8 * (i % kCsel));
-      const int64_t r = r0 + int64_t(st) * kGramStage + rr;
-      v[i] = u32x4{0u, 0u, 0u, 0u};
-      if (r < pooled) {
-        const int64_t n = r / p.group, j = r - n * p.group;
-        v[i] = *reinterpret_cast<const u32x4*>(p.x + (n * p.n_x_heads + int64_t(h) * p.group + j) * D + c8);
-      }
+      const int rr = srow(i);
+      const int t = j0 + rr;
+      const int q = int((float(t) + 0.5f) * inv_g);
+      const int j = t - q * p.group;
+      const bool live = rb + rr < pooled;
+      const int64_t n = live ? nb + q : 0;  // rows past the end read row 0 (and are zeroed)
+      const u32x4 w = *reinterpret_cast<const u32x4*>(xh + (n * p.n_x_heads + (live ? j : 0)) * D + c8);
+      v[i] = live ? w : u32x4{0u, 0u, 0u, 0u};
     }
   };
   // stages past the end of the rows are skipped (a uniform decision); stages
@@ -93,11 +109,11 @@ __global__ __launch_bounds__(kGramThreads) void calib_gram_kernel(GramParams p) 
     __syncthreads();  // the previous stage's operand reads are done
 #pragma unroll
     for (int i = 0; i < kLoads; ++i) {
-      const int rr = lane + 64 * (i / kCsel), c8 = 8 * (wave + 8 * (i % kCsel));
+      const int rr = srow(i);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        s_xt[c8 + 2 * e][rr] = uint16_t(v[i][e] & 0xFFFFu);
-        s_xt[c8 + 2 * e + 1][rr] = uint16_t(v[i][e] >> 16);
+        s_xt[c8 + 2 * e][rr ^ swz(c8 + 2 * e)] = uint16_t(v[i][e] & 0xFFFFu);
+        s_xt[c8 + 2 * e + 1][rr ^ swz(c8 + 2 * e + 1)] = uint16_t(v[i][e] >> 16);
       }
     }
     __syncthreads();
@@ -107,11 +123,13 @@ __global__ __launch_bounds__(kGramThreads) void calib_gram_kernel(GramParams p) 
     if (ti < NB) {
 #pragma unroll
       for (int k0 = 0; k0 < kGramStage; k0 += 32) {
-        const u32x4 a = *reinterpret_cast<const u32x4*>(&s_xt[16 * ti + l16][k0 + 8 * quad]);
+        const int ca = 16 * ti + l16;
+        const u32x4 a = *reinterpret_cast<const u32x4*>(&s_xt[ca][(k0 + 8 * quad) ^ swz(ca)]);
 #pragma unroll
         for (int tj = 0; tj < NB; ++tj) {
           if (tj < ti) continue;
-          const u32x4 b = *reinterpret_cast<const u32x4*>(&s_xt[16 * tj + l16][k0 + 8 * quad]);
+          const int cb = 16 * tj + l16;
+          const u32x4 b = *reinterpret_cast<const u32x4*>(&s_xt[cb][(k0 + 8 * quad) ^ swz(cb)]);
           acc[tj] = mfma_bf16(a, b, acc[tj]);
         }
       }
