@@ -309,7 +309,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   auto int2_requests = [&]() {
     tab_blk = 0;
     tab = clamp_page(*tab_entry(0));
-    tab_dma(1);
     {  // every wave loads (waves past NCB repeat a block) so that no path leaves them unset
       const float* rk = p.r_k + size_t(h) * D * D;
 #pragma unroll
@@ -319,21 +318,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) bqv[kb] = *reinterpret_cast<const u32x4*>(qb + size_t(qcol) * D + 32 * kb + 8 * quad);
     }
-    // The rotation operands are waited for here, before the page requests:
-    // the compiler does not count loads that land in LDS, so a wait for them
-    // placed after the page requests would drain those too, and the rotation
-    // would no longer overlap the page latency.
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      asm volatile("" ::"v"(bqv[kb]));
-#pragma unroll
-      for (int i = 0; i < 8; ++i) asm volatile("" ::"v"(rvals[kb][i]));
-    }
+    // The page requests go out as soon as the page ids are in, behind the
+    // rotation operands (older requests: the compiler may not move loads
+    // across this point), so that the rotation later waits with
+    // vmcnt(kDepth LOADS + 1) for exactly those operands while the pages and
+    // the page-id block stay in flight.
+    asm volatile("" ::: "memory");
     // page loads are issued unconditionally (a wave short of pairs loads
     // unused pages) so that every wait counts exactly the loads issued after
     // the pair it waits for
 #pragma unroll
     for (int u = 0; u < kDepth; ++u) pair_dma(u, ring + u * PD::SLOT);
+    tab_dma(1);
   };
 
   // ---- work layout ----
@@ -511,6 +507,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     // wave w rotates the 16-channel block cb = w (group w/2, half w%2) with a
     // bf16 hi/lo split of R_K (16 significant bits; q~ is rounded to f16 afterwards)
     float* s_qsp = s_misc + 272;  // [NCB][16] per-block query sums
+    wait_vm<kDepth * PD::LOADS + 1>();  // the rotation operands (older than the page-id block and pages)
     if (rot_wave) {
       const int g = wave >> 1, hb = wave & 1;
       f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
