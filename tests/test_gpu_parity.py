@@ -357,6 +357,27 @@ def test_comparison_rotations_end_to_end(variant, hq, hkv, d):
     gh.assert_attention_close(got, ref, "comparison rotation")
 
 
+@pytest.mark.parametrize("S,W", [(0, 0), (0, 16), (4, 0), (16, 48), (32, 0)])
+def test_decode_region_layouts(S, W):
+    # degenerate region layouts: no sink, no recent window, neither, a wide
+    # sink; ragged lengths around page edges; automatic and fixed splits
+    lens = np.array([1, 15, 16, 17, 33, 64, 65, 700, 333])
+    w = synth.Workload("regions", 6, len(lens), 8, 2, 128, S, W, 512, ("fixed", 700, 700))
+    rot = gh.oracle_rotation(w, n_rows=512)
+    inp = synth.decode_inputs(w, seq_lens=lens)
+    gc = gh.alloc_cache(inp, rot)
+    gh.gpu_fill(inp, rot, gc)
+    int2, bf, res, rows = gh.oracle_pools(inp, rot)
+    page, slot = _page_slot(inp, rows)
+    gh.assert_codes_ok(gh.compare_appended(gc.int2.cpu().numpy(), w, inp.n_int2_pages, res, page, slot))
+    ref = gh.oracle_decode(inp, rot, int2, bf)
+    for split in (0, 8):
+        print(f"[decode regions S={S} W={W} split={split}]", flush=True)
+        got = gh.gpu_decode(inp, gc, split_pages=split)
+        print(gh.attention_errors(got, ref))
+        gh.assert_attention_close(got, ref, f"regions S={S} W={W} split={split}")
+
+
 def test_invariances_tables_splits_determinism(tiny_rot):
     w = _tiny(batch=2)
     lens = np.array([512, 400])
