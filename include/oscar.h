@@ -127,7 +127,9 @@ oscar_status oscar_build_rotation(int32_t d, int32_t n_kv_heads, int32_t group_q
  * sums over blocks of 256 pooled rows, float64 sums of the blocks by atomic
  * adds, so the last bits may differ from run to run).
  * x: device bf16 [n_rows][n_x_heads][d], 16-byte aligned.  out: device
- * float64 [n_kv_heads][d][d], overwritten (zeroed by the call first).
+ * float64 [n_kv_heads][d][d], overwritten (the call zeroes it, accumulates
+ * into it with atomic adds, then fills the lower triangle; three launches on
+ * the stream), not overlapping x.
  * Errors: INVALID_ARG for null pointers, n_rows < 1, n_kv_heads < 1,
  * n_x_heads not a positive multiple of n_kv_heads or x not 16-byte aligned;
  * UNSUPPORTED for d not in {64, 128} or more than 2^39 pooled rows. */
