@@ -124,7 +124,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the decode path shards by KV head "
-              f"with no exchange; see DESIGN.md)", file=sys.stderr)
+              f"with no exchange between GPUs)", file=sys.stderr)
         return 2
 
     import torch
