@@ -308,6 +308,27 @@ def main() -> int:
                               "update_us_per_call": round(upd_ms * 1e3, 2)}
     log(f"serving step (update + decode) {serve_ms * 1e3:.1f} us, update alone {upd_ms * 1e3:.1f} us")
 
+    # attainable streaming bandwidth, as context for the roofline fraction: a
+    # vectorized elementwise kernel (read + write) over 1 GiB, several times the
+    # Infinity Cache (torch's reductions stream slower, about 3.9 TB/s)
+    pa = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    pb = torch.empty_like(pa)
+    for _ in range(3):
+        torch.mul(pa, 2.0, out=pb)
+    torch.cuda.synchronize()
+    p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    p0.record()
+    for _ in range(20):
+        torch.mul(pa, 2.0, out=pb)
+    p1.record()
+    torch.cuda.synchronize()
+    probe = 2 * pa.numel() * 4 / (p0.elapsed_time(p1) / 20 * 1e-3) / 1e9
+    del pa, pb
+    result["bw_probe"] = {"stream_GBps": round(probe, 1),
+                          "method": "torch.mul over a 1 GiB float32 buffer, read + write bytes",
+                          "decode_frac_of_probe": round(achieved / probe, 4)}
+    log(f"bw probe {probe:.0f} GB/s streamed; decode at {achieved / probe:.1%} of it")
+
     if not args.no_bf16_baseline:
         # the same decode over an all-BF16 cache (every token in BF16 pages)
         wb = synth.Workload(**{**w.__dict__, "n_sink": 1 << 30, "n_recent": 0})
