@@ -471,16 +471,25 @@ __global__ __launch_bounds__(kRowThreads) void quantize_rows_kernel(QAParams p) 
   __shared__ uint16_t s_x[kRowsPerWg][D];
   __shared__ uint8_t s_code[kRowsPerWg][64];
   __shared__ int32_t s_page[kRowsPerWg], s_slot[kRowsPerWg];  // INT2 destination (-1: none)
+  __shared__ int32_t s_valid[kRowsPerWg];                      // the row is quantized and stored
   __shared__ int32_t s_src[kRowsPerWg];                        // STEP: BF16 page of the row (-1: k_new/v_new)
   __shared__ int32_t s_new[kRowsPerWg], s_newslot[kRowsPerWg];  // STEP: BF16 slot of the new token (-1: none)
+  __shared__ uint16_t s_sz[kRowsPerWg][2][2];                  // f16 scale, zero per (row, group of the pair)
 
-  // row metadata first (the page ids need a second round trip)
-  if (tid < nr) {
-    if (!STEP) {
-      const int32_t seq = p.row_seq[row0 + tid], pos = p.row_pos[row0 + tid];
-      s_page[tid] = p.bt_q[int64_t(seq) * p.max_pages + (pos >> 4)];
-      s_slot[tid] = pos & 15;
-    } else {
+  // Row metadata.  The INT2 page id (a dependent load from the block table)
+  // is needed only by the stores: it stays in a register of thread `tid`
+  // and goes to LDS just before them, so its round trip overlaps the
+  // products, statistics and codes (the barriers below order LDS only).
+  int32_t my_page = -1, my_slot = 0;
+  if (!STEP) {
+    // every thread loads (threads past the chunk: its last row), so that the
+    // compiler's wait counts are the same on every path
+    const int rq = min(tid, nr - 1);
+    my_page = p.row_seq[row0 + rq];  // the sequence, until the page id is looked up below
+    my_slot = p.row_pos[row0 + rq];  // the position, likewise
+    if (tid < nr) s_valid[tid] = 1;
+  } else if (tid < nr) {
+    {
       const int64_t b = row0 + tid;
       const int32_t L = p.seq_lens[b];
       int32_t t = -1, src = -1, nw = -1;
@@ -490,30 +499,34 @@ __global__ __launch_bounds__(kRowThreads) void quantize_rows_kernel(QAParams p) 
         if (t < p.n_sink) t = -1;
         else if (p.n_recent >= 1) src = p.bt_h[b * p.max_pages + (t >> 4)];
       }
-      s_page[tid] = t >= 0 ? p.bt_q[b * p.max_pages + (t >> 4)] : -1;
-      s_slot[tid] = t & 15;
+      if (t >= 0) my_page = p.bt_q[b * p.max_pages + (t >> 4)];
+      my_slot = t & 15;
+      s_valid[tid] = t >= 0 ? 1 : 0;
+      s_slot[tid] = my_slot;  // the BF16 gather reads the same slot
       s_src[tid] = src;
       s_new[tid] = nw;
       s_newslot[tid] = (L - 1) & 15;
     }
   }
-  if (STEP) __syncthreads();
-  // the chunk's x rows to LDS (rows past the chunk re-read its last row;
-  // their results are never stored)
+  if (STEP) lds_barrier();
+  // the chunk's x rows (rows past the chunk re-read its last row; their
+  // results are never stored) and this thread's slice of R, loaded before the
+  // page id so that waiting for them does not wait for it (loads complete in
+  // order)
   constexpr int kXPer = kRowsPerWg * D / kRowThreads;
+  uint16_t xv[kXPer];
 #pragma unroll
   for (int i = 0; i < kXPer; ++i) {
     const int e = tid * kXPer + i, r = e / D, c = e % D, rr = min(r, nr - 1);
-    uint16_t val = 0;
+    xv[i] = 0;
     if (!STEP) {
-      val = X[((row0 + rr) * p.n_kv + h) * D + c];
+      xv[i] = X[((row0 + rr) * p.n_kv + h) * D + c];
     } else if (s_src[rr] >= 0) {  // K token-major, V channel-major in the BF16 page
       const uint16_t* hp = p.bf16_pool + (int64_t(s_src[rr]) * p.n_kv + h) * GG::BF16_HEAD_ELEMS;
-      val = tensor == 0 ? hp[s_slot[rr] * D + c] : hp[16 * D + c * 16 + s_slot[rr]];
-    } else if (s_page[rr] >= 0) {
-      val = X[((row0 + rr) * p.n_kv + h) * D + c];
+      xv[i] = tensor == 0 ? hp[s_slot[rr] * D + c] : hp[16 * D + c * 16 + s_slot[rr]];
+    } else if (s_valid[rr]) {
+      xv[i] = X[((row0 + rr) * p.n_kv + h) * D + c];
     }
-    s_x[r][c] = val;
   }
   // products: thread (k-slice ks, channel quad c4) over the rows
   const int c4 = tid & 15, ks = tid >> 4;
@@ -521,7 +534,18 @@ __global__ __launch_bounds__(kRowThreads) void quantize_rows_kernel(QAParams p) 
 #pragma unroll
   for (int j = 0; j < KS_PER; ++j)
     rr[j] = *reinterpret_cast<const f32x4*>(R + size_t(ks * KS_PER + j) * D + 64 * pair + 4 * c4);
-  __syncthreads();
+  asm volatile("" ::: "memory");  // the page-id load stays behind the x and R loads
+  if (!STEP) {
+    const int32_t seq = my_page, pos = my_slot;
+    my_page = p.bt_q[int64_t(seq) * p.max_pages + (pos >> 4)];
+    my_slot = pos & 15;
+  }
+#pragma unroll
+  for (int i = 0; i < kXPer; ++i) {
+    const int e = tid * kXPer + i;
+    s_x[e / D][e % D] = xv[i];
+  }
+  lds_barrier();
 #pragma unroll
   for (int r = 0; r < kRowsPerWg; ++r) {
     f32x4 a = {0.f, 0.f, 0.f, 0.f};
@@ -533,7 +557,7 @@ __global__ __launch_bounds__(kRowThreads) void quantize_rows_kernel(QAParams p) 
     }
     *reinterpret_cast<f32x4*>(&s_part[r][ks][4 * c4]) = a;
   }
-  __syncthreads();
+  lds_barrier();
 
   // statistics and codes: thread (row rw, channel cc) holds channel cc of the
   // pair's first group and channel cc of its second, a row's 32 lanes being
@@ -560,15 +584,25 @@ __global__ __launch_bounds__(kRowThreads) void quantize_rows_kernel(QAParams p) 
     int code = 0;
     if (sf != 0.0f) code = min(max(int(__builtin_rintf((y[gp] - zf) / sf)), 0), 3);
     s_code[rw][32 * gp + cc] = uint8_t(code);
-    if (cc == 0 && rw < nr && s_page[rw] >= 0) {
-      const int g = 2 * pair + gp, slot = s_slot[rw];
-      uint8_t* base = p.pool + (int64_t(s_page[rw]) * p.n_kv + h) * int64_t(GG::HEAD_BYTES);
-      const int iu = tensor == 0 ? slot * NG + g : ((slot >> 2) * NG + g) * 4 + (slot & 3);
-      reinterpret_cast<uint16_t*>(base + (tensor == 0 ? GG::KS : GG::VS))[iu] = uint16_t(s16);
-      reinterpret_cast<uint16_t*>(base + (tensor == 0 ? GG::KZ : GG::VZ))[iu] = uint16_t(z16);
+    if (cc == 0) {
+      s_sz[rw][gp][0] = uint16_t(s16);
+      s_sz[rw][gp][1] = uint16_t(z16);
     }
   }
-  __syncthreads();
+  if (tid < nr) {  // the page ids, now needed (their round trip overlapped the work above)
+    s_page[tid] = my_page;
+    s_slot[tid] = my_slot;
+  }
+  lds_barrier();
+
+  // f16 scale and zero of each (row, group of the pair)
+  if (tid < 2 * nr && s_page[tid >> 1] >= 0) {
+    const int row = tid >> 1, gp = tid & 1, g = 2 * pair + gp, slot = s_slot[row];
+    uint8_t* base = p.pool + (int64_t(s_page[row]) * p.n_kv + h) * int64_t(GG::HEAD_BYTES);
+    const int iu = tensor == 0 ? slot * NG + g : ((slot >> 2) * NG + g) * 4 + (slot & 3);
+    reinterpret_cast<uint16_t*>(base + (tensor == 0 ? GG::KS : GG::VS))[iu] = s_sz[row][gp][0];
+    reinterpret_cast<uint16_t*>(base + (tensor == 0 ? GG::KZ : GG::VZ))[iu] = s_sz[row][gp][1];
+  }
 
   // code fields of the page layout.  K, row slot m: word (quad 16 + m) NW + pair
   // holds channel 32 gp + 16 hb + 4 quad + r of the pair at bit
