@@ -146,14 +146,21 @@ __global__ __launch_bounds__(kGramThreads) void calib_gram_kernel(GramParams p) 
     if (st + 1 < n_stages) stage(vb, st + 1);
   }
   if (ti < NB) {
-    // acc64[tj][r] = C[16 ti + 4 quad + r][16 tj + l16] (this chunk's part), tj >= ti
+    // acc64[tj][r] = C[16 ti + 4 quad + r][16 tj + l16] (this chunk's part), tj >= ti.
+    // Workgroups start at different blocks (by their index), so that the
+    // atomic adds of workgroups finishing together spread over addresses.
     double* o = p.out + size_t(h) * D * D;
-#pragma unroll
-    for (int tj = 0; tj < NB; ++tj) {
+    for (int k = 0; k < NB; ++k) {
+      const int tj = (k + int(blockIdx.x)) % NB;
       if (tj < ti) continue;
+      double v[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int t = 0; t < NB; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) v[r] = t == tj ? acc64[t][r] : v[r];
 #pragma unroll
       for (int r = 0; r < 4; ++r)
-        __hip_atomic_fetch_add(o + size_t(16 * ti + 4 * quad + r) * D + 16 * tj + l16, acc64[tj][r] * p.scale,
+        __hip_atomic_fetch_add(o + size_t(16 * ti + 4 * quad + r) * D + 16 * tj + l16, v[r] * p.scale,
                                __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
