@@ -304,7 +304,8 @@ oscar_status oscar_write_bf16(const oscar_cache* cache, const void* k_new,
  * Preconditions (device contents): the named pages are valid and not shared
  * with another sequence; the BF16 slot of token t still holds its row and is
  * not the BF16 slot the new token goes to.
- * Arithmetic: as oscar_quantize_append for up to 64 rows (float32 products).
+ * Arithmetic: float32 products, as oscar_quantize_append uses for up to 64
+ * rows, whatever the batch.
  * Errors: as oscar_quantize_append; both pools of the cache are required.
  * batch == 0 returns OSCAR_OK and launches nothing. */
 oscar_status oscar_decode_step_update(const oscar_cache* cache, const void* k_new,
