@@ -132,7 +132,7 @@ oscar_status oscar_build_rotation(int32_t d, int32_t n_kv_heads, int32_t group_q
  * the stream), not overlapping x.
  * Errors: INVALID_ARG for null pointers, n_rows < 1, n_kv_heads < 1,
  * n_x_heads not a positive multiple of n_kv_heads or x not 16-byte aligned;
- * UNSUPPORTED for d not in {64, 128} or more than 2^39 pooled rows. */
+ * UNSUPPORTED for d not in {64, 128}, G > 16 or more than 2^39 pooled rows. */
 oscar_status oscar_calib_gram(const void* x, int64_t n_rows, int32_t n_x_heads,
                               int32_t n_kv_heads, int32_t d, double* out, void* stream);
 

@@ -244,6 +244,7 @@ oscar_status oscar_calib_gram(const void* x, int64_t n_rows, int32_t n_x_heads, 
   if (!supported_d(d)) return fail(OSCAR_ERR_UNSUPPORTED, "d must be 64 or 128");
   if (n_rows < 1 || n_kv_heads < 1) return fail(OSCAR_ERR_INVALID_ARG, "n_rows < 1 or n_kv_heads < 1");
   if (n_x_heads < n_kv_heads || n_x_heads % n_kv_heads) return fail(OSCAR_ERR_INVALID_ARG, "n_x_heads not a multiple of n_kv_heads");
+  if (n_x_heads / n_kv_heads > 16) return fail(OSCAR_ERR_UNSUPPORTED, "more than 16 heads per KV group");
   if (reinterpret_cast<uintptr_t>(x) % 16) return fail(OSCAR_ERR_INVALID_ARG, "x not 16-byte aligned");
   const int64_t pooled = n_rows * (n_x_heads / n_kv_heads);
   if (pooled / 256 >= int64_t(0x7FFFFFFF) || n_rows > (int64_t(1) << 40)) return fail(OSCAR_ERR_UNSUPPORTED, "too many rows");

@@ -90,6 +90,7 @@ def test_device_calls_validate_before_launch():
     assert L.oscar_calib_gram(24, 8, 4, 1, 128, 16, None) == 1     # not 16-byte aligned
     assert b"aligned" in L.oscar_last_error()
     assert L.oscar_calib_gram(16, 0, 4, 1, 128, 16, None) == 1
+    assert L.oscar_calib_gram(16, 8, 17, 1, 128, 16, None) == 2    # 17 heads per KV group
     assert L.oscar_decode_workspace_init(None, 64, None) == 4
 
 
