@@ -111,6 +111,8 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="qwen3-8b-b1-32k")
+    ap.add_argument("--context", type=int, default=0,
+                    help="override the context length of a fixed-length workload (the workload is then named <name>-ctx<L>)")
     ap.add_argument("--split-pages", type=int, default=0)
     ap.add_argument("--copies", type=int, default=0, help="cache copies rotated over (0: >= 1 GiB total)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -152,6 +154,13 @@ def main() -> int:
     if args.calib_gram:
         return run_calib_gram(args, log)
     w = synth.WORKLOADS[args.workload]
+    if args.context:
+        if w.ctx[0] != "fixed" or args.context <= w.n_sink + w.n_recent:
+            print(f"--context needs a fixed-length workload and a length above sink + recent "
+                  f"({w.n_sink + w.n_recent}), so that the cache has an INT2 part", file=sys.stderr)
+            return 2
+        w = synth.Workload(**{**w.__dict__, "name": f"{w.name}-ctx{args.context}",
+                              "ctx": ("fixed", args.context, args.context)})
     t0 = time.time()
     inp = synth.decode_inputs(w)
     log(f"inputs {time.time() - t0:.1f}s  B={len(inp.seq_lens)} max_len={inp.max_seq_len}")
