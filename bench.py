@@ -128,9 +128,21 @@ def main() -> int:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the decode path shards by KV head "
               f"with no exchange between GPUs)", file=sys.stderr)
         return 2
+    from int2_rotated_kv_oscar_amd import synth
+    if args.workload not in synth.WORKLOADS:
+        print(f"unknown workload {args.workload!r}; known: {', '.join(sorted(synth.WORKLOADS))}", file=sys.stderr)
+        return 2
+    w = synth.WORKLOADS[args.workload]
+    if args.context:
+        if w.ctx[0] != "fixed" or args.context <= w.n_sink + w.n_recent:
+            print(f"--context needs a fixed-length workload and a length above sink + recent "
+                  f"({w.n_sink + w.n_recent}), so that the cache has an INT2 part", file=sys.stderr)
+            return 2
+        w = synth.Workload(**{**w.__dict__, "name": f"{w.name}-ctx{args.context}",
+                              "ctx": ("fixed", args.context, args.context)})
 
     import torch
-    from int2_rotated_kv_oscar_amd import lib, synth
+    from int2_rotated_kv_oscar_amd import lib
 
     def log(msg):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
@@ -153,14 +165,6 @@ def main() -> int:
         return run_append_prefill(args, log)
     if args.calib_gram:
         return run_calib_gram(args, log)
-    w = synth.WORKLOADS[args.workload]
-    if args.context:
-        if w.ctx[0] != "fixed" or args.context <= w.n_sink + w.n_recent:
-            print(f"--context needs a fixed-length workload and a length above sink + recent "
-                  f"({w.n_sink + w.n_recent}), so that the cache has an INT2 part", file=sys.stderr)
-            return 2
-        w = synth.Workload(**{**w.__dict__, "name": f"{w.name}-ctx{args.context}",
-                              "ctx": ("fixed", args.context, args.context)})
     t0 = time.time()
     inp = synth.decode_inputs(w)
     log(f"inputs {time.time() - t0:.1f}s  B={len(inp.seq_lens)} max_len={inp.max_seq_len}")
