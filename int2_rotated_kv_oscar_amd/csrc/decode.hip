@@ -95,6 +95,19 @@ __device__ __forceinline__ float ld_dev(const float* p) {
   return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// (a, b) = hi + lo, each a bf16 pair (element 0 in the low half), to 16
+// significant bits: the packed hardware conversion rounds to nearest even, as
+// the scalar split does, in one instruction per pair and part.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+__device__ __forceinline__ void split2x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = bf16x2_rne(a, b);
+  lo = bf16x2_rne(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u));
+}
+
 // Keep-mask of an f16/bf16 pair for tokens (t, t+1): stale bytes in slots
 // outside the region must not reach the value sums (0 * NaN is NaN).
 __device__ __forceinline__ uint32_t pair_keep(bool k0, bool k1) {
@@ -333,7 +346,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   };
 
   // ---- work layout ----
-  const int units = p.batch * p.n_kv;
   bool spec_issued = false;  // INT2 requests issued before the lengths were known
   int spec_b = 0, spec_h = 0;
   auto speculate_at = [&](int bb, int hh, int page) {
@@ -515,12 +527,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
       for (int kb = 0; kb < NKB; ++kb) {
         uint32_t ph[4], pl[4];
 #pragma unroll
-        for (int i = 0; i < 8; i += 2) {
-          uint32_t h0, l0, h1, l1;
-          split2(rvals[kb][i], h0, l0);
-          split2(rvals[kb][i + 1], h1, l1);
-          ph[i / 2] = pack2(h0, h1); pl[i / 2] = pack2(l0, l1);
-        }
+        for (int i = 0; i < 8; i += 2) split2x2(rvals[kb][i], rvals[kb][i + 1], ph[i / 2], pl[i / 2]);
         a4 = mfma_bf16(u32x4{pl[0], pl[1], pl[2], pl[3]}, bqv[kb], a4);
         a4 = mfma_bf16(u32x4{ph[0], ph[1], ph[2], ph[3]}, bqv[kb], a4);
       }
@@ -862,13 +869,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
         const float* rot_row = m_rot + qrow * D + 32 * kb + 8 * quad;
 #pragma unroll
         for (int k = 0; k < 8; k += 2) {
-          uint32_t h0, l0, h1, l1;
-          split2(rva[kb][k / 4][k % 4], h0, l0);
-          split2(rva[kb][(k + 1) / 4][(k + 1) % 4], h1, l1);
-          ah[k / 2] = pack2(h0, h1); al[k / 2] = pack2(l0, l1);
-          split2(rot_row[k], h0, l0);
-          split2(rot_row[k + 1], h1, l1);
-          bh[k / 2] = pack2(h0, h1); bl[k / 2] = pack2(l0, l1);
+          split2x2(rva[kb][k / 4][k % 4], rva[kb][(k + 1) / 4][(k + 1) % 4], ah[k / 2], al[k / 2]);
+          split2x2(rot_row[k], rot_row[k + 1], bh[k / 2], bl[k / 2]);
         }
         const u32x4 AH{ah[0], ah[1], ah[2], ah[3]}, AL{al[0], al[1], al[2], al[3]};
         const u32x4 BH{bh[0], bh[1], bh[2], bh[3]}, BL{bl[0], bl[1], bl[2], bl[3]};
