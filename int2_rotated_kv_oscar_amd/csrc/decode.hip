@@ -491,8 +491,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
         for (int r = 0; r < 4; ++r) l_part += pv[j][r];
       if (ALL_RAW) {
         // baseline: bf16 probabilities against bf16 values
-        const u32x4 bpr = {pack2(bf16_rne(pv[0][0]), bf16_rne(pv[0][1])), pack2(bf16_rne(pv[0][2]), bf16_rne(pv[0][3])),
-                           pack2(bf16_rne(pv[1][0]), bf16_rne(pv[1][1])), pack2(bf16_rne(pv[1][2]), bf16_rne(pv[1][3]))};
+        const u32x4 bpr = {bf16x2_rne(pv[0][0], pv[0][1]), bf16x2_rne(pv[0][2], pv[0][3]),
+                           bf16x2_rne(pv[1][0], pv[1][1]), bf16x2_rne(pv[1][2], pv[1][3])};
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb)
           acc[cb] = mfma_bf16(u32x4{vraw[0][cb][0], vraw[0][cb][1], vraw[1][cb][0], vraw[1][cb][1]}, bpr, acc[cb]);
@@ -825,13 +825,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) Mn = fmaxf(Mn, s_red[w * 16 + ms_n]);
   float lsum = 0.f;
+  // pass i holds records [32 i, 32 i + 32), the value rounds below read the
+  // weights of records [0, 32 n_pass): later passes are neither read nor written
+  static_assert(kMergeBatch == kThreads / 16, "a merge round reads the records of one pass");
 #pragma unroll
   for (int i = 0; i < kPass; ++i) {
+    if (i >= n_pass) break;
     const int s = (tid >> 4) + i * (kThreads / 16);
     const bool ok = s < n_s && ms_n < G && cm[i] != kNegInf;
     const float wgt = ok ? exp2f(cm[i] - Mn) : 0.f;
     lsum = fmaf(wgt, cl[i], lsum);
-    s_wr[s * 16 + ms_n] = cf[i] != 0.f ? 0.f : wgt;  // every slot written: zero past n_s
+    s_wr[s * 16 + ms_n] = cf[i] != 0.f ? 0.f : wgt;  // every slot read is written: zero past n_s
     s_wu[s * 16 + ms_n] = cf[i] != 0.f ? wgt : 0.f;
   }
   lsum = wave_sum16(lsum);
@@ -883,8 +887,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
       uint16_t* o = p.out + (size_t(b) * p.Hq + h * G + l16) * D + 16 * wave + 4 * quad;
       const float* rw = m_raw + l16 * D + 16 * wave + 4 * quad;
       u32x2 ov;
-      ov[0] = pack2(bf16_rne(a4[0] + rw[0]), bf16_rne(a4[1] + rw[1]));
-      ov[1] = pack2(bf16_rne(a4[2] + rw[2]), bf16_rne(a4[3] + rw[3]));
+      ov[0] = bf16x2_rne(a4[0] + rw[0], a4[1] + rw[1]);
+      ov[1] = bf16x2_rne(a4[2] + rw[2], a4[3] + rw[3]);
       *reinterpret_cast<u32x2*>(o) = ov;
     }
   }
