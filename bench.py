@@ -36,6 +36,16 @@ HBM_PEAK_GBPS = 8000.0
 METRIC = "INT2 paged decode-attn KV-tokens/s + achieved HBM GB/s (% of peak), Qwen3-8B layer"
 
 
+def blas_threads(n: int):
+    """Limit the host BLAS pools to n threads (threadpoolctl) and report the
+    count they then hold: the core count a cpu_baseline states is measured,
+    not assumed."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    lim = threadpool_limits(limits=n, user_api="blas")
+    got = [p.get("num_threads") for p in threadpool_info() if p.get("user_api") == "blas"]
+    return lim, (max(got) if got else 1)
+
+
 def algorithmic_bytes(inp, w) -> dict:
     """Unique bytes the decode must move: INT2 middle tokens at 96 B (d=128)
     per KV head (2 x d/4 B codes + 2 x 2 (d/32) f16 scale/zero x 2 B), BF16
@@ -117,6 +127,8 @@ def main() -> int:
     ap.add_argument("--copies", type=int, default=0, help="cache copies rotated over (0: >= 1 GiB total)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-bf16-baseline", action="store_true")
+    ap.add_argument("--no-append", action="store_true",
+                    help="leave out the quantize-append prefill line (kernel A) of the default run")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run 5 plain device copies of MIB MiB (calibrates HBM byte counters), then exit")
     ap.add_argument("--append-prefill", action="store_true",
@@ -321,13 +333,17 @@ def main() -> int:
                               "update_us_per_call": round(upd_ms * 1e3, 2)}
     log(f"serving step (update + decode) {serve_ms * 1e3:.1f} us, update alone {upd_ms * 1e3:.1f} us")
 
-    # attainable streaming bandwidth, as context for the roofline fraction: a
-    # vectorized elementwise kernel (read + write) over 1 GiB, several times the
-    # Infinity Cache (torch's reductions stream slower, about 3.9 TB/s)
+    # attainable bandwidth, as context for the roofline fraction, over 1 GiB
+    # (several times the Infinity Cache): a streaming read of the buffer with
+    # nothing written back (the library's probe kernel; the decode reads far
+    # more than it writes), and torch's vectorized elementwise kernel (read +
+    # write bytes)
     pa = torch.ones(1 << 28, dtype=torch.float32, device=dev)
     pb = torch.empty_like(pa)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
     for _ in range(3):
         torch.mul(pa, 2.0, out=pb)
+        lib.bw_probe_read(pa, sink)
     torch.cuda.synchronize()
     p0, p1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     p0.record()
@@ -336,11 +352,18 @@ def main() -> int:
     p1.record()
     torch.cuda.synchronize()
     probe = 2 * pa.numel() * 4 / (p0.elapsed_time(p1) / 20 * 1e-3) / 1e9
+    p0.record()
+    for _ in range(20):
+        lib.bw_probe_read(pa, sink)
+    p1.record()
+    torch.cuda.synchronize()
+    rprobe = pa.numel() * 4 / (p0.elapsed_time(p1) / 20 * 1e-3) / 1e9
     del pa, pb
-    result["bw_probe"] = {"stream_GBps": round(probe, 1),
-                          "method": "torch.mul over a 1 GiB float32 buffer, read + write bytes",
-                          "decode_frac_of_probe": round(achieved / probe, 4)}
-    log(f"bw probe {probe:.0f} GB/s streamed; decode at {achieved / probe:.1%} of it")
+    result["bw_probe"] = {"read_GBps": round(rprobe, 1), "stream_GBps": round(probe, 1),
+                          "method": "oscar_bw_probe_read over a 1 GiB buffer (read bytes); torch.mul over a "
+                                    "1 GiB float32 buffer (read + write bytes)",
+                          "decode_frac_of_read_probe": round(achieved / rprobe, 4)}
+    log(f"bw probes: read {rprobe:.0f} GB/s, read+write {probe:.0f} GB/s; decode at {achieved / rprobe:.1%} of the read probe")
 
     if not args.no_bf16_baseline:
         # the same decode over an all-BF16 cache (every token in BF16 pages)
@@ -373,8 +396,14 @@ def main() -> int:
         log(f"bf16 baseline {bms * 1e3:.1f} us/call")
         del hpools, hcaches
 
+    if not args.no_append:
+        # kernel A alone on the large-GQA layer's prefill, its own roofline
+        result["quantize_append"] = append_prefill_line(args, log, cpu=False)
+
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = _cpu_baseline(inp, w, cache, int2, bf16, rt, tokens, log)
+        cores = len(os.sched_getaffinity(0))
+        result["cpu_baseline"] = _cpu_baseline(inp, w, cache, int2, bf16, rt, tokens, log, cores, 10.0)
+        result["cpu_baseline_single_core"] = _cpu_baseline(inp, w, cache, int2, bf16, rt, tokens, log, 1, 5.0)
     print(json.dumps(result), flush=True)
     return 0
 
@@ -392,6 +421,11 @@ def append_bytes(n_rows: int, n_kv: int, d: int, n_pages: int) -> int:
 
 
 def run_append_prefill(args, log) -> int:
+    print(json.dumps(append_prefill_line(args, log, cpu=not args.no_cpu_baseline)), flush=True)
+    return 0
+
+
+def append_prefill_line(args, log, cpu: bool) -> dict:
     """Kernel A alone on the large-GQA layer's prefill: 8 sequences append an
     8192-token chunk each (page-aligned, shuffled pages), 8 KV heads, d = 128.
     The timed launches rotate over input/pool copies totalling >= 1 GiB."""
@@ -467,10 +501,11 @@ def run_append_prefill(args, log) -> int:
                      "avg_launch_us": round(ms * 1e3, 2),
                      "mfma_tflops_algorithmic": round(flops / (ms * 1e-3) / 1e12, 2)},
     }
-    if not args.no_cpu_baseline:
+    if cpu:
         result["cpu_baseline"] = _cpu_append_baseline(k, v, row_seq, row_pos, bt, rt, w, n_rows, log)
-    print(json.dumps(result), flush=True)
-    return 0
+    del sets, base
+    torch.cuda.empty_cache()
+    return result
 
 
 GRAM_METRIC = "calibration Gram pooled rows/s + achieved HBM GB/s (% of peak), Qwen3-8B calibration"
@@ -520,7 +555,7 @@ def run_calib_gram(args, log) -> int:
     }
     if not args.no_cpu_baseline:
         from oracle import rotation as orot
-        cores = len(os.sched_getaffinity(0))
+        lim, threads = blas_threads(len(os.sched_getaffinity(0)))
         q64 = cal.q.astype(np.float64)
         t0 = time.time()
         heads = 0
@@ -531,10 +566,11 @@ def run_calib_gram(args, log) -> int:
             if time.time() - t0 > 10.0:
                 break
         dt = (time.time() - t0) / 2  # each call forms the Q and the O target
-        result["cpu_baseline"] = {"value": round(n * 4 * heads / dt, 1), "unit": "pooled rows/s", "cores": cores,
+        lim.restore_original_limits()
+        result["cpu_baseline"] = {"value": round(n * 4 * heads / dt, 1), "unit": "pooled rows/s", "cores": threads,
                                   "kind": "oracle",
                                   "sample": f"oracle float64 targets of {heads}/{w.n_kv_heads} KV heads "
-                                            f"(numpy BLAS threads = {cores})"}
+                                            f"(BLAS pool measured at {threads} threads)"}
     print(json.dumps(result), flush=True)
     return 0
 
@@ -544,6 +580,7 @@ def _cpu_append_baseline(k, v, row_seq, row_pos, bt, rt, w, n_rows, log) -> dict
     from oracle import cache as ocache
     from oracle import layout as olayout
     cores = len(os.sched_getaffinity(0))
+    lim, threads = blas_threads(cores)
     rk = rt["r_k"].astype(np.float32).astype(np.float64)
     rv = rt["r_v"].astype(np.float32).astype(np.float64)
     n_pages = bt.size
@@ -557,10 +594,12 @@ def _cpu_append_baseline(k, v, row_seq, row_pos, bt, rt, w, n_rows, log) -> dict
         dt += time.time() - t0
         done = sel.stop
         n *= 2
-    log(f"cpu oracle: {done} rows in {dt:.1f}s on {cores} cores")
-    return {"value": round(done / dt, 1), "unit": "rows/s", "cores": cores, "kind": "oracle",
+    lim.restore_original_limits()
+    log(f"cpu oracle: {done} rows in {dt:.1f}s, BLAS threads {threads}")
+    return {"value": round(done / dt, 1), "unit": "rows/s", "cores": threads, "kind": "oracle",
             "sample": f"oracle float64 quantize-append of the first {done} of the {n_rows} rows "
-                      f"(all {w.n_kv_heads} KV heads, K and V); numpy BLAS threads = {cores}"}
+                      f"(all {w.n_kv_heads} KV heads, K and V); BLAS pool limited to {cores} and measured at "
+                      f"{threads} threads"}
 
 
 def _all_bf16_tables(inp):
@@ -574,13 +613,13 @@ def _all_bf16_tables(inp):
     return bt, inp.n_int2_pages, max(n, 1), mp
 
 
-def _cpu_baseline(inp, w, cache, int2, bf16, rt, tokens, log) -> dict:
-    """The oracle (float64 NumPy) decoding the same cache, on the host cores."""
-    import torch
+def _cpu_baseline(inp, w, cache, int2, bf16, rt, tokens, log, cores: int, budget_s: float) -> dict:
+    """The oracle (float64 NumPy) decoding the same cache on `cores` host
+    threads (the BLAS pool limited to them), for about budget_s seconds."""
     from oracle import attention as oatt
     from oracle import layout as olayout
     from int2_rotated_kv_oscar_amd import lib, synth
-    cores = len(os.sched_getaffinity(0))
+    lim, threads = blas_threads(cores)
     pool_q = olayout.Int2Pool(inp.n_int2_pages, w.n_kv_heads, w.d, int2.cpu().numpy())
     pool_h = olayout.Bf16Pool(bf16.numel() * 2 // lib.bf16_page_bytes(w.d, w.n_kv_heads), w.n_kv_heads, w.d,
                               bf16.cpu().numpy().view(np.uint16))
@@ -597,14 +636,16 @@ def _cpu_baseline(inp, w, cache, int2, bf16, rt, tokens, log) -> dict:
         oatt.decode_attention(q[:, h * G:(h + 1) * G], one_q, one_h, inp.seq_lens, inp.bt_q, inp.bt_h,
                               rk[h:h + 1], rv[h:h + 1], w.n_sink, w.n_recent)
         heads.append(h)
-        if time.time() - t0 > 10.0:
+        if time.time() - t0 > budget_s:
             break
     dt = time.time() - t0
+    lim.restore_original_limits()
     per_layer = dt * w.n_kv_heads / len(heads)
-    log(f"cpu oracle: {len(heads)} KV heads in {dt:.1f}s on {cores} cores")
-    return {"value": round(tokens / per_layer, 1), "unit": "KV-tokens/s", "cores": cores, "kind": "oracle",
+    log(f"cpu oracle: {len(heads)} KV heads in {dt:.1f}s, BLAS threads {threads}")
+    return {"value": round(tokens / per_layer, 1), "unit": "KV-tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"oracle float64 decode of {len(heads)}/{w.n_kv_heads} KV heads of the same cache "
-                      f"({tokens} tokens), time scaled to all heads; numpy BLAS threads = {cores}"}
+                      f"({tokens} tokens), time scaled to all heads; BLAS pool limited to {cores} and measured at "
+                      f"{threads} threads"}
 
 
 if __name__ == "__main__":

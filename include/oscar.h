@@ -339,7 +339,13 @@ oscar_status oscar_decode_step_update(const oscar_cache* cache, const void* k_ne
  * units for small batches, equal page slices over the whole batch for large
  * ones).  workspace: device memory of at least
  * oscar_decode_workspace_bytes(...) bytes, prepared once with
- * oscar_decode_workspace_init; every completed call leaves it prepared.
+ * oscar_decode_workspace_init.  It holds one arrival counter per (sequence,
+ * KV head), which the call counts up and its last workgroup of that pair
+ * resets to zero, and the per-workgroup partial results; every completed call
+ * leaves it prepared.  A call that does not complete (a launch error, a
+ * device fault) can leave counters non-zero, and a later call on that
+ * workspace then merges at the wrong time and returns wrong values:
+ * oscar_decode_workspace_init restores it.
  * out: device bf16 [B][H_q][d].
  * Preconditions (device contents): 0 <= seq_lens[b] <= max_seq_len, valid
  * page ids wherever they are read.  A sequence with seq_lens[b] == 0 gets a
@@ -375,6 +381,18 @@ oscar_status oscar_paged_decode_attn_bf16(const oscar_cache* cache, const void* 
                                           float sm_scale, int32_t split_pages,
                                           void* workspace, size_t workspace_bytes,
                                           void* out, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Measurement context (not part of the method): reads `bytes` bytes of the
+ * device buffer `buf` once, streaming, and writes nothing back (`sink`, a
+ * device uint32, is written only if the data fold to one particular value),
+ * so that timing it gives the attainable HBM read bandwidth the decode
+ * kernels, which read far more than they write, can be compared with ([TS] 4
+ * attributes the batch-1 decode speedup to reduced memory traffic).
+ * buf and bytes: multiples of 16 bytes.  Asynchronous on `stream`.
+ * Errors: INVALID_ARG for null pointers or unaligned buf or bytes.
+ * ------------------------------------------------------------------------ */
+oscar_status oscar_bw_probe_read(const void* buf, size_t bytes, uint32_t* sink, void* stream);
 
 #ifdef __cplusplus
 }

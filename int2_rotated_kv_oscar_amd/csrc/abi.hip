@@ -7,7 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 
-#include "common.h"
+#include "abi_internal.h"
 #include "kernels.h"
 
 namespace oscar {
@@ -30,6 +30,10 @@ namespace {
 
 bool supported_d(int32_t d) { return d == 64 || d == 128; }
 
+}  // namespace
+
+namespace oscar {
+
 oscar_status hip_status(hipError_t e, const char* what) {
   if (e == hipSuccess) return OSCAR_OK;
   oscar::set_error("OSCAR_ERR_HIP: %s: %s", what, hipGetErrorString(e));
@@ -46,17 +50,16 @@ oscar_status check_cache(const oscar_cache* c, bool need_int2, bool need_bf16) {
   return OSCAR_OK;
 }
 
-// Decode work planning shared by the workspace query and the decode calls.
-struct DecodePlan {
-  bool per_unit;    // per-unit items, or balanced slices over all units
-  int unit_items;   // per-unit items: workgroups per (sequence, KV head)
-  int fixed_ppw;    // per-unit items: pages per item; slices: pages per slice (0: spread evenly)
-  int n_wg;         // workgroups in the grid
-  int cap;          // record slots per (sequence, KV head)
-  int rec_floats;
-  size_t counter_bytes;
-  size_t bytes;
-};
+}  // namespace oscar
+
+namespace {
+
+using oscar::check_cache;
+using oscar::hip_status;
+
+}  // namespace
+
+namespace oscar {
 
 int device_cu_count() {
   static int cached[64] = {0};
@@ -127,6 +130,14 @@ oscar_status plan_decode(int32_t batch, int32_t n_kv, int32_t n_q, int32_t d, in
   plan->bytes = plan->counter_bytes + size_t(units) * plan->cap * plan->rec_floats * 4;
   return OSCAR_OK;
 }
+
+}  // namespace oscar
+
+namespace {
+
+using oscar::DecodePlan;
+using oscar::device_cu_count;
+using oscar::plan_decode;
 
 __global__ void fill_zero_kernel(uint32_t* p, size_t n_words) {
   for (size_t i = size_t(blockIdx.x) * blockDim.x + threadIdx.x; i < n_words; i += size_t(gridDim.x) * blockDim.x)
@@ -277,15 +288,16 @@ oscar_status oscar_decode_workspace_init(void* workspace, size_t workspace_bytes
   return hip_status(hipGetLastError(), "workspace init launch");
 }
 
-static oscar_status decode_common(bool all_raw, const oscar_cache* cache, const void* q, int32_t batch,
-                                  int32_t n_q_heads, const int32_t* seq_lens, int32_t max_seq_len,
-                                  const int32_t* bt_q, const int32_t* bt_h, int32_t max_pages, const float* r_k,
-                                  const float* r_v, float sm_scale, int32_t split_pages, void* workspace,
-                                  size_t workspace_bytes, void* out, void* stream) {
-  oscar::clear_error();
+}  // extern "C"
+
+namespace oscar {
+
+oscar_status decode_validate(bool all_raw, const oscar_cache* cache, const void* q, int32_t batch,
+                             int32_t n_q_heads, const int32_t* seq_lens, int32_t max_seq_len, const int32_t* bt_q,
+                             const int32_t* bt_h, int32_t max_pages, const float* r_k, const float* r_v,
+                             float sm_scale, int32_t split_pages, const void* out, DecodePlan* plan) {
   if (oscar_status s = check_cache(cache, !all_raw, true)) return s;
-  DecodePlan plan;
-  if (oscar_status s = plan_decode(batch, cache->n_kv_heads, n_q_heads, cache->d, max_seq_len, split_pages, all_raw, &plan))
+  if (oscar_status s = plan_decode(batch, cache->n_kv_heads, n_q_heads, cache->d, max_seq_len, split_pages, all_raw, plan))
     return s;
   if (batch == 0) return OSCAR_OK;
   if (!q || !seq_lens || !bt_h || !out || (!all_raw && (!bt_q || !r_k || !r_v)))
@@ -293,12 +305,15 @@ static oscar_status decode_common(bool all_raw, const oscar_cache* cache, const 
   if (max_pages < 1 || int64_t(max_seq_len) > int64_t(max_pages) * 16)
     return fail(OSCAR_ERR_INVALID_ARG, "max_seq_len exceeds 16 * max_pages");
   if (!(std::isfinite(sm_scale) && sm_scale > 0.f)) return fail(OSCAR_ERR_INVALID_ARG, "sm_scale must be finite and positive");
-  if (!workspace) return fail(OSCAR_ERR_WORKSPACE, "workspace is NULL");
-  if (workspace_bytes < plan.bytes) return fail(OSCAR_ERR_WORKSPACE, "workspace smaller than oscar_decode_workspace_bytes");
   if (batch > 65535) return fail(OSCAR_ERR_UNSUPPORTED, "batch above 65535");
+  return OSCAR_OK;
+}
+
+oscar_status decode_launch(bool all_raw, const oscar_cache* cache, const void* q, int32_t batch, int32_t n_q_heads,
+                           const int32_t* seq_lens, int32_t max_seq_len, const int32_t* bt_q, const int32_t* bt_h,
+                           int32_t max_pages, const float* r_k, const float* r_v, float sm_scale,
+                           const DecodePlan& plan, int32_t* counters, float* partials, void* out, void* stream) {
   const int G = n_q_heads / cache->n_kv_heads;
-  int32_t* counters = static_cast<int32_t*>(workspace);
-  float* partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.counter_bytes);
   return hip_status(
       oscar_launch::paged_decode(cache->d, all_raw, cache->int2_pool, cache->n_int2_pages, cache->bf16_pool, cache->n_kv_heads, G,
                                  cache->n_sink, cache->n_recent, n_q_heads, q, batch, seq_lens, all_raw ? bt_h : bt_q,
@@ -307,6 +322,29 @@ static oscar_status decode_common(bool all_raw, const oscar_cache* cache, const 
                                  4LL * batch * cache->n_kv_heads < device_cu_count(), static_cast<hipStream_t>(stream)),
       "decode launch");
 }
+
+}  // namespace oscar
+
+static oscar_status decode_common(bool all_raw, const oscar_cache* cache, const void* q, int32_t batch,
+                                  int32_t n_q_heads, const int32_t* seq_lens, int32_t max_seq_len,
+                                  const int32_t* bt_q, const int32_t* bt_h, int32_t max_pages, const float* r_k,
+                                  const float* r_v, float sm_scale, int32_t split_pages, void* workspace,
+                                  size_t workspace_bytes, void* out, void* stream) {
+  oscar::clear_error();
+  DecodePlan plan;
+  if (oscar_status s = oscar::decode_validate(all_raw, cache, q, batch, n_q_heads, seq_lens, max_seq_len, bt_q, bt_h,
+                                              max_pages, r_k, r_v, sm_scale, split_pages, out, &plan))
+    return s;
+  if (batch == 0) return OSCAR_OK;
+  if (!workspace) return fail(OSCAR_ERR_WORKSPACE, "workspace is NULL");
+  if (workspace_bytes < plan.bytes) return fail(OSCAR_ERR_WORKSPACE, "workspace smaller than oscar_decode_workspace_bytes");
+  int32_t* counters = static_cast<int32_t*>(workspace);
+  float* partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.counter_bytes);
+  return oscar::decode_launch(all_raw, cache, q, batch, n_q_heads, seq_lens, max_seq_len, bt_q, bt_h, max_pages, r_k,
+                              r_v, sm_scale, plan, counters, partials, out, stream);
+}
+
+extern "C" {
 
 oscar_status oscar_paged_decode_attn(const oscar_cache* cache, const void* q, int32_t batch, int32_t n_q_heads,
                                      const int32_t* seq_lens, int32_t max_seq_len, const int32_t* bt_q,

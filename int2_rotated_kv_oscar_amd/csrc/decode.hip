@@ -82,10 +82,6 @@ constexpr float kNegInf = -__builtin_inff();
 
 __device__ __forceinline__ bool overlaps(int a0, int a1, int b0, int b1) { return max(a0, b0) < min(a1, b1); }
 
-__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v) {
-  return pack_f16x2(bf16_to_f32(v & 0xFFFFu), bf16_to_f32(v >> 16));
-}
-
 // device-coherent (write-through / L2-bypassing) 32-bit accesses for the
 // chunk records exchanged between workgroups on different XCDs
 __device__ __forceinline__ void st_dev(float* p, float v) {
@@ -497,14 +493,20 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
         for (int cb = 0; cb < NCB; ++cb)
           acc[cb] = mfma_bf16(u32x4{vraw[0][cb][0], vraw[0][cb][1], vraw[1][cb][0], vraw[1][cb][1]}, bpr, acc[cb]);
       } else {
-        // sink/recent tokens of the mixed cache: f16 probabilities and values
-        const u32x4 bpr = {pack_f16x2(pv[0][0], pv[0][1]), pack_f16x2(pv[0][2], pv[0][3]),
-                           pack_f16x2(pv[1][0], pv[1][1]), pack_f16x2(pv[1][2], pv[1][3])};
+        // sink/recent tokens of the mixed cache: the raw bf16 values (any
+        // bf16 magnitude) against the probabilities split into bf16 hi + lo
+        // (16 significant bits), two products per block
+        uint32_t ph[4], pl[4];
+        split2x2(pv[0][0], pv[0][1], ph[0], pl[0]);
+        split2x2(pv[0][2], pv[0][3], ph[1], pl[1]);
+        split2x2(pv[1][0], pv[1][1], ph[2], pl[2]);
+        split2x2(pv[1][2], pv[1][3], ph[3], pl[3]);
+        const u32x4 bph = {ph[0], ph[1], ph[2], ph[3]}, bpl = {pl[0], pl[1], pl[2], pl[3]};
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
-          const u32x4 a = {bf16x2_to_f16x2(vraw[0][cb][0]), bf16x2_to_f16x2(vraw[0][cb][1]),
-                           bf16x2_to_f16x2(vraw[1][cb][0]), bf16x2_to_f16x2(vraw[1][cb][1])};
-          acc[cb] = mfma_f16(a, bpr, acc[cb]);
+          const u32x4 a = {vraw[0][cb][0], vraw[0][cb][1], vraw[1][cb][0], vraw[1][cb][1]};
+          acc[cb] = mfma_bf16(a, bpl, acc[cb]);
+          acc[cb] = mfma_bf16(a, bph, acc[cb]);
         }
       }
     }
@@ -756,10 +758,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     for (int w = 0; w < kWaves; ++w) a += s_res[w * G * D + e];
     st_dev(rec + 2 * G + e, a);
   }
-  __builtin_amdgcn_s_waitcnt(0);  // records acknowledged before the arrival is counted
+  // Hand-off to the unit's last workgroup: every thread's record stores are
+  // ordered before the barrier, the barrier before thread 0's arrival, a
+  // release at device scope; the last arrival acquires at device scope and
+  // its barrier orders the acquire before every thread's record loads.
+  __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (tid == 0) {
-    const int old = __hip_atomic_fetch_add(p.counters + b * p.n_kv + h, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const int old = __hip_atomic_fetch_add(p.counters + b * p.n_kv + h, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     s_flag[8] = (old == nseg - 1) ? 1 : 0;
   }
   __syncthreads();

@@ -334,9 +334,14 @@ __device__ void qa_tiles(const QAParams& p, int h, QAShared<D, ONE>& sh) {
     }
   };
 
-  // bf16 -> f16 is exact for |x| < 2^15 (down to 2^-17; smaller values round
-  // at 2^-25).  A row holding a larger value is scaled by a power of two
-  // 2^-e (e recorded per row and undone in the epilogue) before conversion.
+  // bf16 -> f16 is exact for 2^-17 <= |x| < 2^15; smaller values are cut
+  // to the 2^-24 grid.  Rows of ordinary magnitude (every value of a lane
+  // below 2^15, and some value of every lane at least 2^-3) are converted as
+  // they are: a cut value then errs by at most 2^-21 of the row's largest.
+  // Otherwise every row of this wave's quarter is scaled by the power of two
+  // 2^-e that brings its largest magnitude into [2^14, 2^15) (e recorded per
+  // row and undone in the epilogue; e >= -118 keeps the epilogue's factors
+  // finite), so small rows keep their precision as large ones do.
   auto stage_x = [&](const u32x4& v, int buf) {
     const int row = kQuarterRows * g + lane / kChunks;
     // largest bf16 magnitude of each half over the lane's 8 values
@@ -345,15 +350,17 @@ __device__ void qa_tiles(const QAParams& p, int h, QAShared<D, ONE>& sh) {
         __builtin_elementwise_max(__builtin_bit_cast(us2, v[0] & 0x7FFF7FFFu), __builtin_bit_cast(us2, v[1] & 0x7FFF7FFFu)),
         __builtin_elementwise_max(__builtin_bit_cast(us2, v[2] & 0x7FFF7FFFu), __builtin_bit_cast(us2, v[3] & 0x7FFF7FFFu)));
     const uint32_t mb = __builtin_bit_cast(uint32_t, mm);
-    const bool big = (mb & 0xFFFFu) >= (142u << 7) || mb >= ((142u << 7) << 16);
+    const uint32_t lo = mb & 0xFFFFu, hi = mb >> 16;
+    const bool big = lo >= (142u << 7) || hi >= (142u << 7);
+    const bool small = lo < (124u << 7) && hi < (124u << 7);
     u32x4 o;
     int e = 0;
-    if (__builtin_expect(__any(big), 0)) {
+    if (__builtin_expect(__any(big || small), 0)) {
       // exponent of the row's largest value, over the row's kChunks lanes
-      int ex = int(max(mb & 0x7F80u, (mb >> 16) & 0x7F80u) >> 7);
+      int ex = int(max(lo, hi) >> 7);
 #pragma unroll
       for (int msk = 1; msk < kChunks; msk <<= 1) ex = max(ex, __shfl_xor(ex, msk, 64));
-      e = max(0, ex - 141);
+      e = max(-118, ex - 141);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         o[i] = pack_f16x2_rtz(__builtin_ldexpf(bf16_to_f32(v[i] & 0xFFFFu), -e), __builtin_ldexpf(bf16_to_f32(v[i] >> 16), -e));

@@ -27,7 +27,7 @@ EXPORTS = [
     "oscar_build_fixed_rotation", "oscar_int2_page_bytes", "oscar_bf16_page_bytes", "oscar_quantize_append",
     "oscar_write_bf16", "oscar_decode_step_update", "oscar_decode_workspace_bytes", "oscar_calib_gram",
     "oscar_build_rotation_from_targets", "oscar_decode_workspace_init", "oscar_paged_decode_attn",
-    "oscar_paged_decode_attn_bf16",
+    "oscar_paged_decode_attn_bf16", "oscar_bw_probe_read",
 ]
 
 
@@ -85,6 +85,7 @@ def load(path: str = LIB_PATH):
                                               _P, _P, _F32, _I32, _P, _SZ, _P, _P]),
         "oscar_paged_decode_attn_bf16": (_STATUS, [ctypes.POINTER(OscarCache), _P, _I32, _I32, _P, _I32, _P, _I32,
                                                    _F32, _I32, _P, _SZ, _P, _P]),
+        "oscar_bw_probe_read": (_STATUS, [_P, _SZ, _P, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -264,3 +265,8 @@ def paged_decode_attn_bf16(cache: OscarCache, q, seq_lens, max_seq_len: int, bt_
                                                _dptr(bt_h), bt_h.shape[1], sc, split_pages, _dptr(workspace),
                                                workspace.numel() * workspace.element_size(), _dptr(out),
                                                _stream(stream)))
+
+
+def bw_probe_read(buf, sink, stream=None):
+    """One streaming read of the device tensor ``buf`` (nothing written back)."""
+    _check(load().oscar_bw_probe_read(_dptr(buf), buf.numel() * buf.element_size(), _dptr(sink), _stream(stream)))

@@ -19,7 +19,13 @@ from oracle import rotation as orot
 DEV = "cuda:0"
 BOUNDARY_EPS = 1e-5        # codes may differ where (y - z)/s is this close to k + 1/2
 MIDPOINT_REL = 1e-6        # f16 scale/zero may differ this close to an f16 midpoint, relative to max|y| of the group
-FLIP_BUDGET = 1e-4         # at most 0.01 % of codes may be exempt flips
+FLIP_BUDGET = 1e-4         # at most 0.01 % of codes may differ from the oracle's (all exempt)
+# Groups whose f16 scale or zero rounds to the neighbouring f16 value (the
+# oracle's float64 value lies within the 1e-6 window of a rounding midpoint).
+# Agreement to 1e-6 of the group's magnitude, the acceptance bar, lets up to
+# about 2 * 1e-6 / 2^-11 = 0.4 % of f16 values straddle a midpoint; the kernels'
+# float32 values (about 2^-22 of the magnitude) move about 0.03 % of groups.
+GROUP_BUDGET = 1e-3
 ATT_REL_L2 = 5e-3
 ATT_MAX_ABS = 2e-2
 
@@ -81,6 +87,24 @@ def alloc_cache(inp: synth.DecodeInputs, rot: Rotation, int2_bytes: np.ndarray |
     return GpuCache(int2, bf16, cache, i32(inp.bt_q), i32(inp.bt_h),
                     torch.from_numpy(rot.r_k.astype(np.float32)).to(DEV),
                     torch.from_numpy(rot.r_v.astype(np.float32)).to(DEV))
+
+
+def fill_stale(gc: GpuCache, seed: int = 0):
+    """Pools as paged serving leaves them (recycled pages): every 16-bit half
+    random, a quarter of them f16/bf16 NaN or infinity bit patterns.  A fill
+    afterwards rewrites only the slots of the regions; the decode must never
+    let the rest reach its sums."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(1234 + seed)
+    pats = torch.tensor([0x7E00, 0x7C00, 0xFC00, 0x7FC0, 0x7F80, 0xFF80, 0xFFFF, 0x7FFF], dtype=torch.int32,
+                        device=DEV)
+    for buf in (gc.int2, gc.bf16):
+        h = buf.view(torch.int16)
+        r = torch.randint(0, 65536, h.shape, generator=g, device=DEV, dtype=torch.int32)
+        pick = torch.randint(0, 4 * len(pats), h.shape, generator=g, device=DEV, dtype=torch.int32)
+        r = torch.where(pick < len(pats), pats[pick.clamp(max=len(pats) - 1)], r)
+        h.copy_((r - 65536 * (r >= 32768).int()).to(torch.int16))
+    torch.cuda.synchronize()
 
 
 def gpu_fill(inp: synth.DecodeInputs, rot: Rotation, gc: GpuCache, rows=None):
@@ -159,11 +183,12 @@ def assert_attention_close(got, ref, what=""):
 @dataclasses.dataclass
 class CodeReport:
     n_codes: int
-    exempt_flips: int
-    bad_codes: int
+    exempt_flips: int   # codes at a rounding boundary that differ (against the reference codes below)
+    bad_codes: int      # codes that differ away from any exemption
     n_groups: int
-    exempt_groups: int
-    bad_groups: int
+    exempt_groups: int  # scale or zero one f16 step off, at an f16 rounding midpoint
+    bad_groups: int     # scale or zero different away from a midpoint
+    changed_codes: int = 0  # codes different from the oracle's own codes, for any (exempt) reason
 
 
 def compare_appended(gpu_int2: np.ndarray, inp_w: synth.Workload, n_pages: int, res: ocache.AppendResult,
@@ -171,7 +196,7 @@ def compare_appended(gpu_int2: np.ndarray, inp_w: synth.Workload, n_pages: int, 
     """Codes and f16 scale/zero the GPU wrote for rows (page, slot) vs the
     oracle's record ``res`` of the same rows."""
     pool = olayout.Int2Pool(n_pages, inp_w.n_kv_heads, inp_w.d, gpu_int2)
-    n_codes = flips = bad = n_groups = ex_groups = bad_groups = 0
+    n_codes = flips = bad = n_groups = ex_groups = bad_groups = changed = 0
     for h in range(inp_w.n_kv_heads):
         ck, cv, ks, kz, vs, vz = pool.read(page, slot, h)
         for codes, s16, z16, ref in ((ck, ks, kz, res.k[h]), (cv, vs, vz, res.v[h])):
@@ -209,14 +234,17 @@ def compare_appended(gpu_int2: np.ndarray, inp_w: synth.Workload, n_pages: int, 
                 t[sel] = t2[sel]
                 ref_codes[sel] = c2[sel]
             mism = codes.reshape(n, ng, 32).astype(np.int64) != ref_codes
+            changed += int((codes.reshape(-1).astype(np.int64) != ref.codes.reshape(-1).astype(np.int64)).sum())
             exempt = oquant.boundary_distance(t) <= BOUNDARY_EPS
             n_codes += codes.size
             flips += int((mism & exempt).sum())
             bad += int((mism & ~exempt).sum())
-    return CodeReport(n_codes, flips, bad, n_groups, ex_groups, bad_groups)
+    return CodeReport(n_codes, flips, bad, n_groups, ex_groups, bad_groups, changed)
 
 
 def assert_codes_ok(rep: CodeReport, what=""):
     assert rep.bad_codes == 0, f"{what}: {rep.bad_codes} non-exempt code mismatches ({rep})"
     assert rep.bad_groups == 0, f"{what}: {rep.bad_groups} scale/zero mismatches away from f16 midpoints ({rep})"
     assert rep.exempt_flips <= FLIP_BUDGET * rep.n_codes, f"{what}: too many boundary flips ({rep})"
+    assert rep.changed_codes <= FLIP_BUDGET * rep.n_codes, f"{what}: too many codes differ from the oracle's ({rep})"
+    assert rep.exempt_groups <= GROUP_BUDGET * rep.n_groups, f"{what}: too many scale/zero midpoint groups ({rep})"

@@ -28,7 +28,7 @@ pytestmark = pytest.mark.gpu
 CALIB_ROWS = 1024  # the rotation is an input of both sides; its calibration size does not matter here
 
 
-def _run(name, sample_seqs, n_code_rows=2048, seed=0):
+def _run(name, sample_seqs, n_code_rows=2048, seed=0, splits=(0,), stale=False):
     w = synth.WORKLOADS[name]
     lens = synth.context_lengths(w)
     if sample_seqs == "all":
@@ -37,6 +37,8 @@ def _run(name, sample_seqs, n_code_rows=2048, seed=0):
     inp = synth.decode_inputs(w, draw_seqs=sample_seqs)
     rot = gh.oracle_rotation(w, n_rows=CALIB_ROWS)
     gc = gh.alloc_cache(inp, rot)
+    if stale:  # recycled pages: random bytes and NaN/infinity patterns wherever the fill does not write
+        gh.fill_stale(gc, seed=seed)
     rows = synth.middle_rows(inp)
     print(f"[fullsize {name}] quantize_append rows={len(rows[0])}", flush=True)
     gh.gpu_fill(inp, rot, gc, rows)
@@ -79,10 +81,8 @@ def _run(name, sample_seqs, n_code_rows=2048, seed=0):
         print(rep2, flush=True)
         gh.assert_codes_ok(rep2, name + " leaving rows")
 
-    # decode (all sequences on the GPU), checked on the sampled ones
-    print(f"[fullsize {name}] decode", flush=True)
-    got = gh.gpu_decode(inp, gc, split_pages=0)
-    assert np.isfinite(got).all()
+    # decode (all sequences on the GPU), checked on the sampled ones, for
+    # each work split (0: the automatic one the bench uses)
     int2 = olayout.Int2Pool(inp.n_int2_pages, w.n_kv_heads, w.d, int2_bytes)
     bf = olayout.Bf16Pool(inp.n_bf16_pages, w.n_kv_heads, w.d, gc.bf16.cpu().numpy().view(np.uint16))
     from oracle import attention as oatt
@@ -90,9 +90,13 @@ def _run(name, sample_seqs, n_code_rows=2048, seed=0):
     q = synth.bf16_bits_to_f32(inp.q[sb]).astype(np.float64)
     ref = oatt.decode_attention(q, int2, bf, inp.seq_lens[sb], inp.bt_q[sb], inp.bt_h[sb], rot.r_k, rot.r_v,
                                 w.n_sink, w.n_recent)
-    err = gh.attention_errors(got[sb], ref)
-    print(f"[fullsize {name}] decode errors {err}", flush=True)
-    gh.assert_attention_close(got[sb], ref, name)
+    for split in splits:
+        print(f"[fullsize {name}] decode split_pages={split}", flush=True)
+        got = gh.gpu_decode(inp, gc, split_pages=split)
+        assert np.isfinite(got).all()
+        err = gh.attention_errors(got[sb], ref)
+        print(f"[fullsize {name}] decode split_pages={split} errors {err}", flush=True)
+        gh.assert_attention_close(got[sb], ref, f"{name} split_pages={split}")
 
 
 def test_qwen3_8b_b1_32k_bench_config():
@@ -100,19 +104,23 @@ def test_qwen3_8b_b1_32k_bench_config():
 
 
 def test_qwen3_8b_b28_ragged_shared_prefix():
-    _run("qwen3-8b-b28-ragged", [0, 13, 27])
+    # on recycled pools (stale bytes and NaN/infinity patterns outside the regions)
+    _run("qwen3-8b-b28-ragged", [0, 13, 27], stale=True)
 
 
 def test_qwen3_32b_b1_128k():
-    _run("qwen3-32b-b1-128k", "all", n_code_rows=1024)
+    # automatic split, then split-K over 64 (128 pages each) and 205 (40
+    # pages each) INT2 context chunks with the log-sum-exp merge
+    _run("qwen3-32b-b1-128k", "all", n_code_rows=1024, splits=(0, 128, 40))
 
 
 def test_qwen3_32b_b4_128k():
-    _run("qwen3-32b-b4-128k", [2], n_code_rows=1024)
+    # automatic split, then 64 INT2 chunks (128 pages) per (sequence, KV head)
+    _run("qwen3-32b-b4-128k", [2], n_code_rows=1024, splits=(0, 128))
 
 
 def test_gqa96_b64_ragged():
-    _run("gqa96-b64-ragged", [5, 40])
+    _run("gqa96-b64-ragged", [5, 40], stale=True)
 
 
 def test_prefill_8x8192_rows_per_sequence():

@@ -50,8 +50,8 @@ def test_quantize_append_tiny(tiny_rot):
     print(f"[quantize_append tiny] rows={len(rows[0])}", flush=True)
     gh.gpu_fill(inp, tiny_rot, gc, rows)
     torch.cuda.synchronize()
-    _, _, res, _ = gh.oracle_pools(inp, tiny_rot)
-    page, slot = _page_slot(inp, rows)
+    _, _, res, orows = gh.oracle_pools(inp, tiny_rot)
+    page, slot = _page_slot(inp, orows)
     rep = gh.compare_appended(gc.int2.cpu().numpy(), w, inp.n_int2_pages, res, page, slot)
     print(rep)
     gh.assert_codes_ok(rep, "tiny")
@@ -114,6 +114,51 @@ def test_quantize_append_large_inputs(tiny_rot):
     rep = gh.compare_appended(gc.int2.cpu().numpy(), w, inp.n_int2_pages, res, page, slot)
     print(rep)
     gh.assert_codes_ok(rep, "large inputs")
+
+
+def test_quantize_append_small_magnitude_rows(tiny_rot):
+    # more than 64 rows (the matrix-core kernel) where some rows are scaled
+    # down by powers of two (exact in bf16): their values fall below the f16
+    # normal range, so the kernel must rescale them before its f16 staging;
+    # the scale and zero of the smallest rows are f16 subnormals or zero
+    w = _tiny()
+    inp = synth.decode_inputs(w)
+    ms, mp, mr = synth.middle_rows(inp)
+    k = synth.bf16_bits_to_f32(inp.k_rows[mr]).astype(np.float64)
+    v = synth.bf16_bits_to_f32(inp.v_rows[mr]).astype(np.float64)
+    rng = np.random.default_rng(21)
+    rows = rng.permutation(len(ms))
+    exps = [-3, -5, -10, -14, -17, -20, -24, -30]
+    for j, r in enumerate(rows[:8 * 20]):
+        k[r] *= 2.0 ** exps[j % 8]
+        v[r] *= 2.0 ** exps[(j + 3) % 8]
+    kb, vb = synth.to_bf16_bits(k), synth.to_bf16_bits(v)
+    assert np.array_equal(synth.bf16_bits_to_f32(kb).astype(np.float64), k)  # the scaling was exact
+    gc = gh.alloc_cache(inp, tiny_rot)
+    print(f"[quantize_append small-magnitude rows] rows={len(ms)}", flush=True)
+    lib.quantize_append(gc.cache, gh.bits_to_dev_bf16(kb), gh.bits_to_dev_bf16(vb), gh.i32(ms), gh.i32(mp), gc.bt_q,
+                        gc.r_k, gc.r_v, tiny_rot.tau_k, tiny_rot.tau_v)
+    torch.cuda.synchronize()
+    pool = olayout.Int2Pool(inp.n_int2_pages, w.n_kv_heads, w.d)
+    res = ocache.quantize_append(pool, kb, vb, ms, mp, inp.bt_q, tiny_rot.r_k, tiny_rot.r_v, tiny_rot.tau_k,
+                                 tiny_rot.tau_v, olayout.bf16_to_f64)
+    page, slot = _page_slot(inp, (ms, mp, mr))
+    rep = gh.compare_appended(gc.int2.cpu().numpy(), w, inp.n_int2_pages, res, page, slot)
+    print(rep)
+    gh.assert_codes_ok(rep, "small-magnitude rows")
+    # the same rows through the few-row kernel (float32 products)
+    sel = rows[:64]
+    gc2 = gh.alloc_cache(inp, tiny_rot)
+    lib.quantize_append(gc2.cache, gh.bits_to_dev_bf16(kb[sel]), gh.bits_to_dev_bf16(vb[sel]), gh.i32(ms[sel]),
+                        gh.i32(mp[sel]), gc2.bt_q, gc2.r_k, gc2.r_v, tiny_rot.tau_k, tiny_rot.tau_v)
+    torch.cuda.synchronize()
+    res2 = ocache.quantize_append(olayout.Int2Pool(inp.n_int2_pages, w.n_kv_heads, w.d), kb[sel], vb[sel], ms[sel],
+                                  mp[sel], inp.bt_q, tiny_rot.r_k, tiny_rot.r_v, tiny_rot.tau_k, tiny_rot.tau_v,
+                                  olayout.bf16_to_f64)
+    page2, slot2 = _page_slot(inp, (ms[sel], mp[sel], mr[sel]))
+    rep2 = gh.compare_appended(gc2.int2.cpu().numpy(), w, inp.n_int2_pages, res2, page2, slot2)
+    print(rep2)
+    gh.assert_codes_ok(rep2, "small-magnitude rows, few-row kernel")
 
 
 def test_quantize_append_scattered_single_rows(tiny_rot):
@@ -376,6 +421,68 @@ def test_decode_region_layouts(S, W):
         got = gh.gpu_decode(inp, gc, split_pages=split)
         print(gh.attention_errors(got, ref))
         gh.assert_attention_close(got, ref, f"regions S={S} W={W} split={split}")
+
+
+@pytest.mark.parametrize("all_raw", [False, True])
+def test_decode_on_recycled_pools(tiny_rot, all_raw):
+    # pools holding random bytes and NaN/infinity patterns everywhere the fill
+    # does not write: sink slots of the first INT2 page, the middle tokens of
+    # BF16 pages, BF16 page tails, whole pages past each length; per-unit
+    # items (fixed splits) and balanced slices (many units)
+    lens = np.array([512, 1, 17, 36, 37, 100, 333, 479, 480, 481, 0, 250])
+    kw = dict(batch=len(lens))
+    if all_raw:
+        kw.update(n_sink=100000, n_recent=0)
+    w = _tiny(**kw)
+    inp = synth.decode_inputs(w, seq_lens=lens, spare_pages=7)
+    gc = gh.alloc_cache(inp, tiny_rot)
+    gh.fill_stale(gc, seed=int(all_raw))
+    gh.gpu_fill(inp, tiny_rot, gc)
+    int2, bf, _, _ = gh.oracle_pools(inp, tiny_rot)
+    ref = gh.oracle_decode(inp, tiny_rot, int2, bf)
+    for split in (0, 8, 16):
+        print(f"[decode recycled pools all_raw={all_raw} split={split}]", flush=True)
+        got = gh.gpu_decode(inp, gc, split_pages=split, all_raw=all_raw)
+        for b, L in enumerate(lens):
+            if L == 0:
+                assert np.all(got[b] == 0)
+            else:
+                gh.assert_attention_close(got[b], ref[b], f"recycled pools split {split} len {L}")
+    # many units: the balanced-slice kernel over the same stale pools
+    lens2 = np.random.default_rng(31).integers(1, 600, size=70)
+    w2 = _tiny(**{**kw, "batch": len(lens2)})
+    inp2 = synth.decode_inputs(w2, seq_lens=lens2)
+    gc2 = gh.alloc_cache(inp2, tiny_rot)
+    gh.fill_stale(gc2, seed=2 + int(all_raw))
+    gh.gpu_fill(inp2, tiny_rot, gc2)
+    int2b, bfb, _, _ = gh.oracle_pools(inp2, tiny_rot)
+    ref2 = gh.oracle_decode(inp2, tiny_rot, int2b, bfb)
+    print(f"[decode recycled pools, balanced slices all_raw={all_raw}]", flush=True)
+    got2 = gh.gpu_decode(inp2, gc2, all_raw=all_raw)
+    for b in range(len(lens2)):
+        gh.assert_attention_close(got2[b], ref2[b], f"recycled pools balanced slices seq {b}")
+
+
+@pytest.mark.parametrize("hq,hkv,d,L,split", [(4, 1, 64, 9000, 8), (8, 1, 128, 32100, 8), (4, 2, 128, 20000, 8)])
+def test_decode_many_chunks_multipass_merge(hq, hkv, d, L, split):
+    # more than 32 records per (sequence, KV head): 70 to 252 INT2 chunks, so
+    # the merge runs several weight passes and value rounds (grouped columns
+    # for G = 4, one column per query for G = 8), against the oracle
+    w = synth.Workload("chunks", 6, 1, hq, hkv, d, 4, 128, 512, ("fixed", L, L))
+    rot = gh.oracle_rotation(w, n_rows=512)
+    inp = synth.decode_inputs(w)
+    gc = gh.alloc_cache(inp, rot)
+    gh.fill_stale(gc, seed=5)
+    gh.gpu_fill(inp, rot, gc)
+    int2, bf, _, _ = gh.oracle_pools(inp, rot)
+    ref = gh.oracle_decode(inp, rot, int2, bf)
+    n_items = 1 + (L + 15) // 16 // split
+    print(f"[decode many chunks hq={hq} d={d} L={L} split={split}: about {n_items} records]", flush=True)
+    got = gh.gpu_decode(inp, gc, split_pages=split)
+    print(gh.attention_errors(got, ref))
+    gh.assert_attention_close(got, ref, f"{n_items} chunks")
+    auto = gh.gpu_decode(inp, gc)
+    gh.assert_attention_close(auto, ref, "automatic split")
 
 
 def test_invariances_tables_splits_determinism(tiny_rot):

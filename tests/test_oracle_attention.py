@@ -202,3 +202,35 @@ def test_step_updates_rebuild_the_batch_fill(S, W):
     for x, y in zip(bf.read(page_h, slot_h, 0), bff.read(page_h, slot_h, 0)):
         assert np.array_equal(x, y)
     assert len(mid) == L - W - S and len(raw) == S + W
+
+
+def test_region_split_hand_values():
+    # the tiny workload's 512 tokens are 4 sink + 476 middle + 32 recent; a
+    # sequence no longer than sink + recent has no middle; a short one is all sink
+    from oracle.attention import regions
+    assert regions(512, 4, 32) == ((0, 4), (4, 480), (480, 512))
+    assert regions(36, 4, 32) == ((0, 4), (4, 4), (4, 36))
+    assert regions(37, 4, 32) == ((0, 4), (4, 5), (5, 37))
+    assert regions(3, 4, 32) == ((0, 3), (4, 4), (4, 3))
+    assert regions(100, 0, 0) == ((0, 0), (0, 100), (100, 100))
+
+
+def test_fill_rows_cover_each_slot_once_and_match_the_generator():
+    # the oracle's fill split (sink/recent to BF16, the rest to INT2, shared
+    # prefix slots written once) against hand counts and against the
+    # generator's own row lists, which drive the GPU fills in the tests
+    from int2_rotated_kv_oscar_amd import synth
+    from oracle.cache import fill_rows
+    (ms, mp), (hs, hp) = fill_rows([1300, 1500, 1200], 4, 128, shared_prefix=1024)
+    assert len(ms) == 1020 + (1300 - 128 - 1024) + (1500 - 128 - 1024) + (1200 - 128 - 1024)
+    assert len(hs) == 4 + 3 * 128
+    assert set(zip(ms.tolist(), mp.tolist())).isdisjoint(zip(hs.tolist(), hp.tolist()))
+    w = synth.Workload(**{**synth.WORKLOADS["qwen3-8b-b28-ragged"].__dict__, "batch": 3, "name": "small-ragged"})
+    inp = synth.decode_inputs(w, seq_lens=np.array([1300, 1500, 1200]))
+    gs, gp, _ = synth.middle_rows(inp)
+    g2s, g2p, _ = synth.bf16_rows(inp)
+    assert np.array_equal(gs, ms) and np.array_equal(gp, mp)
+    assert np.array_equal(g2s, hs) and np.array_equal(g2p, hp)
+    (ms1, mp1), (hs1, hp1) = fill_rows([0, 1, 40, 41], 4, 32)
+    assert mp1.tolist() == [4, 5, 6, 7, 4, 5, 6, 7, 8] and ms1.tolist() == [2] * 4 + [3] * 5
+    assert len(hs1) == 1 + 36 + 36
