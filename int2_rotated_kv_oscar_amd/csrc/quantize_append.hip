@@ -75,6 +75,17 @@ __device__ __forceinline__ uint32_t code_bits(float v, float z, float inv, float
   return uint32_t(min(max(b, int(kMagicBits)), int(kMagicBits + 3u)));
 }
 
+// r / 3: the product with 1/3 refined once with its exact residual, so that
+// a quotient representable in float32 comes out exactly.  With coarse
+// rotated values (a Hadamard or identity rotation of bf16 rows) the range is
+// often three times an f16 rounding midpoint; the exact quotient then rounds
+// to even on the way to f16, as the definition's real-number division does.
+__device__ __forceinline__ float div3(float r) {
+  constexpr float kThird = 1.0f / 3.0f;
+  const float s0 = r * kThird;
+  return __builtin_fmaf(__builtin_fmaf(-3.0f, s0, r), kThird, s0);
+}
+
 // Reduction over the four lanes l16 + 16q of a row: the minimum of mn and the
 // maximum of mx, both computed in every lane with three lane swaps (the lower
 // half of the wave carries the minima, the upper half the negated maxima).
@@ -296,7 +307,7 @@ __device__ void qa_tiles(const QAParams& p, int h, QAShared<D, ONE>& sh) {
     row_min_max(mn, mx);
     // s = (max - min) / 3 and z = min in true units (F is a power of two:
     // the scalings are exact), rounded to f16; codes against the f16 values
-    const uint32_t s16 = f16_bits((mx - mn) * (F * (1.0f / 3.0f)));
+    const uint32_t s16 = f16_bits(div3(mx - mn) * F);
     const uint32_t z16 = f16_bits(mn * F);
     const float sf = f16_to_f32(s16);
     const float inv = sf == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(sf);  // s16 = 0: every code is 0
@@ -585,7 +596,7 @@ __global__ __launch_bounds__(kRowThreads) void quantize_rows_kernel(QAParams p) 
       mn = fminf(mn, __shfl_xor(mn, m, 64));
       mx = fmaxf(mx, __shfl_xor(mx, m, 64));
     }
-    const uint32_t s16 = f16_bits((mx - mn) / 3.0f);
+    const uint32_t s16 = f16_bits(div3(mx - mn));
     const uint32_t z16 = f16_bits(mn);
     const float sf = f16_to_f32(s16), zf = f16_to_f32(z16);
     int code = 0;

@@ -153,6 +153,25 @@ def oracle_decode(inp: synth.DecodeInputs, rot: Rotation, int2: olayout.Int2Pool
                                  inp.w.n_recent)
 
 
+def oracle_decode_gpu_pages(inp: synth.DecodeInputs, rot: Rotation, gc: GpuCache, seq_lens=None) -> np.ndarray:
+    """The oracle's decode over the very pages the GPU wrote (read back), so a
+    code or scale the GPU legitimately rounded the other way at an exempt
+    boundary is decoded the same way on both sides."""
+    w = inp.w
+    int2 = olayout.Int2Pool(inp.n_int2_pages, w.n_kv_heads, w.d, gc.int2.cpu().numpy())
+    bf = olayout.Bf16Pool(inp.n_bf16_pages, w.n_kv_heads, w.d, gc.bf16.cpu().numpy().view(np.uint16))
+    return oracle_decode(inp, rot, int2, bf, seq_lens=seq_lens)
+
+
+def check_fill(inp: synth.DecodeInputs, rot: Rotation, gc: GpuCache, what=""):
+    """Codes and scale/zero of every middle row the GPU fill wrote, against the oracle's fill."""
+    _, _, res, (ms, mp, _) = oracle_pools(inp, rot)
+    page = inp.bt_q[ms, mp // 16].astype(np.int64)
+    rep = compare_appended(gc.int2.cpu().numpy(), inp.w, inp.n_int2_pages, res, page, (mp % 16).astype(np.int64))
+    assert_codes_ok(rep, what)
+    return rep
+
+
 def bf16_ulp(x: np.ndarray) -> np.ndarray:
     """Spacing of bfloat16 numbers at |x| (8 significant bits)."""
     ax = np.maximum(np.abs(np.asarray(x, np.float64)), 2.0 ** -126)

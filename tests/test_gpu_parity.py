@@ -438,8 +438,9 @@ def test_decode_on_recycled_pools(tiny_rot, all_raw):
     gc = gh.alloc_cache(inp, tiny_rot)
     gh.fill_stale(gc, seed=int(all_raw))
     gh.gpu_fill(inp, tiny_rot, gc)
-    int2, bf, _, _ = gh.oracle_pools(inp, tiny_rot)
-    ref = gh.oracle_decode(inp, tiny_rot, int2, bf)
+    if not all_raw:
+        gh.check_fill(inp, tiny_rot, gc, "recycled pools fill")
+    ref = gh.oracle_decode_gpu_pages(inp, tiny_rot, gc)
     for split in (0, 8, 16):
         print(f"[decode recycled pools all_raw={all_raw} split={split}]", flush=True)
         got = gh.gpu_decode(inp, gc, split_pages=split, all_raw=all_raw)
@@ -448,6 +449,12 @@ def test_decode_on_recycled_pools(tiny_rot, all_raw):
                 assert np.all(got[b] == 0)
             else:
                 gh.assert_attention_close(got[b], ref[b], f"recycled pools split {split} len {L}")
+    # stale bytes outside the regions must not change a single output bit
+    clean = gh.alloc_cache(inp, tiny_rot)
+    gh.gpu_fill(inp, tiny_rot, clean)
+    for split in (0, 8):
+        assert np.array_equal(gh.gpu_decode(inp, clean, split_pages=split, all_raw=all_raw),
+                              gh.gpu_decode(inp, gc, split_pages=split, all_raw=all_raw)), "stale bytes changed the output"
     # many units: the balanced-slice kernel over the same stale pools
     lens2 = np.random.default_rng(31).integers(1, 600, size=70)
     w2 = _tiny(**{**kw, "batch": len(lens2)})
@@ -455,12 +462,14 @@ def test_decode_on_recycled_pools(tiny_rot, all_raw):
     gc2 = gh.alloc_cache(inp2, tiny_rot)
     gh.fill_stale(gc2, seed=2 + int(all_raw))
     gh.gpu_fill(inp2, tiny_rot, gc2)
-    int2b, bfb, _, _ = gh.oracle_pools(inp2, tiny_rot)
-    ref2 = gh.oracle_decode(inp2, tiny_rot, int2b, bfb)
+    ref2 = gh.oracle_decode_gpu_pages(inp2, tiny_rot, gc2)
     print(f"[decode recycled pools, balanced slices all_raw={all_raw}]", flush=True)
     got2 = gh.gpu_decode(inp2, gc2, all_raw=all_raw)
     for b in range(len(lens2)):
         gh.assert_attention_close(got2[b], ref2[b], f"recycled pools balanced slices seq {b}")
+    clean2 = gh.alloc_cache(inp2, tiny_rot)
+    gh.gpu_fill(inp2, tiny_rot, clean2)
+    assert np.array_equal(gh.gpu_decode(inp2, clean2, all_raw=all_raw), got2), "stale bytes changed the output"
 
 
 @pytest.mark.parametrize("hq,hkv,d,L,split", [(4, 1, 64, 9000, 8), (8, 1, 128, 32100, 8), (4, 2, 128, 20000, 8)])
@@ -474,8 +483,8 @@ def test_decode_many_chunks_multipass_merge(hq, hkv, d, L, split):
     gc = gh.alloc_cache(inp, rot)
     gh.fill_stale(gc, seed=5)
     gh.gpu_fill(inp, rot, gc)
-    int2, bf, _, _ = gh.oracle_pools(inp, rot)
-    ref = gh.oracle_decode(inp, rot, int2, bf)
+    gh.check_fill(inp, rot, gc, "many chunks fill")
+    ref = gh.oracle_decode_gpu_pages(inp, rot, gc)
     n_items = 1 + (L + 15) // 16 // split
     print(f"[decode many chunks hq={hq} d={d} L={L} split={split}: about {n_items} records]", flush=True)
     got = gh.gpu_decode(inp, gc, split_pages=split)
