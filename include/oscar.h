@@ -382,6 +382,28 @@ oscar_status oscar_paged_decode_attn_bf16(const oscar_cache* cache, const void* 
                                           void* workspace, size_t workspace_bytes,
                                           void* out, void* stream);
 
+/* The same decode for callers that cannot allocate device memory (code
+ * under HIP graph capture, serving loops that must not call the allocator,
+ * harnesses that forbid it): no workspace argument; the arrival counters and
+ * per-workgroup records live in one 32 MiB array inside the library, one copy
+ * per device, held until the process ends.  The first call on a device looks
+ * the array up and clears its counters with a kernel on `stream`.
+ * Limits: at most 65536 (sequence, KV head) units and 32512 KiB of records
+ * (oscar_decode_workspace_bytes minus its counter part, for the same
+ * arguments); beyond that OSCAR_ERR_WORKSPACE, nothing launched.  Every call
+ * on a device shares that array: calls that overlap in time on one device
+ * (two streams, two threads) race and return wrong values; a call that does
+ * not complete can leave counters non-zero for the rest of the process.
+ * Outputs are bit-identical to oscar_paged_decode_attn for the same
+ * arguments.  No hipMalloc or other allocation is made. */
+oscar_status oscar_paged_decode_attn_noalloc(const oscar_cache* cache, const void* q,
+                                             int32_t batch, int32_t n_q_heads,
+                                             const int32_t* seq_lens, int32_t max_seq_len,
+                                             const int32_t* bt_q, const int32_t* bt_h,
+                                             int32_t max_pages, const float* r_k,
+                                             const float* r_v, float sm_scale,
+                                             int32_t split_pages, void* out, void* stream);
+
 /* ------------------------------------------------------------------------ *
  * Measurement context (not part of the method): reads `bytes` bytes of the
  * device buffer `buf` once, streaming, and writes nothing back (`sink`, a

@@ -27,7 +27,7 @@ EXPORTS = [
     "oscar_build_fixed_rotation", "oscar_int2_page_bytes", "oscar_bf16_page_bytes", "oscar_quantize_append",
     "oscar_write_bf16", "oscar_decode_step_update", "oscar_decode_workspace_bytes", "oscar_calib_gram",
     "oscar_build_rotation_from_targets", "oscar_decode_workspace_init", "oscar_paged_decode_attn",
-    "oscar_paged_decode_attn_bf16", "oscar_bw_probe_read",
+    "oscar_paged_decode_attn_bf16", "oscar_bw_probe_read", "oscar_paged_decode_attn_noalloc",
 ]
 
 
@@ -86,6 +86,8 @@ def load(path: str = LIB_PATH):
         "oscar_paged_decode_attn_bf16": (_STATUS, [ctypes.POINTER(OscarCache), _P, _I32, _I32, _P, _I32, _P, _I32,
                                                    _F32, _I32, _P, _SZ, _P, _P]),
         "oscar_bw_probe_read": (_STATUS, [_P, _SZ, _P, _P]),
+        "oscar_paged_decode_attn_noalloc": (_STATUS, [ctypes.POINTER(OscarCache), _P, _I32, _I32, _P, _I32, _P, _P,
+                                                      _I32, _P, _P, _F32, _I32, _P, _P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -265,6 +267,16 @@ def paged_decode_attn_bf16(cache: OscarCache, q, seq_lens, max_seq_len: int, bt_
                                                _dptr(bt_h), bt_h.shape[1], sc, split_pages, _dptr(workspace),
                                                workspace.numel() * workspace.element_size(), _dptr(out),
                                                _stream(stream)))
+
+
+def paged_decode_attn_noalloc(cache: OscarCache, q, seq_lens, max_seq_len: int, bt_q, bt_h, r_k, r_v, out,
+                              sm_scale: Optional[float] = None, split_pages: int = 0, stream=None):
+    """As paged_decode_attn, with the library's built-in device scratch instead of a workspace."""
+    B, hq, d = q.shape
+    sc = 1.0 / np.sqrt(d) if sm_scale is None else sm_scale
+    _check(load().oscar_paged_decode_attn_noalloc(ctypes.byref(cache), _dptr(q), B, hq, _dptr(seq_lens),
+                                                  max_seq_len, _dptr(bt_q), _dptr(bt_h), bt_h.shape[1], _dptr(r_k),
+                                                  _dptr(r_v), sc, split_pages, _dptr(out), _stream(stream)))
 
 
 def bw_probe_read(buf, sink, stream=None):
