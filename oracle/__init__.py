@@ -16,8 +16,9 @@ seeded input generator ``int2_rotated_kv_oscar_amd.synth``.
 
 Modules: ``rotation`` (calibration targets, eigenbases, Hadamard, bit reversal,
 composite rotation, clip threshold), ``quant`` (rotate, clip, asymmetric INT2
-per token and group), ``layout`` (INT2 and BF16 page images), ``attention``
-(decode attention over the mixed cache, the split/merge formula, plain
-attention).  Every function is pinned by ``tests/test_oracle_*.py`` against
+per token and group, and the 16-level INT4 variant), ``layout`` (INT2, INT4
+and BF16 page images), ``cache`` (filling pages, the decode-step update),
+``attention`` (decode attention over the mixed cache, chunked-prefill
+"extend" attention over it, the split/merge formula, plain attention).  Every function is pinned by ``tests/test_oracle_*.py`` against
 closed forms, invariants, brute force or an independent library routine.
 """

@@ -63,6 +63,46 @@ def sequence_kv(int2: Int2Pool, bf16: Bf16Pool, bt_q_row, bt_h_row, L: int, S: i
     return raw_idx, k_raw, v_raw, mid_idx, k_rot, v_rot
 
 
+def extend_attention(q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, pool, bf16: Bf16Pool, cu, cache_lens,
+                     bt_q, bt_h, r_k: np.ndarray, r_v: np.ndarray, S: int, W: int,
+                     scale: float | None = None) -> np.ndarray:
+    """Chunked-prefill ("extend") attention over the mixed paged cache, fp64.
+
+    [TS] 2.2.B "Kernel Integration" (paged attention with prefix caching) and
+    [TS] 3: a request whose prefix is already cached prefills only its new
+    tokens, which attend the cached prefix through its pages.  Reading: the
+    new rows of sequence b (rows cu[b] .. cu[b+1] - 1 of q, k_new, v_new) sit
+    at positions P + i, P = cache_lens[b]; row i attends the cached prefix
+    [0, P), whose regions are those of a length-P cache (sink and recent raw
+    from BF16 pages, the middle decoded from the quantized pages and rotated
+    back), and the new rows 0..i (causal), raw.  ``pool`` is an Int2Pool or an
+    Int4Pool.  q float64 [T, H_q, d]; k_new, v_new float64 [T, H_kv, d];
+    returns float64 [T, H_q, d].
+    """
+    T, hq, d = q.shape
+    hkv = k_new.shape[1]
+    G = hq // hkv
+    sc = 1.0 / np.sqrt(d) if scale is None else scale
+    out = np.zeros((T, hq, d))
+    cu = np.asarray(cu, np.int64)
+    for b in range(len(cu) - 1):
+        r0, r1 = int(cu[b]), int(cu[b + 1])
+        P = int(cache_lens[b])
+        for h in range(hkv):
+            if P > 0:
+                _, k_raw, v_raw, _, k_rot, v_rot = sequence_kv(pool, bf16, bt_q[b], bt_h[b], P, S, W, h)
+                kc = np.concatenate([k_raw, k_rot @ np.asarray(r_k[h], np.float64).T])
+                vc = np.concatenate([v_raw, v_rot @ np.asarray(r_v[h], np.float64).T])
+            else:
+                kc = vc = np.zeros((0, d))
+            for i in range(r1 - r0):
+                k = np.concatenate([kc, np.asarray(k_new[r0:r0 + i + 1, h], np.float64)])
+                v = np.concatenate([vc, np.asarray(v_new[r0:r0 + i + 1, h], np.float64)])
+                out[r0 + i, h * G:(h + 1) * G] = softmax_attention(np.asarray(q[r0 + i, h * G:(h + 1) * G], np.float64),
+                                                                   k, v, sc)
+    return out
+
+
 def decode_attention(q: np.ndarray, int2: Int2Pool, bf16: Bf16Pool, seq_lens, bt_q, bt_h,
                      r_k: np.ndarray, r_v: np.ndarray, S: int, W: int, scale: float | None = None) -> np.ndarray:
     """Output [B, H_q, d] float64: plain attention over the decoded cache with

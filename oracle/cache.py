@@ -7,7 +7,7 @@ import dataclasses
 import numpy as np
 
 from .attention import regions
-from .layout import Bf16Pool, Int2Pool, bf16_to_f64
+from .layout import Bf16Pool, Int2Pool, Int4Pool, bf16_to_f64
 from .quant import QuantRows, quantize_rows
 
 PAGE = 16
@@ -20,17 +20,18 @@ class AppendResult:
     v: list
 
 
-def quantize_append(pool: Int2Pool, k_bits: np.ndarray, v_bits: np.ndarray, row_seq, row_pos, bt_q,
-                    r_k, r_v, tau_k: float, tau_v: float, bf16_to_f64) -> AppendResult:
-    """Quantize rows (bf16 bits [n, H_kv, d]) and store them in their slots."""
+def quantize_append(pool, k_bits: np.ndarray, v_bits: np.ndarray, row_seq, row_pos, bt_q,
+                    r_k, r_v, tau_k: float, tau_v: float, bf16_to_f64, bits: int = 2) -> AppendResult:
+    """Quantize rows (bf16 bits [n, H_kv, d]) and store them in their slots
+    (an Int2Pool with bits = 2, an Int4Pool with bits = 4)."""
     row_seq = np.asarray(row_seq, np.int64)
     row_pos = np.asarray(row_pos, np.int64)
     page = np.asarray(bt_q)[row_seq, row_pos // PAGE]
     slot = row_pos % PAGE
     kr, vr = [], []
     for h in range(pool.hkv):
-        qk = quantize_rows(bf16_to_f64(k_bits[:, h, :]), np.asarray(r_k[h], np.float64), float(tau_k))
-        qv = quantize_rows(bf16_to_f64(v_bits[:, h, :]), np.asarray(r_v[h], np.float64), float(tau_v))
+        qk = quantize_rows(bf16_to_f64(k_bits[:, h, :]), np.asarray(r_k[h], np.float64), float(tau_k), bits)
+        qv = quantize_rows(bf16_to_f64(v_bits[:, h, :]), np.asarray(r_v[h], np.float64), float(tau_v), bits)
         pool.write(page, slot, h, qk.codes, qv.codes, qk.s16, qk.z16, qv.s16, qv.z16)
         kr.append(qk)
         vr.append(qv)
@@ -68,19 +69,19 @@ def fill_rows(seq_lens, n_sink: int, n_recent: int, shared_prefix: int = 0):
     return (cat(ms), cat(mp)), (cat(hs), cat(hp))
 
 
-def build_from_inputs(inp, r_k, r_v, tau_k: float, tau_v: float):
+def build_from_inputs(inp, r_k, r_v, tau_k: float, tau_v: float, bits: int = 2):
     """Oracle page images for a generated decode batch: every middle row
     quantized into its INT2 slot, every sink/recent row stored in its BF16
     slot (the split into regions taken here, by ``fill_rows``).  Returns
     (int2 pool, bf16 pool, AppendResult, middle row triple (seq, pos, row))."""
     w = inp.w
-    int2 = Int2Pool(inp.n_int2_pages, w.n_kv_heads, w.d)
+    int2 = (Int2Pool if bits == 2 else Int4Pool)(inp.n_int2_pages, w.n_kv_heads, w.d)
     bf = Bf16Pool(inp.n_bf16_pages, w.n_kv_heads, w.d)
     (ms, mp), (hs, hp) = fill_rows(inp.seq_lens, w.n_sink, w.n_recent, w.shared_prefix)
     mr = np.array([inp.row_of[b][t] for b, t in zip(ms, mp)], np.int64)
     hr = np.array([inp.row_of[b][t] for b, t in zip(hs, hp)], np.int64)
     res = quantize_append(int2, inp.k_rows[mr], inp.v_rows[mr], ms, mp, inp.bt_q, r_k, r_v, tau_k, tau_v,
-                          bf16_to_f64)
+                          bf16_to_f64, bits)
     write_bf16(bf, inp.k_rows[hr], inp.v_rows[hr], hs, hp, inp.bt_h)
     return int2, bf, res, (ms, mp, mr)
 

@@ -124,6 +124,59 @@ class Int2Pool:
         return tuple(out)
 
 
+def int4_head_bytes(d: int) -> int:
+    return 20 * d
+
+
+class Int4Pool:
+    """INT4 page images, uint8 [n_pages, H_kv, 20 d].  One page-head holds,
+    one after the other: K codes [16 slots][d/2] bytes, V codes [16][d/2]
+    (channel 2i in the low nibble of byte i, channel 2i + 1 in the high
+    nibble), then f16 K scales [16][n_g], K zeros [16][n_g], V scales
+    [16][n_g], V zeros [16][n_g].  Every slot owns its bytes."""
+
+    def __init__(self, n_pages: int, n_kv_heads: int, d: int, data: np.ndarray | None = None):
+        self.d, self.hkv, self.n_pages = d, n_kv_heads, n_pages
+        nb = int4_head_bytes(d)
+        if data is None:
+            data = np.zeros((n_pages, n_kv_heads, nb), np.uint8)
+        self.data = np.ascontiguousarray(data, dtype=np.uint8).reshape(n_pages, n_kv_heads, nb)
+        ng = d // GROUP
+        self.off_codes = (0, PAGE * d // 2)
+        base = PAGE * d
+        self.off_sz = tuple(base + 2 * PAGE * ng * i for i in range(4))
+
+    def _codes(self, area: int) -> np.ndarray:
+        o = self.off_codes[area]
+        return self.data[:, :, o:o + PAGE * self.d // 2].reshape(self.n_pages, self.hkv, PAGE, self.d // 2)
+
+    def _halves(self, area: int) -> np.ndarray:
+        ng = self.d // GROUP
+        o = self.off_sz[area]
+        return self.data[:, :, o:o + 2 * PAGE * ng].view(np.float16).reshape(self.n_pages, self.hkv, PAGE, ng)
+
+    def write(self, page, slot, head: int, codes_k, codes_v, ks, kz, vs, vz):
+        page = np.asarray(page, np.int64); slot = np.asarray(slot, np.int64)
+        for area, codes in ((0, codes_k), (1, codes_v)):
+            c = np.asarray(codes, np.uint8) & 15
+            self._codes(area)[page, head, slot] = c[:, 0::2] | (c[:, 1::2] << 4)
+        for area, vals in ((0, ks), (1, kz), (2, vs), (3, vz)):
+            self._halves(area)[page, head, slot] = np.asarray(vals, np.float16)
+
+    def read(self, page, slot, head: int):
+        page = np.asarray(page, np.int64); slot = np.asarray(slot, np.int64)
+        out = []
+        for area in (0, 1):
+            b = self._codes(area)[page, head, slot]
+            c = np.empty((len(page), self.d), np.uint8)
+            c[:, 0::2] = b & 15
+            c[:, 1::2] = b >> 4
+            out.append(c)
+        for area in range(4):
+            out.append(self._halves(area)[page, head, slot].copy())
+        return tuple(out)
+
+
 class Bf16Pool:
     """uint16 (bf16 bits) [n_pages, H_kv, 32 d]: K [16][d] then V [d][16]."""
 

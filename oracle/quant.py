@@ -6,6 +6,10 @@ groups of 32 consecutive rotated channels per token, zero = group minimum,
 scale = range / 3, scale and zero stored as f16 (round-half-to-even) and codes
 computed against the stored f16 values, codes rounded half-to-even and clamped
 to [0, 3], code 0 when the stored scale is 0.
+
+The INT4 cache variant ([TS] 4 "Scalability": the INT4 KV baseline OSCAR's
+capacity is compared with) is the same quantizer with 16 levels: scale =
+range / 15, codes clamped to [0, 15] (``bits=4``).
 """
 from __future__ import annotations
 
@@ -33,13 +37,20 @@ def rotate_clip(x: np.ndarray, r: np.ndarray, tau: float) -> np.ndarray:
     return np.clip(y, -tau, tau)
 
 
-def quantize_rotated(y: np.ndarray) -> QuantRows:
+def levels(bits: int) -> int:
+    """Largest code of a ``bits``-bit asymmetric quantizer (3 for INT2, 15 for INT4)."""
+    assert bits in (2, 4)
+    return (1 << bits) - 1
+
+
+def quantize_rotated(y: np.ndarray, bits: int = 2) -> QuantRows:
     n, d = y.shape
     ng = d // GROUP
+    top = levels(bits)
     yg = y.reshape(n, ng, GROUP)
     mn = yg.min(axis=2)
     mx = yg.max(axis=2)
-    s = (mx - mn) / 3.0
+    s = (mx - mn) / float(top)
     z = mn
     s16 = s.astype(np.float16)
     z16 = z.astype(np.float16)
@@ -47,12 +58,12 @@ def quantize_rotated(y: np.ndarray) -> QuantRows:
     z64 = z16.astype(np.float64)[:, :, None]
     with np.errstate(divide="ignore", invalid="ignore"):
         t = np.where(s64 != 0.0, (yg - z64) / s64, np.nan)
-    codes = np.where(s64 != 0.0, np.clip(np.rint(np.nan_to_num(t)), 0, 3), 0).astype(np.uint8)
+    codes = np.where(s64 != 0.0, np.clip(np.rint(np.nan_to_num(t)), 0, top), 0).astype(np.uint8)
     return QuantRows(codes.reshape(n, d), s16, z16, t.reshape(n, d), s, z, y)
 
 
-def quantize_rows(x: np.ndarray, r: np.ndarray, tau: float) -> QuantRows:
-    return quantize_rotated(rotate_clip(x, r, tau))
+def quantize_rows(x: np.ndarray, r: np.ndarray, tau: float, bits: int = 2) -> QuantRows:
+    return quantize_rotated(rotate_clip(x, r, tau), bits)
 
 
 def dequantize(codes: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.ndarray:
@@ -63,9 +74,9 @@ def dequantize(codes: np.ndarray, s16: np.ndarray, z16: np.ndarray) -> np.ndarra
     return (c * s16.astype(np.float64)[:, :, None] + z16.astype(np.float64)[:, :, None]).reshape(n, d)
 
 
-def boundary_distance(t: np.ndarray) -> np.ndarray:
-    """Distance of t from the nearest rounding boundary k + 1/2, k in {0, 1, 2}."""
-    bounds = np.array([0.5, 1.5, 2.5])
+def boundary_distance(t: np.ndarray, bits: int = 2) -> np.ndarray:
+    """Distance of t from the nearest rounding boundary k + 1/2, k in {0, .., levels - 1}."""
+    bounds = np.arange(levels(bits)) + 0.5
     return np.min(np.abs(np.nan_to_num(t, nan=-10.0)[..., None] - bounds), axis=-1)
 
 
