@@ -382,6 +382,103 @@ oscar_status oscar_paged_decode_attn_bf16(const oscar_cache* cache, const void* 
                                           void* workspace, size_t workspace_bytes,
                                           void* out, void* stream);
 
+/* ------------------------------------------------------------------------ *
+ * INT4 cache variant ([TS] 4 "Scalability": the INT4 KV cache OSCAR's
+ * capacity is compared with).  The same rotation, clip and per-token group-32
+ * asymmetric quantizer with 16 levels: s = f16_rne((mx - mn) / 15),
+ * z = f16_rne(mn), code = clamp(rne((y - z) / s), 0, 15), code 0 where
+ * s == 0.  Sink and recent tokens stay in the BF16 pages as for INT2.
+ *
+ * INT4 page.  Head h of physical page P starts at byte (P * H_kv + h) * B_4,
+ * B_4 = 20 d (2560 B at d = 128, 1280 B at d = 64), and holds, one after the
+ * other: K codes [16 slots][d / 2] bytes, V codes [16][d / 2] (channel 2i in
+ * the low nibble of byte i, channel 2i + 1 in the high nibble), then f16 K
+ * scales [16 slots][n_g], K zeros [16][n_g], V scales [16][n_g], V zeros
+ * [16][n_g].  Every slot owns its bytes.
+ * The oscar_cache fields int2_pool / n_int2_pages describe the INT4 pool for
+ * the calls below.
+ * ------------------------------------------------------------------------ */
+size_t oscar_int4_page_bytes(int32_t d, int32_t n_kv_heads); /* per physical page */
+
+/* Quantize-append into INT4 pages: oscar_quantize_append with 16 levels and
+ * the INT4 page layout; same arguments, preconditions, arithmetic and errors. */
+oscar_status oscar_quantize_append_int4(const oscar_cache* cache, const void* k_new,
+                                        const void* v_new, int64_t n_rows,
+                                        const int32_t* row_seq, const int32_t* row_pos,
+                                        const int32_t* bt_q, int32_t max_pages,
+                                        const float* r_k, const float* r_v,
+                                        float tau_k, float tau_v, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * Chunked-prefill ("extend") attention over the mixed cache ([TS] 2.2.B
+ * "Kernel Integration" and [TS] 3: paged KV layouts with prefix caching, so
+ * a request whose prefix is cached prefills only its new tokens, which attend
+ * the cached pages).  For sequence b with P = cache_lens[b] cached tokens
+ * and new rows r = cu_rows[b] .. cu_rows[b+1] - 1 (row i = r - cu_rows[b] at
+ * position P + i), query head j of row r, h = floor(j / G):
+ *   keys/values: the cached tokens [0, P) under the regions of a length-P
+ *     cache (sink and recent raw from BF16 pages via bt_h; the middle decoded
+ *     from the INT2 (code_bits 2) or INT4 (code_bits 4) pages via bt_q and
+ *     attended in the rotated basis, as the decode does), and the new rows
+ *     0 .. i of the sequence, raw (causal);
+ *   out[r][j] = softmax attention of q[r][j] over them, scale sm_scale, with
+ *     the middle's value sum rotated back by R_V(h)^T.
+ * The call only reads the cache: writing the new rows into it (BF16 for the
+ * recent window, quantize-append for the rest) is a separate step.
+ * q: device bf16 [T][H_q][d]; k_new, v_new: device bf16 [T][H_kv][d] (T =
+ * cu_rows[batch]); cu_rows: device int32 [batch + 1], non-decreasing from 0;
+ * cache_lens: device int32 [batch]; bt_q, bt_h: device int32
+ * [batch][max_pages]; r_k, r_v: device float32 [H_kv][d][d]; out: device
+ * bf16 [T][H_q][d].  max_cache_len, max_new: host bounds of cache_lens[b]
+ * and of the rows per sequence (they size the grid); max_cache_len <=
+ * 16 max_pages.  split_steps: steps of 32 tokens per workgroup chunk (0:
+ * automatic); with more than one chunk per (sequence, KV head, column tile)
+ * the call writes chunk records to `workspace` (at least
+ * oscar_extend_workspace_bytes bytes, no preparation needed; 0 bytes when a
+ * single chunk suffices) and merges them in a second launch.
+ * Preconditions (device contents): 0 <= cache_lens[b] <= max_cache_len, at
+ * most max_new rows per sequence, valid page ids wherever they are read.
+ * Arithmetic: middle keys and values decoded to f16, the rotated query f16,
+ * their probabilities f16; raw keys, values and queries as bf16 (exact
+ * products), their probabilities as bf16 hi + lo; float32 sums.
+ * Errors: as oscar_paged_decode_attn; UNSUPPORTED for code_bits other than
+ * 2 or 4.  batch == 0 or max_new == 0 returns OSCAR_OK and launches nothing.
+ * ------------------------------------------------------------------------ */
+oscar_status oscar_extend_workspace_bytes(int32_t batch, int32_t n_kv_heads,
+                                          int32_t n_q_heads, int32_t d, int32_t n_sink,
+                                          int32_t n_recent, int32_t max_cache_len,
+                                          int32_t max_new, int32_t split_steps,
+                                          size_t* bytes);
+oscar_status oscar_paged_extend_attn(const oscar_cache* cache, int32_t code_bits,
+                                     const void* q, const void* k_new, const void* v_new,
+                                     int32_t batch, int32_t n_q_heads,
+                                     const int32_t* cu_rows, const int32_t* cache_lens,
+                                     int32_t max_cache_len, int32_t max_new,
+                                     const int32_t* bt_q, const int32_t* bt_h,
+                                     int32_t max_pages, const float* r_k, const float* r_v,
+                                     float sm_scale, int32_t split_steps, void* workspace,
+                                     size_t workspace_bytes, void* out, void* stream);
+
+/* Decode attention over a cache whose middle is INT4: the definition of
+ * oscar_paged_decode_attn with INT4 pages (seq_lens[b] = L counts the token
+ * being decoded; regions of a length-L cache).  The work is cut into chunks
+ * of split_steps steps of 32 tokens (0: automatic); the chunk records need
+ * oscar_decode_int4_workspace_bytes bytes of workspace (no preparation;
+ * 0 bytes when a single chunk suffices) and are merged in a second launch.
+ * Arithmetic as oscar_paged_extend_attn.  Errors as oscar_paged_decode_attn. */
+oscar_status oscar_decode_int4_workspace_bytes(int32_t batch, int32_t n_kv_heads,
+                                               int32_t n_q_heads, int32_t d, int32_t n_sink,
+                                               int32_t n_recent, int32_t max_seq_len,
+                                               int32_t split_steps, size_t* bytes);
+oscar_status oscar_paged_decode_attn_int4(const oscar_cache* cache, const void* q,
+                                          int32_t batch, int32_t n_q_heads,
+                                          const int32_t* seq_lens, int32_t max_seq_len,
+                                          const int32_t* bt_q, const int32_t* bt_h,
+                                          int32_t max_pages, const float* r_k,
+                                          const float* r_v, float sm_scale,
+                                          int32_t split_steps, void* workspace,
+                                          size_t workspace_bytes, void* out, void* stream);
+
 /* The same decode for callers that cannot allocate device memory (code
  * under HIP graph capture, serving loops that must not call the allocator,
  * harnesses that forbid it): no workspace argument; the arrival counters and

@@ -14,7 +14,7 @@ LIB = os.path.join(HERE, "liboscar.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")
 
-HIP_SOURCES = ["abi.hip", "quantize_append.hip", "decode.hip", "calib.hip", "probe.hip", "noalloc.hip"]
+HIP_SOURCES = ["abi.hip", "quantize_append.hip", "decode.hip", "calib.hip", "probe.hip", "noalloc.hip", "attend.hip"]
 CXX_SOURCES = ["rotation_host.cpp"]
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
              # hipcc -O3 forms packed fp32 arithmetic by itself; keep it off

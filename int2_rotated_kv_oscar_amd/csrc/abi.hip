@@ -191,10 +191,10 @@ size_t oscar_bf16_page_bytes(int32_t d, int32_t n_kv_heads) {
   return size_t(64) * d * n_kv_heads;
 }
 
-oscar_status oscar_quantize_append(const oscar_cache* cache, const void* k_new, const void* v_new, int64_t n_rows,
-                                   const int32_t* row_seq, const int32_t* row_pos, const int32_t* bt_q,
-                                   int32_t max_pages, const float* r_k, const float* r_v, float tau_k, float tau_v,
-                                   void* stream) {
+static oscar_status quantize_append_common(int bits, const oscar_cache* cache, const void* k_new, const void* v_new,
+                                           int64_t n_rows, const int32_t* row_seq, const int32_t* row_pos,
+                                           const int32_t* bt_q, int32_t max_pages, const float* r_k, const float* r_v,
+                                           float tau_k, float tau_v, void* stream) {
   oscar::clear_error();
   if (oscar_status s = check_cache(cache, true, false)) return s;
   if (n_rows < 0) return fail(OSCAR_ERR_INVALID_ARG, "n_rows < 0");
@@ -205,10 +205,31 @@ oscar_status oscar_quantize_append(const oscar_cache* cache, const void* k_new, 
   if (!(tau_k > 0.f) || !(tau_v > 0.f) || !std::isfinite(tau_k) || !std::isfinite(tau_v))
     return fail(OSCAR_ERR_INVALID_ARG, "clip thresholds must be finite and positive");
   if ((n_rows + 15) / 16 > int64_t(0x7FFFFFFF)) return fail(OSCAR_ERR_UNSUPPORTED, "n_rows too large");
-  return hip_status(oscar_launch::quantize_append(cache->d, cache->n_kv_heads, cache->int2_pool, k_new, v_new, n_rows,
+  return hip_status(oscar_launch::quantize_append(cache->d, bits, cache->n_kv_heads, cache->int2_pool, k_new, v_new, n_rows,
                                                   row_seq, row_pos, bt_q, max_pages, r_k, r_v, tau_k, tau_v,
                                                   device_cu_count(), static_cast<hipStream_t>(stream)),
                     "quantize_append launch");
+}
+
+oscar_status oscar_quantize_append(const oscar_cache* cache, const void* k_new, const void* v_new, int64_t n_rows,
+                                   const int32_t* row_seq, const int32_t* row_pos, const int32_t* bt_q,
+                                   int32_t max_pages, const float* r_k, const float* r_v, float tau_k, float tau_v,
+                                   void* stream) {
+  return quantize_append_common(2, cache, k_new, v_new, n_rows, row_seq, row_pos, bt_q, max_pages, r_k, r_v, tau_k,
+                                tau_v, stream);
+}
+
+oscar_status oscar_quantize_append_int4(const oscar_cache* cache, const void* k_new, const void* v_new, int64_t n_rows,
+                                        const int32_t* row_seq, const int32_t* row_pos, const int32_t* bt_q,
+                                        int32_t max_pages, const float* r_k, const float* r_v, float tau_k,
+                                        float tau_v, void* stream) {
+  return quantize_append_common(4, cache, k_new, v_new, n_rows, row_seq, row_pos, bt_q, max_pages, r_k, r_v, tau_k,
+                                tau_v, stream);
+}
+
+size_t oscar_int4_page_bytes(int32_t d, int32_t n_kv_heads) {
+  if (!supported_d(d) || n_kv_heads < 1) return 0;
+  return size_t(20) * d * n_kv_heads;
 }
 
 oscar_status oscar_write_bf16(const oscar_cache* cache, const void* k_new, const void* v_new, int64_t n_rows,
@@ -345,6 +366,135 @@ static oscar_status decode_common(bool all_raw, const oscar_cache* cache, const 
 }
 
 extern "C" {
+
+}  // extern "C"
+
+namespace {
+
+// Work plan of the many-column attention (chunked prefill, INT4 decode): a
+// workgroup takes one tile of 16 NWV query columns of one (sequence, KV
+// head) and one chunk of `spc` steps of 32 tokens (BF16 page pairs,
+// quantized page pairs, tiles of new rows); with more than one chunk per
+// tile, records of 2 + 2d floats per column and chunk go to the workspace
+// and a second launch merges them.  Automatic: about 2 (extend) or 6 (decode,
+// one-wave workgroups) workgroups per compute unit, at least 8 steps a chunk.
+struct AttendPlan {
+  int n_ct, n_chunks, spc;
+  size_t bytes;
+};
+
+oscar_status plan_attend(bool extend, int32_t batch, int32_t n_kv, int32_t n_q, int32_t d, int32_t S, int32_t W,
+                         int32_t max_cache_len, int32_t max_new, int32_t split_steps, AttendPlan* plan) {
+  if (batch < 0 || max_cache_len < 0 || max_new < 0) return fail(OSCAR_ERR_INVALID_ARG, "negative batch or lengths");
+  if (!supported_d(d)) return fail(OSCAR_ERR_UNSUPPORTED, "d must be 64 or 128");
+  if (n_kv < 1 || n_q < 1 || n_q % n_kv) return fail(OSCAR_ERR_INVALID_ARG, "n_q_heads must be a positive multiple of n_kv_heads");
+  if (S < 0 || W < 0) return fail(OSCAR_ERR_INVALID_ARG, "negative n_sink or n_recent");
+  const int G = n_q / n_kv;
+  if (G > 16) return fail(OSCAR_ERR_UNSUPPORTED, "query group size above 16");
+  if (split_steps < 0) return fail(OSCAR_ERR_INVALID_ARG, "split_steps < 0");
+  const int nwv = oscar_launch::attend_waves(extend);
+  const long long cols = extend ? (long long)max_new * G : G;
+  plan->n_ct = int(std::max(1LL, (cols + 16 * nwv - 1) / (16 * nwv)));
+  const long long pages = (max_cache_len + 15LL) / 16;
+  const long long raw = std::min(pages, (S + 15LL) / 16 + (W + 15LL) / 16 + 2);
+  const long long steps = (raw + 1) / 2 + (pages + 2) / 2 + (extend ? (max_new + 31LL) / 32 : 0);
+  const long long units = (long long)batch * n_kv;
+  if (units * plan->n_ct > (1LL << 30)) return fail(OSCAR_ERR_UNSUPPORTED, "grid too large; split the batch");
+  long long spc = split_steps;
+  if (!spc) {
+    const long long target = (extend ? 2LL : 6LL) * device_cu_count();
+    const long long base = std::max(1LL, units * plan->n_ct);
+    const long long chunks = std::max(1LL, (target + base - 1) / base);
+    spc = std::max(8LL, (steps + chunks - 1) / chunks);
+  }
+  const long long n_chunks = std::max(1LL, (steps + spc - 1) / spc);
+  if (units * plan->n_ct * n_chunks > (1LL << 31) - 1) return fail(OSCAR_ERR_UNSUPPORTED, "grid too large; use a larger split_steps");
+  plan->spc = int(std::min<long long>(spc, 1 << 30));
+  plan->n_chunks = int(n_chunks);
+  plan->bytes = plan->n_chunks > 1 ? size_t(units) * plan->n_ct * plan->n_chunks * 16 * nwv * (2 + 2 * size_t(d)) * 4 : 0;
+  return OSCAR_OK;
+}
+
+oscar_status attend_common(bool extend, int bits, const oscar_cache* cache, const void* q, const void* k_new,
+                           const void* v_new, int32_t batch, int32_t n_q_heads, const int32_t* cu,
+                           const int32_t* clen, int32_t max_cache_len, int32_t max_new, const int32_t* bt_q,
+                           const int32_t* bt_h, int32_t max_pages, const float* r_k, const float* r_v, float sm_scale,
+                           int32_t split_steps, void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  oscar::clear_error();
+  if (oscar_status s = check_cache(cache, true, true)) return s;
+  if (bits != 2 && bits != 4) return fail(OSCAR_ERR_UNSUPPORTED, "code_bits must be 2 or 4");
+  AttendPlan plan;
+  if (oscar_status s = plan_attend(extend, batch, cache->n_kv_heads, n_q_heads, cache->d, cache->n_sink,
+                                   cache->n_recent, max_cache_len, max_new, split_steps, &plan))
+    return s;
+  if (batch == 0 || (extend && max_new == 0)) return OSCAR_OK;
+  if (!q || !clen || !bt_q || !bt_h || !r_k || !r_v || !out || (extend && (!k_new || !v_new || !cu)))
+    return fail(OSCAR_ERR_INVALID_ARG, "null device pointer");
+  if (max_pages < 1 || int64_t(max_cache_len) > int64_t(max_pages) * 16)
+    return fail(OSCAR_ERR_INVALID_ARG, "max cache length exceeds 16 * max_pages");
+  if (!(std::isfinite(sm_scale) && sm_scale > 0.f)) return fail(OSCAR_ERR_INVALID_ARG, "sm_scale must be finite and positive");
+  if (plan.bytes && (!workspace || workspace_bytes < plan.bytes))
+    return fail(OSCAR_ERR_WORKSPACE, "workspace missing or smaller than the workspace query's size");
+  const int G = n_q_heads / cache->n_kv_heads;
+  return hip_status(oscar_launch::paged_attend(cache->d, bits, extend, cache->int2_pool, int(std::min<int64_t>(cache->n_int2_pages, 0x7FFFFFFF)),
+                                               cache->bf16_pool, int(std::min<int64_t>(cache->n_bf16_pages, 0x7FFFFFFF)),
+                                               cache->n_kv_heads, G, cache->n_sink, cache->n_recent, n_q_heads, q,
+                                               k_new, v_new, cu, clen, batch, bt_q, bt_h, max_pages, r_k, r_v,
+                                               sm_scale, plan.n_ct, plan.n_chunks, plan.spc,
+                                               static_cast<float*>(workspace), out, static_cast<hipStream_t>(stream)),
+                    "attention launch");
+}
+
+}  // namespace
+
+extern "C" {
+
+oscar_status oscar_extend_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads, int32_t d,
+                                          int32_t n_sink, int32_t n_recent, int32_t max_cache_len, int32_t max_new,
+                                          int32_t split_steps, size_t* bytes) {
+  oscar::clear_error();
+  if (!bytes) return fail(OSCAR_ERR_INVALID_ARG, "bytes is NULL");
+  AttendPlan plan;
+  if (oscar_status s = plan_attend(true, batch, n_kv_heads, n_q_heads, d, n_sink, n_recent, max_cache_len, max_new,
+                                   split_steps, &plan))
+    return s;
+  *bytes = plan.bytes;
+  return OSCAR_OK;
+}
+
+oscar_status oscar_paged_extend_attn(const oscar_cache* cache, int32_t code_bits, const void* q, const void* k_new,
+                                     const void* v_new, int32_t batch, int32_t n_q_heads, const int32_t* cu_rows,
+                                     const int32_t* cache_lens, int32_t max_cache_len, int32_t max_new,
+                                     const int32_t* bt_q, const int32_t* bt_h, int32_t max_pages, const float* r_k,
+                                     const float* r_v, float sm_scale, int32_t split_steps, void* workspace,
+                                     size_t workspace_bytes, void* out, void* stream) {
+  return attend_common(true, code_bits, cache, q, k_new, v_new, batch, n_q_heads, cu_rows, cache_lens, max_cache_len,
+                       max_new, bt_q, bt_h, max_pages, r_k, r_v, sm_scale, split_steps, workspace, workspace_bytes,
+                       out, stream);
+}
+
+oscar_status oscar_decode_int4_workspace_bytes(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads, int32_t d,
+                                               int32_t n_sink, int32_t n_recent, int32_t max_seq_len,
+                                               int32_t split_steps, size_t* bytes) {
+  oscar::clear_error();
+  if (!bytes) return fail(OSCAR_ERR_INVALID_ARG, "bytes is NULL");
+  AttendPlan plan;
+  if (oscar_status s = plan_attend(false, batch, n_kv_heads, n_q_heads, d, n_sink, n_recent, max_seq_len, 0,
+                                   split_steps, &plan))
+    return s;
+  *bytes = plan.bytes;
+  return OSCAR_OK;
+}
+
+oscar_status oscar_paged_decode_attn_int4(const oscar_cache* cache, const void* q, int32_t batch, int32_t n_q_heads,
+                                          const int32_t* seq_lens, int32_t max_seq_len, const int32_t* bt_q,
+                                          const int32_t* bt_h, int32_t max_pages, const float* r_k, const float* r_v,
+                                          float sm_scale, int32_t split_steps, void* workspace,
+                                          size_t workspace_bytes, void* out, void* stream) {
+  return attend_common(false, 4, cache, q, nullptr, nullptr, batch, n_q_heads, nullptr, seq_lens, max_seq_len, 0,
+                       bt_q, bt_h, max_pages, r_k, r_v, sm_scale, split_steps, workspace, workspace_bytes, out,
+                       stream);
+}
 
 oscar_status oscar_paged_decode_attn(const oscar_cache* cache, const void* q, int32_t batch, int32_t n_q_heads,
                                      const int32_t* seq_lens, int32_t max_seq_len, const int32_t* bt_q,

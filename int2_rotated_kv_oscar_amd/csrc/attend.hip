@@ -1,0 +1,709 @@
+// Paged attention over the mixed cache with many query columns: chunked
+// prefill ("extend") over INT2 or INT4 pages, and the INT4 cache's decode
+// ([TS] 2.2.B "Kernel Integration": paged attention, prefix caching; [TS] 3:
+// serving with paged KV layouts and prefix caching; [TS] 4 "Scalability": the
+// INT4 KV cache OSCAR is compared with).
+//
+// A workgroup of NWV waves owns 16 NWV query columns of one (sequence, KV
+// head): a column is one (new row, query head of the group) pair, taken
+// row-major, so the G heads of a row sit side by side.  It walks a chunk of
+// the unit's work, 32 tokens per step: page pairs of the BF16 sink/recent
+// pages, page pairs of the quantized middle pages, then (extend) tiles of 32
+// new rows.  Each step is decoded once into an LDS tile shared by the waves:
+// keys token-major and values channel-major, as f16 (quantized tokens: c s + z
+// in the rotated basis) or as the raw bf16 bits (BF16 pages, new rows).  Tokens
+// outside their region (stale slots of recycled pages, rows past the end) are
+// written as zeros and their logits masked, so nothing stale reaches a sum.
+// Every wave then runs, for its 16 columns, the transposed products of
+// flash attention on the matrix cores: logits^T = K Q^T (16x16x32, tokens x
+// columns) and out^T += V^T P^T, with the online softmax over the tokens of a
+// column in between.  Quantized tokens use the rotated query q~ = q R_K and
+// a value sum in the rotated basis; raw tokens use q and a second value sum;
+// out = raw + rot R_V^T at the end.  With more than one chunk per unit the
+// chunks' states (max, sum, both value sums) go to a workspace and a second
+// kernel merges them by log-sum-exp.
+#include <algorithm>
+
+#include "device_utils.h"
+#include "kernels.h"
+#include "layout.h"
+
+using namespace oscar_dev;
+
+namespace {
+
+constexpr float kNegInfA = -__builtin_inff();
+
+struct AttParams {
+  const uint8_t* qpool;    // INT2 or INT4 pool
+  int32_t n_qpages;
+  const uint16_t* bf16_pool;
+  int32_t n_bpages;
+  int32_t n_kv, G, S, W, Hq;
+  const uint16_t* q;       // bf16 [rows][Hq][D]
+  const uint16_t* k_new;   // bf16 [rows][n_kv][D] (extend)
+  const uint16_t* v_new;
+  const int32_t* cu;       // extend: [B + 1] row offsets
+  const int32_t* clen;     // cached length per sequence (decode: the length)
+  const int32_t* bt_q;
+  const int32_t* bt_h;
+  int32_t max_pages;
+  const float* r_k;
+  const float* r_v;
+  float sm_scale;
+  int32_t n_ct;            // column tiles per unit in the grid
+  int32_t n_chunks;        // chunks per (unit, column tile)
+  int32_t spc;             // steps per chunk
+  float* rec;              // [unit][tile][chunk][column][2 + 2D] when n_chunks > 1
+  uint16_t* out;           // bf16 [rows][Hq][D]
+};
+
+// Geometry of the quantized page-heads (INT2: the MFMA-shaped layout; INT4:
+// row-owned nibbles).
+template <int D, int BITS>
+struct QGeo : QLayout<D, BITS> {
+  static constexpr int BYTES = QLayout<D, BITS>::HEAD_BYTES;
+};
+
+// LDS tile of one step: keys [32 tokens][KROW], values [D][VROW] (u16 bits).
+template <int D>
+struct Tile {
+  static constexpr int KROW = D + 8;   // padded rows: the lanes of an operand read hit distinct banks
+  static constexpr int VROW = 32 + 8;
+  static constexpr int ELEMS = 32 * KROW + D * VROW;
+};
+
+__device__ __forceinline__ uint32_t f16pair(float a, float b) { return pack_f16x2(a, b); }
+
+// Region plan of a length-P cache: BF16 pages (range A = sink, range B =
+// recent; one range when they meet) and the quantized pages [q0, q1).
+struct Regions {
+  int P, s1, m0, m1, r0;
+  int ra1, rb0, rb1, q0, q1, n_raw;
+  __device__ __forceinline__ int raw_page(int i) const { return i < ra1 ? i : rb0 + (i - ra1); }
+};
+__device__ __forceinline__ Regions make_regions(int P, int S, int W) {
+  Regions g;
+  g.P = P;
+  const int n_pages = (P + 15) >> 4;
+  g.s1 = min(S, P);
+  g.m0 = S;
+  g.m1 = P - W;
+  g.r0 = max(S, P - W);
+  const int hs1 = (g.s1 + 15) >> 4;
+  const int hr0 = g.r0 < P ? (g.r0 >> 4) : n_pages;
+  if (hs1 >= hr0) {
+    g.ra1 = n_pages; g.rb0 = g.rb1 = n_pages;
+  } else {
+    g.ra1 = hs1; g.rb0 = hr0; g.rb1 = n_pages;
+  }
+  g.n_raw = g.ra1 + (g.rb1 - g.rb0);
+  if (g.m1 > g.m0) { g.q0 = g.m0 >> 4; g.q1 = (g.m1 + 15) >> 4; }
+  else { g.q0 = g.q1 = 0; }
+  return g;
+}
+
+// ---- step fill: one 32-token step into the LDS tile ----
+// Each thread loads its share of the step's bytes into registers (issued a
+// step ahead, so the loads overlap the previous step's products) and then
+// decodes them into the tile.  Shares: raw steps (BF16 page pair, 32 new
+// rows) 4D key chunks and 4D value chunks of 16 B; INT2 page pairs 2D items
+// (a key code word, a value code word, their scales and zeros); INT4 page
+// pairs 4D items (a key and a value code word of 8 nibbles, their scales and
+// zeros).  One-wave workgroups (decode) load their few raw steps when storing
+// them, which keeps their registers for the quantized items.
+template <int D, int BITS, int NTH>
+struct Stage {
+  static constexpr int NR = (4 * D + NTH - 1) / NTH;       // raw chunks per tensor per thread
+  static constexpr bool RAW_AHEAD = NTH >= 256;
+  static constexpr int NRS = RAW_AHEAD ? NR : 1;
+  static constexpr int NQ = BITS == 2 ? (2 * D + NTH - 1) / NTH : (4 * D + NTH - 1) / NTH;  // quantized items
+  static constexpr int QW = BITS == 2 ? 12 : 6;            // registers per item
+  u32x4 kr[NRS], vr[NRS];
+  uint32_t qw[NQ][QW];
+};
+
+struct StepInfo {
+  int kind;  // 0 BF16 page pair, 1 quantized page pair, 2 new rows
+  int i0;    // first list position (pages) or first new row
+};
+
+__device__ __forceinline__ bool raw_token(const Regions& rg, int pos) {
+  return pos < rg.s1 || (pos >= rg.r0 && pos < rg.P);
+}
+
+// The raw chunk e (< 4D) of a raw step: its key chunk and its value chunk.
+template <int D>
+__device__ __forceinline__ void raw_chunk_load(const AttParams& p, const Regions& rg, const int32_t* bth, int h,
+                                               int row0, int n_rows, const StepInfo& si, int e, u32x4& kv, u32x4& vv) {
+  constexpr int KCH = D / 8;
+  kv = u32x4{0, 0, 0, 0};
+  vv = u32x4{0, 0, 0, 0};
+  if (e >= 4 * D) return;
+  if (si.kind == 0) {
+    const int j = e / (16 * KCH), tok = (e / KCH) % 16, ch = e % KCH;
+    const int li = si.i0 + j;
+    if (li < rg.n_raw) {
+      const int pg = rg.raw_page(li);
+      const uint16_t* base = p.bf16_pool + (size_t(min(max(bth[pg], 0), p.n_bpages - 1)) * p.n_kv + h) * Geo<D>::BF16_HEAD_ELEMS;
+      kv = *reinterpret_cast<const u32x4*>(base + tok * D + 8 * ch);
+    }
+    const int jv = e / (2 * D), c = (e / 2) % D, half = e % 2;
+    const int lv = si.i0 + jv;
+    if (lv < rg.n_raw) {
+      const int pg = rg.raw_page(lv);
+      const uint16_t* base = p.bf16_pool + (size_t(min(max(bth[pg], 0), p.n_bpages - 1)) * p.n_kv + h) * Geo<D>::BF16_HEAD_ELEMS;
+      vv = *reinterpret_cast<const u32x4*>(base + 16 * D + c * 16 + 8 * half);
+    }
+  } else {
+    const int tok = e / KCH, ch = e % KCH;
+    if (si.i0 + tok < n_rows) {
+      const size_t off = (size_t(row0 + si.i0 + tok) * p.n_kv + h) * D + 8 * ch;
+      kv = *reinterpret_cast<const u32x4*>(p.k_new + off);
+      vv = *reinterpret_cast<const u32x4*>(p.v_new + off);
+    }
+  }
+}
+
+template <int D, int BITS, int NTH>
+__device__ __forceinline__ void step_load(const AttParams& p, const Regions& rg, const int32_t* btq, const int32_t* bth,
+                                          int h, int row0, int n_rows, const StepInfo& si, Stage<D, BITS, NTH>& st,
+                                          int t) {
+  using SG = Stage<D, BITS, NTH>;
+  constexpr int NG = D / 32;
+  if (si.kind != 1) {
+    if constexpr (SG::RAW_AHEAD) {
+#pragma unroll
+      for (int it = 0; it < SG::NRS; ++it)
+        raw_chunk_load<D>(p, rg, bth, h, row0, n_rows, si, t + it * NTH, st.kr[it], st.vr[it]);
+    }
+  } else if constexpr (BITS == 2) {
+    using QG = QGeo<D, 2>;
+    constexpr int NW = D / 64;
+#pragma unroll
+    for (int it = 0; it < SG::NQ; ++it) {
+      const int e0 = t + it * NTH;
+      const int e = e0 < 2 * D ? e0 : 0;
+      const int j = e / D, wi = e % D;
+      const int pg = min(rg.q0 + si.i0 + j, rg.q1 - 1);
+      const uint8_t* base = p.qpool + (size_t(min(max(btq[pg], 0), p.n_qpages - 1)) * p.n_kv + h) * QG::BYTES;
+      const int m = (wi / NW) % 16, w = wi % NW, q = wi / (16 * NW);
+      st.qw[it][0] = reinterpret_cast<const uint32_t*>(base + QG::KC)[wi];
+      st.qw[it][1] = reinterpret_cast<const uint32_t*>(base + QG::KS)[(m * NG + 2 * w) / 2];
+      st.qw[it][2] = reinterpret_cast<const uint32_t*>(base + QG::KZ)[(m * NG + 2 * w) / 2];
+      st.qw[it][3] = reinterpret_cast<const uint32_t*>(base + QG::VC)[wi];
+      const u32x4 vs = *reinterpret_cast<const u32x4*>(base + QG::VS + 8 * (q * NG + 2 * w));
+      const u32x4 vz = *reinterpret_cast<const u32x4*>(base + QG::VZ + 8 * (q * NG + 2 * w));
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        st.qw[it][4 + k] = vs[k];
+        st.qw[it][8 + k] = vz[k];
+      }
+    }
+  } else {
+    using QG = QGeo<D, 4>;
+    constexpr int WPR = D / 8, WPP = 16 * WPR;
+#pragma unroll
+    for (int it = 0; it < SG::NQ; ++it) {
+      const int e0 = t + it * NTH;
+      const int e = e0 < 2 * WPP ? e0 : 0;
+      const int j = e / WPP, wi = e % WPP;
+      const int pg = min(rg.q0 + si.i0 + j, rg.q1 - 1);
+      const uint8_t* base = p.qpool + (size_t(min(max(btq[pg], 0), p.n_qpages - 1)) * p.n_kv + h) * QG::BYTES;
+      const int m = wi / WPR, g = (8 * (wi % WPR)) / 32;
+      st.qw[it][0] = reinterpret_cast<const uint32_t*>(base + QG::KC)[wi];
+      st.qw[it][1] = reinterpret_cast<const uint32_t*>(base + QG::VC)[wi];
+      st.qw[it][2] = reinterpret_cast<const uint16_t*>(base + QG::KS)[m * NG + g];
+      st.qw[it][3] = reinterpret_cast<const uint16_t*>(base + QG::KZ)[m * NG + g];
+      st.qw[it][4] = reinterpret_cast<const uint16_t*>(base + QG::VS)[m * NG + g];
+      st.qw[it][5] = reinterpret_cast<const uint16_t*>(base + QG::VZ)[m * NG + g];
+    }
+  }
+}
+
+template <int D, int BITS, int NTH>
+__device__ __forceinline__ void step_store(const AttParams& p, const Regions& rg, const int32_t* bth, int h, int row0,
+                                           int n_rows, const StepInfo& si, const Stage<D, BITS, NTH>& st,
+                                           uint16_t* tile, int t) {
+  using T = Tile<D>;
+  using SG = Stage<D, BITS, NTH>;
+  uint16_t* vt = tile + 32 * T::KROW;
+  if (si.kind != 1) {
+    constexpr int KCH = D / 8;
+#pragma unroll
+    for (int it = 0; it < SG::NR; ++it) {
+      const int e = t + it * NTH;
+      if (e >= 4 * D) break;
+      u32x4 kv, vv;
+      if constexpr (SG::RAW_AHEAD) {
+        kv = st.kr[it];
+        vv = st.vr[it];
+      } else {
+        raw_chunk_load<D>(p, rg, bth, h, row0, n_rows, si, e, kv, vv);
+      }
+      uint32_t vw[4] = {vv[0], vv[1], vv[2], vv[3]};
+      if (si.kind == 0) {
+        const int j = e / (16 * KCH), tok = (e / KCH) % 16, ch = e % KCH;
+        const int li = si.i0 + j;
+        if (!(li < rg.n_raw && raw_token(rg, 16 * rg.raw_page(li) + tok))) kv = u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4*>(tile + (16 * j + tok) * T::KROW + 8 * ch) = kv;
+        const int jv = e / (2 * D), c = (e / 2) % D, half = e % 2;
+        const int lv = si.i0 + jv;
+        const int pg = lv < rg.n_raw ? rg.raw_page(lv) : -1;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {  // tokens outside the BF16 regions: zero (their bytes may be stale)
+          const int pos = 16 * pg + 8 * half + k;
+          if (pg < 0 || !raw_token(rg, pos)) vw[k / 2] &= (k & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+        }
+        *reinterpret_cast<u32x4*>(vt + c * T::VROW + 16 * jv + 8 * half) = u32x4{vw[0], vw[1], vw[2], vw[3]};
+      } else {
+        const int tok = e / KCH, ch = e % KCH;
+        *reinterpret_cast<u32x4*>(tile + tok * T::KROW + 8 * ch) = kv;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) vt[(8 * ch + k) * T::VROW + tok] = uint16_t(vw[k / 2] >> (16 * (k & 1)));
+      }
+    }
+  } else if constexpr (BITS == 2) {
+    constexpr int NW = D / 64;
+#pragma unroll
+    for (int it = 0; it < SG::NQ; ++it) {
+      const int e = t + it * NTH;
+      if (e >= 2 * D) break;
+      const int j = e / D, wi = e % D;
+      const int pg = rg.q0 + si.i0 + j;
+      auto live = [&](int slot) {
+        const int pos = 16 * pg + slot;
+        return pg < rg.q1 && pos >= rg.m0 && pos < rg.m1;
+      };
+      {  // K word: token m, channels 32 g + 16 hb + 4 quad + r, g in {2w, 2w + 1}
+        const int quad = wi / (16 * NW), m = (wi / NW) % 16, w = wi % NW;
+        const bool ok = live(m);
+        const uint32_t word = st.qw[it][0], ks = st.qw[it][1], kz = st.qw[it][2];
+#pragma unroll
+        for (int gg = 0; gg < 2; ++gg) {
+          const float s = f16_to_f32(ks >> (16 * gg)), z = f16_to_f32(kz >> (16 * gg));
+#pragma unroll
+          for (int hb = 0; hb < 2; ++hb) {
+            float v[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int bit = 16 * (r & 1) + 8 * gg + 4 * hb + 2 * (r >> 1);
+              v[r] = ok ? __builtin_fmaf(float((word >> bit) & 3u), s, z) : 0.f;
+            }
+            const int c = 32 * (2 * w + gg) + 16 * hb + 4 * quad;
+            *reinterpret_cast<u32x2*>(tile + (16 * j + m) * T::KROW + c) = u32x2{f16pair(v[0], v[1]), f16pair(v[2], v[3])};
+          }
+        }
+      }
+      {  // V word: tokens 4 q + r, channels c16 + 16 (4 w + bb), group 2 w + bb / 2
+        const int q = wi / (16 * NW), c16 = (wi / NW) % 16, w = wi % NW;
+        const uint32_t word = st.qw[it][3];
+#pragma unroll
+        for (int bb = 0; bb < 4; ++bb) {
+          const int c = c16 + 16 * (4 * w + bb), gg = bb >> 1;
+          float v[4];
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int bit = 16 * (r & 1) + 8 * (r >> 1) + 2 * bb;
+            const int hidx = 4 * gg + r;  // f16 index in the 16-byte scale/zero loads
+            const float s = f16_to_f32(st.qw[it][4 + hidx / 2] >> (16 * (hidx & 1)));
+            const float z = f16_to_f32(st.qw[it][8 + hidx / 2] >> (16 * (hidx & 1)));
+            v[r] = live(4 * q + r) ? __builtin_fmaf(float((word >> bit) & 3u), s, z) : 0.f;
+          }
+          *reinterpret_cast<u32x2*>(vt + c * T::VROW + 16 * j + 4 * q) = u32x2{f16pair(v[0], v[1]), f16pair(v[2], v[3])};
+        }
+      }
+    }
+  } else {
+    constexpr int WPR = D / 8, WPP = 16 * WPR;
+#pragma unroll
+    for (int it = 0; it < SG::NQ; ++it) {
+      const int e = t + it * NTH;
+      if (e >= 2 * WPP) break;
+      const int j = e / WPP, wi = e % WPP;
+      const int pg = rg.q0 + si.i0 + j;
+      const int m = wi / WPR, c0 = 8 * (wi % WPR);
+      const int pos = 16 * pg + m;
+      const bool ok = pg < rg.q1 && pos >= rg.m0 && pos < rg.m1;
+      const uint32_t kw = st.qw[it][0], vw = st.qw[it][1];
+      const float ks = f16_to_f32(st.qw[it][2]), kz = f16_to_f32(st.qw[it][3]);
+      const float vs = f16_to_f32(st.qw[it][4]), vz = f16_to_f32(st.qw[it][5]);
+      float v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = ok ? __builtin_fmaf(float((kw >> (4 * k)) & 15u), ks, kz) : 0.f;
+      *reinterpret_cast<u32x4*>(tile + (16 * j + m) * T::KROW + c0) =
+          u32x4{f16pair(v[0], v[1]), f16pair(v[2], v[3]), f16pair(v[4], v[5]), f16pair(v[6], v[7])};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const float x = ok ? __builtin_fmaf(float((vw >> (4 * k)) & 15u), vs, vz) : 0.f;
+        vt[(c0 + k) * T::VROW + 16 * j + m] = uint16_t(f16_bits(x));
+      }
+    }
+  }
+}
+
+// out^T[c][n] = (raw^T[c][n] + sum_k R_V[c][k] rot[n][k]) / l for the 16
+// columns of a wave: rot (fp32 [16][D]) in the wave's LDS area, raw in the
+// accumulator layout; R_V rows and rot split into bf16 hi + lo (three
+// products per block).  Writes the bf16 row of column l16 if `ok`.
+template <int D>
+__device__ __forceinline__ void finish_columns(const float* rv, const float* rot, const f32x4 (&acc_raw)[D / 16],
+                                               float l_tot, bool ok, uint16_t* orow, int l16, int quad) {
+  constexpr int NCB = D / 16, NKB = D / 32;
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+#pragma unroll 1
+  for (int cb = 0; cb < NCB; ++cb) {
+    f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const f32x4 ra0 = *reinterpret_cast<const f32x4*>(rv + size_t(16 * cb + l16) * D + 32 * kb + 8 * quad);
+      const f32x4 ra1 = *reinterpret_cast<const f32x4*>(rv + size_t(16 * cb + l16) * D + 32 * kb + 8 * quad + 4);
+      const float* rb = rot + l16 * D + 32 * kb + 8 * quad;
+      const float ra[8] = {ra0[0], ra0[1], ra0[2], ra0[3], ra1[0], ra1[1], ra1[2], ra1[3]};
+      uint32_t ah[4], al[4], bh[4], bl[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ah[i] = pack2(bf16_rne(ra[2 * i]), bf16_rne(ra[2 * i + 1]));
+        al[i] = pack2(bf16_rne(ra[2 * i] - bf16_to_f32(ah[i] & 0xFFFFu)), bf16_rne(ra[2 * i + 1] - bf16_to_f32(ah[i] >> 16)));
+        bh[i] = pack2(bf16_rne(rb[2 * i]), bf16_rne(rb[2 * i + 1]));
+        bl[i] = pack2(bf16_rne(rb[2 * i] - bf16_to_f32(bh[i] & 0xFFFFu)), bf16_rne(rb[2 * i + 1] - bf16_to_f32(bh[i] >> 16)));
+      }
+      const u32x4 AH{ah[0], ah[1], ah[2], ah[3]}, AL{al[0], al[1], al[2], al[3]};
+      const u32x4 BH{bh[0], bh[1], bh[2], bh[3]}, BL{bl[0], bl[1], bl[2], bl[3]};
+      a4 = mfma_bf16(AL, BH, a4);
+      a4 = mfma_bf16(AH, BL, a4);
+      a4 = mfma_bf16(AH, BH, a4);
+    }
+    if (ok) {
+      u32x2 ov;
+      ov[0] = pack2(bf16_rne((a4[0] + acc_raw[cb][0]) * inv), bf16_rne((a4[1] + acc_raw[cb][1]) * inv));
+      ov[1] = pack2(bf16_rne((a4[2] + acc_raw[cb][2]) * inv), bf16_rne((a4[3] + acc_raw[cb][3]) * inv));
+      *reinterpret_cast<u32x2*>(orow + 16 * cb + 4 * quad) = ov;
+    }
+  }
+}
+
+// Unit of a workgroup and the rows of its sequence.
+struct UnitRows {
+  int b, h, row0, n_rows, P;
+};
+template <int MODE>
+__device__ __forceinline__ UnitRows unit_rows(const AttParams& p, int unit) {
+  UnitRows u;
+  u.b = unit / p.n_kv;
+  u.h = unit % p.n_kv;
+  if (MODE == 0) {
+    u.row0 = p.cu[u.b];
+    u.n_rows = p.cu[u.b + 1] - u.row0;
+  } else {
+    u.row0 = u.b;
+    u.n_rows = 1;
+  }
+  u.P = p.clen[u.b];
+  return u;
+}
+
+// ---- the kernel ----
+// MODE 0: extend (rows of new tokens at positions P + i, causal over them);
+// MODE 1: decode (one query row per sequence at position L - 1, over the
+// whole length-L cache).
+template <int D, int BITS, int NWV, int MODE>
+__global__ __launch_bounds__(64 * NWV) void attend_kernel(AttParams p) {
+  using T = Tile<D>;
+  constexpr int NCB = D / 16, NKB = D / 32, NTH = 64 * NWV;
+  constexpr int NBUF = NWV > 1 ? 2 : 1;
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  uint16_t* tiles = lds;                                               // [NBUF][T::ELEMS]
+  float* fbuf = reinterpret_cast<float*>(lds + NBUF * T::ELEMS);       // [NWV][16][D] per-wave staging
+
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, quad = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = p.G;
+  const int chunk = blockIdx.x % p.n_chunks;
+  const int ct = (blockIdx.x / p.n_chunks) % p.n_ct;
+  const int unit = blockIdx.x / (p.n_chunks * p.n_ct);
+  const UnitRows u = unit_rows<MODE>(p, unit);
+  const int b = u.b, h = u.h, row0 = u.row0, n_rows = u.n_rows, P = u.P;
+
+  if (MODE == 1 && P <= 0) {  // no tokens: a zero output (written once per sequence)
+    if (h == 0 && ct == 0 && chunk == 0)
+      for (int e = tid; e < p.Hq * D; e += NTH) p.out[size_t(b) * p.Hq * D + e] = 0;
+    return;
+  }
+  const int col0 = ct * 16 * NWV;                  // first column of the tile
+  const int n_cols = n_rows * G;                   // columns of the unit
+  if (col0 >= n_cols) return;
+  // this lane's column: row ri, head hi of the group
+  const int col = col0 + 16 * wave + l16;
+  const bool col_ok = col < n_cols;
+  const int ri = col_ok ? col / G : 0, hi = col_ok ? col % G : 0;
+  const int qpos = MODE == 0 ? P + ri : P - 1;     // the column's query position
+  const int last_row = min(n_rows, (col0 + 16 * NWV + G - 1) / G) - 1;  // last row with a column in the tile
+  const uint16_t* qrow = p.q + (size_t(row0 + ri) * p.Hq + h * G + hi) * D;
+  const float qscale = p.sm_scale * kLog2e;
+
+  // ---- work of the unit: BF16 page pairs, quantized page pairs, new-row tiles ----
+  const Regions rg = make_regions(max(P, 0), p.S, p.W);
+  const int32_t* btq = p.bt_q + size_t(b) * p.max_pages;
+  const int32_t* bth = p.bt_h + size_t(b) * p.max_pages;
+  const int n_rp = (rg.n_raw + 1) >> 1;
+  const int n_qp = (rg.q1 - rg.q0 + 1) >> 1;
+  const int n_nt = MODE == 0 ? (last_row + 1 + 31) / 32 : 0;
+  const int total = n_rp + n_qp + n_nt;
+  const int s_begin = chunk * p.spc, s_end = min(total, s_begin + p.spc);
+  auto info = [&](int s) {
+    StepInfo si;
+    if (s < n_rp) { si.kind = 0; si.i0 = 2 * s; }
+    else if (s < n_rp + n_qp) { si.kind = 1; si.i0 = 2 * (s - n_rp); }
+    else { si.kind = 2; si.i0 = 32 * (s - n_rp - n_qp); }
+    return si;
+  };
+  Stage<D, BITS, NTH> st;
+  if (s_begin < s_end) step_load<D, BITS, NTH>(p, rg, btq, bth, h, row0, n_rows, info(s_begin), st, tid);
+
+  // ---- query operands: raw q (bf16) and q~ = q R_K (f16, pre-scaled by qscale) ----
+  u32x4 bq_raw[NKB], bq_rot[NKB];
+#pragma unroll
+  for (int kb = 0; kb < NKB; ++kb) bq_raw[kb] = *reinterpret_cast<const u32x4*>(qrow + 32 * kb + 8 * quad);
+  {
+    // q~^T[c][n] = sum_k R_K[k][c] q[n][k]: A = R_K^T rows c = 16 cb + l16 (bf16 hi/lo), B = q
+    float* qst = fbuf + wave * 16 * D;  // q~ [16 columns][D]
+    const float* rk = p.r_k + size_t(h) * D * D;
+#pragma unroll 1
+    for (int cb = 0; cb < NCB; ++cb) {
+      f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        float rv[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) rv[i] = rk[size_t(32 * kb + 8 * quad + i) * D + 16 * cb + l16];
+        uint32_t ph[4], pl[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ph[i] = pack2(bf16_rne(rv[2 * i]), bf16_rne(rv[2 * i + 1]));
+          pl[i] = pack2(bf16_rne(rv[2 * i] - bf16_to_f32(ph[i] & 0xFFFFu)), bf16_rne(rv[2 * i + 1] - bf16_to_f32(ph[i] >> 16)));
+        }
+        a4 = mfma_bf16(u32x4{pl[0], pl[1], pl[2], pl[3]}, bq_raw[kb], a4);
+        a4 = mfma_bf16(u32x4{ph[0], ph[1], ph[2], ph[3]}, bq_raw[kb], a4);
+      }
+      // a4[r] = q~[n = l16][c = 16 cb + 4 quad + r]
+      *reinterpret_cast<f32x4*>(qst + l16 * D + 16 * cb + 4 * quad) = a4 * qscale;
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const float* src = qst + l16 * D + 32 * kb + 8 * quad;
+      bq_rot[kb] = u32x4{f16pair(src[0], src[1]), f16pair(src[2], src[3]), f16pair(src[4], src[5]), f16pair(src[6], src[7])};
+    }
+  }
+
+  float m_run = kNegInfA, l_part = 0.f;
+  f32x4 acc_rot[NCB], acc_raw[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) {
+    acc_rot[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc_raw[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+
+#pragma unroll 1
+  for (int s = s_begin; s < s_end; ++s) {
+    uint16_t* tile = tiles + (NBUF == 2 ? (s & 1) : 0) * T::ELEMS;
+    const StepInfo si = info(s);
+    step_store<D, BITS, NTH>(p, rg, bth, h, row0, n_rows, si, st, tile, tid);
+    if (s + 1 < s_end) step_load<D, BITS, NTH>(p, rg, btq, bth, h, row0, n_rows, info(s + 1), st, tid);
+    lds_barrier();  // the tile is complete; the next step's loads stay in flight
+    const bool quantized = si.kind == 1;
+    f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const u32x4 a = *reinterpret_cast<const u32x4*>(tile + (16 * j + l16) * T::KROW + 32 * kb + 8 * quad);
+        sc[j] = quantized ? mfma_f16(a, bq_rot[kb], sc[j]) : mfma_bf16(a, bq_raw[kb], sc[j]);
+      }
+    // logits of tokens 16 j + 4 quad + r for column l16 (log2 units), masked
+    float lg[2][4];
+    float mx = kNegInfA;
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int tk = 16 * j + 4 * quad + r;
+        bool ok = col_ok;
+        if (si.kind == 0) {
+          const int li = si.i0 + j;
+          ok = ok && li < rg.n_raw && raw_token(rg, 16 * rg.raw_page(li) + (tk & 15));
+        } else if (quantized) {
+          const int pg = rg.q0 + si.i0 + j, pos = 16 * pg + (tk & 15);
+          ok = ok && pg < rg.q1 && pos >= rg.m0 && pos < rg.m1;
+        } else {
+          const int i = si.i0 + tk;  // new row index
+          ok = ok && i < n_rows && P + i <= qpos;
+        }
+        lg[j][r] = ok ? (quantized ? sc[j][r] : sc[j][r] * qscale) : kNegInfA;
+        mx = fmaxf(mx, lg[j][r]);
+      }
+    mx = wave_max16(mx);
+    if (__any(mx > m_run)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float f = (m_run == kNegInfA) ? 0.f : exp2f(m_run - m_new);
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        acc_rot[cb] *= f;
+        acc_raw[cb] *= f;
+      }
+      l_part *= f;
+      m_run = m_new;
+    }
+    const float m_use = (m_run == kNegInfA) ? 0.f : m_run;
+    float pv[2][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pv[j][r] = __builtin_amdgcn_exp2f(lg[j][r] - m_use);
+        l_part += pv[j][r];
+      }
+    // values: A = V^T rows (channel 16 cb + l16), K-slot 4 j + r = token 16 j + 4 quad + r
+    const uint16_t* vt = tile + 32 * T::KROW;
+    if (quantized) {
+      const u32x4 bp = {f16pair(pv[0][0], pv[0][1]), f16pair(pv[0][2], pv[0][3]), f16pair(pv[1][0], pv[1][1]),
+                        f16pair(pv[1][2], pv[1][3])};
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const uint16_t* vr = vt + (16 * cb + l16) * T::VROW + 4 * quad;
+        const u32x2 a0 = *reinterpret_cast<const u32x2*>(vr), a1 = *reinterpret_cast<const u32x2*>(vr + 16);
+        acc_rot[cb] = mfma_f16(u32x4{a0[0], a0[1], a1[0], a1[1]}, bp, acc_rot[cb]);
+      }
+    } else {
+      uint32_t ph[4], pl[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float a = pv[i >> 1][2 * (i & 1)], c = pv[i >> 1][2 * (i & 1) + 1];
+        ph[i] = pack2(bf16_rne(a), bf16_rne(c));
+        pl[i] = pack2(bf16_rne(a - bf16_to_f32(ph[i] & 0xFFFFu)), bf16_rne(c - bf16_to_f32(ph[i] >> 16)));
+      }
+      const u32x4 bph = {ph[0], ph[1], ph[2], ph[3]}, bpl = {pl[0], pl[1], pl[2], pl[3]};
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const uint16_t* vr = vt + (16 * cb + l16) * T::VROW + 4 * quad;
+        const u32x2 a0 = *reinterpret_cast<const u32x2*>(vr), a1 = *reinterpret_cast<const u32x2*>(vr + 16);
+        const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
+        acc_raw[cb] = mfma_bf16(a, bpl, acc_raw[cb]);
+        acc_raw[cb] = mfma_bf16(a, bph, acc_raw[cb]);
+      }
+    }
+    if (NBUF == 1) lds_barrier();  // one buffer: the next step rewrites it
+  }
+
+  const float l_tot = wave_sum16(l_part);
+  constexpr int RF = 2 + 2 * D;
+  if (p.n_chunks > 1) {
+    // record of this chunk: [m][l][raw D][rot D] per column
+    float* rec = p.rec + (((size_t(unit) * p.n_ct + ct) * p.n_chunks + chunk) * size_t(16 * NWV) + 16 * wave + l16) * RF;
+    if (quad == 0) {
+      rec[0] = m_run;
+      rec[1] = l_tot;
+    }
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      *reinterpret_cast<f32x4*>(rec + 2 + 16 * cb + 4 * quad) = acc_raw[cb];
+      *reinterpret_cast<f32x4*>(rec + 2 + D + 16 * cb + 4 * quad) = acc_rot[cb];
+    }
+    return;
+  }
+  // ---- single chunk: out = (raw + rot R_V^T) / l ----
+  float* rot = fbuf + wave * 16 * D;
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) *reinterpret_cast<f32x4*>(rot + l16 * D + 16 * cb + 4 * quad) = acc_rot[cb];
+  finish_columns<D>(p.r_v + size_t(h) * D * D, rot, acc_raw, l_tot, col_ok,
+                    p.out + (size_t(row0 + ri) * p.Hq + h * G + hi) * D, l16, quad);
+}
+
+// Log-sum-exp merge of the chunk records of one (unit, column tile), then
+// the output rotation: out = (sum_k w_k raw_k + (sum_k w_k rot_k) R_V^T) /
+// sum_k w_k l_k with w_k = 2^(m_k - M).
+template <int D, int NWV, int MODE>
+__global__ __launch_bounds__(64 * NWV) void attend_merge_kernel(AttParams p) {
+  constexpr int NCB = D / 16, RF = 2 + 2 * D;
+  extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  float* fbuf = reinterpret_cast<float*>(lds);
+  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, quad = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int G = p.G;
+  const int ct = blockIdx.x % p.n_ct, unit = blockIdx.x / p.n_ct;
+  const UnitRows u = unit_rows<MODE>(p, unit);
+  if (MODE == 1 && u.P <= 0) return;
+  const int col0 = ct * 16 * NWV, n_cols = u.n_rows * G;
+  if (col0 >= n_cols) return;
+  const int col = col0 + 16 * wave + l16;
+  const bool col_ok = col < n_cols;
+  const int ri = col_ok ? col / G : 0, hi = col_ok ? col % G : 0;
+  const float* rec0 = p.rec + ((size_t(unit) * p.n_ct + ct) * p.n_chunks * size_t(16 * NWV) + 16 * wave + l16) * RF;
+  const size_t cstride = size_t(16 * NWV) * RF;
+  float M = kNegInfA;
+  for (int k = 0; k < p.n_chunks; ++k) M = fmaxf(M, rec0[k * cstride]);
+  float l = 0.f;
+  f32x4 raw[NCB], rotv[NCB];
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) raw[cb] = rotv[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0; k < p.n_chunks; ++k) {
+    const float* r = rec0 + k * cstride;
+    const float mk = r[0];
+    const float w = mk == kNegInfA ? 0.f : exp2f(mk - M);
+    l = __builtin_fmaf(w, r[1], l);
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      raw[cb] += w * *reinterpret_cast<const f32x4*>(r + 2 + 16 * cb + 4 * quad);
+      rotv[cb] += w * *reinterpret_cast<const f32x4*>(r + 2 + D + 16 * cb + 4 * quad);
+    }
+  }
+  float* rot = fbuf + wave * 16 * D;
+#pragma unroll
+  for (int cb = 0; cb < NCB; ++cb) *reinterpret_cast<f32x4*>(rot + l16 * D + 16 * cb + 4 * quad) = rotv[cb];
+  finish_columns<D>(p.r_v + size_t(u.h) * D * D, rot, raw, l, col_ok,
+                    p.out + (size_t(u.row0 + ri) * p.Hq + u.h * G + hi) * D, l16, quad);
+}
+
+}  // namespace
+
+namespace oscar_launch {
+
+size_t attend_lds_bytes(int d, bool extend) {
+  const int nwv = extend ? 4 : 1, nbuf = extend ? 2 : 1;
+  const size_t elems = d == 128 ? Tile<128>::ELEMS : Tile<64>::ELEMS;
+  return size_t(nbuf) * elems * 2 + size_t(nwv) * 16 * d * 4;
+}
+
+int attend_waves(bool extend) { return extend ? 4 : 1; }
+
+hipError_t paged_attend(int d, int bits, bool extend, const void* qpool, int n_qpages, const void* bf16_pool,
+                        int n_bpages, int n_kv, int G, int S, int W, int Hq, const void* q, const void* k_new,
+                        const void* v_new, const int32_t* cu, const int32_t* clen, int batch, const int32_t* bt_q,
+                        const int32_t* bt_h, int max_pages, const float* r_k, const float* r_v, float sm_scale,
+                        int n_ct, int n_chunks, int spc, float* rec, void* out, hipStream_t stream) {
+  AttParams p{static_cast<const uint8_t*>(qpool), std::max(1, n_qpages), static_cast<const uint16_t*>(bf16_pool),
+              std::max(1, n_bpages), n_kv, G, S, W, Hq, static_cast<const uint16_t*>(q),
+              static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new), cu, clen, bt_q, bt_h,
+              max_pages, r_k, r_v, sm_scale, n_ct, n_chunks, spc, rec, static_cast<uint16_t*>(out)};
+  const unsigned units = unsigned(batch) * unsigned(n_kv);
+  const dim3 grid(units * unsigned(n_ct) * unsigned(n_chunks));
+  const dim3 mgrid(units * unsigned(n_ct));
+  const size_t lds = attend_lds_bytes(d, extend);
+  const size_t mlds = size_t(attend_waves(extend)) * 16 * d * 4;
+#define OSCAR_ATTEND(DD, BB, NW, MM)                                                                        \
+  do {                                                                                                      \
+    hipLaunchKernelGGL((attend_kernel<DD, BB, NW, MM>), grid, dim3(64 * NW), lds, stream, p);               \
+    if (n_chunks > 1) hipLaunchKernelGGL((attend_merge_kernel<DD, NW, MM>), mgrid, dim3(64 * NW), mlds, stream, p); \
+  } while (0)
+  if (d == 128) {
+    if (extend) { if (bits == 2) OSCAR_ATTEND(128, 2, 4, 0); else OSCAR_ATTEND(128, 4, 4, 0); }
+    else { if (bits == 2) OSCAR_ATTEND(128, 2, 1, 1); else OSCAR_ATTEND(128, 4, 1, 1); }
+  } else {
+    if (extend) { if (bits == 2) OSCAR_ATTEND(64, 2, 4, 0); else OSCAR_ATTEND(64, 4, 4, 0); }
+    else { if (bits == 2) OSCAR_ATTEND(64, 2, 1, 1); else OSCAR_ATTEND(64, 4, 1, 1); }
+  }
+#undef OSCAR_ATTEND
+  return hipGetLastError();
+}
+
+}  // namespace oscar_launch

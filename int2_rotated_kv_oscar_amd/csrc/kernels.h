@@ -7,7 +7,7 @@
 
 namespace oscar_launch {
 
-hipError_t quantize_append(int d, int n_kv, void* pool, const void* k_new, const void* v_new, int64_t n_rows,
+hipError_t quantize_append(int d, int bits, int n_kv, void* pool, const void* k_new, const void* v_new, int64_t n_rows,
                            const int32_t* row_seq, const int32_t* row_pos, const int32_t* bt_q,
                            int32_t max_pages, const float* r_k, const float* r_v, float tau_k, float tau_v,
                            int n_cus, hipStream_t stream);
@@ -34,5 +34,15 @@ hipError_t paged_decode(int d, bool all_raw, const void* int2_pool, int n_int2_p
                         bool per_unit, int unit_items, int fixed_ppw, int n_wg, int cap, int max_seq_len,
                         float* partials, int32_t* counters, int rec_floats, void* out, bool speculate,
                         hipStream_t stream);
+
+// paged attention with many query columns (extend: chunked prefill over
+// INT2/INT4 pages; otherwise decode over an INT4 cache), and its merge
+size_t attend_lds_bytes(int d, bool extend);
+int attend_waves(bool extend);
+hipError_t paged_attend(int d, int bits, bool extend, const void* qpool, int n_qpages, const void* bf16_pool,
+                        int n_bpages, int n_kv, int G, int S, int W, int Hq, const void* q, const void* k_new,
+                        const void* v_new, const int32_t* cu, const int32_t* clen, int batch, const int32_t* bt_q,
+                        const int32_t* bt_h, int max_pages, const float* r_k, const float* r_v, float sm_scale,
+                        int n_ct, int n_chunks, int spc, float* rec, void* out, hipStream_t stream);
 
 }  // namespace oscar_launch

@@ -20,4 +20,27 @@ struct Geo {
   static constexpr int BF16_HEAD_ELEMS = 32 * D;  // K [16][D] then V [D][16]
 };
 
+// INT4 page-head (the 16-level variant): K codes [16 slots][D/2] bytes, V
+// codes [16][D/2] (channel 2i in the low nibble of byte i), then f16 K
+// scales, K zeros, V scales, V zeros, each [16 slots][NG].
+template <int D>
+struct Geo4 {
+  static constexpr int NG = D / 32;
+  static constexpr int HEAD_BYTES = 20 * D;
+  static constexpr int KC = 0;
+  static constexpr int VC = 8 * D;
+  static constexpr int KS = 16 * D;
+  static constexpr int KZ = 16 * D + 32 * NG;
+  static constexpr int VS = 16 * D + 64 * NG;
+  static constexpr int VZ = 16 * D + 96 * NG;
+};
+
+// The quantized page-head of a code width: Geo (INT2) or Geo4 (INT4).
+template <int D, int BITS>
+struct QLayout;
+template <int D>
+struct QLayout<D, 2> : Geo<D> {};
+template <int D>
+struct QLayout<D, 4> : Geo4<D> {};
+
 }  // namespace oscar_dev

@@ -67,12 +67,13 @@ struct TileMeta {
 // the reciprocal's error happens to fall on.  s = 0 gives inv = 0 and code 0.
 constexpr float kMagic = 12582912.0f;
 constexpr uint32_t kMagicBits = 0x4B400000u;
+template <int TOP = 3>
 __device__ __forceinline__ uint32_t code_bits(float v, float z, float inv, float s) {
   const float d = v - z;
   const float t0 = d * inv;
   const float t = __builtin_fmaf(__builtin_fmaf(-t0, s, d), inv, t0);
   const int b = __float_as_int(t + kMagic);
-  return uint32_t(min(max(b, int(kMagicBits)), int(kMagicBits + 3u)));
+  return uint32_t(min(max(b, int(kMagicBits)), int(kMagicBits + uint32_t(TOP))));
 }
 
 // r / 3: the product with 1/3 refined once with its exact residual, so that
@@ -80,10 +81,12 @@ __device__ __forceinline__ uint32_t code_bits(float v, float z, float inv, float
 // rotated values (a Hadamard or identity rotation of bf16 rows) the range is
 // often three times an f16 rounding midpoint; the exact quotient then rounds
 // to even on the way to f16, as the definition's real-number division does.
+// The 16-level variant divides by 15 the same way.
+template <int TOP = 3>
 __device__ __forceinline__ float div3(float r) {
-  constexpr float kThird = 1.0f / 3.0f;
-  const float s0 = r * kThird;
-  return __builtin_fmaf(__builtin_fmaf(-3.0f, s0, r), kThird, s0);
+  constexpr float kInv = 1.0f / float(TOP);
+  const float s0 = r * kInv;
+  return __builtin_fmaf(__builtin_fmaf(-float(TOP), s0, r), kInv, s0);
 }
 
 // Reduction over the four lanes l16 + 16q of a row: the minimum of mn and the
@@ -122,10 +125,14 @@ struct QAShared {
   int32_t rexp[2][16];      // per-row power-of-two prescale of the x tile
 };
 
-// ONE: every workgroup has exactly one tile (a decode step's appends)
-template <int D, int TENSOR, bool ONE>
+// ONE: every workgroup has exactly one tile (a decode step's appends).
+// BITS: 2 (the INT2 cache, MFMA-shaped code words) or 4 (the INT4 variant,
+// row-owned nibbles: each wave stores its group's codes of a row directly).
+template <int D, int TENSOR, bool ONE, int BITS>
 __device__ void qa_tiles(const QAParams& p, int h, QAShared<D, ONE>& sh) {
   using GG = Geo<D>;
+  using QL = QLayout<D, BITS>;
+  constexpr int TOP = (1 << BITS) - 1;
   constexpr int NG = GG::NG, NKB = GG::NKB, NW = GG::NW;
   constexpr int kX = QAShared<D, ONE>::kX, kS = QAShared<D, ONE>::kS;
   constexpr int kRowBytes = QAShared<D, ONE>::kRowBytes;
@@ -225,15 +232,20 @@ __device__ void qa_tiles(const QAParams& p, int h, QAShared<D, ONE>& sh) {
     word0 = 0u - ((kMagicBits << vsh0) + (kMagicBits << vsh1));
   }
 
-  // stores of a finished tile: wave 0 the codes, wave 1 the scales/zeros
+  // f16 index of the scale/zero of (slot m, group gg) inside its area: K
+  // (and every INT4 area) [16][NG], INT2 V in token-quad order [4][NG][4]
+  auto sz_index = [](int m, int gg) {
+    return (TENSOR == 0 || BITS == 4) ? m * NG + gg : ((m >> 2) * NG + gg) * 4 + (m & 3);
+  };
+  // stores of a finished tile: wave 0 the INT2 codes, wave 1 the scales/zeros
   auto store_tile = [&](const TileMeta& mc, int buf) {
     if (g > 1) return;
     if (g == 1) {
       if (mc.aligned) {
         // scale and zero areas of the page are contiguous: 2 x 32 NG bytes
         const int page0 = __builtin_amdgcn_readfirstlane(mc.page);
-        uint8_t* base = p.pool + (int64_t(page0) * p.n_kv + h) * int64_t(GG::HEAD_BYTES);
-        uint32_t* dst = reinterpret_cast<uint32_t*>(base + (TENSOR == 0 ? GG::KS : GG::VS));
+        uint8_t* base = p.pool + (int64_t(page0) * p.n_kv + h) * int64_t(QL::HEAD_BYTES);
+        uint32_t* dst = reinterpret_cast<uint32_t*>(base + (TENSOR == 0 ? QL::KS : QL::VS));
         if (lane < 16 * NG) dst[lane] = s_sz[buf][lane];
       } else {
         // lane j: row m = j / NG, group gg = j % NG, to that row's page and slot
@@ -242,15 +254,15 @@ __device__ void qa_tiles(const QAParams& p, int h, QAShared<D, ONE>& sh) {
         const bool valid = __shfl(int(mc.valid), m, 64) != 0;
         if (lane < 16 * NG && valid) {
           const uint16_t* sz16 = reinterpret_cast<const uint16_t*>(s_sz[buf]);
-          const int ia = TENSOR == 0 ? m * NG + gg : ((m >> 2) * NG + gg) * 4 + (m & 3);
-          const int iu = TENSOR == 0 ? slot * NG + gg : ((slot >> 2) * NG + gg) * 4 + (slot & 3);
-          uint8_t* base = p.pool + (int64_t(page) * p.n_kv + h) * int64_t(GG::HEAD_BYTES);
-          reinterpret_cast<uint16_t*>(base + (TENSOR == 0 ? GG::KS : GG::VS))[iu] = sz16[ia];
-          reinterpret_cast<uint16_t*>(base + (TENSOR == 0 ? GG::KZ : GG::VZ))[iu] = sz16[16 * NG + ia];
+          const int ia = sz_index(m, gg), iu = sz_index(slot, gg);
+          uint8_t* base = p.pool + (int64_t(page) * p.n_kv + h) * int64_t(QL::HEAD_BYTES);
+          reinterpret_cast<uint16_t*>(base + (TENSOR == 0 ? QL::KS : QL::VS))[iu] = sz16[ia];
+          reinterpret_cast<uint16_t*>(base + (TENSOR == 0 ? QL::KZ : QL::VZ))[iu] = sz16[16 * NG + ia];
         }
       }
       return;
     }
+    if (BITS == 4) return;  // INT4 codes were stored by their waves
     uint32_t wd[NW];
 #pragma unroll
     for (int w = 0; w < NW; ++w) wd[w] = s_part[buf][2 * w][lane] | s_part[buf][2 * w + 1][lane];
@@ -289,7 +301,7 @@ __device__ void qa_tiles(const QAParams& p, int h, QAShared<D, ONE>& sh) {
     }
   };
 
-  auto epilogue = [&](const f32x4 (&acc)[2], int rexp, int buf) {
+  auto epilogue = [&](const f32x4 (&acc)[2], int rexp, int buf, const TileMeta& mc) {
     // ---- group g of row m = l16: acc[hb][r] = y / F for channel
     // 32g + 16hb + 4quad + r, F = 2^(e - 8) (R scale and row prescale); the
     // clip, the statistics and the codes run on acc with F folded in ----
@@ -307,15 +319,29 @@ __device__ void qa_tiles(const QAParams& p, int h, QAShared<D, ONE>& sh) {
     row_min_max(mn, mx);
     // s = (max - min) / 3 and z = min in true units (F is a power of two:
     // the scalings are exact), rounded to f16; codes against the f16 values
-    const uint32_t s16 = f16_bits(div3(mx - mn) * F);
+    const uint32_t s16 = f16_bits(div3<TOP>(mx - mn) * F);
     const uint32_t z16 = f16_bits(mn * F);
     const float sf = f16_to_f32(s16);
     const float inv = sf == 0.0f ? 0.0f : __builtin_amdgcn_rcpf(sf);  // s16 = 0: every code is 0
     const float zr = f16_to_f32(z16) * iF;  // (y - z) / s = (acc - z/F) / (s/F)
     const float invr = inv * F, sr = sf * iF;
     const int m = l16;
-    uint32_t bits;
-    if (TENSOR == 0) {
+    uint32_t bits = 0;
+    if (BITS == 4) {
+      // row m owns bytes [16 g, 16 g + 16) of its code row: channels
+      // 32g + 16hb + 4quad + r as nibbles r of the 16-bit word at byte 16g + 8hb + 2quad
+      if (mc.valid) {
+        uint8_t* base = p.pool + (int64_t(mc.page) * p.n_kv + h) * int64_t(QL::HEAD_BYTES) +
+                        (TENSOR == 0 ? QL::KC : QL::VC) + mc.slot * (D / 2) + 16 * g + 2 * quad;
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+          uint32_t w16 = 0;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) w16 |= (code_bits<TOP>(y[hb][r], zr, invr, sr) - kMagicBits) << (4 * r);
+          *reinterpret_cast<uint16_t*>(base + 8 * hb) = uint16_t(w16);
+        }
+      }
+    } else if (TENSOR == 0) {
       bits = word0;
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
@@ -336,9 +362,9 @@ __device__ void qa_tiles(const QAParams& p, int h, QAShared<D, ONE>& sh) {
         bits = (m & 3) == r ? wr : bits;
       }
     }
-    s_part[buf][g][pidx] = bits;
+    if (BITS == 2) s_part[buf][g][pidx] = bits;
     if (quad == 0) {  // in the page-area order of an aligned tile (slot = m)
-      const int ia = TENSOR == 0 ? m * NG + g : ((m >> 2) * NG + g) * 4 + (m & 3);
+      const int ia = sz_index(m, g);
       uint16_t* sz16 = reinterpret_cast<uint16_t*>(s_sz[buf]);
       sz16[ia] = uint16_t(s16);
       sz16[16 * NG + ia] = uint16_t(z16);
@@ -433,21 +459,21 @@ __device__ void qa_tiles(const QAParams& p, int h, QAShared<D, ONE>& sh) {
 #pragma unroll
           for (int j = 1; j >= 0; --j)  // lo, then hi
             acc[hb] = mfma_f16(rop[hb][kb][j], xc[kb], acc[hb]);
-      epilogue(acc, s_rexp[buf][l16], buf);
+      epilogue(acc, s_rexp[buf][l16], buf, mc);
     }
     mprev = mc;
   }
   wait_vm<0>();  // no ring request lands after the workgroup ends
 }
 
-template <int D, bool ONE>
+template <int D, bool ONE, int BITS>
 __global__ __launch_bounds__(64 * (D / 32), 4) void quantize_append_kernel(QAParams p) {
   __shared__ QAShared<D, ONE> sh;
   const int h = blockIdx.y;
   if (blockIdx.z == 0)
-    qa_tiles<D, 0, ONE>(p, h, sh);
+    qa_tiles<D, 0, ONE, BITS>(p, h, sh);
   else
-    qa_tiles<D, 1, ONE>(p, h, sh);
+    qa_tiles<D, 1, ONE, BITS>(p, h, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -471,9 +497,11 @@ constexpr int kRowsPerWg = 8;
 constexpr int kRowThreads = 256;
 constexpr int64_t kFewRows = 64;  // row counts up to this take the few-row kernel
 
-template <int D, bool STEP>
+template <int D, bool STEP, int BITS>
 __global__ __launch_bounds__(kRowThreads) void quantize_rows_kernel(QAParams p) {
   using GG = Geo<D>;
+  using QL = QLayout<D, BITS>;
+  constexpr int TOP = (1 << BITS) - 1;
   constexpr int NG = GG::NG, NW = GG::NW;
   constexpr int KS_PER = D / 16;  // reduction length of one k-slice (16 slices)
   const int tid = threadIdx.x;
@@ -596,11 +624,11 @@ __global__ __launch_bounds__(kRowThreads) void quantize_rows_kernel(QAParams p) 
       mn = fminf(mn, __shfl_xor(mn, m, 64));
       mx = fmaxf(mx, __shfl_xor(mx, m, 64));
     }
-    const uint32_t s16 = f16_bits(div3(mx - mn));
+    const uint32_t s16 = f16_bits(div3<TOP>(mx - mn));
     const uint32_t z16 = f16_bits(mn);
     const float sf = f16_to_f32(s16), zf = f16_to_f32(z16);
     int code = 0;
-    if (sf != 0.0f) code = min(max(int(__builtin_rintf((y[gp] - zf) / sf)), 0), 3);
+    if (sf != 0.0f) code = min(max(int(__builtin_rintf((y[gp] - zf) / sf)), 0), TOP);
     s_code[rw][32 * gp + cc] = uint8_t(code);
     if (cc == 0) {
       s_sz[rw][gp][0] = uint16_t(s16);
@@ -616,10 +644,10 @@ __global__ __launch_bounds__(kRowThreads) void quantize_rows_kernel(QAParams p) 
   // f16 scale and zero of each (row, group of the pair)
   if (tid < 2 * nr && s_page[tid >> 1] >= 0) {
     const int row = tid >> 1, gp = tid & 1, g = 2 * pair + gp, slot = s_slot[row];
-    uint8_t* base = p.pool + (int64_t(s_page[row]) * p.n_kv + h) * int64_t(GG::HEAD_BYTES);
-    const int iu = tensor == 0 ? slot * NG + g : ((slot >> 2) * NG + g) * 4 + (slot & 3);
-    reinterpret_cast<uint16_t*>(base + (tensor == 0 ? GG::KS : GG::VS))[iu] = s_sz[row][gp][0];
-    reinterpret_cast<uint16_t*>(base + (tensor == 0 ? GG::KZ : GG::VZ))[iu] = s_sz[row][gp][1];
+    uint8_t* base = p.pool + (int64_t(s_page[row]) * p.n_kv + h) * int64_t(QL::HEAD_BYTES);
+    const int iu = (tensor == 0 || BITS == 4) ? slot * NG + g : ((slot >> 2) * NG + g) * 4 + (slot & 3);
+    reinterpret_cast<uint16_t*>(base + (tensor == 0 ? QL::KS : QL::VS))[iu] = s_sz[row][gp][0];
+    reinterpret_cast<uint16_t*>(base + (tensor == 0 ? QL::KZ : QL::VZ))[iu] = s_sz[row][gp][1];
   }
 
   // code fields of the page layout.  K, row slot m: word (quad 16 + m) NW + pair
@@ -627,7 +655,16 @@ __global__ __launch_bounds__(kRowThreads) void quantize_rows_kernel(QAParams p) 
   // 16 (r % 2) + 8 gp + 4 hb + 2 (r / 2).  V, row slot t = 4q + r: the byte
   // 2 (r % 2) + r / 2 of word (q 16 + c16) NW + pair holds channel 16 bb + c16
   // of the pair at bit 2 bb.
-  if (tensor == 0) {
+  if (BITS == 4) {
+    // INT4: the pair's 64 channels are bytes [32 pair, 32 pair + 32) of the row
+    // (channel 2i in the low nibble of byte i)
+    if (tid < 32 * nr && s_page[tid >> 5] >= 0) {
+      const int row = tid >> 5, bi = tid & 31, slot = s_slot[row];
+      uint8_t* base = p.pool + (int64_t(s_page[row]) * p.n_kv + h) * int64_t(QL::HEAD_BYTES);
+      base[(tensor == 0 ? QL::KC : QL::VC) + slot * (D / 2) + 32 * pair + bi] =
+          uint8_t(s_code[row][2 * bi] | (s_code[row][2 * bi + 1] << 4));
+    }
+  } else if (tensor == 0) {
     if (tid < 4 * nr && s_page[tid >> 2] >= 0) {
       const int row = tid >> 2, quad = tid & 3, slot = s_slot[row];
       uint32_t w = 0;
@@ -652,7 +689,7 @@ __global__ __launch_bounds__(kRowThreads) void quantize_rows_kernel(QAParams p) 
       base[GG::VC + ((q * 16 + c16) * NW + pair) * 4 + 2 * (r & 1) + (r >> 1)] = uint8_t(bits);
     }
   }
-  if (STEP && pair == 0) {
+  if (STEP && BITS == 2 && pair == 0) {
     // the new tokens to their BF16 slots (the first group pair's workgroups)
     const int rw2 = tid >> 5;
     if (rw2 < nr && s_new[rw2] >= 0) {
@@ -671,7 +708,7 @@ __global__ __launch_bounds__(kRowThreads) void quantize_rows_kernel(QAParams p) 
 
 namespace oscar_launch {
 
-hipError_t quantize_append(int d, int n_kv, void* pool, const void* k_new, const void* v_new, int64_t n_rows,
+hipError_t quantize_append(int d, int bits, int n_kv, void* pool, const void* k_new, const void* v_new, int64_t n_rows,
                            const int32_t* row_seq, const int32_t* row_pos, const int32_t* bt_q,
                            int32_t max_pages, const float* r_k, const float* r_v, float tau_k, float tau_v,
                            int n_cus, hipStream_t stream) {
@@ -683,8 +720,13 @@ hipError_t quantize_append(int d, int n_kv, void* pool, const void* k_new, const
     // few rows: plain float32 products, a slice of R per workgroup
     const dim3 grid(static_cast<unsigned>((n_rows + kRowsPerWg - 1) / kRowsPerWg), static_cast<unsigned>(n_kv),
                     static_cast<unsigned>(d / 32));  // (tensor, group pair)
-    if (d == 128) hipLaunchKernelGGL((quantize_rows_kernel<128, false>), grid, dim3(kRowThreads), 0, stream, p);
-    else hipLaunchKernelGGL((quantize_rows_kernel<64, false>), grid, dim3(kRowThreads), 0, stream, p);
+    if (bits == 4) {
+      if (d == 128) hipLaunchKernelGGL((quantize_rows_kernel<128, false, 4>), grid, dim3(kRowThreads), 0, stream, p);
+      else hipLaunchKernelGGL((quantize_rows_kernel<64, false, 4>), grid, dim3(kRowThreads), 0, stream, p);
+    } else {
+      if (d == 128) hipLaunchKernelGGL((quantize_rows_kernel<128, false, 2>), grid, dim3(kRowThreads), 0, stream, p);
+      else hipLaunchKernelGGL((quantize_rows_kernel<64, false, 2>), grid, dim3(kRowThreads), 0, stream, p);
+    }
     return hipGetLastError();
   }
   const int64_t tiles = (n_rows + 15) / 16;
@@ -692,13 +734,15 @@ hipError_t quantize_append(int d, int n_kv, void* pool, const void* k_new, const
   const dim3 grid(static_cast<unsigned>(std::min(tiles, per_pair)), static_cast<unsigned>(n_kv), 2u);
   // one tile per workgroup (few rows, as in a decode step): the unpipelined variant
   const bool one = tiles <= per_pair;
-  if (d == 128) {
-    if (one) hipLaunchKernelGGL((quantize_append_kernel<128, true>), grid, dim3(256), 0, stream, p);
-    else hipLaunchKernelGGL((quantize_append_kernel<128, false>), grid, dim3(256), 0, stream, p);
+#define OSCAR_QA(DD, ONE_, BB) hipLaunchKernelGGL((quantize_append_kernel<DD, ONE_, BB>), grid, dim3(2 * DD), 0, stream, p)
+  if (bits == 4) {
+    if (d == 128) { if (one) OSCAR_QA(128, true, 4); else OSCAR_QA(128, false, 4); }
+    else { if (one) OSCAR_QA(64, true, 4); else OSCAR_QA(64, false, 4); }
   } else {
-    if (one) hipLaunchKernelGGL((quantize_append_kernel<64, true>), grid, dim3(128), 0, stream, p);
-    else hipLaunchKernelGGL((quantize_append_kernel<64, false>), grid, dim3(128), 0, stream, p);
+    if (d == 128) { if (one) OSCAR_QA(128, true, 2); else OSCAR_QA(128, false, 2); }
+    else { if (one) OSCAR_QA(64, true, 2); else OSCAR_QA(64, false, 2); }
   }
+#undef OSCAR_QA
   return hipGetLastError();
 }
 
@@ -711,8 +755,8 @@ hipError_t decode_step_update(int d, int n_kv, int n_sink, int n_recent, void* i
              seq_lens, bt_h, static_cast<uint16_t*>(bf16_pool), n_sink, n_recent};
   const dim3 grid(static_cast<unsigned>((batch + kRowsPerWg - 1) / kRowsPerWg), static_cast<unsigned>(n_kv),
                   static_cast<unsigned>(d / 32));
-  if (d == 128) hipLaunchKernelGGL((quantize_rows_kernel<128, true>), grid, dim3(kRowThreads), 0, stream, p);
-  else hipLaunchKernelGGL((quantize_rows_kernel<64, true>), grid, dim3(kRowThreads), 0, stream, p);
+  if (d == 128) hipLaunchKernelGGL((quantize_rows_kernel<128, true, 2>), grid, dim3(kRowThreads), 0, stream, p);
+  else hipLaunchKernelGGL((quantize_rows_kernel<64, true, 2>), grid, dim3(kRowThreads), 0, stream, p);
   return hipGetLastError();
 }
 

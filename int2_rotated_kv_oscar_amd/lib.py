@@ -28,6 +28,8 @@ EXPORTS = [
     "oscar_write_bf16", "oscar_decode_step_update", "oscar_decode_workspace_bytes", "oscar_calib_gram",
     "oscar_build_rotation_from_targets", "oscar_decode_workspace_init", "oscar_paged_decode_attn",
     "oscar_paged_decode_attn_bf16", "oscar_bw_probe_read", "oscar_paged_decode_attn_noalloc",
+    "oscar_int4_page_bytes", "oscar_quantize_append_int4", "oscar_extend_workspace_bytes",
+    "oscar_paged_extend_attn", "oscar_decode_int4_workspace_bytes", "oscar_paged_decode_attn_int4",
 ]
 
 
@@ -86,6 +88,17 @@ def load(path: str = LIB_PATH):
         "oscar_paged_decode_attn_bf16": (_STATUS, [ctypes.POINTER(OscarCache), _P, _I32, _I32, _P, _I32, _P, _I32,
                                                    _F32, _I32, _P, _SZ, _P, _P]),
         "oscar_bw_probe_read": (_STATUS, [_P, _SZ, _P, _P]),
+        "oscar_int4_page_bytes": (_SZ, [_I32, _I32]),
+        "oscar_quantize_append_int4": (_STATUS, [ctypes.POINTER(OscarCache), _P, _P, _I64, _P, _P, _P, _I32, _P, _P,
+                                                 _F32, _F32, _P]),
+        "oscar_extend_workspace_bytes": (_STATUS, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                   ctypes.POINTER(_SZ)]),
+        "oscar_paged_extend_attn": (_STATUS, [ctypes.POINTER(OscarCache), _I32, _P, _P, _P, _I32, _I32, _P, _P, _I32,
+                                              _I32, _P, _P, _I32, _P, _P, _F32, _I32, _P, _SZ, _P, _P]),
+        "oscar_decode_int4_workspace_bytes": (_STATUS, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
+                                                        ctypes.POINTER(_SZ)]),
+        "oscar_paged_decode_attn_int4": (_STATUS, [ctypes.POINTER(OscarCache), _P, _I32, _I32, _P, _I32, _P, _P, _I32,
+                                                   _P, _P, _F32, _I32, _P, _SZ, _P, _P]),
         "oscar_paged_decode_attn_noalloc": (_STATUS, [ctypes.POINTER(OscarCache), _P, _I32, _I32, _P, _I32, _P, _P,
                                                       _I32, _P, _P, _F32, _I32, _P, _P]),
     }
@@ -189,12 +202,19 @@ def _stream(stream) -> Optional[int]:
     return s.cuda_stream
 
 
-def make_cache(d: int, n_kv_heads: int, n_sink: int, n_recent: int, int2_pool=None, bf16_pool=None) -> OscarCache:
+def int4_page_bytes(d: int, n_kv_heads: int) -> int:
+    return load().oscar_int4_page_bytes(d, n_kv_heads)
+
+
+def make_cache(d: int, n_kv_heads: int, n_sink: int, n_recent: int, int2_pool=None, bf16_pool=None,
+               code_bits: int = 2) -> OscarCache:
+    """The cache description; with code_bits = 4 the quantized pool is an INT4 pool."""
     c = OscarCache()
     c.d, c.n_kv_heads, c.n_sink, c.n_recent = d, n_kv_heads, n_sink, n_recent
     if int2_pool is not None:
         c.int2_pool = _dptr(int2_pool)
-        c.n_int2_pages = int2_pool.numel() * int2_pool.element_size() // int2_page_bytes(d, n_kv_heads)
+        pb = int2_page_bytes(d, n_kv_heads) if code_bits == 2 else int4_page_bytes(d, n_kv_heads)
+        c.n_int2_pages = int2_pool.numel() * int2_pool.element_size() // pb
     if bf16_pool is not None:
         c.bf16_pool = _dptr(bf16_pool)
         c.n_bf16_pages = bf16_pool.numel() * bf16_pool.element_size() // bf16_page_bytes(d, n_kv_heads)
@@ -208,6 +228,15 @@ def quantize_append(cache: OscarCache, k_new, v_new, row_seq, row_pos, bt_q, r_k
     _check(load().oscar_quantize_append(ctypes.byref(cache), _dptr(k_new), _dptr(v_new), n, _dptr(row_seq),
                                         _dptr(row_pos), _dptr(bt_q), bt_q.shape[1], _dptr(r_k), _dptr(r_v),
                                         float(tau_k), float(tau_v), _stream(stream)))
+
+
+def quantize_append_int4(cache: OscarCache, k_new, v_new, row_seq, row_pos, bt_q, r_k, r_v, tau_k: float,
+                         tau_v: float, stream=None):
+    """As quantize_append, into INT4 pages."""
+    n = k_new.shape[0]
+    _check(load().oscar_quantize_append_int4(ctypes.byref(cache), _dptr(k_new), _dptr(v_new), n, _dptr(row_seq),
+                                             _dptr(row_pos), _dptr(bt_q), bt_q.shape[1], _dptr(r_k), _dptr(r_v),
+                                             float(tau_k), float(tau_v), _stream(stream)))
 
 
 def write_bf16(cache: OscarCache, k_new, v_new, row_seq, row_pos, bt_h, stream=None):
@@ -282,3 +311,45 @@ def paged_decode_attn_noalloc(cache: OscarCache, q, seq_lens, max_seq_len: int, 
 def bw_probe_read(buf, sink, stream=None):
     """One streaming read of the device tensor ``buf`` (nothing written back)."""
     _check(load().oscar_bw_probe_read(_dptr(buf), buf.numel() * buf.element_size(), _dptr(sink), _stream(stream)))
+
+
+def extend_workspace_bytes(batch: int, n_kv_heads: int, n_q_heads: int, d: int, n_sink: int, n_recent: int,
+                           max_cache_len: int, max_new: int, split_steps: int = 0) -> int:
+    out = _SZ()
+    _check(load().oscar_extend_workspace_bytes(batch, n_kv_heads, n_q_heads, d, n_sink, n_recent, max_cache_len,
+                                               max_new, split_steps, ctypes.byref(out)))
+    return out.value
+
+
+def paged_extend_attn(cache: OscarCache, code_bits: int, q, k_new, v_new, cu_rows, cache_lens, max_cache_len: int,
+                      max_new: int, bt_q, bt_h, r_k, r_v, out, workspace=None, sm_scale: Optional[float] = None,
+                      split_steps: int = 0, stream=None):
+    """q bf16 [T, H_q, d], k_new/v_new bf16 [T, H_kv, d], cu_rows int32 [B + 1], cache_lens int32 [B]."""
+    B = cache_lens.shape[0]
+    hq, d = q.shape[1], q.shape[2]
+    sc = 1.0 / np.sqrt(d) if sm_scale is None else sm_scale
+    ws = _dptr(workspace) if workspace is not None else None
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().oscar_paged_extend_attn(ctypes.byref(cache), code_bits, _dptr(q), _dptr(k_new), _dptr(v_new), B, hq,
+                                          _dptr(cu_rows), _dptr(cache_lens), max_cache_len, max_new, _dptr(bt_q),
+                                          _dptr(bt_h), bt_h.shape[1], _dptr(r_k), _dptr(r_v), sc, split_steps, ws, wsb,
+                                          _dptr(out), _stream(stream)))
+
+
+def decode_int4_workspace_bytes(batch: int, n_kv_heads: int, n_q_heads: int, d: int, n_sink: int, n_recent: int,
+                                max_seq_len: int, split_steps: int = 0) -> int:
+    out = _SZ()
+    _check(load().oscar_decode_int4_workspace_bytes(batch, n_kv_heads, n_q_heads, d, n_sink, n_recent, max_seq_len,
+                                                    split_steps, ctypes.byref(out)))
+    return out.value
+
+
+def paged_decode_attn_int4(cache: OscarCache, q, seq_lens, max_seq_len: int, bt_q, bt_h, r_k, r_v, out,
+                           workspace=None, sm_scale: Optional[float] = None, split_steps: int = 0, stream=None):
+    B, hq, d = q.shape
+    sc = 1.0 / np.sqrt(d) if sm_scale is None else sm_scale
+    ws = _dptr(workspace) if workspace is not None else None
+    wsb = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().oscar_paged_decode_attn_int4(ctypes.byref(cache), _dptr(q), B, hq, _dptr(seq_lens), max_seq_len,
+                                               _dptr(bt_q), _dptr(bt_h), bt_h.shape[1], _dptr(r_k), _dptr(r_v), sc,
+                                               split_steps, ws, wsb, _dptr(out), _stream(stream)))
