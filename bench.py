@@ -135,6 +135,12 @@ def main() -> int:
                     help="measure quantize-append alone on the large-GQA layer's prefill (8 sequences x 8192 rows)")
     ap.add_argument("--calib-gram", action="store_true",
                     help="measure the GPU calibration target (Q^T Q per KV head) on the Qwen3-8B calibration rows")
+    ap.add_argument("--extend", action="store_true",
+                    help="measure chunked-prefill attention alone: the 28-sequence Qwen3-8B cache, 512 new rows each")
+    ap.add_argument("--int4", action="store_true",
+                    help="measure the INT4-cache decode alone on the workload's shape")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="leave the extend and INT4-decode lines out of the default run")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported (the decode path shards by KV head "
@@ -177,6 +183,12 @@ def main() -> int:
         return run_append_prefill(args, log)
     if args.calib_gram:
         return run_calib_gram(args, log)
+    if args.extend:
+        print(json.dumps(extend_line(args, log, cpu=not args.no_cpu_baseline)), flush=True)
+        return 0
+    if args.int4:
+        print(json.dumps(int4_decode_line(args, log, w, cpu=not args.no_cpu_baseline)), flush=True)
+        return 0
     t0 = time.time()
     inp = synth.decode_inputs(w)
     log(f"inputs {time.time() - t0:.1f}s  B={len(inp.seq_lens)} max_len={inp.max_seq_len}")
@@ -399,6 +411,11 @@ def main() -> int:
     if not args.no_append:
         # kernel A alone on the large-GQA layer's prefill, its own roofline
         result["quantize_append"] = append_prefill_line(args, log, cpu=False)
+    if not args.no_extras:
+        # the rows beside the decode: chunked prefill over the mixed cache and
+        # the INT4-cache decode, each with its own roofline
+        result["extend"] = extend_line(args, log, cpu=False)
+        result["int4_decode"] = int4_decode_line(args, log, w, cpu=False)
 
     if not args.no_cpu_baseline:
         cores = len(os.sched_getaffinity(0))
@@ -506,6 +523,228 @@ def append_prefill_line(args, log, cpu: bool) -> dict:
     del sets, base
     torch.cuda.empty_cache()
     return result
+
+
+EXTEND_METRIC = "chunked-prefill attention new rows/s + MFMA TFLOP/s (% of dense bf16 peak), Qwen3-8B layer"
+MFMA_PEAK_TFLOPS = 2500.0
+
+
+def extend_flops(cache_lens, n_new, n_q_heads: int, d: int) -> int:
+    """Algorithmic flops of one extend call: per new row i of a sequence with
+    P cached tokens, per query head, 2 d multiply-adds for each of the
+    P + i + 1 keys it attends (q k and p v)."""
+    tot = 0
+    for P, n in zip(cache_lens, n_new):
+        P, n = int(P), int(n)
+        tot += n * P + n * (n + 1) // 2
+    return 4 * d * n_q_heads * tot
+
+
+def extend_line(args, log, cpu: bool) -> dict:
+    """Chunked prefill ("extend") over the mixed INT2 cache: the 28-sequence
+    Qwen3-8B batch (ragged cached contexts, a 1024-token prefix shared by all)
+    each extended by a chunk of 512 new rows, causal.  Launches rotate over
+    cache copies totalling >= 1 GiB; HIP events on the launch stream."""
+    import torch
+    from int2_rotated_kv_oscar_amd import lib, synth
+    dev = "cuda:0"
+    w = synth.WORKLOADS["qwen3-8b-b28-ragged"]
+    n_new = 512
+    t0 = time.time()
+    inp = synth.decode_inputs(w)
+    B = len(inp.seq_lens)
+    cu = np.arange(B + 1, dtype=np.int32) * n_new
+    rng = synth.rng_for(w.cfg_id, 100)
+    kn, vn = synth.kv_rows(rng, B * n_new, w)
+    qn = synth.q_rows(rng, B * n_new, w, synth.query_mixers(w))
+    cal = synth.calibration_set(w, n_rows=1024)
+    rt = lib.build_rotation(cal.q, cal.k, cal.v, w.group_q)
+    log(f"extend inputs + calibration {time.time() - t0:.1f}s")
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    r_k = torch.from_numpy(rt["r_k"].astype(np.float32)).to(dev)
+    r_v = torch.from_numpy(rt["r_v"].astype(np.float32)).to(dev)
+    tau_k, tau_v = float(np.float32(rt["tau_k"])), float(np.float32(rt["tau_v"]))
+    int2 = torch.zeros(inp.n_int2_pages * lib.int2_page_bytes(w.d, w.n_kv_heads), dtype=torch.uint8, device=dev)
+    bf16 = torch.zeros(inp.n_bf16_pages * lib.bf16_page_bytes(w.d, w.n_kv_heads) // 2, dtype=torch.int16, device=dev)
+    cache = lib.make_cache(w.d, w.n_kv_heads, w.n_sink, w.n_recent, int2, bf16)
+    bt_q, bt_h = i32(inp.bt_q), i32(inp.bt_h)
+    ms, mp, mr = synth.middle_rows(inp)
+    lib.quantize_append(cache, bf(inp.k_rows[mr]), bf(inp.v_rows[mr]), i32(ms), i32(mp), bt_q, r_k, r_v, tau_k, tau_v)
+    hs, hp, hr = synth.bf16_rows(inp)
+    lib.write_bf16(cache, bf(inp.k_rows[hr]), bf(inp.v_rows[hr]), i32(hs), i32(hp), bt_h)
+    torch.cuda.synchronize()
+    footprint = int2.numel() + bf16.numel() * 2
+    copies = max(1, int(np.ceil((1 << 30) / footprint)))
+    pools = [(int2, bf16)] + [(int2.clone(), bf16.clone()) for _ in range(copies - 1)]
+    caches = [lib.make_cache(w.d, w.n_kv_heads, w.n_sink, w.n_recent, a, b) for a, b in pools]
+    q, k_new, v_new = bf(qn), bf(kn), bf(vn)
+    cu_d, lens_d = i32(cu), i32(inp.seq_lens)
+    max_cache = int(inp.seq_lens.max())
+    wsb = lib.extend_workspace_bytes(B, w.n_kv_heads, w.n_q_heads, w.d, w.n_sink, w.n_recent, max_cache, n_new)
+    ws = torch.empty(max(1, (wsb + 3) // 4), dtype=torch.int32, device=dev)
+    out = torch.empty(B * n_new, w.n_q_heads, w.d, dtype=torch.bfloat16, device=dev)
+
+    def launch(i):
+        lib.paged_extend_attn(caches[i % copies], 2, q, k_new, v_new, cu_d, lens_d, max_cache, n_new, bt_q, bt_h,
+                              r_k, r_v, out, ws)
+
+    for i in range(max(2, args.warmup)):
+        launch(i)
+    torch.cuda.synchronize()
+    K = max(5, args.steps // 4)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(K):
+        launch(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_call = e0.elapsed_time(e1) / K
+    flops = extend_flops(inp.seq_lens, np.full(B, n_new), w.n_q_heads, w.d)
+    tflops = flops / (ms_call * 1e-3) / 1e12
+    rows = B * n_new
+    log(f"extend {ms_call * 1e3:.1f} us per call, {tflops:.1f} TFLOP/s, {rows / (ms_call * 1e-3):.3g} rows/s "
+        f"(workspace {wsb / 1e6:.1f} MB, {copies} cache copies)")
+    res = {
+        "metric": EXTEND_METRIC, "value": round(rows / (ms_call * 1e-3), 1), "unit": "new rows/s",
+        "ms_per_call": round(ms_call, 5), "dtype": "int2 codes -> f16 tiles, bf16 raw rows, f32 accumulate",
+        "config": {"workload": "qwen3-8b-b28-extend512", "batch": B, "cached_context": "U[4096, 32768], 1024 shared",
+                   "new_rows_per_sequence": n_new, "q_heads": w.n_q_heads, "kv_heads": w.n_kv_heads,
+                   "head_dim": w.d, "cache_copies": copies},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": None,
+                     "kernel": "attend_kernel<128,2,4,0>", "algorithmic_flops_per_launch": flops,
+                     "avg_launch_us": round(ms_call * 1e3, 2)},
+    }
+    if cpu:
+        from oracle import attention as oatt
+        from oracle import layout as olayout
+        lim, threads = blas_threads(len(os.sched_getaffinity(0)))
+        pool = olayout.Int2Pool(inp.n_int2_pages, w.n_kv_heads, w.d, int2.cpu().numpy())
+        bfp = olayout.Bf16Pool(inp.n_bf16_pages, w.n_kv_heads, w.d, bf16.cpu().numpy().view(np.uint16))
+        f = lambda x: synth.bf16_bits_to_f32(x).astype(np.float64)  # noqa: E731
+        n, dt = 4, 0.0
+        while dt < 8.0 and n <= n_new:  # rows 0 .. n-1 of sequence 0, growing until ~10 s
+            t0 = time.time()
+            oatt.extend_attention(f(qn[:n]), f(kn[:n]), f(vn[:n]), pool, bfp, [0, n], inp.seq_lens[:1], inp.bt_q[:1],
+                                  inp.bt_h[:1], rt["r_k"].astype(np.float32), rt["r_v"].astype(np.float32),
+                                  w.n_sink, w.n_recent)
+            dt = time.time() - t0
+            n *= 2
+        lim.restore_original_limits()
+        res["cpu_baseline"] = {"value": round((n // 2) / dt, 1), "unit": "new rows/s", "cores": threads, "kind": "oracle",
+                               "sample": f"oracle float64 extend of the first {n // 2} new rows of sequence 0 "
+                                         f"({int(inp.seq_lens[0])} cached tokens); BLAS threads {threads}"}
+    del pools, caches
+    torch.cuda.empty_cache()
+    return res
+
+
+INT4_METRIC = "INT4 paged decode-attn KV-tokens/s + achieved HBM GB/s (% of peak)"
+
+
+def int4_decode_line(args, log, w, cpu: bool) -> dict:
+    """The INT4-cache decode on the decode workload's shape: the middle history
+    quantized to 16 levels in INT4 pages, the same BF16 sink/recent pages.
+    Launches rotate over >= 1 GiB of cache copies; HIP events on the stream."""
+    import torch
+    from int2_rotated_kv_oscar_amd import lib, synth
+    dev = "cuda:0"
+    inp = synth.decode_inputs(w)
+    cal = synth.calibration_set(w, n_rows=1024)
+    rt = lib.build_rotation(cal.q, cal.k, cal.v, w.group_q)
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    def i32(a):
+        return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).to(dev)
+
+    r_k = torch.from_numpy(rt["r_k"].astype(np.float32)).to(dev)
+    r_v = torch.from_numpy(rt["r_v"].astype(np.float32)).to(dev)
+    tau_k, tau_v = float(np.float32(rt["tau_k"])), float(np.float32(rt["tau_v"]))
+    q4 = torch.zeros(inp.n_int2_pages * lib.int4_page_bytes(w.d, w.n_kv_heads), dtype=torch.uint8, device=dev)
+    bf16 = torch.zeros(inp.n_bf16_pages * lib.bf16_page_bytes(w.d, w.n_kv_heads) // 2, dtype=torch.int16, device=dev)
+    cache = lib.make_cache(w.d, w.n_kv_heads, w.n_sink, w.n_recent, q4, bf16, code_bits=4)
+    bt_q, bt_h = i32(inp.bt_q), i32(inp.bt_h)
+    ms, mp, mr = synth.middle_rows(inp)
+    lib.quantize_append_int4(cache, bf(inp.k_rows[mr]), bf(inp.v_rows[mr]), i32(ms), i32(mp), bt_q, r_k, r_v, tau_k,
+                             tau_v)
+    hs, hp, hr = synth.bf16_rows(inp)
+    lib.write_bf16(cache, bf(inp.k_rows[hr]), bf(inp.v_rows[hr]), i32(hs), i32(hp), bt_h)
+    torch.cuda.synchronize()
+    footprint = q4.numel() + bf16.numel() * 2 + r_k.numel() * 8
+    copies = max(1, int(np.ceil((1 << 30) / footprint)))
+    pools = [(q4, bf16, r_k, r_v)] + [(q4.clone(), bf16.clone(), r_k.clone(), r_v.clone()) for _ in range(copies - 1)]
+    caches = [lib.make_cache(w.d, w.n_kv_heads, w.n_sink, w.n_recent, a, b, code_bits=4) for a, b, _, _ in pools]
+    q = bf(inp.q)
+    B = len(inp.seq_lens)
+    seq_lens = i32(inp.seq_lens)
+    wsb = lib.decode_int4_workspace_bytes(B, w.n_kv_heads, w.n_q_heads, w.d, w.n_sink, w.n_recent, inp.max_seq_len)
+    ws = torch.empty(max(1, (wsb + 3) // 4), dtype=torch.int32, device=dev)
+    out = torch.empty(B, w.n_q_heads, w.d, dtype=torch.bfloat16, device=dev)
+
+    def launch(i):
+        _, _, rk, rv = pools[i % copies]
+        lib.paged_decode_attn_int4(caches[i % copies], q, seq_lens, inp.max_seq_len, bt_q, bt_h, rk, rv, out, ws)
+
+    for i in range(args.warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(K):
+        launch(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms_call = e0.elapsed_time(e1) / K
+    d, hkv = w.d, w.n_kv_heads
+    per_mid = 2 * (d // 2) + 2 * 2 * (d // 32) * 2  # INT4: 2 x d/2 B codes + 2 x 2 n_g x 2 B scale/zero
+    mid = raw = pages = 0
+    for b, L in enumerate(inp.seq_lens):
+        sink, m, rec = synth.regions(int(L), w.n_sink, w.n_recent)
+        lo = m[0] if (b == 0 or not w.shared_prefix) else max(m[0], w.shared_prefix)
+        mid += max(0, m[1] - lo)
+        raw += (sink[1] - sink[0]) + (rec[1] - rec[0]) if (b == 0 or not w.shared_prefix) else (rec[1] - rec[0])
+        pages += (int(L) + 15) // 16
+    nbytes = (mid * per_mid * hkv + raw * 4 * d * hkv + 2 * d * d * 4 * hkv + 2 * B * w.n_q_heads * d * 2 + pages * 4)
+    gbs = nbytes / (ms_call * 1e-3) / 1e9
+    tokens = int(inp.seq_lens.sum())
+    log(f"int4 decode {ms_call * 1e3:.1f} us per call, {gbs:.0f} GB/s algorithmic")
+    res = {
+        "metric": INT4_METRIC, "value": round(tokens / (ms_call * 1e-3), 1), "unit": "KV-tokens/s",
+        "ms_per_call": round(ms_call, 5), "dtype": "int4 codes -> f16 tiles, f32 accumulate",
+        "config": {"workload": w.name + "-int4", "batch": B, "context": inp.max_seq_len, "q_heads": w.n_q_heads,
+                   "kv_heads": hkv, "head_dim": d, "cache_copies": copies},
+        "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(gbs / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": f"attend_kernel<{d},4,1,1>", "algorithmic_bytes_per_launch": nbytes,
+                     "avg_launch_us": round(ms_call * 1e3, 2)},
+    }
+    if cpu:
+        from oracle import attention as oatt
+        from oracle import layout as olayout
+        lim, threads = blas_threads(len(os.sched_getaffinity(0)))
+        pool = olayout.Int4Pool(inp.n_int2_pages, hkv, d, q4.cpu().numpy())
+        bfp = olayout.Bf16Pool(inp.n_bf16_pages, hkv, d, bf16.cpu().numpy().view(np.uint16))
+        t0 = time.time()
+        oatt.decode_attention(synth.bf16_bits_to_f32(inp.q).astype(np.float64), pool, bfp, inp.seq_lens, inp.bt_q,
+                              inp.bt_h, rt["r_k"].astype(np.float32), rt["r_v"].astype(np.float32), w.n_sink,
+                              w.n_recent)
+        dt = time.time() - t0
+        lim.restore_original_limits()
+        res["cpu_baseline"] = {"value": round(tokens / dt, 1), "unit": "KV-tokens/s", "cores": threads, "kind": "oracle",
+                               "sample": f"oracle float64 decode of the whole INT4 cache ({tokens} tokens); "
+                                         f"BLAS threads {threads}"}
+    del pools, caches
+    torch.cuda.empty_cache()
+    return res
 
 
 GRAM_METRIC = "calibration Gram pooled rows/s + achieved HBM GB/s (% of peak), Qwen3-8B calibration"

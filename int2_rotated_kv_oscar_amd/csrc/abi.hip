@@ -376,8 +376,9 @@ namespace {
 // head) and one chunk of `spc` steps of 32 tokens (BF16 page pairs,
 // quantized page pairs, tiles of new rows); with more than one chunk per
 // tile, records of 2 + 2d floats per column and chunk go to the workspace
-// and a second launch merges them.  Automatic: about 2 (extend) or 6 (decode,
-// one-wave workgroups) workgroups per compute unit, at least 8 steps a chunk.
+// and a second launch merges them.  Automatic: about 2 (extend) or 3 (decode,
+// one-wave workgroups) workgroups per compute unit, at least 8 (16) steps a
+// chunk, which amortizes a chunk's query rotation and record.
 struct AttendPlan {
   int n_ct, n_chunks, spc;
   size_t bytes;
@@ -402,10 +403,10 @@ oscar_status plan_attend(bool extend, int32_t batch, int32_t n_kv, int32_t n_q, 
   if (units * plan->n_ct > (1LL << 30)) return fail(OSCAR_ERR_UNSUPPORTED, "grid too large; split the batch");
   long long spc = split_steps;
   if (!spc) {
-    const long long target = (extend ? 2LL : 6LL) * device_cu_count();
+    const long long target = (extend ? 2LL : 3LL) * device_cu_count();
     const long long base = std::max(1LL, units * plan->n_ct);
     const long long chunks = std::max(1LL, (target + base - 1) / base);
-    spc = std::max(8LL, (steps + chunks - 1) / chunks);
+    spc = std::max(extend ? 8LL : 16LL, (steps + chunks - 1) / chunks);
   }
   const long long n_chunks = std::max(1LL, (steps + spc - 1) / spc);
   if (units * plan->n_ct * n_chunks > (1LL << 31) - 1) return fail(OSCAR_ERR_UNSUPPORTED, "grid too large; use a larger split_steps");

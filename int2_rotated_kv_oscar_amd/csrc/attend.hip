@@ -104,22 +104,19 @@ __device__ __forceinline__ Regions make_regions(int P, int S, int W) {
 }
 
 // ---- step fill: one 32-token step into the LDS tile ----
-// Each thread loads its share of the step's bytes into registers (issued a
-// step ahead, so the loads overlap the previous step's products) and then
-// decodes them into the tile.  Shares: raw steps (BF16 page pair, 32 new
-// rows) 4D key chunks and 4D value chunks of 16 B; INT2 page pairs 2D items
-// (a key code word, a value code word, their scales and zeros); INT4 page
-// pairs 4D items (a key and a value code word of 8 nibbles, their scales and
-// zeros).  One-wave workgroups (decode) load their few raw steps when storing
-// them, which keeps their registers for the quantized items.
+// Each thread loads its share of a quantized step's bytes into registers
+// (issued one or two steps ahead, unconditionally, so that the loads overlap
+// the products of the steps before) and then decodes them into the tile.
+// Shares: INT2 page pairs 2D items (a key code word, a value code word, their
+// scales and zeros), INT4 page pairs 4D items (a key and a value code word of
+// 8 nibbles, their scales and zeros).  Raw steps (BF16 page pairs: 4D key and
+// 4D value chunks of 16 B; tiles of 32 new rows likewise) are few per unit
+// and are loaded when stored.
 template <int D, int BITS, int NTH>
 struct Stage {
   static constexpr int NR = (4 * D + NTH - 1) / NTH;       // raw chunks per tensor per thread
-  static constexpr bool RAW_AHEAD = NTH >= 256;
-  static constexpr int NRS = RAW_AHEAD ? NR : 1;
   static constexpr int NQ = BITS == 2 ? (2 * D + NTH - 1) / NTH : (4 * D + NTH - 1) / NTH;  // quantized items
   static constexpr int QW = BITS == 2 ? 12 : 6;            // registers per item
-  u32x4 kr[NRS], vr[NRS];
   uint32_t qw[NQ][QW];
 };
 
@@ -172,11 +169,7 @@ __device__ __forceinline__ void step_load(const AttParams& p, const Regions& rg,
   using SG = Stage<D, BITS, NTH>;
   constexpr int NG = D / 32;
   if (si.kind != 1) {
-    if constexpr (SG::RAW_AHEAD) {
-#pragma unroll
-      for (int it = 0; it < SG::NRS; ++it)
-        raw_chunk_load<D>(p, rg, bth, h, row0, n_rows, si, t + it * NTH, st.kr[it], st.vr[it]);
-    }
+    return;  // raw steps are loaded when stored
   } else if constexpr (BITS == 2) {
     using QG = QGeo<D, 2>;
     constexpr int NW = D / 64;
@@ -235,12 +228,7 @@ __device__ __forceinline__ void step_store(const AttParams& p, const Regions& rg
       const int e = t + it * NTH;
       if (e >= 4 * D) break;
       u32x4 kv, vv;
-      if constexpr (SG::RAW_AHEAD) {
-        kv = st.kr[it];
-        vv = st.vr[it];
-      } else {
-        raw_chunk_load<D>(p, rg, bth, h, row0, n_rows, si, e, kv, vv);
-      }
+      raw_chunk_load<D>(p, rg, bth, h, row0, n_rows, si, e, kv, vv);
       uint32_t vw[4] = {vv[0], vv[1], vv[2], vv[3]};
       if (si.kind == 0) {
         const int j = e / (16 * KCH), tok = (e / KCH) % 16, ch = e % KCH;
@@ -451,49 +439,85 @@ __global__ __launch_bounds__(64 * NWV) void attend_kernel(AttParams p) {
   const int n_nt = MODE == 0 ? (last_row + 1 + 31) / 32 : 0;
   const int total = n_rp + n_qp + n_nt;
   const int s_begin = chunk * p.spc, s_end = min(total, s_begin + p.spc);
-  auto info = [&](int s) {
+  // the chunk's quantized steps [qa, qb) (global step numbers)
+  const int qa = max(s_begin, n_rp), qb = min(s_end, n_rp + n_qp);
+  constexpr int DEPTH = NWV > 1 ? 2 : 1;  // quantized steps whose loads are in flight
+  Stage<D, BITS, NTH> stq[DEPTH];
+  auto qinfo = [&](int s) {  // steps past the chunk load a valid pair of it, never used
     StepInfo si;
-    if (s < n_rp) { si.kind = 0; si.i0 = 2 * s; }
-    else if (s < n_rp + n_qp) { si.kind = 1; si.i0 = 2 * (s - n_rp); }
-    else { si.kind = 2; si.i0 = 32 * (s - n_rp - n_qp); }
+    si.kind = 1;
+    si.i0 = 2 * (min(s, max(qb - 1, n_rp)) - n_rp);
     return si;
   };
-  Stage<D, BITS, NTH> st;
-  if (s_begin < s_end) step_load<D, BITS, NTH>(p, rg, btq, bth, h, row0, n_rows, info(s_begin), st, tid);
+#pragma unroll
+  for (int k = 0; k < DEPTH; ++k)
+    if (qa < qb) step_load<D, BITS, NTH>(p, rg, btq, bth, h, row0, n_rows, qinfo(qa + k), stq[k], tid);
 
-  // ---- query operands: raw q (bf16) and q~ = q R_K (f16, pre-scaled by qscale) ----
+  // ---- query operands: raw q (bf16) of this wave's columns, and q~ = q R_K
+  // (f16, pre-scaled by qscale) for all the tile's columns: R_K staged in
+  // LDS 32 rows at a time, wave w computing channel blocks w, w + NWV, ... of
+  // every column block; q~ goes through LDS to the waves that own the columns ----
   u32x4 bq_raw[NKB], bq_rot[NKB];
 #pragma unroll
   for (int kb = 0; kb < NKB; ++kb) bq_raw[kb] = *reinterpret_cast<const u32x4*>(qrow + 32 * kb + 8 * quad);
   {
-    // q~^T[c][n] = sum_k R_K[k][c] q[n][k]: A = R_K^T rows c = 16 cb + l16 (bf16 hi/lo), B = q
-    float* qst = fbuf + wave * 16 * D;  // q~ [16 columns][D]
+    constexpr int CPW = NCB / NWV;  // channel blocks per wave
+    const uint16_t* qcols[NWV];  // the q rows of the tile's column blocks (lane l16's column)
+#pragma unroll
+    for (int cbk = 0; cbk < NWV; ++cbk) {
+      const int c = col0 + 16 * cbk + l16;
+      const int rr = c < n_cols ? c / G : 0, hh = c < n_cols ? c % G : 0;
+      qcols[cbk] = p.q + (size_t(row0 + rr) * p.Hq + h * G + hh) * D;
+    }
+    f32x4 qacc[CPW][NWV];
+#pragma unroll
+    for (int j = 0; j < CPW; ++j)
+#pragma unroll
+      for (int cbk = 0; cbk < NWV; ++cbk) qacc[j][cbk] = f32x4{0.f, 0.f, 0.f, 0.f};
+    float* rs = reinterpret_cast<float*>(tiles);  // [32][D] rows of R_K
     const float* rk = p.r_k + size_t(h) * D * D;
 #pragma unroll 1
-    for (int cb = 0; cb < NCB; ++cb) {
-      f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+    for (int kb = 0; kb < NKB; ++kb) {
+      u32x4 qk[NWV];  // B operands: the q slice kb of every column block
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
+      for (int cbk = 0; cbk < NWV; ++cbk) qk[cbk] = *reinterpret_cast<const u32x4*>(qcols[cbk] + 32 * kb + 8 * quad);
+      for (int e = tid; e < 32 * D / 4; e += NTH)
+        *reinterpret_cast<f32x4*>(rs + 4 * e) = *reinterpret_cast<const f32x4*>(rk + size_t(32 * kb) * D + 4 * e);
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < CPW; ++j) {
+        const int cb = wave + NWV * j;
         float rv[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) rv[i] = rk[size_t(32 * kb + 8 * quad + i) * D + 16 * cb + l16];
+        for (int i = 0; i < 8; ++i) rv[i] = rs[(8 * quad + i) * D + 16 * cb + l16];
         uint32_t ph[4], pl[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           ph[i] = pack2(bf16_rne(rv[2 * i]), bf16_rne(rv[2 * i + 1]));
           pl[i] = pack2(bf16_rne(rv[2 * i] - bf16_to_f32(ph[i] & 0xFFFFu)), bf16_rne(rv[2 * i + 1] - bf16_to_f32(ph[i] >> 16)));
         }
-        a4 = mfma_bf16(u32x4{pl[0], pl[1], pl[2], pl[3]}, bq_raw[kb], a4);
-        a4 = mfma_bf16(u32x4{ph[0], ph[1], ph[2], ph[3]}, bq_raw[kb], a4);
+        const u32x4 AH{ph[0], ph[1], ph[2], ph[3]}, AL{pl[0], pl[1], pl[2], pl[3]};
+#pragma unroll
+        for (int cbk = 0; cbk < NWV; ++cbk) {
+          qacc[j][cbk] = mfma_bf16(AL, qk[cbk], qacc[j][cbk]);
+          qacc[j][cbk] = mfma_bf16(AH, qk[cbk], qacc[j][cbk]);
+        }
       }
-      // a4[r] = q~[n = l16][c = 16 cb + 4 quad + r]
-      *reinterpret_cast<f32x4*>(qst + l16 * D + 16 * cb + 4 * quad) = a4 * qscale;
+      lds_barrier();
     }
+    // qacc[j][cbk][r] = q~[column 16 cbk + l16][channel 16 (wave + NWV j) + 4 quad + r]
+#pragma unroll
+    for (int j = 0; j < CPW; ++j)
+#pragma unroll
+      for (int cbk = 0; cbk < NWV; ++cbk)
+        *reinterpret_cast<f32x4*>(fbuf + (16 * cbk + l16) * D + 16 * (wave + NWV * j) + 4 * quad) = qacc[j][cbk] * qscale;
+    lds_barrier();
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
-      const float* src = qst + l16 * D + 32 * kb + 8 * quad;
+      const float* src = fbuf + (16 * wave + l16) * D + 32 * kb + 8 * quad;
       bq_rot[kb] = u32x4{f16pair(src[0], src[1]), f16pair(src[2], src[3]), f16pair(src[4], src[5]), f16pair(src[6], src[7])};
     }
+    lds_barrier();  // fbuf is reused at the end
   }
 
   float m_run = kNegInfA, l_part = 0.f;
@@ -504,13 +528,8 @@ __global__ __launch_bounds__(64 * NWV) void attend_kernel(AttParams p) {
     acc_raw[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 
-#pragma unroll 1
-  for (int s = s_begin; s < s_end; ++s) {
-    uint16_t* tile = tiles + (NBUF == 2 ? (s & 1) : 0) * T::ELEMS;
-    const StepInfo si = info(s);
-    step_store<D, BITS, NTH>(p, rg, bth, h, row0, n_rows, si, st, tile, tid);
-    if (s + 1 < s_end) step_load<D, BITS, NTH>(p, rg, btq, bth, h, row0, n_rows, info(s + 1), st, tid);
-    lds_barrier();  // the tile is complete; the next step's loads stay in flight
+  // products and online softmax of one step over the tile
+  auto compute = [&](const uint16_t* tile, const StepInfo& si) __attribute__((always_inline)) {
     const bool quantized = si.kind == 1;
     f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -592,14 +611,55 @@ __global__ __launch_bounds__(64 * NWV) void attend_kernel(AttParams p) {
         acc_raw[cb] = mfma_bf16(a, bph, acc_raw[cb]);
       }
     }
-    if (NBUF == 1) lds_barrier();  // one buffer: the next step rewrites it
+  };
+  auto tile_of = [&](int s) { return tiles + (NBUF == 2 ? (s & 1) : 0) * T::ELEMS; };
+  // raw steps (BF16 pages, new rows): few per unit, loaded when stored
+  auto raw_step = [&](int s, const StepInfo& si) {
+    uint16_t* tile = tile_of(s);
+    step_store<D, BITS, NTH>(p, rg, bth, h, row0, n_rows, si, stq[0], tile, tid);
+    lds_barrier();
+    compute(tile, si);
+    if (NBUF == 1) lds_barrier();
+  };
+#pragma unroll 1
+  for (int s = s_begin; s < min(s_end, n_rp); ++s) {
+    StepInfo si;
+    si.kind = 0;
+    si.i0 = 2 * s;
+    raw_step(s, si);
+  }
+  // quantized steps: the loads of the next DEPTH steps stay in flight (every
+  // step reloads its stage right after decoding it)
+#pragma unroll 1
+  for (int s = qa; s < qb; s += DEPTH) {
+#pragma unroll
+    for (int k = 0; k < DEPTH; ++k) {
+      if (s + k < qb) {
+        const StepInfo si = qinfo(s + k);
+        uint16_t* tile = tile_of(s + k);
+        step_store<D, BITS, NTH>(p, rg, bth, h, row0, n_rows, si, stq[k], tile, tid);
+        step_load<D, BITS, NTH>(p, rg, btq, bth, h, row0, n_rows, qinfo(s + k + DEPTH), stq[k], tid);
+        lds_barrier();  // the tile is complete; the loads just issued stay in flight
+        compute(tile, si);
+        if (NBUF == 1) lds_barrier();
+      }
+    }
+  }
+#pragma unroll 1
+  for (int s = max(s_begin, n_rp + n_qp); s < s_end; ++s) {
+    StepInfo si;
+    si.kind = 2;
+    si.i0 = 32 * (s - n_rp - n_qp);
+    raw_step(s, si);
   }
 
   const float l_tot = wave_sum16(l_part);
   constexpr int RF = 2 + 2 * D;
   if (p.n_chunks > 1) {
     // record of this chunk: [m][l][raw D][rot D] per column
+    // (columns past the unit's last are never merged: no record)
     float* rec = p.rec + (((size_t(unit) * p.n_ct + ct) * p.n_chunks + chunk) * size_t(16 * NWV) + 16 * wave + l16) * RF;
+    if (!col_ok) return;
     if (quad == 0) {
       rec[0] = m_run;
       rec[1] = l_tot;
@@ -620,48 +680,82 @@ __global__ __launch_bounds__(64 * NWV) void attend_kernel(AttParams p) {
 }
 
 // Log-sum-exp merge of the chunk records of one (unit, column tile), then
-// the output rotation: out = (sum_k w_k raw_k + (sum_k w_k rot_k) R_V^T) /
-// sum_k w_k l_k with w_k = 2^(m_k - M).
+// the output rotation, column by column: M = max_k m_k, w_k = 2^(m_k - M),
+// out = (sum_k w_k raw_k + (sum_k w_k rot_k) R_V^T) / sum_k w_k l_k.  All
+// 256 threads share a column: the chunks' maxima and weights, then one of
+// the 2d value sums each (eight chunks' loads in flight), then one output
+// channel each (float32 products with R_V's row).
 template <int D, int NWV, int MODE>
-__global__ __launch_bounds__(64 * NWV) void attend_merge_kernel(AttParams p) {
-  constexpr int NCB = D / 16, RF = 2 + 2 * D;
+__global__ __launch_bounds__(256) void attend_merge_kernel(AttParams p) {
+  constexpr int RF = 2 + 2 * D, NC = 16 * NWV, MT = 256;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  float* fbuf = reinterpret_cast<float*>(lds);
-  const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, quad = lane >> 4;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  float* s_w = reinterpret_cast<float*>(lds);   // [n_chunks] weights of the current column
+  float* s_v = s_w + p.n_chunks;                // [2 D] merged raw, rot
+  float* s_red = s_v + 2 * D;                   // [8] partial reductions
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = p.G;
   const int ct = blockIdx.x % p.n_ct, unit = blockIdx.x / p.n_ct;
   const UnitRows u = unit_rows<MODE>(p, unit);
   if (MODE == 1 && u.P <= 0) return;
-  const int col0 = ct * 16 * NWV, n_cols = u.n_rows * G;
+  const int col0 = ct * NC, n_cols = u.n_rows * G;
   if (col0 >= n_cols) return;
-  const int col = col0 + 16 * wave + l16;
-  const bool col_ok = col < n_cols;
-  const int ri = col_ok ? col / G : 0, hi = col_ok ? col % G : 0;
-  const float* rec0 = p.rec + ((size_t(unit) * p.n_ct + ct) * p.n_chunks * size_t(16 * NWV) + 16 * wave + l16) * RF;
-  const size_t cstride = size_t(16 * NWV) * RF;
-  float M = kNegInfA;
-  for (int k = 0; k < p.n_chunks; ++k) M = fmaxf(M, rec0[k * cstride]);
-  float l = 0.f;
-  f32x4 raw[NCB], rotv[NCB];
+  const size_t cstride = size_t(NC) * RF;
+  const float* rv = p.r_v + size_t(u.h) * D * D;
+  for (int cl = 0; cl < NC && col0 + cl < n_cols; ++cl) {
+    const int col = col0 + cl, ri = col / G, hi = col % G;
+    const float* rec0 = p.rec + ((size_t(unit) * p.n_ct + ct) * p.n_chunks * NC + cl) * RF;
+    // maximum over the chunks
+    float mx = kNegInfA;
+    for (int k = tid; k < p.n_chunks; k += MT) mx = fmaxf(mx, rec0[k * cstride]);
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) raw[cb] = rotv[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k = 0; k < p.n_chunks; ++k) {
-    const float* r = rec0 + k * cstride;
-    const float mk = r[0];
-    const float w = mk == kNegInfA ? 0.f : exp2f(mk - M);
-    l = __builtin_fmaf(w, r[1], l);
-#pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      raw[cb] += w * *reinterpret_cast<const f32x4*>(r + 2 + 16 * cb + 4 * quad);
-      rotv[cb] += w * *reinterpret_cast<const f32x4*>(r + 2 + D + 16 * cb + 4 * quad);
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    if (lane == 0) s_red[wave] = mx;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+    __syncthreads();
+    float l = 0.f;
+    for (int k = tid; k < p.n_chunks; k += MT) {
+      const float mk = rec0[k * cstride];
+      const float w = mk == kNegInfA ? 0.f : exp2f(mk - M);
+      s_w[k] = w;
+      l = __builtin_fmaf(w, rec0[k * cstride + 1], l);
     }
-  }
-  float* rot = fbuf + wave * 16 * D;
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) *reinterpret_cast<f32x4*>(rot + l16 * D + 16 * cb + 4 * quad) = rotv[cb];
-  finish_columns<D>(p.r_v + size_t(u.h) * D * D, rot, raw, l, col_ok,
-                    p.out + (size_t(u.row0 + ri) * p.Hq + u.h * G + hi) * D, l16, quad);
+    for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
+    if (lane == 0) s_red[4 + wave] = l;
+    __syncthreads();
+    const float L = (s_red[4] + s_red[5]) + (s_red[6] + s_red[7]);
+    // value sums: thread f < 2D sums float f over the chunks
+    for (int f = tid; f < 2 * D; f += MT) {
+      float a = 0.f;
+      int k = 0;
+      for (; k + 8 <= p.n_chunks; k += 8) {
+        float v[8];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) v[t] = rec0[(k + t) * cstride + 2 + f];
+#pragma unroll
+        for (int t = 0; t < 8; ++t) a = __builtin_fmaf(s_w[k + t], v[t], a);
+      }
+      for (; k < p.n_chunks; ++k) a = __builtin_fmaf(s_w[k], rec0[k * cstride + 2 + f], a);
+      s_v[f] = a;
+    }
+    __syncthreads();
+    // out[c] = (raw[c] + sum_k rot[k] R_V[c][k]) / L
+    if (tid < D) {
+      const float* rrow = rv + size_t(tid) * D;
+      float a = s_v[tid];
+#pragma unroll 4
+      for (int k = 0; k < D; k += 4) {
+        const f32x4 r4 = *reinterpret_cast<const f32x4*>(rrow + k);
+        a = __builtin_fmaf(s_v[D + k], r4[0], a);
+        a = __builtin_fmaf(s_v[D + k + 1], r4[1], a);
+        a = __builtin_fmaf(s_v[D + k + 2], r4[2], a);
+        a = __builtin_fmaf(s_v[D + k + 3], r4[3], a);
+      }
+      p.out[(size_t(u.row0 + ri) * p.Hq + u.h * G + hi) * D + tid] = uint16_t(bf16_rne(L > 0.f ? a / L : 0.f));
+    }
+    __syncthreads();
+  }
 }
 
 }  // namespace
@@ -689,11 +783,11 @@ hipError_t paged_attend(int d, int bits, bool extend, const void* qpool, int n_q
   const dim3 grid(units * unsigned(n_ct) * unsigned(n_chunks));
   const dim3 mgrid(units * unsigned(n_ct));
   const size_t lds = attend_lds_bytes(d, extend);
-  const size_t mlds = size_t(attend_waves(extend)) * 16 * d * 4;
+  const size_t mlds = (size_t(n_chunks) + 2 * d + 8) * 4;
 #define OSCAR_ATTEND(DD, BB, NW, MM)                                                                        \
   do {                                                                                                      \
     hipLaunchKernelGGL((attend_kernel<DD, BB, NW, MM>), grid, dim3(64 * NW), lds, stream, p);               \
-    if (n_chunks > 1) hipLaunchKernelGGL((attend_merge_kernel<DD, NW, MM>), mgrid, dim3(64 * NW), mlds, stream, p); \
+    if (n_chunks > 1) hipLaunchKernelGGL((attend_merge_kernel<DD, NW, MM>), mgrid, dim3(256), mlds, stream, p); \
   } while (0)
   if (d == 128) {
     if (extend) { if (bits == 2) OSCAR_ATTEND(128, 2, 4, 0); else OSCAR_ATTEND(128, 4, 4, 0); }

@@ -65,7 +65,7 @@ def sequence_kv(int2: Int2Pool, bf16: Bf16Pool, bt_q_row, bt_h_row, L: int, S: i
 
 def extend_attention(q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, pool, bf16: Bf16Pool, cu, cache_lens,
                      bt_q, bt_h, r_k: np.ndarray, r_v: np.ndarray, S: int, W: int,
-                     scale: float | None = None) -> np.ndarray:
+                     scale: float | None = None, rows=None) -> np.ndarray:
     """Chunked-prefill ("extend") attention over the mixed paged cache, fp64.
 
     [TS] 2.2.B "Kernel Integration" (paged attention with prefix caching) and
@@ -77,7 +77,8 @@ def extend_attention(q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, pool, 
     from BF16 pages, the middle decoded from the quantized pages and rotated
     back), and the new rows 0..i (causal), raw.  ``pool`` is an Int2Pool or an
     Int4Pool.  q float64 [T, H_q, d]; k_new, v_new float64 [T, H_kv, d];
-    returns float64 [T, H_q, d].
+    returns float64 [T, H_q, d].  ``rows``: if given, only these global rows
+    are computed (the others stay zero).
     """
     T, hq, d = q.shape
     hkv = k_new.shape[1]
@@ -96,6 +97,8 @@ def extend_attention(q: np.ndarray, k_new: np.ndarray, v_new: np.ndarray, pool, 
             else:
                 kc = vc = np.zeros((0, d))
             for i in range(r1 - r0):
+                if rows is not None and r0 + i not in rows:
+                    continue
                 k = np.concatenate([kc, np.asarray(k_new[r0:r0 + i + 1, h], np.float64)])
                 v = np.concatenate([vc, np.asarray(v_new[r0:r0 + i + 1, h], np.float64)])
                 out[r0 + i, h * G:(h + 1) * G] = softmax_attention(np.asarray(q[r0 + i, h * G:(h + 1) * G], np.float64),

@@ -325,9 +325,11 @@ def gpu_extend(ext: ExtendInputs, gc: GpuCache, bits: int = 2, split_steps: int 
     return dev_bf16_to_f64(out)
 
 
-def oracle_extend_gpu_pages(ext: ExtendInputs, rot: Rotation, gc: GpuCache, bits: int = 2, seqs=None) -> np.ndarray:
+def oracle_extend_gpu_pages(ext: ExtendInputs, rot: Rotation, gc: GpuCache, bits: int = 2, seqs=None,
+                            rows=None) -> np.ndarray:
     """The oracle's extend attention over the pages the GPU wrote, for the
-    sequences ``seqs`` (all by default); rows of other sequences stay zero."""
+    sequences ``seqs`` (all by default) and, if given, only the global rows
+    ``rows``; other rows stay zero."""
     from oracle import attention as oatt
     w = ext.cache.w
     pool, bf = gpu_pages(ext.cache, gc, bits)
@@ -337,7 +339,8 @@ def oracle_extend_gpu_pages(ext: ExtendInputs, rot: Rotation, gc: GpuCache, bits
         r0, r1 = int(ext.cu[b]), int(ext.cu[b + 1])
         out[r0:r1] = oatt.extend_attention(f(ext.q[r0:r1]), f(ext.k_new[r0:r1]), f(ext.v_new[r0:r1]), pool, bf,
                                            [0, r1 - r0], ext.cache.seq_lens[b:b + 1], ext.cache.bt_q[b:b + 1],
-                                           ext.cache.bt_h[b:b + 1], rot.r_k, rot.r_v, w.n_sink, w.n_recent)
+                                           ext.cache.bt_h[b:b + 1], rot.r_k, rot.r_v, w.n_sink, w.n_recent,
+                                           rows=None if rows is None else {r - r0 for r in rows if r0 <= r < r1})
     return out
 
 

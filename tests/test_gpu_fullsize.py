@@ -147,3 +147,43 @@ def test_prefill_8x8192_rows_per_sequence():
     rep = gh.compare_appended(int2.cpu().numpy(), w, n_seq * pages_per, res, page, (row_pos[sel] % 16).astype(np.int64))
     print(rep, flush=True)
     gh.assert_codes_ok(rep, "prefill 8x8192")
+
+
+def test_extend_prefix_hit_qwen3_8b_b28_ragged():
+    # the bench's chunked-prefill launch: the 28-sequence Qwen3-8B cache
+    # (ragged contexts, a 1024-token prefix aliased by every table) extended by
+    # 512 new rows per sequence, written by the library's kernels on recycled
+    # pools; the oracle checks sampled rows of two sequences over those pages
+    w = synth.WORKLOADS["qwen3-8b-b28-ragged"]
+    lens = synth.context_lengths(w)
+    print(f"[fullsize extend] B={len(lens)} max cached={int(lens.max())} new=512", flush=True)
+    ext = gh.extend_inputs(w, lens, [512] * len(lens), seed=0, draw_seqs=[0, 27])
+    rot = gh.oracle_rotation(w, n_rows=CALIB_ROWS)
+    gc = gh.alloc_cache(ext.cache, rot)
+    gh.fill_stale(gc, seed=3)
+    gh.gpu_fill(ext.cache, rot, gc)
+    got = gh.gpu_extend(ext, gc, 2)
+    assert np.isfinite(got).all()
+    rng = np.random.default_rng(7)
+    rows = sorted(set(rng.choice(512, size=24, replace=False).tolist()) | {0, 511})
+    sel = [r for r in rows] + [ext.cu[27] + r for r in rows]
+    ref = gh.oracle_extend_gpu_pages(ext, rot, gc, 2, seqs=[0, 27], rows=set(sel))
+    err = gh.attention_errors(got[sel], ref[sel])
+    print(f"[fullsize extend] errors {err}", flush=True)
+    gh.assert_attention_close(got[sel], ref[sel], "extend b28")
+
+
+def test_int4_decode_qwen3_8b_b1_32k():
+    # the INT4 variant of the bench's decode workload at full size
+    w = synth.WORKLOADS["qwen3-8b-b1-32k"]
+    inp = synth.decode_inputs(w)
+    rot = gh.oracle_rotation(w, n_rows=CALIB_ROWS)
+    gc = gh.alloc_cache(inp, rot, bits=4)
+    print("[fullsize int4 decode] fill", flush=True)
+    gh.gpu_fill(inp, rot, gc, bits=4)
+    torch.cuda.synchronize()
+    got = gh.gpu_decode_int4(inp, gc)
+    ref = gh.oracle_decode_gpu_pages(inp, rot, gc, bits=4)
+    err = gh.attention_errors(got, ref)
+    print(f"[fullsize int4 decode] errors {err}", flush=True)
+    gh.assert_attention_close(got, ref, "int4 decode 32k")

@@ -197,3 +197,14 @@ def test_extend_brute_force_small():
             e = [np.exp(x - mx) for x in lg]
             o = sum(ei * vv for ei, vv in zip(e, vs_)) / sum(e)
             np.testing.assert_allclose(got[i, g], o, rtol=1e-11, atol=1e-12)
+
+
+def test_extend_row_subset_equals_full_rows():
+    rng = np.random.default_rng(21)
+    d, hkv, G, n, P = 64, 1, 2, 12, 90
+    pool, bf, bt, rk, rv = _cache(rng, d, hkv, P, 4, 32, 2)
+    q = rng.standard_normal((n, G, d)); kn = rng.standard_normal((n, 1, d)); vn = rng.standard_normal((n, 1, d))
+    full = att.extend_attention(q, kn, vn, pool, bf, [0, n], [P], bt, bt, rk, rv, 4, 32)
+    sub = att.extend_attention(q, kn, vn, pool, bf, [0, n], [P], bt, bt, rk, rv, 4, 32, rows={3, 11})
+    np.testing.assert_array_equal(sub[[3, 11]], full[[3, 11]])
+    assert not sub[[0, 1, 2, 4, 10]].any()
