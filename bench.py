@@ -1,18 +1,22 @@
 """Benchmark of the OSCAR INT2 decode hot path on one MI355X.
 
-One step = quantize-append of the token leaving each sequence's BF16 recent
-window (its INT2 slot re-written) + fused paged INT2 decode attention of one
-query per sequence, over a cache filled once by the same kernels.  The timed
-steps rotate over enough copies of the cache (pools, tables, rotations,
-queries) that the 256 MB Infinity Cache cannot serve them, as consecutive
-layers of a model would.
+One step = one launch of the fused decode step (oscar_decode_step): each
+sequence's new token written to its BF16 slot, the token leaving the recent
+window quantized into its INT2 slot, and the paged INT2 decode attention of
+one query per sequence, over a cache filled once by the library's kernels.
+The timed steps rotate over enough copies of the cache (pools, tables,
+rotations, queries) that the 256 MB Infinity Cache cannot serve them, as
+consecutive layers of a model would.
 
 Prints ONE JSON line (rank 0):
   value        KV-tokens/s  (sum of context lengths / step time, all KV heads)
-  roofline     decode kernel: algorithmic bytes / its average launch time
-               (HIP events on the launch stream around K decode launches back
-               to back over the same cache copies, a second pass) vs 8 TB/s
+  roofline     the fused step kernel: algorithmic bytes (the decode's and the
+               update's) / its average launch time (HIP events on the launch
+               stream around the K timed launches) vs 8 TB/s
   cpu_baseline the float64 NumPy oracle decoding the same cache on host cores
+Context beside it: the decode launch alone, the two-launch step (update, then
+decode), the all-BF16 decode, the quantize-append prefill (kernel A), the
+chunked-prefill attention and the INT4-cache decode, each timed the same way.
 
 --append-prefill measures quantize-append alone on the large-GQA layer's
 prefill (8 sequences x 8192 rows, 96 q / 8 KV heads, d = 128) and prints the
@@ -75,17 +79,40 @@ def algorithmic_bytes(inp, w) -> dict:
     return parts
 
 
-def decode_kernel_name(w, split_pages: int, all_raw: bool) -> str:
+def step_update_bytes(inp, w) -> int:
+    """Unique bytes of the step's cache update beside the decode's: per
+    sequence and KV head, the new K/V row read (4 d B) and, when it lands in a
+    BF16 region, written to its slot (4 d B); when a token enters the middle
+    history, its raw row read from its BF16 slot (4 d B, unless it is the new
+    token) and its INT2 slot written (96 B at d = 128)."""
+    d, hkv, S, W = w.d, w.n_kv_heads, w.n_sink, w.n_recent
+    per_mid = 2 * (d // 4) + 2 * 2 * (d // 32) * 2
+    total = 0
+    for L in inp.seq_lens:
+        L = int(L)
+        if L < 1:
+            continue
+        total += 4 * d
+        if W >= 1 or L - 1 < S:
+            total += 4 * d
+        t = L - 1 - W
+        if t >= S:
+            total += per_mid + (4 * d if W >= 1 else 0)
+    return total * hkv
+
+
+def decode_kernel_name(w, split_pages: int, all_raw: bool, fused: bool = False) -> str:
     """The decode kernel instance the library launches for this workload
     (template arguments: head dim, all-BF16 cache, balanced slices, grouped
-    columns), by the library's rule: per-unit items when split_pages is given
-    or the (sequence, KV head) units are at most a quarter of the CUs."""
+    columns, fused step update), by the library's rule: per-unit items when
+    split_pages is given or the (sequence, KV head) units are at most a
+    quarter of the CUs."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     slices = not (split_pages != 0 or 4 * w.batch * w.n_kv_heads <= cus)
     gc = (not all_raw) and w.n_q_heads // w.n_kv_heads <= 4
     b = lambda x: "true" if x else "false"  # noqa: E731
-    return f"decode_kernel<{w.d},{b(all_raw)},{b(slices)},{b(gc)}>"
+    return f"decode_kernel<{w.d},{b(all_raw)},{b(slices)},{b(gc)},{b(fused)}>"
 
 
 DECODE_SOURCES = ["decode.hip", "device_utils.h", "layout.h"]
@@ -119,7 +146,7 @@ def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=300)
     ap.add_argument("--workload", default="qwen3-8b-b1-32k")
     ap.add_argument("--context", type=int, default=0,
                     help="override the context length of a fixed-length workload (the workload is then named <name>-ctx<L>)")
@@ -235,15 +262,6 @@ def main() -> int:
     n_k, n_v = bf(inp.k_rows[new_rows]), bf(inp.v_rows[new_rows])
     torch.cuda.synchronize()
 
-    # per step: the row leaving the recent window of every sequence
-    ap_seq, ap_pos, ap_row = [], [], []
-    for b, L in enumerate(inp.seq_lens):
-        t = int(L) - w.n_recent - 1
-        if t >= w.n_sink:
-            ap_seq.append(b); ap_pos.append(t); ap_row.append(inp.row_of[b][t])
-    a_seq, a_pos = i32(ap_seq), i32(ap_pos)
-    a_k, a_v = bf(inp.k_rows[np.array(ap_row)]), bf(inp.v_rows[np.array(ap_row)])
-
     nbytes = algorithmic_bytes(inp, w)
     footprint = int2.numel() + bf16.numel() * 2 + r_k.numel() * 8
     copies = args.copies or max(1, int(np.ceil((1 << 30) / footprint)))
@@ -261,43 +279,68 @@ def main() -> int:
     out = torch.empty(B, w.n_q_heads, w.d, dtype=torch.bfloat16, device=dev)
     log(f"cache footprint {footprint / 1e6:.1f} MB x {copies} copies; workspace {ws_bytes / 1e6:.2f} MB")
 
+    upd_bytes = step_update_bytes(inp, w)
+
     def step(i):
         c = caches[i % copies]
-        pk, _, prk, prv = pools[i % copies]
-        lib.quantize_append(c, a_k, a_v, a_seq, a_pos, bt_q, prk, prv, tau_k, tau_v)
-        lib.paged_decode_attn(c, qs[i % copies], seq_lens, inp.max_seq_len, bt_q, bt_h, prk, prv, out, ws,
-                              split_pages=args.split_pages)
+        _, _, prk, prv = pools[i % copies]
+        lib.decode_step(c, n_k, n_v, qs[i % copies], seq_lens, inp.max_seq_len, bt_q, bt_h, prk, prv, tau_k, tau_v,
+                        out, ws, split_pages=args.split_pages)
+
+    def timed(fn, n):
+        """Average ms of n calls of fn back to back: HIP events on the
+        launch stream (torch's current stream, which the binding uses)."""
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(n):
+            fn(i)
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / n
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
     K = args.steps
-    # throughput: K steps back to back, nothing else on the stream
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record()
-    for i in range(K):
-        step(i)
-    t_end.record()
-    torch.cuda.synchronize()
-    ms_step = t_start.elapsed_time(t_end) / K
-    # decode launch duration: K decode launches back to back over the same
-    # rotating cache copies, HIP events on their stream around the block
-    # (torch's current stream, which the binding launches on)
-    d0 = torch.cuda.Event(enable_timing=True)
-    d1 = torch.cuda.Event(enable_timing=True)
-    d0.record()
-    for i in range(K):
-        lib.paged_decode_attn(caches[i % copies], qs[i % copies], seq_lens, inp.max_seq_len, bt_q, bt_h,
-                              pools[i % copies][2], pools[i % copies][3], out, ws, split_pages=args.split_pages)
-    d1.record()
-    torch.cuda.synchronize()
-    dec_avg = d0.elapsed_time(d1) / K
+    # throughput: K steps back to back, nothing else on the stream; a step is
+    # one launch, so this is also the fused kernel's average launch time
+    ms_step = timed(step, K)
     tokens = int(inp.seq_lens.sum())
     value = tokens / (ms_step * 1e-3)
-    achieved = nbytes["total"] / (dec_avg * 1e-3) / 1e9
-    log(f"step {ms_step * 1e3:.1f} us, decode kernel avg {dec_avg * 1e3:.1f} us, {achieved:.0f} GB/s, bytes {nbytes}")
+    step_bytes = nbytes["total"] + upd_bytes
+    # the library fuses the update into the decode launch under the per-unit
+    # plan (split_pages given, or units at most a quarter of the CUs); with
+    # more units the step is the update kernel, then the decode
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    fused = args.split_pages != 0 or 4 * B * w.n_kv_heads <= cus
+    log(f"step ({'one fused launch' if fused else 'update + decode launches'}) {ms_step * 1e3:.1f} us, "
+        f"{step_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s, bytes {nbytes} + update {upd_bytes}")
+
+    # context: the decode launch alone, and the two-launch step (the update
+    # kernel, then the decode)
+    def decode_only(i):
+        lib.paged_decode_attn(caches[i % copies], qs[i % copies], seq_lens, inp.max_seq_len, bt_q, bt_h,
+                              pools[i % copies][2], pools[i % copies][3], out, ws, split_pages=args.split_pages)
+
+    def update_only(i):
+        lib.decode_step_update(caches[i % copies], n_k, n_v, seq_lens, bt_q, bt_h, pools[i % copies][2],
+                               pools[i % copies][3], tau_k, tau_v)
+
+    def two_launch(i):
+        update_only(i)
+        decode_only(i)
+
+    for i in range(args.warmup):
+        two_launch(i)
+    dec_avg = timed(decode_only, K)
+    upd_ms = timed(update_only, K)
+    serve_ms = timed(two_launch, K)
+    dec_gbps = nbytes["total"] / (dec_avg * 1e-3) / 1e9
+    # the roofline's kernel: the fused launch (it is the step), else the decode
+    achieved = step_bytes / (ms_step * 1e-3) / 1e9 if fused else dec_gbps
+    log(f"decode launch alone {dec_avg * 1e3:.1f} us ({dec_gbps:.0f} GB/s); two-launch step {serve_ms * 1e3:.1f} us, "
+        f"update alone {upd_ms * 1e3:.1f} us")
 
     result = {
         "metric": METRIC, "value": round(value, 1), "unit": "KV-tokens/s", "n_gpus": 1, "steps": K,
@@ -307,43 +350,21 @@ def main() -> int:
                    "kv_heads": w.n_kv_heads, "head_dim": w.d, "page_tokens": 16, "sink": w.n_sink,
                    "recent": w.n_recent, "split_pages": args.split_pages or "auto", "cache_copies": copies},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(w.name),
-                     "kernel": decode_kernel_name(w, args.split_pages, False), "algorithmic_bytes_per_launch": nbytes["total"],
-                     "avg_launch_us": round(dec_avg * 1e3, 2)},
+                     "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": measured_traffic(w.name, "decode_step" if fused else "decode_kernel"),
+                     "kernel": decode_kernel_name(w, args.split_pages, False, fused=fused),
+                     "algorithmic_bytes_per_launch": step_bytes if fused else nbytes["total"],
+                     "avg_launch_us": round((ms_step if fused else dec_avg) * 1e3, 2),
+                     "step_launches": 1 if fused else 2},
+        "decode_only": {"kernel": decode_kernel_name(w, args.split_pages, False),
+                        "avg_launch_us": round(dec_avg * 1e3, 2), "algorithmic_bytes_per_launch": nbytes["total"],
+                        "achieved_GBps": round(dec_gbps, 1), "frac": round(dec_gbps / HBM_PEAK_GBPS, 4),
+                        "traffic": measured_traffic(w.name)},
+        "two_launch_step": {"kernels": [f"quantize_rows_kernel<{w.d},true,2>", decode_kernel_name(w, args.split_pages, False)],
+                            "us_per_step": round(serve_ms * 1e3, 2),
+                            "KV_tokens_per_s": round(tokens / (serve_ms * 1e-3), 1),
+                            "update_us_per_call": round(upd_ms * 1e3, 2)},
     }
-
-    # serving step: one launch of the decode-step cache update (the new token
-    # to its BF16 slot, the token leaving the recent window quantized into
-    # INT2 from its BF16 slot) + the decode
-    def serve(i):
-        c = caches[i % copies]
-        _, _, prk, prv = pools[i % copies]
-        lib.decode_step_update(c, n_k, n_v, seq_lens, bt_q, bt_h, prk, prv, tau_k, tau_v)
-        lib.paged_decode_attn(c, qs[i % copies], seq_lens, inp.max_seq_len, bt_q, bt_h, prk, prv, out, ws,
-                              split_pages=args.split_pages)
-
-    for i in range(args.warmup):
-        serve(i)
-    torch.cuda.synchronize()
-    s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    s0.record()
-    for i in range(K):
-        serve(i)
-    s1.record()
-    torch.cuda.synchronize()
-    serve_ms = s0.elapsed_time(s1) / K
-    s0.record()
-    for i in range(K):
-        lib.decode_step_update(caches[i % copies], n_k, n_v, seq_lens, bt_q, bt_h, pools[i % copies][2],
-                               pools[i % copies][3], tau_k, tau_v)
-    s1.record()
-    torch.cuda.synchronize()
-    upd_ms = s0.elapsed_time(s1) / K
-    result["serving_step"] = {"kernels": [f"quantize_rows_kernel<{w.d},true>", decode_kernel_name(w, args.split_pages, False)],
-                              "us_per_step": round(serve_ms * 1e3, 2),
-                              "KV_tokens_per_s": round(tokens / (serve_ms * 1e-3), 1),
-                              "update_us_per_call": round(upd_ms * 1e3, 2)}
-    log(f"serving step (update + decode) {serve_ms * 1e3:.1f} us, update alone {upd_ms * 1e3:.1f} us")
 
     # attainable bandwidth, as context for the roofline fraction, over 1 GiB
     # (several times the Infinity Cache): a streaming read of the buffer with
@@ -374,8 +395,8 @@ def main() -> int:
     result["bw_probe"] = {"read_GBps": round(rprobe, 1), "stream_GBps": round(probe, 1),
                           "method": "oscar_bw_probe_read over a 1 GiB buffer (read bytes); torch.mul over a "
                                     "1 GiB float32 buffer (read + write bytes)",
-                          "decode_frac_of_read_probe": round(achieved / rprobe, 4)}
-    log(f"bw probes: read {rprobe:.0f} GB/s, read+write {probe:.0f} GB/s; decode at {achieved / rprobe:.1%} of the read probe")
+                          "step_frac_of_read_probe": round(achieved / rprobe, 4)}
+    log(f"bw probes: read {rprobe:.0f} GB/s, read+write {probe:.0f} GB/s; step at {achieved / rprobe:.1%} of the read probe")
 
     if not args.no_bf16_baseline:
         # the same decode over an all-BF16 cache (every token in BF16 pages)

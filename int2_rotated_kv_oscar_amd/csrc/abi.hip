@@ -333,14 +333,16 @@ oscar_status decode_validate(bool all_raw, const oscar_cache* cache, const void*
 oscar_status decode_launch(bool all_raw, const oscar_cache* cache, const void* q, int32_t batch, int32_t n_q_heads,
                            const int32_t* seq_lens, int32_t max_seq_len, const int32_t* bt_q, const int32_t* bt_h,
                            int32_t max_pages, const float* r_k, const float* r_v, float sm_scale,
-                           const DecodePlan& plan, int32_t* counters, float* partials, void* out, void* stream) {
+                           const DecodePlan& plan, int32_t* counters, float* partials, void* out, void* stream,
+                           const void* k_new, const void* v_new, float tau_k, float tau_v) {
   const int G = n_q_heads / cache->n_kv_heads;
   return hip_status(
       oscar_launch::paged_decode(cache->d, all_raw, cache->int2_pool, cache->n_int2_pages, cache->bf16_pool, cache->n_kv_heads, G,
                                  cache->n_sink, cache->n_recent, n_q_heads, q, batch, seq_lens, all_raw ? bt_h : bt_q,
                                  bt_h, max_pages, r_k, r_v, sm_scale, plan.per_unit, plan.unit_items, plan.fixed_ppw,
                                  plan.n_wg, plan.cap, max_seq_len, partials, counters, plan.rec_floats, out,
-                                 4LL * batch * cache->n_kv_heads < device_cu_count(), static_cast<hipStream_t>(stream)),
+                                 4LL * batch * cache->n_kv_heads < device_cu_count(), k_new, v_new, tau_k, tau_v,
+                                 static_cast<hipStream_t>(stream)),
       "decode launch");
 }
 
@@ -364,10 +366,6 @@ static oscar_status decode_common(bool all_raw, const oscar_cache* cache, const 
   return oscar::decode_launch(all_raw, cache, q, batch, n_q_heads, seq_lens, max_seq_len, bt_q, bt_h, max_pages, r_k,
                               r_v, sm_scale, plan, counters, partials, out, stream);
 }
-
-extern "C" {
-
-}  // extern "C"
 
 namespace {
 
@@ -504,6 +502,42 @@ oscar_status oscar_paged_decode_attn(const oscar_cache* cache, const void* q, in
                                      void* out, void* stream) {
   return decode_common(false, cache, q, batch, n_q_heads, seq_lens, max_seq_len, bt_q, bt_h, max_pages, r_k, r_v,
                        sm_scale, split_pages, workspace, workspace_bytes, out, stream);
+}
+
+oscar_status oscar_decode_step(const oscar_cache* cache, const void* k_new, const void* v_new, const void* q,
+                               int32_t batch, int32_t n_q_heads, const int32_t* seq_lens, int32_t max_seq_len,
+                               const int32_t* bt_q, const int32_t* bt_h, int32_t max_pages, const float* r_k,
+                               const float* r_v, float tau_k, float tau_v, float sm_scale, int32_t split_pages,
+                               void* workspace, size_t workspace_bytes, void* out, void* stream) {
+  oscar::clear_error();
+  DecodePlan plan;
+  if (oscar_status s = oscar::decode_validate(false, cache, q, batch, n_q_heads, seq_lens, max_seq_len, bt_q, bt_h,
+                                              max_pages, r_k, r_v, sm_scale, split_pages, out, &plan))
+    return s;
+  if (batch == 0) return OSCAR_OK;
+  if (!k_new || !v_new) return fail(OSCAR_ERR_INVALID_ARG, "null device pointer");
+  if (!(tau_k > 0.f) || !(tau_v > 0.f) || !std::isfinite(tau_k) || !std::isfinite(tau_v))
+    return fail(OSCAR_ERR_INVALID_ARG, "clip thresholds must be finite and positive");
+  if (!workspace) return fail(OSCAR_ERR_WORKSPACE, "workspace is NULL");
+  if (workspace_bytes < plan.bytes) return fail(OSCAR_ERR_WORKSPACE, "workspace smaller than oscar_decode_workspace_bytes");
+  int32_t* counters = static_cast<int32_t*>(workspace);
+  float* partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.counter_bytes);
+  if (!plan.per_unit) {
+    // Many units (balanced slices, one workgroup per CU with no slack): the
+    // update's round trips to memory would stall the workgroups that hold
+    // it, so the few-row update kernel runs first and the decode after it.
+    if (oscar_status s = hip_status(
+            oscar_launch::decode_step_update(cache->d, cache->n_kv_heads, cache->n_sink, cache->n_recent,
+                                             cache->int2_pool, cache->bf16_pool, k_new, v_new, batch, seq_lens,
+                                             bt_q, bt_h, max_pages, r_k, r_v, tau_k, tau_v,
+                                             static_cast<hipStream_t>(stream)),
+            "decode_step_update launch"))
+      return s;
+    return oscar::decode_launch(false, cache, q, batch, n_q_heads, seq_lens, max_seq_len, bt_q, bt_h, max_pages,
+                                r_k, r_v, sm_scale, plan, counters, partials, out, stream);
+  }
+  return oscar::decode_launch(false, cache, q, batch, n_q_heads, seq_lens, max_seq_len, bt_q, bt_h, max_pages, r_k,
+                              r_v, sm_scale, plan, counters, partials, out, stream, k_new, v_new, tau_k, tau_v);
 }
 
 oscar_status oscar_paged_decode_attn_bf16(const oscar_cache* cache, const void* q, int32_t batch, int32_t n_q_heads,

@@ -41,6 +41,8 @@ oscar_status decode_validate(bool all_raw, const oscar_cache* cache, const void*
 oscar_status decode_launch(bool all_raw, const oscar_cache* cache, const void* q, int32_t batch, int32_t n_q_heads,
                            const int32_t* seq_lens, int32_t max_seq_len, const int32_t* bt_q, const int32_t* bt_h,
                            int32_t max_pages, const float* r_k, const float* r_v, float sm_scale,
-                           const DecodePlan& plan, int32_t* counters, float* partials, void* out, void* stream);
+                           const DecodePlan& plan, int32_t* counters, float* partials, void* out, void* stream,
+                           const void* k_new = nullptr, const void* v_new = nullptr, float tau_k = 0.f,
+                           float tau_v = 0.f);
 
 }  // namespace oscar

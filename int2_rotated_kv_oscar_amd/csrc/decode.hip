@@ -63,6 +63,11 @@ struct DecParams {
   int32_t batch;
   int32_t per_unit;    // per-unit items (1) or balanced slices (0)
   int32_t unit_items;  // per-unit items: workgroups per (sequence, KV head)
+  // fused decode step: the step's new tokens (bf16 [B][n_kv][D]) and the clip
+  // thresholds of the token entering the middle history
+  const uint16_t* k_new;
+  const uint16_t* v_new;
+  float tau_k, tau_v;
 };
 
 constexpr int kWaves = 8;
@@ -167,7 +172,7 @@ struct PageOps {
   uint32_t kz[2];       // K zeros of token l16 (quads 0, 1 only)
   uint32_t vc[NW];      // VC words: channel l16 of each block, tokens of this quad
   uint32_t vs[2 * NG];  // V scales [quad][g][4 tokens]
-  uint32_t vz[2];       // V zeros of group l16, tokens 4quad..4quad+3 (l16 < NG only)
+  uint32_t vz[2];       // V zeros of group l16, tokens 4quad..4quad+3 (meaningful for l16 < NG)
 
   __device__ __forceinline__ void read_k(const uint8_t* base, int l16, int quad) {
     using GG = Geo<D>;
@@ -177,12 +182,11 @@ struct PageOps {
     for (int i = 0; i < NW; ++i) kc[i] = kcp[i];
 #pragma unroll
     for (int i = 0; i < 2 * NG; ++i) ks[i] = ksp[i];
-    kz[0] = kz[1] = 0;
-    if (quad < 2) {
-      const uint32_t* kzp = reinterpret_cast<const uint32_t*>(base + GG::KZ) + l16 * (NG / 2);
-      kz[0] = kzp[0];
-      if (NG == 4) kz[1] = kzp[1];
-    }
+    // every lane reads (the zero-term operand's rows for quads 2 and 3 are
+    // zero, so what those lanes hold does not reach a sum that is kept)
+    const uint32_t* kzp = reinterpret_cast<const uint32_t*>(base + GG::KZ) + l16 * (NG / 2);
+    kz[0] = kzp[0];
+    kz[1] = NG == 4 ? kzp[1] : 0u;
   }
   // GROUPED: only the V scales of group gsel (in vs[0], vs[1])
   template <bool GROUPED = false>
@@ -194,12 +198,11 @@ struct PageOps {
     for (int i = 0; i < NW; ++i) vc[i] = vcp[i];
 #pragma unroll
     for (int i = 0; i < (GROUPED ? 2 : 2 * NG); ++i) vs[i] = vsp[i];
-    vz[0] = vz[1] = 0;
-    if (l16 < NG) {
-      const uint32_t* vzp = reinterpret_cast<const uint32_t*>(base + GG::VZ) + (quad * NG + l16) * 2;
-      vz[0] = vzp[0];
-      vz[1] = vzp[1];
-    }
+    // every lane reads a valid slot (group min(l16, NG - 1)); rows l16 >= NG
+    // of the zero-term operand are cleared by the caller's lane mask
+    const uint32_t* vzp = reinterpret_cast<const uint32_t*>(base + GG::VZ) + (quad * NG + min(l16, NG - 1)) * 2;
+    vz[0] = vzp[0];
+    vz[1] = vzp[1];
   }
 };
 
@@ -224,7 +227,15 @@ constexpr int kRing = 6;  // pair slots per wave: the two steps being computed a
 // value products it also stands for channel group n%4, so that one B operand
 // (probability times that group's V scale) serves every channel block;
 // otherwise column n carries query n and each group has its own B operand.
-template <int D, bool ALL_RAW, bool SLICES, bool GC>
+// UPD (fused decode step): the launch also does the step's cache update.  The
+// segment whose BF16 pages include the new token's page writes the new token
+// to its slot before reading it; the INT2 segment holding the last middle
+// page quantizes the token entering the middle history (exactly as the
+// few-row quantize-append does), writes it to its INT2 slot for later steps,
+// leaves that slot out of its own page loop and adds the token to its record
+// from the decoded values.  Launched with per-unit items only: balanced
+// slices leave no workgroup the slack to absorb the update's round trips.
+template <int D, bool ALL_RAW, bool SLICES, bool GC, bool UPD>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   using GG = Geo<D>;
   constexpr int NG = GG::NG, NCB = GG::NCB, NKB = GG::NKB, HB = GG::HEAD_BYTES;
@@ -370,7 +381,139 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   const int lane = tid & 63, l16 = lane & 15, quad = lane >> 4;
   const int qcol = GC ? min(l16 >> 2, G - 1) : min(l16, G - 1);
   const int n_pairs = (c1 - c0 + 1) >> 1;
-  const int m0 = sp.m0, m1 = sp.m1, s1 = sp.s1, r0 = sp.r0;
+  // fused step: this INT2 segment holds the last middle token (the one that
+  // enters the middle history this step) and handles it apart from its loop
+  const bool owner = UPD && !is_raw && sp.m1 > sp.m0 && ((sp.m1 - 1) >> 4) >= c0 && ((sp.m1 - 1) >> 4) < c1;
+  const int m0 = sp.m0, m1 = owner ? sp.m1 - 1 : sp.m1, s1 = sp.s1, r0 = sp.r0;
+  float qf4[4] = {0.f, 0.f, 0.f, 0.f};  // fused step: this lane's q~ block (log2 units)
+  // Owner scratch past the per-wave results (8 waves x 16 queries x D floats)
+  // in the ring area, free once the page loop is over: slice partials
+  // [2][16][D], raw rows [2][D], decoded rotated k~, v~ [2][D], q~ [16][D],
+  // then [16] logits of the token, [16] and [16] rescale factors, codes and
+  // f16 scale/zero words
+  float* const own_s = reinterpret_cast<float*>(s_slots) + 8 * 16 * D;
+  float* const own_part = own_s;
+  float* const own_x = own_part + 2 * 16 * D;
+  float* const own_kv = own_x + 2 * D;
+  float* const own_q = own_kv + 2 * D;
+  float* const own_l = own_q + 16 * D;
+  uint8_t* const own_code = reinterpret_cast<uint8_t*>(own_l + 48);
+  uint16_t* const own_sz = reinterpret_cast<uint16_t*>(own_code + 2 * D);  // [tensor][g][scale, zero]
+  auto own_token = [&](const float (&qv)[4]) __attribute__((always_inline)) {
+    const int t = sp.m1 - 1;           // the token entering the middle history
+    const int slot = t & 15;
+    const size_t row = (size_t(b) * p.n_kv + h) * D;
+    // y = x R as the few-row kernel sums it: 16 slices of D/16 inputs, each a
+    // float32 multiply-add chain from zero, then the slices in order.  Thread
+    // task (tensor T, slice ks, channel quad c4); its R values are requested
+    // first, together with the raw row, so that the token costs one round
+    // trip to memory
+    constexpr int KS = D / 16, C4 = D / 4, NT = 2 * 16 * C4 / kThreads;
+    static_assert(2 * 16 * C4 == NT * kThreads, "tasks per thread");
+    f32x4 rr[NT][KS];
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int task = tid + n * kThreads, T = task / (16 * C4), ks = (task / C4) % 16, c4 = task % C4;
+      const float* R = (T ? p.r_v : p.r_k) + size_t(h) * D * D;
+#pragma unroll
+      for (int j = 0; j < KS; ++j) rr[n][j] = *reinterpret_cast<const f32x4*>(R + size_t(ks * KS + j) * D + 4 * c4);
+    }
+    // its raw K and V rows: from its BF16 slot (W >= 1), or the new token (W = 0)
+    uint16_t xb = 0;
+    if (tid < 2 * D) {
+      const int T = tid / D, c = tid % D;
+      if (p.W >= 1) {
+        const uint16_t* hp = p.bf16_pool + (size_t(bth[t >> 4]) * p.n_kv + h) * GG::BF16_HEAD_ELEMS;
+        xb = T == 0 ? hp[slot * D + c] : hp[16 * D + c * 16 + slot];
+      } else {
+        xb = (T == 0 ? p.k_new : p.v_new)[row + c];
+      }
+    }
+    // the scratch lies in the page rings: every wave is done reading its ring
+    lds_barrier();
+    if (tid < 2 * D) own_x[tid] = bf16_to_f32(xb);
+    // q~ of the group's queries (the columns that hold each query once)
+    if (rot_wave && (GC ? ((l16 & 3) == 0 && (l16 >> 2) < G) : l16 < G)) {
+      const int qi = GC ? (l16 >> 2) : l16;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) own_q[qi * D + 16 * wave + 4 * quad + r] = qv[r];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int n = 0; n < NT; ++n) {
+      const int task = tid + n * kThreads, T = task / (16 * C4), ks = (task / C4) % 16, c4 = task % C4;
+      f32x4 a = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < KS; ++j) {
+        const float x = own_x[T * D + ks * KS + j];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) a[c] = __builtin_fmaf(x, rr[n][j][c], a[c]);
+      }
+      *reinterpret_cast<f32x4*>(own_part + (T * 16 + ks) * D + 4 * c4) = a;
+    }
+    __syncthreads();
+    if (tid < 2 * D) {  // whole waves: a 32-channel group is half a wave
+      const int T = tid / D, c = tid % D;
+      float y = 0.f;
+#pragma unroll
+      for (int k = 0; k < 16; ++k) y += own_part[(T * 16 + k) * D + c];
+      const float tau = T ? p.tau_v : p.tau_k;
+      y = __builtin_amdgcn_fmed3f(y, -tau, tau);
+      float mn = y, mx = y;
+#pragma unroll
+      for (int m = 1; m < 32; m <<= 1) {
+        mn = fminf(mn, __shfl_xor(mn, m, 64));
+        mx = fmaxf(mx, __shfl_xor(mx, m, 64));
+      }
+      const uint32_t s16 = f16_bits(div3(mx - mn));
+      const uint32_t z16 = f16_bits(mn);
+      const float sf = f16_to_f32(s16), zf = f16_to_f32(z16);
+      int code = 0;
+      if (sf != 0.0f) code = min(max(int(__builtin_rintf((y - zf) / sf)), 0), 3);
+      own_code[T * D + c] = uint8_t(code);
+      if ((c & 31) == 0) {
+        own_sz[(T * NG + (c >> 5)) * 2] = uint16_t(s16);
+        own_sz[(T * NG + (c >> 5)) * 2 + 1] = uint16_t(z16);
+      }
+      own_kv[T * D + c] = __builtin_fmaf(float(code), sf, zf);
+    }
+    __syncthreads();
+    // the token's codes, scales and zeros into its INT2 slot (the layout the
+    // few-row quantize-append writes: whole K words, whole V bytes)
+    uint8_t* base = const_cast<uint8_t*>(p.int2_pool) + (size_t(btq[t >> 4]) * p.n_kv + h) * HB;
+    if (tid < 4 * GG::NW) {
+      const int quad2 = tid / GG::NW, w = tid % GG::NW;
+      uint32_t wd = 0;
+#pragma unroll
+      for (int gp = 0; gp < 2; ++gp)
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            wd |= uint32_t(own_code[64 * w + 32 * gp + 16 * hb + 4 * quad2 + r]) << (16 * (r & 1) + 8 * gp + 4 * hb + 2 * (r >> 1));
+      reinterpret_cast<uint32_t*>(base + GG::KC)[(quad2 * 16 + slot) * GG::NW + w] = wd;
+    } else if (tid >= 64 && tid < 64 + 16 * GG::NW) {
+      const int i = tid - 64, c16 = i & 15, w = i >> 4;
+      const int q4 = slot >> 2, r = slot & 3;
+      uint32_t bits = 0;
+#pragma unroll
+      for (int bb = 0; bb < 4; ++bb) bits |= uint32_t(own_code[D + 64 * w + 16 * bb + c16]) << (2 * bb);
+      base[GG::VC + ((q4 * 16 + c16) * GG::NW + w) * 4 + 2 * (r & 1) + (r >> 1)] = uint8_t(bits);
+    } else if (tid >= 128 && tid < 128 + 2 * NG) {
+      const int T = (tid - 128) / NG, g = (tid - 128) % NG;
+      const int iu = T == 0 ? slot * NG + g : ((slot >> 2) * NG + g) * 4 + (slot & 3);
+      reinterpret_cast<uint16_t*>(base + (T == 0 ? GG::KS : GG::VS))[iu] = own_sz[(T * NG + g) * 2];
+      reinterpret_cast<uint16_t*>(base + (T == 0 ? GG::KZ : GG::VZ))[iu] = own_sz[(T * NG + g) * 2 + 1];
+    }
+    // the token's logit for each query of the group (log2 units, as the loop's)
+    for (int qi = wave; qi < G; qi += kWaves) {
+      float a = 0.f;
+      for (int c = lane; c < D; c += 64) a = __builtin_fmaf(own_q[qi * D + c], own_kv[c], a);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) a += __shfl_xor(a, o, 64);
+      if (lane == 0) own_l[qi] = a;
+    }
+  };
 
   float m_run = kNegInf, l_part = 0.f;
   f32x4 acc[NCB];
@@ -418,7 +561,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     for (int j = 0; j < NP; ++j)
       mx = fmaxf(mx, fmaxf(fmaxf(lg[j][0], lg[j][1]), fmaxf(lg[j][2], lg[j][3])));
     mx = wave_max16(mx);
-    if (__any(mx > kSlack || m_run == kNegInf)) {
+    if (__any(mx > kSlack || m_run == kNegInf)) {  // rare: everything rescaled in place
       const float m_new = fmaxf(m_run, mx + m_off);
       const float f = (m_run == kNegInf) ? 0.f : exp2f(m_run - m_new);
 #pragma unroll
@@ -430,17 +573,30 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
 #pragma unroll
       for (int j = 0; j < NP; ++j)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) pv[j][r] = __builtin_amdgcn_exp2f(lg[j][r] - dl);
-    } else {
-#pragma unroll
-      for (int j = 0; j < NP; ++j)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) pv[j][r] = __builtin_amdgcn_exp2f(lg[j][r]);
+        for (int r = 0; r < 4; ++r) lg[j][r] -= dl;
     }
+#pragma unroll
+    for (int j = 0; j < NP; ++j)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pv[j][r] = __builtin_amdgcn_exp2f(lg[j][r]);
   };
 
   if (is_raw) {
     // ---------------- BF16 chunk: raw q . k, raw-basis value sums ----------------
+    if (UPD && (p.W >= 1 || sp.L - 1 < p.S)) {
+      // fused step: the new token (position L - 1) to its BF16 slot, if this
+      // segment reads that page, before the page is read
+      const int pg = (sp.L - 1) >> 4, n_a = sp.ra1 - sp.ra0;
+      const int li = pg < sp.ra1 ? pg - sp.ra0 : n_a + (pg - sp.rb0);
+      if (li >= c0 && li < c1) {
+        uint16_t* hp = const_cast<uint16_t*>(p.bf16_pool) + (size_t(bth[pg]) * p.n_kv + h) * GG::BF16_HEAD_ELEMS;
+        const size_t src = (size_t(b) * p.n_kv + h) * D;
+        const int slot = (sp.L - 1) & 15;
+        if (tid < D) hp[slot * D + tid] = p.k_new[src + tid];
+        else if (tid < 2 * D) hp[16 * D + (tid - D) * 16 + slot] = p.v_new[src + tid - D];
+        __syncthreads();  // stores done and visible to this workgroup's page loads
+      }
+    }
     u32x4 bqr[NKB];
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) bqr[kb] = *reinterpret_cast<const u32x4*>(qb + size_t(qcol) * D + 32 * kb + 8 * quad);
@@ -535,6 +691,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
       }
       // a4[r] = q~[n = l16][c = 32g + 16hb + 4quad + r]; K-slot (e = 2hb + r/2, half r%2)
       const float v0 = a4[0] * qscale, v1 = a4[1] * qscale, v2 = a4[2] * qscale, v3 = a4[3] * qscale;
+      if (UPD) {
+        qf4[0] = v0; qf4[1] = v1; qf4[2] = v2; qf4[3] = v3;
+      }
       const float f0 = hb ? 1.f / 16.f : 1.f, f1 = hb ? 1.f / 64.f : 1.f / 4.f;
       s_qhat[(g * 64 + lane) * 4 + 2 * hb] = pack_f16x2(v0 * f0, v1 * f0);
       s_qhat[(g * 64 + lane) * 4 + 2 * hb + 1] = pack_f16x2(v2 * f1, v3 * f1);
@@ -559,6 +718,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
       bz = u32x4{pack2(hv[0], hv[1]), pack2(hv[2], hv[3]), pack2(hv[4], hv[5]), pack2(hv[6], hv[7])};
     }
     const uint32_t ones = l16 == NG ? 0x3C003C00u : 0u;  // f16 1.0 pairs in A row NG
+    const uint32_t zrow = l16 < NG ? 0xFFFFFFFFu : 0u;    // A rows that carry V zeros
     constexpr int NGV = GC ? 1 : NG;                       // V-scale B operands per pair
     const int gsel = min(l16 & 3, NG - 1);                 // GC: the group of column l16
     // one page pair: logits, softmax, value sums
@@ -633,7 +793,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
                                 pack_f16x2_rtz(pv[2 * pr + 1][2], pv[2 * pr + 1][3])};
         // zero terms (rows g < NG) and the softmax denominator (row NG: ones),
         // both from the same f16 probabilities the value sums use
-        acc_z = mfma_f16(u32x4{P[0].vz[0] | ones, P[0].vz[1] | ones, P[1].vz[0] | ones, P[1].vz[1] | ones},
+        acc_z = mfma_f16(u32x4{(P[0].vz[0] & zrow) | ones, (P[0].vz[1] & zrow) | ones, (P[1].vz[0] & zrow) | ones,
+                               (P[1].vz[1] & zrow) | ones},
                          u32x4{bp[0], bp[1], bp[2], bp[3]}, acc_z);
         // B operands: probabilities times V scales, one per group (GC: the
         // column's own group, one operand for every block)
@@ -698,6 +859,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
       step(k + 2);
     }
     wait_vm<0>();  // no ring load lands after the results reuse the ring
+    if (UPD && owner) own_token(qf4);
   }
 
   // ---- per-wave results -> LDS, merged over the 8 waves ----
@@ -748,14 +910,25 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
       const float mw = s_m[w * 16 + cq];
       if (mw != kNegInf) ll += exp2f(mw - mm) * s_l[w * 16 + cq];
     }
+    if (UPD && owner) {  // fused step: the token handled apart joins the record
+      const float lt = own_l[tid];
+      const float mn = fmaxf(mm, lt);
+      const float f1 = (mm == kNegInf) ? 0.f : exp2f(mm - mn), f2 = exp2f(lt - mn);
+      ll = __builtin_fmaf(ll, f1, f2);
+      mm = mn;
+      own_l[16 + tid] = f1;
+      own_l[32 + tid] = f2;
+    }
     st_dev(rec + tid, mm);
     st_dev(rec + G + tid, ll);
   }
+  if (UPD && owner) lds_barrier();
   if (tid == 0) st_dev(rec + 2 * G + G * D, is_raw ? 1.f : 0.f);
   for (int e = tid; e < G * D; e += kThreads) {
     float a = 0.f;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) a += s_res[w * G * D + e];
+    if (UPD && owner) a = __builtin_fmaf(a, own_l[16 + e / D], own_l[32 + e / D] * own_kv[D + e % D]);
     st_dev(rec + 2 * G + e, a);
   }
   // Hand-off to the unit's last workgroup: every thread's record stores are
@@ -1069,19 +1242,26 @@ hipError_t paged_decode(int d, bool all_raw, const void* int2_pool, int n_int2_p
                         const int32_t* bt_h, int max_pages, const float* r_k, const float* r_v, float sm_scale,
                         bool per_unit, int unit_items, int fixed_ppw, int n_wg, int cap, int max_seq_len,
                         float* partials, int32_t* counters, int rec_floats, void* out, bool speculate,
-                        hipStream_t stream) {
+                        const void* k_new, const void* v_new, float tau_k, float tau_v, hipStream_t stream) {
   DecParams p{static_cast<const uint8_t*>(int2_pool), std::max(1, n_int2_pages), static_cast<const uint16_t*>(bf16_pool), n_kv, G, S, W, Hq,
               static_cast<const uint16_t*>(q), seq_lens, bt_q, bt_h, max_pages, r_k, r_v, sm_scale, fixed_ppw,
               partials, counters, rec_floats, cap, static_cast<uint16_t*>(out), speculate ? 1 : 0, max_seq_len, batch,
-              per_unit ? 1 : 0, unit_items};
+              per_unit ? 1 : 0, unit_items, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+              tau_k, tau_v};
+  const bool upd = k_new != nullptr;
   const dim3 grid(static_cast<unsigned>(n_wg));
   const size_t lds = decode_lds_bytes(d, G, all_raw);
   // grouped columns when the query group fits four columns per query
   const bool gc = !all_raw && G <= 4;
-#define OSCAR_DECODE_LAUNCH(DD, RAW, GCOL)                                                                     \
-  do {                                                                                                        \
-    if (per_unit) hipLaunchKernelGGL((decode_kernel<DD, RAW, false, GCOL>), grid, dim3(kThreads), lds, stream, p); \
-    else hipLaunchKernelGGL((decode_kernel<DD, RAW, true, GCOL>), grid, dim3(kThreads), lds, stream, p);           \
+#define OSCAR_DECODE_LAUNCH(DD, RAW, GCOL)                                                                              \
+  do {                                                                                                                 \
+    if (upd && !RAW) {                                                                                                 \
+      if (!per_unit) return hipErrorInvalidValue;                                                                      \
+      hipLaunchKernelGGL((decode_kernel<DD, RAW, false, GCOL, !RAW>), grid, dim3(kThreads), lds, stream, p);           \
+    } else {                                                                                                           \
+      if (per_unit) hipLaunchKernelGGL((decode_kernel<DD, RAW, false, GCOL, false>), grid, dim3(kThreads), lds, stream, p); \
+      else hipLaunchKernelGGL((decode_kernel<DD, RAW, true, GCOL, false>), grid, dim3(kThreads), lds, stream, p);           \
+    }                                                                                                                  \
   } while (0)
   if (d == 128) {
     if (all_raw) OSCAR_DECODE_LAUNCH(128, true, false);

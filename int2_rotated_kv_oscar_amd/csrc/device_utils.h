@@ -85,6 +85,19 @@ __device__ __forceinline__ uint32_t shr8_halves(uint32_t x) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// r / 3: the product with 1/3 refined once with its exact residual, so that
+// a quotient representable in float32 comes out exactly.  With coarse
+// rotated values (a Hadamard or identity rotation of bf16 rows) the range is
+// often three times an f16 rounding midpoint; the exact quotient then rounds
+// to even on the way to f16, as the definition's real-number division does.
+// The 16-level variant divides by 15 the same way.
+template <int TOP = 3>
+__device__ __forceinline__ float div3(float r) {
+  constexpr float kInv = 1.0f / float(TOP);
+  const float s0 = r * kInv;
+  return __builtin_fmaf(__builtin_fmaf(-float(TOP), s0, r), kInv, s0);
+}
+
 __device__ __forceinline__ float shfl_xor_f(float v, int m) { return __shfl_xor(v, m, 64); }
 // Workgroup barrier that orders LDS accesses only: global loads still in
 // flight (prefetched pages) are not waited for, unlike __syncthreads().

@@ -28,12 +28,13 @@ int decode_max_records();  // record slots per (sequence, KV head) the merge can
 int decode_min_slice();    // pages per workgroup slice at least
 int decode_seg_pages();    // extra positions per nonempty page range in balanced slices
 
+// k_new != nullptr: the fused decode step (the step's cache update in the same launch)
 hipError_t paged_decode(int d, bool all_raw, const void* int2_pool, int n_int2_pages, const void* bf16_pool, int n_kv, int G, int S,
                         int W, int Hq, const void* q, int batch, const int32_t* seq_lens, const int32_t* bt_q,
                         const int32_t* bt_h, int max_pages, const float* r_k, const float* r_v, float sm_scale,
                         bool per_unit, int unit_items, int fixed_ppw, int n_wg, int cap, int max_seq_len,
                         float* partials, int32_t* counters, int rec_floats, void* out, bool speculate,
-                        hipStream_t stream);
+                        const void* k_new, const void* v_new, float tau_k, float tau_v, hipStream_t stream);
 
 // paged attention with many query columns (extend: chunked prefill over
 // INT2/INT4 pages; otherwise decode over an INT4 cache), and its merge

@@ -76,19 +76,6 @@ __device__ __forceinline__ uint32_t code_bits(float v, float z, float inv, float
   return uint32_t(min(max(b, int(kMagicBits)), int(kMagicBits + uint32_t(TOP))));
 }
 
-// r / 3: the product with 1/3 refined once with its exact residual, so that
-// a quotient representable in float32 comes out exactly.  With coarse
-// rotated values (a Hadamard or identity rotation of bf16 rows) the range is
-// often three times an f16 rounding midpoint; the exact quotient then rounds
-// to even on the way to f16, as the definition's real-number division does.
-// The 16-level variant divides by 15 the same way.
-template <int TOP = 3>
-__device__ __forceinline__ float div3(float r) {
-  constexpr float kInv = 1.0f / float(TOP);
-  const float s0 = r * kInv;
-  return __builtin_fmaf(__builtin_fmaf(-float(TOP), s0, r), kInv, s0);
-}
-
 // Reduction over the four lanes l16 + 16q of a row: the minimum of mn and the
 // maximum of mx, both computed in every lane with three lane swaps (the lower
 // half of the wave carries the minima, the upper half the negated maxima).

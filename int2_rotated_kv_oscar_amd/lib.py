@@ -30,6 +30,7 @@ EXPORTS = [
     "oscar_paged_decode_attn_bf16", "oscar_bw_probe_read", "oscar_paged_decode_attn_noalloc",
     "oscar_int4_page_bytes", "oscar_quantize_append_int4", "oscar_extend_workspace_bytes",
     "oscar_paged_extend_attn", "oscar_decode_int4_workspace_bytes", "oscar_paged_decode_attn_int4",
+    "oscar_decode_step",
 ]
 
 
@@ -89,6 +90,8 @@ def load(path: str = LIB_PATH):
                                                    _F32, _I32, _P, _SZ, _P, _P]),
         "oscar_bw_probe_read": (_STATUS, [_P, _SZ, _P, _P]),
         "oscar_int4_page_bytes": (_SZ, [_I32, _I32]),
+        "oscar_decode_step": (_STATUS, [ctypes.POINTER(OscarCache), _P, _P, _P, _I32, _I32, _P, _I32, _P, _P, _I32,
+                                        _P, _P, _F32, _F32, _F32, _I32, _P, _SZ, _P, _P]),
         "oscar_quantize_append_int4": (_STATUS, [ctypes.POINTER(OscarCache), _P, _P, _I64, _P, _P, _P, _I32, _P, _P,
                                                  _F32, _F32, _P]),
         "oscar_extend_workspace_bytes": (_STATUS, [_I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32, _I32,
@@ -353,3 +356,14 @@ def paged_decode_attn_int4(cache: OscarCache, q, seq_lens, max_seq_len: int, bt_
     _check(load().oscar_paged_decode_attn_int4(ctypes.byref(cache), _dptr(q), B, hq, _dptr(seq_lens), max_seq_len,
                                                _dptr(bt_q), _dptr(bt_h), bt_h.shape[1], _dptr(r_k), _dptr(r_v), sc,
                                                split_steps, ws, wsb, _dptr(out), _stream(stream)))
+
+
+def decode_step(cache: OscarCache, k_new, v_new, q, seq_lens, max_seq_len: int, bt_q, bt_h, r_k, r_v, tau_k: float,
+                tau_v: float, out, workspace, sm_scale: Optional[float] = None, split_pages: int = 0, stream=None):
+    """The step's cache update and the decode in one launch (oscar_decode_step)."""
+    B, hq, d = q.shape
+    sc = 1.0 / np.sqrt(d) if sm_scale is None else sm_scale
+    _check(load().oscar_decode_step(ctypes.byref(cache), _dptr(k_new), _dptr(v_new), _dptr(q), B, hq, _dptr(seq_lens),
+                                    max_seq_len, _dptr(bt_q), _dptr(bt_h), bt_h.shape[1], _dptr(r_k), _dptr(r_v),
+                                    float(tau_k), float(tau_v), sc, split_pages, _dptr(workspace),
+                                    workspace.numel() * workspace.element_size(), _dptr(out), _stream(stream)))
