@@ -112,7 +112,7 @@ oscar_status plan_decode(int32_t batch, int32_t n_kv, int32_t n_q, int32_t d, in
       split = (split + 7) / 8 * 8;  // measured: fewer, slightly larger items beat an uneven last pair round
     }
     const long long n_items = 1 + (max_pages + split - 1) / split;
-    if (n_items > max_rec) return fail(OSCAR_ERR_UNSUPPORTED, "more than 256 chunks per (sequence, KV head); use a larger split_pages");
+    if (n_items > max_rec) return fail(OSCAR_ERR_UNSUPPORTED, "more chunks per (sequence, KV head) than one merge takes; use a larger split_pages");
     if (units * n_items > (1LL << 31) - 1) return fail(OSCAR_ERR_UNSUPPORTED, "grid too large; use a larger split_pages");
     plan->fixed_ppw = int(split);
     plan->unit_items = int(n_items);

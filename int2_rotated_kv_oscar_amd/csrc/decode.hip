@@ -70,16 +70,27 @@ struct DecParams {
   float tau_k, tau_v;
 };
 
-constexpr int kWaves = 8;
+// Waves per workgroup (one workgroup per CU): 8 (two per SIMD, four page
+// pairs in flight per wave) or 12 (three per SIMD, at most 168 VGPRs each,
+// two pairs in flight).  Twelve passes the same tests but measured 10-15%
+// slower on every decode workload, so eight is the build.
+#ifndef OSCAR_DECODE_WAVES
+#define OSCAR_DECODE_WAVES 8
+#endif
+constexpr int kWaves = OSCAR_DECODE_WAVES;
+static_assert(kWaves == 8 || kWaves == 12, "8 or 12 waves per workgroup");
 constexpr int kThreads = 64 * kWaves;
-constexpr int kMaxChunks = 256;   // records (segments) per (sequence, KV head)
-constexpr int kMinSlice = 16;     // pages per workgroup slice at least (a page pair per wave)
+constexpr int kMergeBatch = kThreads / 16;  // chunk records loaded per merge round
+constexpr int kMaxChunks = 8 * kMergeBatch; // records (segments) per (sequence, KV head)
+constexpr int kMinSlice = 2 * kWaves;       // pages per workgroup slice at least (a page pair per wave)
+// LDS floats before the page-id blocks: per-wave max [kWaves][16], per-wave
+// sum [kWaves][16], flags [16], per-block query sums [8][16]
+constexpr int kMisc = 32 * kWaves + 16 + 128;
 // Balanced slices count each nonempty page range (a unit's BF16 pages, its
 // INT2 pages) as this many extra pages: the fixed cost of a segment
 // (requests, query rotation, record, arrival), about what a CU streams of
 // INT2 pages in that time.  Slices crossing many short units get fewer pages.
 constexpr int kSegPages = 96;
-constexpr int kMergeBatch = 32;   // chunk records loaded per merge round
 static_assert(kMaxChunks * 16 % kThreads == 0, "merge: (record, query row) slots split evenly over threads");
 constexpr float kTwo24 = 16777216.0f;
 constexpr float kSlack = 4.0f;    // log2 units
@@ -217,7 +228,10 @@ struct PairDma {
   static constexpr int LOADS = (2 * HB + 1023) / 1024;
   static constexpr int SLOT = LOADS * 1024;
 };
-constexpr int kRing = 6;  // pair slots per wave: the two steps being computed and two pairs in flight
+// page pairs requested ahead of the step being computed, and ring slots per
+// wave (the two pairs being computed and those in flight)
+constexpr int kDepth = kWaves == 8 ? 4 : 2;
+constexpr int kRing = kDepth + 2;
 
 
 // SLICES: balanced slices over all units (several segments per workgroup),
@@ -242,18 +256,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   const int G = p.G;
   // LDS: q-hat B operands [NG][64][4] u32 | zero-term operand [64][4] u32 |
-  // misc 512 floats | page rings [8 waves][kRing][SLOT], which the per-wave
+  // misc kMisc floats | page-id blocks | page rings [kWaves][kRing][SLOT], which the per-wave
   // results and the merge reuse once the page loop is over
   uint32_t* s_qhat = reinterpret_cast<uint32_t*>(smem);
   uint32_t* s_qz = s_qhat + NG * 256;
   float* s_misc = reinterpret_cast<float*>(s_qz + 256);
-  float* s_m = s_misc;             // [8][16] per-wave max
-  float* s_l = s_misc + 128;       // [8][16] per-wave sum
-  int* s_flag = reinterpret_cast<int*>(s_misc + 256);  // [16]
-  uint32_t* s_tabs = reinterpret_cast<uint32_t*>(s_misc + 512);  // [8 waves][2][64] page-id blocks
+  float* s_m = s_misc;                // [kWaves][16] per-wave max
+  float* s_l = s_misc + 16 * kWaves;  // [kWaves][16] per-wave sum
+  int* s_flag = reinterpret_cast<int*>(s_misc + 32 * kWaves);  // [16]
+  uint32_t* s_tabs = reinterpret_cast<uint32_t*>(s_misc + kMisc);  // [kWaves][2][64] page-id blocks
   uint8_t* s_slots = reinterpret_cast<uint8_t*>(s_tabs + kWaves * 2 * 64);
   float* s_res = reinterpret_cast<float*>(s_slots);
-  // s_res: per-wave results [8][G][D]; in the last workgroup: merged [G][D] rot
+  // s_res: per-wave results [kWaves][G][D]; in the last workgroup: merged [G][D] rot
   // and [G][D] raw
 
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, quad = lane >> 4;
@@ -286,8 +300,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   // table reads stay inside the row and page ids are clamped into the pool;
   // such pages are never used unmasked. ----
   using PD = PairDma<D>;
-  constexpr int kDepth = 4;  // page pairs requested ahead of the step being computed
-  static_assert(kRing == kDepth + 2, "ring: two pairs computed, kDepth in flight");
   uint8_t* const ring = s_slots + wave * kRing * PD::SLOT;
   const bool rot_wave = wave < NCB;
   float rvals[NKB][8];
@@ -386,12 +398,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   const bool owner = UPD && !is_raw && sp.m1 > sp.m0 && ((sp.m1 - 1) >> 4) >= c0 && ((sp.m1 - 1) >> 4) < c1;
   const int m0 = sp.m0, m1 = owner ? sp.m1 - 1 : sp.m1, s1 = sp.s1, r0 = sp.r0;
   float qf4[4] = {0.f, 0.f, 0.f, 0.f};  // fused step: this lane's q~ block (log2 units)
-  // Owner scratch past the per-wave results (8 waves x 16 queries x D floats)
+  // Owner scratch past the per-wave results (kWaves x 16 queries x D floats)
   // in the ring area, free once the page loop is over: slice partials
   // [2][16][D], raw rows [2][D], decoded rotated k~, v~ [2][D], q~ [16][D],
   // then [16] logits of the token, [16] and [16] rescale factors, codes and
   // f16 scale/zero words
-  float* const own_s = reinterpret_cast<float*>(s_slots) + 8 * 16 * D;
+  float* const own_s = reinterpret_cast<float*>(s_slots) + kWaves * 16 * D;
   float* const own_part = own_s;
   float* const own_x = own_part + 2 * 16 * D;
   float* const own_kv = own_x + 2 * D;
@@ -408,12 +420,11 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     // task (tensor T, slice ks, channel quad c4); its R values are requested
     // first, together with the raw row, so that the token costs one round
     // trip to memory
-    constexpr int KS = D / 16, C4 = D / 4, NT = 2 * 16 * C4 / kThreads;
-    static_assert(2 * 16 * C4 == NT * kThreads, "tasks per thread");
+    constexpr int KS = D / 16, C4 = D / 4, NTASK = 2 * 16 * C4, NT = (NTASK + kThreads - 1) / kThreads;
     f32x4 rr[NT][KS];
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
-      const int task = tid + n * kThreads, T = task / (16 * C4), ks = (task / C4) % 16, c4 = task % C4;
+      const int task = min(tid + n * kThreads, NTASK - 1), T = task / (16 * C4), ks = (task / C4) % 16, c4 = task % C4;
       const float* R = (T ? p.r_v : p.r_k) + size_t(h) * D * D;
 #pragma unroll
       for (int j = 0; j < KS; ++j) rr[n][j] = *reinterpret_cast<const f32x4*>(R + size_t(ks * KS + j) * D + 4 * c4);
@@ -442,6 +453,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
 #pragma unroll
     for (int n = 0; n < NT; ++n) {
       const int task = tid + n * kThreads, T = task / (16 * C4), ks = (task / C4) % 16, c4 = task % C4;
+      if (task >= NTASK) break;
       f32x4 a = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < KS; ++j) {
@@ -676,7 +688,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     // the rotation of the query runs while the first page pairs are in flight:
     // wave w rotates the 16-channel block cb = w (group w/2, half w%2) with a
     // bf16 hi/lo split of R_K (16 significant bits; q~ is rounded to f16 afterwards)
-    float* s_qsp = s_misc + 272;  // [NCB][16] per-block query sums
+    float* s_qsp = s_misc + 32 * kWaves + 16;  // [NCB][16] per-block query sums
     wait_vm<kDepth * PD::LOADS + 1>();  // the rotation operands (older than the page-id block and pages)
     if (rot_wave) {
       const int g = wave >> 1, hb = wave & 1;
@@ -813,16 +825,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
       }
     };
 
-    // Ring of kRing pair slots per wave, pair j in slot j % kRing.  Four pairs
-    // per iteration, two steps of two: before each step the next two pairs
-    // are requested (into the slots the previous step read) and the step's
-    // own pairs are waited for.  The loads after a step's pairs are the
-    // 4 pairs requested since, hence vmcnt(4 LOADS).
+    // Ring of kRing pair slots per wave, pair j in slot j % kRing.  kDepth
+    // pairs per iteration, in steps of two: before each step the next two
+    // pairs are requested (into the slots the previous step read) and the
+    // step's own pairs are waited for.  The loads after a step's pairs are
+    // the kDepth pairs requested since, hence vmcnt(kDepth LOADS).
     // Loads run unconditionally, past the last pair too (clamped), so that
     // the count holds; only the compute is skipped.
     // (A page-id block request between them only makes the wait stronger.)
-    static_assert(32 % kDepth == 0 && kDepth == 4, "page-id blocks and pair steps");
-    constexpr int kAfter = 4 * PD::LOADS;
+    static_assert(32 % kDepth == 0 && kDepth % 2 == 0, "page-id blocks and pair steps");
+    constexpr int kAfter = kDepth * PD::LOADS;
     for (int k = 0; k < n_mine; k += kDepth) {
       // page-id block of this group's prefetch targets (advances one block at
       // a time; its LDS copy was requested a whole block of pairs ago)
@@ -849,14 +861,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
           else do_two(kk, sa, sb, has_b, std::false_type{});
         }
       };
-      pair_dma(min(k + 4, n_mine - 1), slot(4));
-      pair_dma(min(k + 5, n_mine - 1), slot(5));
-      wait_vm<kAfter>();
-      step(k);
-      pair_dma(min(k + 6, n_mine - 1), slot(6));
-      pair_dma(min(k + 7, n_mine - 1), slot(7));
-      wait_vm<kAfter>();
-      step(k + 2);
+#pragma unroll
+      for (int st = 0; st < kDepth; st += 2) {
+        pair_dma(min(k + kDepth + st, n_mine - 1), slot(kDepth + st));
+        pair_dma(min(k + kDepth + st + 1, n_mine - 1), slot(kDepth + st + 1));
+        wait_vm<kAfter>();
+        step(k + st);
+      }
     }
     wait_vm<0>();  // no ring load lands after the results reuse the ring
     if (UPD && owner) own_token(qf4);
@@ -939,10 +950,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   __syncthreads();
   if (tid == 0) {
     const int old = __hip_atomic_fetch_add(p.counters + b * p.n_kv + h, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    s_flag[8] = (old == nseg - 1) ? 1 : 0;
+    s_flag[0] = (old == nseg - 1) ? 1 : 0;
   }
   __syncthreads();
-  if (s_flag[8]) {
+  if (s_flag[0]) {
 
   // ---- last workgroup: log-sum-exp merge of the chunk records ----
   // The weights w_s[n] = 2^(m_s[n] - M[n]) come first, from every record's
@@ -1018,7 +1029,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     s_wu[s * 16 + ms_n] = cf[i] != 0.f ? wgt : 0.f;
   }
   lsum = wave_sum16(lsum);
-  if (quad == 0) s_red[128 + wave * 16 + ms_n] = lsum;
+  if (quad == 0) s_red[16 * kWaves + wave * 16 + ms_n] = lsum;
   lds_barrier();
   for (int e0 = 0; e0 < G * D; e0 += kThreads) {
     const int e = e0 + tid;
@@ -1035,7 +1046,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     if (e < G * D) {
       float Ln = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) Ln += s_red[128 + w * 16 + n];
+      for (int w = 0; w < kWaves; ++w) Ln += s_red[16 * kWaves + w * 16 + n];
       const float inv = 1.f / Ln;
       m_rot[e] = orot * inv;
       m_raw[e] = oraw * inv;
@@ -1076,14 +1087,17 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   };
 
   if constexpr (!SLICES) {
-    // Per-unit items (few units): workgroup wg is item x of unit u.  Item 0
+    // Per-unit items (few units): workgroup wg is item x of unit (b, h).  Item 0
     // takes the unit's BF16 pages, item x >= 1 INT2 pages
     // [q0 + (x-1) split, q0 + x split) (for the all-BF16 cache: item x takes
     // BF16 positions [x split, (x+1) split)).  INT2 items do not depend on the
     // length, so their requests go out before it is read.
+    // The KV head varies fastest over the workgroup index: the workgroups
+    // dispatched together read the same pages' head images (one page holds
+    // every head of its 16 tokens), which keeps HBM rows open.
     const int per = p.unit_items, split = p.fixed_ppw;
-    const int u = wg / per, x = wg - u * per;
-    set_unit(u / p.n_kv, u - (u / p.n_kv) * p.n_kv);
+    const int hw = wg % p.n_kv, bx = wg / p.n_kv, x = bx % per;
+    set_unit(bx / per, hw);
     // the length is requested first: waiting for it then leaves the early
     // page requests in flight
     const int L = p.seq_lens[b];
@@ -1114,8 +1128,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   // last segment to finish merges its records.
   // Work of the sequences: thread t sums a block of them; a block scan gives
   // each block's first position.
-  int* s_scan = reinterpret_cast<int*>(s_res);  // [8] wave totals, [8] owner's first position
-  int* s_scani = s_scan + 16;                   // [8] wave max cost, [8] owner
+  int* s_scan = reinterpret_cast<int*>(s_res);  // [kWaves] wave totals, [kWaves] owner's first position
+  int* s_scani = s_scan + 32;                   // [kWaves] wave max cost, [kWaves] owner
   const int seq_blk = (p.batch + kThreads - 1) / kThreads;
   int v = 0, cmax = 0;
   {
@@ -1160,14 +1174,14 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   const int hi = int(min((long long)total, (long long)lo + ppw));
   const int excl = woff + inc - v;  // first position of this thread's sequences
   if (v > 0 && excl <= lo && lo < excl + v) {
-    s_scan[8] = excl;
-    s_scani[8] = tid;
+    s_scan[kWaves] = excl;
+    s_scani[kWaves] = tid;
   }
   lds_barrier();
   // walk the owner's block to the unit holding position lo
-  int Cu = __builtin_amdgcn_readfirstlane(s_scan[8]);
+  int Cu = __builtin_amdgcn_readfirstlane(s_scan[kWaves]);
   {
-    int bb = __builtin_amdgcn_readfirstlane(s_scani[8]) * seq_blk;
+    int bb = __builtin_amdgcn_readfirstlane(s_scani[kWaves]) * seq_blk;
     sp = make_plan<ALL_RAW>(p, max(p.seq_lens[bb], 0));
     while (Cu + p.n_kv * sp.cost <= lo) {
       Cu += p.n_kv * sp.cost;
@@ -1234,7 +1248,7 @@ size_t decode_lds_bytes(int d, int G, bool all_raw) {
   const size_t rings = all_raw ? 0 : size_t(kWaves) * kRing * slot;
   size_t res = size_t(kWaves) * G * d;                              // per-wave results
   res = std::max(res, size_t(kMaxChunks) * 32 + 2 * kWaves * 16 + size_t(2) * G * d);  // merge
-  return (size_t(ng) * 256 + 256 + 512 + kWaves * 2 * 64) * 4 + std::max(rings, res * 4);
+  return (size_t(ng) * 256 + 256 + kMisc + kWaves * 2 * 64) * 4 + std::max(rings, res * 4);
 }
 
 hipError_t paged_decode(int d, bool all_raw, const void* int2_pool, int n_int2_pages, const void* bf16_pool, int n_kv, int G, int S,
