@@ -395,8 +395,10 @@ __device__ __forceinline__ UnitRows unit_rows(const AttParams& p, int unit) {
 // MODE 0: extend (rows of new tokens at positions P + i, causal over them);
 // MODE 1: decode (one query row per sequence at position L - 1, over the
 // whole length-L cache).
+// At least two waves per SIMD: without the bound the compiler takes up to 288
+// registers per lane, which leaves one wave per SIMD (one 4-wave workgroup per CU).
 template <int D, int BITS, int NWV, int MODE>
-__global__ __launch_bounds__(64 * NWV) void attend_kernel(AttParams p) {
+__global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
   using T = Tile<D>;
   constexpr int NCB = D / 16, NKB = D / 32, NTH = 64 * NWV;
   constexpr int NBUF = NWV > 1 ? 2 : 1;
