@@ -391,7 +391,7 @@ oscar_status plan_attend(bool extend, int32_t batch, int32_t n_kv, int32_t n_q, 
   const int G = n_q / n_kv;
   if (G > 16) return fail(OSCAR_ERR_UNSUPPORTED, "query group size above 16");
   if (split_steps < 0) return fail(OSCAR_ERR_INVALID_ARG, "split_steps < 0");
-  const int nwv = oscar_launch::attend_waves(extend);
+  const int nwv = oscar_launch::attend_waves(extend, d);
   const long long cols = extend ? (long long)max_new * G : G;
   plan->n_ct = int(std::max(1LL, (cols + 16 * nwv - 1) / (16 * nwv)));
   const long long pages = (max_cache_len + 15LL) / 16;

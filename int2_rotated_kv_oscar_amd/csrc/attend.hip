@@ -176,6 +176,7 @@ __device__ __forceinline__ void step_load(const AttParams& p, const Regions& rg,
 #pragma unroll
     for (int it = 0; it < SG::NQ; ++it) {
       const int e0 = t + it * NTH;
+      if (NTH > 2 * D && e0 >= 2 * D) break;  // whole waves without an item (wide workgroups)
       const int e = e0 < 2 * D ? e0 : 0;
       const int j = e / D, wi = e % D;
       const int pg = min(rg.q0 + si.i0 + j, rg.q1 - 1);
@@ -764,13 +765,18 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttParams p) {
 
 namespace oscar_launch {
 
+// Waves per workgroup: extend at d = 128 takes 8 waves (128 query columns), so
+// each decoded step feeds twice the products of a 4-wave workgroup; at d = 64
+// the query rotation's channel blocks (d/16 = 4) bound it to 4 waves.
+int attend_waves(bool extend, int d) { return extend ? (d == 128 ? 8 : 4) : 1; }
+
 size_t attend_lds_bytes(int d, bool extend) {
-  const int nwv = extend ? 4 : 1, nbuf = extend ? 2 : 1;
+  const int nwv = attend_waves(extend, d), nbuf = extend ? 2 : 1;
   const size_t elems = d == 128 ? Tile<128>::ELEMS : Tile<64>::ELEMS;
   return size_t(nbuf) * elems * 2 + size_t(nwv) * 16 * d * 4;
 }
 
-int attend_waves(bool extend) { return extend ? 4 : 1; }
+
 
 hipError_t paged_attend(int d, int bits, bool extend, const void* qpool, int n_qpages, const void* bf16_pool,
                         int n_bpages, int n_kv, int G, int S, int W, int Hq, const void* q, const void* k_new,
@@ -792,7 +798,7 @@ hipError_t paged_attend(int d, int bits, bool extend, const void* qpool, int n_q
     if (n_chunks > 1) hipLaunchKernelGGL((attend_merge_kernel<DD, NW, MM>), mgrid, dim3(256), mlds, stream, p); \
   } while (0)
   if (d == 128) {
-    if (extend) { if (bits == 2) OSCAR_ATTEND(128, 2, 4, 0); else OSCAR_ATTEND(128, 4, 4, 0); }
+    if (extend) { if (bits == 2) OSCAR_ATTEND(128, 2, 8, 0); else OSCAR_ATTEND(128, 4, 8, 0); }
     else { if (bits == 2) OSCAR_ATTEND(128, 2, 1, 1); else OSCAR_ATTEND(128, 4, 1, 1); }
   } else {
     if (extend) { if (bits == 2) OSCAR_ATTEND(64, 2, 4, 0); else OSCAR_ATTEND(64, 4, 4, 0); }
