@@ -532,7 +532,10 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
   }
 
   // products and online softmax of one step over the tile
-  auto compute = [&](const uint16_t* tile, const StepInfo& si) __attribute__((always_inline)) {
+  // full: a quantized step whose 32 tokens all lie in the middle region (no
+  // per-token masks; columns past the unit's last carry finite values that
+  // are never written)
+  auto compute = [&](const uint16_t* tile, const StepInfo& si, const bool full) __attribute__((always_inline)) {
     const bool quantized = si.kind == 1;
     f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -545,6 +548,15 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
     // logits of tokens 16 j + 4 quad + r for column l16 (log2 units), masked
     float lg[2][4];
     float mx = kNegInfA;
+    if (full) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          lg[j][r] = sc[j][r];
+          mx = fmaxf(mx, lg[j][r]);
+        }
+    } else {
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -564,6 +576,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
         lg[j][r] = ok ? (quantized ? sc[j][r] : sc[j][r] * qscale) : kNegInfA;
         mx = fmaxf(mx, lg[j][r]);
       }
+    }
     mx = wave_max16(mx);
     if (__any(mx > m_run)) {
       const float m_new = fmaxf(m_run, mx);
@@ -621,7 +634,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
     uint16_t* tile = tile_of(s);
     step_store<D, BITS, NTH>(p, rg, bth, h, row0, n_rows, si, stq[0], tile, tid);
     lds_barrier();
-    compute(tile, si);
+    compute(tile, si, false);
     if (NBUF == 1) lds_barrier();
   };
 #pragma unroll 1
@@ -643,7 +656,9 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
         step_store<D, BITS, NTH>(p, rg, bth, h, row0, n_rows, si, stq[k], tile, tid);
         step_load<D, BITS, NTH>(p, rg, btq, bth, h, row0, n_rows, qinfo(s + k + DEPTH), stq[k], tid);
         lds_barrier();  // the tile is complete; the loads just issued stay in flight
-        compute(tile, si);
+        const int pg0 = rg.q0 + si.i0;
+        const bool full = pg0 + 1 < rg.q1 && 16 * pg0 >= rg.m0 && 16 * (pg0 + 2) <= rg.m1;
+        compute(tile, si, full);
         if (NBUF == 1) lds_barrier();
       }
     }
