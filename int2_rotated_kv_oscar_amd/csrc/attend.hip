@@ -33,6 +33,7 @@ using namespace oscar_dev;
 namespace {
 
 constexpr float kNegInfA = -__builtin_inff();
+constexpr float kSlackA = 4.0f;  // log2 units
 
 struct AttParams {
   const uint8_t* qpool;    // INT2 or INT4 pool
@@ -578,7 +579,9 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
       }
     }
     mx = wave_max16(mx);
-    if (__any(mx > m_run)) {
+    // lazy rescale: the reference max moves only when a logit exceeds it by
+    // more than kSlackA (probabilities stay <= 2^kSlackA, exact enough in f16)
+    if (__any(mx > m_run + kSlackA)) {
       const float m_new = fmaxf(m_run, mx);
       const float f = (m_run == kNegInfA) ? 0.f : exp2f(m_run - m_new);
 #pragma unroll
