@@ -391,9 +391,9 @@ oscar_status plan_attend(bool extend, int32_t batch, int32_t n_kv, int32_t n_q, 
   const int G = n_q / n_kv;
   if (G > 16) return fail(OSCAR_ERR_UNSUPPORTED, "query group size above 16");
   if (split_steps < 0) return fail(OSCAR_ERR_INVALID_ARG, "split_steps < 0");
-  const int nwv = oscar_launch::attend_waves(extend, d);
+  const int nct = oscar_launch::attend_cols(extend, d);  // query columns of a workgroup tile
   const long long cols = extend ? (long long)max_new * G : G;
-  plan->n_ct = int(std::max(1LL, (cols + 16 * nwv - 1) / (16 * nwv)));
+  plan->n_ct = int(std::max(1LL, (cols + nct - 1) / nct));
   const long long pages = (max_cache_len + 15LL) / 16;
   const long long raw = std::min(pages, (S + 15LL) / 16 + (W + 15LL) / 16 + 2);
   const long long steps = (raw + 1) / 2 + (pages + 2) / 2 + (extend ? (max_new + 31LL) / 32 : 0);
@@ -410,7 +410,7 @@ oscar_status plan_attend(bool extend, int32_t batch, int32_t n_kv, int32_t n_q, 
   if (units * plan->n_ct * n_chunks > (1LL << 31) - 1) return fail(OSCAR_ERR_UNSUPPORTED, "grid too large; use a larger split_steps");
   plan->spc = int(std::min<long long>(spc, 1 << 30));
   plan->n_chunks = int(n_chunks);
-  plan->bytes = plan->n_chunks > 1 ? size_t(units) * plan->n_ct * plan->n_chunks * 16 * nwv * (2 + 2 * size_t(d)) * 4 : 0;
+  plan->bytes = plan->n_chunks > 1 ? size_t(units) * plan->n_ct * plan->n_chunks * nct * (2 + 2 * size_t(d)) * 4 : 0;
   return OSCAR_OK;
 }
 

@@ -332,47 +332,6 @@ __device__ __forceinline__ void step_store(const AttParams& p, const Regions& rg
   }
 }
 
-// out^T[c][n] = (raw^T[c][n] + sum_k R_V[c][k] rot[n][k]) / l for the 16
-// columns of a wave: rot (fp32 [16][D]) in the wave's LDS area, raw in the
-// accumulator layout; R_V rows and rot split into bf16 hi + lo (three
-// products per block).  Writes the bf16 row of column l16 if `ok`.
-template <int D>
-__device__ __forceinline__ void finish_columns(const float* rv, const float* rot, const f32x4 (&acc_raw)[D / 16],
-                                               float l_tot, bool ok, uint16_t* orow, int l16, int quad) {
-  constexpr int NCB = D / 16, NKB = D / 32;
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-#pragma unroll 1
-  for (int cb = 0; cb < NCB; ++cb) {
-    f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const f32x4 ra0 = *reinterpret_cast<const f32x4*>(rv + size_t(16 * cb + l16) * D + 32 * kb + 8 * quad);
-      const f32x4 ra1 = *reinterpret_cast<const f32x4*>(rv + size_t(16 * cb + l16) * D + 32 * kb + 8 * quad + 4);
-      const float* rb = rot + l16 * D + 32 * kb + 8 * quad;
-      const float ra[8] = {ra0[0], ra0[1], ra0[2], ra0[3], ra1[0], ra1[1], ra1[2], ra1[3]};
-      uint32_t ah[4], al[4], bh[4], bl[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ah[i] = pack2(bf16_rne(ra[2 * i]), bf16_rne(ra[2 * i + 1]));
-        al[i] = pack2(bf16_rne(ra[2 * i] - bf16_to_f32(ah[i] & 0xFFFFu)), bf16_rne(ra[2 * i + 1] - bf16_to_f32(ah[i] >> 16)));
-        bh[i] = pack2(bf16_rne(rb[2 * i]), bf16_rne(rb[2 * i + 1]));
-        bl[i] = pack2(bf16_rne(rb[2 * i] - bf16_to_f32(bh[i] & 0xFFFFu)), bf16_rne(rb[2 * i + 1] - bf16_to_f32(bh[i] >> 16)));
-      }
-      const u32x4 AH{ah[0], ah[1], ah[2], ah[3]}, AL{al[0], al[1], al[2], al[3]};
-      const u32x4 BH{bh[0], bh[1], bh[2], bh[3]}, BL{bl[0], bl[1], bl[2], bl[3]};
-      a4 = mfma_bf16(AL, BH, a4);
-      a4 = mfma_bf16(AH, BL, a4);
-      a4 = mfma_bf16(AH, BH, a4);
-    }
-    if (ok) {
-      u32x2 ov;
-      ov[0] = pack2(bf16_rne((a4[0] + acc_raw[cb][0]) * inv), bf16_rne((a4[1] + acc_raw[cb][1]) * inv));
-      ov[1] = pack2(bf16_rne((a4[2] + acc_raw[cb][2]) * inv), bf16_rne((a4[3] + acc_raw[cb][3]) * inv));
-      *reinterpret_cast<u32x2*>(orow + 16 * cb + 4 * quad) = ov;
-    }
-  }
-}
-
 // Unit of a workgroup and the rows of its sequence.
 struct UnitRows {
   int b, h, row0, n_rows, P;
@@ -396,14 +355,19 @@ __device__ __forceinline__ UnitRows unit_rows(const AttParams& p, int unit) {
 // ---- the kernel ----
 // MODE 0: extend (rows of new tokens at positions P + i, causal over them);
 // MODE 1: decode (one query row per sequence at position L - 1, over the
-// whole length-L cache).
-// At least two waves per SIMD: without the bound the compiler takes up to 288
-// registers per lane, which leaves one wave per SIMD (one 4-wave workgroup per CU).
-template <int D, int BITS, int NWV, int MODE>
+// whole length-L cache).  A wave owns CB blocks of 16 columns (CB = 2 for
+// extend), so every decoded step feeds CB times the products.  The steps of
+// a unit are listed quantized page pairs first, then BF16 page pairs, then
+// (extend) tiles of new rows.  A chunk runs its quantized steps with the
+// value sums in the rotated basis, turns them into the model basis (times
+// R_V^T on the MFMA) before its first raw step, so one accumulator set
+// serves both kinds.
+template <int D, int BITS, int NWV, int CB, int MODE>
 __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
   using T = Tile<D>;
   constexpr int NCB = D / 16, NKB = D / 32, NTH = 64 * NWV;
   constexpr int NBUF = NWV > 1 ? 2 : 1;
+  constexpr int NC = 16 * NWV * CB;  // columns of a tile
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   uint16_t* tiles = lds;                                               // [NBUF][T::ELEMS]
   float* fbuf = reinterpret_cast<float*>(lds + NBUF * T::ELEMS);       // [NWV][16][D] per-wave staging
@@ -422,231 +386,294 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
       for (int e = tid; e < p.Hq * D; e += NTH) p.out[size_t(b) * p.Hq * D + e] = 0;
     return;
   }
-  const int col0 = ct * 16 * NWV;                  // first column of the tile
+  const int col0 = ct * NC;                        // first column of the tile
   const int n_cols = n_rows * G;                   // columns of the unit
   if (col0 >= n_cols) return;
-  // this lane's column: row ri, head hi of the group
-  const int col = col0 + 16 * wave + l16;
-  const bool col_ok = col < n_cols;
-  const int ri = col_ok ? col / G : 0, hi = col_ok ? col % G : 0;
-  const int qpos = MODE == 0 ? P + ri : P - 1;     // the column's query position
-  const int last_row = min(n_rows, (col0 + 16 * NWV + G - 1) / G) - 1;  // last row with a column in the tile
-  const uint16_t* qrow = p.q + (size_t(row0 + ri) * p.Hq + h * G + hi) * D;
+  // this lane's columns: block c of the wave holds columns col0 + 16 (CB wave + c) + l16
+  bool col_ok[CB];
+  int ri[CB], hi[CB], qpos[CB];
+#pragma unroll
+  for (int c = 0; c < CB; ++c) {
+    const int col = col0 + 16 * (CB * wave + c) + l16;
+    col_ok[c] = col < n_cols;
+    ri[c] = col_ok[c] ? col / G : 0;
+    hi[c] = col_ok[c] ? col % G : 0;
+    qpos[c] = MODE == 0 ? P + ri[c] : P - 1;       // the column's query position
+  }
+  const int last_row = min(n_rows, (col0 + NC + G - 1) / G) - 1;  // last row with a column in the tile
+  auto qrow_of = [&](int c) { return p.q + (size_t(row0 + ri[c]) * p.Hq + h * G + hi[c]) * D; };
   const float qscale = p.sm_scale * kLog2e;
 
-  // ---- work of the unit: BF16 page pairs, quantized page pairs, new-row tiles ----
+  // ---- work of the unit: quantized page pairs, BF16 page pairs, new-row tiles ----
   const Regions rg = make_regions(max(P, 0), p.S, p.W);
   const int32_t* btq = p.bt_q + size_t(b) * p.max_pages;
   const int32_t* bth = p.bt_h + size_t(b) * p.max_pages;
   const int n_rp = (rg.n_raw + 1) >> 1;
   const int n_qp = (rg.q1 - rg.q0 + 1) >> 1;
   const int n_nt = MODE == 0 ? (last_row + 1 + 31) / 32 : 0;
-  const int total = n_rp + n_qp + n_nt;
+  const int total = n_qp + n_rp + n_nt;
   const int s_begin = chunk * p.spc, s_end = min(total, s_begin + p.spc);
-  // the chunk's quantized steps [qa, qb) (global step numbers)
-  const int qa = max(s_begin, n_rp), qb = min(s_end, n_rp + n_qp);
+  // the chunk's quantized steps [qa, qb) and raw steps [ra, s_end) (global step numbers)
+  const int qa = s_begin, qb = min(s_end, n_qp), ra = max(s_begin, n_qp);
+  const bool has_q = qa < qb;
   constexpr int DEPTH = NWV > 1 ? 2 : 1;  // quantized steps whose loads are in flight
   Stage<D, BITS, NTH> stq[DEPTH];
   auto qinfo = [&](int s) {  // steps past the chunk load a valid pair of it, never used
     StepInfo si;
     si.kind = 1;
-    si.i0 = 2 * (min(s, max(qb - 1, n_rp)) - n_rp);
+    si.i0 = 2 * min(s, max(qb - 1, 0));
     return si;
   };
 #pragma unroll
   for (int k = 0; k < DEPTH; ++k)
-    if (qa < qb) step_load<D, BITS, NTH>(p, rg, btq, bth, h, row0, n_rows, qinfo(qa + k), stq[k], tid);
+    if (has_q) step_load<D, BITS, NTH>(p, rg, btq, bth, h, row0, n_rows, qinfo(qa + k), stq[k], tid);
 
-  // ---- query operands: raw q (bf16) of this wave's columns, and q~ = q R_K
-  // (f16, pre-scaled by qscale) for all the tile's columns: R_K staged in
-  // LDS 32 rows at a time, wave w computing channel blocks w, w + NWV, ... of
-  // every column block; q~ goes through LDS to the waves that own the columns ----
-  u32x4 bq_raw[NKB], bq_rot[NKB];
+  // ---- query operands: q~ = q R_K (f16, pre-scaled by qscale) for the
+  // quantized steps, computed for all the tile's columns in CB rounds: R_K
+  // staged in LDS 32 rows at a time, wave w computing channel blocks w,
+  // w + NWV, ... of the round's column blocks; q~ goes through LDS to the
+  // waves that own the columns.  The raw steps take the raw q (bf16). ----
+  u32x4 bq[CB][NKB];
+  auto load_raw_q = [&]() {
 #pragma unroll
-  for (int kb = 0; kb < NKB; ++kb) bq_raw[kb] = *reinterpret_cast<const u32x4*>(qrow + 32 * kb + 8 * quad);
-  {
-    constexpr int CPW = NCB / NWV;  // channel blocks per wave
-    const uint16_t* qcols[NWV];  // the q rows of the tile's column blocks (lane l16's column)
+    for (int c = 0; c < CB; ++c) {
+      const uint16_t* qr = qrow_of(c);
 #pragma unroll
-    for (int cbk = 0; cbk < NWV; ++cbk) {
-      const int c = col0 + 16 * cbk + l16;
-      const int rr = c < n_cols ? c / G : 0, hh = c < n_cols ? c % G : 0;
-      qcols[cbk] = p.q + (size_t(row0 + rr) * p.Hq + h * G + hh) * D;
+      for (int kb = 0; kb < NKB; ++kb) bq[c][kb] = *reinterpret_cast<const u32x4*>(qr + 32 * kb + 8 * quad);
     }
-    f32x4 qacc[CPW][NWV];
-#pragma unroll
-    for (int j = 0; j < CPW; ++j)
-#pragma unroll
-      for (int cbk = 0; cbk < NWV; ++cbk) qacc[j][cbk] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+  if (has_q) {
+    constexpr int CPW = NCB / NWV;  // channel blocks per wave
+    static_assert(CPW >= 1 && NCB % NWV == 0, "channel blocks split over the waves");
     float* rs = reinterpret_cast<float*>(tiles);  // [32][D] rows of R_K
     const float* rk = p.r_k + size_t(h) * D * D;
-#pragma unroll 1
-    for (int kb = 0; kb < NKB; ++kb) {
-      u32x4 qk[NWV];  // B operands: the q slice kb of every column block
 #pragma unroll
-      for (int cbk = 0; cbk < NWV; ++cbk) qk[cbk] = *reinterpret_cast<const u32x4*>(qcols[cbk] + 32 * kb + 8 * quad);
-      for (int e = tid; e < 32 * D / 4; e += NTH)
-        *reinterpret_cast<f32x4*>(rs + 4 * e) = *reinterpret_cast<const f32x4*>(rk + size_t(32 * kb) * D + 4 * e);
-      __syncthreads();
+    for (int c = 0; c < CB; ++c) {  // unrolled: bq[c] needs a constant index
+      const uint16_t* qcols[NWV];  // the q rows of the round's column blocks (lane l16's column)
 #pragma unroll
-      for (int j = 0; j < CPW; ++j) {
-        const int cb = wave + NWV * j;
-        float rv[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) rv[i] = rs[(8 * quad + i) * D + 16 * cb + l16];
-        uint32_t ph[4], pl[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          ph[i] = pack2(bf16_rne(rv[2 * i]), bf16_rne(rv[2 * i + 1]));
-          pl[i] = pack2(bf16_rne(rv[2 * i] - bf16_to_f32(ph[i] & 0xFFFFu)), bf16_rne(rv[2 * i + 1] - bf16_to_f32(ph[i] >> 16)));
-        }
-        const u32x4 AH{ph[0], ph[1], ph[2], ph[3]}, AL{pl[0], pl[1], pl[2], pl[3]};
-#pragma unroll
-        for (int cbk = 0; cbk < NWV; ++cbk) {
-          qacc[j][cbk] = mfma_bf16(AL, qk[cbk], qacc[j][cbk]);
-          qacc[j][cbk] = mfma_bf16(AH, qk[cbk], qacc[j][cbk]);
-        }
+      for (int cbk = 0; cbk < NWV; ++cbk) {
+        const int col = col0 + 16 * (CB * cbk + c) + l16;
+        const int rr = col < n_cols ? col / G : 0, hh = col < n_cols ? col % G : 0;
+        qcols[cbk] = p.q + (size_t(row0 + rr) * p.Hq + h * G + hh) * D;
       }
+      f32x4 qacc[CPW][NWV];
+#pragma unroll
+      for (int j = 0; j < CPW; ++j)
+#pragma unroll
+        for (int cbk = 0; cbk < NWV; ++cbk) qacc[j][cbk] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+      for (int kb = 0; kb < NKB; ++kb) {
+        u32x4 qk[NWV];  // B operands: the q slice kb of every column block
+#pragma unroll
+        for (int cbk = 0; cbk < NWV; ++cbk) qk[cbk] = *reinterpret_cast<const u32x4*>(qcols[cbk] + 32 * kb + 8 * quad);
+        for (int e = tid; e < 32 * D / 4; e += NTH)
+          *reinterpret_cast<f32x4*>(rs + 4 * e) = *reinterpret_cast<const f32x4*>(rk + size_t(32 * kb) * D + 4 * e);
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < CPW; ++j) {
+          const int cb = wave + NWV * j;
+          float rv[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) rv[i] = rs[(8 * quad + i) * D + 16 * cb + l16];
+          uint32_t ph[4], pl[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            ph[i] = pack2(bf16_rne(rv[2 * i]), bf16_rne(rv[2 * i + 1]));
+            pl[i] = pack2(bf16_rne(rv[2 * i] - bf16_to_f32(ph[i] & 0xFFFFu)), bf16_rne(rv[2 * i + 1] - bf16_to_f32(ph[i] >> 16)));
+          }
+          const u32x4 AH{ph[0], ph[1], ph[2], ph[3]}, AL{pl[0], pl[1], pl[2], pl[3]};
+#pragma unroll
+          for (int cbk = 0; cbk < NWV; ++cbk) {
+            qacc[j][cbk] = mfma_bf16(AL, qk[cbk], qacc[j][cbk]);
+            qacc[j][cbk] = mfma_bf16(AH, qk[cbk], qacc[j][cbk]);
+          }
+        }
+        lds_barrier();
+      }
+      // qacc[j][cbk][r] = q~[column block (CB cbk + c), column l16][channel 16 (wave + NWV j) + 4 quad + r]
+#pragma unroll
+      for (int j = 0; j < CPW; ++j)
+#pragma unroll
+        for (int cbk = 0; cbk < NWV; ++cbk)
+          *reinterpret_cast<f32x4*>(fbuf + (16 * cbk + l16) * D + 16 * (wave + NWV * j) + 4 * quad) = qacc[j][cbk] * qscale;
       lds_barrier();
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const float* src = fbuf + (16 * wave + l16) * D + 32 * kb + 8 * quad;
+        bq[c][kb] = u32x4{f16pair(src[0], src[1]), f16pair(src[2], src[3]), f16pair(src[4], src[5]), f16pair(src[6], src[7])};
+      }
+      lds_barrier();  // fbuf and the tiles are reused
     }
-    // qacc[j][cbk][r] = q~[column 16 cbk + l16][channel 16 (wave + NWV j) + 4 quad + r]
-#pragma unroll
-    for (int j = 0; j < CPW; ++j)
-#pragma unroll
-      for (int cbk = 0; cbk < NWV; ++cbk)
-        *reinterpret_cast<f32x4*>(fbuf + (16 * cbk + l16) * D + 16 * (wave + NWV * j) + 4 * quad) = qacc[j][cbk] * qscale;
-    lds_barrier();
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const float* src = fbuf + (16 * wave + l16) * D + 32 * kb + 8 * quad;
-      bq_rot[kb] = u32x4{f16pair(src[0], src[1]), f16pair(src[2], src[3]), f16pair(src[4], src[5]), f16pair(src[6], src[7])};
-    }
-    lds_barrier();  // fbuf is reused at the end
+  } else {
+    load_raw_q();
   }
 
-  float m_run = kNegInfA, l_part = 0.f;
-  f32x4 acc_rot[NCB], acc_raw[NCB];
+  float m_run[CB], l_part[CB];
+  f32x4 acc[CB][NCB];
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) {
-    acc_rot[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc_raw[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < CB; ++c) {
+    m_run[c] = kNegInfA;
+    l_part[c] = 0.f;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) acc[c][cb] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  bool rotated = has_q;  // the accumulators hold rotated-basis value sums
 
-  // products and online softmax of one step over the tile
-  // full: a quantized step whose 32 tokens all lie in the middle region (no
+  // products and online softmax of one step over the tile.  full: a
+  // quantized step whose 32 tokens all lie in the middle region (no
   // per-token masks; columns past the unit's last carry finite values that
   // are never written)
   auto compute = [&](const uint16_t* tile, const StepInfo& si, const bool full) __attribute__((always_inline)) {
     const bool quantized = si.kind == 1;
-    f32x4 sc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    f32x4 sc[CB][2];
+#pragma unroll
+    for (int c = 0; c < CB; ++c) sc[c][0] = sc[c][1] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
         const u32x4 a = *reinterpret_cast<const u32x4*>(tile + (16 * j + l16) * T::KROW + 32 * kb + 8 * quad);
-        sc[j] = quantized ? mfma_f16(a, bq_rot[kb], sc[j]) : mfma_bf16(a, bq_raw[kb], sc[j]);
+#pragma unroll
+        for (int c = 0; c < CB; ++c)
+          sc[c][j] = quantized ? mfma_f16(a, bq[c][kb], sc[c][j]) : mfma_bf16(a, bq[c][kb], sc[c][j]);
       }
-    // logits of tokens 16 j + 4 quad + r for column l16 (log2 units), masked
-    float lg[2][4];
-    float mx = kNegInfA;
-    if (full) {
+    // logits of tokens 16 j + 4 quad + r for column l16 of block c (log2 units), masked
+    u32x4 bph[CB], bpl[CB];
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {
+      float lg[2][4];
+      float mx = kNegInfA;
+      if (full) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            lg[j][r] = sc[c][j][r];
+            mx = fmaxf(mx, lg[j][r]);
+          }
+      } else {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int tk = 16 * j + 4 * quad + r;
+            bool ok = col_ok[c];
+            if (si.kind == 0) {
+              const int li = si.i0 + j;
+              ok = ok && li < rg.n_raw && raw_token(rg, 16 * rg.raw_page(li) + (tk & 15));
+            } else if (quantized) {
+              const int pg = rg.q0 + si.i0 + j, pos = 16 * pg + (tk & 15);
+              ok = ok && pg < rg.q1 && pos >= rg.m0 && pos < rg.m1;
+            } else {
+              const int i = si.i0 + tk;  // new row index
+              ok = ok && i < n_rows && P + i <= qpos[c];
+            }
+            lg[j][r] = ok ? (quantized ? sc[c][j][r] : sc[c][j][r] * qscale) : kNegInfA;
+            mx = fmaxf(mx, lg[j][r]);
+          }
+      }
+      mx = wave_max16(mx);
+      // lazy rescale: the reference max moves only when a logit exceeds it by
+      // more than kSlackA (probabilities stay <= 2^kSlackA, exact enough in f16)
+      if (__any(mx > m_run[c] + kSlackA)) {
+        const float m_new = fmaxf(m_run[c], mx);
+        const float f = (m_run[c] == kNegInfA) ? 0.f : exp2f(m_run[c] - m_new);
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) acc[c][cb] *= f;
+        l_part[c] *= f;
+        m_run[c] = m_new;
+      }
+      const float m_use = (m_run[c] == kNegInfA) ? 0.f : m_run[c];
+      float pv[2][4];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-          lg[j][r] = sc[j][r];
-          mx = fmaxf(mx, lg[j][r]);
+          pv[j][r] = __builtin_amdgcn_exp2f(lg[j][r] - m_use);
+          l_part[c] += pv[j][r];
         }
-    } else {
+      if (quantized) {
+        bph[c] = u32x4{f16pair(pv[0][0], pv[0][1]), f16pair(pv[0][2], pv[0][3]), f16pair(pv[1][0], pv[1][1]),
+                       f16pair(pv[1][2], pv[1][3])};
+      } else {
+        uint32_t ph[4], pl[4];
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int tk = 16 * j + 4 * quad + r;
-        bool ok = col_ok;
-        if (si.kind == 0) {
-          const int li = si.i0 + j;
-          ok = ok && li < rg.n_raw && raw_token(rg, 16 * rg.raw_page(li) + (tk & 15));
-        } else if (quantized) {
-          const int pg = rg.q0 + si.i0 + j, pos = 16 * pg + (tk & 15);
-          ok = ok && pg < rg.q1 && pos >= rg.m0 && pos < rg.m1;
-        } else {
-          const int i = si.i0 + tk;  // new row index
-          ok = ok && i < n_rows && P + i <= qpos;
+        for (int i = 0; i < 4; ++i) {
+          const float a = pv[i >> 1][2 * (i & 1)], e = pv[i >> 1][2 * (i & 1) + 1];
+          ph[i] = pack2(bf16_rne(a), bf16_rne(e));
+          pl[i] = pack2(bf16_rne(a - bf16_to_f32(ph[i] & 0xFFFFu)), bf16_rne(e - bf16_to_f32(ph[i] >> 16)));
         }
-        lg[j][r] = ok ? (quantized ? sc[j][r] : sc[j][r] * qscale) : kNegInfA;
-        mx = fmaxf(mx, lg[j][r]);
+        bph[c] = u32x4{ph[0], ph[1], ph[2], ph[3]};
+        bpl[c] = u32x4{pl[0], pl[1], pl[2], pl[3]};
       }
     }
-    mx = wave_max16(mx);
-    // lazy rescale: the reference max moves only when a logit exceeds it by
-    // more than kSlackA (probabilities stay <= 2^kSlackA, exact enough in f16)
-    if (__any(mx > m_run + kSlackA)) {
-      const float m_new = fmaxf(m_run, mx);
-      const float f = (m_run == kNegInfA) ? 0.f : exp2f(m_run - m_new);
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        acc_rot[cb] *= f;
-        acc_raw[cb] *= f;
-      }
-      l_part *= f;
-      m_run = m_new;
-    }
-    const float m_use = (m_run == kNegInfA) ? 0.f : m_run;
-    float pv[2][4];
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        pv[j][r] = __builtin_amdgcn_exp2f(lg[j][r] - m_use);
-        l_part += pv[j][r];
-      }
     // values: A = V^T rows (channel 16 cb + l16), K-slot 4 j + r = token 16 j + 4 quad + r
     const uint16_t* vt = tile + 32 * T::KROW;
-    if (quantized) {
-      const u32x4 bp = {f16pair(pv[0][0], pv[0][1]), f16pair(pv[0][2], pv[0][3]), f16pair(pv[1][0], pv[1][1]),
-                        f16pair(pv[1][2], pv[1][3])};
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const uint16_t* vr = vt + (16 * cb + l16) * T::VROW + 4 * quad;
-        const u32x2 a0 = *reinterpret_cast<const u32x2*>(vr), a1 = *reinterpret_cast<const u32x2*>(vr + 16);
-        acc_rot[cb] = mfma_f16(u32x4{a0[0], a0[1], a1[0], a1[1]}, bp, acc_rot[cb]);
-      }
-    } else {
-      uint32_t ph[4], pl[4];
+    for (int cb = 0; cb < NCB; ++cb) {
+      const uint16_t* vr = vt + (16 * cb + l16) * T::VROW + 4 * quad;
+      const u32x2 a0 = *reinterpret_cast<const u32x2*>(vr), a1 = *reinterpret_cast<const u32x2*>(vr + 16);
+      const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float a = pv[i >> 1][2 * (i & 1)], c = pv[i >> 1][2 * (i & 1) + 1];
-        ph[i] = pack2(bf16_rne(a), bf16_rne(c));
-        pl[i] = pack2(bf16_rne(a - bf16_to_f32(ph[i] & 0xFFFFu)), bf16_rne(c - bf16_to_f32(ph[i] >> 16)));
-      }
-      const u32x4 bph = {ph[0], ph[1], ph[2], ph[3]}, bpl = {pl[0], pl[1], pl[2], pl[3]};
-#pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const uint16_t* vr = vt + (16 * cb + l16) * T::VROW + 4 * quad;
-        const u32x2 a0 = *reinterpret_cast<const u32x2*>(vr), a1 = *reinterpret_cast<const u32x2*>(vr + 16);
-        const u32x4 a = {a0[0], a0[1], a1[0], a1[1]};
-        acc_raw[cb] = mfma_bf16(a, bpl, acc_raw[cb]);
-        acc_raw[cb] = mfma_bf16(a, bph, acc_raw[cb]);
+      for (int c = 0; c < CB; ++c) {
+        if (quantized) {
+          acc[c][cb] = mfma_f16(a, bph[c], acc[c][cb]);
+        } else {
+          acc[c][cb] = mfma_bf16(a, bpl[c], acc[c][cb]);
+          acc[c][cb] = mfma_bf16(a, bph[c], acc[c][cb]);
+        }
       }
     }
   };
-  auto tile_of = [&](int s) { return tiles + (NBUF == 2 ? (s & 1) : 0) * T::ELEMS; };
-  // raw steps (BF16 pages, new rows): few per unit, loaded when stored
-  auto raw_step = [&](int s, const StepInfo& si) {
-    uint16_t* tile = tile_of(s);
-    step_store<D, BITS, NTH>(p, rg, bth, h, row0, n_rows, si, stq[0], tile, tid);
-    lds_barrier();
-    compute(tile, si, false);
-    if (NBUF == 1) lds_barrier();
+  // rotated-basis value sums of block c -> model basis: acc^T[ch][n] = sum_k R_V[ch][k] rot[n][k]
+  // (R_V rows and rot split into bf16 hi + lo, three products per block)
+  float* wstage = fbuf + wave * 16 * D;
+  const float* rvh = p.r_v + size_t(h) * D * D;
+  auto rotate_back = [&]() {
+#pragma unroll
+    for (int c = 0; c < CB; ++c) {  // unrolled: acc[c] needs a constant index
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) *reinterpret_cast<f32x4*>(wstage + l16 * D + 16 * cb + 4 * quad) = acc[c][cb];
+      // the other lanes of the wave read these values: no LDS access may move
+      // across this point, and the writes complete first
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
+      asm volatile("" ::: "memory");
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          const f32x4 ra0 = *reinterpret_cast<const f32x4*>(rvh + size_t(16 * cb + l16) * D + 32 * kb + 8 * quad);
+          const f32x4 ra1 = *reinterpret_cast<const f32x4*>(rvh + size_t(16 * cb + l16) * D + 32 * kb + 8 * quad + 4);
+          const float* rb = wstage + l16 * D + 32 * kb + 8 * quad;
+          const float rav[8] = {ra0[0], ra0[1], ra0[2], ra0[3], ra1[0], ra1[1], ra1[2], ra1[3]};
+          uint32_t ah[4], al[4], bh[4], bl[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            ah[i] = pack2(bf16_rne(rav[2 * i]), bf16_rne(rav[2 * i + 1]));
+            al[i] = pack2(bf16_rne(rav[2 * i] - bf16_to_f32(ah[i] & 0xFFFFu)), bf16_rne(rav[2 * i + 1] - bf16_to_f32(ah[i] >> 16)));
+            bh[i] = pack2(bf16_rne(rb[2 * i]), bf16_rne(rb[2 * i + 1]));
+            bl[i] = pack2(bf16_rne(rb[2 * i] - bf16_to_f32(bh[i] & 0xFFFFu)), bf16_rne(rb[2 * i + 1] - bf16_to_f32(bh[i] >> 16)));
+          }
+          const u32x4 AH{ah[0], ah[1], ah[2], ah[3]}, AL{al[0], al[1], al[2], al[3]};
+          const u32x4 BH{bh[0], bh[1], bh[2], bh[3]}, BL{bl[0], bl[1], bl[2], bl[3]};
+          a4 = mfma_bf16(AL, BH, a4);
+          a4 = mfma_bf16(AH, BL, a4);
+          a4 = mfma_bf16(AH, BH, a4);
+        }
+        acc[c][cb] = a4;
+      }
+      // the next block's values overwrite the staging area only after every
+      // lane has read this block's
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      asm volatile("" ::: "memory");
+    }
+    rotated = false;
   };
-#pragma unroll 1
-  for (int s = s_begin; s < min(s_end, n_rp); ++s) {
-    StepInfo si;
-    si.kind = 0;
-    si.i0 = 2 * s;
-    raw_step(s, si);
-  }
+  auto tile_of = [&](int s) { return tiles + (NBUF == 2 ? (s & 1) : 0) * T::ELEMS; };
+
   // quantized steps: the loads of the next DEPTH steps stay in flight (every
   // step reloads its stage right after decoding it)
 #pragma unroll 1
@@ -666,38 +693,67 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
       }
     }
   }
+  // raw steps (BF16 pages, new rows): few per unit, loaded when stored
+  if (ra < s_end && rotated) {
+    rotate_back();
+    load_raw_q();
+  }
 #pragma unroll 1
-  for (int s = max(s_begin, n_rp + n_qp); s < s_end; ++s) {
+  for (int s = ra; s < s_end; ++s) {
     StepInfo si;
-    si.kind = 2;
-    si.i0 = 32 * (s - n_rp - n_qp);
-    raw_step(s, si);
+    if (s < n_qp + n_rp) {
+      si.kind = 0;
+      si.i0 = 2 * (s - n_qp);
+    } else {
+      si.kind = 2;
+      si.i0 = 32 * (s - n_qp - n_rp);
+    }
+    uint16_t* tile = tile_of(s);
+    step_store<D, BITS, NTH>(p, rg, bth, h, row0, n_rows, si, stq[0], tile, tid);
+    lds_barrier();
+    compute(tile, si, false);
+    if (NBUF == 1) lds_barrier();
   }
 
-  const float l_tot = wave_sum16(l_part);
   constexpr int RF = 2 + 2 * D;
   if (p.n_chunks > 1) {
-    // record of this chunk: [m][l][raw D][rot D] per column
-    // (columns past the unit's last are never merged: no record)
-    float* rec = p.rec + (((size_t(unit) * p.n_ct + ct) * p.n_chunks + chunk) * size_t(16 * NWV) + 16 * wave + l16) * RF;
-    if (!col_ok) return;
-    if (quad == 0) {
-      rec[0] = m_run;
-      rec[1] = l_tot;
-    }
+    // record of this chunk: [m][l][raw D][rot D] per column, the sums in the
+    // field of their basis and zeros in the other (columns past the unit's
+    // last are never merged: no record)
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
-      *reinterpret_cast<f32x4*>(rec + 2 + 16 * cb + 4 * quad) = acc_raw[cb];
-      *reinterpret_cast<f32x4*>(rec + 2 + D + 16 * cb + 4 * quad) = acc_rot[cb];
+    for (int c = 0; c < CB; ++c) {
+      const float l_tot = wave_sum16(l_part[c]);
+      if (!col_ok[c]) continue;
+      float* rec = p.rec + (((size_t(unit) * p.n_ct + ct) * p.n_chunks + chunk) * size_t(NC) + 16 * (CB * wave + c) + l16) * RF;
+      if (quad == 0) {
+        rec[0] = m_run[c];
+        rec[1] = l_tot;
+      }
+      const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        *reinterpret_cast<f32x4*>(rec + 2 + 16 * cb + 4 * quad) = rotated ? zero : acc[c][cb];
+        *reinterpret_cast<f32x4*>(rec + 2 + D + 16 * cb + 4 * quad) = rotated ? acc[c][cb] : zero;
+      }
     }
     return;
   }
-  // ---- single chunk: out = (raw + rot R_V^T) / l ----
-  float* rot = fbuf + wave * 16 * D;
+  // ---- single chunk: out = model-basis sums / l ----
+  if (rotated) rotate_back();
 #pragma unroll
-  for (int cb = 0; cb < NCB; ++cb) *reinterpret_cast<f32x4*>(rot + l16 * D + 16 * cb + 4 * quad) = acc_rot[cb];
-  finish_columns<D>(p.r_v + size_t(h) * D * D, rot, acc_raw, l_tot, col_ok,
-                    p.out + (size_t(row0 + ri) * p.Hq + h * G + hi) * D, l16, quad);
+  for (int c = 0; c < CB; ++c) {
+    const float l_tot = wave_sum16(l_part[c]);
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    if (!col_ok[c]) continue;
+    uint16_t* orow = p.out + (size_t(row0 + ri[c]) * p.Hq + h * G + hi[c]) * D;
+#pragma unroll
+    for (int cb = 0; cb < NCB; ++cb) {
+      u32x2 ov;
+      ov[0] = pack2(bf16_rne(acc[c][cb][0] * inv), bf16_rne(acc[c][cb][1] * inv));
+      ov[1] = pack2(bf16_rne(acc[c][cb][2] * inv), bf16_rne(acc[c][cb][3] * inv));
+      *reinterpret_cast<u32x2*>(orow + 16 * cb + 4 * quad) = ov;
+    }
+  }
 }
 
 // Log-sum-exp merge of the chunk records of one (unit, column tile), then
@@ -706,9 +762,9 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
 // 256 threads share a column: the chunks' maxima and weights, then one of
 // the 2d value sums each (eight chunks' loads in flight), then one output
 // channel each (float32 products with R_V's row).
-template <int D, int NWV, int MODE>
+template <int D, int NC, int MODE>
 __global__ __launch_bounds__(256) void attend_merge_kernel(AttParams p) {
-  constexpr int RF = 2 + 2 * D, NC = 16 * NWV, MT = 256;
+  constexpr int RF = 2 + 2 * D, MT = 256;
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   float* s_w = reinterpret_cast<float*>(lds);   // [n_chunks] weights of the current column
   float* s_v = s_w + p.n_chunks;                // [2 D] merged raw, rot
@@ -783,10 +839,12 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttParams p) {
 
 namespace oscar_launch {
 
-// Waves per workgroup: extend at d = 128 takes 8 waves (128 query columns), so
-// each decoded step feeds twice the products of a 4-wave workgroup; at d = 64
-// the query rotation's channel blocks (d/16 = 4) bound it to 4 waves.
+// Waves per workgroup and 16-column blocks per wave: extend at d = 128 takes 8
+// waves of 2 blocks (256 query columns), at d = 64 4 waves (the query
+// rotation's d/16 = 4 channel blocks are split over the waves) of 2 blocks;
+// the decode one wave of one block.
 int attend_waves(bool extend, int d) { return extend ? (d == 128 ? 8 : 4) : 1; }
+int attend_cols(bool extend, int d) { return 16 * attend_waves(extend, d) * (extend ? 2 : 1); }
 
 size_t attend_lds_bytes(int d, bool extend) {
   const int nwv = attend_waves(extend, d), nbuf = extend ? 2 : 1;
@@ -812,8 +870,10 @@ hipError_t paged_attend(int d, int bits, bool extend, const void* qpool, int n_q
   const size_t mlds = (size_t(n_chunks) + 2 * d + 8) * 4;
 #define OSCAR_ATTEND(DD, BB, NW, MM)                                                                        \
   do {                                                                                                      \
-    hipLaunchKernelGGL((attend_kernel<DD, BB, NW, MM>), grid, dim3(64 * NW), lds, stream, p);               \
-    if (n_chunks > 1) hipLaunchKernelGGL((attend_merge_kernel<DD, NW, MM>), mgrid, dim3(256), mlds, stream, p); \
+    constexpr int CB_ = MM == 0 ? 2 : 1;                                                                    \
+    hipLaunchKernelGGL((attend_kernel<DD, BB, NW, CB_, MM>), grid, dim3(64 * NW), lds, stream, p);          \
+    if (n_chunks > 1)                                                                                       \
+      hipLaunchKernelGGL((attend_merge_kernel<DD, 16 * NW * CB_, MM>), mgrid, dim3(256), mlds, stream, p);  \
   } while (0)
   if (d == 128) {
     if (extend) { if (bits == 2) OSCAR_ATTEND(128, 2, 8, 0); else OSCAR_ATTEND(128, 4, 8, 0); }

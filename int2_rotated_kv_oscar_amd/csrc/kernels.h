@@ -40,6 +40,7 @@ hipError_t paged_decode(int d, bool all_raw, const void* int2_pool, int n_int2_p
 // INT2/INT4 pages; otherwise decode over an INT4 cache), and its merge
 size_t attend_lds_bytes(int d, bool extend);
 int attend_waves(bool extend, int d);
+int attend_cols(bool extend, int d);
 hipError_t paged_attend(int d, int bits, bool extend, const void* qpool, int n_qpages, const void* bf16_pool,
                         int n_bpages, int n_kv, int G, int S, int W, int Hq, const void* q, const void* k_new,
                         const void* v_new, const int32_t* cu, const int32_t* clen, int batch, const int32_t* bt_q,
