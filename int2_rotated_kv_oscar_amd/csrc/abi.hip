@@ -408,6 +408,7 @@ oscar_status plan_attend(bool extend, int32_t batch, int32_t n_kv, int32_t n_q, 
   }
   const long long n_chunks = std::max(1LL, (steps + spc - 1) / spc);
   if (units * plan->n_ct * n_chunks > (1LL << 31) - 1) return fail(OSCAR_ERR_UNSUPPORTED, "grid too large; use a larger split_steps");
+  if (n_chunks > 8192) return fail(OSCAR_ERR_UNSUPPORTED, "more than 8192 chunks per unit; use a larger split_steps");
   plan->spc = int(std::min<long long>(spc, 1 << 30));
   plan->n_chunks = int(n_chunks);
   plan->bytes = plan->n_chunks > 1 ? size_t(units) * plan->n_ct * plan->n_chunks * nct * (2 + 2 * size_t(d)) * 4 : 0;

@@ -205,9 +205,12 @@ __device__ __forceinline__ void step_load(const AttParams& p, const Regions& rg,
       const int j = e / WPP, wi = e % WPP;
       const int pg = min(rg.q0 + si.i0 + j, rg.q1 - 1);
       const uint8_t* base = p.qpool + (size_t(min(max(btq[pg], 0), p.n_qpages - 1)) * p.n_kv + h) * QG::BYTES;
-      const int m = wi / WPR, g = (8 * (wi % WPR)) / 32;
-      st.qw[it][0] = reinterpret_cast<const uint32_t*>(base + QG::KC)[wi];
-      st.qw[it][1] = reinterpret_cast<const uint32_t*>(base + QG::VC)[wi];
+      // token m = wi % 16 (consecutive lanes take consecutive tokens: the
+      // value tile's channel rows are then written contiguously), code word
+      // cw = wi / 16 (channels 8 cw .. 8 cw + 7)
+      const int m = wi % 16, cw = wi / 16, g = (8 * cw) / 32;
+      st.qw[it][0] = reinterpret_cast<const uint32_t*>(base + QG::KC)[m * WPR + cw];
+      st.qw[it][1] = reinterpret_cast<const uint32_t*>(base + QG::VC)[m * WPR + cw];
       st.qw[it][2] = reinterpret_cast<const uint16_t*>(base + QG::KS)[m * NG + g];
       st.qw[it][3] = reinterpret_cast<const uint16_t*>(base + QG::KZ)[m * NG + g];
       st.qw[it][4] = reinterpret_cast<const uint16_t*>(base + QG::VS)[m * NG + g];
@@ -312,7 +315,7 @@ __device__ __forceinline__ void step_store(const AttParams& p, const Regions& rg
       if (e >= 2 * WPP) break;
       const int j = e / WPP, wi = e % WPP;
       const int pg = rg.q0 + si.i0 + j;
-      const int m = wi / WPR, c0 = 8 * (wi % WPR);
+      const int m = wi % 16, c0 = 8 * (wi / 16);  // as in step_load
       const int pos = 16 * pg + m;
       const bool ok = pg < rg.q1 && pos >= rg.m0 && pos < rg.m1;
       const uint32_t kw = st.qw[it][0], vw = st.qw[it][1];
@@ -367,7 +370,10 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
   using T = Tile<D>;
   constexpr int NCB = D / 16, NKB = D / 32, NTH = 64 * NWV;
   constexpr int NBUF = NWV > 1 ? 2 : 1;
-  constexpr int NC = 16 * NWV * CB;  // columns of a tile
+  // waves that own columns: every wave for extend; for the decode (at most
+  // 16 query heads per KV head) wave 0, the others decode steps only
+  constexpr int NCW = MODE == 1 ? 1 : NWV;
+  constexpr int NC = 16 * NCW * CB;  // columns of a tile
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   uint16_t* tiles = lds;                                               // [NBUF][T::ELEMS]
   float* fbuf = reinterpret_cast<float*>(lds + NBUF * T::ELEMS);       // [NWV][16][D] per-wave staging
@@ -395,12 +401,13 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
 #pragma unroll
   for (int c = 0; c < CB; ++c) {
     const int col = col0 + 16 * (CB * wave + c) + l16;
-    col_ok[c] = col < n_cols;
+    col_ok[c] = wave < NCW && col < n_cols;
     ri[c] = col_ok[c] ? col / G : 0;
     hi[c] = col_ok[c] ? col % G : 0;
     qpos[c] = MODE == 0 ? P + ri[c] : P - 1;       // the column's query position
   }
   const int last_row = min(n_rows, (col0 + NC + G - 1) / G) - 1;  // last row with a column in the tile
+  const bool wave_cols = wave < NCW && col0 + 16 * CB * wave < n_cols;  // this wave has columns (uniform)
   auto qrow_of = [&](int c) { return p.q + (size_t(row0 + ri[c]) * p.Hq + h * G + hi[c]) * D; };
   const float qscale = p.sm_scale * kLog2e;
 
@@ -416,7 +423,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
   // the chunk's quantized steps [qa, qb) and raw steps [ra, s_end) (global step numbers)
   const int qa = s_begin, qb = min(s_end, n_qp), ra = max(s_begin, n_qp);
   const bool has_q = qa < qb;
-  constexpr int DEPTH = NWV > 1 ? 2 : 1;  // quantized steps whose loads are in flight
+  constexpr int DEPTH = 2;  // quantized steps whose loads are in flight
   Stage<D, BITS, NTH> stq[DEPTH];
   auto qinfo = [&](int s) {  // steps past the chunk load a valid pair of it, never used
     StepInfo si;
@@ -524,6 +531,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
   // per-token masks; columns past the unit's last carry finite values that
   // are never written)
   auto compute = [&](const uint16_t* tile, const StepInfo& si, const bool full) __attribute__((always_inline)) {
+    if (!wave_cols) return;  // a wave without columns only decodes steps
     const bool quantized = si.kind == 1;
     f32x4 sc[CB][2];
 #pragma unroll
@@ -630,6 +638,8 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
   float* wstage = fbuf + wave * 16 * D;
   const float* rvh = p.r_v + size_t(h) * D * D;
   auto rotate_back = [&]() {
+    rotated = false;
+    if (!wave_cols) return;
 #pragma unroll
     for (int c = 0; c < CB; ++c) {  // unrolled: acc[c] needs a constant index
 #pragma unroll
@@ -670,7 +680,6 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
       __builtin_amdgcn_s_waitcnt(0xC07F);
       asm volatile("" ::: "memory");
     }
-    rotated = false;
   };
   auto tile_of = [&](int s) { return tiles + (NBUF == 2 ? (s & 1) : 0) * T::ELEMS; };
 
@@ -757,19 +766,18 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
 }
 
 // Log-sum-exp merge of the chunk records of one (unit, column tile), then
-// the output rotation, column by column: M = max_k m_k, w_k = 2^(m_k - M),
-// out = (sum_k w_k raw_k + (sum_k w_k rot_k) R_V^T) / sum_k w_k l_k.  All
-// 256 threads share a column: the chunks' maxima and weights, then one of
-// the 2d value sums each (eight chunks' loads in flight), then one output
-// channel each (float32 products with R_V's row).
+// the output rotation, one column per wave: M = max_k m_k, w_k = 2^(m_k - M),
+// out = (sum_k w_k raw_k + (sum_k w_k rot_k) R_V^T) / sum_k w_k l_k.  A
+// lane holds four of the 2d value sums (sixteen chunks' loads in flight),
+// then two output channels (float32 products with R_V's rows).
 template <int D, int NC, int MODE>
 __global__ __launch_bounds__(256) void attend_merge_kernel(AttParams p) {
-  constexpr int RF = 2 + 2 * D, MT = 256;
+  constexpr int RF = 2 + 2 * D, NWM = 4, FPL = 2 * D / 64;  // waves, value floats per lane
+  static_assert(FPL == 4 || FPL == 2, "d = 64 or 128");
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
-  float* s_w = reinterpret_cast<float*>(lds);   // [n_chunks] weights of the current column
-  float* s_v = s_w + p.n_chunks;                // [2 D] merged raw, rot
-  float* s_red = s_v + 2 * D;                   // [8] partial reductions
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  float* s_w = reinterpret_cast<float*>(lds) + wave * (p.n_chunks + 2 * D);  // [n_chunks] weights of this wave's column
+  float* s_v = s_w + p.n_chunks;                                               // [2 D] merged raw, rot
   const int G = p.G;
   const int ct = blockIdx.x % p.n_ct, unit = blockIdx.x / p.n_ct;
   const UnitRows u = unit_rows<MODE>(p, unit);
@@ -778,60 +786,69 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttParams p) {
   if (col0 >= n_cols) return;
   const size_t cstride = size_t(NC) * RF;
   const float* rv = p.r_v + size_t(u.h) * D * D;
-  for (int cl = 0; cl < NC && col0 + cl < n_cols; ++cl) {
+  const int nk = p.n_chunks;
+  for (int cl = wave; cl < NC && col0 + cl < n_cols; cl += NWM) {
     const int col = col0 + cl, ri = col / G, hi = col % G;
-    const float* rec0 = p.rec + ((size_t(unit) * p.n_ct + ct) * p.n_chunks * NC + cl) * RF;
-    // maximum over the chunks
+    const float* rec0 = p.rec + ((size_t(unit) * p.n_ct + ct) * nk * NC + cl) * RF;
     float mx = kNegInfA;
-    for (int k = tid; k < p.n_chunks; k += MT) mx = fmaxf(mx, rec0[k * cstride]);
+    for (int k = lane; k < nk; k += 64) mx = fmaxf(mx, rec0[k * cstride]);
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-    if (lane == 0) s_red[wave] = mx;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-    __syncthreads();
     float l = 0.f;
-    for (int k = tid; k < p.n_chunks; k += MT) {
+    for (int k = lane; k < nk; k += 64) {
       const float mk = rec0[k * cstride];
-      const float w = mk == kNegInfA ? 0.f : exp2f(mk - M);
+      const float w = mk == kNegInfA ? 0.f : exp2f(mk - mx);
       s_w[k] = w;
       l = __builtin_fmaf(w, rec0[k * cstride + 1], l);
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
-    if (lane == 0) s_red[4 + wave] = l;
-    __syncthreads();
-    const float L = (s_red[4] + s_red[5]) + (s_red[6] + s_red[7]);
-    // value sums: thread f < 2D sums float f over the chunks
-    for (int f = tid; f < 2 * D; f += MT) {
-      float a = 0.f;
-      int k = 0;
-      for (; k + 8 <= p.n_chunks; k += 8) {
-        float v[8];
+    // the weights written by other lanes are read below (wave-local LDS)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    asm volatile("" ::: "memory");
+    float a[FPL];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) v[t] = rec0[(k + t) * cstride + 2 + f];
+    for (int f = 0; f < FPL; ++f) a[f] = 0.f;
+    const float* vb = rec0 + 2 + FPL * lane;
+    int k = 0;
+    for (; k + 16 <= nk; k += 16) {
+      float v[16][FPL];
 #pragma unroll
-        for (int t = 0; t < 8; ++t) a = __builtin_fmaf(s_w[k + t], v[t], a);
-      }
-      for (; k < p.n_chunks; ++k) a = __builtin_fmaf(s_w[k], rec0[k * cstride + 2 + f], a);
-      s_v[f] = a;
+      for (int t = 0; t < 16; ++t)
+#pragma unroll
+        for (int f = 0; f < FPL; ++f) v[t][f] = vb[(k + t) * cstride + f];
+#pragma unroll
+      for (int t = 0; t < 16; ++t)
+#pragma unroll
+        for (int f = 0; f < FPL; ++f) a[f] = __builtin_fmaf(s_w[k + t], v[t][f], a[f]);
     }
-    __syncthreads();
-    // out[c] = (raw[c] + sum_k rot[k] R_V[c][k]) / L
-    if (tid < D) {
-      const float* rrow = rv + size_t(tid) * D;
-      float a = s_v[tid];
+    for (; k < nk; ++k)
+#pragma unroll
+      for (int f = 0; f < FPL; ++f) a[f] = __builtin_fmaf(s_w[k], vb[k * cstride + f], a[f]);
+#pragma unroll
+    for (int f = 0; f < FPL; ++f) s_v[FPL * lane + f] = a[f];
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    asm volatile("" ::: "memory");
+    // out[c] = (raw[c] + sum_k rot[k] R_V[c][k]) / L, channels c = lane, lane + 64
+    for (int c = lane; c < D; c += 64) {
+      const float* rrow = rv + size_t(c) * D;
+      float o = s_v[c];
 #pragma unroll 4
-      for (int k = 0; k < D; k += 4) {
-        const f32x4 r4 = *reinterpret_cast<const f32x4*>(rrow + k);
-        a = __builtin_fmaf(s_v[D + k], r4[0], a);
-        a = __builtin_fmaf(s_v[D + k + 1], r4[1], a);
-        a = __builtin_fmaf(s_v[D + k + 2], r4[2], a);
-        a = __builtin_fmaf(s_v[D + k + 3], r4[3], a);
+      for (int kk = 0; kk < D; kk += 4) {
+        const f32x4 r4 = *reinterpret_cast<const f32x4*>(rrow + kk);
+        o = __builtin_fmaf(s_v[D + kk], r4[0], o);
+        o = __builtin_fmaf(s_v[D + kk + 1], r4[1], o);
+        o = __builtin_fmaf(s_v[D + kk + 2], r4[2], o);
+        o = __builtin_fmaf(s_v[D + kk + 3], r4[3], o);
       }
-      p.out[(size_t(u.row0 + ri) * p.Hq + u.h * G + hi) * D + tid] = uint16_t(bf16_rne(L > 0.f ? a / L : 0.f));
+      p.out[(size_t(u.row0 + ri) * p.Hq + u.h * G + hi) * D + c] = uint16_t(bf16_rne(l > 0.f ? o / l : 0.f));
     }
-    __syncthreads();
+    // the next column's weights and sums overwrite this wave's areas after every lane read them
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    asm volatile("" ::: "memory");
   }
 }
 
@@ -842,12 +859,13 @@ namespace oscar_launch {
 // Waves per workgroup and 16-column blocks per wave: extend at d = 128 takes 8
 // waves of 2 blocks (256 query columns), at d = 64 4 waves (the query
 // rotation's d/16 = 4 channel blocks are split over the waves) of 2 blocks;
-// the decode one wave of one block.
-int attend_waves(bool extend, int d) { return extend ? (d == 128 ? 8 : 4) : 1; }
-int attend_cols(bool extend, int d) { return 16 * attend_waves(extend, d) * (extend ? 2 : 1); }
+// the decode 4 waves that share each step's decoding, one of them holding
+// the 16 columns.
+int attend_waves(bool extend, int d) { return extend ? (d == 128 ? 8 : 4) : 4; }
+int attend_cols(bool extend, int d) { return extend ? 16 * attend_waves(extend, d) * 2 : 16; }
 
 size_t attend_lds_bytes(int d, bool extend) {
-  const int nwv = attend_waves(extend, d), nbuf = extend ? 2 : 1;
+  const int nwv = attend_waves(extend, d), nbuf = nwv > 1 ? 2 : 1;
   const size_t elems = d == 128 ? Tile<128>::ELEMS : Tile<64>::ELEMS;
   return size_t(nbuf) * elems * 2 + size_t(nwv) * 16 * d * 4;
 }
@@ -867,20 +885,20 @@ hipError_t paged_attend(int d, int bits, bool extend, const void* qpool, int n_q
   const dim3 grid(units * unsigned(n_ct) * unsigned(n_chunks));
   const dim3 mgrid(units * unsigned(n_ct));
   const size_t lds = attend_lds_bytes(d, extend);
-  const size_t mlds = (size_t(n_chunks) + 2 * d + 8) * 4;
+  const size_t mlds = 4 * (size_t(n_chunks) + 2 * d) * 4;
 #define OSCAR_ATTEND(DD, BB, NW, MM)                                                                        \
   do {                                                                                                      \
     constexpr int CB_ = MM == 0 ? 2 : 1;                                                                    \
     hipLaunchKernelGGL((attend_kernel<DD, BB, NW, CB_, MM>), grid, dim3(64 * NW), lds, stream, p);          \
     if (n_chunks > 1)                                                                                       \
-      hipLaunchKernelGGL((attend_merge_kernel<DD, 16 * NW * CB_, MM>), mgrid, dim3(256), mlds, stream, p);  \
+      hipLaunchKernelGGL((attend_merge_kernel<DD, MM == 0 ? 16 * NW * CB_ : 16, MM>), mgrid, dim3(256), mlds, stream, p); \
   } while (0)
   if (d == 128) {
     if (extend) { if (bits == 2) OSCAR_ATTEND(128, 2, 8, 0); else OSCAR_ATTEND(128, 4, 8, 0); }
-    else { if (bits == 2) OSCAR_ATTEND(128, 2, 1, 1); else OSCAR_ATTEND(128, 4, 1, 1); }
+    else { if (bits == 2) OSCAR_ATTEND(128, 2, 4, 1); else OSCAR_ATTEND(128, 4, 4, 1); }
   } else {
     if (extend) { if (bits == 2) OSCAR_ATTEND(64, 2, 4, 0); else OSCAR_ATTEND(64, 4, 4, 0); }
-    else { if (bits == 2) OSCAR_ATTEND(64, 2, 1, 1); else OSCAR_ATTEND(64, 4, 1, 1); }
+    else { if (bits == 2) OSCAR_ATTEND(64, 2, 4, 1); else OSCAR_ATTEND(64, 4, 4, 1); }
   }
 #undef OSCAR_ATTEND
   return hipGetLastError();
