@@ -456,23 +456,23 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
     const float* rk = p.r_k + size_t(h) * D * D;
 #pragma unroll
     for (int c = 0; c < CB; ++c) {  // unrolled: bq[c] needs a constant index
-      const uint16_t* qcols[NWV];  // the q rows of the round's column blocks (lane l16's column)
+      const uint16_t* qcols[NCW];  // the q rows of the round's column blocks (lane l16's column)
 #pragma unroll
-      for (int cbk = 0; cbk < NWV; ++cbk) {
+      for (int cbk = 0; cbk < NCW; ++cbk) {
         const int col = col0 + 16 * (CB * cbk + c) + l16;
         const int rr = col < n_cols ? col / G : 0, hh = col < n_cols ? col % G : 0;
         qcols[cbk] = p.q + (size_t(row0 + rr) * p.Hq + h * G + hh) * D;
       }
-      f32x4 qacc[CPW][NWV];
+      f32x4 qacc[CPW][NCW];
 #pragma unroll
       for (int j = 0; j < CPW; ++j)
 #pragma unroll
-        for (int cbk = 0; cbk < NWV; ++cbk) qacc[j][cbk] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int cbk = 0; cbk < NCW; ++cbk) qacc[j][cbk] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
       for (int kb = 0; kb < NKB; ++kb) {
-        u32x4 qk[NWV];  // B operands: the q slice kb of every column block
+        u32x4 qk[NCW];  // B operands: the q slice kb of every column block
 #pragma unroll
-        for (int cbk = 0; cbk < NWV; ++cbk) qk[cbk] = *reinterpret_cast<const u32x4*>(qcols[cbk] + 32 * kb + 8 * quad);
+        for (int cbk = 0; cbk < NCW; ++cbk) qk[cbk] = *reinterpret_cast<const u32x4*>(qcols[cbk] + 32 * kb + 8 * quad);
         for (int e = tid; e < 32 * D / 4; e += NTH)
           *reinterpret_cast<f32x4*>(rs + 4 * e) = *reinterpret_cast<const f32x4*>(rk + size_t(32 * kb) * D + 4 * e);
         __syncthreads();
@@ -490,7 +490,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
           }
           const u32x4 AH{ph[0], ph[1], ph[2], ph[3]}, AL{pl[0], pl[1], pl[2], pl[3]};
 #pragma unroll
-          for (int cbk = 0; cbk < NWV; ++cbk) {
+          for (int cbk = 0; cbk < NCW; ++cbk) {
             qacc[j][cbk] = mfma_bf16(AL, qk[cbk], qacc[j][cbk]);
             qacc[j][cbk] = mfma_bf16(AH, qk[cbk], qacc[j][cbk]);
           }
@@ -501,7 +501,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
 #pragma unroll
       for (int j = 0; j < CPW; ++j)
 #pragma unroll
-        for (int cbk = 0; cbk < NWV; ++cbk)
+        for (int cbk = 0; cbk < NCW; ++cbk)
           *reinterpret_cast<f32x4*>(fbuf + (16 * cbk + l16) * D + 16 * (wave + NWV * j) + 4 * quad) = qacc[j][cbk] * qscale;
       lds_barrier();
 #pragma unroll
