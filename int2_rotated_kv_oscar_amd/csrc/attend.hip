@@ -454,6 +454,17 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
     static_assert(CPW >= 1 && NCB % NWV == 0, "channel blocks split over the waves");
     float* rs = reinterpret_cast<float*>(tiles);  // [32][D] rows of R_K
     const float* rk = p.r_k + size_t(h) * D * D;
+    // all of R_K requested at once (this thread's share of every 32-row
+    // slab), so the rounds below wait for memory once
+    constexpr int RPT = (32 * D / 4 + NTH - 1) / NTH;  // f32x4 per thread per slab
+    f32x4 rkr[NKB][RPT];
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+      for (int i = 0; i < RPT; ++i) {
+        const int e = min(tid + i * NTH, 32 * D / 4 - 1);
+        rkr[kb][i] = *reinterpret_cast<const f32x4*>(rk + size_t(32 * kb) * D + 4 * e);
+      }
 #pragma unroll
     for (int c = 0; c < CB; ++c) {  // unrolled: bq[c] needs a constant index
       const uint16_t* qcols[NCW];  // the q rows of the round's column blocks (lane l16's column)
@@ -468,13 +479,14 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
       for (int j = 0; j < CPW; ++j)
 #pragma unroll
         for (int cbk = 0; cbk < NCW; ++cbk) qacc[j][cbk] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-      for (int kb = 0; kb < NKB; ++kb) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {  // unrolled: rkr[kb] needs a constant index
         u32x4 qk[NCW];  // B operands: the q slice kb of every column block
 #pragma unroll
         for (int cbk = 0; cbk < NCW; ++cbk) qk[cbk] = *reinterpret_cast<const u32x4*>(qcols[cbk] + 32 * kb + 8 * quad);
-        for (int e = tid; e < 32 * D / 4; e += NTH)
-          *reinterpret_cast<f32x4*>(rs + 4 * e) = *reinterpret_cast<const f32x4*>(rk + size_t(32 * kb) * D + 4 * e);
+#pragma unroll
+        for (int i = 0; i < RPT; ++i)
+          if (tid + i * NTH < 32 * D / 4) *reinterpret_cast<f32x4*>(rs + 4 * (tid + i * NTH)) = rkr[kb][i];
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < CPW; ++j) {
