@@ -777,91 +777,94 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
   }
 }
 
-// Log-sum-exp merge of the chunk records of one (unit, column tile), then
-// the output rotation, one column per wave: M = max_k m_k, w_k = 2^(m_k - M),
-// out = (sum_k w_k raw_k + (sum_k w_k rot_k) R_V^T) / sum_k w_k l_k.  A
-// lane holds four of the 2d value sums (sixteen chunks' loads in flight),
-// then two output channels (float32 products with R_V's rows).
+// Log-sum-exp merge of the chunk records of one column, then the output
+// rotation: M = max_k m_k, w_k = 2^(m_k - M),
+// out = (sum_k w_k raw_k + (sum_k w_k rot_k) R_V^T) / sum_k w_k l_k.
+// One workgroup per (unit, column tile, column).  Its R_V entries (output
+// channel c = tid / TPC, a KPT-long run of k) are requested first, so they
+// arrive while the records are read; the four waves take every fourth chunk
+// (a lane holds FPL of the 2d value sums, sixteen chunks' loads in flight)
+// and meet in LDS.
 template <int D, int NC, int MODE>
 __global__ __launch_bounds__(256) void attend_merge_kernel(AttParams p) {
   constexpr int RF = 2 + 2 * D, NWM = 4, FPL = 2 * D / 64;  // waves, value floats per lane
+  constexpr int TPC = 256 / D, KPT = D / TPC;                // threads per output channel, R_V entries each
   static_assert(FPL == 4 || FPL == 2, "d = 64 or 128");
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
+  const int nk = p.n_chunks;
+  float* s_w = reinterpret_cast<float*>(lds);  // [n_chunks] weights
+  float* s_part = s_w + nk;                     // [NWM][2 D] per-wave value sums
+  float* s_v = s_part + NWM * 2 * D;            // [2 D] merged raw, rot
+  float* s_red = s_v + 2 * D;                   // [2 NWM] per-wave max, sum
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  float* s_w = reinterpret_cast<float*>(lds) + wave * (p.n_chunks + 2 * D);  // [n_chunks] weights of this wave's column
-  float* s_v = s_w + p.n_chunks;                                               // [2 D] merged raw, rot
-  const int G = p.G;
-  const int ct = blockIdx.x % p.n_ct, unit = blockIdx.x / p.n_ct;
+  const int cl = blockIdx.y, ct = blockIdx.x % p.n_ct, unit = blockIdx.x / p.n_ct;
   const UnitRows u = unit_rows<MODE>(p, unit);
   if (MODE == 1 && u.P <= 0) return;
-  const int col0 = ct * NC, n_cols = u.n_rows * G;
-  if (col0 >= n_cols) return;
+  const int G = p.G, col = ct * NC + cl;
+  if (col >= u.n_rows * G) return;
+  const int ri = col / G, hi = col % G;
   const size_t cstride = size_t(NC) * RF;
-  const float* rv = p.r_v + size_t(u.h) * D * D;
-  const int nk = p.n_chunks;
-  for (int cl = wave; cl < NC && col0 + cl < n_cols; cl += NWM) {
-    const int col = col0 + cl, ri = col / G, hi = col % G;
-    const float* rec0 = p.rec + ((size_t(unit) * p.n_ct + ct) * nk * NC + cl) * RF;
-    float mx = kNegInfA;
-    for (int k = lane; k < nk; k += 64) mx = fmaxf(mx, rec0[k * cstride]);
+  const float* rec0 = p.rec + ((size_t(unit) * p.n_ct + ct) * nk * NC + cl) * RF;
+  const int c = tid / TPC, k0 = KPT * (tid % TPC);
+  const float* rrow = p.r_v + size_t(u.h) * D * D + size_t(c) * D + k0;
+  f32x4 rr[KPT / 4];
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-    float l = 0.f;
-    for (int k = lane; k < nk; k += 64) {
-      const float mk = rec0[k * cstride];
-      const float w = mk == kNegInfA ? 0.f : exp2f(mk - mx);
-      s_w[k] = w;
-      l = __builtin_fmaf(w, rec0[k * cstride + 1], l);
-    }
+  for (int i = 0; i < KPT / 4; ++i) rr[i] = *reinterpret_cast<const f32x4*>(rrow + 4 * i);
+  float mx = kNegInfA;
+  for (int k = tid; k < nk; k += 256) mx = fmaxf(mx, rec0[k * cstride]);
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
-    // the weights written by other lanes are read below (wave-local LDS)
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    asm volatile("" ::: "memory");
-    float a[FPL];
-#pragma unroll
-    for (int f = 0; f < FPL; ++f) a[f] = 0.f;
-    const float* vb = rec0 + 2 + FPL * lane;
-    int k = 0;
-    for (; k + 16 <= nk; k += 16) {
-      float v[16][FPL];
-#pragma unroll
-      for (int t = 0; t < 16; ++t)
-#pragma unroll
-        for (int f = 0; f < FPL; ++f) v[t][f] = vb[(k + t) * cstride + f];
-#pragma unroll
-      for (int t = 0; t < 16; ++t)
-#pragma unroll
-        for (int f = 0; f < FPL; ++f) a[f] = __builtin_fmaf(s_w[k + t], v[t][f], a[f]);
-    }
-    for (; k < nk; ++k)
-#pragma unroll
-      for (int f = 0; f < FPL; ++f) a[f] = __builtin_fmaf(s_w[k], vb[k * cstride + f], a[f]);
-#pragma unroll
-    for (int f = 0; f < FPL; ++f) s_v[FPL * lane + f] = a[f];
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    asm volatile("" ::: "memory");
-    // out[c] = (raw[c] + sum_k rot[k] R_V[c][k]) / L, channels c = lane, lane + 64
-    for (int c = lane; c < D; c += 64) {
-      const float* rrow = rv + size_t(c) * D;
-      float o = s_v[c];
-#pragma unroll 4
-      for (int kk = 0; kk < D; kk += 4) {
-        const f32x4 r4 = *reinterpret_cast<const f32x4*>(rrow + kk);
-        o = __builtin_fmaf(s_v[D + kk], r4[0], o);
-        o = __builtin_fmaf(s_v[D + kk + 1], r4[1], o);
-        o = __builtin_fmaf(s_v[D + kk + 2], r4[2], o);
-        o = __builtin_fmaf(s_v[D + kk + 3], r4[3], o);
-      }
-      p.out[(size_t(u.row0 + ri) * p.Hq + u.h * G + hi) * D + c] = uint16_t(bf16_rne(l > 0.f ? o / l : 0.f));
-    }
-    // the next column's weights and sums overwrite this wave's areas after every lane read them
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);
-    asm volatile("" ::: "memory");
+  for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+  if (lane == 0) s_red[wave] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  float l = 0.f;
+  for (int k = tid; k < nk; k += 256) {
+    const float mk = rec0[k * cstride];
+    const float w = mk == kNegInfA ? 0.f : exp2f(mk - mx);
+    s_w[k] = w;
+    l = __builtin_fmaf(w, rec0[k * cstride + 1], l);
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) l += __shfl_xor(l, o, 64);
+  if (lane == 0) s_red[NWM + wave] = l;
+  __syncthreads();  // the weights and the sums are visible to every wave
+  l = (s_red[NWM] + s_red[NWM + 1]) + (s_red[NWM + 2] + s_red[NWM + 3]);
+  float a[FPL];
+#pragma unroll
+  for (int f = 0; f < FPL; ++f) a[f] = 0.f;
+  const float* vb = rec0 + 2 + FPL * lane;
+  int k = wave;
+  for (; k + NWM * 15 < nk; k += NWM * 16) {
+    float v[16][FPL];
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+#pragma unroll
+      for (int f = 0; f < FPL; ++f) v[t][f] = vb[(k + NWM * t) * cstride + f];
+#pragma unroll
+    for (int t = 0; t < 16; ++t)
+#pragma unroll
+      for (int f = 0; f < FPL; ++f) a[f] = __builtin_fmaf(s_w[k + NWM * t], v[t][f], a[f]);
+  }
+  for (; k < nk; k += NWM)
+#pragma unroll
+    for (int f = 0; f < FPL; ++f) a[f] = __builtin_fmaf(s_w[k], vb[k * cstride + f], a[f]);
+#pragma unroll
+  for (int f = 0; f < FPL; ++f) s_part[wave * 2 * D + FPL * lane + f] = a[f];
+  __syncthreads();
+  for (int j = tid; j < 2 * D; j += 256)
+    s_v[j] = (s_part[j] + s_part[2 * D + j]) + (s_part[4 * D + j] + s_part[6 * D + j]);
+  __syncthreads();
+  // out[c] = (raw[c] + sum_k rot[k] R_V[c][k]) / L: each thread a KPT-long
+  // run of k, the TPC runs of a channel summed over neighbouring lanes
+  float o = 0.f;
+#pragma unroll
+  for (int i = 0; i < KPT / 4; ++i)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o = __builtin_fmaf(s_v[D + k0 + 4 * i + e], rr[i][e], o);
+#pragma unroll
+  for (int m = 1; m < TPC; m <<= 1) o += __shfl_xor(o, m, 64);
+  if (tid % TPC == 0)
+    p.out[(size_t(u.row0 + ri) * p.Hq + u.h * G + hi) * D + c] = uint16_t(bf16_rne(l > 0.f ? (s_v[c] + o) / l : 0.f));
 }
 
 }  // namespace
@@ -895,9 +898,10 @@ hipError_t paged_attend(int d, int bits, bool extend, const void* qpool, int n_q
               max_pages, r_k, r_v, sm_scale, n_ct, n_chunks, spc, rec, static_cast<uint16_t*>(out)};
   const unsigned units = unsigned(batch) * unsigned(n_kv);
   const dim3 grid(units * unsigned(n_ct) * unsigned(n_chunks));
-  const dim3 mgrid(units * unsigned(n_ct));
+  const int ncols = extend ? attend_cols(true, d) : std::min(G, 16);  // merge workgroups per column tile
+  const dim3 mgrid(units * unsigned(n_ct), unsigned(ncols));
   const size_t lds = attend_lds_bytes(d, extend);
-  const size_t mlds = 4 * (size_t(n_chunks) + 2 * d) * 4;
+  const size_t mlds = (size_t(n_chunks) + 10 * size_t(d) + 8) * 4;
 #define OSCAR_ATTEND(DD, BB, NW, MM)                                                                        \
   do {                                                                                                      \
     constexpr int CB_ = MM == 0 ? 2 : 1;                                                                    \
