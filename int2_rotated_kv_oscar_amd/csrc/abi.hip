@@ -396,7 +396,8 @@ oscar_status plan_attend(bool extend, int32_t batch, int32_t n_kv, int32_t n_q, 
   plan->n_ct = int(std::max(1LL, (cols + nct - 1) / nct));
   const long long pages = (max_cache_len + 15LL) / 16;
   const long long raw = std::min(pages, (S + 15LL) / 16 + (W + 15LL) / 16 + 2);
-  const long long steps = (raw + 1) / 2 + (pages + 2) / 2 + (extend ? (max_new + 31LL) / 32 : 0);
+  const long long qsteps = (pages + 2) / 2, osteps = (raw + 1) / 2 + (extend ? (max_new + 31LL) / 32 : 0);
+  const long long steps = qsteps + osteps;
   const long long units = (long long)batch * n_kv;
   if (units * plan->n_ct > (1LL << 30)) return fail(OSCAR_ERR_UNSUPPORTED, "grid too large; split the batch");
   long long spc = split_steps;
@@ -406,7 +407,8 @@ oscar_status plan_attend(bool extend, int32_t batch, int32_t n_kv, int32_t n_q, 
     const long long chunks = std::max(1LL, (target + base - 1) / base);
     spc = std::max(extend ? 8LL : 16LL, (steps + chunks - 1) / chunks);
   }
-  const long long n_chunks = std::max(1LL, (steps + spc - 1) / spc);
+  // several chunks: quantized steps and the others in chunks of their own
+  const long long n_chunks = steps <= spc ? 1 : (qsteps + spc - 1) / spc + (osteps + spc - 1) / spc;
   if (units * plan->n_ct * n_chunks > (1LL << 31) - 1) return fail(OSCAR_ERR_UNSUPPORTED, "grid too large; use a larger split_steps");
   if (n_chunks > 8192) return fail(OSCAR_ERR_UNSUPPORTED, "more than 8192 chunks per unit; use a larger split_steps");
   plan->spc = int(std::min<long long>(spc, 1 << 30));

@@ -419,7 +419,15 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
   const int n_qp = (rg.q1 - rg.q0 + 1) >> 1;
   const int n_nt = MODE == 0 ? (last_row + 1 + 31) / 32 : 0;
   const int total = n_qp + n_rp + n_nt;
-  const int s_begin = chunk * p.spc, s_end = min(total, s_begin + p.spc);
+  // one chunk: every step; several: the quantized steps in chunks of spc,
+  // then the raw steps in chunks of their own (no chunk mixes the bases, and
+  // the raw steps, loaded without prefetch, run beside the quantized chunks)
+  const int nqc = (n_qp + p.spc - 1) / p.spc;
+  int s_begin = 0, s_end = total;
+  if (p.n_chunks > 1) {
+    s_begin = chunk < nqc ? chunk * p.spc : n_qp + (chunk - nqc) * p.spc;
+    s_end = min(chunk < nqc ? n_qp : total, s_begin + p.spc);
+  }
   // the chunk's quantized steps [qa, qb) and raw steps [ra, s_end) (global step numbers)
   const int qa = s_begin, qb = min(s_end, n_qp), ra = max(s_begin, n_qp);
   const bool has_q = qa < qb;
