@@ -376,7 +376,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
   constexpr int NC = 16 * NCW * CB;  // columns of a tile
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
   uint16_t* tiles = lds;                                               // [NBUF][T::ELEMS]
-  float* fbuf = reinterpret_cast<float*>(lds + NBUF * T::ELEMS);       // [NWV][16][D] per-wave staging
+  float* fbuf = reinterpret_cast<float*>(lds + NBUF * T::ELEMS);       // [NCW][16][D] per-wave staging
 
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, quad = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -449,6 +449,9 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
   // w + NWV, ... of the round's column blocks; q~ goes through LDS to the
   // waves that own the columns.  The raw steps take the raw q (bf16). ----
   u32x4 bq[CB][NKB];
+  if (MODE == 1)  // the waves without columns never set bq (nor use it)
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) bq[0][kb] = u32x4{0u, 0u, 0u, 0u};
   auto load_raw_q = [&]() {
 #pragma unroll
     for (int c = 0; c < CB; ++c) {
@@ -524,10 +527,12 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
         for (int cbk = 0; cbk < NCW; ++cbk)
           *reinterpret_cast<f32x4*>(fbuf + (16 * cbk + l16) * D + 16 * (wave + NWV * j) + 4 * quad) = qacc[j][cbk] * qscale;
       lds_barrier();
+      if (MODE == 0 || wave < NCW) {  // the waves that own columns
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const float* src = fbuf + (16 * wave + l16) * D + 32 * kb + 8 * quad;
-        bq[c][kb] = u32x4{f16pair(src[0], src[1]), f16pair(src[2], src[3]), f16pair(src[4], src[5]), f16pair(src[6], src[7])};
+        for (int kb = 0; kb < NKB; ++kb) {
+          const float* src = fbuf + (16 * wave + l16) * D + 32 * kb + 8 * quad;
+          bq[c][kb] = u32x4{f16pair(src[0], src[1]), f16pair(src[2], src[3]), f16pair(src[4], src[5]), f16pair(src[6], src[7])};
+        }
       }
       lds_barrier();  // fbuf and the tiles are reused
     }
@@ -889,8 +894,9 @@ int attend_cols(bool extend, int d) { return extend ? 16 * attend_waves(extend, 
 
 size_t attend_lds_bytes(int d, bool extend) {
   const int nwv = attend_waves(extend, d), nbuf = nwv > 1 ? 2 : 1;
+  const int ncw = extend ? nwv : 1;  // waves that own columns (per-wave staging)
   const size_t elems = d == 128 ? Tile<128>::ELEMS : Tile<64>::ELEMS;
-  return size_t(nbuf) * elems * 2 + size_t(nwv) * 16 * d * 4;
+  return size_t(nbuf) * elems * 2 + size_t(ncw) * 16 * d * 4;
 }
 
 
