@@ -400,15 +400,19 @@ oscar_status plan_attend(bool extend, int32_t batch, int32_t n_kv, int32_t n_q, 
   const long long steps = qsteps + osteps;
   const long long units = (long long)batch * n_kv;
   if (units * plan->n_ct > (1LL << 30)) return fail(OSCAR_ERR_UNSUPPORTED, "grid too large; split the batch");
+  // several chunks: quantized steps and the others in chunks of their own
+  auto chunks_of = [&](long long sp) { return steps <= sp ? 1 : (qsteps + sp - 1) / sp + (osteps + sp - 1) / sp; };
   long long spc = split_steps;
   if (!spc) {
-    const long long target = (extend ? 2LL : 3LL) * device_cu_count();
+    // at most two workgroups per CU (measured: a few workgroups past a whole
+    // round cost more than the longer chunks), the steps spread evenly
+    const long long target = 2LL * device_cu_count();
     const long long base = std::max(1LL, units * plan->n_ct);
-    const long long chunks = std::max(1LL, (target + base - 1) / base);
+    const long long chunks = std::max(1LL, target / base);
     spc = std::max(extend ? 8LL : 16LL, (steps + chunks - 1) / chunks);
+    while (chunks_of(spc) > chunks && spc < steps) ++spc;
   }
-  // several chunks: quantized steps and the others in chunks of their own
-  const long long n_chunks = steps <= spc ? 1 : (qsteps + spc - 1) / spc + (osteps + spc - 1) / spc;
+  const long long n_chunks = chunks_of(spc);
   if (units * plan->n_ct * n_chunks > (1LL << 31) - 1) return fail(OSCAR_ERR_UNSUPPORTED, "grid too large; use a larger split_steps");
   if (n_chunks > 8192) return fail(OSCAR_ERR_UNSUPPORTED, "more than 8192 chunks per unit; use a larger split_steps");
   plan->spc = int(std::min<long long>(spc, 1 << 30));

@@ -444,10 +444,11 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
     if (has_q) step_load<D, BITS, NTH>(p, rg, btq, bth, h, row0, n_rows, qinfo(qa + k), stq[k], tid);
 
   // ---- query operands: q~ = q R_K (f16, pre-scaled by qscale) for the
-  // quantized steps, computed for all the tile's columns in CB rounds: R_K
-  // staged in LDS 32 rows at a time, wave w computing channel blocks w,
-  // w + NWV, ... of the round's column blocks; q~ goes through LDS to the
-  // waves that own the columns.  The raw steps take the raw q (bf16). ----
+  // quantized steps, computed for all the tile's columns in CB rounds, wave
+  // w computing channel blocks w, w + NWV, ... of the round's column blocks
+  // from the R_K values of its A operands (loaded once, straight into
+  // registers); q~ goes through LDS to the waves that own the columns.  The
+  // raw steps take the raw q (bf16). ----
   u32x4 bq[CB][NKB];
   if (MODE == 1)  // the waves without columns never set bq (nor use it)
 #pragma unroll
@@ -463,19 +464,33 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
   if (has_q) {
     constexpr int CPW = NCB / NWV;  // channel blocks per wave
     static_assert(CPW >= 1 && NCB % NWV == 0, "channel blocks split over the waves");
-    float* rs = reinterpret_cast<float*>(tiles);  // [32][D] rows of R_K
     const float* rk = p.r_k + size_t(h) * D * D;
-    // all of R_K requested at once (this thread's share of every 32-row
-    // slab), so the rounds below wait for memory once
-    constexpr int RPT = (32 * D / 4 + NTH - 1) / NTH;  // f32x4 per thread per slab
-    f32x4 rkr[NKB][RPT];
+    // A operands of channel block cb = wave + NWV j, slice kb: lane (l16,
+    // quad) holds R_K[32 kb + 8 quad + i][16 cb + l16], i < 8, as bf16 hi + lo
+    u32x4 rah[CPW][NKB], ral[CPW][NKB];
+    {
+      float rv[CPW][NKB][8];
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
+      for (int j = 0; j < CPW; ++j)
 #pragma unroll
-      for (int i = 0; i < RPT; ++i) {
-        const int e = min(tid + i * NTH, 32 * D / 4 - 1);
-        rkr[kb][i] = *reinterpret_cast<const f32x4*>(rk + size_t(32 * kb) * D + 4 * e);
-      }
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) rv[j][kb][i] = rk[size_t(32 * kb + 8 * quad + i) * D + 16 * (wave + NWV * j) + l16];
+#pragma unroll
+      for (int j = 0; j < CPW; ++j)
+#pragma unroll
+        for (int kb = 0; kb < NKB; ++kb) {
+          uint32_t ph[4], pl[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float a = rv[j][kb][2 * i], b2 = rv[j][kb][2 * i + 1];
+            ph[i] = pack2(bf16_rne(a), bf16_rne(b2));
+            pl[i] = pack2(bf16_rne(a - bf16_to_f32(ph[i] & 0xFFFFu)), bf16_rne(b2 - bf16_to_f32(ph[i] >> 16)));
+          }
+          rah[j][kb] = u32x4{ph[0], ph[1], ph[2], ph[3]};
+          ral[j][kb] = u32x4{pl[0], pl[1], pl[2], pl[3]};
+        }
+    }
 #pragma unroll
     for (int c = 0; c < CB; ++c) {  // unrolled: bq[c] needs a constant index
       const uint16_t* qcols[NCW];  // the q rows of the round's column blocks (lane l16's column)
@@ -491,34 +506,17 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
 #pragma unroll
         for (int cbk = 0; cbk < NCW; ++cbk) qacc[j][cbk] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {  // unrolled: rkr[kb] needs a constant index
+      for (int kb = 0; kb < NKB; ++kb) {
         u32x4 qk[NCW];  // B operands: the q slice kb of every column block
 #pragma unroll
         for (int cbk = 0; cbk < NCW; ++cbk) qk[cbk] = *reinterpret_cast<const u32x4*>(qcols[cbk] + 32 * kb + 8 * quad);
 #pragma unroll
-        for (int i = 0; i < RPT; ++i)
-          if (tid + i * NTH < 32 * D / 4) *reinterpret_cast<f32x4*>(rs + 4 * (tid + i * NTH)) = rkr[kb][i];
-        __syncthreads();
-#pragma unroll
-        for (int j = 0; j < CPW; ++j) {
-          const int cb = wave + NWV * j;
-          float rv[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) rv[i] = rs[(8 * quad + i) * D + 16 * cb + l16];
-          uint32_t ph[4], pl[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            ph[i] = pack2(bf16_rne(rv[2 * i]), bf16_rne(rv[2 * i + 1]));
-            pl[i] = pack2(bf16_rne(rv[2 * i] - bf16_to_f32(ph[i] & 0xFFFFu)), bf16_rne(rv[2 * i + 1] - bf16_to_f32(ph[i] >> 16)));
-          }
-          const u32x4 AH{ph[0], ph[1], ph[2], ph[3]}, AL{pl[0], pl[1], pl[2], pl[3]};
+        for (int j = 0; j < CPW; ++j)
 #pragma unroll
           for (int cbk = 0; cbk < NCW; ++cbk) {
-            qacc[j][cbk] = mfma_bf16(AL, qk[cbk], qacc[j][cbk]);
-            qacc[j][cbk] = mfma_bf16(AH, qk[cbk], qacc[j][cbk]);
+            qacc[j][cbk] = mfma_bf16(ral[j][kb], qk[cbk], qacc[j][cbk]);
+            qacc[j][cbk] = mfma_bf16(rah[j][kb], qk[cbk], qacc[j][cbk]);
           }
-        }
-        lds_barrier();
       }
       // qacc[j][cbk][r] = q~[column block (CB cbk + c), column l16][channel 16 (wave + NWV j) + 4 quad + r]
 #pragma unroll
