@@ -713,9 +713,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
       if (quad == 0) s_qsp[wave * 16 + l16] = qs;
     }
     lds_barrier();
-    u32x4 bq[NG];
-#pragma unroll
-    for (int g = 0; g < NG; ++g) bq[g] = *reinterpret_cast<const u32x4*>(s_qhat + (g * 64 + lane) * 4);
     // zero-term B operand: K-slots of quad 0 carry the per-group query sums
     // (f16 hi), quad 1 their f16 remainders, the rest zero
     u32x4 bz = {0, 0, 0, 0};
@@ -760,7 +757,10 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
         for (int g = 0; g < NG; ++g) {
           const uint32_t src = (g & 1) ? shr8_halves(P.kc[g >> 1]) : P.kc[g >> 1];
           const u32x4 a = {src & 0x00030003u, src & 0x000C000Cu, src & 0x00300030u, src & 0x00C000C0u};
-          const f32x4 dg = mfma_f16(a, bq[g], f32x4{0.f, 0.f, 0.f, 0.f});
+          // q~ operand of group g, read from LDS at each use (measured: a little
+          // faster than holding the NG operands in registers)
+          const u32x4 bqg = *reinterpret_cast<const u32x4*>(s_qhat + (g * 64 + lane) * 4);
+          const f32x4 dg = mfma_f16(a, bqg, f32x4{0.f, 0.f, 0.f, 0.f});
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int idx = r * NG + g;  // scale of token 4quad + r, group g
