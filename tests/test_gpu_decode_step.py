@@ -7,7 +7,10 @@ then oscar_paged_decode_attn) writes, and each step's output must match the
 oracle's decode over the pages the GPU wrote (rel-L2 <= 5e-3, max-abs <=
 2e-2).  After the last step every middle token's codes and f16 scale/zero are
 checked against the oracle's fill of the whole history, and every sink and
-recent token's BF16 slot against its raw row, bit for bit.
+recent token's BF16 slot against its raw row, bit for bit.  At full size (the
+benchmark's default Qwen3-8B 32k workload and the 128k batch-4 one, automatic
+plan, stale pools) the same holds on sampled sequences, with the rows each step
+wrote checked against the oracle.
 """
 import dataclasses
 
@@ -16,6 +19,8 @@ import pytest
 import torch
 
 from int2_rotated_kv_oscar_amd import lib, synth
+from oracle import attention as oatt
+from oracle import cache as ocache
 from oracle import layout as olayout
 
 import gpu_helpers as gh
@@ -161,3 +166,95 @@ def test_decode_step_rejects_bad_arguments():
     with pytest.raises(lib.OscarError) as e:
         lib.decode_step(gc.cache, kv, kv, q, sl, 40, gc.bt_q, gc.bt_h, gc.r_k, gc.r_v, 1.0, 1.0, out, ws[:4])
     assert e.value.status == 4
+
+
+def _run_full_size_steps(name: str, n_steps: int, check_seqs):
+    """The benchmark's timed call (oscar_decode_step, automatic plan) at a
+    workload's full size, on a stale pool: every step's pools equal the
+    two-launch sequence's bytes, the sampled sequences' outputs match the
+    oracle over the GPU's pages, and the rows the steps wrote (each new
+    token's BF16 slot, each entering token's INT2 codes and f16 scale/zero)
+    match their raw rows and the oracle's quantization."""
+    w = synth.WORKLOADS[name]
+    final = synth.context_lengths(w)
+    sb = np.asarray(check_seqs)
+    inp_f = _full_tables(synth.decode_inputs(w, seq_lens=final, draw_seqs=check_seqs), 900)
+    rot = gh.oracle_rotation(w, n_rows=1024)
+    lens0 = (final - n_steps).astype(np.int32)
+    inp0 = dataclasses.replace(inp_f, seq_lens=lens0)
+    print(f"[full-size step {name}] B={len(final)} max_len={int(final.max())} steps={n_steps} checked={list(sb)}",
+          flush=True)
+    fused = gh.alloc_cache(inp0, rot)
+    gh.fill_stale(fused, 7)
+    gh.gpu_fill(inp0, rot, fused)
+    torch.cuda.synchronize()
+    two = _clone(fused, w)
+    B, hq, hkv, d = len(final), w.n_q_heads, w.n_kv_heads, w.d
+    mixers = synth.query_mixers(w)
+    ws_b = lib.decode_workspace_bytes(B, hkv, hq, d, int(final.max()))
+    ws_f = torch.empty((ws_b + 3) // 4, dtype=torch.int32, device=gh.DEV)
+    ws_t = torch.empty_like(ws_f)
+    lib.decode_workspace_init(ws_f)
+    lib.decode_workspace_init(ws_t)
+    entered = []  # (sequence, position) of the tokens the steps moved into INT2
+    for s in range(n_steps):
+        lens = (lens0 + s + 1).astype(np.int32)
+        max_len = int(lens.max())
+        newrow = np.array([inp_f.row_of[b][L - 1] for b, L in enumerate(lens)], np.int64)
+        k_new = gh.bits_to_dev_bf16(inp_f.k_rows[newrow])
+        v_new = gh.bits_to_dev_bf16(inp_f.v_rows[newrow])
+        q_bits = synth.q_rows(synth.rng_for(w.cfg_id, 70 + s), B, w, mixers)
+        q = gh.bits_to_dev_bf16(q_bits)
+        sl = gh.i32(lens)
+        out_f = torch.full((B, hq, d), float("nan"), dtype=torch.bfloat16, device=gh.DEV)
+        out_t = torch.full_like(out_f, float("nan"))
+        print(f"[full-size step {name}] step {s} max_len={max_len}", flush=True)
+        lib.decode_step(fused.cache, k_new, v_new, q, sl, max_len, fused.bt_q, fused.bt_h, fused.r_k, fused.r_v,
+                        rot.tau_k, rot.tau_v, out_f, ws_f)
+        lib.decode_step_update(two.cache, k_new, v_new, sl, two.bt_q, two.bt_h, two.r_k, two.r_v, rot.tau_k,
+                               rot.tau_v)
+        lib.paged_decode_attn(two.cache, q, sl, max_len, two.bt_q, two.bt_h, two.r_k, two.r_v, out_t, ws_t)
+        torch.cuda.synchronize()
+        assert torch.equal(fused.int2, two.int2), f"step {s}: INT2 pool differs from the two-launch step"
+        assert torch.equal(fused.bf16, two.bf16), f"step {s}: BF16 pool differs from the two-launch step"
+        got = gh.dev_bf16_to_f64(out_f)
+        assert np.isfinite(got).all()
+        inp_s = dataclasses.replace(inp_f, seq_lens=lens)
+        int2, bf = gh.gpu_pages(inp_s, fused)
+        qs = synth.bf16_bits_to_f32(q_bits[sb]).astype(np.float64)
+        ref = oatt.decode_attention(qs, int2, bf, lens[sb], inp_f.bt_q[sb], inp_f.bt_h[sb], rot.r_k, rot.r_v,
+                                    w.n_sink, w.n_recent)
+        err = gh.attention_errors(got[sb], ref)
+        print(f"[full-size step {name}] step {s} errors {err}", flush=True)
+        gh.assert_attention_close(got[sb], ref, f"{name} step {s}")
+        entered += [(int(b), int(lens[b]) - 1 - w.n_recent) for b in sb if int(lens[b]) - 1 - w.n_recent >= w.n_sink]
+    # the entering tokens' codes and f16 scale/zero, against the oracle
+    es = np.array([b for b, _ in entered]); ep = np.array([t for _, t in entered])
+    er = np.array([inp_f.row_of[b][t] for b, t in entered])
+    res = ocache.quantize_append(olayout.Int2Pool(inp_f.n_int2_pages, hkv, d), inp_f.k_rows[er], inp_f.v_rows[er],
+                                 es, ep, inp_f.bt_q, rot.r_k, rot.r_v, rot.tau_k, rot.tau_v, olayout.bf16_to_f64)
+    rep = gh.compare_appended(fused.int2.cpu().numpy(), w, inp_f.n_int2_pages, res,
+                              inp_f.bt_q[es, ep // 16].astype(np.int64), (ep % 16).astype(np.int64))
+    print(rep, flush=True)
+    gh.assert_codes_ok(rep, f"{name} entering tokens")
+    # the new tokens' BF16 slots hold their raw rows
+    bfp = olayout.Bf16Pool(inp_f.n_bf16_pages, hkv, d, fused.bf16.cpu().numpy().view(np.uint16))
+    for b in sb:
+        for s in range(n_steps):
+            t = int(lens0[b]) + s
+            page = inp_f.bt_h[b, t // 16]
+            for h in range(hkv):
+                k, v = bfp.read(np.array([page]), np.array([t % 16]), h)
+                r = inp_f.row_of[b][t]
+                assert np.array_equal(k[0], inp_f.k_rows[r, h]) and np.array_equal(v[0], inp_f.v_rows[r, h]), \
+                    f"BF16 slot of token {t} (sequence {b}, head {h})"
+
+
+def test_decode_step_full_size_bench_config():
+    # the benchmark's default workload: Qwen3-8B layer, one 32k sequence (one fused launch per step)
+    _run_full_size_steps("qwen3-8b-b1-32k", 2, [0])
+
+
+def test_decode_step_full_size_qwen3_32b_b4_128k():
+    # four 128k sequences, 8 queries per KV head (one fused launch per step)
+    _run_full_size_steps("qwen3-32b-b4-128k", 1, [1])
