@@ -116,8 +116,8 @@ __device__ __forceinline__ Regions make_regions(int P, int S, int W) {
 template <int D, int BITS, int NTH>
 struct Stage {
   static constexpr int NR = (4 * D + NTH - 1) / NTH;       // raw chunks per tensor per thread
-  static constexpr int NQ = BITS == 2 ? (2 * D + NTH - 1) / NTH : (4 * D + NTH - 1) / NTH;  // quantized items
-  static constexpr int QW = BITS == 2 ? 12 : 6;            // registers per item
+  static constexpr int NQ = (2 * D + NTH - 1) / NTH;       // quantized items per thread
+  static constexpr int QW = BITS == 2 ? 12 : 8;            // registers per item
   uint32_t qw[NQ][QW];
 };
 
@@ -197,24 +197,29 @@ __device__ __forceinline__ void step_load(const AttParams& p, const Regions& rg,
     }
   } else {
     using QG = QGeo<D, 4>;
-    constexpr int WPR = D / 8, WPP = 16 * WPR;
+    constexpr int IPP = 16 * (D / 16);  // items per page: (token, 16-channel half group)
 #pragma unroll
     for (int it = 0; it < SG::NQ; ++it) {
       const int e0 = t + it * NTH;
-      const int e = e0 < 2 * WPP ? e0 : 0;
-      const int j = e / WPP, wi = e % WPP;
+      if (NTH > 2 * IPP && e0 >= 2 * IPP) break;  // whole waves without an item
+      const int e = e0 < 2 * IPP ? e0 : 0;
+      const int j = e / IPP, wi = e % IPP;
       const int pg = min(rg.q0 + si.i0 + j, rg.q1 - 1);
       const uint8_t* base = p.qpool + (size_t(min(max(btq[pg], 0), p.n_qpages - 1)) * p.n_kv + h) * QG::BYTES;
       // token m = wi % 16 (consecutive lanes take consecutive tokens: the
-      // value tile's channel rows are then written contiguously), code word
-      // cw = wi / 16 (channels 8 cw .. 8 cw + 7)
-      const int m = wi % 16, cw = wi / 16, g = (8 * cw) / 32;
-      st.qw[it][0] = reinterpret_cast<const uint32_t*>(base + QG::KC)[m * WPR + cw];
-      st.qw[it][1] = reinterpret_cast<const uint32_t*>(base + QG::VC)[m * WPR + cw];
-      st.qw[it][2] = reinterpret_cast<const uint16_t*>(base + QG::KS)[m * NG + g];
-      st.qw[it][3] = reinterpret_cast<const uint16_t*>(base + QG::KZ)[m * NG + g];
-      st.qw[it][4] = reinterpret_cast<const uint16_t*>(base + QG::VS)[m * NG + g];
-      st.qw[it][5] = reinterpret_cast<const uint16_t*>(base + QG::VZ)[m * NG + g];
+      // value tile's channel rows are then written contiguously), channels
+      // 16 hc .. 16 hc + 15 (8 bytes of codes), group hc / 2
+      const int m = wi % 16, hc = wi / 16, g = hc / 2;
+      const u32x2 kc = *reinterpret_cast<const u32x2*>(base + QG::KC + m * (D / 2) + 8 * hc);
+      const u32x2 vc = *reinterpret_cast<const u32x2*>(base + QG::VC + m * (D / 2) + 8 * hc);
+      st.qw[it][0] = kc[0];
+      st.qw[it][1] = kc[1];
+      st.qw[it][2] = vc[0];
+      st.qw[it][3] = vc[1];
+      st.qw[it][4] = reinterpret_cast<const uint16_t*>(base + QG::KS)[m * NG + g];
+      st.qw[it][5] = reinterpret_cast<const uint16_t*>(base + QG::KZ)[m * NG + g];
+      st.qw[it][6] = reinterpret_cast<const uint16_t*>(base + QG::VS)[m * NG + g];
+      st.qw[it][7] = reinterpret_cast<const uint16_t*>(base + QG::VZ)[m * NG + g];
     }
   }
 }
@@ -308,28 +313,31 @@ __device__ __forceinline__ void step_store(const AttParams& p, const Regions& rg
       }
     }
   } else {
-    constexpr int WPR = D / 8, WPP = 16 * WPR;
+    constexpr int IPP = 16 * (D / 16);
 #pragma unroll
     for (int it = 0; it < SG::NQ; ++it) {
       const int e = t + it * NTH;
-      if (e >= 2 * WPP) break;
-      const int j = e / WPP, wi = e % WPP;
+      if (e >= 2 * IPP) break;
+      const int j = e / IPP, wi = e % IPP;
       const int pg = rg.q0 + si.i0 + j;
-      const int m = wi % 16, c0 = 8 * (wi / 16);  // as in step_load
+      const int m = wi % 16, c0 = 16 * (wi / 16);  // as in step_load
       const int pos = 16 * pg + m;
       const bool ok = pg < rg.q1 && pos >= rg.m0 && pos < rg.m1;
-      const uint32_t kw = st.qw[it][0], vw = st.qw[it][1];
-      const float ks = f16_to_f32(st.qw[it][2]), kz = f16_to_f32(st.qw[it][3]);
-      const float vs = f16_to_f32(st.qw[it][4]), vz = f16_to_f32(st.qw[it][5]);
-      float v[8];
+      const float ks = f16_to_f32(st.qw[it][4]), kz = f16_to_f32(st.qw[it][5]);
+      const float vs = f16_to_f32(st.qw[it][6]), vz = f16_to_f32(st.qw[it][7]);
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = ok ? __builtin_fmaf(float((kw >> (4 * k)) & 15u), ks, kz) : 0.f;
-      *reinterpret_cast<u32x4*>(tile + (16 * j + m) * T::KROW + c0) =
-          u32x4{f16pair(v[0], v[1]), f16pair(v[2], v[3]), f16pair(v[4], v[5]), f16pair(v[6], v[7])};
+      for (int hw = 0; hw < 2; ++hw) {
+        const uint32_t kw = st.qw[it][hw], vw = st.qw[it][2 + hw];
+        float v[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const float x = ok ? __builtin_fmaf(float((vw >> (4 * k)) & 15u), vs, vz) : 0.f;
-        vt[(c0 + k) * T::VROW + 16 * j + m] = uint16_t(f16_bits(x));
+        for (int k = 0; k < 8; ++k) v[k] = ok ? __builtin_fmaf(float((kw >> (4 * k)) & 15u), ks, kz) : 0.f;
+        *reinterpret_cast<u32x4*>(tile + (16 * j + m) * T::KROW + c0 + 8 * hw) =
+            u32x4{f16pair(v[0], v[1]), f16pair(v[2], v[3]), f16pair(v[4], v[5]), f16pair(v[6], v[7])};
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const float x = ok ? __builtin_fmaf(float((vw >> (4 * k)) & 15u), vs, vz) : 0.f;
+          vt[(c0 + 8 * hw + k) * T::VROW + 16 * j + m] = uint16_t(f16_bits(x));
+        }
       }
     }
   }
