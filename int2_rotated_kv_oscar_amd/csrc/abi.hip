@@ -404,12 +404,14 @@ oscar_status plan_attend(bool extend, int32_t batch, int32_t n_kv, int32_t n_q, 
   auto chunks_of = [&](long long sp) { return steps <= sp ? 1 : (qsteps + sp - 1) / sp + (osteps + sp - 1) / sp; };
   long long spc = split_steps;
   if (!spc) {
-    // at most two workgroups per CU (measured: a few workgroups past a whole
-    // round cost more than the longer chunks), the steps spread evenly
-    const long long target = 2LL * device_cu_count();
+    // as many workgroups as fit on the device at once (the decode kernel
+    // holds three per CU; extend is measured best at two) and no more
+    // (measured: a few workgroups past a whole round cost more than longer
+    // chunks), the steps spread evenly
+    const long long target = (extend ? 2LL : 3LL) * device_cu_count();
     const long long base = std::max(1LL, units * plan->n_ct);
     const long long chunks = std::max(1LL, target / base);
-    spc = std::max(extend ? 8LL : 16LL, (steps + chunks - 1) / chunks);
+    spc = std::max(8LL, (steps + chunks - 1) / chunks);
     while (chunks_of(spc) > chunks && spc < steps) ++spc;
   }
   const long long n_chunks = chunks_of(spc);
