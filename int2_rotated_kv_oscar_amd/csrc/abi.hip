@@ -419,7 +419,7 @@ oscar_status plan_attend(bool extend, int32_t batch, int32_t n_kv, int32_t n_q, 
   if (n_chunks > 8192) return fail(OSCAR_ERR_UNSUPPORTED, "more than 8192 chunks per unit; use a larger split_steps");
   plan->spc = int(std::min<long long>(spc, 1 << 30));
   plan->n_chunks = int(n_chunks);
-  plan->bytes = plan->n_chunks > 1 ? size_t(units) * plan->n_ct * plan->n_chunks * nct * (2 + 2 * size_t(d)) * 4 : 0;
+  plan->bytes = plan->n_chunks > 1 ? size_t(units) * plan->n_ct * plan->n_chunks * nct * (4 + 2 * size_t(d)) * 4 : 0;
   return OSCAR_OK;
 }
 

@@ -32,6 +32,8 @@ using namespace oscar_dev;
 
 namespace {
 
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
 constexpr float kNegInfA = -__builtin_inff();
 constexpr float kSlackA = 4.0f;  // log2 units
 
@@ -755,9 +757,10 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
     if (NBUF == 1) lds_barrier();
   }
 
-  constexpr int RF = 2 + 2 * D;
+  constexpr int RF = 4 + 2 * D;
   if (p.n_chunks > 1) {
-    // record of this chunk: [m][l][raw D][rot D] per column, the sums in the
+    // record of this chunk: [m][l][2 unused][raw D][rot D] per column (the
+    // value sums 16-byte aligned), the sums in the
     // field of their basis and zeros in the other (columns past the unit's
     // last are never merged: no record)
 #pragma unroll
@@ -772,8 +775,8 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
       const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        *reinterpret_cast<f32x4*>(rec + 2 + 16 * cb + 4 * quad) = rotated ? zero : acc[c][cb];
-        *reinterpret_cast<f32x4*>(rec + 2 + D + 16 * cb + 4 * quad) = rotated ? acc[c][cb] : zero;
+        *reinterpret_cast<f32x4*>(rec + 4 + 16 * cb + 4 * quad) = rotated ? zero : acc[c][cb];
+        *reinterpret_cast<f32x4*>(rec + 4 + D + 16 * cb + 4 * quad) = rotated ? acc[c][cb] : zero;
       }
     }
     return;
@@ -800,13 +803,13 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
 // rotation: M = max_k m_k, w_k = 2^(m_k - M),
 // out = (sum_k w_k raw_k + (sum_k w_k rot_k) R_V^T) / sum_k w_k l_k.
 // One workgroup per (unit, column tile, column).  Its R_V entries (output
-// channel c = tid / TPC, a KPT-long run of k) are requested first, so they
-// arrive while the records are read; the four waves take every fourth chunk
-// (a lane holds FPL of the 2d value sums, sixteen chunks' loads in flight)
-// and meet in LDS.
+// channel c = tid / TPC, a KPT-long run of k) and the first sixteen records'
+// values of each wave are requested first, so they arrive while the maxima
+// and sums are reduced; the four waves take every fourth chunk (a lane holds
+// FPL of the 2d value sums, sixteen chunks' loads in flight) and meet in LDS.
 template <int D, int NC, int MODE>
 __global__ __launch_bounds__(256) void attend_merge_kernel(AttParams p) {
-  constexpr int RF = 2 + 2 * D, NWM = 4, FPL = 2 * D / 64;  // waves, value floats per lane
+  constexpr int RF = 4 + 2 * D, NWM = 4, FPL = 2 * D / 64;  // waves, value floats per lane
   constexpr int TPC = 256 / D, KPT = D / TPC;                // threads per output channel, R_V entries each
   static_assert(FPL == 4 || FPL == 2, "d = 64 or 128");
   extern __shared__ __attribute__((aligned(16))) uint16_t lds[];
@@ -829,15 +832,48 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttParams p) {
   f32x4 rr[KPT / 4];
 #pragma unroll
   for (int i = 0; i < KPT / 4; ++i) rr[i] = *reinterpret_cast<const f32x4*>(rrow + 4 * i);
-  float mx = kNegInfA;
-  for (int k = tid; k < nk; k += 256) mx = fmaxf(mx, rec0[k * cstride]);
+  // this wave's chunks k = wave + NWM t, t < nt, sixteen at a time (indices
+  // clamped into the records; the first sixteen requested before the weights,
+  // which they do not need)
+  const float* vb = rec0 + 4 + FPL * lane;
+  const int nt = (nk - wave + NWM - 1) / NWM;
+  float v[16][FPL];
+  auto load16 = [&](int t0) {
+#pragma unroll
+    for (int t = 0; t < 16; ++t) {
+      const int kk = min(wave + NWM * (t0 + t), nk - 1);
+      if constexpr (FPL == 4) {
+        const f32x4 x = *reinterpret_cast<const f32x4*>(vb + kk * cstride);
+#pragma unroll
+        for (int f = 0; f < 4; ++f) v[t][f] = x[f];
+      } else {
+        const f32x2 x = *reinterpret_cast<const f32x2*>(vb + kk * cstride);
+        v[t][0] = x[0];
+        v[t][1] = x[1];
+      }
+    }
+  };
+  load16(0);
+  // maxima and sums: thread k holds chunk k's (first 256 chunks)
+  float m0 = kNegInfA, l0 = 0.f;
+  if (tid < nk) {
+    m0 = rec0[tid * cstride];
+    l0 = rec0[tid * cstride + 1];
+  }
+  float mx = m0;
+  for (int k = tid + 256; k < nk; k += 256) mx = fmaxf(mx, rec0[k * cstride]);
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
   if (lane == 0) s_red[wave] = mx;
   __syncthreads();
   mx = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
   float l = 0.f;
-  for (int k = tid; k < nk; k += 256) {
+  if (tid < nk) {
+    const float w = m0 == kNegInfA ? 0.f : exp2f(m0 - mx);
+    s_w[tid] = w;
+    l = w * l0;
+  }
+  for (int k = tid + 256; k < nk; k += 256) {
     const float mk = rec0[k * cstride];
     const float w = mk == kNegInfA ? 0.f : exp2f(mk - mx);
     s_w[k] = w;
@@ -851,22 +887,14 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttParams p) {
   float a[FPL];
 #pragma unroll
   for (int f = 0; f < FPL; ++f) a[f] = 0.f;
-  const float* vb = rec0 + 2 + FPL * lane;
-  int k = wave;
-  for (; k + NWM * 15 < nk; k += NWM * 16) {
-    float v[16][FPL];
+  for (int t0 = 0; t0 < nt; t0 += 16) {
+    if (t0 > 0) load16(t0);
 #pragma unroll
     for (int t = 0; t < 16; ++t)
+      if (t0 + t < nt)
 #pragma unroll
-      for (int f = 0; f < FPL; ++f) v[t][f] = vb[(k + NWM * t) * cstride + f];
-#pragma unroll
-    for (int t = 0; t < 16; ++t)
-#pragma unroll
-      for (int f = 0; f < FPL; ++f) a[f] = __builtin_fmaf(s_w[k + NWM * t], v[t][f], a[f]);
+        for (int f = 0; f < FPL; ++f) a[f] = __builtin_fmaf(s_w[wave + NWM * (t0 + t)], v[t][f], a[f]);
   }
-  for (; k < nk; k += NWM)
-#pragma unroll
-    for (int f = 0; f < FPL; ++f) a[f] = __builtin_fmaf(s_w[k], vb[k * cstride + f], a[f]);
 #pragma unroll
   for (int f = 0; f < FPL; ++f) s_part[wave * 2 * D + FPL * lane + f] = a[f];
   __syncthreads();
