@@ -412,7 +412,15 @@ oscar_status plan_attend(bool extend, int32_t batch, int32_t n_kv, int32_t n_q, 
     const long long base = std::max(1LL, units * plan->n_ct);
     const long long chunks = std::max(1LL, target / base);
     spc = std::max(8LL, (steps + chunks - 1) / chunks);
-    while (chunks_of(spc) > chunks && spc < steps) ++spc;
+    if (chunks_of(spc) > chunks) {  // the smallest larger spc that fits (chunks_of does not grow with spc)
+      long long lo = spc, hi = std::max(spc, steps);
+      while (lo < hi) {
+        const long long mid = lo + (hi - lo) / 2;
+        if (chunks_of(mid) > chunks) lo = mid + 1;
+        else hi = mid;
+      }
+      spc = lo;
+    }
   }
   const long long n_chunks = chunks_of(spc);
   if (units * plan->n_ct * n_chunks > (1LL << 31) - 1) return fail(OSCAR_ERR_UNSUPPORTED, "grid too large; use a larger split_steps");
