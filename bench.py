@@ -639,7 +639,7 @@ def extend_line(args, log, cpu: bool) -> dict:
                    "head_dim": w.d, "cache_copies": copies},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 2), "peak": MFMA_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / MFMA_PEAK_TFLOPS, 4), "traffic": None,
-                     "kernel": "attend_kernel<128,2,4,0>", "algorithmic_flops_per_launch": flops,
+                     "kernel": "attend_kernel<128,2,8,2,0>", "algorithmic_flops_per_launch": flops,
                      "avg_launch_us": round(ms_call * 1e3, 2)},
     }
     if cpu:
@@ -745,8 +745,9 @@ def int4_decode_line(args, log, w, cpu: bool) -> dict:
                    "kv_heads": hkv, "head_dim": d, "cache_copies": copies},
         "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                      "frac": round(gbs / HBM_PEAK_GBPS, 4), "traffic": None,
-                     "kernel": f"attend_kernel<{d},4,1,1>", "algorithmic_bytes_per_launch": nbytes,
-                     "avg_launch_us": round(ms_call * 1e3, 2)},
+                     "kernel": f"attend_kernel<{d},4,4,1,1> + attend_merge_kernel<{d},16,1>",
+                     "algorithmic_bytes_per_launch": nbytes,
+                     "avg_launch_us": round(ms_call * 1e3, 2), "note": "avg_launch_us: one call (both launches)"},
     }
     if cpu:
         from oracle import attention as oatt
