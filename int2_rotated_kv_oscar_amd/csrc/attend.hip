@@ -4,9 +4,11 @@
 // serving with paged KV layouts and prefix caching; [TS] 4 "Scalability": the
 // INT4 KV cache OSCAR is compared with).
 //
-// A workgroup of NWV waves owns 16 NWV query columns of one (sequence, KV
+// A workgroup of NWV waves owns 16 NCW CB query columns of one (sequence, KV
 // head): a column is one (new row, query head of the group) pair, taken
-// row-major, so the G heads of a row sit side by side.  It walks a chunk of
+// row-major, so the G heads of a row sit side by side.  Extend: every wave
+// holds CB = 2 blocks of 16 columns.  The decode (at most 16 query heads per
+// KV head): wave 0 holds the one block, the other waves help decode steps.  It walks a chunk of
 // the unit's work, 32 tokens per step: page pairs of the BF16 sink/recent
 // pages, page pairs of the quantized middle pages, then (extend) tiles of 32
 // new rows.  Each step is decoded once into an LDS tile shared by the waves:
@@ -14,7 +16,7 @@
 // in the rotated basis) or as the raw bf16 bits (BF16 pages, new rows).  Tokens
 // outside their region (stale slots of recycled pages, rows past the end) are
 // written as zeros and their logits masked, so nothing stale reaches a sum.
-// Every wave then runs, for its 16 columns, the transposed products of
+// Every column-holding wave then runs, for its columns, the transposed products of
 // flash attention on the matrix cores: logits^T = K Q^T (16x16x32, tokens x
 // columns) and out^T += V^T P^T, with the online softmax over the tokens of a
 // column in between.  Quantized tokens use the rotated query q~ = q R_K and
@@ -108,11 +110,11 @@ __device__ __forceinline__ Regions make_regions(int P, int S, int W) {
 
 // ---- step fill: one 32-token step into the LDS tile ----
 // Each thread loads its share of a quantized step's bytes into registers
-// (issued one or two steps ahead, unconditionally, so that the loads overlap
-// the products of the steps before) and then decodes them into the tile.
-// Shares: INT2 page pairs 2D items (a key code word, a value code word, their
-// scales and zeros), INT4 page pairs 4D items (a key and a value code word of
-// 8 nibbles, their scales and zeros).  Raw steps (BF16 page pairs: 4D key and
+// (issued two steps ahead, so that the loads overlap the products of the
+// steps before) and then decodes them into the tile.  Shares: INT2 page pairs
+// 2D items (a key code word, a value code word, their scales and zeros), INT4
+// page pairs 2D items (a token's 16 channels: two key and two value code words
+// of 8 nibbles, their scales and zeros).  Raw steps (BF16 page pairs: 4D key and
 // 4D value chunks of 16 B; tiles of 32 new rows likewise) are few per unit
 // and are loaded when stored.
 template <int D, int BITS, int NTH>
