@@ -74,7 +74,9 @@ struct QGeo : QLayout<D, BITS> {
 template <int D>
 struct Tile {
   static constexpr int KROW = D + 8;   // padded rows: the lanes of an operand read hit distinct banks
-  static constexpr int VROW = 32 + 8;
+  // 18 words: the 16 rows of an 8-byte value-operand read fall on distinct
+  // bank pairs (rows are 8-byte aligned, not 16)
+  static constexpr int VROW = 32 + 4;
   static constexpr int ELEMS = 32 * KROW + D * VROW;
 };
 
@@ -257,7 +259,8 @@ __device__ __forceinline__ void step_store(const AttParams& p, const Regions& rg
           const int pos = 16 * pg + 8 * half + k;
           if (pg < 0 || !raw_token(rg, pos)) vw[k / 2] &= (k & 1) ? 0x0000FFFFu : 0xFFFF0000u;
         }
-        *reinterpret_cast<u32x4*>(vt + c * T::VROW + 16 * jv + 8 * half) = u32x4{vw[0], vw[1], vw[2], vw[3]};
+        *reinterpret_cast<u32x2*>(vt + c * T::VROW + 16 * jv + 8 * half) = u32x2{vw[0], vw[1]};
+        *reinterpret_cast<u32x2*>(vt + c * T::VROW + 16 * jv + 8 * half + 4) = u32x2{vw[2], vw[3]};
       } else {
         const int tok = e / KCH, ch = e % KCH;
         *reinterpret_cast<u32x4*>(tile + tok * T::KROW + 8 * ch) = kv;
