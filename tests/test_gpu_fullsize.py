@@ -187,3 +187,28 @@ def test_int4_decode_qwen3_8b_b1_32k():
     err = gh.attention_errors(got, ref)
     print(f"[fullsize int4 decode] errors {err}", flush=True)
     gh.assert_attention_close(got, ref, "int4 decode 32k")
+
+
+def test_int4_decode_qwen3_32b_b4_128k():
+    # the INT4 decode at the 128k batch-4 shape (8 queries per KV head, stale
+    # pools), checked on one sampled sequence
+    w = synth.WORKLOADS["qwen3-32b-b4-128k"]
+    seqs = [3]
+    inp = synth.decode_inputs(w, draw_seqs=seqs)
+    rot = gh.oracle_rotation(w, n_rows=CALIB_ROWS)
+    gc = gh.alloc_cache(inp, rot, bits=4)
+    gh.fill_stale(gc, seed=3)
+    print("[fullsize int4 decode 128k b4] fill", flush=True)
+    gh.gpu_fill(inp, rot, gc, bits=4)
+    torch.cuda.synchronize()
+    got = gh.gpu_decode_int4(inp, gc)
+    assert np.isfinite(got).all()
+    from oracle import attention as oatt
+    pool, bf = gh.gpu_pages(inp, gc, bits=4)
+    sb = np.asarray(seqs)
+    q = synth.bf16_bits_to_f32(inp.q[sb]).astype(np.float64)
+    ref = oatt.decode_attention(q, pool, bf, inp.seq_lens[sb], inp.bt_q[sb], inp.bt_h[sb], rot.r_k, rot.r_v,
+                                w.n_sink, w.n_recent)
+    err = gh.attention_errors(got[seqs], ref)
+    print(f"[fullsize int4 decode 128k b4] errors {err}", flush=True)
+    gh.assert_attention_close(got[seqs], ref, "int4 decode 128k b4")
