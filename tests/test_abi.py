@@ -51,6 +51,30 @@ def test_workspace_planning():
         assert e.value.status == status
 
 
+def test_attention_chunk_planning():
+    # chunks of split_steps 32-token steps: the quantized page pairs in chunks
+    # of their own, then the raw steps (and new-row tiles); one record of
+    # 4 + 2d floats per column (16 per decode tile, 256 per extend tile at d = 128)
+    rec = (4 + 2 * 128) * 4
+    # a 32k sequence, 8 KV heads, S = 4, W = 128: 1025 quantized steps, 6 raw
+    assert lib.decode_int4_workspace_bytes(1, 8, 32, 128, 4, 128, 32768, 16) == 8 * (65 + 1) * 16 * rec
+    # automatic (256 CUs here and on the MI355X): at most three workgroups per CU
+    auto = lib.decode_int4_workspace_bytes(1, 8, 32, 128, 4, 128, 32768) // (8 * 16 * rec)
+    assert auto == 95 and 8 * auto <= 3 * 256
+    auto4 = lib.decode_int4_workspace_bytes(4, 8, 64, 128, 4, 128, 131072) // (32 * 16 * rec)
+    assert 32 * auto4 <= 3 * 256 and auto4 >= 16
+    # one chunk suffices: no workspace
+    assert lib.decode_int4_workspace_bytes(1, 1, 4, 64, 4, 32, 100, 64) == 0
+    # extend: 512 new rows x 4 heads = 8 column tiles of 256; 6 raw steps + 16
+    # new-row tiles in 3 chunks of 8, the 1025 quantized steps in 129
+    assert lib.extend_workspace_bytes(1, 1, 4, 128, 4, 128, 32768, 512, 8) == 8 * (129 + 3) * 256 * rec
+    for bad, status in (((1, 8, 30, 128, 4, 128, 100, 0), 1), ((1, 1, 4, 96, 4, 128, 100, 0), 2),
+                        ((1, 1, 4, 128, 4, 128, 100, -1), 1), ((1, 1, 4, 128, 4, 128, 2 ** 20, 1), 2)):
+        with pytest.raises(lib.OscarError) as e:
+            lib.decode_int4_workspace_bytes(*bad)
+        assert e.value.status == status
+
+
 def test_device_calls_validate_before_launch():
     L = lib.load()
     c = lib.OscarCache()
