@@ -103,16 +103,17 @@ def step_update_bytes(inp, w) -> int:
 
 def decode_kernel_name(w, split_pages: int, all_raw: bool, fused: bool = False) -> str:
     """The decode kernel instance the library launches for this workload
-    (template arguments: head dim, all-BF16 cache, balanced slices, grouped
-    columns, fused step update), by the library's rule: per-unit items when
-    split_pages is given or the (sequence, KV head) units are at most a
-    quarter of the CUs."""
+    (template arguments: head dim, all-BF16 cache, balanced slices, MFMA
+    column slots per query, fused step update), by the library's rule:
+    per-unit items when split_pages is given or the (sequence, KV head) units
+    are at most a quarter of the CUs."""
     import torch
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     slices = not (split_pages != 0 or 4 * w.batch * w.n_kv_heads <= cus)
-    gc = (not all_raw) and w.n_q_heads // w.n_kv_heads <= 4
+    g = w.n_q_heads // w.n_kv_heads
+    cs = 1 if all_raw else 4 if g <= 4 else 2 if g <= 8 else 1
     b = lambda x: "true" if x else "false"  # noqa: E731
-    return f"decode_kernel<{w.d},{b(all_raw)},{b(slices)},{b(gc)},{b(fused)}>"
+    return f"decode_kernel<{w.d},{b(all_raw)},{b(slices)},{cs},{b(fused)}>"
 
 
 DECODE_SOURCES = ["decode.hip", "device_utils.h", "layout.h"]

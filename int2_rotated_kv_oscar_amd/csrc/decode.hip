@@ -199,16 +199,28 @@ struct PageOps {
     kz[0] = kzp[0];
     kz[1] = NG == 4 ? kzp[1] : 0u;
   }
-  // GROUPED: only the V scales of group gsel (in vs[0], vs[1])
-  template <bool GROUPED = false>
-  __device__ __forceinline__ void read_v(const uint8_t* base, int l16, int quad, int gsel = 0) {
+  // CS > 1 (CS column slots per query): only the V scales of the NGV groups
+  // this lane's column stands for, group min(CS h + l16 % CS, NG - 1) in
+  // vs[2h], vs[2h + 1]; CS = 1: every group's
+  template <int CS = 1>
+  __device__ __forceinline__ void read_v(const uint8_t* base, int l16, int quad) {
     using GG = Geo<D>;
+    constexpr int NGV = NG / CS > 0 ? NG / CS : 1;
     const uint32_t* vcp = reinterpret_cast<const uint32_t*>(base + GG::VC) + (quad * 16 + l16) * NW;
-    const uint32_t* vsp = reinterpret_cast<const uint32_t*>(base + GG::VS) + quad * 2 * NG + (GROUPED ? 2 * gsel : 0);
+    const uint32_t* vsp = reinterpret_cast<const uint32_t*>(base + GG::VS) + quad * 2 * NG;
 #pragma unroll
     for (int i = 0; i < NW; ++i) vc[i] = vcp[i];
+    if (CS == 1) {
 #pragma unroll
-    for (int i = 0; i < (GROUPED ? 2 : 2 * NG); ++i) vs[i] = vsp[i];
+      for (int i = 0; i < 2 * NG; ++i) vs[i] = vsp[i];
+    } else {
+#pragma unroll
+      for (int hh = 0; hh < NGV; ++hh) {
+        const int g = min(CS * hh + l16 % CS, NG - 1);
+        vs[2 * hh] = vsp[2 * g];
+        vs[2 * hh + 1] = vsp[2 * g + 1];
+      }
+    }
     // every lane reads a valid slot (group min(l16, NG - 1)); rows l16 >= NG
     // of the zero-term operand are cleared by the caller's lane mask
     const uint32_t* vzp = reinterpret_cast<const uint32_t*>(base + GG::VZ) + (quad * NG + min(l16, NG - 1)) * 2;
@@ -237,10 +249,10 @@ constexpr int kRing = kDepth + 2;
 // SLICES: balanced slices over all units (several segments per workgroup),
 // else per-unit items (one segment per workgroup, early requests).  Separate
 // kernels keep each one's code to a single instance of the segment.
-// GC (grouped columns, G <= 4): MFMA column n carries query n/4, and in the
-// value products it also stands for channel group n%4, so that one B operand
-// (probability times that group's V scale) serves every channel block;
-// otherwise column n carries query n and each group has its own B operand.
+// CS (column slots per query: 4 for G <= 4, 2 for G <= 8, else 1): MFMA
+// column n carries query n/CS, and in the value products its h-th B operand
+// (probability times a V scale) stands for channel group CS h + n%CS, so
+// that NG/CS operands (at least one) serve every channel block instead of NG.
 // UPD (fused decode step): the launch also does the step's cache update.  The
 // segment whose BF16 pages include the new token's page writes the new token
 // to its slot before reading it; the INT2 segment holding the last middle
@@ -249,7 +261,7 @@ constexpr int kRing = kDepth + 2;
 // leaves that slot out of its own page loop and adds the token to its record
 // from the decoded values.  Launched with per-unit items only: balanced
 // slices leave no workgroup the slack to absorb the update's round trips.
-template <int D, bool ALL_RAW, bool SLICES, bool GC, bool UPD>
+template <int D, bool ALL_RAW, bool SLICES, int CS, bool UPD>
 __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   using GG = Geo<D>;
   constexpr int NG = GG::NG, NCB = GG::NCB, NKB = GG::NKB, HB = GG::HEAD_BYTES;
@@ -278,7 +290,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   const int qrow = min(l16, G - 1);  // per-query rows of the merge
   // query of MFMA column l16 (columns past the group repeat a real head;
   // their results are dropped)
-  const int qcol = GC ? min(l16 >> 2, G - 1) : min(l16, G - 1);
+  const int qcol = min(l16 / CS, G - 1);
   const float qscale = p.sm_scale * kLog2e;
 
   // the (sequence, KV head) unit of the current segment
@@ -391,7 +403,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   int tid = threadIdx.x;
   asm volatile("" : "+v"(tid));
   const int lane = tid & 63, l16 = lane & 15, quad = lane >> 4;
-  const int qcol = GC ? min(l16 >> 2, G - 1) : min(l16, G - 1);
+  const int qcol = min(l16 / CS, G - 1);
   const int n_pairs = (c1 - c0 + 1) >> 1;
   // fused step: this INT2 segment holds the last middle token (the one that
   // enters the middle history this step) and handles it apart from its loop
@@ -444,8 +456,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     lds_barrier();
     if (tid < 2 * D) own_x[tid] = bf16_to_f32(xb);
     // q~ of the group's queries (the columns that hold each query once)
-    if (rot_wave && (GC ? ((l16 & 3) == 0 && (l16 >> 2) < G) : l16 < G)) {
-      const int qi = GC ? (l16 >> 2) : l16;
+    if (rot_wave && l16 % CS == 0 && l16 / CS < G) {
+      const int qi = l16 / CS;
 #pragma unroll
       for (int r = 0; r < 4; ++r) own_q[qi * D + 16 * wave + 4 * quad + r] = qv[r];
     }
@@ -728,8 +740,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     }
     const uint32_t ones = l16 == NG ? 0x3C003C00u : 0u;  // f16 1.0 pairs in A row NG
     const uint32_t zrow = l16 < NG ? 0xFFFFFFFFu : 0u;    // A rows that carry V zeros
-    constexpr int NGV = GC ? 1 : NG;                       // V-scale B operands per pair
-    const int gsel = min(l16 & 3, NG - 1);                 // GC: the group of column l16
+    constexpr int NGV = NG / CS > 0 ? NG / CS : 1;         // V-scale B operands per pair
     // one page pair: logits, softmax, value sums
     // Two page pairs per step (pair k from slot A, pair k+1 from slot B): K
     // operands and logits of the four pages, one softmax step over their 64
@@ -782,7 +793,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
         PageOps<D> P[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
-          P[j].template read_v<GC>(slot + j * HB, l16, quad, gsel);
+          P[j].template read_v<CS>(slot + j * HB, l16, quad);
           const int pg = page_of(k + pr, j);
           if (!INTERIOR && (!page_live(pg) || 16 * pg < m0 || 16 * pg + 16 > m1)) {
             // boundary (or absent) page: clear scale/zero of slots outside the middle
@@ -808,8 +819,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
         acc_z = mfma_f16(u32x4{(P[0].vz[0] & zrow) | ones, (P[0].vz[1] & zrow) | ones, (P[1].vz[0] & zrow) | ones,
                                (P[1].vz[1] & zrow) | ones},
                          u32x4{bp[0], bp[1], bp[2], bp[3]}, acc_z);
-        // B operands: probabilities times V scales, one per group (GC: the
-        // column's own group, one operand for every block)
+        // B operands: probabilities times V scales, NGV of them (CS = 1: one
+        // per group; else operand h holds column n's group CS h + n%CS)
         u32x4 bs[NGV];
 #pragma unroll
         for (int g = 0; g < NGV; ++g)
@@ -820,7 +831,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
           const int w = cb >> 2, bb = cb & 3;
           const uint32_t m = 0x00030003u << (2 * bb);
           const u32x4 a = {P[0].vc[w] & m, shr8_halves(P[0].vc[w]) & m, P[1].vc[w] & m, shr8_halves(P[1].vc[w]) & m};
-          acc[cb] = mfma_f16(a, bs[GC ? 0 : cb >> 1], acc[cb]);
+          acc[cb] = mfma_f16(a, bs[(cb >> 1) / CS], acc[cb]);
         }
       }
     };
@@ -890,12 +901,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w * 16 + l16]);
   const float sc = (m_run == kNegInf) ? 0.f : exp2f(m_run - M);
   {
-    // the column holding query qi's value sums of block cb (GC: column
-    // 4 qi + group of cb for INT2 chunks, 4 qi for BF16 chunks)
-    const int qi = GC ? (l16 >> 2) : l16;
+    // the column holding query qi's value sums of block cb: CS qi + (group
+    // of cb) % CS for INT2 chunks, CS qi for BF16 chunks
+    const int qi = l16 / CS;
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
-      const bool mine = qi < G && (!GC || (l16 & 3) == (is_raw ? 0 : (cb >> 1)));
+      const bool mine = qi < G && (CS == 1 || l16 % CS == (is_raw ? 0 : (cb >> 1) % CS));
       if (!mine) continue;
       f32x4 v;
       if (is_raw) {
@@ -913,7 +924,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   // ---- workgroup record [m G][l G][value sums G D][basis flag] -> workspace ----
   float* rec = p.partials + ((size_t(b) * p.n_kv + h) * p.cap + kseg) * size_t(p.rec_floats);
   if (tid < G) {
-    const int cq = GC ? 4 * tid : tid;  // a column of query tid
+    const int cq = CS * tid;  // a column of query tid
     float mm = kNegInf;
     for (int w = 0; w < kWaves; ++w) mm = fmaxf(mm, s_m[w * 16 + cq]);
     float ll = 0.f;
@@ -1265,8 +1276,8 @@ hipError_t paged_decode(int d, bool all_raw, const void* int2_pool, int n_int2_p
   const bool upd = k_new != nullptr;
   const dim3 grid(static_cast<unsigned>(n_wg));
   const size_t lds = decode_lds_bytes(d, G, all_raw);
-  // grouped columns when the query group fits four columns per query
-  const bool gc = !all_raw && G <= 4;
+  // column slots per query: as many as the 16 MFMA columns give every query
+  const int cs = all_raw ? 1 : G <= 4 ? 4 : G <= 8 ? 2 : 1;
 #define OSCAR_DECODE_LAUNCH(DD, RAW, GCOL)                                                                              \
   do {                                                                                                                 \
     if (upd && !RAW) {                                                                                                 \
@@ -1278,13 +1289,15 @@ hipError_t paged_decode(int d, bool all_raw, const void* int2_pool, int n_int2_p
     }                                                                                                                  \
   } while (0)
   if (d == 128) {
-    if (all_raw) OSCAR_DECODE_LAUNCH(128, true, false);
-    else if (gc) OSCAR_DECODE_LAUNCH(128, false, true);
-    else OSCAR_DECODE_LAUNCH(128, false, false);
+    if (all_raw) OSCAR_DECODE_LAUNCH(128, true, 1);
+    else if (cs == 4) OSCAR_DECODE_LAUNCH(128, false, 4);
+    else if (cs == 2) OSCAR_DECODE_LAUNCH(128, false, 2);
+    else OSCAR_DECODE_LAUNCH(128, false, 1);
   } else {
-    if (all_raw) OSCAR_DECODE_LAUNCH(64, true, false);
-    else if (gc) OSCAR_DECODE_LAUNCH(64, false, true);
-    else OSCAR_DECODE_LAUNCH(64, false, false);
+    if (all_raw) OSCAR_DECODE_LAUNCH(64, true, 1);
+    else if (cs == 4) OSCAR_DECODE_LAUNCH(64, false, 4);
+    else if (cs == 2) OSCAR_DECODE_LAUNCH(64, false, 2);
+    else OSCAR_DECODE_LAUNCH(64, false, 1);
   }
 #undef OSCAR_DECODE_LAUNCH
   return hipGetLastError();

@@ -124,7 +124,9 @@ def test_decode_step_region_edges():
 
 
 @pytest.mark.parametrize("d,hq,hkv,S,W,split", [
-    (128, 32, 8, 4, 128, 0),    # group of 4: grouped columns
+    (128, 32, 8, 4, 128, 0),    # group of 4: four column slots per query
+    (128, 16, 2, 4, 32, 0),     # group of 8: two column slots per query
+    (64, 6, 1, 4, 16, 8),       # group of 6: two slots, the last four columns unused
     (128, 16, 1, 4, 64, 0),     # group of 16
     (64, 8, 2, 0, 16, 8),       # no sink; 8 INT2 pages per workgroup, the last middle page in one of several
     (64, 4, 1, 4, 0, 0),        # no recent window: the new token goes straight to INT2
@@ -137,15 +139,16 @@ def test_decode_step_shapes(d, hq, hkv, S, W, split):
                seed=d + W)
 
 
-def test_decode_step_balanced_slices():
+@pytest.mark.parametrize("d,hq,hkv", [(64, 8, 2), (128, 16, 2)])
+def test_decode_step_balanced_slices(d, hq, hkv):
     # many (sequence, KV head) units: the balanced-slice kernel, whose
-    # workgroups cross units and page kinds
+    # workgroups cross units and page kinds (groups of 4 and of 8)
     rng = np.random.default_rng(5)
     starts = rng.integers(0, 400, size=72).astype(np.int32)
     starts[:4] = [0, 35, 36, 37]
     lens = starts + 6
     lens[9] = 0   # an empty sequence in the batch
-    _run_steps(_wl(64, 8, 2, 4, 32, len(lens), cfg=47), lens, 6, seed=3)
+    _run_steps(_wl(d, hq, hkv, 4, 32, len(lens), cfg=47), lens, 6, seed=3)
 
 
 def test_decode_step_rejects_bad_arguments():

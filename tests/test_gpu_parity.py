@@ -361,7 +361,8 @@ def test_decode_lengths_and_ragged_batch(tiny_rot, lens):
 
 
 @pytest.mark.parametrize("hq,hkv,d,q_scale", [(4, 4, 64, 1.0), (16, 1, 128, 1.0), (12, 1, 128, 8.0),
-                                              (8, 2, 128, 8.0), (3, 1, 64, 1.0)])
+                                              (8, 2, 128, 8.0), (3, 1, 64, 1.0), (8, 1, 64, 1.0),
+                                              (6, 1, 128, 8.0), (5, 1, 64, 8.0), (16, 2, 128, 1.0)])
 def test_decode_group_shapes(hq, hkv, d, q_scale):
     w = synth.Workload("shape", 6, 2, hq, hkv, d, 4, 32, 512, ("fixed", 700, 700), q_scale=q_scale)
     rot = gh.oracle_rotation(w, n_rows=512, q_scale=q_scale)
@@ -475,8 +476,8 @@ def test_decode_on_recycled_pools(tiny_rot, all_raw):
 @pytest.mark.parametrize("hq,hkv,d,L,split", [(4, 1, 64, 9000, 8), (8, 1, 128, 32100, 8), (4, 2, 128, 20000, 8)])
 def test_decode_many_chunks_multipass_merge(hq, hkv, d, L, split):
     # more than 32 records per (sequence, KV head): 70 to 252 INT2 chunks, so
-    # the merge runs several weight passes and value rounds (grouped columns
-    # for G = 4, one column per query for G = 8), against the oracle
+    # the merge runs several weight passes and value rounds (four column
+    # slots per query for G = 4, two for G = 8), against the oracle
     w = synth.Workload("chunks", 6, 1, hq, hkv, d, 4, 128, 512, ("fixed", L, L))
     rot = gh.oracle_rotation(w, n_rows=512)
     inp = synth.decode_inputs(w)
