@@ -244,14 +244,6 @@ struct PairDma {
 // wave (the two pairs being computed and those in flight)
 constexpr int kDepth = kWaves == 8 ? 4 : 2;
 constexpr int kRing = kDepth + 2;
-// floats of the fused step's owner scratch (slice partials, raw rows, decoded
-// k~ and v~, q~, logits and factors, codes, scale/zero words), rounded up
-template <int D>
-constexpr int kOwnFloats = (2 * 16 * D + 2 * D + 2 * D + 16 * D + 48 + D / 2 + 2 * (D / 32) + 3) / 4 * 4;
-// the ring area holds the per-wave results (at most 16 queries), the owner
-// scratch and an INT2 segment's rotated sums
-static_assert((kWaves * 16 * 128 + kOwnFloats<128> + 16 * 128) * 4 <= kWaves * kRing * PairDma<128>::SLOT, "ring area");
-static_assert((kWaves * 16 * 64 + kOwnFloats<64> + 16 * 64) * 4 <= kWaves * kRing * PairDma<64>::SLOT, "ring area");
 
 
 // SLICES: balanced slices over all units (several segments per workgroup),
@@ -287,8 +279,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   uint32_t* s_tabs = reinterpret_cast<uint32_t*>(s_misc + kMisc);  // [kWaves][2][64] page-id blocks
   uint8_t* s_slots = reinterpret_cast<uint8_t*>(s_tabs + kWaves * 2 * 64);
   float* s_res = reinterpret_cast<float*>(s_slots);
-  // s_res: per-wave results [kWaves][G][D]; in the last workgroup: the merge's
-  // record weights and partial reductions
+  // s_res: per-wave results [kWaves][G][D]; in the last workgroup: merged [G][D] rot
+  // and [G][D] raw
 
   const int tid = threadIdx.x, lane = tid & 63, l16 = lane & 15, quad = lane >> 4;
   // wave index in a scalar register: page-table lookups become scalar loads,
@@ -613,9 +605,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
       for (int r = 0; r < 4; ++r) pv[j][r] = __builtin_amdgcn_exp2f(lg[j][r]);
   };
 
-  // R_V rows of output block 16 wave .. 16 wave + 15 (INT2 segments): requested
-  // when the page loop ends, used once the per-wave results are merged
-  f32x4 rva[NKB][2];
   if (is_raw) {
     // ---------------- BF16 chunk: raw q . k, raw-basis value sums ----------------
     if (UPD && (p.W >= 1 || sp.L - 1 < p.S)) {
@@ -892,15 +881,6 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
       }
     }
     wait_vm<0>();  // no ring load lands after the results reuse the ring
-    if (wave < NCB) {
-      const float* rv = p.r_v + size_t(h) * D * D;
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const float* src = rv + size_t(16 * wave + l16) * D + 32 * kb + 8 * quad;
-        rva[kb][0] = *reinterpret_cast<const f32x4*>(src);
-        rva[kb][1] = *reinterpret_cast<const f32x4*>(src + 4);
-      }
-    }
     if (UPD && owner) own_token(qf4);
   }
 
@@ -941,9 +921,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   }
   lds_barrier();
 
-  // ---- workgroup record [m G][l G][value sums G D][chunk kind] -> workspace;
-  // the value sums are in the model basis: an INT2 segment applies R_V^T to
-  // its own sums, so the merge only weights and adds records ----
+  // ---- workgroup record [m G][l G][value sums G D][basis flag] -> workspace ----
   float* rec = p.partials + ((size_t(b) * p.n_kv + h) * p.cap + kseg) * size_t(p.rec_floats);
   if (tid < G) {
     const int cq = CS * tid;  // a column of query tid
@@ -968,49 +946,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   }
   if (UPD && owner) lds_barrier();
   if (tid == 0) st_dev(rec + 2 * G + G * D, is_raw ? 1.f : 0.f);
-  if (ALL_RAW || is_raw) {
-    for (int e = tid; e < G * D; e += kThreads) {
-      float a = 0.f;
+  for (int e = tid; e < G * D; e += kThreads) {
+    float a = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) a += s_res[w * G * D + e];
-      st_dev(rec + 2 * G + e, a);
-    }
-  } else {
-    // rotated sums [G][D] past the per-wave results and the owner scratch
-    float* const s_vsum = reinterpret_cast<float*>(s_slots) + kWaves * 16 * D + kOwnFloats<D>;
-    for (int e = tid; e < G * D; e += kThreads) {
-      float a = 0.f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) a += s_res[w * G * D + e];
-      if (UPD && owner) a = __builtin_fmaf(a, own_l[16 + e / D], own_l[32 + e / D] * own_kv[D + e % D]);
-      s_vsum[e] = a;
-    }
-    lds_barrier();
-    // sums^T[c][n] = sum_k R_V[c][k] rot[n][k]   (bf16 hi/lo splits, 3 MFMAs per
-    // 32 k): wave cb computes channels 16 cb .. 16 cb + 15 of every query
-    if (wave < NCB) {
-      f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        uint32_t ah[4], al[4], bh[4], bl[4];
-        const float* rot_row = s_vsum + qrow * D + 32 * kb + 8 * quad;
-#pragma unroll
-        for (int k = 0; k < 8; k += 2) {
-          split2x2(rva[kb][k / 4][k % 4], rva[kb][(k + 1) / 4][(k + 1) % 4], ah[k / 2], al[k / 2]);
-          split2x2(rot_row[k], rot_row[k + 1], bh[k / 2], bl[k / 2]);
-        }
-        const u32x4 AH{ah[0], ah[1], ah[2], ah[3]}, AL{al[0], al[1], al[2], al[3]};
-        const u32x4 BH{bh[0], bh[1], bh[2], bh[3]}, BL{bl[0], bl[1], bl[2], bl[3]};
-        a4 = mfma_bf16(AL, BH, a4);
-        a4 = mfma_bf16(AH, BL, a4);
-        a4 = mfma_bf16(AH, BH, a4);
-      }
-      if (l16 < G) {
-        float* dst = rec + 2 * G + l16 * D + 16 * wave + 4 * quad;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) st_dev(dst + r, a4[r]);
-      }
-    }
+    for (int w = 0; w < kWaves; ++w) a += s_res[w * G * D + e];
+    if (UPD && owner) a = __builtin_fmaf(a, own_l[16 + e / D], own_l[32 + e / D] * own_kv[D + e % D]);
+    st_dev(rec + 2 * G + e, a);
   }
   // Hand-off to the unit's last workgroup: every thread's record stores are
   // ordered before the barrier, the barrier before thread 0's arrival, a
@@ -1026,26 +967,31 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   if (s_flag[0]) {
 
   // ---- last workgroup: log-sum-exp merge of the chunk records ----
-  // Every record holds model-basis value sums, so with the weights
-  // w_s[n] = 2^(m_s[n] - M[n]) from every record's max and sum
-  //   out = sum_s w_s v_s / sum_s w_s l_s
-  // Loads of maxima, sums and the first values go out together.
+  // The weights w_s[n] = 2^(m_s[n] - M[n]) come first, from every record's
+  // max and sum, so the value sums are added without rescaling:
+  //   out = (R_V^T-rotated sum_s w_s v_s over INT2 chunks + sum_s w_s v_s over
+  //          BF16 chunks) / sum_s w_s l_s
+  // Loads of maxima, sums, flags and the first values go out together, then R_V.
   const int n_s = nseg;
   const float* recs = p.partials + (size_t(b) * p.n_kv + h) * p.cap * size_t(p.rec_floats);
-  float* s_wr = s_res;                       // [kMaxChunks][16] record weights
-  float* s_red = s_wr + kMaxChunks * 16;     // [2][8 waves][16] partial max / sum
+  float* s_wr = s_res;                       // [kMaxChunks][16] weights of INT2 records
+  float* s_wu = s_wr + kMaxChunks * 16;      // [kMaxChunks][16] weights of BF16 records
+  float* s_red = s_wu + kMaxChunks * 16;     // [2][8 waves][16] partial max / sum
+  float* m_rot = s_red + 2 * kWaves * 16;    // [G][D] merged, rotated basis
+  float* m_raw = m_rot + G * D;              // [G][D] merged, model basis
   constexpr int kPass = kMaxChunks * 16 / kThreads;  // (record, row) slots per thread
   const int ms_n = tid & 15;
   const int n_pass = (n_s * 16 + kThreads - 1) / kThreads;  // passes holding real records
-  float cm[kPass], cl[kPass];
+  float cm[kPass], cl[kPass], cf[kPass];
 #pragma unroll
   for (int i = 0; i < kPass; ++i) {  // clamped addresses: every load is in bounds
     cm[i] = kNegInf;
-    cl[i] = 0.f;
+    cl[i] = cf[i] = 0.f;
     if (i < n_pass) {
       const int s = min((tid >> 4) + i * (kThreads / 16), n_s - 1), n = min(ms_n, G - 1);
       cm[i] = ld_dev(recs + size_t(s) * p.rec_floats + n);
       cl[i] = ld_dev(recs + size_t(s) * p.rec_floats + G + n);
+      cf[i] = ld_dev(recs + size_t(s) * p.rec_floats + 2 * G + G * D);
     }
   }
   float vv[kMergeBatch];
@@ -1055,6 +1001,18 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     for (int k = 0; k < kMergeBatch; ++k) vv[k] = ld_dev(recs + size_t(min(s0 + k, n_s - 1)) * p.rec_floats + e);
   };
   load_batch(0, 0);
+  // R_V rows of output block cb = wave, requested after the records (the
+  // weights wait only for the records; R_V is needed last)
+  const float* rv = p.r_v + size_t(h) * D * D;
+  f32x4 rva[NKB][2];
+  if (!ALL_RAW && wave < NCB) {
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+      const float* src = rv + size_t(16 * wave + l16) * D + 32 * kb + 8 * quad;
+      rva[kb][0] = *reinterpret_cast<const f32x4*>(src);
+      rva[kb][1] = *reinterpret_cast<const f32x4*>(src + 4);
+    }
+  }
   float mx = kNegInf;
 #pragma unroll
   for (int i = 0; i < kPass; ++i) {
@@ -1078,7 +1036,8 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     const bool ok = s < n_s && ms_n < G && cm[i] != kNegInf;
     const float wgt = ok ? exp2f(cm[i] - Mn) : 0.f;
     lsum = fmaf(wgt, cl[i], lsum);
-    s_wr[s * 16 + ms_n] = wgt;  // every slot read is written: zero past n_s
+    s_wr[s * 16 + ms_n] = cf[i] != 0.f ? 0.f : wgt;  // every slot read is written: zero past n_s
+    s_wu[s * 16 + ms_n] = cf[i] != 0.f ? wgt : 0.f;
   }
   lsum = wave_sum16(lsum);
   if (quad == 0) s_red[16 * kWaves + wave * 16 + ms_n] = lsum;
@@ -1086,17 +1045,52 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   for (int e0 = 0; e0 < G * D; e0 += kThreads) {
     const int e = e0 + tid;
     const int n = min(e / D, 15);
-    float o = 0.f;
+    float orot = 0.f, oraw = 0.f;
     for (int s0 = 0; s0 < n_s; s0 += kMergeBatch) {
       if (e0 > 0 || s0 > 0) load_batch(e0, s0);
 #pragma unroll
-      for (int k = 0; k < kMergeBatch; ++k) o = fmaf(s_wr[(s0 + k) * 16 + n], vv[k], o);
+      for (int k = 0; k < kMergeBatch; ++k) {
+        orot = fmaf(s_wr[(s0 + k) * 16 + n], vv[k], orot);
+        oraw = fmaf(s_wu[(s0 + k) * 16 + n], vv[k], oraw);
+      }
     }
     if (e < G * D) {
       float Ln = 0.f;
 #pragma unroll
       for (int w = 0; w < kWaves; ++w) Ln += s_red[16 * kWaves + w * 16 + n];
-      p.out[(size_t(b) * p.Hq + h * G) * D + e] = uint16_t(bf16x2_rne(o / Ln, 0.f) & 0xFFFFu);
+      const float inv = 1.f / Ln;
+      m_rot[e] = orot * inv;
+      m_raw[e] = oraw * inv;
+    }
+  }
+  lds_barrier();
+  // out^T[c][n] = raw[n][c] + sum_k R_V[c][k] rot[n][k]   (bf16 hi/lo splits, 3 MFMAs)
+  if (wave < NCB) {
+    f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+    if (!ALL_RAW) {
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        uint32_t ah[4], al[4], bh[4], bl[4];
+        const float* rot_row = m_rot + qrow * D + 32 * kb + 8 * quad;
+#pragma unroll
+        for (int k = 0; k < 8; k += 2) {
+          split2x2(rva[kb][k / 4][k % 4], rva[kb][(k + 1) / 4][(k + 1) % 4], ah[k / 2], al[k / 2]);
+          split2x2(rot_row[k], rot_row[k + 1], bh[k / 2], bl[k / 2]);
+        }
+        const u32x4 AH{ah[0], ah[1], ah[2], ah[3]}, AL{al[0], al[1], al[2], al[3]};
+        const u32x4 BH{bh[0], bh[1], bh[2], bh[3]}, BL{bl[0], bl[1], bl[2], bl[3]};
+        a4 = mfma_bf16(AL, BH, a4);
+        a4 = mfma_bf16(AH, BL, a4);
+        a4 = mfma_bf16(AH, BH, a4);
+      }
+    }
+    if (l16 < G) {
+      uint16_t* o = p.out + (size_t(b) * p.Hq + h * G + l16) * D + 16 * wave + 4 * quad;
+      const float* rw = m_raw + l16 * D + 16 * wave + 4 * quad;
+      u32x2 ov;
+      ov[0] = bf16x2_rne(a4[0] + rw[0], a4[1] + rw[1]);
+      ov[1] = bf16x2_rne(a4[2] + rw[2], a4[3] + rw[3]);
+      *reinterpret_cast<u32x2*>(o) = ov;
     }
   }
   if (tid == 0) __hip_atomic_store(p.counters + b * p.n_kv + h, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1264,7 +1258,7 @@ size_t decode_lds_bytes(int d, int G, bool all_raw) {
   const size_t slot = d == 128 ? PairDma<128>::SLOT : PairDma<64>::SLOT;
   const size_t rings = all_raw ? 0 : size_t(kWaves) * kRing * slot;
   size_t res = size_t(kWaves) * G * d;                              // per-wave results
-  res = std::max(res, size_t(kMaxChunks) * 16 + 2 * kWaves * 16);  // merge
+  res = std::max(res, size_t(kMaxChunks) * 32 + 2 * kWaves * 16 + size_t(2) * G * d);  // merge
   return (size_t(ng) * 256 + 256 + kMisc + kWaves * 2 * 64) * 4 + std::max(rings, res * 4);
 }
 
