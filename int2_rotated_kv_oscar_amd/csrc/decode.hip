@@ -70,15 +70,19 @@ struct DecParams {
   float tau_k, tau_v;
 };
 
-// Waves per workgroup (one workgroup per CU): 8 (two per SIMD, four page
-// pairs in flight per wave) or 12 (three per SIMD, at most 168 VGPRs each,
-// two pairs in flight).  Twelve passes the same tests but measured 10-15%
-// slower on every decode workload, so eight is the build.
+// Waves per workgroup: 8 (one workgroup per CU, two waves per SIMD, four page
+// pairs in flight per wave), 12 (three per SIMD, at most 168 VGPRs each, two
+// pairs in flight) or 4 (two workgroups per CU, each wave rotating and merging
+// two channel blocks).  Twelve passes the same tests but measured 10-15%
+// slower on every decode workload; four (balanced slices over twice the
+// workgroups) was faster on ragged batches of many units but up to 26% slower
+// on uniform long ones, and the better slice costs below made it unnecessary:
+// eight is the build.
 #ifndef OSCAR_DECODE_WAVES
 #define OSCAR_DECODE_WAVES 8
 #endif
 constexpr int kWaves = OSCAR_DECODE_WAVES;
-static_assert(kWaves == 8 || kWaves == 12, "8 or 12 waves per workgroup");
+static_assert(kWaves == 4 || kWaves == 8 || kWaves == 12, "4, 8 or 12 waves per workgroup");
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMergeBatch = kThreads / 16;  // chunk records loaded per merge round
 constexpr int kMaxChunks = 8 * kMergeBatch; // records (segments) per (sequence, KV head)
@@ -87,10 +91,14 @@ constexpr int kMinSlice = 2 * kWaves;       // pages per workgroup slice at leas
 // sum [kWaves][16], flags [16], per-block query sums [8][16]
 constexpr int kMisc = 32 * kWaves + 16 + 128;
 // Balanced slices count each nonempty page range (a unit's BF16 pages, its
-// INT2 pages) as this many extra pages: the fixed cost of a segment
-// (requests, query rotation, record, arrival), about what a CU streams of
-// INT2 pages in that time.  Slices crossing many short units get fewer pages.
-constexpr int kSegPages = 96;
+// INT2 pages) as seg_pages(G) extra pages: the fixed cost of a segment
+// (requests, query rotation, record, arrival, the unit's merge), in INT2 pages
+// a CU streams meanwhile.  It grows with the query group (the rotation, the
+// per-wave results, the record and the merge scale with G); fitted to
+// per-workgroup timestamps of ragged batches: about 160 pages at G = 4 and
+// 224 at G = 12.  Slices crossing many short units get fewer pages.
+__host__ __device__ constexpr int seg_pages(int G) { return 128 + 8 * G; }
+constexpr int kSegPagesMax = seg_pages(16);
 static_assert(kMaxChunks * 16 % kThreads == 0, "merge: (record, query row) slots split evenly over threads");
 constexpr float kTwo24 = 16777216.0f;
 constexpr float kSlack = 4.0f;    // log2 units
@@ -159,7 +167,7 @@ __device__ __forceinline__ SeqPlan make_plan(const DecParams& p, int L) {
   }
   sp.n_raw = (sp.ra1 - sp.ra0) + (sp.rb1 - sp.rb0);
   sp.real = sp.n_raw + (sp.q1 - sp.q0);
-  sp.cost = sp.real + kSegPages * ((sp.n_raw > 0 ? 1 : 0) + (sp.q1 > sp.q0 ? 1 : 0));
+  sp.cost = sp.real + seg_pages(p.G) * ((sp.n_raw > 0 ? 1 : 0) + (sp.q1 > sp.q0 ? 1 : 0));
   return sp;
 }
 
@@ -242,7 +250,7 @@ struct PairDma {
 };
 // page pairs requested ahead of the step being computed, and ring slots per
 // wave (the two pairs being computed and those in flight)
-constexpr int kDepth = kWaves == 8 ? 4 : 2;
+constexpr int kDepth = kWaves <= 8 ? 4 : 2;
 constexpr int kRing = kDepth + 2;
 
 
@@ -262,17 +270,16 @@ constexpr int kRing = kDepth + 2;
 // from the decoded values.  Launched with per-unit items only: balanced
 // slices leave no workgroup the slack to absorb the update's round trips.
 template <int D, bool ALL_RAW, bool SLICES, int CS, bool UPD>
-__global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
+__global__ __launch_bounds__(kThreads, kWaves == 4 ? 2 : 1) void decode_kernel(DecParams p) {
   using GG = Geo<D>;
   constexpr int NG = GG::NG, NCB = GG::NCB, NKB = GG::NKB, HB = GG::HEAD_BYTES;
   extern __shared__ __attribute__((aligned(16))) float smem[];
   const int G = p.G;
-  // LDS: q-hat B operands [NG][64][4] u32 | zero-term operand [64][4] u32 |
-  // misc kMisc floats | page-id blocks | page rings [kWaves][kRing][SLOT], which the per-wave
-  // results and the merge reuse once the page loop is over
+  // LDS: q-hat B operands [NG][64][4] u32 | misc kMisc floats | page-id
+  // blocks | page rings [kWaves][kRing][SLOT], which the per-wave results and
+  // the merge reuse once the page loop is over
   uint32_t* s_qhat = reinterpret_cast<uint32_t*>(smem);
-  uint32_t* s_qz = s_qhat + NG * 256;
-  float* s_misc = reinterpret_cast<float*>(s_qz + 256);
+  float* s_misc = reinterpret_cast<float*>(s_qhat + NG * 256);
   float* s_m = s_misc;                // [kWaves][16] per-wave max
   float* s_l = s_misc + 16 * kWaves;  // [kWaves][16] per-wave sum
   int* s_flag = reinterpret_cast<int*>(s_misc + 32 * kWaves);  // [16]
@@ -313,8 +320,13 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   // such pages are never used unmasked. ----
   using PD = PairDma<D>;
   uint8_t* const ring = s_slots + wave * kRing * PD::SLOT;
+  // 16-channel blocks of the query rotation and of the merge's R_V^T: block
+  // cb = wave + kWaves j (j < NB) when there are fewer waves than blocks;
+  // with more waves, waves past NCB repeat a block and keep no result
+  constexpr int NB = NCB > kWaves ? NCB / kWaves : 1;
+  static_assert(NB * kWaves >= NCB && (NCB <= kWaves || NCB % kWaves == 0), "blocks over waves");
   const bool rot_wave = wave < NCB;
-  float rvals[NKB][8];
+  float rvals[NB][NKB][8];
   u32x4 bqv[NKB];
   int sc0 = 0;  // first page of the segment the requests are for
   // Page ids of this wave's pairs, 32 pairs per register block: lane L holds
@@ -356,9 +368,12 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     {  // every wave loads (waves past NCB repeat a block) so that no path leaves them unset
       const float* rk = p.r_k + size_t(h) * D * D;
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb)
+      for (int j = 0; j < NB; ++j)
 #pragma unroll
-        for (int i = 0; i < 8; ++i) rvals[kb][i] = rk[size_t(32 * kb + 8 * quad + i) * D + 16 * (wave & (NCB - 1)) + l16];
+        for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            rvals[j][kb][i] = rk[size_t(32 * kb + 8 * quad + i) * D + 16 * ((wave + kWaves * j) & (NCB - 1)) + l16];
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) bqv[kb] = *reinterpret_cast<const u32x4*>(qb + size_t(qcol) * D + 32 * kb + 8 * quad);
     }
@@ -409,7 +424,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   // enters the middle history this step) and handles it apart from its loop
   const bool owner = UPD && !is_raw && sp.m1 > sp.m0 && ((sp.m1 - 1) >> 4) >= c0 && ((sp.m1 - 1) >> 4) < c1;
   const int m0 = sp.m0, m1 = owner ? sp.m1 - 1 : sp.m1, s1 = sp.s1, r0 = sp.r0;
-  float qf4[4] = {0.f, 0.f, 0.f, 0.f};  // fused step: this lane's q~ block (log2 units)
+  float qf4[NB][4] = {};  // fused step: this lane's q~ blocks (log2 units)
   // Owner scratch past the per-wave results (kWaves x 16 queries x D floats)
   // in the ring area, free once the page loop is over: slice partials
   // [2][16][D], raw rows [2][D], decoded rotated k~, v~ [2][D], q~ [16][D],
@@ -423,7 +438,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   float* const own_l = own_q + 16 * D;
   uint8_t* const own_code = reinterpret_cast<uint8_t*>(own_l + 48);
   uint16_t* const own_sz = reinterpret_cast<uint16_t*>(own_code + 2 * D);  // [tensor][g][scale, zero]
-  auto own_token = [&](const float (&qv)[4]) __attribute__((always_inline)) {
+  auto own_token = [&](const float (&qv)[NB][4]) __attribute__((always_inline)) {
     const int t = sp.m1 - 1;           // the token entering the middle history
     const int slot = t & 15;
     const size_t row = (size_t(b) * p.n_kv + h) * D;
@@ -459,7 +474,9 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     if (rot_wave && l16 % CS == 0 && l16 / CS < G) {
       const int qi = l16 / CS;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) own_q[qi * D + 16 * wave + 4 * quad + r] = qv[r];
+      for (int j = 0; j < NB; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) own_q[qi * D + 16 * (wave + kWaves * j) + 4 * quad + r] = qv[j][r];
     }
     __syncthreads();
 #pragma unroll
@@ -698,31 +715,34 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
     }
     const int n_mine = n_pairs > wave ? (n_pairs - wave + kWaves - 1) / kWaves : 0;
     // the rotation of the query runs while the first page pairs are in flight:
-    // wave w rotates the 16-channel block cb = w (group w/2, half w%2) with a
+    // the wave of 16-channel block cb (group cb/2, half cb%2) rotates it with a
     // bf16 hi/lo split of R_K (16 significant bits; q~ is rounded to f16 afterwards)
     float* s_qsp = s_misc + 32 * kWaves + 16;  // [NCB][16] per-block query sums
     wait_vm<kDepth * PD::LOADS + 1>();  // the rotation operands (older than the page-id block and pages)
     if (rot_wave) {
-      const int g = wave >> 1, hb = wave & 1;
-      f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        uint32_t ph[4], pl[4];
+      for (int j = 0; j < NB; ++j) {
+        const int cb = wave + kWaves * j, g = cb >> 1, hb = cb & 1;
+        f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 8; i += 2) split2x2(rvals[kb][i], rvals[kb][i + 1], ph[i / 2], pl[i / 2]);
-        a4 = mfma_bf16(u32x4{pl[0], pl[1], pl[2], pl[3]}, bqv[kb], a4);
-        a4 = mfma_bf16(u32x4{ph[0], ph[1], ph[2], ph[3]}, bqv[kb], a4);
+        for (int kb = 0; kb < NKB; ++kb) {
+          uint32_t ph[4], pl[4];
+#pragma unroll
+          for (int i = 0; i < 8; i += 2) split2x2(rvals[j][kb][i], rvals[j][kb][i + 1], ph[i / 2], pl[i / 2]);
+          a4 = mfma_bf16(u32x4{pl[0], pl[1], pl[2], pl[3]}, bqv[kb], a4);
+          a4 = mfma_bf16(u32x4{ph[0], ph[1], ph[2], ph[3]}, bqv[kb], a4);
+        }
+        // a4[r] = q~[n = l16][c = 32g + 16hb + 4quad + r]; K-slot (e = 2hb + r/2, half r%2)
+        const float v0 = a4[0] * qscale, v1 = a4[1] * qscale, v2 = a4[2] * qscale, v3 = a4[3] * qscale;
+        if (UPD) {
+          qf4[j][0] = v0; qf4[j][1] = v1; qf4[j][2] = v2; qf4[j][3] = v3;
+        }
+        const float f0 = hb ? 1.f / 16.f : 1.f, f1 = hb ? 1.f / 64.f : 1.f / 4.f;
+        s_qhat[(g * 64 + lane) * 4 + 2 * hb] = pack_f16x2(v0 * f0, v1 * f0);
+        s_qhat[(g * 64 + lane) * 4 + 2 * hb + 1] = pack_f16x2(v2 * f1, v3 * f1);
+        const float qs = wave_sum16((v0 + v1) + (v2 + v3));
+        if (quad == 0) s_qsp[cb * 16 + l16] = qs;
       }
-      // a4[r] = q~[n = l16][c = 32g + 16hb + 4quad + r]; K-slot (e = 2hb + r/2, half r%2)
-      const float v0 = a4[0] * qscale, v1 = a4[1] * qscale, v2 = a4[2] * qscale, v3 = a4[3] * qscale;
-      if (UPD) {
-        qf4[0] = v0; qf4[1] = v1; qf4[2] = v2; qf4[3] = v3;
-      }
-      const float f0 = hb ? 1.f / 16.f : 1.f, f1 = hb ? 1.f / 64.f : 1.f / 4.f;
-      s_qhat[(g * 64 + lane) * 4 + 2 * hb] = pack_f16x2(v0 * f0, v1 * f0);
-      s_qhat[(g * 64 + lane) * 4 + 2 * hb + 1] = pack_f16x2(v2 * f1, v3 * f1);
-      const float qs = wave_sum16((v0 + v1) + (v2 + v3));
-      if (quad == 0) s_qsp[wave * 16 + l16] = qs;
     }
     lds_barrier();
     // zero-term B operand: K-slots of quad 0 carry the per-group query sums
@@ -1004,14 +1024,16 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   // R_V rows of output block cb = wave, requested after the records (the
   // weights wait only for the records; R_V is needed last)
   const float* rv = p.r_v + size_t(h) * D * D;
-  f32x4 rva[NKB][2];
+  f32x4 rva[NB][NKB][2];
   if (!ALL_RAW && wave < NCB) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) {
-      const float* src = rv + size_t(16 * wave + l16) * D + 32 * kb + 8 * quad;
-      rva[kb][0] = *reinterpret_cast<const f32x4*>(src);
-      rva[kb][1] = *reinterpret_cast<const f32x4*>(src + 4);
-    }
+    for (int j = 0; j < NB; ++j)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const float* src = rv + size_t(16 * (wave + kWaves * j) + l16) * D + 32 * kb + 8 * quad;
+        rva[j][kb][0] = *reinterpret_cast<const f32x4*>(src);
+        rva[j][kb][1] = *reinterpret_cast<const f32x4*>(src + 4);
+      }
   }
   float mx = kNegInf;
 #pragma unroll
@@ -1066,31 +1088,35 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
   lds_barrier();
   // out^T[c][n] = raw[n][c] + sum_k R_V[c][k] rot[n][k]   (bf16 hi/lo splits, 3 MFMAs)
   if (wave < NCB) {
-    f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
-    if (!ALL_RAW) {
 #pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        uint32_t ah[4], al[4], bh[4], bl[4];
-        const float* rot_row = m_rot + qrow * D + 32 * kb + 8 * quad;
+    for (int j = 0; j < NB; ++j) {
+      const int cb = wave + kWaves * j;
+      f32x4 a4 = {0.f, 0.f, 0.f, 0.f};
+      if (!ALL_RAW) {
 #pragma unroll
-        for (int k = 0; k < 8; k += 2) {
-          split2x2(rva[kb][k / 4][k % 4], rva[kb][(k + 1) / 4][(k + 1) % 4], ah[k / 2], al[k / 2]);
-          split2x2(rot_row[k], rot_row[k + 1], bh[k / 2], bl[k / 2]);
+        for (int kb = 0; kb < NKB; ++kb) {
+          uint32_t ah[4], al[4], bh[4], bl[4];
+          const float* rot_row = m_rot + qrow * D + 32 * kb + 8 * quad;
+#pragma unroll
+          for (int k = 0; k < 8; k += 2) {
+            split2x2(rva[j][kb][k / 4][k % 4], rva[j][kb][(k + 1) / 4][(k + 1) % 4], ah[k / 2], al[k / 2]);
+            split2x2(rot_row[k], rot_row[k + 1], bh[k / 2], bl[k / 2]);
+          }
+          const u32x4 AH{ah[0], ah[1], ah[2], ah[3]}, AL{al[0], al[1], al[2], al[3]};
+          const u32x4 BH{bh[0], bh[1], bh[2], bh[3]}, BL{bl[0], bl[1], bl[2], bl[3]};
+          a4 = mfma_bf16(AL, BH, a4);
+          a4 = mfma_bf16(AH, BL, a4);
+          a4 = mfma_bf16(AH, BH, a4);
         }
-        const u32x4 AH{ah[0], ah[1], ah[2], ah[3]}, AL{al[0], al[1], al[2], al[3]};
-        const u32x4 BH{bh[0], bh[1], bh[2], bh[3]}, BL{bl[0], bl[1], bl[2], bl[3]};
-        a4 = mfma_bf16(AL, BH, a4);
-        a4 = mfma_bf16(AH, BL, a4);
-        a4 = mfma_bf16(AH, BH, a4);
       }
-    }
-    if (l16 < G) {
-      uint16_t* o = p.out + (size_t(b) * p.Hq + h * G + l16) * D + 16 * wave + 4 * quad;
-      const float* rw = m_raw + l16 * D + 16 * wave + 4 * quad;
-      u32x2 ov;
-      ov[0] = bf16x2_rne(a4[0] + rw[0], a4[1] + rw[1]);
-      ov[1] = bf16x2_rne(a4[2] + rw[2], a4[3] + rw[3]);
-      *reinterpret_cast<u32x2*>(o) = ov;
+      if (l16 < G) {
+        uint16_t* o = p.out + (size_t(b) * p.Hq + h * G + l16) * D + 16 * cb + 4 * quad;
+        const float* rw = m_raw + l16 * D + 16 * cb + 4 * quad;
+        u32x2 ov;
+        ov[0] = bf16x2_rne(a4[0] + rw[0], a4[1] + rw[1]);
+        ov[1] = bf16x2_rne(a4[2] + rw[2], a4[3] + rw[3]);
+        *reinterpret_cast<u32x2*>(o) = ov;
+      }
     }
   }
   if (tid == 0) __hip_atomic_store(p.counters + b * p.n_kv + h, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1132,7 +1158,7 @@ __global__ __launch_bounds__(kThreads, 1) void decode_kernel(DecParams p) {
             x == 0 ? 0 : has_raw + x - 1);
   } else {
   // Balanced slices (many units): the units, sequence-major, put their work
-  // (BF16 sink and recent pages, INT2 pages, then kSegPages positions per
+  // (BF16 sink and recent pages, INT2 pages, then seg_pages(G) positions per
   // nonempty range that hold no pages) in one row; workgroup wg takes the
   // slice [wg ppw, wg ppw + ppw) of it.  A segment is the part of a slice
   // inside one unit and one page kind; each leaves one record, and the unit's
@@ -1251,7 +1277,7 @@ int decode_max_records() { return kMaxChunks; }
 
 int decode_min_slice() { return kMinSlice; }
 
-int decode_seg_pages() { return kSegPages; }
+int decode_seg_pages() { return kSegPagesMax; }
 
 size_t decode_lds_bytes(int d, int G, bool all_raw) {
   const int ng = d / 32;
@@ -1259,7 +1285,7 @@ size_t decode_lds_bytes(int d, int G, bool all_raw) {
   const size_t rings = all_raw ? 0 : size_t(kWaves) * kRing * slot;
   size_t res = size_t(kWaves) * G * d;                              // per-wave results
   res = std::max(res, size_t(kMaxChunks) * 32 + 2 * kWaves * 16 + size_t(2) * G * d);  // merge
-  return (size_t(ng) * 256 + 256 + kMisc + kWaves * 2 * 64) * 4 + std::max(rings, res * 4);
+  return (size_t(ng) * 256 + kMisc + kWaves * 2 * 64) * 4 + std::max(rings, res * 4);
 }
 
 hipError_t paged_decode(int d, bool all_raw, const void* int2_pool, int n_int2_pages, const void* bf16_pool, int n_kv, int G, int S,

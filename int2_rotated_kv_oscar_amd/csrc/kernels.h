@@ -26,7 +26,7 @@ hipError_t calib_gram(int d, const void* x, int64_t n_rows, int n_x_heads, int n
 size_t decode_lds_bytes(int d, int G, bool all_raw);
 int decode_max_records();  // record slots per (sequence, KV head) the merge can hold
 int decode_min_slice();    // pages per workgroup slice at least
-int decode_seg_pages();    // extra positions per nonempty page range in balanced slices
+int decode_seg_pages();    // extra positions per nonempty page range in balanced slices (at most)
 
 // k_new != nullptr: the fused decode step (the step's cache update in the same launch)
 hipError_t paged_decode(int d, bool all_raw, const void* int2_pool, int n_int2_pages, const void* bf16_pool, int n_kv, int G, int S,
