@@ -310,11 +310,11 @@ def main() -> int:
     tokens = int(inp.seq_lens.sum())
     value = tokens / (ms_step * 1e-3)
     step_bytes = nbytes["total"] + upd_bytes
-    # the library fuses the update into the decode launch under the per-unit
-    # plan (split_pages given, or units at most a quarter of the CUs); with
-    # more units the step is the update kernel, then the decode
+    # the library fuses the update into the decode launch with split_pages
+    # given or at most as many (sequence, KV head) units as CUs; with more
+    # units the step is the update kernel, then the decode
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    fused = args.split_pages != 0 or 4 * B * w.n_kv_heads <= cus
+    fused = args.split_pages != 0 or B * w.n_kv_heads <= cus
     log(f"step ({'one fused launch' if fused else 'update + decode launches'}) {ms_step * 1e3:.1f} us, "
         f"{step_bytes / (ms_step * 1e-3) / 1e9:.0f} GB/s, bytes {nbytes} + update {upd_bytes}")
 

@@ -376,15 +376,14 @@ oscar_status oscar_paged_decode_attn(const oscar_cache* cache, const void* q,
  * max_pages, r_k, r_v, tau_k, tau_v) followed by
  * oscar_paged_decode_attn(cache, q, ...) with the same arguments, so the
  * cache afterwards holds the same bytes and the output meets the same
- * definition.  With few (sequence, KV head) units (the plan that gives each
- * unit several workgroups: split_pages set, or units at most a quarter of
- * the compute units) it is one launch: the workgroup that reads the new
- * token's BF16 page writes it there first, and the workgroup that reads the
- * last middle page quantizes the token entering the middle history, writes
- * it to its INT2 slot and attends to it from the decoded values (its slot in
- * the page is not read).  With more units it launches the update kernel,
- * then the decode, on the same stream.  Arguments, workspace rules,
- * preconditions and errors as the two calls. */
+ * definition.  With at most as many (sequence, KV head) units as compute
+ * units it is one launch: the workgroup that reads the new token's BF16 page
+ * writes it there first, and the workgroup that reads the last middle page
+ * quantizes the token entering the middle history, writes it to its INT2
+ * slot and attends to it from the decoded values (its slot in the page is
+ * not read).  With more units it launches the update kernel, then the
+ * decode, on the same stream.  Arguments, workspace rules, preconditions and
+ * errors as the two calls. */
 oscar_status oscar_decode_step(const oscar_cache* cache, const void* k_new, const void* v_new,
                                const void* q, int32_t batch, int32_t n_q_heads,
                                const int32_t* seq_lens, int32_t max_seq_len,

@@ -98,7 +98,7 @@ oscar_status plan_decode(int32_t batch, int32_t n_kv, int32_t n_q, int32_t d, in
     return fail(OSCAR_ERR_INVALID_ARG, "split_pages must be 0 or a multiple of 8 in [8, 2^20]");
   const long long units = (long long)batch * n_kv;
   const long long max_pages = (max_seq_len + 15LL) / 16;
-  const long long max_cost = max_pages + 2 + 2LL * oscar_launch::decode_seg_pages();
+  const long long max_cost = max_pages + 2 + 2LL * oscar_launch::decode_seg_pages() + oscar_launch::decode_own_pages();
   if (units * max_cost >= (1LL << 31)) return fail(OSCAR_ERR_UNSUPPORTED, "2^31 or more pages of work in one call; split the batch");
   const int max_rec = oscar_launch::decode_max_records();
   const long long cus = device_cu_count();
@@ -539,10 +539,11 @@ oscar_status oscar_decode_step(const oscar_cache* cache, const void* k_new, cons
   if (workspace_bytes < plan.bytes) return fail(OSCAR_ERR_WORKSPACE, "workspace smaller than oscar_decode_workspace_bytes");
   int32_t* counters = static_cast<int32_t*>(workspace);
   float* partials = reinterpret_cast<float*>(static_cast<char*>(workspace) + plan.counter_bytes);
-  if (!plan.per_unit) {
-    // Many units (balanced slices, one workgroup per CU with no slack): the
-    // update's round trips to memory would stall the workgroups that hold
-    // it, so the few-row update kernel runs first and the decode after it.
+  if (!plan.per_unit && (long long)batch * cache->n_kv_heads > device_cu_count()) {
+    // Balanced slices over more units than CUs: a fused launch would give
+    // every workgroup several quantized tokens, each a chain of round trips
+    // to memory inside the workgroup; the few-row update kernel does them all
+    // in parallel first (measured faster from 512 units on), then the decode.
     if (oscar_status s = hip_status(
             oscar_launch::decode_step_update(cache->d, cache->n_kv_heads, cache->n_sink, cache->n_recent,
                                              cache->int2_pool, cache->bf16_pool, k_new, v_new, batch, seq_lens,
@@ -553,6 +554,8 @@ oscar_status oscar_decode_step(const oscar_cache* cache, const void* k_new, cons
     return oscar::decode_launch(false, cache, q, batch, n_q_heads, seq_lens, max_seq_len, bt_q, bt_h, max_pages,
                                 r_k, r_v, sm_scale, plan, counters, partials, out, stream);
   }
+  // one launch (per-unit items, or balanced slices that count each unit's
+  // quantized token in its row)
   return oscar::decode_launch(false, cache, q, batch, n_q_heads, seq_lens, max_seq_len, bt_q, bt_h, max_pages, r_k,
                               r_v, sm_scale, plan, counters, partials, out, stream, k_new, v_new, tau_k, tau_v);
 }

@@ -99,6 +99,11 @@ constexpr int kMisc = 32 * kWaves + 16 + 128;
 // 224 at G = 12.  Slices crossing many short units get fewer pages.
 __host__ __device__ constexpr int seg_pages(int G) { return 128 + 8 * G; }
 constexpr int kSegPagesMax = seg_pages(16);
+// In a fused decode step the segment holding a unit's last middle page also
+// quantizes the token entering the middle history (its rotation slices, raw
+// row and INT2 slot: about two round trips to memory): that unit's row
+// counts this many more positions.
+constexpr int kOwnPages = 80;
 static_assert(kMaxChunks * 16 % kThreads == 0, "merge: (record, query row) slots split evenly over threads");
 constexpr float kTwo24 = 16777216.0f;
 constexpr float kSlack = 4.0f;    // log2 units
@@ -167,7 +172,8 @@ __device__ __forceinline__ SeqPlan make_plan(const DecParams& p, int L) {
   }
   sp.n_raw = (sp.ra1 - sp.ra0) + (sp.rb1 - sp.rb0);
   sp.real = sp.n_raw + (sp.q1 - sp.q0);
-  sp.cost = sp.real + seg_pages(p.G) * ((sp.n_raw > 0 ? 1 : 0) + (sp.q1 > sp.q0 ? 1 : 0));
+  sp.cost = sp.real + seg_pages(p.G) * ((sp.n_raw > 0 ? 1 : 0) + (sp.q1 > sp.q0 ? 1 : 0)) +
+            (p.k_new != nullptr && sp.m1 > sp.m0 ? kOwnPages : 0);
   return sp;
 }
 
@@ -1279,6 +1285,8 @@ int decode_min_slice() { return kMinSlice; }
 
 int decode_seg_pages() { return kSegPagesMax; }
 
+int decode_own_pages() { return kOwnPages; }
+
 size_t decode_lds_bytes(int d, int G, bool all_raw) {
   const int ng = d / 32;
   const size_t slot = d == 128 ? PairDma<128>::SLOT : PairDma<64>::SLOT;
@@ -1307,8 +1315,8 @@ hipError_t paged_decode(int d, bool all_raw, const void* int2_pool, int n_int2_p
 #define OSCAR_DECODE_LAUNCH(DD, RAW, GCOL)                                                                              \
   do {                                                                                                                 \
     if (upd && !RAW) {                                                                                                 \
-      if (!per_unit) return hipErrorInvalidValue;                                                                      \
-      hipLaunchKernelGGL((decode_kernel<DD, RAW, false, GCOL, !RAW>), grid, dim3(kThreads), lds, stream, p);           \
+      if (per_unit) hipLaunchKernelGGL((decode_kernel<DD, RAW, false, GCOL, !RAW>), grid, dim3(kThreads), lds, stream, p); \
+      else hipLaunchKernelGGL((decode_kernel<DD, RAW, true, GCOL, !RAW>), grid, dim3(kThreads), lds, stream, p);           \
     } else {                                                                                                           \
       if (per_unit) hipLaunchKernelGGL((decode_kernel<DD, RAW, false, GCOL, false>), grid, dim3(kThreads), lds, stream, p); \
       else hipLaunchKernelGGL((decode_kernel<DD, RAW, true, GCOL, false>), grid, dim3(kThreads), lds, stream, p);           \

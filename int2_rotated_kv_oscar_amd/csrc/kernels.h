@@ -27,6 +27,7 @@ size_t decode_lds_bytes(int d, int G, bool all_raw);
 int decode_max_records();  // record slots per (sequence, KV head) the merge can hold
 int decode_min_slice();    // pages per workgroup slice at least
 int decode_seg_pages();    // extra positions per nonempty page range in balanced slices (at most)
+int decode_own_pages();    // extra positions of a unit whose fused step quantizes a token
 
 // k_new != nullptr: the fused decode step (the step's cache update in the same launch)
 hipError_t paged_decode(int d, bool all_raw, const void* int2_pool, int n_int2_pages, const void* bf16_pool, int n_kv, int G, int S,

@@ -139,10 +139,12 @@ def test_decode_step_shapes(d, hq, hkv, S, W, split):
                seed=d + W)
 
 
-@pytest.mark.parametrize("d,hq,hkv", [(64, 8, 2), (128, 16, 2)])
+@pytest.mark.parametrize("d,hq,hkv", [(64, 8, 2), (128, 16, 2), (64, 16, 8)])
 def test_decode_step_balanced_slices(d, hq, hkv):
     # many (sequence, KV head) units: the balanced-slice kernel, whose
-    # workgroups cross units and page kinds (groups of 4 and of 8)
+    # workgroups cross units and page kinds (groups of 4 and of 8); 144 units
+    # take the fused launch, 576 units (more than the CUs) the update kernel
+    # and then the decode
     rng = np.random.default_rng(5)
     starts = rng.integers(0, 400, size=72).astype(np.int32)
     starts[:4] = [0, 35, 36, 37]
