@@ -808,10 +808,12 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
 // rotation: M = max_k m_k, w_k = 2^(m_k - M),
 // out = (sum_k w_k raw_k + (sum_k w_k rot_k) R_V^T) / sum_k w_k l_k.
 // One workgroup per (unit, column tile, column).  Its R_V entries (output
-// channel c = tid / TPC, a KPT-long run of k) and the first sixteen records'
+// channel c = tid / TPC, a KPT-long run of k) and the first LB records'
 // values of each wave are requested first, so they arrive while the maxima
 // and sums are reduced; the four waves take every fourth chunk (a lane holds
-// FPL of the 2d value sums, sixteen chunks' loads in flight) and meet in LDS.
+// FPL of the 2d value sums, LB chunks' loads in flight) and meet in LDS.
+// LB = 32 for the decode (about 3 CUs of chunks per column: one batch per
+// wave), 16 for extend (many more merge workgroups, fewer registers).
 template <int D, int NC, int MODE>
 __global__ __launch_bounds__(256) void attend_merge_kernel(AttParams p) {
   constexpr int RF = 4 + 2 * D, NWM = 4, FPL = 2 * D / 64;  // waves, value floats per lane
@@ -837,15 +839,16 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttParams p) {
   f32x4 rr[KPT / 4];
 #pragma unroll
   for (int i = 0; i < KPT / 4; ++i) rr[i] = *reinterpret_cast<const f32x4*>(rrow + 4 * i);
-  // this wave's chunks k = wave + NWM t, t < nt, sixteen at a time (indices
-  // clamped into the records; the first sixteen requested before the weights,
+  // this wave's chunks k = wave + NWM t, t < nt, LB at a time (indices
+  // clamped into the records; the first LB requested before the weights,
   // which they do not need)
+  constexpr int LB = MODE == 1 ? 32 : 16;
   const float* vb = rec0 + 4 + FPL * lane;
   const int nt = (nk - wave + NWM - 1) / NWM;
-  float v[16][FPL];
-  auto load16 = [&](int t0) {
+  float v[LB][FPL];
+  auto load_batch = [&](int t0) {
 #pragma unroll
-    for (int t = 0; t < 16; ++t) {
+    for (int t = 0; t < LB; ++t) {
       const int kk = min(wave + NWM * (t0 + t), nk - 1);
       if constexpr (FPL == 4) {
         const f32x4 x = *reinterpret_cast<const f32x4*>(vb + kk * cstride);
@@ -858,7 +861,7 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttParams p) {
       }
     }
   };
-  load16(0);
+  load_batch(0);
   // maxima and sums: thread k holds chunk k's (first 256 chunks)
   float m0 = kNegInfA, l0 = 0.f;
   if (tid < nk) {
@@ -892,10 +895,10 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttParams p) {
   float a[FPL];
 #pragma unroll
   for (int f = 0; f < FPL; ++f) a[f] = 0.f;
-  for (int t0 = 0; t0 < nt; t0 += 16) {
-    if (t0 > 0) load16(t0);
+  for (int t0 = 0; t0 < nt; t0 += LB) {
+    if (t0 > 0) load_batch(t0);
 #pragma unroll
-    for (int t = 0; t < 16; ++t)
+    for (int t = 0; t < LB; ++t)
       if (t0 + t < nt)
 #pragma unroll
         for (int f = 0; f < FPL; ++f) a[f] = __builtin_fmaf(s_w[wave + NWM * (t0 + t)], v[t][f], a[f]);
