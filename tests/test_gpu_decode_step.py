@@ -30,11 +30,17 @@ pytestmark = pytest.mark.gpu
 
 def _full_tables(inp: synth.DecodeInputs, seed: int) -> synth.DecodeInputs:
     """Every logical page of every sequence mapped in both pools (the region
-    of a position changes from step to step), each pool a seeded permutation."""
+    of a position changes from step to step), each pool a seeded permutation;
+    the pages of a shared prefix stay shared (every sequence maps them to
+    sequence 0's pages, which the fill writes once)."""
     B, mp = inp.bt_q.shape
     rng = np.random.default_rng(seed)
     bt_q = rng.permutation(B * mp).astype(np.int32).reshape(B, mp)
     bt_h = rng.permutation(B * mp).astype(np.int32).reshape(B, mp)
+    pre_pages = inp.w.shared_prefix // 16
+    if pre_pages:
+        bt_q[:, :pre_pages] = bt_q[0, :pre_pages]
+        bt_h[:, :pre_pages] = bt_h[0, :pre_pages]
     return dataclasses.replace(inp, bt_q=bt_q, bt_h=bt_h, n_int2_pages=B * mp, n_bf16_pages=B * mp)
 
 
@@ -263,3 +269,9 @@ def test_decode_step_full_size_bench_config():
 def test_decode_step_full_size_qwen3_32b_b4_128k():
     # four 128k sequences, 8 queries per KV head (one fused launch per step)
     _run_full_size_steps("qwen3-32b-b4-128k", 1, [1])
+
+
+def test_decode_step_full_size_qwen3_8b_b28_ragged():
+    # 28 ragged sequences with a shared prefix: balanced slices over 224
+    # units, one fused launch per step
+    _run_full_size_steps("qwen3-8b-b28-ragged", 2, [0, 13])
