@@ -35,6 +35,19 @@ using namespace oscar_dev;
 namespace {
 
 typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// bf16 pair of (a, b), element 0 in the low half, rounded to nearest even by
+// the packed hardware conversion (one instruction per pair; the same bits as
+// the scalar rounding for finite values)
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{a, b}, bf16x2));
+}
+// (a, b) = hi + lo, each a bf16 pair, to 16 significant bits
+__device__ __forceinline__ void split2x2(float a, float b, uint32_t& hi, uint32_t& lo) {
+  hi = bf16x2_rne(a, b);
+  lo = bf16x2_rne(a - __uint_as_float(hi << 16), b - __uint_as_float(hi & 0xFFFF0000u));
+}
 
 constexpr float kNegInfA = -__builtin_inff();
 constexpr float kSlackA = 4.0f;  // log2 units
@@ -497,11 +510,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
         for (int kb = 0; kb < NKB; ++kb) {
           uint32_t ph[4], pl[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const float a = rv[j][kb][2 * i], b2 = rv[j][kb][2 * i + 1];
-            ph[i] = pack2(bf16_rne(a), bf16_rne(b2));
-            pl[i] = pack2(bf16_rne(a - bf16_to_f32(ph[i] & 0xFFFFu)), bf16_rne(b2 - bf16_to_f32(ph[i] >> 16)));
-          }
+          for (int i = 0; i < 4; ++i) split2x2(rv[j][kb][2 * i], rv[j][kb][2 * i + 1], ph[i], pl[i]);
           rah[j][kb] = u32x4{ph[0], ph[1], ph[2], ph[3]};
           ral[j][kb] = u32x4{pl[0], pl[1], pl[2], pl[3]};
         }
@@ -644,11 +653,7 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
       } else {
         uint32_t ph[4], pl[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float a = pv[i >> 1][2 * (i & 1)], e = pv[i >> 1][2 * (i & 1) + 1];
-          ph[i] = pack2(bf16_rne(a), bf16_rne(e));
-          pl[i] = pack2(bf16_rne(a - bf16_to_f32(ph[i] & 0xFFFFu)), bf16_rne(e - bf16_to_f32(ph[i] >> 16)));
-        }
+        for (int i = 0; i < 4; ++i) split2x2(pv[i >> 1][2 * (i & 1)], pv[i >> 1][2 * (i & 1) + 1], ph[i], pl[i]);
         bph[c] = u32x4{ph[0], ph[1], ph[2], ph[3]};
         bpl[c] = u32x4{pl[0], pl[1], pl[2], pl[3]};
       }
@@ -698,6 +703,8 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
           const float rav[8] = {ra0[0], ra0[1], ra0[2], ra0[3], ra1[0], ra1[1], ra1[2], ra1[3]};
           uint32_t ah[4], al[4], bh[4], bl[4];
 #pragma unroll
+          // scalar splits here: with the packed conversion the register
+          // allocator spills the extend kernel (measured 5x slower)
           for (int i = 0; i < 4; ++i) {
             ah[i] = pack2(bf16_rne(rav[2 * i]), bf16_rne(rav[2 * i + 1]));
             al[i] = pack2(bf16_rne(rav[2 * i] - bf16_to_f32(ah[i] & 0xFFFFu)), bf16_rne(rav[2 * i + 1] - bf16_to_f32(ah[i] >> 16)));
@@ -797,8 +804,8 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       u32x2 ov;
-      ov[0] = pack2(bf16_rne(acc[c][cb][0] * inv), bf16_rne(acc[c][cb][1] * inv));
-      ov[1] = pack2(bf16_rne(acc[c][cb][2] * inv), bf16_rne(acc[c][cb][3] * inv));
+      ov[0] = bf16x2_rne(acc[c][cb][0] * inv, acc[c][cb][1] * inv);
+      ov[1] = bf16x2_rne(acc[c][cb][2] * inv, acc[c][cb][3] * inv);
       *reinterpret_cast<u32x2*>(orow + 16 * cb + 4 * quad) = ov;
     }
   }
