@@ -610,6 +610,35 @@ def test_decode_balanced_slices_many_units(tiny_rot):
             gh.assert_attention_close(got[b], ref[b], f"seq {b} len {L}")
 
 
+@pytest.mark.parametrize("d,hq,hkv,mode", [(128, 16, 1, "uniform"), (128, 12, 2, "skewed"), (64, 8, 2, "skewed")])
+def test_decode_balanced_slices_groups_and_skew(d, hq, hkv, mode):
+    # balanced slices with the largest query group (16: the biggest per-range
+    # overhead), a group of 6 (two column slots), and a skewed batch (one
+    # sequence far longer than the rest, so the slice width is set by how many
+    # records a unit may leave rather than by the even share), every sequence
+    # against the oracle over the pages the GPU wrote
+    from oracle import attention as oatt
+    rng = np.random.default_rng(13 + d + hq)
+    if mode == "uniform":
+        lens = rng.integers(1, 700, size=70)
+    else:
+        lens = rng.integers(1, 200, size=40)
+        lens[7] = 20000
+    w = synth.Workload("slices", 21, len(lens), hq, hkv, d, 4, 32, 512, ("fixed", 1, 1))
+    rot = gh.oracle_rotation(w, n_rows=512)
+    inp = synth.decode_inputs(w, seq_lens=lens)
+    gc = gh.alloc_cache(inp, rot)
+    gh.fill_stale(gc, seed=3)
+    gh.gpu_fill(inp, rot, gc)
+    print(f"[decode balanced slices d={d} hq={hq} hkv={hkv} {mode}] B={len(lens)} max={int(lens.max())}", flush=True)
+    got = gh.gpu_decode(inp, gc)
+    int2, bf = gh.gpu_pages(inp, gc)
+    q = synth.bf16_bits_to_f32(inp.q).astype(np.float64)
+    ref = oatt.decode_attention(q, int2, bf, inp.seq_lens, inp.bt_q, inp.bt_h, rot.r_k, rot.r_v, w.n_sink, w.n_recent)
+    for b, L in enumerate(lens):
+        gh.assert_attention_close(got[b], ref[b], f"seq {b} len {L}")
+
+
 def test_bf16_baseline_balanced_slices(tiny_rot):
     from oracle import attention as oatt
     lens = np.random.default_rng(12).integers(1, 600, size=72)
