@@ -145,10 +145,10 @@ def test_decode_step_shapes(d, hq, hkv, S, W, split):
                seed=d + W)
 
 
-@pytest.mark.parametrize("d,hq,hkv", [(64, 8, 2), (128, 16, 2), (64, 16, 8)])
+@pytest.mark.parametrize("d,hq,hkv", [(64, 8, 2), (128, 16, 2), (128, 32, 2), (64, 16, 8)])
 def test_decode_step_balanced_slices(d, hq, hkv):
     # many (sequence, KV head) units: the balanced-slice kernel, whose
-    # workgroups cross units and page kinds (groups of 4 and of 8); 144 units
+    # workgroups cross units and page kinds (groups of 4, 8 and 16); 144 units
     # take the fused launch, 576 units (more than the CUs) the update kernel
     # and then the decode
     rng = np.random.default_rng(5)
