@@ -94,6 +94,17 @@ struct Tile {
 };
 
 __device__ __forceinline__ uint32_t f16pair(float a, float b) { return pack_f16x2(a, b); }
+// Dequantized f16 pair (c0 s0 + z0, c1 s1 + z1) from a code pair held as f16
+// subnormals (c 2^-24 in each half of x, from one mask of the code word):
+// with S = s 2^24 the products c s are exact, and each half is one mixed-
+// precision FMA rounded once to f16, as fma(float(c), s, z) then to f16.
+constexpr float kTwo24 = 16777216.0f;
+typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t dq_pair(uint32_t x, float S0, float z0, float S1, float z1) {
+  const h16x2 c = __builtin_bit_cast(h16x2, x);
+  const h16x2 v = {(_Float16)__builtin_fmaf((float)c[0], S0, z0), (_Float16)__builtin_fmaf((float)c[1], S1, z1)};
+  return __builtin_bit_cast(uint32_t, v);
+}
 
 // Region plan of a length-P cache: BF16 pages (range A = sink, range B =
 // recent; one range when they meet) and the quantized pages [q0, q1).
@@ -293,27 +304,29 @@ __device__ __forceinline__ void step_store(const AttParams& p, const Regions& rg
         const int pos = 16 * pg + slot;
         return pg < rg.q1 && pos >= rg.m0 && pos < rg.m1;
       };
+      // Key codes r and r + 1 of a word (one token, one group) sit 16 bits
+      // apart (the MFMA-shaped page layout), so one shift and mask gives a
+      // pair as f16 subnormals.  A slot outside the middle region gets scale
+      // and zero 0: its value is 0 whatever stale bytes it holds.
       {  // K word: token m, channels 32 g + 16 hb + 4 quad + r, g in {2w, 2w + 1}
         const int quad = wi / (16 * NW), m = (wi / NW) % 16, w = wi % NW;
         const bool ok = live(m);
         const uint32_t word = st.qw[it][0], ks = st.qw[it][1], kz = st.qw[it][2];
 #pragma unroll
         for (int gg = 0; gg < 2; ++gg) {
-          const float s = f16_to_f32(ks >> (16 * gg)), z = f16_to_f32(kz >> (16 * gg));
+          const float S = ok ? f16_to_f32(ks >> (16 * gg)) * kTwo24 : 0.f, z = ok ? f16_to_f32(kz >> (16 * gg)) : 0.f;
 #pragma unroll
           for (int hb = 0; hb < 2; ++hb) {
-            float v[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int bit = 16 * (r & 1) + 8 * gg + 4 * hb + 2 * (r >> 1);
-              v[r] = ok ? __builtin_fmaf(float((word >> bit) & 3u), s, z) : 0.f;
-            }
+            const int b = 8 * gg + 4 * hb;  // codes r = 0, 1 at b, b + 16; r = 2, 3 at b + 2, b + 18
             const int c = 32 * (2 * w + gg) + 16 * hb + 4 * quad;
-            *reinterpret_cast<u32x2*>(tile + (16 * j + m) * T::KROW + c) = u32x2{f16pair(v[0], v[1]), f16pair(v[2], v[3])};
+            *reinterpret_cast<u32x2*>(tile + (16 * j + m) * T::KROW + c) =
+                u32x2{dq_pair((word >> b) & 0x00030003u, S, z, S, z), dq_pair((word >> (b + 2)) & 0x00030003u, S, z, S, z)};
           }
         }
       }
       {  // V word: tokens 4 q + r, channels c16 + 16 (4 w + bb), group 2 w + bb / 2
+        // (each code of a pair has its own token's scale: one code at a time,
+        // the f16 scale and zero going into the FMA as they are)
         const int q = wi / (16 * NW), c16 = (wi / NW) % 16, w = wi % NW;
         const uint32_t word = st.qw[it][3];
 #pragma unroll
@@ -343,19 +356,26 @@ __device__ __forceinline__ void step_store(const AttParams& p, const Regions& rg
       const int m = wi % 16, c0 = 16 * (wi / 16);  // as in step_load
       const int pos = 16 * pg + m;
       const bool ok = pg < rg.q1 && pos >= rg.m0 && pos < rg.m1;
-      const float ks = f16_to_f32(st.qw[it][4]), kz = f16_to_f32(st.qw[it][5]);
-      const float vs = f16_to_f32(st.qw[it][6]), vz = f16_to_f32(st.qw[it][7]);
+      // codes as f16 subnormals (c 2^-24) with S = s 2^24, as in the INT2
+      // case; a key code pair is the two nibbles of one byte: the byte is
+      // placed in both halves of a word and masked to its low nibble (low
+      // half) and its high nibble (high half, 16 c 2^-24: scale S / 16)
+      const float KS = ok ? f16_to_f32(st.qw[it][4]) * kTwo24 : 0.f, kz = ok ? f16_to_f32(st.qw[it][5]) : 0.f;
+      const float VS = ok ? f16_to_f32(st.qw[it][6]) * kTwo24 : 0.f, vz = ok ? f16_to_f32(st.qw[it][7]) : 0.f;
 #pragma unroll
       for (int hw = 0; hw < 2; ++hw) {
         const uint32_t kw = st.qw[it][hw], vw = st.qw[it][2 + hw];
-        float v[8];
+        uint32_t kp[4];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) v[k] = ok ? __builtin_fmaf(float((kw >> (4 * k)) & 15u), ks, kz) : 0.f;
-        *reinterpret_cast<u32x4*>(tile + (16 * j + m) * T::KROW + c0 + 8 * hw) =
-            u32x4{f16pair(v[0], v[1]), f16pair(v[2], v[3]), f16pair(v[4], v[5]), f16pair(v[6], v[7])};
+        for (int i = 0; i < 4; ++i) {
+          // byte i of kw into bytes 0 and 2 (selector 0x0C: a zero byte)
+          const uint32_t x = __builtin_amdgcn_perm(0u, kw, uint32_t(i) | 0x0C00u | (uint32_t(i) << 16) | 0x0C000000u);
+          kp[i] = dq_pair(x & 0x00F0000Fu, KS, kz, KS * 0.0625f, kz);
+        }
+        *reinterpret_cast<u32x4*>(tile + (16 * j + m) * T::KROW + c0 + 8 * hw) = u32x4{kp[0], kp[1], kp[2], kp[3]};
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
-          const float x = ok ? __builtin_fmaf(float((vw >> (4 * k)) & 15u), vs, vz) : 0.f;
+          const float x = __builtin_fmaf(f16_to_f32((vw >> (4 * k)) & 15u), VS, vz);
           vt[(c0 + 8 * hw + k) * T::VROW + 16 * j + m] = uint16_t(f16_bits(x));
         }
       }
