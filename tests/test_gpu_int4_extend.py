@@ -131,7 +131,8 @@ def test_int4_append_scattered_rows_keep_the_rest(d, hkv, n_rows):
 
 
 @pytest.mark.parametrize("hq,hkv,d,lens", [(4, 1, 64, [512]), (4, 1, 64, [1, 17, 36, 37, 100, 0, 300]),
-                                           (8, 2, 128, [700, 333]), (12, 1, 128, [650, 64]), (3, 1, 64, [400])])
+                                           (8, 2, 128, [700, 333]), (12, 1, 128, [650, 64]), (3, 1, 64, [400]),
+                                           (16, 1, 128, [900, 45])])
 def test_int4_decode(hq, hkv, d, lens):
     w = synth.Workload("dec4", 6, len(lens), hq, hkv, d, 4, 32, 512, ("fixed", 700, 700))
     rot = _rot_for(w, 512)
@@ -171,7 +172,7 @@ def test_int4_decode_many_units_and_regions():
 
 
 @pytest.mark.parametrize("bits", [2, 4])
-@pytest.mark.parametrize("hq,hkv,d", [(4, 1, 64), (8, 2, 128), (12, 1, 128), (3, 1, 64)])
+@pytest.mark.parametrize("hq,hkv,d", [(4, 1, 64), (8, 2, 128), (12, 1, 128), (3, 1, 64), (16, 1, 128)])
 def test_extend_attention(bits, hq, hkv, d):
     # cached prefixes of many lengths (none, inside the sink, boundary pages,
     # long middles) extended by 1 .. 70 new rows, causal over them; pools
