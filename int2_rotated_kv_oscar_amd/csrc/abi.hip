@@ -103,20 +103,42 @@ oscar_status plan_decode(int32_t batch, int32_t n_kv, int32_t n_q, int32_t d, in
   const int max_rec = oscar_launch::decode_max_records();
   const long long cus = device_cu_count();
   plan->per_unit = split_pages != 0 || 4 * units <= cus;
+  plan->first_int2 = 0;
   if (plan->per_unit) {
-    long long split = split_pages;
+    long long split = split_pages, first = 0;
     if (!split) {
-      const long long items = std::max(1LL, all_raw ? cus : cus - units);
-      split = std::max<long long>(oscar_launch::decode_min_slice(), (units * max_pages + items - 1) / items);
-      split = std::max(split, (max_pages + max_rec - 2) / (max_rec - 1));
-      split = (split + 7) / 8 * 8;  // measured: fewer, slightly larger items beat an uneven last pair round
+      // With long INT2 items the BF16 pages join item 0, which then takes
+      // `first` INT2 pages fewer than a full item, the BF16 segment's cost
+      // (its fixed cost plus its pages, in INT2 pages: about seg_pages(G) +
+      // 64), so that every workgroup of the round holds INT2 work; kept when
+      // that first chunk is at least 64 pages (not for short histories, whose
+      // items are mostly fixed cost).
+      const long long per = all_raw || units == 0 ? 0 : cus / units;
+      const long long c0 = oscar_launch::decode_seg_pages_of(G) + 64;
+      if (per >= 2) {
+        const long long sp = ((max_pages + c0 + per - 1) / per + 7) / 8 * 8;
+        if (sp - c0 >= 64 && sp >= (max_pages + max_rec - 3) / (max_rec - 2)) {
+          split = sp;
+          first = (sp - c0) / 8 * 8;
+        }
+      }
+      if (!split) {
+        const long long items = std::max(1LL, all_raw ? cus : cus - units);
+        split = std::max<long long>(oscar_launch::decode_min_slice(), (units * max_pages + items - 1) / items);
+        split = std::max(split, (max_pages + max_rec - 2) / (max_rec - 1));
+        split = (split + 7) / 8 * 8;  // measured: fewer, slightly larger items beat an uneven last pair round
+      }
     }
-    const long long n_items = 1 + (max_pages + split - 1) / split;
-    if (n_items > max_rec) return fail(OSCAR_ERR_UNSUPPORTED, "more chunks per (sequence, KV head) than one merge takes; use a larger split_pages");
+    // workgroups per unit: item 0 (BF16 pages and `first` INT2 pages), then
+    // the INT2 items; records: one per segment
+    const long long n_items = 1 + (std::max(0LL, max_pages - first) + split - 1) / split;
+    const long long n_rec = n_items + (first > 0 ? 1 : 0);
+    if (n_rec > max_rec) return fail(OSCAR_ERR_UNSUPPORTED, "more chunks per (sequence, KV head) than one merge takes; use a larger split_pages");
     if (units * n_items > (1LL << 31) - 1) return fail(OSCAR_ERR_UNSUPPORTED, "grid too large; use a larger split_pages");
     plan->fixed_ppw = int(split);
+    plan->first_int2 = int(first);
     plan->unit_items = int(n_items);
-    plan->cap = int(n_items);
+    plan->cap = int(n_rec);
     plan->n_wg = int(std::max(1LL, units * n_items));
   } else {
     plan->fixed_ppw = 0;
@@ -339,7 +361,7 @@ oscar_status decode_launch(bool all_raw, const oscar_cache* cache, const void* q
   return hip_status(
       oscar_launch::paged_decode(cache->d, all_raw, cache->int2_pool, cache->n_int2_pages, cache->bf16_pool, cache->n_kv_heads, G,
                                  cache->n_sink, cache->n_recent, n_q_heads, q, batch, seq_lens, all_raw ? bt_h : bt_q,
-                                 bt_h, max_pages, r_k, r_v, sm_scale, plan.per_unit, plan.unit_items, plan.fixed_ppw,
+                                 bt_h, max_pages, r_k, r_v, sm_scale, plan.per_unit, plan.unit_items, plan.first_int2, plan.fixed_ppw,
                                  plan.n_wg, plan.cap, max_seq_len, partials, counters, plan.rec_floats, out,
                                  4LL * batch * cache->n_kv_heads < device_cu_count(), k_new, v_new, tau_k, tau_v,
                                  static_cast<hipStream_t>(stream)),

@@ -15,6 +15,7 @@ int device_cu_count();
 struct DecodePlan {
   bool per_unit;    // per-unit items, or balanced slices over all units
   int unit_items;   // per-unit items: workgroups per (sequence, KV head)
+  int first_int2;   // per-unit items: INT2 pages item 0 takes after the BF16 pages (0: none)
   int fixed_ppw;    // per-unit items: pages per item; slices: pages per slice (0: spread evenly)
   int n_wg;         // workgroups in the grid
   int cap;          // record slots per (sequence, KV head)

@@ -63,6 +63,7 @@ struct DecParams {
   int32_t batch;
   int32_t per_unit;    // per-unit items (1) or balanced slices (0)
   int32_t unit_items;  // per-unit items: workgroups per (sequence, KV head)
+  int32_t first_int2;  // per-unit items: INT2 pages item 0 takes after the BF16 pages (0: none)
   // fused decode step: the step's new tokens (bf16 [B][n_kv][D]) and the clip
   // thresholds of the token entering the middle history
   const uint16_t* k_new;
@@ -1131,20 +1132,21 @@ __global__ __launch_bounds__(kThreads, kWaves == 4 ? 2 : 1) void decode_kernel(D
 
   if constexpr (!SLICES) {
     // Per-unit items (few units): workgroup wg is item x of unit (b, h).  Item 0
-    // takes the unit's BF16 pages, item x >= 1 INT2 pages
-    // [q0 + (x-1) split, q0 + x split) (for the all-BF16 cache: item x takes
-    // BF16 positions [x split, (x+1) split)).  INT2 items do not depend on the
-    // length, so their requests go out before it is read.
+    // takes the unit's BF16 pages and the first f0 INT2 pages (f0 = 0 for
+    // short items), item x >= 1 INT2 pages [q0 + f0 + (x-1) split, + split)
+    // (for the all-BF16 cache: item x takes BF16 positions
+    // [x split, (x+1) split)).  INT2 items x >= 1 do not depend on the length,
+    // so their requests go out before it is read.
     // The KV head varies fastest over the workgroup index: the workgroups
     // dispatched together read the same pages' head images (one page holds
     // every head of its 16 tokens), which keeps HBM rows open.
-    const int per = p.unit_items, split = p.fixed_ppw;
+    const int per = p.unit_items, split = p.fixed_ppw, f0 = p.first_int2;
     const int hw = wg % p.n_kv, bx = wg / p.n_kv, x = bx % per;
     set_unit(bx / per, hw);
     // the length is requested first: waiting for it then leaves the early
     // page requests in flight
     const int L = p.seq_lens[b];
-    if (!ALL_RAW && p.speculate && x >= 1) speculate_at(b, h, (p.S >> 4) + (x - 1) * split);
+    if (!ALL_RAW && p.speculate && x >= 1) speculate_at(b, h, (p.S >> 4) + f0 + (x - 1) * split);
     if (L <= 0) {
       if (x == 0 && h == 0)
         for (int e = tid; e < p.Hq * D; e += kThreads) p.out[size_t(b) * p.Hq * D + e] = 0;
@@ -1157,11 +1159,22 @@ __global__ __launch_bounds__(kThreads, kWaves == 4 ? 2 : 1) void decode_kernel(D
       segment(std::true_type{}, true, x * split, min(sp.n_raw, (x + 1) * split), nseg, x);
       return;
     }
-    const int has_raw = sp.n_raw > 0 ? 1 : 0, nq = (sp.q1 - sp.q0 + split - 1) / split;
-    if (x == 0 ? !has_raw : x - 1 >= nq) return;
-    const int q0 = sp.q0 + (x - 1) * split;
-    segment(std::true_type{}, x == 0, x == 0 ? 0 : q0, x == 0 ? sp.n_raw : min(sp.q1, q0 + split), has_raw + nq,
-            x == 0 ? 0 : has_raw + x - 1);
+    // item 0: the BF16 pages, then the first c0n INT2 pages (a second segment
+    // in the same workgroup); item x >= 1: INT2 pages [q0 + c0n + (x-1) split, + split)
+    const int has_raw = sp.n_raw > 0 ? 1 : 0, nmid = sp.q1 - sp.q0, c0n = min(nmid, f0);
+    const int head = c0n > 0 ? 1 : 0;
+    const int nq = head + (nmid - c0n + split - 1) / split;
+    if (x == 0) {
+      if (has_raw) segment(std::true_type{}, true, 0, sp.n_raw, has_raw + nq, 0);
+      if (head) {
+        if (has_raw) lds_barrier();  // LDS of that segment's merge is rewritten by this one
+        segment(std::false_type{}, false, sp.q0, sp.q0 + c0n, has_raw + nq, has_raw);
+      }
+      return;
+    }
+    if (x - 1 >= nq - head) return;
+    const int q0 = sp.q0 + c0n + (x - 1) * split;
+    segment(std::true_type{}, false, q0, min(sp.q1, q0 + split), has_raw + nq, has_raw + head + x - 1);
   } else {
   // Balanced slices (many units): the units, sequence-major, put their work
   // (BF16 sink and recent pages, INT2 pages, then seg_pages(G) positions per
@@ -1285,6 +1298,8 @@ int decode_min_slice() { return kMinSlice; }
 
 int decode_seg_pages() { return kSegPagesMax; }
 
+int decode_seg_pages_of(int G) { return seg_pages(G); }
+
 int decode_own_pages() { return kOwnPages; }
 
 size_t decode_lds_bytes(int d, int G, bool all_raw) {
@@ -1299,13 +1314,13 @@ size_t decode_lds_bytes(int d, int G, bool all_raw) {
 hipError_t paged_decode(int d, bool all_raw, const void* int2_pool, int n_int2_pages, const void* bf16_pool, int n_kv, int G, int S,
                         int W, int Hq, const void* q, int batch, const int32_t* seq_lens, const int32_t* bt_q,
                         const int32_t* bt_h, int max_pages, const float* r_k, const float* r_v, float sm_scale,
-                        bool per_unit, int unit_items, int fixed_ppw, int n_wg, int cap, int max_seq_len,
+                        bool per_unit, int unit_items, int first_int2, int fixed_ppw, int n_wg, int cap, int max_seq_len,
                         float* partials, int32_t* counters, int rec_floats, void* out, bool speculate,
                         const void* k_new, const void* v_new, float tau_k, float tau_v, hipStream_t stream) {
   DecParams p{static_cast<const uint8_t*>(int2_pool), std::max(1, n_int2_pages), static_cast<const uint16_t*>(bf16_pool), n_kv, G, S, W, Hq,
               static_cast<const uint16_t*>(q), seq_lens, bt_q, bt_h, max_pages, r_k, r_v, sm_scale, fixed_ppw,
               partials, counters, rec_floats, cap, static_cast<uint16_t*>(out), speculate ? 1 : 0, max_seq_len, batch,
-              per_unit ? 1 : 0, unit_items, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
+              per_unit ? 1 : 0, unit_items, first_int2, static_cast<const uint16_t*>(k_new), static_cast<const uint16_t*>(v_new),
               tau_k, tau_v};
   const bool upd = k_new != nullptr;
   const dim3 grid(static_cast<unsigned>(n_wg));

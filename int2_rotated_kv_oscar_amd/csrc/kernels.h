@@ -27,13 +27,14 @@ size_t decode_lds_bytes(int d, int G, bool all_raw);
 int decode_max_records();  // record slots per (sequence, KV head) the merge can hold
 int decode_min_slice();    // pages per workgroup slice at least
 int decode_seg_pages();    // extra positions per nonempty page range in balanced slices (at most)
+int decode_seg_pages_of(int G);  // the same for query group G
 int decode_own_pages();    // extra positions of a unit whose fused step quantizes a token
 
 // k_new != nullptr: the fused decode step (the step's cache update in the same launch)
 hipError_t paged_decode(int d, bool all_raw, const void* int2_pool, int n_int2_pages, const void* bf16_pool, int n_kv, int G, int S,
                         int W, int Hq, const void* q, int batch, const int32_t* seq_lens, const int32_t* bt_q,
                         const int32_t* bt_h, int max_pages, const float* r_k, const float* r_v, float sm_scale,
-                        bool per_unit, int unit_items, int fixed_ppw, int n_wg, int cap, int max_seq_len,
+                        bool per_unit, int unit_items, int first_int2, int fixed_ppw, int n_wg, int cap, int max_seq_len,
                         float* partials, int32_t* counters, int rec_floats, void* out, bool speculate,
                         const void* k_new, const void* v_new, float tau_k, float tau_v, hipStream_t stream);
 
