@@ -159,6 +159,15 @@ def test_decode_step_balanced_slices(d, hq, hkv):
     _run_steps(_wl(d, hq, hkv, 4, 32, len(lens), cfg=47), lens, 6, seed=3)
 
 
+def test_decode_step_long_items_first_item_takes_int2_pages():
+    # 64 units of up to 20k tokens (group of 4) on 256 CUs: per-unit items of
+    # 376 pages, item 0 holding the BF16 pages and the first 152 INT2 pages;
+    # the ragged lengths give middles shorter than that first chunk, empty
+    # middles, an empty sequence and partial last items
+    lens = np.array([20000, 9000, 2500, 150, 0, 18, 16000, 5000], np.int32)
+    _run_steps(_wl(128, 32, 8, 4, 128, len(lens), cfg=49), lens, 3, seed=7)
+
+
 def test_decode_step_rejects_bad_arguments():
     w = _wl(64, 4, 1, 4, 32, 1)
     inp = _full_tables(synth.decode_inputs(w, seq_lens=np.array([40], np.int32)), 1)
