@@ -1021,11 +1021,32 @@ __global__ __launch_bounds__(kThreads, kWaves == 4 ? 2 : 1) void decode_kernel(D
       cf[i] = ld_dev(recs + size_t(s) * p.rec_floats + 2 * G + G * D);
     }
   }
+  // Balanced slices, up to half a batch of records (the usual case) and more
+  // than one round of elements (G D > kThreads): one batch holds the values
+  // of two element rounds, [e0, e0 + kThreads) and the next, so that one wait
+  // serves both (measured: 96q/8kv batch 64, 2% faster).  CS column slots
+  // hold at most 16 / CS queries, so the four-slot kernel at d = 128 and the
+  // two- and four-slot ones at d = 64 never pair.  The per-unit kernels inline
+  // the merge at several segment sites and keep the single-round form: the
+  // second form's code cost them what its wait saved.
+  constexpr int kHalf = kMergeBatch / 2;
+  constexpr bool kCanPair = SLICES && !ALL_RAW && (16 / CS) * D > kThreads;
+  const bool paired = kCanPair && n_s <= kHalf && G * D > kThreads;
   float vv[kMergeBatch];
   auto load_batch = [&](int e0, int s0) {
-    const size_t e = size_t(2 * G + min(e0 + tid, G * D - 1));
+    if (paired) {
+      const size_t ea = size_t(2 * G + min(e0 + tid, G * D - 1));
+      const size_t eb = size_t(2 * G + min(e0 + kThreads + tid, G * D - 1));
 #pragma unroll
-    for (int k = 0; k < kMergeBatch; ++k) vv[k] = ld_dev(recs + size_t(min(s0 + k, n_s - 1)) * p.rec_floats + e);
+      for (int k = 0; k < kHalf; ++k) vv[k] = ld_dev(recs + size_t(min(k, n_s - 1)) * p.rec_floats + ea);
+      if (e0 + kThreads < G * D)
+#pragma unroll
+        for (int k = 0; k < kHalf; ++k) vv[kHalf + k] = ld_dev(recs + size_t(min(k, n_s - 1)) * p.rec_floats + eb);
+    } else {
+      const size_t e = size_t(2 * G + min(e0 + tid, G * D - 1));
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) vv[k] = ld_dev(recs + size_t(min(s0 + k, n_s - 1)) * p.rec_floats + e);
+    }
   };
   load_batch(0, 0);
   // R_V rows of output block cb = wave, requested after the records (the
@@ -1071,18 +1092,7 @@ __global__ __launch_bounds__(kThreads, kWaves == 4 ? 2 : 1) void decode_kernel(D
   lsum = wave_sum16(lsum);
   if (quad == 0) s_red[16 * kWaves + wave * 16 + ms_n] = lsum;
   lds_barrier();
-  for (int e0 = 0; e0 < G * D; e0 += kThreads) {
-    const int e = e0 + tid;
-    const int n = min(e / D, 15);
-    float orot = 0.f, oraw = 0.f;
-    for (int s0 = 0; s0 < n_s; s0 += kMergeBatch) {
-      if (e0 > 0 || s0 > 0) load_batch(e0, s0);
-#pragma unroll
-      for (int k = 0; k < kMergeBatch; ++k) {
-        orot = fmaf(s_wr[(s0 + k) * 16 + n], vv[k], orot);
-        oraw = fmaf(s_wu[(s0 + k) * 16 + n], vv[k], oraw);
-      }
-    }
+  auto store_merged = [&](int e, int n, float orot, float oraw) {
     if (e < G * D) {
       float Ln = 0.f;
 #pragma unroll
@@ -1090,6 +1100,40 @@ __global__ __launch_bounds__(kThreads, kWaves == 4 ? 2 : 1) void decode_kernel(D
       const float inv = 1.f / Ln;
       m_rot[e] = orot * inv;
       m_raw[e] = oraw * inv;
+    }
+  };
+  if (paired) {
+    // weights of records [n_s, kHalf) are zero
+    for (int e0 = 0; e0 < G * D; e0 += 2 * kThreads) {
+      if (e0 > 0) load_batch(e0, 0);
+#pragma unroll
+      for (int r = 0; r < 2; ++r) {
+        if (e0 + r * kThreads >= G * D) break;  // uniform: the second round's values were not loaded
+        const int e = e0 + r * kThreads + tid;
+        const int n = min(e / D, 15);
+        float orot = 0.f, oraw = 0.f;
+#pragma unroll
+        for (int k = 0; k < kHalf; ++k) {
+          orot = fmaf(s_wr[k * 16 + n], vv[r * kHalf + k], orot);
+          oraw = fmaf(s_wu[k * 16 + n], vv[r * kHalf + k], oraw);
+        }
+        store_merged(e, n, orot, oraw);
+      }
+    }
+  } else {
+    for (int e0 = 0; e0 < G * D; e0 += kThreads) {
+      const int e = e0 + tid;
+      const int n = min(e / D, 15);
+      float orot = 0.f, oraw = 0.f;
+      for (int s0 = 0; s0 < n_s; s0 += kMergeBatch) {
+        if (e0 > 0 || s0 > 0) load_batch(e0, s0);
+#pragma unroll
+        for (int k = 0; k < kMergeBatch; ++k) {
+          orot = fmaf(s_wr[(s0 + k) * 16 + n], vv[k], orot);
+          oraw = fmaf(s_wu[(s0 + k) * 16 + n], vv[k], oraw);
+        }
+      }
+      store_merged(e, n, orot, oraw);
     }
   }
   lds_barrier();
