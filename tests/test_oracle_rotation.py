@@ -49,7 +49,7 @@ def test_bit_reversal_textbook_and_involution():
 
 
 def test_eig_recovers_planted_spectrum():
-    # O4/O5 without LAPACK as the judge: plant C = U0 diag(l0) U0^T with known
+    # O4/O5 without LAPACK deciding the outcome: plant C = U0 diag(l0) U0^T with known
     # distinct eigenvalues and check they come back, descending, with columns
     # equal to the planted ones up to the documented sign rule.
     rng = np.random.default_rng(7)
