@@ -834,10 +834,10 @@ __global__ __launch_bounds__(64 * NWV, 2) void attend_kernel(AttParams p) {
 // Log-sum-exp merge of the chunk records of one column, then the output
 // rotation: M = max_k m_k, w_k = 2^(m_k - M),
 // out = (sum_k w_k raw_k + (sum_k w_k rot_k) R_V^T) / sum_k w_k l_k.
-// One workgroup per (unit, column tile, column).  Its R_V entries (output
-// channel c = tid / TPC, a KPT-long run of k) and the first LB records'
-// values of each wave are requested first, so they arrive while the maxima
-// and sums are reduced; the four waves take every fourth chunk (a lane holds
+// One workgroup per (unit, column tile, column).  The chunk maxima and sums
+// are requested first, then its R_V entries (output channel c = tid / TPC, a
+// KPT-long run of k) and the first LB records' values of each wave, which
+// arrive while the maxima and sums are reduced; the four waves take every fourth chunk (a lane holds
 // FPL of the 2d value sums, LB chunks' loads in flight) and meet in LDS.
 // LB = 32 for the decode (about 3 CUs of chunks per column: one batch per
 // wave), 16 for extend (many more merge workgroups, fewer registers).
@@ -861,6 +861,14 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttParams p) {
   const int ri = col / G, hi = col % G;
   const size_t cstride = size_t(NC) * RF;
   const float* rec0 = p.rec + ((size_t(unit) * p.n_ct + ct) * nk * NC + cl) * RF;
+  // maxima and sums first: thread k holds chunk k's (first 256 chunks); the
+  // loads below are requested behind them, so the reduction waits only for
+  // these two (load counters retire in order)
+  float m0 = kNegInfA, l0 = 0.f;
+  if (tid < nk) {
+    m0 = rec0[tid * cstride];
+    l0 = rec0[tid * cstride + 1];
+  }
   const int c = tid / TPC, k0 = KPT * (tid % TPC);
   const float* rrow = p.r_v + size_t(u.h) * D * D + size_t(c) * D + k0;
   f32x4 rr[KPT / 4];
@@ -889,12 +897,6 @@ __global__ __launch_bounds__(256) void attend_merge_kernel(AttParams p) {
     }
   };
   load_batch(0);
-  // maxima and sums: thread k holds chunk k's (first 256 chunks)
-  float m0 = kNegInfA, l0 = 0.f;
-  if (tid < nk) {
-    m0 = rec0[tid * cstride];
-    l0 = rec0[tid * cstride + 1];
-  }
   float mx = m0;
   for (int k = tid + 256; k < nk; k += 256) mx = fmaxf(mx, rec0[k * cstride]);
 #pragma unroll
